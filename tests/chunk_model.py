@@ -1,0 +1,85 @@
+"""NumPy model of the chunkwise form of the KDA recurrence (test helper).
+
+This is the algebra the GPU kernels implement, written out plainly so it can be
+checked against the token-by-token oracle, and so the effect of rounding the
+matrix-core operands to bf16 can be measured on the CPU before any GPU code.
+
+Per chunk of C tokens entering with state S (dk x dv), with G the inclusive
+cumulative sum of g inside the chunk (G_{-1} = 0):
+  A_rj = beta_r sum_c k_rc k_jc e^{G_rc - G_jc}     (j < r)
+  T    = (I + A)^-1
+  W    = T diag(beta) (K * e^G) ;  U~ = T diag(beta) V
+  U    = U~ - W S
+  P_rj = sum_c q_rc k_jc e^{G_rc - G_jc}            (j <= r)
+  O    = (Q * e^G) S + P U
+  S'   = diag(e^{G_C}) S + (K * e^{G_C - G})^T U
+The decay-weighted products use 16-token tiles: row tile a takes the reference
+rho_a = G at the token before the tile (0 for the first tile), so the row factor
+e^{G_r - rho_a} <= 1 and the column factor e^{rho_a - G_j} is <= 1 for earlier
+tiles and bounded by e^{16 max|g|} inside the tile.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+TILE = 16
+
+
+def _bf16(x):
+    """Round to bf16 (nearest even) and back, elementwise, through float32."""
+    f = np.asarray(x, dtype=np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(np.float64)
+
+
+def _fp16(x):
+    """Round to IEEE half (nearest even) and back."""
+    return np.asarray(x, dtype=np.float16).astype(np.float64)
+
+
+def _id(x):
+    return np.asarray(x, dtype=np.float64)
+
+
+def chunk_core(qn, kn, vn, g, beta, S0, C=64, operands=None, tile=TILE):
+    """Chunkwise o_core [T,dv] and final state for one (b,h).
+
+    qn, kn [T,dk] (q already scaled by dk^-1/2), vn [T,dv], g [T,dk], beta [T].
+    operands = None (exact fp64), "bf16" or "fp16": every matrix-core operand is
+    rounded to that type while accumulation, decay factors and the state stay in
+    higher precision, as in the GPU kernels.
+    """
+    rnd = {None: _id, "bf16": _bf16, "fp16": _fp16}[operands]
+    f32 = _id if operands is None else (lambda x: np.asarray(x, dtype=np.float32).astype(np.float64))
+    T, dk = qn.shape
+    dv = vn.shape[1]
+    S = np.array(S0, dtype=np.float64)
+    o = np.zeros((T, dv))
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        n = c1 - c0
+        Q, K, V = f32(qn[c0:c1]), f32(kn[c0:c1]), f32(vn[c0:c1])
+        b = f32(beta[c0:c1])
+        G = f32(np.cumsum(g[c0:c1], axis=0))
+        A = np.zeros((n, n))
+        P = np.zeros((n, n))
+        for a0 in range(0, n, tile):
+            a1 = min(n, a0 + tile)
+            rho = G[a0 - 1] if a0 > 0 else np.zeros(dk)
+            rowf = np.exp(G[a0:a1] - rho)                        # <= 1
+            colf = np.exp(rho - G[:a1])                          # <= 1 before a0
+            Kr, Qr, Kc = rnd(K[a0:a1] * rowf), rnd(Q[a0:a1] * rowf), rnd(K[:a1] * colf)
+            A[a0:a1, :a1] = Kr @ Kc.T
+            P[a0:a1, :a1] = Qr @ Kc.T
+        A = np.tril(A, -1) * b[:, None]
+        P = np.tril(P, 0)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        Tb = rnd(Tm * b[None, :])
+        W = Tb @ rnd(K * np.exp(G))
+        Ut = Tb @ rnd(V)
+        U = Ut - rnd(W) @ rnd(S)
+        Ub = rnd(U)
+        o[c0:c1] = rnd(Q * np.exp(G)) @ rnd(S) + rnd(P) @ Ub
+        S = np.exp(G[-1])[:, None] * S + rnd(K * np.exp(G[-1] - G)).T @ Ub
+    return o, S

@@ -1,0 +1,84 @@
+"""The chunkwise algebra the kernels implement, checked against the oracle (CPU).
+
+* exact in fp64 for several chunk sizes, ragged tails and a non-zero state;
+* the operand-precision budget on prefill-like data: bf16 matrix-core operands
+  put the max error at several times 1e-2 x RMS, too close to (or past) the
+  2e-2 x RMS bound, while fp16 operands (same matrix-core rate, three more
+  mantissa bits) stay under 0.4 of it.  That fixes the kernels' scheme:
+  fp16 operands, fp32 accumulation, fp32 state, fp32 output.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import kda_synth as syn
+from chunk_model import chunk_core
+from kda_synth import Workload, to_f64
+from ref_math import gated_rmsnorm, head_channels, prep_numpy
+
+
+def _case(T, dk, dv, dtype="f32", s0=0.2, seed=11, H=1):
+    w = Workload("c", 1, T, H, dk, dv, 64, dtype, s0_sigma=s0, conv_hist="normal", seed=seed)
+    return w, syn.prefill_inputs_np(w)
+
+
+@pytest.mark.parametrize("C", [1, 2, 16, 64])
+@pytest.mark.parametrize("T", [1, 15, 17, 64, 100])
+def test_chunk_algebra_exact(oracle_mod, C, T):
+    w, inp = _case(T, 16, 24)
+    r = oracle_mod.prefill(inp, want_prep=True)
+    prep = r["prep"][0]
+    qn, kn, vn = prep[:, :16], prep[:, 16:32], prep[:, 32:]
+    g = inp["g"][0, :, 0].astype(np.float64)
+    beta = inp["beta"][0, :, 0].astype(np.float64)
+    oc, S = chunk_core(qn, kn, vn, g, beta, inp["S0"][0, 0].astype(np.float64), C=C)
+    o = gated_rmsnorm(oc, inp["gate"][0, :, 0].astype(np.float64))
+    np.testing.assert_allclose(S, r["S_T"][0], rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(o, r["o"][0], rtol=1e-9, atol=1e-11)
+
+
+def test_tile_references_bound_factors():
+    """With g >= -5 no decay factor inside a 16-token tile exceeds e^80 (bf16 and fp32
+    finite), which is what lets the decay-weighted products run as bf16 products."""
+    g = np.full((64, 4), -5.0)
+    G = np.cumsum(g, axis=0)
+    worst = 0.0
+    for a0 in range(0, 64, 16):
+        rho = G[a0 - 1] if a0 else np.zeros(4)
+        worst = max(worst, float(np.max(rho - G[a0:a0 + 16])))
+        assert np.all(G[a0:a0 + 16] - rho <= 0)
+    assert worst == 80.0 and np.isfinite(np.float32(np.exp(worst)))
+
+
+def _operand_error(oracle_mod, operands, T=512, d=128):
+    """max |err| / RMS for o and S_T with the given operand type, C = 64."""
+    w, inp = _case(T, d, d, dtype="bf16", s0=0.01, seed=5, H=2)
+    r = oracle_mod.prefill(inp, want_prep=True)
+    errs_o, errs_s, ro, rs = [], [], [], []
+    for i in range(2):
+        prep = r["prep"][i]
+        qn, kn, vn = prep[:, :d], prep[:, d:2 * d], prep[:, 2 * d:]
+        g = to_f64(inp["g"], "bf16")[0, :, i]
+        beta = to_f64(inp["beta"], "bf16")[0, :, i]
+        gate = to_f64(inp["gate"], "bf16")[0, :, i]
+        oc, S = chunk_core(qn, kn, vn, g, beta, inp["S0"][0, i].astype(np.float64), C=64,
+                           operands=operands)
+        o = gated_rmsnorm(oc, gate)
+        errs_o.append(np.abs(o - r["o"][i]).max())
+        errs_s.append(np.abs(S - r["S_T"][i]).max())
+        ro.append(r["o"][i])
+        rs.append(r["S_T"][i])
+    rms_o = np.sqrt(np.mean(np.square(ro)))
+    rms_s = np.sqrt(np.mean(np.square(rs)))
+    return max(errs_o) / rms_o, max(errs_s) / rms_s
+
+
+def test_operand_precision_budget(oracle_mod):
+    """fp16 operands (d = 128, C = 64, bf16 inputs, non-zero initial state) keep the
+    max error under 0.4 of the 2e-2 x RMS bound for o and S_T; bf16 operands
+    would not (their error is above half the bound)."""
+    eo, es = _operand_error(oracle_mod, "fp16")
+    assert eo < 0.4 * 2e-2 and es < 0.4 * 2e-2, (eo, es)
+    bo, bs = _operand_error(oracle_mod, "bf16")
+    assert max(bo, bs) > 0.5 * 2e-2, (bo, bs)
