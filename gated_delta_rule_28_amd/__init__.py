@@ -1,0 +1,172 @@
+"""MI355X (gfx950) Kimi Delta Attention: Python binding of libkda.so.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in include/kda.h.  Torch supplies device
+memory and the current stream.  If the library is missing the import still
+works, but every call raises (there is no fallback implementation).
+
+    o, S_T, conv_out = prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64)
+    o = decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state)   # S, conv_state in place
+    qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = ["prefill", "decode_step", "prep", "library_path", "lib", "KDAError",
+           "KDA_F32", "KDA_BF16", "PrefillArgs", "DecodeArgs", "PrepArgs"]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+library_path = os.path.join(_HERE, "libkda.so")
+
+KDA_F32 = 0
+KDA_BF16 = 1
+ABI_VERSION = 1
+
+
+class KDAError(RuntimeError):
+    def __init__(self, fn, code, detail):
+        super().__init__(f"{fn} failed with {code}: {detail}")
+        self.code = code
+
+
+_P = ctypes.c_void_p
+
+
+class PrefillArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P), ("g", _P), ("beta", _P),
+                ("gate", _P), ("S0", _P), ("conv_in", _P), ("o", _P), ("S_T", _P),
+                ("conv_out", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+
+
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P), ("g", _P), ("beta", _P),
+                ("gate", _P), ("S", _P), ("conv_state", _P), ("o", _P)]
+
+
+class PrepArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
+                ("in_dtype", ctypes.c_int), ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P),
+                ("g", _P), ("conv_in", _P), ("q_out", _P), ("k_out", _P), ("v_out", _P),
+                ("G_out", _P)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(library_path):
+            raise RuntimeError(f"{library_path} is missing: run `python -m gated_delta_rule_28_amd.build`")
+        L = ctypes.CDLL(library_path)
+        L.kda_prefill.argtypes = [ctypes.POINTER(PrefillArgs), _P]
+        L.kda_prefill.restype = ctypes.c_int
+        L.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
+        L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
+        L.kda_decode_step.restype = ctypes.c_int
+        L.kda_prep.argtypes = [ctypes.POINTER(PrepArgs), _P]
+        L.kda_prep.restype = ctypes.c_int
+        L.kda_status_string.argtypes = [ctypes.c_int]
+        L.kda_status_string.restype = ctypes.c_char_p
+        L.kda_last_error.restype = ctypes.c_char_p
+        L.kda_abi_version.restype = ctypes.c_int
+        if L.kda_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"libkda ABI {L.kda_abi_version()} != binding ABI {ABI_VERSION}")
+        _lib = L
+    return _lib
+
+
+def _check(fn, rc):
+    if rc != 0:
+        L = lib()
+        raise KDAError(fn, rc, f"{L.kda_status_string(rc).decode()} ({L.kda_last_error().decode()})")
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t):
+    torch = _torch()
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    if t.dtype == torch.float32:
+        return KDA_F32
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device):
+    torch = _torch()
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out_dtype=None,
+            o=None, S_T=None, conv_out=None, want_state=True, want_conv=True):
+    """Chunkwise KDA prefill (kda_prefill).  Shapes as in include/kda.h.
+
+    Returns (o, S_T, conv_out); S_T / conv_out are None when not wanted.
+    Passing S_T=S0 / conv_out=conv_in updates the carry in place.
+    """
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_out is None and want_conv:
+        conv_out = torch.empty((B, 3, H * (2 * dk + dv)), dtype=q.dtype, device=dev)
+    a = PrefillArgs(B, T, H, dk, dv, chunk, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
+                    _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in),
+                    _ptr(o), _ptr(S_T), _ptr(conv_out), None, 0)
+    _check("kda_prefill", lib().kda_prefill(ctypes.byref(a), _stream(dev)))
+    return o, S_T, conv_out
+
+
+def decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype=None):
+    """One KDA decode step (kda_decode_step); S and conv_state are updated in place."""
+    torch = _torch()
+    N, H, dk = q.shape
+    dv = v.shape[-1]
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
+    a = DecodeArgs(N, H, dk, dv, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w),
+                   _ptr(g), _ptr(beta), _ptr(gate), _ptr(S), _ptr(conv_state), _ptr(o))
+    _check("kda_decode_step", lib().kda_decode_step(ctypes.byref(a), _stream(q.device)))
+    return o
+
+
+def prep(q, k, v, conv_w, g, conv_in=None, chunk=64):
+    """Stage 1 on its own (kda_prep): returns fp32 (q^, k^, v^, G)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    f = dict(dtype=torch.float32, device=q.device)
+    qo, ko, vo = torch.empty((B, T, H, dk), **f), torch.empty((B, T, H, dk), **f), torch.empty((B, T, H, dv), **f)
+    Go = torch.empty((B, T, H, dk), **f)
+    a = PrepArgs(B, T, H, dk, dv, chunk, _dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w), _ptr(g),
+                 _ptr(conv_in), _ptr(qo), _ptr(ko), _ptr(vo), _ptr(Go))
+    _check("kda_prep", lib().kda_prep(ctypes.byref(a), _stream(q.device)))
+    return qo, ko, vo, Go

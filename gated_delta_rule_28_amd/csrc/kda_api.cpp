@@ -1,0 +1,144 @@
+// kda_api.cpp -- the C ABI of libkda.so: argument validation, error codes,
+// per-thread error text and dispatch to the kernel launchers.
+//
+// Every check happens before any HIP call, so a call that fails validation
+// launches nothing and touches no device state (and can be made on a machine
+// without a GPU).
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+thread_local char g_err[512] = "";
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned_n(const void* p, unsigned n) { return (reinterpret_cast<uintptr_t>(p) & (n - 1)) == 0; }
+bool dim_ok(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+bool dtype_ok(int t) { return t == KDA_F32 || t == KDA_BF16; }
+unsigned esize(int t) { return t == KDA_BF16 ? 2u : 4u; }
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+#define REQUIRE_PTR(p) \
+  if ((p) == nullptr) return kda::fail(KDA_E_NULL, "%s is NULL", #p)
+#define REQUIRE_A16(p) \
+  if ((p) != nullptr && !kda::aligned16(p)) return kda::fail(KDA_E_ALIGN, "%s is not 16-byte aligned", #p)
+
+int check_common(int B, int T, int H, int dk, int dv, int in_dtype, int out_dtype) {
+  if (B < 1 || H < 1 || T < 0) return fail(KDA_E_SHAPE, "B=%d H=%d T=%d out of range", B, H, T);
+  if (dk < 1 || dv < 1) return fail(KDA_E_SHAPE, "dk=%d dv=%d out of range", dk, dv);
+  if (!dtype_ok(in_dtype) || !dtype_ok(out_dtype))
+    return fail(KDA_E_DTYPE, "in_dtype=%d out_dtype=%d not KDA_F32/KDA_BF16", in_dtype, out_dtype);
+  if (!dim_ok(dk) || !dim_ok(dv) || dk != dv)
+    return fail(KDA_E_UNSUPPORTED, "dk=%d dv=%d: head dims must be equal and in {16,32,64,128}", dk, dv);
+  if ((long long)B * H > 0x7fffffffLL) return fail(KDA_E_SHAPE, "B*H=%lld too large", (long long)B * H);
+  return KDA_OK;
+}
+}  // namespace
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+}
+
+}  // namespace kda
+
+using kda::fail;
+
+extern "C" {
+
+int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+const char* kda_last_error(void) { return kda::g_err; }
+
+const char* kda_status_string(int code) {
+  switch (code) {
+    case KDA_OK: return "ok";
+    case KDA_E_NULL: return "a required pointer is NULL";
+    case KDA_E_SHAPE: return "a size is out of range";
+    case KDA_E_DTYPE: return "unknown dtype";
+    case KDA_E_ALIGN: return "a pointer is not 16-byte aligned";
+    case KDA_E_UNSUPPORTED: return "unsupported head dim or chunk size";
+    case KDA_E_WORKSPACE: return "workspace too small";
+    case KDA_E_HIP: return "HIP runtime error";
+    default: return "unknown status code";
+  }
+}
+
+size_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
+  (void)a;
+  return 0;  // the fused prefill keeps every intermediate on chip
+}
+
+int kda_prefill(const kda_prefill_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(a);
+  int rc = kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype);
+  if (rc != KDA_OK) return rc;
+  if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64)
+    return fail(KDA_E_UNSUPPORTED, "chunk=%d not in {16,32,64}", a->chunk);
+  if (a->T > 0) {
+    REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
+    REQUIRE_PTR(a->g); REQUIRE_PTR(a->beta); REQUIRE_PTR(a->gate); REQUIRE_PTR(a->o);
+  }
+  REQUIRE_A16(a->q); REQUIRE_A16(a->k); REQUIRE_A16(a->v); REQUIRE_A16(a->conv_w);
+  REQUIRE_A16(a->g); REQUIRE_A16(a->gate); REQUIRE_A16(a->o); REQUIRE_A16(a->S0);
+  REQUIRE_A16(a->S_T); REQUIRE_A16(a->conv_in); REQUIRE_A16(a->conv_out);
+  if (a->beta != nullptr && !kda::aligned_n(a->beta, kda::esize(a->in_dtype)))
+    return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
+  if (a->workspace_bytes < kda_prefill_workspace_bytes(a))
+    return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", a->workspace_bytes,
+                kda_prefill_workspace_bytes(a));
+  if (a->T == 0 && a->S_T == nullptr && a->conv_out == nullptr) return KDA_OK;
+  return kda::launch_prefill(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int kda_decode_step(const kda_decode_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(a);
+  int rc = kda::check_common(a->N, 1, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype);
+  if (rc != KDA_OK) return rc;
+  REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
+  REQUIRE_PTR(a->g); REQUIRE_PTR(a->beta); REQUIRE_PTR(a->gate); REQUIRE_PTR(a->S);
+  REQUIRE_PTR(a->conv_state); REQUIRE_PTR(a->o);
+  REQUIRE_A16(a->q); REQUIRE_A16(a->k); REQUIRE_A16(a->v); REQUIRE_A16(a->conv_w);
+  REQUIRE_A16(a->g); REQUIRE_A16(a->gate); REQUIRE_A16(a->S); REQUIRE_A16(a->conv_state);
+  REQUIRE_A16(a->o);
+  if (!kda::aligned_n(a->beta, kda::esize(a->in_dtype)))
+    return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
+  return kda::launch_decode(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int kda_prep(const kda_prep_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(a);
+  int rc = kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, KDA_F32);
+  if (rc != KDA_OK) return rc;
+  if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64)
+    return fail(KDA_E_UNSUPPORTED, "chunk=%d not in {16,32,64}", a->chunk);
+  if (a->T == 0) return KDA_OK;
+  REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
+  REQUIRE_PTR(a->g); REQUIRE_PTR(a->q_out); REQUIRE_PTR(a->k_out); REQUIRE_PTR(a->v_out);
+  REQUIRE_PTR(a->G_out);
+  REQUIRE_A16(a->q); REQUIRE_A16(a->k); REQUIRE_A16(a->v); REQUIRE_A16(a->conv_w);
+  REQUIRE_A16(a->g); REQUIRE_A16(a->conv_in); REQUIRE_A16(a->q_out); REQUIRE_A16(a->k_out);
+  REQUIRE_A16(a->v_out); REQUIRE_A16(a->G_out);
+  const long long nchunks = (a->T + a->chunk - 1) / a->chunk;
+  if ((long long)a->B * a->H * nchunks > 0xffffffffLL)
+    return fail(KDA_E_SHAPE, "B*H*chunks too large for one launch");
+  return kda::launch_prep(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// kda_decode.hip -- batched one-token KDA decode step for gfx950.
+//
+// One workgroup per (sequence n, head h).  The step is the recurrence of the
+// KDA definition at T = 1 (pages: "Kimi K3, previewed", section "Kimi Delta
+// Attention - the workhorse"; "Gemma 4 31B vs Kimi K3", component table, rows
+// "Gated DeltaNet / KDA" and "Output gate + sink"):
+//   conv step over the 3-token raw history, SiLU, L2 norms (q also dk^-1/2),
+//   S' = diag(e^g) S,  y = S'^T k,  u = beta (v - y),  S <- S' + k u^T,
+//   o = RMSNorm(S'^T q + (k.q) u) * sigmoid(gate).
+// The state is the only large operand (dk*dv fp32 per head, 64 KiB at 128x128),
+// so the kernel reads it once and writes it once: each thread keeps its rows
+// of S in registers between the read-out reduction and the update, and
+// S'^T k and S'^T q are formed in the same pass.  Loads and stores of S are
+// 16-byte, nontemporal and coalesced along dv.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+struct DecodeParams {
+  int H;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  float* S;
+  void* conv_state;
+  void* o;
+};
+
+constexpr int kDecodeThreads = 256;
+
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) {
+  constexpr int NC = 2 * DK + DV;          // q | k | v channels of one head
+  constexpr int CG = DV / 4;               // float4 column groups of the state
+  constexpr int RG0 = kDecodeThreads / CG;
+  constexpr int RG = RG0 < DK ? RG0 : DK;  // row groups
+  constexpr int RPT = DK / RG;             // state rows per thread
+
+  const int tid = threadIdx.x;
+  const int nh = blockIdx.x;               // n * H + h
+  const int H = p.H;
+  const int n = nh / H;
+  const int h = nh - n * H;
+  const size_t cch = (size_t)H * NC;
+
+  __shared__ float xs[NC];                 // conv + SiLU of q | k | v
+  __shared__ float aq[DK];                 // e^g * q^
+  __shared__ float ak[DK];                 // e^g * k^
+  __shared__ float kn[DK];                 // k^
+  __shared__ float alpha[DK];              // e^g
+  __shared__ float red[2][RG][DV];         // partial S'^T k and S'^T q
+  __shared__ float us[DV];                 // u
+  __shared__ float ocs[DV];                // o_core
+  __shared__ float scal[4];
+
+  // 1. conv step on the raw history + SiLU; shift the history in place.
+  for (int c = tid; c < NC; c += kDecodeThreads) {
+    size_t ch;
+    float x;
+    if (c < DK) {
+      ch = (size_t)h * DK + c;
+      x = load1<IN_BF16>(p.q, (size_t)nh * DK + c);
+    } else if (c < 2 * DK) {
+      ch = (size_t)H * DK + (size_t)h * DK + (c - DK);
+      x = load1<IN_BF16>(p.k, (size_t)nh * DK + (c - DK));
+    } else {
+      ch = (size_t)2 * H * DK + (size_t)h * DV + (c - 2 * DK);
+      x = load1<IN_BF16>(p.v, (size_t)nh * DV + (c - 2 * DK));
+    }
+    const size_t r0 = ((size_t)n * 3 + 0) * cch + ch;
+    const size_t r1 = r0 + cch;
+    const size_t r2 = r1 + cch;
+    const float h0 = load1<IN_BF16>(p.conv_state, r0);
+    const float h1 = load1<IN_BF16>(p.conv_state, r1);
+    const float h2 = load1<IN_BF16>(p.conv_state, r2);
+    const float4 w = *reinterpret_cast<const float4*>(p.conv_w + ch * 4);
+    const float acc = w.x * h0 + w.y * h1 + w.z * h2 + w.w * x;
+    xs[c] = siluf_(acc);
+    // h1, h2 and x are exact in the history dtype (they came from it or from
+    // the input, which has the same dtype), so the shift is lossless.
+    store1<IN_BF16>(p.conv_state, r0, h1);
+    store1<IN_BF16>(p.conv_state, r1, h2);
+    store1<IN_BF16>(p.conv_state, r2, x);
+  }
+  __syncthreads();
+
+  // 2. |q~|^2, |k~|^2 and q~.k~ in wave 0.
+  if (tid < 64) {
+    float sq = 0.f, sk = 0.f, sqk = 0.f;
+    for (int c = tid; c < DK; c += 64) {
+      const float a = xs[c], b = xs[DK + c];
+      sq += a * a;
+      sk += b * b;
+      sqk += a * b;
+    }
+    sq = group_sum<64>(sq);
+    sk = group_sum<64>(sk);
+    sqk = group_sum<64>(sqk);
+    if (tid == 0) {
+      const float rq = fast_rsq(sq + kL2Eps) * fast_rsq((float)DK);
+      const float rk = fast_rsq(sk + kL2Eps);
+      scal[0] = rq;
+      scal[1] = rk;
+      scal[2] = sqk * rq * rk;  // k^ . q^
+    }
+  }
+  __syncthreads();
+  if (tid < DK) {
+    const float a = fast_exp(load1<IN_BF16>(p.g, (size_t)nh * DK + tid));
+    const float kq = xs[DK + tid] * scal[1];
+    alpha[tid] = a;
+    kn[tid] = kq;
+    ak[tid] = a * kq;
+    aq[tid] = a * xs[tid] * scal[0];
+  }
+  __syncthreads();
+
+  // 3. one pass over S: keep this thread's rows, accumulate S'^T k and S'^T q.
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  const bool active = rg < RG;
+  f4* Sp = reinterpret_cast<f4*>(p.S + (size_t)nh * DK * DV);
+  f4 s[RPT];
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      s[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + RG * i) * CG + cg);
+    f4 y = f4{0.f, 0.f, 0.f, 0.f}, z = y;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      y += s[i] * ak[r];
+      z += s[i] * aq[r];
+    }
+    *reinterpret_cast<f4*>(&red[0][rg][4 * cg]) = y;
+    *reinterpret_cast<f4*>(&red[1][rg][4 * cg]) = z;
+  }
+  __syncthreads();
+
+  // 4. u = beta (v - y); o_core = z + (k.q) u; mean square of o_core.
+  if (tid < DV) {
+    float y = 0.f, z = 0.f;
+#pragma unroll
+    for (int r = 0; r < RG; ++r) {
+      y += red[0][r][tid];
+      z += red[1][r][tid];
+    }
+    const float beta = load1<IN_BF16>(p.beta, (size_t)nh);
+    const float u = beta * (xs[2 * DK + tid] - y);
+    us[tid] = u;
+    ocs[tid] = z + scal[2] * u;
+  }
+  __syncthreads();
+  if (tid < 64) {
+    float ss = 0.f;
+    for (int j = tid; j < DV; j += 64) ss += ocs[j] * ocs[j];
+    ss = group_sum<64>(ss);
+    if (tid == 0) scal[3] = fast_rsq(ss * (1.0f / DV) + kRmsEps);
+  }
+  __syncthreads();
+
+  // 5. S <- S' + k u^T, written once.
+  if (active) {
+    const f4 u = *reinterpret_cast<const f4*>(&us[4 * cg]);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      const f4 t = s[i] * alpha[r] + u * kn[r];
+      __builtin_nontemporal_store(t, Sp + (size_t)r * CG + cg);
+    }
+  }
+  if (tid < DV) {
+    const float gt = load1<IN_BF16>(p.gate, (size_t)nh * DV + tid);
+    store1<OUT_BF16>(p.o, (size_t)nh * DV + tid, ocs[tid] * scal[3] * sigmoidf_(gt));
+  }
+}
+
+template <int DK, int DV, bool IB, bool OB>
+int run(const kda_decode_args& a, hipStream_t s) {
+  DecodeParams p{a.H, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o};
+  const unsigned grid = (unsigned)((size_t)a.N * a.H);
+  hipLaunchKernelGGL((decode_kernel<DK, DV, IB, OB>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("decode launch failed: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  return KDA_OK;
+}
+
+template <int DK, int DV>
+int run_dt(const kda_decode_args& a, hipStream_t s) {
+  const bool ib = a.in_dtype == KDA_BF16, ob = a.out_dtype == KDA_BF16;
+  if (ib && ob) return run<DK, DV, true, true>(a, s);
+  if (ib) return run<DK, DV, true, false>(a, s);
+  if (ob) return run<DK, DV, false, true>(a, s);
+  return run<DK, DV, false, false>(a, s);
+}
+
+}  // namespace
+
+int launch_decode(const kda_decode_args& a, hipStream_t s) {
+  if (a.dk != a.dv) {
+    set_error("decode: dk (%d) != dv (%d) is not instantiated", a.dk, a.dv);
+    return KDA_E_UNSUPPORTED;
+  }
+  switch (a.dk) {
+    case 16: return run_dt<16, 16>(a, s);
+    case 32: return run_dt<32, 32>(a, s);
+    case 64: return run_dt<64, 64>(a, s);
+    case 128: return run_dt<128, 128>(a, s);
+    default:
+      set_error("decode: head dim %d not in {16,32,64,128}", a.dk);
+      return KDA_E_UNSUPPORTED;
+  }
+}
+
+}  // namespace kda

@@ -1,0 +1,106 @@
+// kda_device.h -- gfx950 device helpers shared by the KDA kernels.
+//
+// Vector types, bf16/fp16 conversion, fast transcendental wrappers (single
+// hardware instructions: v_exp_f32, v_rcp_f32, v_rsq_f32), wave/block
+// reductions and the 16x16x32 matrix-core wrappers.
+//
+// Matrix-core lane layout (v_mfma_f32_16x16x32_{f16,bf16}, wave of 64 lanes,
+// lane l, group g = l / 16, i = l % 16):
+//   A operand (16 x 32): lane holds A[i][8g .. 8g+7]
+//   B operand (32 x 16): lane holds B[8g .. 8g+7][i]
+//   C/D       (16 x 16): lane holds D[4g .. 4g+3][i]
+// Only the contraction index has to agree between A and B, so a kernel may
+// permute it; the kernels use that to feed an accumulator straight back in as
+// a B operand (see kda_prefill.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kL2Eps = 1e-6f;   // L2 normalisation epsilon of q and k
+constexpr float kRmsEps = 1e-5f;  // head-wise RMSNorm epsilon (model rms_norm_eps)
+
+// ---- scalar math (one hardware instruction each, ~1 ulp) ----------------------
+__device__ __forceinline__ float fast_exp(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+__device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
+__device__ __forceinline__ float sigmoidf_(float x) { return fast_rcp(1.0f + fast_exp(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x * fast_rcp(1.0f + fast_exp(-x)); }
+
+// ---- bf16 / fp16 ---------------------------------------------------------------
+__device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f(uint16_t u) { return __uint_as_float((uint32_t)u << 16); }
+__device__ __forceinline__ uint16_t f_to_bf16(float x) {
+  __bf16 b = (__bf16)x;  // round to nearest even
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Load 8 consecutive activations (fp32 or bf16) as fp32.
+template <bool BF16>
+__device__ __forceinline__ void load8(const void* base, size_t idx, float* out) {
+  if constexpr (BF16) {
+    const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+    out[0] = bf16lo(u.x); out[1] = bf16hi(u.x); out[2] = bf16lo(u.y); out[3] = bf16hi(u.y);
+    out[4] = bf16lo(u.z); out[5] = bf16hi(u.z); out[6] = bf16lo(u.w); out[7] = bf16hi(u.w);
+  } else {
+    const float4 a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    const float4 b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx + 4);
+    out[0] = a.x; out[1] = a.y; out[2] = a.z; out[3] = a.w;
+    out[4] = b.x; out[5] = b.y; out[6] = b.z; out[7] = b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ float load1(const void* base, size_t idx) {
+  if constexpr (BF16) return bf16_to_f(reinterpret_cast<const uint16_t*>(base)[idx]);
+  else return reinterpret_cast<const float*>(base)[idx];
+}
+
+template <bool BF16>
+__device__ __forceinline__ void store1(void* base, size_t idx, float x) {
+  if constexpr (BF16) reinterpret_cast<uint16_t*>(base)[idx] = f_to_bf16(x);
+  else reinterpret_cast<float*>(base)[idx] = x;
+}
+
+// Store 4 consecutive outputs (fp32 or bf16).
+template <bool BF16>
+__device__ __forceinline__ void store4(void* base, size_t idx, float a, float b, float c, float d) {
+  if constexpr (BF16) {
+    uint2 u;
+    u.x = (uint32_t)f_to_bf16(a) | ((uint32_t)f_to_bf16(b) << 16);
+    u.y = (uint32_t)f_to_bf16(c) | ((uint32_t)f_to_bf16(d) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = u;
+  } else {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(a, b, c, d);
+  }
+}
+
+// ---- reductions ------------------------------------------------------------------
+// Sum over groups of W consecutive lanes (W a power of two <= 64); every lane of
+// the group gets the sum.
+template <int W>
+__device__ __forceinline__ float group_sum(float x) {
+#pragma unroll
+  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  return x;
+}
+
+// ---- matrix core -----------------------------------------------------------------
+__device__ __forceinline__ f4 mma_f16(const half8& a, const half8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+}
+__device__ __forceinline__ f4 mma_bf16(const bf16x8& a, const bf16x8& b, const f4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+}  // namespace kda

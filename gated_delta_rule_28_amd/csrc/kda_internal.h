@@ -1,0 +1,19 @@
+// kda_internal.h -- launcher interface between the C ABI (kda_api.cpp) and the
+// kernels.  Launchers assume validated arguments; they return KDA_OK or
+// KDA_E_UNSUPPORTED (no instantiation for the sizes) or KDA_E_HIP.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include "../../include/kda.h"
+
+namespace kda {
+
+int launch_decode(const kda_decode_args& a, hipStream_t s);
+int launch_prefill(const kda_prefill_args& a, hipStream_t s);
+int launch_prep(const kda_prep_args& a, hipStream_t s);
+
+// Set the calling thread's last-error text (printf-style).
+void set_error(const char* fmt, ...);
+
+}  // namespace kda

@@ -1,0 +1,166 @@
+/*
+ * kda.h -- C ABI of the MI355X (gfx950) Kimi Delta Attention library, libkda.so.
+ *
+ * KDA is the gated delta-rule linear attention of Kimi K3 ("Kimi K3,
+ * previewed", section "Kimi Delta Attention - the workhorse"; component tables
+ * of "Kimi K3.1 Pro vs gpt-oss-120b" and "Gemma 4 31B vs Kimi K3", row
+ * "Gated DeltaNet / KDA"; output gate from "Gemma 4 31B vs Kimi K3", row
+ * "Output gate + sink").  Per (batch b, head h), per token t:
+ *
+ *   x~ = SiLU(causal depthwise conv, kernel 4, of the raw q, k, v channels)
+ *   q  = q~ (|q~|^2 + 1e-6)^-1/2 dk^-1/2 ;  k = k~ (|k~|^2 + 1e-6)^-1/2 ;  v = v~
+ *   S_t = (I - beta_t k k^T) Diag(exp g_t) S_{t-1} + beta_t k v^T     (S: dk x dv)
+ *   o_t = RMSNorm(S_t^T q) * sigmoid(gate_t),  RMSNorm(x) = x / sqrt(mean(x^2) + 1e-5)
+ *
+ * Layouts (all row-major, contiguous, no padding):
+ *   q, k, g      [B, T, H, dk]        v, gate, o  [B, T, H, dv]      beta [B, T, H]
+ *   S0, S_T      [B, H, dk, dv] fp32  (row index = key channel)
+ *   conv_w       [H*(2dk+dv), 4] fp32, tap 3 multiplies the current token
+ *   conv_in/out  [B, 3, H*(2dk+dv)]   raw (pre-conv) tokens, row 0 the oldest
+ *   Conv channel order: q channels (head-major), then k, then v:
+ *     q ch c of head h -> h*dk + c;  k -> H*dk + h*dk + c;  v -> 2*H*dk + h*dv + c
+ *
+ * Dtypes: activations (q, k, v, g, beta, gate, conv history) are all KDA_F32 or
+ * all KDA_BF16 (in_dtype); o is KDA_F32 or KDA_BF16 (out_dtype); state and
+ * conv_w are always fp32.
+ *
+ * Ownership: the caller owns every buffer (device memory).  The library keeps
+ * no device allocations and no global device state; inputs are never written.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream);
+ * execution faults surface at the caller's next synchronisation.  A call that
+ * fails validation returns a negative code and launches nothing.  The library
+ * is reentrant; kda_last_error() is per calling thread.
+ *
+ * Preconditions not checked (for cost): g <= 0; 0 <= beta <= 1; inputs
+ * finite; |v~| and the state below 6e4 (fp16 operand range).
+ * Precision: the prefill's matrix-core operands are fp16 with fp32
+ * accumulation and an fp32 state.  Decay factors inside a 16-token tile are
+ * formed relative to a per-tile reference; when a tile's summed log-decay in
+ * some channel is below -8 the chunk's decay-weighted products switch to bf16
+ * operands (finite for any tile with g >= -5 per token, as K3's bounded decay
+ * g = -5 sigmoid(.) guarantees), at bf16 precision for those products.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KDA_ABI_VERSION 1
+
+/* element types */
+enum { KDA_F32 = 0, KDA_BF16 = 1 };
+
+/* status codes */
+enum {
+  KDA_OK = 0,
+  KDA_E_NULL = -1,        /* a required pointer is NULL                          */
+  KDA_E_SHAPE = -2,       /* a size is out of range (negative, zero, too large)  */
+  KDA_E_DTYPE = -3,       /* in_dtype / out_dtype not one of the enum values     */
+  KDA_E_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
+  KDA_E_UNSUPPORTED = -5, /* dk, dv not in {16,32,64,128}, or chunk not in {16,32,64} */
+  KDA_E_WORKSPACE = -6,   /* workspace smaller than kda_prefill_workspace_bytes  */
+  KDA_E_HIP = -7          /* a HIP runtime call failed (text in kda_last_error)  */
+};
+
+/*
+ * Chunkwise prefill (the definition above over t = 0..T-1 for every (b, h)).
+ * Starts from S0 (NULL = zeros) and the raw conv history conv_in (NULL =
+ * zeros); writes o for every token, the final state S_T and the last three raw
+ * tokens conv_out (taken from conv_in where T < 3).  S_T may alias S0 and
+ * conv_out may alias conv_in, so a long sequence can be processed as
+ * consecutive segments carrying both in place.  T = 0 is allowed (copies the
+ * carry).  T need not be a multiple of `chunk`.
+ */
+typedef struct kda_prefill_args {
+  int B, T, H, dk, dv;
+  int chunk;              /* tokens per chunk: 16, 32 or 64 */
+  int in_dtype;           /* KDA_F32 or KDA_BF16 */
+  int out_dtype;          /* KDA_F32 or KDA_BF16 */
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  const float* S0;        /* may be NULL */
+  const void* conv_in;    /* may be NULL */
+  void* o;
+  float* S_T;             /* may be NULL */
+  void* conv_out;         /* may be NULL */
+  void* workspace;        /* may be NULL when the workspace size is 0 */
+  size_t workspace_bytes;
+} kda_prefill_args;
+
+int kda_prefill(const kda_prefill_args* args, void* stream);
+
+/* Device scratch kda_prefill needs for these sizes (0 when none). */
+size_t kda_prefill_workspace_bytes(const kda_prefill_args* args);
+
+/*
+ * One decode step for N sequences of one new token each: the definition above
+ * with T = 1, updating the state S [N,H,dk,dv] (fp32) and the raw conv history
+ * conv_state [N,3,Cch] (in_dtype) in place, and writing o [N,H,dv].
+ * Inputs q, k, g [N,H,dk]; v, gate [N,H,dv]; beta [N,H].
+ */
+typedef struct kda_decode_args {
+  int N, H, dk, dv;
+  int in_dtype;
+  int out_dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  float* S;               /* in/out */
+  void* conv_state;       /* in/out */
+  void* o;
+} kda_decode_args;
+
+int kda_decode_step(const kda_decode_args* args, void* stream);
+
+/*
+ * The first stage of the prefill on its own: conv + SiLU + L2 normalisation
+ * (q scaled by dk^-1/2) and the chunk-local inclusive cumulative sum of g.
+ * Writes fp32 q^, k^ [B,T,H,dk], v^ [B,T,H,dv] and G [B,T,H,dk], where
+ * G restarts at every multiple of `chunk`.  Same inputs and validation as
+ * kda_prefill (o, S0, S_T, conv_out, gate, beta unused and may be NULL).
+ */
+typedef struct kda_prep_args {
+  int B, T, H, dk, dv;
+  int chunk;
+  int in_dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* conv_in;    /* may be NULL */
+  float* q_out;
+  float* k_out;
+  float* v_out;
+  float* G_out;
+} kda_prep_args;
+
+int kda_prep(const kda_prep_args* args, void* stream);
+
+/* Static text of a status code. */
+const char* kda_status_string(int code);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+/* KDA_ABI_VERSION of the loaded library. */
+int kda_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

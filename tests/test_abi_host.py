@@ -1,0 +1,147 @@
+"""Host-side checks of the C ABI (no GPU needed, nothing is launched).
+
+* libkda.so loads and exports every function include/kda.h declares;
+* the ctypes structures of the binding match the C layout (offsets computed
+  by gcc from the header itself);
+* argument validation returns the documented codes before any HIP call.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kda.h")
+
+
+@pytest.fixture(scope="module")
+def kda():
+    import gated_delta_rule_28_amd as kda
+    if not os.path.exists(kda.library_path):
+        pytest.skip("libkda.so not built")
+    kda.lib()
+    return kda
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kda_\w+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_the_abi():
+    names = declared_functions()
+    for must in ("kda_prefill", "kda_decode_step", "kda_prefill_workspace_bytes", "kda_prep",
+                 "kda_status_string", "kda_last_error", "kda_abi_version"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(kda):
+    L = kda.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", kda.library_path], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r" T (kda_\w+)", out))
+    assert set(declared_functions()) <= exported
+
+
+def _c_offsets(struct, fields):
+    """offsetof/sizeof of a kda.h struct, computed by gcc from the header."""
+    src = "#include <stdio.h>\n#include <stddef.h>\n#include \"kda.h\"\nint main(void){\n"
+    src += f'printf("%zu\\n", sizeof({struct}));\n'
+    for f in fields:
+        src += f'printf("%zu\\n", offsetof({struct}, {f}));\n'
+    src += "return 0;}\n"
+    d = os.path.join(ROOT, "_build_abi_check")
+    os.makedirs(d, exist_ok=True)
+    c = os.path.join(d, f"{struct}.c")
+    exe = os.path.join(d, struct)
+    open(c, "w").write(src)
+    subprocess.run(["gcc", "-I", os.path.join(ROOT, "include"), c, "-o", exe], check=True)
+    vals = [int(x) for x in subprocess.run([exe], capture_output=True, text=True, check=True).stdout.split()]
+    return vals[0], vals[1:]
+
+
+@pytest.mark.parametrize("name", ["PrefillArgs", "DecodeArgs", "PrepArgs"])
+def test_ctypes_layout_matches_header(name):
+    import gated_delta_rule_28_amd as kda
+    cls = getattr(kda, name)
+    struct = {"PrefillArgs": "kda_prefill_args", "DecodeArgs": "kda_decode_args",
+              "PrepArgs": "kda_prep_args"}[name]
+    fields = [f for f, _ in cls._fields_]
+    size, offs = _c_offsets(struct, fields)
+    assert ctypes.sizeof(cls) == size
+    assert [getattr(cls, f).offset for f in fields] == offs
+
+
+def _prefill_args(kda, **over):
+    # fake, 16-byte aligned addresses: validation must reject before touching them
+    base = dict(B=1, T=8, H=2, dk=16, dv=16, chunk=16, in_dtype=kda.KDA_BF16, out_dtype=kda.KDA_F32,
+                q=0x1000, k=0x2000, v=0x3000, conv_w=0x4000, g=0x5000, beta=0x6000, gate=0x7000,
+                S0=None, conv_in=None, o=0x8000, S_T=None, conv_out=None, workspace=None,
+                workspace_bytes=0)
+    base.update(over)
+    return kda.PrefillArgs(**base)
+
+
+CASES = [
+    (dict(q=None), -1), (dict(o=None), -1), (dict(gate=None), -1),
+    (dict(B=0), -2), (dict(H=0), -2), (dict(T=-1), -2),
+    (dict(in_dtype=7), -3), (dict(out_dtype=-1), -3),
+    (dict(k=0x2008), -4), (dict(o=0x8004), -4), (dict(S0=0x9002), -4), (dict(beta=0x6001), -4),
+    (dict(dk=48, dv=48), -5), (dict(dk=16, dv=32), -5), (dict(dk=256, dv=256), -5),
+    (dict(chunk=48), -5), (dict(chunk=128), -5),
+]
+
+
+@pytest.mark.parametrize("over,code", CASES)
+def test_prefill_validation_codes(kda, over, code):
+    a = _prefill_args(kda, **over)
+    L = kda.lib()
+    assert L.kda_prefill(ctypes.byref(a), None) == code
+    assert L.kda_last_error().decode() != ""
+    assert L.kda_status_string(code).decode() not in ("", "unknown status code")
+
+
+def test_prefill_null_args_and_empty(kda):
+    L = kda.lib()
+    assert L.kda_prefill(None, None) == -1
+    # T = 0 with nothing to carry: nothing to do, succeeds without a launch
+    a = _prefill_args(kda, T=0, q=None, k=None, v=None, o=None)
+    assert L.kda_prefill(ctypes.byref(a), None) == 0
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(a)) == 0
+
+
+def test_decode_validation_codes(kda):
+    L = kda.lib()
+    base = dict(N=2, H=2, dk=16, dv=16, in_dtype=kda.KDA_BF16, out_dtype=kda.KDA_F32, q=0x1000,
+                k=0x2000, v=0x3000, conv_w=0x4000, g=0x5000, beta=0x6000, gate=0x7000, S=0x8000,
+                conv_state=0x9000, o=0xa000)
+    for over, code in [(dict(S=None), -1), (dict(conv_state=None), -1), (dict(N=0), -2),
+                       (dict(in_dtype=3), -3), (dict(S=0x8008), -4), (dict(dk=24, dv=24), -5)]:
+        a = kda.DecodeArgs(**{**base, **over})
+        assert L.kda_decode_step(ctypes.byref(a), None) == code, over
+    assert L.kda_decode_step(None, None) == -1
+
+
+def test_prep_validation_codes(kda):
+    L = kda.lib()
+    base = dict(B=1, T=8, H=2, dk=16, dv=16, chunk=16, in_dtype=kda.KDA_F32, q=0x1000, k=0x2000,
+                v=0x3000, conv_w=0x4000, g=0x5000, conv_in=None, q_out=0x6000, k_out=0x7000,
+                v_out=0x8000, G_out=0x9000)
+    for over, code in [(dict(G_out=None), -1), (dict(T=-2), -2), (dict(in_dtype=9), -3),
+                       (dict(q_out=0x6004), -4), (dict(chunk=8), -5)]:
+        a = kda.PrepArgs(**{**base, **over})
+        assert L.kda_prep(ctypes.byref(a), None) == code, over
+
+
+def test_status_strings(kda):
+    L = kda.lib()
+    assert L.kda_status_string(0).decode() == "ok"
+    assert L.kda_status_string(12345).decode() == "unknown status code"
+    assert L.kda_abi_version() == 1
