@@ -1,0 +1,282 @@
+"""KDA benchmark on one MI355X.
+
+Headline: prefill tokens/s on the K3-width workload (B1 T65536 H96 d128, bf16
+inputs, fp32 state and output, chunk 64), one step = one kda_prefill over the
+whole input.  Beside it: the batched decode step (256 sequences x 96 heads,
+1000 consecutive steps) as HBM GB/s, the roofline of each kernel from
+HIP-event timing of its launches, and the fp64 CPU oracle timed on a bounded
+sample of the same prefill workload.
+
+Prints one JSON line.  Options:
+  --gpus N        only 1 is supported (the path runs on one GPU)
+  --steps K       timed prefill steps (default 20)
+  --warmup W      untimed prefill steps first (default 3)
+  --workload      k3width (default) | prefill | long1m (16 x 65536 segments, carry in place)
+  --decode-steps  decode steps timed back to back (default 1000; 0 skips decode)
+  --no-cpu        skip the oracle leg
+  --calibrate     also run a plain 1 GiB device copy (for HBM counter scaling)
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_MFMA_PEAK_TFS = 2500.0  # dense bf16/fp16 matrix-core peak, TFLOP/s
+METRIC = "KDA prefill tokens/s at H=96,d=128 (% MFMA peak); decode-step HBM GB/s"
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def prefill_bytes_per_launch(B, T, H, dk, dv, in_bytes=2, out_bytes=4):
+    """Compulsory HBM bytes of one prefill: q k v g gate in, beta in, o out, plus
+    S0 read and S_T write and the conv history in/out per (b, h)."""
+    per_token_head = in_bytes * (2 * dk + dv + dk + dv) + in_bytes + out_bytes * dv
+    per_head = 4 * dk * dv * 2 + in_bytes * 3 * (2 * dk + dv) * 2
+    return B * T * H * per_token_head + B * H * per_head
+
+
+def prefill_flops(B, T, H, dk, dv, C=64):
+    """Algorithmic FLOPs of the chunkwise form (exact triangular counts)."""
+    n_full, tail = divmod(T, C)
+    def chunk(c):
+        tri_strict = c * (c - 1) // 2
+        tri_incl = c * (c + 1) // 2
+        mac = (tri_strict * dk          # A
+               + tri_incl * dk          # P
+               + tri_incl * dk          # W = T diag(beta) K
+               + tri_incl * dv          # U~ = T diag(beta) V
+               + c * dk * dv * 3        # W S, Q S, K^T U
+               + tri_incl * dv)         # P U
+        return 2 * mac
+    return B * H * (n_full * chunk(C) + (chunk(tail) if tail else 0))
+
+
+def decode_bytes_per_step(N, H, dk, dv, in_bytes=2, out_bytes=4):
+    per = (4 * dk * dv * 2                       # state read + write
+           + in_bytes * (2 * dk + dv + dk + dv)  # q k v g gate
+           + in_bytes                            # beta
+           + out_bytes * dv                      # o
+           + 2 * 3 * (2 * dk + dv) * in_bytes)   # conv history read + write
+    conv_w = H * (2 * dk + dv) * 4 * 4
+    return N * H * per + conv_w
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def load_traffic(kernel_key, src):
+    """HBM traffic measured with rocprofv3 counters, if taken on this kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        d = json.load(open(p)).get(kernel_key)
+    except (OSError, ValueError):
+        return None
+    if not d or d.get("source_sha256_16") != source_hash(src):
+        return None
+    return d.get("bytes_per_launch")
+
+
+def timed_launches(torch, fn, n):
+    """Run fn n times, one event pair per launch on the current stream; returns ms list."""
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in evs:
+        a.record()
+        fn()
+        b.record()
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in evs]
+
+
+def cpu_baseline(w, dev_inp, seconds_target=15.0):
+    """The oracle on a bounded sample: the first n heads over the first Ts tokens."""
+    import numpy as np
+    import kda_synth as syn
+    import oracle
+    nthr = oracle.max_threads()
+    nheads = min(w.H, 2 * max(1, nthr))
+    Ts = min(w.T, 65536)
+    dk, dv, H = w.dk, w.dv, w.H
+    sl = {x: dev_inp[x][:, :Ts, :nheads].contiguous() for x in ("q", "k", "v", "g", "gate")}
+    sl["beta"] = dev_inp["beta"][:, :Ts, :nheads].contiguous()
+    cw = dev_inp["conv_w"]
+    chans = list(range(0, nheads * dk)) + list(range(H * dk, H * dk + nheads * dk)) + \
+        list(range(2 * H * dk, 2 * H * dk + nheads * dv))
+    sl["conv_w"] = cw[chans].contiguous()
+    host = {x: syn.torch_to_np(t) for x, t in sl.items()}
+    if dev_inp.get("S0") is not None:
+        host["S0"] = syn.torch_to_np(dev_inp["S0"][:, :nheads].contiguous())
+    t0 = time.perf_counter()
+    oracle.prefill(host)
+    el = time.perf_counter() - t0
+    head_tokens = w.B * Ts * nheads
+    tok_s = head_tokens / el / H  # whole-token (all H heads) rate
+    return {"value": tok_s, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+            "sample": f"fp64 C oracle, first {nheads} of {H} heads x first {Ts} tokens "
+                      f"({head_tokens} head-tokens, {el:.1f} s); tokens/s = head-tokens/s / {H}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="k3width", choices=["k3width", "prefill", "long1m"])
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--calibrate", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures the single-GPU path only; run it with --gpus 1 "
+              "(multi-GPU sharding is a design note, not built)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_delta_rule_28_amd as kda
+    import kda_synth as syn
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    kda.lib()
+    dev = "cuda"
+    w = syn.WORKLOADS[args.workload]
+    seg = w.T // w.segments
+    log(f"[bench] workload {w.name}: B{w.B} T{w.T} H{w.H} d{w.dk} C{w.chunk} ({w.segments} segment(s))")
+
+    t0 = time.perf_counter()
+    inp = syn.prefill_inputs_torch(w, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated on device in {time.perf_counter() - t0:.1f} s")
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device=dev)
+    S = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    conv = torch.zeros((w.B, 3, w.cch), dtype=torch.bfloat16, device=dev)
+    S0 = inp["S0"]
+
+    def step():
+        if w.segments == 1:
+            kda.prefill(inp["q"], inp["k"], inp["v"], inp["conv_w"], inp["g"], inp["beta"], inp["gate"],
+                        S0=S0, conv_in=None, chunk=w.chunk, o=o, S_T=S, conv_out=conv)
+            return
+        S.zero_()
+        conv.zero_()
+        for s in range(w.segments):
+            t0_, t1_ = s * seg, (s + 1) * seg
+            kda.prefill(inp["q"][:, t0_:t1_], inp["k"][:, t0_:t1_], inp["v"][:, t0_:t1_], inp["conv_w"],
+                        inp["g"][:, t0_:t1_], inp["beta"][:, t0_:t1_], inp["gate"][:, t0_:t1_],
+                        S0=S, conv_in=conv, chunk=w.chunk, o=o[:, t0_:t1_], S_T=S, conv_out=conv)
+
+    if w.segments > 1:
+        # segment views must be contiguous for the ABI: [B=1, seg, H, d] slices are
+        assert w.B == 1
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if torch.distributed.is_available() and torch.distributed.is_initialized():
+        torch.distributed.barrier()
+    per = timed_launches(torch, step, args.steps)
+    torch.cuda.synchronize()
+    ms = sum(per) / len(per)
+    tokens = w.B * w.T
+    value = tokens / (ms * 1e-3)
+    launch_ms = ms / w.segments
+    nbytes = prefill_bytes_per_launch(w.B, seg, w.H, w.dk, w.dv)
+    flops = prefill_flops(w.B, seg, w.H, w.dk, w.dv, w.chunk)
+    achieved = nbytes / (launch_ms * 1e-3) / 1e9
+    src = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc", "kda_prefill.hip")
+    traffic = load_traffic("prefill_kernel", src)
+    log(f"[bench] prefill {ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic")
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic (seeded device draws; q,k,v,gate ~ N(0,1), g = -softplus(N(-3,1)), beta = sigmoid(N(0,1)))",
+        "config": {"workload": f"{w.name}: KDA prefill B{w.B} T{w.T} H{w.H} dk=dv={w.dk} chunk {w.chunk}"
+                               + (f", {w.segments} segments of {seg} with state carried" if w.segments > 1 else ""),
+                   "inputs": "bf16", "state": "f32", "output": "f32",
+                   "matrix_core_operands": "f16 with f32 accumulation"},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "prefill_kernel<64,128,128,bf16 in,f32 out>",
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms},
+        "mfma": {"algorithmic_flops_per_launch": flops,
+                 "tflops": flops / (launch_ms * 1e-3) / 1e12,
+                 "frac_of_bf16_f16_peak": flops / (launch_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
+    }
+    del o
+
+    if args.decode_steps > 0:
+        wd = syn.WORKLOADS["decode"]
+        nsteps = args.decode_steps
+        t0 = time.perf_counter()
+        d = syn.decode_inputs_torch(wd, dev, nsteps)
+        od = torch.empty((wd.B, wd.H, wd.dv), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        log(f"[bench] decode inputs ({nsteps} steps) generated in {time.perf_counter() - t0:.1f} s")
+
+        def dstep(s):
+            kda.decode_step(d["q"][s], d["k"][s], d["v"][s], d["conv_w"], d["g"][s], d["beta"][s],
+                            d["gate"][s], d["S"], d["conv_state"], o=od)
+
+        for s in range(min(20, nsteps)):
+            dstep(s)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for s in range(nsteps):
+            dstep(s)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1) / nsteps
+        dbytes = decode_bytes_per_step(wd.B, wd.H, wd.dk, wd.dv)
+        gbs = dbytes / (dms * 1e-3) / 1e9
+        dsrc = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc", "kda_decode.hip")
+        out["decode"] = {"metric": "decode-step HBM GB/s", "value": gbs, "unit": "GB/s",
+                         "ms_per_step": dms, "steps_timed": nsteps,
+                         "config": f"decode N{wd.B} H{wd.H} dk=dv={wd.dk}, bf16 inputs, f32 state",
+                         "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                                      "frac": gbs / HBM_PEAK_GBS,
+                                      "traffic": load_traffic("decode_kernel", dsrc),
+                                      "algorithmic_bytes_per_launch": dbytes}}
+        log(f"[bench] decode {dms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
+        del d
+
+    if args.calibrate:
+        n = 1 << 28  # 1 GiB of fp32 copied
+        a = torch.empty(n, dtype=torch.float32, device=dev).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        out["calibration_copy_bytes"] = 2 * 4 * n
+
+    if not args.no_cpu:
+        log("[bench] timing the oracle on a bounded sample ...")
+        out["cpu_baseline"] = cpu_baseline(w, inp)
+        log(f"[bench] oracle {out['cpu_baseline']['value']:.1f} tokens/s on {out['cpu_baseline']['cores']} threads")
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

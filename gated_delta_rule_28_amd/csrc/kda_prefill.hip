@@ -88,6 +88,75 @@ template <> struct Frag<true> { float v[8]; };
 template <bool F32>
 using OpT = typename std::conditional<F32, float, uint16_t>::type;
 
+// A value the compiler must treat as unknown at this point: per-lane indices
+// derived from it inside a loop are recomputed each iteration instead of being
+// hoisted out of the loop and kept live (or spilled) across it.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Workgroup barrier that waits only for this wave's LDS operations, not for its
+// outstanding global loads (which __syncthreads' release fence would drain):
+// loads issued for later stages stay in flight across it.  The memory clobber
+// keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// 8 consecutive activations kept packed in registers until used.
+template <bool BF16> struct Raw8;
+template <> struct Raw8<true> { uint4 u; };
+template <> struct Raw8<false> { float4 a, b; };
+
+template <bool BF16>
+__device__ __forceinline__ void raw_load(Raw8<BF16>& r, const void* base, size_t idx) {
+  if constexpr (BF16) r.u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(base) + idx);
+  else {
+    r.a = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx);
+    r.b = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + idx + 4);
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ void raw_zero(Raw8<BF16>& r) {
+  if constexpr (BF16) r.u = make_uint4(0, 0, 0, 0);
+  else { r.a = make_float4(0.f, 0.f, 0.f, 0.f); r.b = r.a; }
+}
+// Unpack, giving zeros when `ok` is false (the mask is applied at use so that
+// the load it guards never has to be waited for early).
+template <bool BF16>
+__device__ __forceinline__ void raw_unpack_if(const Raw8<BF16>& r, bool ok, float* o);
+
+template <bool BF16>
+__device__ __forceinline__ void raw_unpack(const Raw8<BF16>& r, float* o) {
+  if constexpr (BF16) {
+    o[0] = bf16lo(r.u.x); o[1] = bf16hi(r.u.x); o[2] = bf16lo(r.u.y); o[3] = bf16hi(r.u.y);
+    o[4] = bf16lo(r.u.z); o[5] = bf16hi(r.u.z); o[6] = bf16lo(r.u.w); o[7] = bf16hi(r.u.w);
+  } else {
+    o[0] = r.a.x; o[1] = r.a.y; o[2] = r.a.z; o[3] = r.a.w;
+    o[4] = r.b.x; o[5] = r.b.y; o[6] = r.b.z; o[7] = r.b.w;
+  }
+}
+
+// Element e (0..7, a compile-time constant after unrolling) of a packed Raw8.
+template <bool BF16>
+__device__ __forceinline__ float raw_elem(const Raw8<BF16>& r, int e) {
+  if constexpr (BF16) {
+    const uint32_t w = e < 2 ? r.u.x : e < 4 ? r.u.y : e < 6 ? r.u.z : r.u.w;
+    return (e & 1) ? bf16hi(w) : bf16lo(w);
+  } else {
+    return e == 0 ? r.a.x : e == 1 ? r.a.y : e == 2 ? r.a.z : e == 3 ? r.a.w
+         : e == 4 ? r.b.x : e == 5 ? r.b.y : e == 6 ? r.b.z : r.b.w;
+  }
+}
+
+template <bool BF16>
+__device__ __forceinline__ void raw_unpack_if(const Raw8<BF16>& r, bool ok, float* o) {
+  raw_unpack<BF16>(r, o);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) o[e] = ok ? o[e] : 0.f;
+}
+
 __device__ __forceinline__ uint16_t to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
@@ -188,186 +257,230 @@ __device__ __forceinline__ void st_op8(OpT<F32>* p, const float* x, bool bf) {
   }
 }
 
+// Scale the 8 elements of a fragment by f[0..7] (fp32, 16-byte aligned),
+// rounding back to the operand type.
+template <bool F32>
+__device__ __forceinline__ void frag_scale(Frag<F32>& fr, const float* f, bool bf) {
+  const float4 a = *reinterpret_cast<const float4*>(f);
+  const float4 c = *reinterpret_cast<const float4*>(f + 4);
+  const float s[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
+  if constexpr (F32) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fr.v[e] *= s[e];
+  } else if (bf) {
+    bf16x8 v = __builtin_bit_cast(bf16x8, fr.v);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * s[e]);
+    fr.v = __builtin_bit_cast(half8, v);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) fr.v[e] = (_Float16)((float)fr.v[e] * s[e]);
+  }
+}
+
 // ---------------------------------------------------------------------------
-// LDS layout of the fused kernel (byte offsets)
+// LDS layout of the fused kernel (byte offsets).  Operand rows are padded by
+// 16 bytes so 16 lanes reading 16 consecutive rows hit distinct banks; arrays
+// stored transposed ([channel][token]) also XOR-swizzle their 16-byte granules
+// by (row / 16) so the per-token transposed stores spread over banks.
 // ---------------------------------------------------------------------------
 template <int C, int DK, int DV, bool F32>
 struct Smem {
   static constexpr int E = F32 ? 4 : 2;              // operand element bytes
+  static constexpr int PAD = 16 / E;                 // 16 bytes of padding, in elements
   static constexpr int NT = C / 16;                  // 16-token tiles per chunk
-  static constexpr int NKV = NT * (NT + 1) / 2;      // lower tile pairs
+  static constexpr int NOFF = NT * (NT - 1) / 2;     // strictly-lower tile pairs
+  static constexpr int LDR = DK + PAD;               // rows of dk-wide operands
+  static constexpr int LDC = C + PAD;                // rows of chunk-wide operands
+  static constexpr int LDT = C + PAD;                // rows of transposed operands
+  static constexpr int LDA = C + 4;                  // fp32 A and T
   // region X, phase 1: decay-weighted A/P operands
-  static constexpr int QR = 0;                              // [C][DK]
-  static constexpr int KR = QR + C * DK * E;                // [C][DK]
-  static constexpr int KC = KR + C * DK * E;                // [16*NKV][DK]
-  static constexpr int X1 = KC + 16 * NKV * DK * E;
+  static constexpr int QR = 0;                              // [C][LDR]  q^ e^{G - rho_tile}
+  static constexpr int KR = QR + C * LDR * E;               // [C][LDR]  k^ e^{G - rho_tile}
+  static constexpr int KC = KR + C * LDR * E;               // [C][LDR]  k^ e^{rho_tile - G}
+  static constexpr int X1 = KC + C * LDR * E;
   // region X, phase 2 (after the A/P products)
-  static constexpr int AS = 0;                              // [C][C] fp32
-  static constexpr int TS = AS + C * C * 4;                 // [C][C] fp32
-  static constexpr int TB = TS + C * C * 4;                 // [C][C] op
-  static constexpr int PS = TB + C * C * E;                 // [C][C] op
-  static constexpr int WS = PS + C * C * E;                 // [C][DK] op
-  static constexpr int X2 = WS + C * DK * E;
+  static constexpr int AS = 0;                              // [C][LDA] fp32
+  static constexpr int TS = AS + C * LDA * 4;               // [C][LDA] fp32
+  static constexpr int TB = TS + C * LDA * 4;               // [C][LDC] T diag(beta)
+  static constexpr int PS = TB + C * LDC * E;               // [C][LDC] P
+  static constexpr int X2 = PS + C * LDC * E;
   static constexpr int XE = X1 > X2 ? X1 : X2;
   // region Y: operands of the W / U~ / inter-chunk products
-  static constexpr int QG = (XE + 15) / 16 * 16;            // [C][DK]  q^ e^G
-  static constexpr int KGT = QG + C * DK * E;               // [DK][C]  (k^ e^G)^T
-  static constexpr int KBT = KGT + DK * C * E;              // [DK][C]  (k^ e^{G_C-G})^T
-  static constexpr int VT = KBT + DK * C * E;               // [DV][C]  v^T
+  static constexpr int QG = (XE + 15) / 16 * 16;            // [C][LDR]   q^ e^G
+  static constexpr int KGT = QG + C * LDR * E;              // [DK][LDT]  (k^ e^G)^T, later W [C][LDR]
+  static constexpr int KGT_BYTES = (DK * LDT > C * LDR ? DK * LDT : C * LDR) * E;
+  static constexpr int KBT = KGT + KGT_BYTES;               // [DK][LDT]  (k^ e^{G_C-G})^T
+  static constexpr int VT = KBT + DK * LDT * E;             // [DV][LDT]  v^T
   // small fp32 arrays
-  static constexpr int BETA = VT + DV * C * E;              // [C]
+  static constexpr int BETA = VT + DV * LDT * E;            // [C]
   static constexpr int GAM = BETA + C * 4;                  // [DK]  e^{G_C}
   static constexpr int GC = GAM + DK * 4;                   // [DK]  G_C
-  static constexpr int RHO = GC + DK * 4;                   // [NT][DK]
-  static constexpr int ERHO = RHO + NT * DK * 4;            // [NT][DK] e^{rho}
-  static constexpr int BTOT = ERHO + NT * DK * 4;           // [8][DK] token-block sums of g
-  static constexpr int SSQ = BTOT + 8 * DK * 4;             // [8 waves][C]
-  static constexpr int FLAG = SSQ + kWaves * C * 4;         // [4] ints
+  static constexpr int RHO = GC + DK * 4;                   // [NT][DK]  rho_a
+  static constexpr int ERHO = RHO + NT * DK * 4;            // [NT][DK]  e^{rho_a}
+  static constexpr int FAB = ERHO + NT * DK * 4;            // [NOFF][DK] e^{rho_a - rho_b}, b < a
+  static constexpr int BTOT = FAB + (NOFF > 0 ? NOFF : 1) * DK * 4;  // [8][DK] token-block sums of g
+  static constexpr int SSQ = BTOT;                          // [8 waves][C] (reuses BTOT's space)
+  static constexpr int BTOT_BYTES = (8 * DK > kWaves * C ? 8 * DK : kWaves * C) * 4;
+  static constexpr int CW = BTOT + BTOT_BYTES;              // [2dk+dv][4] conv taps of the head
+  static constexpr int FLAG = CW + (2 * DK + DV) * 16;      // [4] ints
   static constexpr int BYTES = FLAG + 16;
 };
 
-template <int C, int DK, int DV>
-struct SmemPrep {  // standalone prep kernel
-  static constexpr int BTOT = 0;
-  static constexpr int BYTES = 8 * DK * 4;
-};
+// index of the pair (a, b), b < a, among the strictly-lower tile pairs
+__device__ __forceinline__ int off_pair(int a, int b) { return a * (a - 1) / 2 + b; }
+
+// element (row, k) of a transposed operand array with LDT columns and
+// 8-element granules swizzled by row / 16
+template <int C, int LDT>
+__device__ __forceinline__ int tidx(int row, int k) {
+  constexpr int NG = C / 8;
+  return row * LDT + ((((k >> 3) ^ (row >> 4)) & (NG - 1)) << 3) + (k & 7);
+}
+
+// Fragment of 8 consecutive tokens k0..k0+7 (k0 % 8 == 0) of row `row` of a
+// transposed operand array.
+template <bool F32, int C, int LDT>
+__device__ __forceinline__ void frag_std_t(Frag<F32>& f, const OpT<F32>* buf, int row, int k0, bool valid) {
+  if (!valid) { frag_zero(f); return; }
+  frag_std<F32>(f, buf + tidx<C, LDT>(row, k0), 0, 0, 0, true);
+}
+
+// Permuted-order fragment (tokens kb + 4g + 0..3 and kb + 16 + 4g + 0..3) of a
+// transposed operand array.
+template <bool F32, int C, int LDT>
+__device__ __forceinline__ void frag_perm_t(Frag<F32>& f, const OpT<F32>* buf, int row, int kb, int g,
+                                            bool hi_valid) {
+  const OpT<F32>* p1 = buf + tidx<C, LDT>(row, kb + 4 * g);
+  if constexpr (F32) {
+    const float4 a = *reinterpret_cast<const float4*>(p1);
+    float4 c = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (hi_valid) c = *reinterpret_cast<const float4*>(buf + tidx<C, LDT>(row, kb + 16 + 4 * g));
+    f.v[0] = a.x; f.v[1] = a.y; f.v[2] = a.z; f.v[3] = a.w;
+    f.v[4] = c.x; f.v[5] = c.y; f.v[6] = c.z; f.v[7] = c.w;
+  } else {
+    const half4 a = *reinterpret_cast<const half4*>(p1);
+    half4 c = half4{0, 0, 0, 0};
+    if (hi_valid) c = *reinterpret_cast<const half4*>(buf + tidx<C, LDT>(row, kb + 16 + 4 * g));
+    f.v = half8{a[0], a[1], a[2], a[3], c[0], c[1], c[2], c[3]};
+  }
+}
 
 // ---------------------------------------------------------------------------
-// Stage 1: conv + SiLU + L2 norm + chunk-local cumsum of g (block-level).
+// Stage 1 pieces (shared by the fused kernel and the standalone kda_prep).
 // Thread roles (NC = 2dk + dv items, one per thread):
 //   item i <  dk        : q, channel octet i % (dk/8), token block i / (dk/8)
 //   dk <= i < 2dk        : k, same mapping
 //   2dk <= i < NC        : v, octet (i-2dk) % (dv/8), token block (i-2dk) / (dv/8)
-// A token block is C/8 consecutive tokens.  q and k items also hold the
-// chunk-local cumsum G for their octet and tokens.  Tokens past n_valid are
-// zero (and have g = 0, beta = 0), which makes a ragged last chunk exact.
-// Must be called by all threads of the block.
+// A token block is C/8 consecutive tokens; a thread walks its block token by
+// token with a 4-token window of raw values, so it never holds the block.
+// Tokens past n_valid are zero (with g = 0 and beta = 0), which makes a
+// ragged last chunk exact.
 // ---------------------------------------------------------------------------
-template <int C, int DK, int DV, bool IN_BF16>
-struct PrepItem {
-  static constexpr int TBS = C / 8;
-  int role;          // 0 q, 1 k, 2 v, -1 idle
-  int oct;           // channel octet within the tensor
-  int tb;            // token block
-  float x[TBS][8];   // normalised q^ / k^ or v^
-  float G[TBS][8];   // chunk-local cumsum (q, k items)
+struct Item {
+  int role;   // 0 q, 1 k, 2 v, -1 idle
+  int oct;    // channel octet within its tensor
+  int tb;     // token block
+  int D;      // channels of the tensor
+  size_t chb; // first conv channel of the octet
+  const void* src;
 };
 
-template <int C, int DK, int DV, bool IN_BF16>
-__device__ __forceinline__ void prep_stage(const PrefillParams& p, int b, int h, int c0, int n_valid,
-                                           float* btot, PrepItem<C, DK, DV, IN_BF16>& it) {
-  constexpr int TBS = C / 8;
+template <int DK, int DV>
+__device__ __forceinline__ Item make_item(const PrefillParams& p, int h, int tid) {
   constexpr int NC = 2 * DK + DV;
-  const int tid = threadIdx.x;
-  const int T = p.T, H = p.H;
-  const size_t cch = (size_t)H * NC;
-
-  int D = DK, base = 0;
-  const void* src = p.q;
-  size_t chb = 0;
-  it.role = -1;
+  Item it;
+  it.role = -1; it.oct = 0; it.tb = 0; it.D = DK; it.chb = 0; it.src = p.q;
+  const int H = p.H;
   if (tid < DK) {
-    it.role = 0; D = DK; base = 0; src = p.q;
+    it.role = 0; it.D = DK; it.src = p.q;
+    it.oct = tid % (DK / 8); it.tb = tid / (DK / 8);
+    it.chb = (size_t)h * DK + 8 * it.oct;
   } else if (tid < 2 * DK) {
-    it.role = 1; D = DK; base = DK; src = p.k;
+    it.role = 1; it.D = DK; it.src = p.k;
+    it.oct = (tid - DK) % (DK / 8); it.tb = (tid - DK) / (DK / 8);
+    it.chb = (size_t)H * DK + (size_t)h * DK + 8 * it.oct;
   } else if (tid < NC) {
-    it.role = 2; D = DV; base = 2 * DK; src = p.v;
+    it.role = 2; it.D = DV; it.src = p.v;
+    it.oct = (tid - 2 * DK) % (DV / 8); it.tb = (tid - 2 * DK) / (DV / 8);
+    it.chb = (size_t)2 * H * DK + (size_t)h * DV + 8 * it.oct;
   }
-  if (it.role >= 0) {
-    const int j = tid - base;
-    it.oct = j % (D / 8);
-    it.tb = j / (D / 8);
-    const int c8 = 8 * it.oct;
-    if (it.role == 0) chb = (size_t)h * DK + c8;
-    else if (it.role == 1) chb = (size_t)H * DK + (size_t)h * DK + c8;
-    else chb = (size_t)2 * H * DK + (size_t)h * DV + c8;
+  return it;
+}
 
-    // conv taps of the octet
-    float w[8][4];
+// Conv + SiLU state of one item for one chunk: taps and the three previous raw
+// tokens (h0 oldest).  The window shifts by assignment, so a rolled token loop
+// never indexes a register array dynamically.
+struct ConvState {
+  float w[8][4];
+  float h0[8], h1[8], h2[8];
+};
+
+template <bool IN_BF16, int NC>
+__device__ __forceinline__ void conv_begin(const PrefillParams& p, const Item& it, int b, int h, int t0,
+                                           ConvState& cs) {
+  const size_t cch = (size_t)p.H * NC;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float4 t = *reinterpret_cast<const float4*>(p.conv_w + (chb + e) * 4);
-      w[e][0] = t.x; w[e][1] = t.y; w[e][2] = t.z; w[e][3] = t.w;
-    }
-    // sliding window over the raw tokens tau0-3 .. tau0+TBS-1 (chunk-relative)
-    const int tau0 = it.tb * TBS;
-    float win[4][8];
+  for (int e = 0; e < 8; ++e) {
+    const float4 t = *reinterpret_cast<const float4*>(p.conv_w + (it.chb + e) * 4);
+    cs.w[e][0] = t.x; cs.w[e][1] = t.y; cs.w[e][2] = t.z; cs.w[e][3] = t.w;
+  }
 #pragma unroll
-    for (int u = 0; u < TBS + 3; ++u) {
-      const int t = c0 + tau0 - 3 + u;  // absolute token
-      float* cur = win[u & 3];
-      if (t >= 0 && t < T) {
-        load8<IN_BF16>(src, ((size_t)b * T + t) * H * D + (size_t)h * D + c8, cur);
-      } else if (t < 0 && p.conv_in != nullptr) {
-        load8<IN_BF16>(p.conv_in, ((size_t)b * 3 + (3 + t)) * cch + chb, cur);
-      } else {
+  for (int u = 0; u < 3; ++u) {
+    const int t = t0 - 3 + u;
+    float* dst = u == 0 ? cs.h0 : u == 1 ? cs.h1 : cs.h2;
+    if (t >= 0 && t < p.T) {
+      load8<IN_BF16>(it.src, ((size_t)b * p.T + t) * p.H * it.D + (size_t)h * it.D + 8 * it.oct, dst);
+    } else if (t < 0 && p.conv_in != nullptr) {
+      load8<IN_BF16>(p.conv_in, ((size_t)b * 3 + (3 + t)) * cch + it.chb, dst);
+    } else {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) cur[e] = 0.f;
-      }
-      if (u >= 3) {
-        const int tt = u - 3;
-        const bool ok = tau0 + tt < n_valid;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float a = w[e][0] * win[(u - 3) & 3][e] + w[e][1] * win[(u - 2) & 3][e] +
-                          w[e][2] * win[(u - 1) & 3][e] + w[e][3] * win[u & 3][e];
-          it.x[tt][e] = ok ? siluf_(a) : 0.f;
-        }
-      }
-    }
-    if (it.role < 2) {
-      // L2 normalisation over the dk channels of each token (dk/8 lanes)
-      const float extra = it.role == 0 ? fast_rsq((float)DK) : 1.0f;
-#pragma unroll
-      for (int tt = 0; tt < TBS; ++tt) {
-        float ss = 0.f;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) ss += it.x[tt][e] * it.x[tt][e];
-        ss = group_sum<DK / 8>(ss);
-        const float r = fast_rsq(ss + kL2Eps) * extra;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) it.x[tt][e] *= r;
-      }
-      // local cumsum of g over the token block
-      float run[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) run[e] = 0.f;
-#pragma unroll
-      for (int tt = 0; tt < TBS; ++tt) {
-        const int t = c0 + tau0 + tt;
-        float gv[8];
-        if (tau0 + tt < n_valid) {
-          load8<IN_BF16>(p.g, ((size_t)b * T + t) * H * DK + (size_t)h * DK + c8, gv);
-        } else {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) gv[e] = 0.f;
-        }
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          run[e] += gv[e];
-          it.G[tt][e] = run[e];
-        }
-      }
-      if (it.role == 0) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) btot[it.tb * DK + c8 + e] = run[e];
-      }
+      for (int e = 0; e < 8; ++e) dst[e] = 0.f;
     }
   }
-  __syncthreads();
-  if (it.role == 0 || it.role == 1) {
-    const int c8 = 8 * it.oct;
-    float pre[8];
+}
+
+// Next token t: SiLU(conv) into x (0 if !valid), then shift the window.
+template <bool IN_BF16>
+__device__ __forceinline__ void conv_step(const PrefillParams& p, const Item& it, int b, int h, int t,
+                                          bool valid, ConvState& cs, float* x) {
+  float cur[8];
+  if (t < p.T) {
+    load8<IN_BF16>(it.src, ((size_t)b * p.T + t) * p.H * it.D + (size_t)h * it.D + 8 * it.oct, cur);
+  } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) pre[e] = 0.f;
-    for (int q = 0; q < it.tb; ++q) {
+    for (int e = 0; e < 8; ++e) cur[e] = 0.f;
+  }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) pre[e] += btot[q * DK + c8 + e];
-    }
+  for (int e = 0; e < 8; ++e) {
+    const float a = cs.w[e][0] * cs.h0[e] + cs.w[e][1] * cs.h1[e] + cs.w[e][2] * cs.h2[e] + cs.w[e][3] * cur[e];
+    x[e] = valid ? siluf_(a) : 0.f;
+    cs.h0[e] = cs.h1[e];
+    cs.h1[e] = cs.h2[e];
+    cs.h2[e] = cur[e];
+  }
+}
+
+// L2 normalisation of one token over dk channels held by DK/8 consecutive lanes.
+template <int DK>
+__device__ __forceinline__ void l2norm(float* x, float extra) {
+  float ss = 0.f;
 #pragma unroll
-    for (int tt = 0; tt < TBS; ++tt)
+  for (int e = 0; e < 8; ++e) ss += x[e] * x[e];
+  ss = group_sum<DK / 8>(ss);
+  const float r = fast_rsq(ss + kL2Eps) * extra;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) it.G[tt][e] += pre[e];
+  for (int e = 0; e < 8; ++e) x[e] *= r;
+}
+
+template <bool IN_BF16>
+__device__ __forceinline__ void load_g(const PrefillParams& p, int b, int h, int t, int c8, int DK, bool valid,
+                                       float* gv) {
+  if (valid) {
+    load8<IN_BF16>(p.g, ((size_t)b * p.T + t) * p.H * DK + (size_t)h * DK + c8, gv);
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] = 0.f;
   }
 }
 
@@ -377,6 +490,7 @@ __device__ __forceinline__ void prep_stage(const PrefillParams& p, int b, int h,
 template <int C, int DK, int DV, bool IN_BF16>
 __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p) {
   constexpr int TBS = C / 8;
+  constexpr int NC = 2 * DK + DV;
   __shared__ float btot[8 * DK];
   const int nchunks = (p.T + C - 1) / C;
   const int bh = blockIdx.x / nchunks;
@@ -384,23 +498,52 @@ __global__ __launch_bounds__(kThreads) void prep_kernel(PrefillParams p) {
   const int b = bh / p.H, h = bh - b * p.H;
   const int c0 = ci * C;
   const int n_valid = min(C, p.T - c0);
-  PrepItem<C, DK, DV, IN_BF16> it;
-  prep_stage<C, DK, DV, IN_BF16>(p, b, h, c0, n_valid, btot, it);
-  if (it.role < 0) return;
-  const int D = it.role == 2 ? DV : DK;
-  float* dst = it.role == 0 ? p.q_out : it.role == 1 ? p.k_out : p.v_out;
+  const Item it = make_item<DK, DV>(p, h, threadIdx.x);
   const int c8 = 8 * it.oct;
+  const int tau0 = it.tb * TBS;
+  // block sums of g, then each thread's prefix
+  if (it.role == 0) {
+    float s[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int tt = 0; tt < TBS; ++tt) {
+      float gv[8];
+      load_g<IN_BF16>(p, b, h, c0 + tau0 + tt, c8, DK, tau0 + tt < n_valid, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s[e] += gv[e];
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) btot[it.tb * DK + c8 + e] = s[e];
+  }
+  __syncthreads();
+  if (it.role < 0) return;
+  float G[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  if (it.role == 0) {
+    for (int q = 0; q < it.tb; ++q)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[e] += btot[q * DK + c8 + e];
+  }
+  ConvState cs;
+  conv_begin<IN_BF16, NC>(p, it, b, h, c0 + tau0, cs);
+  float* dst = it.role == 0 ? p.q_out : it.role == 1 ? p.k_out : p.v_out;
+#pragma unroll 1
   for (int tt = 0; tt < TBS; ++tt) {
-    const int tau = it.tb * TBS + tt;
-    if (tau >= n_valid) break;
+    const int tau = tau0 + tt;
+    const bool valid = tau < n_valid;
+    float x[8];
+    conv_step<IN_BF16>(p, it, b, h, c0 + tau, valid, cs, x);
+    if (it.role < 2) l2norm<DK>(x, it.role == 0 ? fast_rsq((float)DK) : 1.0f);
+    if (!valid) continue;
     const size_t row = ((size_t)b * p.T + c0 + tau) * p.H + h;
-    float* o = dst + row * D + c8;
-    *reinterpret_cast<float4*>(o) = make_float4(it.x[tt][0], it.x[tt][1], it.x[tt][2], it.x[tt][3]);
-    *reinterpret_cast<float4*>(o + 4) = make_float4(it.x[tt][4], it.x[tt][5], it.x[tt][6], it.x[tt][7]);
+    float* o = dst + row * it.D + c8;
+    *reinterpret_cast<float4*>(o) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
     if (it.role == 0) {
+      float gv[8];
+      load_g<IN_BF16>(p, b, h, c0 + tau, c8, DK, true, gv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) G[e] += gv[e];
       float* go = p.G_out + row * DK + c8;
-      *reinterpret_cast<float4*>(go) = make_float4(it.G[tt][0], it.G[tt][1], it.G[tt][2], it.G[tt][3]);
-      *reinterpret_cast<float4*>(go + 4) = make_float4(it.G[tt][4], it.G[tt][5], it.G[tt][6], it.G[tt][7]);
+      *reinterpret_cast<float4*>(go) = make_float4(G[0], G[1], G[2], G[3]);
+      *reinterpret_cast<float4*>(go + 4) = make_float4(G[4], G[5], G[6], G[7]);
     }
   }
 }
@@ -413,15 +556,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   using L = Smem<C, DK, DV, F32>;
   using Op = OpT<F32>;
   constexpr int NT = C / 16;
-  constexpr int NKV = L::NKV;
+  constexpr int NKV = NT * (NT + 1) / 2;
   constexpr int TBS = C / 8;
   constexpr int NC = 2 * DK + DV;
   constexpr int KSD = (DK + 31) / 32;   // 32-wide contraction steps over dk
   constexpr int KSC = (C + 31) / 32;    // ... over the tokens of a chunk
   constexpr int RTK = DK / 16;          // 16-row tiles of the state
   constexpr int CTV = DV / 16;          // 16-column tiles of dv (one per wave)
+  constexpr int LDR = L::LDR, LDC = L::LDC, LDT = L::LDT, LDA = L::LDA;
   static_assert(CTV <= kWaves && DK / 16 <= kWaves, "head dim too large for 8 waves");
   static_assert(TBS <= 16 && 16 % TBS == 0, "token blocks must tile the 16-token tiles");
+  static_assert(NT + 2 <= 8, "chunk too long for the per-tile setup threads");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Op* sQR = reinterpret_cast<Op*>(smem + L::QR);
@@ -431,9 +576,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float* sT = reinterpret_cast<float*>(smem + L::TS);
   Op* sTB = reinterpret_cast<Op*>(smem + L::TB);
   Op* sP = reinterpret_cast<Op*>(smem + L::PS);
-  Op* sW = reinterpret_cast<Op*>(smem + L::WS);
   Op* sQG = reinterpret_cast<Op*>(smem + L::QG);
   Op* sKGT = reinterpret_cast<Op*>(smem + L::KGT);
+  Op* sW = reinterpret_cast<Op*>(smem + L::KGT);   // W replaces (k e^G)^T after stage 4
   Op* sKBT = reinterpret_cast<Op*>(smem + L::KBT);
   Op* sVT = reinterpret_cast<Op*>(smem + L::VT);
   float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
@@ -441,27 +586,26 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float* sGC = reinterpret_cast<float*>(smem + L::GC);
   float* sRho = reinterpret_cast<float*>(smem + L::RHO);
   float* sERho = reinterpret_cast<float*>(smem + L::ERHO);
+  float* sFab = reinterpret_cast<float*>(smem + L::FAB);
   float* sBtot = reinterpret_cast<float*>(smem + L::BTOT);
   float* sSsq = reinterpret_cast<float*>(smem + L::SSQ);
   int* sFlag = reinterpret_cast<int*>(smem + L::FLAG);
+  float4* sCW = reinterpret_cast<float4*>(smem + L::CW);
 
-  const int tid = threadIdx.x;
-  const int wave = tid >> 6;
-  const int lane = tid & 63;
-  const int gq = lane >> 4;   // lane group (0..3)
-  const int li = lane & 15;   // index within the group
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int bh = blockIdx.x;
   const int H = p.H, T = p.T;
   const int b = bh / H, h = bh - b * H;
   const bool owns_cols = wave < CTV;
   const int col0 = 16 * wave;  // first dv column of this wave
 
-  // state columns [col0, col0+16) of S, as RTK accumulator tiles (C/D layout:
-  // element r of tile t is S[16t + 4gq + r][col0 + li])
+  // state columns [col0, col0+16) of S as RTK accumulator tiles: element r of
+  // tile t is S[16t + 4gq + r][col0 + li]
   f4 S[RTK];
 #pragma unroll
   for (int t = 0; t < RTK; ++t) S[t] = f4{0.f, 0.f, 0.f, 0.f};
   if (owns_cols && p.S0 != nullptr) {
+    const int gq = (threadIdx.x & 63) >> 4, li = threadIdx.x & 15;
     const float* s0 = p.S0 + (size_t)bh * DK * DV;
 #pragma unroll
     for (int t = 0; t < RTK; ++t)
@@ -469,120 +613,202 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       for (int r = 0; r < 4; ++r) S[t][r] = s0[(16 * t + 4 * gq + r) * DV + col0 + li];
   }
 
+  // conv taps of this head's q | k | v channels, in the head-local channel order
+  for (int c = threadIdx.x; c < NC; c += kThreads) {
+    size_t ch;
+    if (c < DK) ch = (size_t)h * DK + c;
+    else if (c < 2 * DK) ch = (size_t)H * DK + (size_t)h * DK + (c - DK);
+    else ch = (size_t)2 * H * DK + (size_t)h * DV + (c - 2 * DK);
+    sCW[c] = *reinterpret_cast<const float4*>(p.conv_w + ch * 4);
+  }
+
   const int nchunks = (T + C - 1) / C;
   for (int ci = 0; ci < nchunks; ++ci) {
     const int c0 = ci * C;
     const int n_valid = min(C, T - c0);
+    // per-lane indices, recomputed every chunk (see opaque())
+    const int tid = opaque((int)threadIdx.x);
+    const int lane = tid & 63;
+    const int gq = lane >> 4;   // lane group (0..3)
+    const int li = lane & 15;   // index within the group
+    const Item it = make_item<DK, DV>(p, h, tid);
+    const int c8 = 8 * it.oct;
+    const int tau0 = it.tb * TBS;
 
-    // ---- stage 1: prep ----------------------------------------------------
-    if (tid < 4) sFlag[tid] = 0;
-    PrepItem<C, DK, DV, IN_BF16> it;
-    prep_stage<C, DK, DV, IN_BF16>(p, b, h, c0, n_valid, sBtot, it);
-    if (tid < C) {
-      const int t = c0 + tid;
-      sBeta[tid] = tid < n_valid ? load1<IN_BF16>(p.beta, ((size_t)b * T + t) * H + h) : 0.f;
+    // ---- all global loads of the chunk, issued up front ---------------------
+    // raw q/k/v tokens tau0-3 .. tau0+TBS-1 of the item's octet, g for q/k
+    // items and beta; they stay packed until used
+    Raw8<IN_BF16> rw[TBS + 3];
+    Raw8<IN_BF16> gr[TBS];
+    float beta_v = 0.f;
+    // Loads are unconditional from clamped, in-bounds addresses; which of them
+    // hold real data is kept in bit masks applied when the values are used.  A
+    // load under a branch, or a register overwritten after a load, would make
+    // the compiler wait for it right away and serialise every load.
+    uint32_t rw_ok = 0, gr_ok = 0;
+    if (it.role >= 0) {
+      const size_t cch = (size_t)H * NC;
+      const bool has_hist = p.conv_in != nullptr;
+#pragma unroll
+      for (int u = 0; u < TBS + 3; ++u) {
+        const int t = c0 + tau0 - 3 + u;
+        const bool hist = t < 0 && has_hist;
+        const int tc = min(max(t, 0), T - 1);
+        const void* base = hist ? p.conv_in : it.src;
+        const size_t idx = hist ? ((size_t)b * 3 + (3 + t)) * cch + it.chb
+                                : ((size_t)b * T + tc) * H * it.D + (size_t)h * it.D + c8;
+        raw_load<IN_BF16>(rw[u], base, idx);
+        rw_ok |= (hist || (t >= 0 && t < T)) ? (1u << u) : 0u;
+      }
+      if (it.role < 2) {
+#pragma unroll
+        for (int tt = 0; tt < TBS; ++tt) {
+          const int t = min(c0 + tau0 + tt, T - 1);
+          raw_load<IN_BF16>(gr[tt], p.g, ((size_t)b * T + t) * H * DK + (size_t)h * DK + c8);
+          gr_ok |= (tau0 + tt < n_valid) ? (1u << tt) : 0u;
+        }
+      }
     }
-    // tile references rho_a = G(16a - 1), G_C, and the fp16-range check
+    if (tid < C) beta_v = load1<IN_BF16>(p.beta, ((size_t)b * T + c0 + min(tid, n_valid - 1)) * H + h);
+
+    // ---- stage 1a: beta, token-block sums of g ------------------------------
+    if (tid < 4) sFlag[tid] = 0;
+    if (tid < C) sBeta[tid] = tid < n_valid ? beta_v : 0.f;
     if (it.role == 0) {
-      const int c8 = 8 * it.oct;
-      const int last = it.tb * TBS + TBS - 1;  // chunk-relative last token of the block
-      if (((last + 1) & 15) == 0) {
-        const int a = (last + 1) >> 4;         // tile that starts after this block
+      float s8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int tt = 0; tt < TBS; ++tt) {
+        float gv[8];
+        raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) s8[e] += gv[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sBtot[it.tb * DK + c8 + e] = s8[e];
+    }
+    lds_barrier();
+
+    // ---- stage 1b: per-tile decay scalars (q-item threads, one job per tb) ---
+    //   tb <  NT : rho_tb = G before tile tb, e^{rho_tb}, e^{rho_tb - rho_b} (b < tb)
+    //   tb == NT : G_C and e^{G_C}
+    //   tb == NT+1 : fp16 range check of the tile spans
+    if (it.role == 0 && it.tb < NT + 2) {
+      float rho[NT + 1][8];  // rho[a] = sum of the blocks before tile a; rho[NT] = G_C
+#pragma unroll
+      for (int e = 0; e < 8; ++e) rho[0][e] = 0.f;
+#pragma unroll
+      for (int a = 0; a < NT; ++a) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const float gv = it.G[TBS - 1][e];
-          if (a < NT) {
-            sRho[a * DK + c8 + e] = gv;
-            sERho[a * DK + c8 + e] = fast_exp(gv);
-          } else {
-            sGC[c8 + e] = gv;
-            sGam[c8 + e] = fast_exp(gv);
-          }
-        }
-      }
-      if (it.tb == 0) {
+          float sa = rho[a][e];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          sRho[c8 + e] = 0.f;
-          sERho[c8 + e] = 1.f;
+          for (int q = a * (16 / TBS); q < (a + 1) * (16 / TBS); ++q) sa += sBtot[q * DK + c8 + e];
+          rho[a + 1][e] = sa;
         }
       }
-      if constexpr (!F32) {
-        // span of every tile for this octet: -(sum of g over the tile)
-        float mx = 0.f;
+      if (it.tb < NT) {
+#pragma unroll
         for (int a = 0; a < NT; ++a) {
+          if (a != it.tb) continue;  // static indices into rho[][]
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            float s = 0.f;
-            for (int q = a * (16 / TBS); q < (a + 1) * (16 / TBS); ++q) s -= sBtot[q * DK + c8 + e];
-            mx = fmaxf(mx, s);
+            sRho[a * DK + c8 + e] = rho[a][e];
+            sERho[a * DK + c8 + e] = fast_exp(rho[a][e]);
           }
+#pragma unroll
+          for (int bb = 0; bb < a; ++bb)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sFab[off_pair(a, bb) * DK + c8 + e] = fast_exp(rho[a][e] - rho[bb][e]);
         }
+      } else if (it.tb == NT) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          sGC[c8 + e] = rho[NT][e];
+          sGam[c8 + e] = fast_exp(rho[NT][e]);
+        }
+      } else if constexpr (!F32) {
+        float mx = 0.f;
+#pragma unroll
+        for (int a = 0; a < NT; ++a)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) mx = fmaxf(mx, rho[a][e] - rho[a + 1][e]);
         if (mx > kF16SpanMax) atomicOr(&sFlag[0], 1);
       }
     }
-    // v items write v^T now (no G needed)
-    if (it.role == 2) {
-      const int c8 = 8 * it.oct;
-      const int tau0 = it.tb * TBS;
+    // each q / k thread: G just before its token block
+    float G[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    if (it.role == 0 || it.role == 1) {
+      for (int q = 0; q < it.tb; ++q)
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-#pragma unroll
-        for (int tt = 0; tt < TBS; ++tt) st_op<F32>(sVT + (c8 + e) * C + tau0 + tt, it.x[tt][e], false);
+        for (int e = 0; e < 8; ++e) G[e] += sBtot[q * DK + c8 + e];
     }
-    __syncthreads();
+    lds_barrier();
     const bool bfAP = sFlag[0] != 0;  // decay-weighted operands in bf16 for this chunk
 
-    // q / k items: decay-scaled operands
-    if (it.role == 0 || it.role == 1) {
-      const int c8 = 8 * it.oct;
-      const int tau0 = it.tb * TBS;
+    // ---- stage 1c: conv + SiLU + L2, then the decay-scaled operands -----------
+    if (it.role >= 0) {
       const int bt = tau0 >> 4;  // 16-token tile of this block
-      float rho[8], erho[8];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        rho[e] = sRho[bt * DK + c8 + e];
-        erho[e] = sERho[bt * DK + c8 + e];
-      }
+      const float* rho = sRho + bt * DK + c8;    // per-tile scalars, read from LDS on use
+      const float* erho = sERho + bt * DK + c8;
+      const float* gcv = sGC + c8;
 #pragma unroll
       for (int tt = 0; tt < TBS; ++tt) {
         const int tau = tau0 + tt;
-        float er[8], rowv[8], gv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          er[e] = fast_exp(it.G[tt][e] - rho[e]);  // e^{G - rho_bt} <= 1
-          rowv[e] = it.x[tt][e] * er[e];
-          gv[e] = rowv[e] * erho[e];                // x e^{G}
-        }
-        if (it.role == 0) {
-          st_op8<F32>(sQR + tau * DK + c8, rowv, bfAP);
-          st_op8<F32>(sQG + tau * DK + c8, gv, false);
-        } else {
-          st_op8<F32>(sKR + tau * DK + c8, rowv, bfAP);
+        const bool valid = tau < n_valid;
+        float x[8];
+        {
+          // raw tokens tau-3 .. tau, unpacked per channel; taps from LDS
+          const bool ok0 = (rw_ok >> tt) & 1u, ok1 = (rw_ok >> (tt + 1)) & 1u;
+          const bool ok2 = (rw_ok >> (tt + 2)) & 1u, ok3 = (rw_ok >> (tt + 3)) & 1u;
+          const float4* cw = sCW + (it.role == 0 ? 0 : it.role == 1 ? DK : 2 * DK) + c8;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            st_op<F32>(sKGT + (c8 + e) * C + tau, gv[e], false);
-            st_op<F32>(sKBT + (c8 + e) * C + tau, it.x[tt][e] * fast_exp(sGC[c8 + e] - it.G[tt][e]), false);
+            const float4 wv = cw[e];
+            const float a = wv.x * (ok0 ? raw_elem<IN_BF16>(rw[tt], e) : 0.f) +
+                            wv.y * (ok1 ? raw_elem<IN_BF16>(rw[tt + 1], e) : 0.f) +
+                            wv.z * (ok2 ? raw_elem<IN_BF16>(rw[tt + 2], e) : 0.f) +
+                            wv.w * (ok3 ? raw_elem<IN_BF16>(rw[tt + 3], e) : 0.f);
+            x[e] = valid ? siluf_(a) : 0.f;
           }
-          // column operands for row tiles a >= bt: k e^{rho_a - G}
-          float ec[8];
+        }
+        if (it.role == 2) {
 #pragma unroll
-          for (int e = 0; e < 8; ++e) ec[e] = it.x[tt][e] * fast_rcp(er[e]);
-          for (int a = bt; a < NT; ++a) {
-            float cv[8];
+          for (int e = 0; e < 8; ++e) st_op<F32>(sVT + tidx<C, LDT>(c8 + e, tau), x[e], false);
+          continue;
+        }
+        l2norm<DK>(x, it.role == 0 ? fast_rsq((float)DK) : 1.0f);
+        float gv[8];
+        raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
+        float er[8], rowv[8], xg[8];
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-              cv[e] = a == bt ? ec[e] : ec[e] * fast_exp(sRho[a * DK + c8 + e] - rho[e]);
-            const int vrow = 16 * (a * (a + 1) / 2) + tau;  // rows of variant a start at 16*a(a+1)/2
-            st_op8<F32>(sKC + vrow * DK + c8, cv, bfAP);
+        for (int e = 0; e < 8; ++e) {
+          G[e] += gv[e];
+          er[e] = fast_exp(G[e] - rho[e]);  // e^{G - rho_bt} <= 1
+          rowv[e] = x[e] * er[e];
+          xg[e] = rowv[e] * erho[e];         // x e^{G}
+        }
+        if (it.role == 0) {
+          st_op8<F32>(sQR + tau * LDR + c8, rowv, bfAP);
+          st_op8<F32>(sQG + tau * LDR + c8, xg, false);
+        } else {
+          st_op8<F32>(sKR + tau * LDR + c8, rowv, bfAP);
+          float cv[8];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            cv[e] = x[e] * fast_rcp(er[e]);  // k e^{rho_bt - G}
+            st_op<F32>(sKGT + tidx<C, LDT>(c8 + e, tau), xg[e], false);
+            st_op<F32>(sKBT + tidx<C, LDT>(c8 + e, tau), x[e] * fast_exp(gcv[e] - G[e]), false);
           }
+          st_op8<F32>(sKC + tau * LDR + c8, cv, bfAP);
         }
       }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 2: A and P tiles on the matrix cores --------------------------
     // jobs: A(a,b) for b <= a (NKV), then P(a,b) (NKV); wave w takes w, w+8, ...
+    // The column operand of tile b is k e^{rho_b - G}; for b < a it is scaled
+    // by e^{rho_a - rho_b} <= 1 while loading, giving the reference rho_a.
     constexpr int NJ = 2 * NKV;
     constexpr int JPW = (NJ + kWaves - 1) / kWaves;
     f4 acc[JPW];
@@ -597,18 +823,18 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         while ((a + 1) * (a + 2) / 2 <= pj) ++a;
         const int bcol = pj - a * (a + 1) / 2;
         const Op* rowb = isP ? sQR : sKR;
-        const int vrow = 16 * (a * (a + 1) / 2) + 16 * bcol + li;
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           const int k0 = 32 * ks + 8 * gq;
           Frag<F32> fa, fb;
-          frag_std<F32>(fa, rowb, 16 * a + li, DK, k0, k0 < DK);
-          frag_std<F32>(fb, sKC, vrow, DK, k0, k0 < DK);
+          frag_std<F32>(fa, rowb, 16 * a + li, LDR, k0, k0 < DK);
+          frag_std<F32>(fb, sKC, 16 * bcol + li, LDR, k0, k0 < DK);
+          if (bcol < a && k0 < DK) frag_scale<F32>(fb, sFab + off_pair(a, bcol) * DK + k0, bfAP);
           acc[jj] = mma<F32>(fa, fb, acc[jj], bfAP);
         }
       }
     }
-    __syncthreads();  // region X (A/P operands) is dead from here on
+    lds_barrier();  // region X (A/P operands) is dead from here on
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
       const int job = wave + kWaves * jj;
@@ -622,17 +848,17 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * a + 4 * gq + r;
           const int col = 16 * bcol + li;
-          if (isP) st_op<F32>(sP + row * C + col, row >= col ? acc[jj][r] : 0.f, false);
-          else sA[row * C + col] = row > col ? sBeta[row] * acc[jj][r] : 0.f;
+          if (isP) st_op<F32>(sP + row * LDC + col, row >= col ? acc[jj][r] : 0.f, false);
+          else sA[row * LDA + col] = row > col ? sBeta[row] * acc[jj][r] : 0.f;
         }
       }
     }
     // upper tiles of P are zero (P.U runs over whole 32-token steps)
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int row = idx / C, col = idx - row * C;
-      if ((col >> 4) > (row >> 4)) st_op<F32>(sP + idx, 0.f, false);
+      if ((col >> 4) > (row >> 4)) st_op<F32>(sP + row * LDC + col, 0.f, false);
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 3: T = (I + A)^-1 ------------------------------------------------
     // diagonal 16x16 blocks by forward substitution: wave 0, lane = (block, column)
@@ -643,80 +869,79 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         float col[16];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float s = 0.f;
+          float s0 = 0.f, s1 = 0.f;  // two partial sums shorten the dependency chain
 #pragma unroll
-          for (int m = 0; m < i; ++m) s += sA[(16 * a + i) * C + 16 * a + m] * col[m];
-          col[i] = i == j ? 1.f : (i > j ? -s : 0.f);
+          for (int m = 0; m < i; ++m) {
+            const float t = sA[(16 * a + i) * LDA + 16 * a + m] * col[m];
+            if (m & 1) s1 += t; else s0 += t;
+          }
+          col[i] = i == j ? 1.f : (i > j ? -(s0 + s1) : 0.f);
         }
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sT[(16 * a + i) * C + 16 * a + j] = col[i];
+        for (int i = 0; i < 16; ++i) sT[(16 * a + i) * LDA + 16 * a + j] = col[i];
       }
     }
-    // zero the upper blocks of T
+    lds_barrier();
+    // off-diagonal blocks, one wave per block column b (fp32 matrix cores):
+    //   T_ab = -T_aa * sum_{m=b}^{a-1} A_am T_mb,  a = b+1 .. NT-1 in order.
+    // The blocks of column b stay in registers (C layout: element e of lane
+    // (g, i) is row 4g+e, column i) and feed the next products as B operands,
+    // with the contraction index k = 4g + s in sub-step s.
+    if (wave < NT - 1) {
+      const int bb = wave;
+      f4 Tcol[NT];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) Tcol[0][e] = sT[(16 * bb + 4 * gq + e) * LDA + 16 * bb + li];
+#pragma unroll
+      for (int d = 1; d < NT; ++d) {
+        const int a = bb + d;
+        if (a < NT) {
+          f4 X = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int md = 0; md < d; ++md) {  // m = bb + md
+            const int m = bb + md;
+#pragma unroll
+            for (int s4 = 0; s4 < 4; ++s4)
+              X = __builtin_amdgcn_mfma_f32_16x16x4f32(sA[(16 * a + li) * LDA + 16 * m + 4 * gq + s4],
+                                                       Tcol[md][s4], X, 0, 0, 0);
+          }
+          f4 Y = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            Y = __builtin_amdgcn_mfma_f32_16x16x4f32(sT[(16 * a + li) * LDA + 16 * a + 4 * gq + s4], X[s4], Y,
+                                                     0, 0, 0);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            Tcol[d][e] = -Y[e];
+            sT[(16 * a + 4 * gq + e) * LDA + 16 * bb + li] = -Y[e];
+          }
+        }
+      }
+    }
+    lds_barrier();
+    // Tb = T diag(beta), zero above the block diagonal
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int row = idx / C, col = idx - row * C;
-      if ((col >> 4) > (row >> 4)) sT[idx] = 0.f;
+      const float v = (col >> 4) > (row >> 4) ? 0.f : sT[row * LDA + col] * sBeta[col];
+      st_op<F32>(sTB + row * LDC + col, v, false);
     }
-    __syncthreads();
-    // off-diagonal blocks by block diagonals d = a - b:
-    //   T_ab = -T_aa * sum_{m=b}^{a-1} A_am T_mb
-    float* scratch = reinterpret_cast<float*>(smem + L::TB);  // TB is free until stage 3 ends
-    for (int d = 1; d < NT; ++d) {
-      const int nb = NT - d;
-      if (wave < nb) {
-        const int bb = wave, a = wave + d;
-        float* X = scratch + wave * 256;
-        const int j = li;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int i = gq + 4 * s4;
-          float x = 0.f;
-          for (int m = bb; m < a; ++m)
-#pragma unroll
-            for (int kk = 0; kk < 16; ++kk)
-              x += sA[(16 * a + i) * C + 16 * m + kk] * sT[(16 * m + kk) * C + 16 * bb + j];
-          X[i * 16 + j] = x;
-        }
-      }
-      __syncthreads();
-      if (wave < nb) {
-        const int bb = wave, a = wave + d;
-        const float* X = scratch + wave * 256;
-        const int j = li;
-#pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          const int i = gq + 4 * s4;
-          float x = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < 16; ++kk) x += sT[(16 * a + i) * C + 16 * a + kk] * X[kk * 16 + j];
-          sT[(16 * a + i) * C + 16 * bb + j] = -x;
-        }
-      }
-      __syncthreads();
-    }
-    // Tb = T diag(beta)
-    for (int idx = tid; idx < C * C; idx += kThreads) {
-      const int col = idx % C;
-      st_op<F32>(sTB + idx, sT[idx] * sBeta[col], false);
-    }
-    __syncthreads();
+    lds_barrier();
 
     // ---- stage 4: W = Tb (K e^G)  (all dk columns) and U~ = Tb V (own columns)
+    f4 Wt[NT];
     if (wave < DK / 16) {
       const int ct = wave;
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt) {
-        f4 w = f4{0.f, 0.f, 0.f, 0.f};
+        Wt[rt] = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kt = 0; kt < KSC; ++kt) {
           const int k0 = 32 * kt + 8 * gq;
           Frag<F32> fa, fb;
-          frag_std<F32>(fa, sTB, 16 * rt + li, C, k0, k0 < C);
-          frag_std<F32>(fb, sKGT, 16 * ct + li, C, k0, k0 < C);
-          w = mma<F32>(fa, fb, w);
+          frag_std<F32>(fa, sTB, 16 * rt + li, LDC, k0, k0 < C);
+          frag_std_t<F32, C, LDT>(fb, sKGT, 16 * ct + li, k0, k0 < C);
+          Wt[rt] = mma<F32>(fa, fb, Wt[rt]);
         }
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st_op<F32>(sW + (16 * rt + 4 * gq + r) * DK + 16 * ct + li, w[r], false);
       }
     }
     f4 U[NT];
@@ -728,15 +953,35 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int kt = 0; kt < KSC; ++kt) {
           const int k0 = 32 * kt + 8 * gq;
           Frag<F32> fa, fb;
-          frag_std<F32>(fa, sTB, 16 * rt + li, C, k0, k0 < C);
-          frag_std<F32>(fb, sVT, col0 + li, C, k0, k0 < C);
+          frag_std<F32>(fa, sTB, 16 * rt + li, LDC, k0, k0 < C);
+          frag_std_t<F32, C, LDT>(fb, sVT, col0 + li, k0, k0 < C);
           U[rt] = mma<F32>(fa, fb, U[rt]);
         }
       }
     }
-    __syncthreads();
+    lds_barrier();  // (k e^G)^T is dead: W goes in its place
+    if (wave < DK / 16) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st_op<F32>(sW + (16 * rt + 4 * gq + r) * LDR + 16 * wave + li, Wt[rt][r], false);
+    }
+    lds_barrier();
 
     // ---- stage 5: inter-chunk products and state update (own dv columns) -----
+    // gate values for the epilogue, loaded now so their latency hides behind
+    // the products below
+    float gpre[NT][4];
+    if (owns_cols) {
+#pragma unroll
+      for (int rt = 0; rt < NT; ++rt)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = 16 * rt + 4 * gq + r;
+          // rows past the end are never stored; load a valid row for them
+          gpre[rt][r] = load1<IN_BF16>(p.gate, (((size_t)b * T + c0 + min(row, n_valid - 1)) * H + h) * DV + col0 + li);
+        }
+    }
     f4 O[NT];
     if (owns_cols) {
       // S as B operand, contraction rows {32ks + 4gq + r} u {32ks + 16 + 4gq + r}
@@ -758,7 +1003,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           Frag<F32> fa;
-          frag_perm<F32>(fa, sW, 16 * rt + li, DK, 32 * ks, gq, true, 32 * ks + 16 < DK);
+          frag_perm<F32>(fa, sW, 16 * rt + li, LDR, 32 * ks, gq, true, 32 * ks + 16 < DK);
           ws = mma<F32>(fa, Sb[ks], ws);
         }
         U[rt] = U[rt] - ws;
@@ -782,14 +1027,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           Frag<F32> fa;
-          frag_perm<F32>(fa, sQG, 16 * rt + li, DK, 32 * ks, gq, true, 32 * ks + 16 < DK);
+          frag_perm<F32>(fa, sQG, 16 * rt + li, LDR, 32 * ks, gq, true, 32 * ks + 16 < DK);
           o = mma<F32>(fa, Sb[ks], o);
         }
 #pragma unroll
         for (int kt = 0; kt < KSC; ++kt) {
           if (32 * kt <= 16 * rt + 15) {
             Frag<F32> fa;
-            frag_perm<F32>(fa, sP, 16 * rt + li, C, 32 * kt, gq, true, 32 * kt + 16 < C);
+            frag_perm<F32>(fa, sP, 16 * rt + li, LDC, 32 * kt, gq, true, 32 * kt + 16 < C);
             o = mma<F32>(fa, Ub[kt], o);
           }
         }
@@ -804,7 +1049,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int kt = 0; kt < KSC; ++kt) {
           Frag<F32> fa;
-          frag_perm<F32>(fa, sKBT, 16 * t + li, C, 32 * kt, gq, true, 32 * kt + 16 < C);
+          frag_perm_t<F32, C, LDT>(fa, sKBT, 16 * t + li, 32 * kt, gq, 32 * kt + 16 < C);
           s = mma<F32>(fa, Ub[kt], s);
         }
         S[t] = s;
@@ -818,7 +1063,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           if (li == 0) sSsq[wave * C + 16 * rt + 4 * gq + r] = ss;
         }
     }
-    __syncthreads();
+    lds_barrier();
 
     // ---- epilogue: head-wise RMSNorm * sigmoid(gate) ----------------------------
     if (owns_cols) {
@@ -833,15 +1078,16 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             for (int w2 = 0; w2 < CTV; ++w2) ss += sSsq[w2 * C + row];
             const float rs = fast_rsq(ss * (1.0f / DV) + kRmsEps);
             const size_t oi = (((size_t)b * T + c0 + row) * H + h) * DV + col0 + li;
-            const float gt = load1<IN_BF16>(p.gate, oi);
-            store1<OUT_BF16>(p.o, oi, O[rt][r] * rs * sigmoidf_(gt));
+            store1<OUT_BF16>(p.o, oi, O[rt][r] * rs * sigmoidf_(gpre[rt][r]));
           }
         }
     }
-    __syncthreads();  // LDS is rewritten by the next chunk
+    lds_barrier();  // LDS is rewritten by the next chunk
   }
 
   // ---- final state and conv history ------------------------------------------
+  const int tid = threadIdx.x;
+  const int gq = (tid & 63) >> 4, li = tid & 15;
   if (owns_cols && p.S_T != nullptr) {
     float* st = p.S_T + (size_t)bh * DK * DV;
 #pragma unroll
