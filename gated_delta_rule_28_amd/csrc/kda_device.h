@@ -86,12 +86,26 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
 }
 
 // ---- reductions ------------------------------------------------------------------
-// Sum over groups of W consecutive lanes (W a power of two <= 64); every lane of
-// the group gets the sum.
+// DPP lane moves inside a row of 16 lanes: quad_perm xor 1 and xor 2, then
+// half-row and row mirrors.  Each step pairs every lane with a lane of the
+// other half of its current group, so after log2(W) steps every lane of an
+// aligned group of W lanes holds the group's sum (no LDS round trip).
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over aligned groups of W consecutive lanes (W a power of two <= 64);
+// every lane of the group gets the sum.  All lanes of a group must be active.
 template <int W>
 __device__ __forceinline__ float group_sum(float x) {
-#pragma unroll
-  for (int o = W / 2; o > 0; o >>= 1) x += __shfl_xor(x, o, 64);
+  static_assert(W >= 1 && W <= 64 && (W & (W - 1)) == 0, "W must be a power of two <= 64");
+  if constexpr (W >= 2) x += dpp_mov<0xB1>(x);    // quad_perm [1,0,3,2]: lane ^ 1
+  if constexpr (W >= 4) x += dpp_mov<0x4E>(x);    // quad_perm [2,3,0,1]: lane ^ 2
+  if constexpr (W >= 8) x += dpp_mov<0x141>(x);   // row_half_mirror: other quad of the half-row
+  if constexpr (W >= 16) x += dpp_mov<0x140>(x);  // row_mirror: other half of the row
+  if constexpr (W >= 32) x += __shfl_xor(x, 16, 64);
+  if constexpr (W >= 64) x += __shfl_xor(x, 32, 64);
   return x;
 }
 

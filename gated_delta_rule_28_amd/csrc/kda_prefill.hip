@@ -278,6 +278,23 @@ __device__ __forceinline__ void frag_scale(Frag<F32>& fr, const float* f, bool b
   }
 }
 
+// 8 consecutive outputs (fp32 or bf16) to global memory.
+template <bool BF16>
+__device__ __forceinline__ void store8(void* base, size_t idx, const float* x) {
+  if constexpr (BF16) {
+    uint4 u;
+    u.x = (uint32_t)f_to_bf16(x[0]) | ((uint32_t)f_to_bf16(x[1]) << 16);
+    u.y = (uint32_t)f_to_bf16(x[2]) | ((uint32_t)f_to_bf16(x[3]) << 16);
+    u.z = (uint32_t)f_to_bf16(x[4]) | ((uint32_t)f_to_bf16(x[5]) << 16);
+    u.w = (uint32_t)f_to_bf16(x[6]) | ((uint32_t)f_to_bf16(x[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + idx) = u;
+  } else {
+    float* o = reinterpret_cast<float*>(base) + idx;
+    *reinterpret_cast<float4*>(o) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(o + 4) = make_float4(x[4], x[5], x[6], x[7]);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // LDS layout of the fused kernel (byte offsets).  Operand rows are padded by
 // 16 bytes so 16 lanes reading 16 consecutive rows hit distinct banks; arrays
@@ -319,12 +336,16 @@ struct Smem {
   static constexpr int RHO = GC + DK * 4;                   // [NT][DK]  rho_a
   static constexpr int ERHO = RHO + NT * DK * 4;            // [NT][DK]  e^{rho_a}
   static constexpr int FAB = ERHO + NT * DK * 4;            // [NOFF][DK] e^{rho_a - rho_b}, b < a
-  static constexpr int BTOT = FAB + (NOFF > 0 ? NOFF : 1) * DK * 4;  // [8][DK] token-block sums of g
-  static constexpr int SSQ = BTOT;                          // [8 waves][C] (reuses BTOT's space)
-  static constexpr int BTOT_BYTES = (8 * DK > kWaves * C ? 8 * DK : kWaves * C) * 4;
+  static constexpr int BTOT = FAB + (NOFF > 0 ? NOFF : 1) * DK * 4;  // [16][DK] sums of g per k block
+  static constexpr int BTOT_BYTES = 16 * DK * 4;
   static constexpr int CW = BTOT + BTOT_BYTES;              // [2dk+dv][4] conv taps of the head
   static constexpr int FLAG = CW + (2 * DK + DV) * 16;      // [4] ints
-  static constexpr int BYTES = FLAG + 16;
+  // O of a chunk, staged for the epilogue: [C][DV+4] fp32, in A / T's space
+  // (dead by then) when it fits, else after everything else
+  static constexpr int LDO = DV + 4;
+  static constexpr int OS_BYTES = C * LDO * 4;
+  static constexpr int OS = OS_BYTES <= TB ? 0 : FLAG + 16;
+  static constexpr int BYTES = OS_BYTES <= TB ? FLAG + 16 : FLAG + 16 + OS_BYTES;
 };
 
 // index of the pair (a, b), b < a, among the strictly-lower tile pairs
@@ -557,7 +578,6 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   using Op = OpT<F32>;
   constexpr int NT = C / 16;
   constexpr int NKV = NT * (NT + 1) / 2;
-  constexpr int TBS = C / 8;
   constexpr int NC = 2 * DK + DV;
   constexpr int KSD = (DK + 31) / 32;   // 32-wide contraction steps over dk
   constexpr int KSC = (C + 31) / 32;    // ... over the tokens of a chunk
@@ -565,8 +585,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   constexpr int CTV = DV / 16;          // 16-column tiles of dv (one per wave)
   constexpr int LDR = L::LDR, LDC = L::LDC, LDT = L::LDT, LDA = L::LDA;
   static_assert(CTV <= kWaves && DK / 16 <= kWaves, "head dim too large for 8 waves");
-  static_assert(TBS <= 16 && 16 % TBS == 0, "token blocks must tile the 16-token tiles");
-  static_assert(NT + 2 <= 8, "chunk too long for the per-tile setup threads");
+  static_assert(C >= 16 && 256 % C == 0, "k blocks must tile the 16-token tiles");
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Op* sQR = reinterpret_cast<Op*>(smem + L::QR);
@@ -588,7 +607,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   float* sERho = reinterpret_cast<float*>(smem + L::ERHO);
   float* sFab = reinterpret_cast<float*>(smem + L::FAB);
   float* sBtot = reinterpret_cast<float*>(smem + L::BTOT);
-  float* sSsq = reinterpret_cast<float*>(smem + L::SSQ);
+  float* sO = reinterpret_cast<float*>(smem + L::OS);
   int* sFlag = reinterpret_cast<int*>(smem + L::FLAG);
   float4* sCW = reinterpret_cast<float4*>(smem + L::CW);
 
@@ -622,7 +641,94 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     sCW[c] = *reinterpret_cast<const float4*>(p.conv_w + ch * 4);
   }
 
+  // Stage-1 roles (one per wave, so every role branch is wave-uniform):
+  //   q items: threads [0, DK)         octet i % (DK/8), block i / (DK/8) of C/8 tokens
+  //   k items: threads [DK, 3DK)       octet j % (DK/8), block j / (DK/8) of C/16 tokens
+  //   v items: threads [3DK, 3DK + DV) octet j % (DV/8), block j / (DV/8) of C/8 tokens
+  // Keys get twice the threads: their per-token work (row, column and two
+  // transposed operands, two exponentials) is the heaviest.
+  constexpr int TBQ = C / 8;            // tokens per q / v block
+  constexpr int TBK = C / 16;           // tokens per k block
+  constexpr int BPT = 16 / TBK;         // k blocks per 16-token tile
+  constexpr int NE = C * DV / 8;        // epilogue items: (token, dv octet)
+  constexpr int EPT = (NE + kThreads - 1) / kThreads;
+  static_assert(3 * DK + DV <= kThreads, "stage-1 roles need 3dk + dv threads");
+
   const int nchunks = (T + C - 1) / C;
+  const size_t cch = (size_t)H * NC;
+  const bool has_hist = p.conv_in != nullptr;
+
+  // per-thread role, recomputed from an opaque thread id wherever needed
+  struct Role { int role, oct, blk, tau0, D; size_t chb; const void* src; };
+  auto make_role = [&](int t) {
+    Role r;
+    if (t < DK) {
+      r.role = 0; r.D = DK; r.src = p.q; r.oct = t % (DK / 8); r.blk = t / (DK / 8); r.tau0 = r.blk * TBQ;
+      r.chb = (size_t)h * DK + 8 * r.oct;
+    } else if (t < 3 * DK) {
+      const int j = t - DK;
+      r.role = 1; r.D = DK; r.src = p.k; r.oct = j % (DK / 8); r.blk = j / (DK / 8); r.tau0 = r.blk * TBK;
+      r.chb = (size_t)H * DK + (size_t)h * DK + 8 * r.oct;
+    } else if (t < 3 * DK + DV) {
+      const int j = t - 3 * DK;
+      r.role = 2; r.D = DV; r.src = p.v; r.oct = j % (DV / 8); r.blk = j / (DV / 8); r.tau0 = r.blk * TBQ;
+      r.chb = (size_t)2 * H * DK + (size_t)h * DV + 8 * r.oct;
+    } else {
+      r.role = -1; r.D = DK; r.src = p.q; r.oct = 0; r.blk = 0; r.tau0 = 0; r.chb = 0;
+    }
+    return r;
+  };
+
+  // Loads of one chunk: raw tokens tau0-3 .. tau0+ntok-1 of the item's octet,
+  // g for q / k items, beta.  Unconditional from clamped, in-bounds addresses;
+  // which values are real is kept in bit masks applied at use.  (A load under
+  // a per-load branch, or a register overwritten after a load, makes the
+  // compiler wait for it on the spot and serialises the loads.)
+  Raw8<IN_BF16> rw[TBQ + 3];
+  Raw8<IN_BF16> gr[TBQ];
+  uint32_t rw_ok = 0, gr_ok = 0;
+  float beta_v = 0.f;
+  auto issue_loads = [&](int ci_load) {
+    const int tl = opaque((int)threadIdx.x);
+    const Role r = make_role(tl);
+    const int cl = ci_load * C;
+    const int nv = min(C, T - cl);
+    const int c8 = 8 * r.oct;
+    rw_ok = 0;
+    gr_ok = 0;
+    auto load_raw = [&](int u) {
+      const int t = cl + r.tau0 - 3 + u;
+      const bool hist = t < 0 && has_hist;
+      const int tc = min(max(t, 0), T - 1);
+      const void* base = hist ? p.conv_in : r.src;
+      const size_t idx = hist ? ((size_t)b * 3 + (3 + t)) * cch + r.chb
+                              : ((size_t)b * T + tc) * H * r.D + (size_t)h * r.D + c8;
+      raw_load<IN_BF16>(rw[u], base, idx);
+      rw_ok |= (hist || (t >= 0 && t < T)) ? (1u << u) : 0u;
+    };
+    auto load_g = [&](int tt) {
+      const int t = min(cl + r.tau0 + tt, T - 1);
+      raw_load<IN_BF16>(gr[tt], p.g, ((size_t)b * T + t) * H * DK + (size_t)h * DK + c8);
+      gr_ok |= (r.tau0 + tt < nv) ? (1u << tt) : 0u;
+    };
+    if (r.role == 1) {
+#pragma unroll
+      for (int u = 0; u < TBK + 3; ++u) load_raw(u);
+#pragma unroll
+      for (int tt = 0; tt < TBK; ++tt) load_g(tt);
+    } else if (r.role >= 0) {
+#pragma unroll
+      for (int u = 0; u < TBQ + 3; ++u) load_raw(u);
+      if (r.role == 0) {
+#pragma unroll
+        for (int tt = 0; tt < TBQ; ++tt) load_g(tt);
+      }
+    }
+    if (tl < C) beta_v = load1<IN_BF16>(p.beta, ((size_t)b * T + cl + min(tl, nv - 1)) * H + h);
+  };
+
+  if (nchunks > 0) issue_loads(0);
+
   for (int ci = 0; ci < nchunks; ++ci) {
     const int c0 = ci * C;
     const int n_valid = min(C, T - c0);
@@ -631,68 +737,32 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const int lane = tid & 63;
     const int gq = lane >> 4;   // lane group (0..3)
     const int li = lane & 15;   // index within the group
-    const Item it = make_item<DK, DV>(p, h, tid);
+    const Role it = make_role(tid);
     const int c8 = 8 * it.oct;
-    const int tau0 = it.tb * TBS;
+    const int tau0 = it.tau0;
 
-    // ---- all global loads of the chunk, issued up front ---------------------
-    // raw q/k/v tokens tau0-3 .. tau0+TBS-1 of the item's octet, g for q/k
-    // items and beta; they stay packed until used
-    Raw8<IN_BF16> rw[TBS + 3];
-    Raw8<IN_BF16> gr[TBS];
-    float beta_v = 0.f;
-    // Loads are unconditional from clamped, in-bounds addresses; which of them
-    // hold real data is kept in bit masks applied when the values are used.  A
-    // load under a branch, or a register overwritten after a load, would make
-    // the compiler wait for it right away and serialise every load.
-    uint32_t rw_ok = 0, gr_ok = 0;
-    if (it.role >= 0) {
-      const size_t cch = (size_t)H * NC;
-      const bool has_hist = p.conv_in != nullptr;
-#pragma unroll
-      for (int u = 0; u < TBS + 3; ++u) {
-        const int t = c0 + tau0 - 3 + u;
-        const bool hist = t < 0 && has_hist;
-        const int tc = min(max(t, 0), T - 1);
-        const void* base = hist ? p.conv_in : it.src;
-        const size_t idx = hist ? ((size_t)b * 3 + (3 + t)) * cch + it.chb
-                                : ((size_t)b * T + tc) * H * it.D + (size_t)h * it.D + c8;
-        raw_load<IN_BF16>(rw[u], base, idx);
-        rw_ok |= (hist || (t >= 0 && t < T)) ? (1u << u) : 0u;
-      }
-      if (it.role < 2) {
-#pragma unroll
-        for (int tt = 0; tt < TBS; ++tt) {
-          const int t = min(c0 + tau0 + tt, T - 1);
-          raw_load<IN_BF16>(gr[tt], p.g, ((size_t)b * T + t) * H * DK + (size_t)h * DK + c8);
-          gr_ok |= (tau0 + tt < n_valid) ? (1u << tt) : 0u;
-        }
-      }
-    }
-    if (tid < C) beta_v = load1<IN_BF16>(p.beta, ((size_t)b * T + c0 + min(tid, n_valid - 1)) * H + h);
-
-    // ---- stage 1a: beta, token-block sums of g ------------------------------
+    // ---- stage 1a: beta, sums of g over the k blocks --------------------------
     if (tid < 4) sFlag[tid] = 0;
     if (tid < C) sBeta[tid] = tid < n_valid ? beta_v : 0.f;
-    if (it.role == 0) {
+    if (it.role == 1) {
       float s8[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
-      for (int tt = 0; tt < TBS; ++tt) {
+      for (int tt = 0; tt < TBK; ++tt) {
         float gv[8];
         raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s8[e] += gv[e];
       }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sBtot[it.tb * DK + c8 + e] = s8[e];
+      for (int e = 0; e < 8; ++e) sBtot[it.blk * DK + c8 + e] = s8[e];
     }
     lds_barrier();
 
-    // ---- stage 1b: per-tile decay scalars (q-item threads, one job per tb) ---
-    //   tb <  NT : rho_tb = G before tile tb, e^{rho_tb}, e^{rho_tb - rho_b} (b < tb)
-    //   tb == NT : G_C and e^{G_C}
-    //   tb == NT+1 : fp16 range check of the tile spans
-    if (it.role == 0 && it.tb < NT + 2) {
+    // ---- stage 1b: per-tile decay scalars (k-item threads, one job per block) -
+    //   blk <  NT : rho_blk = G before tile blk, e^{rho_blk}, e^{rho_blk - rho_b} (b < blk)
+    //   blk == NT : G_C and e^{G_C}
+    //   blk == NT+1 : fp16 range check of the tile spans
+    if (it.role == 1 && it.blk < NT + 2) {
       float rho[NT + 1][8];  // rho[a] = sum of the blocks before tile a; rho[NT] = G_C
 #pragma unroll
       for (int e = 0; e < 8; ++e) rho[0][e] = 0.f;
@@ -702,14 +772,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 8; ++e) {
           float sa = rho[a][e];
 #pragma unroll
-          for (int q = a * (16 / TBS); q < (a + 1) * (16 / TBS); ++q) sa += sBtot[q * DK + c8 + e];
+          for (int q = a * BPT; q < (a + 1) * BPT; ++q) sa += sBtot[q * DK + c8 + e];
           rho[a + 1][e] = sa;
         }
       }
-      if (it.tb < NT) {
+      if (it.blk < NT) {
 #pragma unroll
         for (int a = 0; a < NT; ++a) {
-          if (a != it.tb) continue;  // static indices into rho[][]
+          if (a != it.blk) continue;  // static indices into rho[][]
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             sRho[a * DK + c8 + e] = rho[a][e];
@@ -720,7 +790,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sFab[off_pair(a, bb) * DK + c8 + e] = fast_exp(rho[a][e] - rho[bb][e]);
         }
-      } else if (it.tb == NT) {
+      } else if (it.blk == NT) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           sGC[c8 + e] = rho[NT][e];
@@ -735,10 +805,11 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         if (mx > kF16SpanMax) atomicOr(&sFlag[0], 1);
       }
     }
-    // each q / k thread: G just before its token block
+    // each q / k thread: G just before its first token
     float G[8] = {0, 0, 0, 0, 0, 0, 0, 0};
     if (it.role == 0 || it.role == 1) {
-      for (int q = 0; q < it.tb; ++q)
+      const int nb = tau0 / TBK;  // k blocks before tau0
+      for (int q = 0; q < nb; ++q)
 #pragma unroll
         for (int e = 0; e < 8; ++e) G[e] += sBtot[q * DK + c8 + e];
     }
@@ -746,62 +817,65 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     const bool bfAP = sFlag[0] != 0;  // decay-weighted operands in bf16 for this chunk
 
     // ---- stage 1c: conv + SiLU + L2, then the decay-scaled operands -----------
-    if (it.role >= 0) {
-      const int bt = tau0 >> 4;  // 16-token tile of this block
-      const float* rho = sRho + bt * DK + c8;    // per-tile scalars, read from LDS on use
-      const float* erho = sERho + bt * DK + c8;
-      const float* gcv = sGC + c8;
-#pragma unroll
-      for (int tt = 0; tt < TBS; ++tt) {
-        const int tau = tau0 + tt;
-        const bool valid = tau < n_valid;
-        float x[8];
-        {
-          // raw tokens tau-3 .. tau, unpacked per channel; taps from LDS
-          const bool ok0 = (rw_ok >> tt) & 1u, ok1 = (rw_ok >> (tt + 1)) & 1u;
-          const bool ok2 = (rw_ok >> (tt + 2)) & 1u, ok3 = (rw_ok >> (tt + 3)) & 1u;
-          const float4* cw = sCW + (it.role == 0 ? 0 : it.role == 1 ? DK : 2 * DK) + c8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float4 wv = cw[e];
-            const float a = wv.x * (ok0 ? raw_elem<IN_BF16>(rw[tt], e) : 0.f) +
-                            wv.y * (ok1 ? raw_elem<IN_BF16>(rw[tt + 1], e) : 0.f) +
-                            wv.z * (ok2 ? raw_elem<IN_BF16>(rw[tt + 2], e) : 0.f) +
-                            wv.w * (ok3 ? raw_elem<IN_BF16>(rw[tt + 3], e) : 0.f);
-            x[e] = valid ? siluf_(a) : 0.f;
-          }
-        }
-        if (it.role == 2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) st_op<F32>(sVT + tidx<C, LDT>(c8 + e, tau), x[e], false);
-          continue;
-        }
-        l2norm<DK>(x, it.role == 0 ? fast_rsq((float)DK) : 1.0f);
-        float gv[8];
-        raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
-        float er[8], rowv[8], xg[8];
+    auto token_work = [&](int tt, bool is_k) {
+      const int tau = tau0 + tt;
+      const bool valid = tau < n_valid;
+      float x[8];
+      {
+        // raw tokens tau-3 .. tau, unpacked per channel; taps from LDS
+        const bool ok0 = (rw_ok >> tt) & 1u, ok1 = (rw_ok >> (tt + 1)) & 1u;
+        const bool ok2 = (rw_ok >> (tt + 2)) & 1u, ok3 = (rw_ok >> (tt + 3)) & 1u;
+        const float4* cw = sCW + (it.role == 0 ? 0 : it.role == 1 ? DK : 2 * DK) + c8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          G[e] += gv[e];
-          er[e] = fast_exp(G[e] - rho[e]);  // e^{G - rho_bt} <= 1
-          rowv[e] = x[e] * er[e];
-          xg[e] = rowv[e] * erho[e];         // x e^{G}
-        }
-        if (it.role == 0) {
-          st_op8<F32>(sQR + tau * LDR + c8, rowv, bfAP);
-          st_op8<F32>(sQG + tau * LDR + c8, xg, false);
-        } else {
-          st_op8<F32>(sKR + tau * LDR + c8, rowv, bfAP);
-          float cv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            cv[e] = x[e] * fast_rcp(er[e]);  // k e^{rho_bt - G}
-            st_op<F32>(sKGT + tidx<C, LDT>(c8 + e, tau), xg[e], false);
-            st_op<F32>(sKBT + tidx<C, LDT>(c8 + e, tau), x[e] * fast_exp(gcv[e] - G[e]), false);
-          }
-          st_op8<F32>(sKC + tau * LDR + c8, cv, bfAP);
+          const float4 wv = cw[e];
+          const float a = wv.x * (ok0 ? raw_elem<IN_BF16>(rw[tt], e) : 0.f) +
+                          wv.y * (ok1 ? raw_elem<IN_BF16>(rw[tt + 1], e) : 0.f) +
+                          wv.z * (ok2 ? raw_elem<IN_BF16>(rw[tt + 2], e) : 0.f) +
+                          wv.w * (ok3 ? raw_elem<IN_BF16>(rw[tt + 3], e) : 0.f);
+          x[e] = valid ? siluf_(a) : 0.f;
         }
       }
+      if (it.role == 2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) st_op<F32>(sVT + tidx<C, LDT>(c8 + e, tau), x[e], false);
+        return;
+      }
+      l2norm<DK>(x, is_k ? 1.0f : fast_rsq((float)DK));
+      const int bt = tau >> 4;  // 16-token tile
+      const float* rho = sRho + bt * DK + c8;
+      const float* erho = sERho + bt * DK + c8;
+      float gv[8];
+      raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
+      float er[8], rowv[8], xg[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        G[e] += gv[e];
+        er[e] = fast_exp(G[e] - rho[e]);  // e^{G - rho_bt} <= 1
+        rowv[e] = x[e] * er[e];
+        xg[e] = rowv[e] * erho[e];         // x e^{G}
+      }
+      if (!is_k) {
+        st_op8<F32>(sQR + tau * LDR + c8, rowv, bfAP);
+        st_op8<F32>(sQG + tau * LDR + c8, xg, false);
+      } else {
+        st_op8<F32>(sKR + tau * LDR + c8, rowv, bfAP);
+        float cv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          cv[e] = x[e] * fast_rcp(er[e]);  // k e^{rho_bt - G}
+          st_op<F32>(sKGT + tidx<C, LDT>(c8 + e, tau), xg[e], false);
+          st_op<F32>(sKBT + tidx<C, LDT>(c8 + e, tau), x[e] * fast_exp(sGC[c8 + e] - G[e]), false);
+        }
+        st_op8<F32>(sKC + tau * LDR + c8, cv, bfAP);
+      }
+    };
+    if (it.role == 1) {
+#pragma unroll
+      for (int tt = 0; tt < TBK; ++tt) token_work(tt, true);
+    } else if (it.role >= 0) {
+#pragma unroll
+      for (int tt = 0; tt < TBQ; ++tt) token_work(tt, false);
     }
     lds_barrier();
 
@@ -969,18 +1043,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     lds_barrier();
 
     // ---- stage 5: inter-chunk products and state update (own dv columns) -----
-    // gate values for the epilogue, loaded now so their latency hides behind
-    // the products below
-    float gpre[NT][4];
-    if (owns_cols) {
+    // gate octets of this thread's epilogue items, loaded now so their latency
+    // hides behind the products below
+    Raw8<IN_BF16> gt[EPT];
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * gq + r;
-          // rows past the end are never stored; load a valid row for them
-          gpre[rt][r] = load1<IN_BF16>(p.gate, (((size_t)b * T + c0 + min(row, n_valid - 1)) * H + h) * DV + col0 + li);
-        }
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + kThreads * j;
+      const int tok = min(e / (DV / 8), n_valid - 1);
+      raw_load<IN_BF16>(gt[j], p.gate, (((size_t)b * T + c0 + tok) * H + h) * DV + 8 * (e % (DV / 8)));
     }
     f4 O[NT];
     if (owns_cols) {
@@ -1054,33 +1124,37 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         }
         S[t] = s;
       }
-      // partial sums of squares of each output row over this wave's 16 columns
+      // stage O for the epilogue (A / T space is dead by now)
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float ss = group_sum<16>(O[rt][r] * O[rt][r]);
-          if (li == 0) sSsq[wave * C + 16 * rt + 4 * gq + r] = ss;
-        }
+        for (int r = 0; r < 4; ++r) sO[(16 * rt + 4 * gq + r) * L::LDO + col0 + li] = O[rt][r];
     }
+    // the next chunk's loads fly while the epilogue runs
+    if (ci + 1 < nchunks) issue_loads(ci + 1);
     lds_barrier();
 
     // ---- epilogue: head-wise RMSNorm * sigmoid(gate) ----------------------------
-    if (owns_cols) {
+    // item (token, dv octet): DV/8 consecutive lanes hold one token's row
 #pragma unroll
-      for (int rt = 0; rt < NT; ++rt)
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + kThreads * j;
+      if (e < NE) {
+        const int tok = e / (DV / 8), oc = e % (DV / 8);
+        const float4 a4 = *reinterpret_cast<const float4*>(sO + tok * L::LDO + 8 * oc);
+        const float4 b4 = *reinterpret_cast<const float4*>(sO + tok * L::LDO + 8 * oc + 4);
+        float x[8] = {a4.x, a4.y, a4.z, a4.w, b4.x, b4.y, b4.z, b4.w};
+        float ss = 0.f;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int row = 16 * rt + 4 * gq + r;
-          if (row < n_valid) {
-            float ss = 0.f;
+        for (int q = 0; q < 8; ++q) ss += x[q] * x[q];
+        ss = group_sum<DV / 8>(ss);
+        const float rs = fast_rsq(ss * (1.0f / DV) + kRmsEps);
+        float gv[8];
+        raw_unpack<IN_BF16>(gt[j], gv);
 #pragma unroll
-            for (int w2 = 0; w2 < CTV; ++w2) ss += sSsq[w2 * C + row];
-            const float rs = fast_rsq(ss * (1.0f / DV) + kRmsEps);
-            const size_t oi = (((size_t)b * T + c0 + row) * H + h) * DV + col0 + li;
-            store1<OUT_BF16>(p.o, oi, O[rt][r] * rs * sigmoidf_(gpre[rt][r]));
-          }
-        }
+        for (int q = 0; q < 8; ++q) x[q] = x[q] * rs * sigmoidf_(gv[q]);
+        if (tok < n_valid) store8<OUT_BF16>(p.o, (((size_t)b * T + c0 + tok) * H + h) * DV + 8 * oc, x);
+      }
     }
     lds_barrier();  // LDS is rewritten by the next chunk
   }
