@@ -1,0 +1,132 @@
+"""The full-size workloads on the GPU, checked on sampled heads against the oracle.
+
+Inputs are drawn on the device (kda_synth's torch backend) at the exact
+shapes the benchmark times; the GPU runs the whole workload; the sampled
+(batch, head) pairs' inputs are copied to the host and the fp64 oracle
+recomputes those pairs over the full sequence.  The tolerance RMS is taken
+over the sampled pairs' outputs.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import kda_synth as syn
+from gpu_util import TOL_BF16, assert_rms_close, need_gpu
+
+# The decode step keeps every operand in fp32 (no reduced-precision matrix
+# operands), so after 1000 steps its error stays at fp32 rounding level
+# (measured ~4e-6 of the RMS); 1e-4 leaves a 25x margin.
+TOL_DECODE = 1e-4
+
+pytestmark = pytest.mark.gpu
+
+
+def head_inputs(dev, h, H, dk, dv, b=0, decode_pair=None):
+    """Host inputs of one (b, h) pair as a B=1, H=1 problem (conv_w rows of head h)."""
+    torch, _ = need_gpu()
+    b = 0 if decode_pair is not None else b
+    if decode_pair is None:
+        sl = {x: dev[x][b:b + 1, :, h:h + 1].contiguous() for x in ("q", "k", "v", "g", "gate")}
+        sl["beta"] = dev["beta"][b:b + 1, :, h:h + 1].contiguous()
+    else:
+        n = decode_pair
+        sl = {x: dev[x][:, n:n + 1, h:h + 1].transpose(0, 1).contiguous() for x in ("q", "k", "v", "g", "gate")}
+        sl["beta"] = dev["beta"][:, n:n + 1, h:h + 1].transpose(0, 1).contiguous()
+    chans = np.concatenate([h * dk + np.arange(dk), H * dk + h * dk + np.arange(dk),
+                            2 * H * dk + h * dv + np.arange(dv)])
+    idx = torch.as_tensor(chans, device=dev["conv_w"].device)
+    out = {x: syn.torch_to_np(t) for x, t in sl.items()}
+    out["conv_w"] = syn.torch_to_np(dev["conv_w"][idx].contiguous())
+    return out, idx
+
+
+def _compare_heads(oracle_mod, picks, per_head_inputs, what, tol):
+    """picks: per pair (o [T,dv], S_T [dk,dv]) from the GPU; the oracle reruns each pair."""
+    o_ref, o_got, s_ref, s_got = [], [], [], []
+    for (got_o, got_s), inp in zip(picks, per_head_inputs):
+        r = oracle_mod.prefill(inp)
+        o_ref.append(r["o"][0])
+        s_ref.append(r["S_T"][0])
+        o_got.append(got_o)
+        s_got.append(got_s)
+    assert_rms_close(np.stack(o_got), np.stack(o_ref), tol, f"{what} o")
+    assert_rms_close(np.stack(s_got), np.stack(s_ref), tol, f"{what} S_T")
+
+
+def test_k3width_prefill_sampled_heads(oracle_mod):
+    """B1 T65536 H96 d128, S0 ~ N(0, 0.01^2), chunk 64: four sampled heads over all
+    65536 tokens."""
+    torch, kda = need_gpu()
+    w = syn.WORKLOADS["k3width"]
+    dev = syn.prefill_inputs_torch(w, "cuda")
+    o, S_T, _ = kda.prefill(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"],
+                            dev["gate"], S0=dev["S0"], chunk=w.chunk)
+    torch.cuda.synchronize()
+    heads = sorted(np.random.default_rng(7).choice(w.H, 4, replace=False).tolist())
+    print(f"  sampled heads {heads}", flush=True)
+    picks, inputs = [], []
+    for h in heads:
+        inp, _ = head_inputs(dev, h, w.H, w.dk, w.dv)
+        inp["S0"] = dev["S0"][0:1, h:h + 1].cpu().numpy()
+        inputs.append(inp)
+        picks.append((o[0, :, h].float().cpu().numpy(), S_T[0, h].cpu().numpy()))
+    _compare_heads(oracle_mod, picks, inputs, "k3width", TOL_BF16)
+
+
+@pytest.mark.timeout(900)
+def test_long1m_prefill_sampled_head(oracle_mod):
+    """B1 T1048576 H96 d128 in 16 segments of 65536 with S and the conv history
+    carried in place: one sampled head over all 1M tokens."""
+    torch, kda = need_gpu()
+    w = syn.WORKLOADS["long1m"]
+    dev = syn.prefill_inputs_torch(w, "cuda")
+    seg = w.T // w.segments
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device="cuda")
+    S = torch.zeros((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device="cuda")
+    conv = torch.zeros((w.B, 3, w.cch), dtype=torch.bfloat16, device="cuda")
+    for s in range(w.segments):
+        t0, t1 = s * seg, (s + 1) * seg
+        kda.prefill(dev["q"][:, t0:t1], dev["k"][:, t0:t1], dev["v"][:, t0:t1], dev["conv_w"],
+                    dev["g"][:, t0:t1], dev["beta"][:, t0:t1], dev["gate"][:, t0:t1], S0=S, conv_in=conv,
+                    chunk=w.chunk, o=o[:, t0:t1], S_T=S, conv_out=conv)
+    torch.cuda.synchronize()
+    h = int(np.random.default_rng(11).integers(w.H))
+    print(f"  sampled head {h}", flush=True)
+    inp, idx = head_inputs(dev, h, w.H, w.dk, w.dv)
+    got = (o[0, :, h].cpu().numpy(), S[0, h].cpu().numpy())
+    conv_np = syn.torch_to_np(conv[0][:, idx].contiguous())
+    del o, dev
+    torch.cuda.empty_cache()
+    r = oracle_mod.prefill(inp)
+    assert_rms_close(got[0], r["o"][0], TOL_BF16, "long1m o")
+    assert_rms_close(got[1], r["S_T"][0], TOL_BF16, "long1m S_T")
+    assert np.array_equal(conv_np, syn.bf16_bits_from_f64(r["conv_out"][0])), "long1m conv history"
+
+
+def test_decode_1000_steps_sampled_pairs(oracle_mod):
+    """256 sequences x 96 heads, 1000 consecutive decode steps; eight sampled
+    (sequence, head) pairs over all steps (the oracle runs them as one
+    1000-token prefill, which its pins show equals 1000 decode steps)."""
+    torch, kda = need_gpu()
+    w = syn.WORKLOADS["decode"]
+    steps = w.steps
+    dev = syn.decode_inputs_torch(w, "cuda", steps)
+    S0 = dev["S"].clone()
+    conv0 = dev["conv_state"].clone()
+    o = torch.empty((steps, w.B, w.H, w.dv), dtype=torch.float32, device="cuda")
+    for s in range(steps):
+        kda.decode_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["conv_w"], dev["g"][s], dev["beta"][s],
+                        dev["gate"][s], dev["S"], dev["conv_state"], o=o[s])
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(13)
+    pairs = [(int(rng.integers(w.B)), int(rng.integers(w.H))) for _ in range(8)]
+    print(f"  sampled pairs {pairs}", flush=True)
+    picks, inputs = [], []
+    for n, h in pairs:
+        inp, idx = head_inputs(dev, h, w.H, w.dk, w.dv, decode_pair=n)
+        inp["S0"] = S0[n:n + 1, h:h + 1].cpu().numpy()
+        inp["conv_in"] = syn.torch_to_np(conv0[n:n + 1][:, :, idx].contiguous())
+        inputs.append(inp)
+        picks.append((o[:, n, h].cpu().numpy(), dev["S"][n, h].cpu().numpy()))
+    _compare_heads(oracle_mod, picks, inputs, "decode x1000", TOL_DECODE)
