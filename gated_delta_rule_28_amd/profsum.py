@@ -1,0 +1,166 @@
+"""Summaries of rocprofv3 CSV output for the KDA kernels.
+
+    python -m gated_delta_rule_28_amd.profsum stats  KERNEL_STATS_CSV --cmd "..." --out FILE.md
+    python -m gated_delta_rule_28_amd.profsum traffic FETCH_CSV WRITE_CSV --cmd "..." --out FILE.md
+    python -m gated_delta_rule_28_amd.profsum counters COUNTER_CSV --cmd "..." --out FILE.md
+
+`traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
+counters read for the largest `neg` elementwise kernel in the run (bench.py
+--calibrate: 1 GiB read + 1 GiB written), and records the HBM bytes per launch
+of each KDA kernel, with a hash of the kernel's source, in profiles/traffic.json
+(bench.py reports them only while the source is unchanged).
+"""
+from __future__ import annotations
+
+import argparse
+import collections
+import csv
+import hashlib
+import json
+import os
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+CSRC = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc")
+
+# kernel key -> (substring of the demangled name, source file)
+KERNELS = {
+    "prefill_kernel": ("prefill_kernel<64, 128, 128, true, false, false>", "kda_prefill.hip"),
+    "decode_kernel": ("decode_kernel<128, 128, true, false>", "kda_decode.hip"),
+}
+CALIB_BYTES = 1 << 30   # bytes read, and bytes written, by the calibration kernel
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _short(name, n=90):
+    name = name.replace("kda::(anonymous namespace)::", "")
+    return name if len(name) <= n else name[:n - 3] + "..."
+
+
+def stats(path, cmd, out):
+    rows = list(csv.DictReader(open(path)))
+    rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
+    lines = ["# Kernel time (rocprofv3 --kernel-trace --stats)", "", "Command:", "",
+             "```", cmd, "```", "",
+             "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
+             "|---|---:|---:|---:|---:|---:|"]
+    for r in rows[:8]:
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def _per_kernel(path):
+    """kernel name -> counter name -> list of per-dispatch values; plus grid sizes."""
+    d = collections.defaultdict(lambda: collections.defaultdict(list))
+    grid = {}
+    for r in csv.DictReader(open(path)):
+        d[r["Kernel_Name"]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+        grid.setdefault((r["Kernel_Name"], r["Dispatch_Id"]), int(r["Grid_Size"]))
+    return d, grid
+
+
+def _calib(path, counter):
+    """Mean counter value of the largest-grid `neg` dispatches (the calibration kernel)."""
+    best, vals = -1, []
+    for r in csv.DictReader(open(path)):
+        if "neg_kernel" not in r["Kernel_Name"] or r["Counter_Name"] != counter:
+            continue
+        g = int(r["Grid_Size"])
+        if g > best:
+            best, vals = g, []
+        if g == best:
+            vals.append(float(r["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{path}: no calibration dispatch (run bench.py with --calibrate)")
+    return sum(vals) / len(vals)
+
+
+def _match(d, sub):
+    names = [n for n in d if sub in n]
+    return names[0] if names else None
+
+
+def traffic(fetch_csv, write_csv, cmd, out, json_out):
+    f_d, _ = _per_kernel(fetch_csv)
+    w_d, _ = _per_kernel(write_csv)
+    f_cal = _calib(fetch_csv, "FETCH_SIZE")
+    w_cal = _calib(write_csv, "WRITE_SIZE")
+    f_scale = (CALIB_BYTES / 1024) / f_cal
+    w_scale = (CALIB_BYTES / 1024) / w_cal
+    lines = ["# HBM traffic per launch (rocprofv3 --pmc FETCH_SIZE, then --pmc WRITE_SIZE)", "",
+             "Commands (one counter per run):", "", "```", cmd, "```", "",
+             f"Calibration: a `neg` elementwise kernel reading 1 GiB and writing 1 GiB reads as "
+             f"FETCH_SIZE {f_cal:.0f} KiB and WRITE_SIZE {w_cal:.0f} KiB, so the counters are scaled "
+             f"by {f_scale:.3f} (fetch) and {w_scale:.3f} (write).", "",
+             "| kernel | dispatches | FETCH_SIZE (KiB) | WRITE_SIZE (KiB) | HBM read (GB) | HBM write (GB) | total (GB) |",
+             "|---|---:|---:|---:|---:|---:|---:|"]
+    res = json.load(open(json_out)) if os.path.exists(json_out) else {}
+    for key, (sub, src) in KERNELS.items():
+        nf, nw = _match(f_d, sub), _match(w_d, sub)
+        if nf is None or nw is None:
+            continue
+        fv, wv = f_d[nf]["FETCH_SIZE"], w_d[nw]["WRITE_SIZE"]
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        rd, wr = fk * 1024 * f_scale, wk * 1024 * w_scale
+        lines.append(f"| `{_short(nf)}` | {len(fv)} | {fk:.0f} | {wk:.0f} | {rd / 1e9:.3f} | "
+                     f"{wr / 1e9:.3f} | {(rd + wr) / 1e9:.3f} |")
+        res[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                    "source_sha256_16": source_hash(os.path.join(CSRC, src)),
+                    "fetch_scale": f_scale, "write_scale": w_scale}
+    open(out, "w").write("\n".join(lines) + "\n")
+    json.dump(res, open(json_out, "w"), indent=1, sort_keys=True)
+
+
+def counters(path, cmd, out, simds=1024):
+    """Per-kernel means of the raw counters of one --pmc run, with the derived
+    utilisations that their definitions give (MFMA busy and VALU active cycles
+    over GPU-active cycles per SIMD / CU)."""
+    d, _ = _per_kernel(path)
+    lines = ["# Compute counters per dispatch (rocprofv3 --pmc)", "", "Command:", "", "```", cmd, "```", ""]
+    for key, (sub, _src) in KERNELS.items():
+        n = _match(d, sub)
+        if n is None:
+            continue
+        c = {k: sum(v) / len(v) for k, v in d[n].items()}
+        lines.append(f"## `{_short(n)}`")
+        lines.append("")
+        for k in sorted(c):
+            lines.append(f"- {k}: {c[k]:.6g}")
+        gui = c.get("GRBM_GUI_ACTIVE")
+        if gui:
+            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
+                lines.append(f"- MFMA busy: {100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.2f}% of SIMD cycles")
+            if "SQ_ACTIVE_INST_VALU" in c:
+                lines.append(f"- VALU active: {100 * c['SQ_ACTIVE_INST_VALU'] / (gui * simds / 4):.2f}% of CU cycles")
+        lines.append("")
+    open(out, "w").write("\n".join(lines) + "\n")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="what", required=True)
+    a = sub.add_parser("stats")
+    a.add_argument("csv")
+    b = sub.add_parser("traffic")
+    b.add_argument("fetch_csv")
+    b.add_argument("write_csv")
+    b.add_argument("--json", default=os.path.join(ROOT, "profiles", "traffic.json"))
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    for p in (a, b, c):
+        p.add_argument("--cmd", required=True)
+        p.add_argument("--out", required=True)
+    args = ap.parse_args()
+    if args.what == "stats":
+        stats(args.csv, args.cmd, args.out)
+    elif args.what == "traffic":
+        traffic(args.fetch_csv, args.write_csv, args.cmd, args.out, args.json)
+    else:
+        counters(args.csv, args.cmd, args.out)
+
+
+if __name__ == "__main__":
+    main()
