@@ -6,6 +6,7 @@ memory and the current stream.  If the library is missing the import still
 works, but every call raises (there is no fallback implementation).
 
     o, S_T, conv_out = prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64)
+    nbytes = workspace_bytes(B, T, H, dk, dv, chunk, in_dtype)  # what prefill allocates
     o = decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state)   # S, conv_state in place
     qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
 """
@@ -14,7 +15,7 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["prefill", "decode_step", "prep", "library_path", "lib", "KDAError",
+__all__ = ["prefill", "decode_step", "prep", "workspace_bytes", "library_path", "lib", "KDAError",
            "KDA_F32", "KDA_BF16", "PrefillArgs", "DecodeArgs", "PrepArgs"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
@@ -72,6 +73,8 @@ def lib():
         L.kda_prefill.restype = ctypes.c_int
         L.kda_prefill_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
         L.kda_prefill_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_prefill_workspace_min_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
+        L.kda_prefill_workspace_min_bytes.restype = ctypes.c_size_t
         L.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         L.kda_decode_step.restype = ctypes.c_int
         L.kda_prep.argtypes = [ctypes.POINTER(PrepArgs), _P]
@@ -120,11 +123,14 @@ def _stream(device):
 
 
 def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out_dtype=None,
-            o=None, S_T=None, conv_out=None, want_state=True, want_conv=True):
+            o=None, S_T=None, conv_out=None, want_state=True, want_conv=True, workspace="auto"):
     """Chunkwise KDA prefill (kda_prefill).  Shapes as in include/kda.h.
 
     Returns (o, S_T, conv_out); S_T / conv_out are None when not wanted.
     Passing S_T=S0 / conv_out=conv_in updates the carry in place.
+    workspace: "auto" allocates what kda_prefill_workspace_bytes asks for (the
+    two-kernel path where the sizes have one), None passes no workspace (the
+    single-kernel path), or a uint8 device tensor to use.
     """
     torch = _torch()
     B, T, H, dk = q.shape
@@ -140,8 +146,23 @@ def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out
     a = PrefillArgs(B, T, H, dk, dv, chunk, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
                     _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in),
                     _ptr(o), _ptr(S_T), _ptr(conv_out), None, 0)
+    if isinstance(workspace, str):
+        if workspace != "auto":
+            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+        nbytes = lib().kda_prefill_workspace_bytes(ctypes.byref(a))
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
+    if workspace is not None:
+        a.workspace = _ptr(workspace)
+        a.workspace_bytes = workspace.numel() * workspace.element_size()
     _check("kda_prefill", lib().kda_prefill(ctypes.byref(a), _stream(dev)))
     return o, S_T, conv_out
+
+
+def workspace_bytes(B, T, H, dk, dv, chunk=64, in_dtype=KDA_BF16, out_dtype=KDA_F32, minimum=False):
+    """kda_prefill_workspace_bytes (or _min_bytes) for these sizes (0: no two-kernel path)."""
+    a = PrefillArgs(B, T, H, dk, dv, chunk, in_dtype, out_dtype)
+    fn = lib().kda_prefill_workspace_min_bytes if minimum else lib().kda_prefill_workspace_bytes
+    return int(fn(ctypes.byref(a)))
 
 
 def decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype=None):

@@ -78,8 +78,15 @@ const char* kda_status_string(int code) {
 }
 
 size_t kda_prefill_workspace_bytes(const kda_prefill_args* a) {
-  (void)a;
-  return 0;  // the fused prefill keeps every intermediate on chip
+  if (a == nullptr) return 0;
+  if (kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype) != KDA_OK) return 0;
+  return kda::prefill_split_workspace_bytes(*a);
+}
+
+size_t kda_prefill_workspace_min_bytes(const kda_prefill_args* a) {
+  if (a == nullptr) return 0;
+  if (kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype) != KDA_OK) return 0;
+  return kda::prefill_split_workspace_min_bytes(*a);
 }
 
 int kda_prefill(const kda_prefill_args* a, void* stream) {
@@ -98,9 +105,10 @@ int kda_prefill(const kda_prefill_args* a, void* stream) {
   REQUIRE_A16(a->S_T); REQUIRE_A16(a->conv_in); REQUIRE_A16(a->conv_out);
   if (a->beta != nullptr && !kda::aligned_n(a->beta, kda::esize(a->in_dtype)))
     return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
-  if (a->workspace_bytes < kda_prefill_workspace_bytes(a))
+  REQUIRE_A16(a->workspace);
+  if (a->workspace != nullptr && a->workspace_bytes < kda_prefill_workspace_min_bytes(a))
     return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", a->workspace_bytes,
-                kda_prefill_workspace_bytes(a));
+                kda_prefill_workspace_min_bytes(a));
   if (a->T == 0 && a->S_T == nullptr && a->conv_out == nullptr) return KDA_OK;
   return kda::launch_prefill(*a, reinterpret_cast<hipStream_t>(stream));
 }

@@ -109,6 +109,14 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Workgroup barrier that waits only for this wave's LDS operations, not for its
+// outstanding global loads (which __syncthreads' release fence would drain):
+// loads issued for later stages stay in flight across it.  The memory clobber
+// keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---- matrix core -----------------------------------------------------------------
 __device__ __forceinline__ f4 mma_f16(const half8& a, const half8& b, const f4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);

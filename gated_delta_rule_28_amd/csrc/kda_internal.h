@@ -13,6 +13,12 @@ int launch_decode(const kda_decode_args& a, hipStream_t s);
 int launch_prefill(const kda_prefill_args& a, hipStream_t s);
 int launch_prep(const kda_prep_args& a, hipStream_t s);
 
+// Two-kernel prefill (bf16 inputs, chunk 64, dk = dv = 128) through a workspace.
+bool prefill_split_eligible(const kda_prefill_args& a);
+size_t prefill_split_workspace_bytes(const kda_prefill_args& a);
+size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a);
+int launch_prefill_split(const kda_prefill_args& a, hipStream_t s);
+
 // Set the calling thread's last-error text (printf-style).
 void set_error(const char* fmt, ...);
 

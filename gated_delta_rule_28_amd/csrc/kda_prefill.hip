@@ -96,14 +96,6 @@ __device__ __forceinline__ int opaque(int x) {
   return x;
 }
 
-// Workgroup barrier that waits only for this wave's LDS operations, not for its
-// outstanding global loads (which __syncthreads' release fence would drain):
-// loads issued for later stages stay in flight across it.  The memory clobber
-// keeps the compiler from moving LDS accesses across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
-
 // 8 consecutive activations kept packed in registers until used.
 template <bool BF16> struct Raw8;
 template <> struct Raw8<true> { uint4 u; };
@@ -1282,6 +1274,7 @@ int prep_d(const kda_prep_args& a, hipStream_t s) {
 }  // namespace
 
 int launch_prefill(const kda_prefill_args& a, hipStream_t s) {
+  if (a.workspace != nullptr && prefill_split_eligible(a)) return launch_prefill_split(a, s);
   if (a.dk != a.dv) {
     set_error("prefill: dk (%d) != dv (%d) is not instantiated", a.dk, a.dv);
     return KDA_E_UNSUPPORTED;

@@ -1,0 +1,970 @@
+// kda_prefill_split.hip -- two-kernel chunkwise KDA prefill for bf16 inputs,
+// chunk 64, dk = dv = 128 (the K3 head shape: "Kimi K3.1 Pro vs gpt-oss-120b"
+// and "Gemma 4 31B vs Kimi K3", component tables, row "Gated DeltaNet / KDA").
+//
+// Same algebra as the single-kernel path in kda_prefill.hip (the chunkwise
+// WY / UT form of the KDA recurrence, 16-token decay tiles), split where the
+// work stops being parallel:
+//
+//   intra_chunk_kernel  one workgroup (4 waves) per (b, h, chunk); every chunk
+//     of every head at once.  Conv + SiLU + L2 normalisation + chunk-local
+//     cumulative sum of g, then A, P, T = (I + A)^-1, W = T diag(beta) (K e^G)
+//     and U~ = T diag(beta) V on the matrix cores.
+//   inter_chunk_kernel  one workgroup (4 waves) per (b, h) walks the chunks in
+//     order: U = U~ - W S, O = (Q e^G) S + P U, S <- e^{G_C} S + (K e^{G_C-G})^T U
+//     with the fp32 state in registers, then RMSNorm * sigmoid(gate).
+//
+// The first kernel hands the second its operands in a workspace laid out as
+// matrix-core fragments (64 lanes x 16 bytes, lane order), so every operand
+// moves with one coalesced 16-byte access per lane and reaches the matrix
+// cores with no conversion or transpose.
+//
+// Lane layout in intra_chunk_kernel: wave a owns the 16-token tile a; lane
+// (g = lane / 16, i = lane % 16) holds token 16a + i and channels
+// 32k + 8g + 0..7 of each 32-channel step k.  That is the operand layout of
+// the 16x16x32 matrix-core instruction for products contracting over channels
+// (A, P), the causal conv reads the previous tokens from lanes i-1 .. i-3
+// (DPP row shifts), and the cumulative sum of g is a DPP scan over the row.
+//
+// State row order: the state lives in registers as accumulator tiles whose
+// row 4g + e of tile m is used directly as the contraction index of the next
+// products.  Register row R = 16m + r holds channel perm_row(R), chosen so the
+// eight contraction values of lane group g in step k are channels
+// 32k + 8g + 0..7: W and Q e^G fragments are then plain row-major pieces.
+// S0 and S_T stay in natural order in memory.
+//
+// Precision as in kda_prefill.hip: fp16 operands (bf16 for the decay-weighted
+// A / P operands of a chunk in which some 16-token tile decays by more than
+// e^8), fp32 accumulation, fp32 state and output.  U~ is passed between the
+// kernels in fp32: U = U~ - W S can cancel (the state already predicts v), and
+// an fp16 U~ then puts the state's error at about 2e-2 of its RMS on some heads.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kC = 64;          // chunk
+constexpr int kD = 128;         // dk = dv
+constexpr int kNCh = 3 * kD;    // conv channels of one head (q | k | v)
+constexpr float kSpanF16 = 8.0f;
+
+// ---- workspace block of one (b, h, chunk), bytes ------------------------------
+constexpr int kFrag = 1024;                  // 64 lanes x 16 bytes
+constexpr int WS_W = 0;                      // -W     fragments (rt, k)        16
+constexpr int WS_QG = WS_W + 16 * kFrag;     // Q e^G  fragments (rt, k)        16
+constexpr int WS_KB = WS_QG + 16 * kFrag;    // (K e^{G_C-G})^T fragments (m, k') 16
+constexpr int WS_P = WS_KB + 16 * kFrag;     // P      fragments (rt, k'), k' <= rt/2: 6
+constexpr int WS_GAM = WS_P + 6 * kFrag;     // e^{G_C} in state row order, 128 fp32 (+pad)
+constexpr int WS_STAGE = WS_GAM + 2 * kFrag; // bytes the second kernel stages through LDS (56 KiB)
+constexpr int WS_U = WS_STAGE;               // U~ (rt, w): 64 lanes x 8 fp32   32 KiB
+constexpr int WS_CHUNK = WS_U + 32 * kFrag;  // 88 KiB per chunk
+constexpr size_t kSlabBytesMax = (size_t)16 << 30;  // workspace cap for the chunk blocks
+
+__device__ __forceinline__ int p_frag(int rt, int kp) { return rt < 2 ? rt : 2 * rt - 2 + kp; }
+
+// channel held by register row R of the state
+__device__ __forceinline__ int perm_row(int R) {
+  const int m = R >> 4, r = R & 15;
+  return 32 * (m >> 1) + 8 * (r >> 2) + 4 * (m & 1) + (r & 3);
+}
+
+struct SplitParams {
+  int B, T, H;
+  int c_begin, n_chunks;  // chunks [c_begin, c_begin + n_chunks) of this launch
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  const float* S_in;      // state entering chunk c_begin, or null (zeros)
+  const void* conv_in;
+  void* o;
+  float* S_out;           // state after the last chunk, or null
+  void* conv_out;         // raw conv history after the last token, or null
+  unsigned char* ws;      // n_chunks * B * H chunk blocks
+};
+
+// DPP move inside rows of 16 lanes; lanes with no source or outside the bank
+// mask read 0.
+template <int CTRL, int BANK>
+__device__ __forceinline__ float dppf(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, BANK, false));
+}
+
+__device__ __forceinline__ float bf16_at(const uint4& u, int e) {
+  const uint32_t w = e < 2 ? u.x : e < 4 ? u.y : e < 6 ? u.z : u.w;
+  return (e & 1) ? bf16hi(w) : bf16lo(w);
+}
+
+__device__ __forceinline__ half8 to_half8(const float* x) {
+  half8 h;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
+  return h;
+}
+
+// Eight fp32 values as a matrix-core operand: fp16, or bf16 bits when `bf`.
+__device__ __forceinline__ half8 to_op8(const float* x, bool bf) {
+  if (bf) {
+    bf16x8 t;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) t[e] = (__bf16)x[e];
+    return __builtin_bit_cast(half8, t);
+  }
+  return to_half8(x);
+}
+
+__device__ __forceinline__ void from_op8(const half8& h, bool bf, float* x) {
+  if (bf) {
+    const bf16x8 t = __builtin_bit_cast(bf16x8, h);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)t[e];
+  } else {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
+  }
+}
+
+__device__ __forceinline__ f4 mma16(const half8& a, const half8& b, const f4& c, bool bf) {
+  if (bf) return mma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
+  return mma_f16(a, b, c);
+}
+
+// Causal depthwise conv (kernel 4) + SiLU of one tensor for this lane's token
+// and 32 channels.  `cur` are the raw token's channels, `hal` the raw values of
+// the token 16 positions earlier (only lanes 13..15 carry them: the three
+// tokens before the tile), `cw` this lane's taps (32k + e indexing).
+__device__ __forceinline__ void conv_silu(const uint4 (&cur)[4], const uint4 (&hal)[4], bool hok, bool valid,
+                                          const float4* cw, float (&x)[32]) {
+#pragma unroll
+  for (int kp = 0; kp < 4; ++kp) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float xc = bf16_at(cur[kp], e);
+      const float y = hok ? bf16_at(hal[kp], e) : 0.f;
+      const float4 w = cw[32 * kp + e];
+      // token t-j: lane i-j of the row, or for i < j the halo in lane 16+i-j
+      // (a rotation written to lanes 0..3 only)
+      float a = w.w * xc;
+      a += w.z * (dppf<0x111, 0xF>(xc) + dppf<0x121, 0x1>(y));
+      a += w.y * (dppf<0x112, 0xF>(xc) + dppf<0x122, 0x1>(y));
+      a += w.x * (dppf<0x113, 0xF>(xc) + dppf<0x123, 0x1>(y));
+      x[8 * kp + e] = valid ? siluf_(a) : 0.f;
+    }
+  }
+}
+
+// Scale x[32] to unit L2 norm over the token's 128 channels (held by lanes
+// i, i+16, i+32, i+48), times `extra`.
+__device__ __forceinline__ void l2norm128(float (&x)[32], float extra) {
+  float ss = 0.f;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) ss += x[c] * x[c];
+  ss += __shfl_xor(ss, 16, 64);
+  ss += __shfl_xor(ss, 32, 64);
+  const float r = fast_rsq(ss + kL2Eps) * extra;
+#pragma unroll
+  for (int c = 0; c < 32; ++c) x[c] *= r;
+}
+
+__device__ __forceinline__ void ld8f(const float* p, float* x) {
+  const float4 a = *reinterpret_cast<const float4*>(p);
+  const float4 b = *reinterpret_cast<const float4*>(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+
+// transposed [channel][token] fp16 arrays: 64 tokens + 8 pad per row, 8-token
+// granules XOR-swizzled by row / 16 to spread the per-token stores over banks
+constexpr int kLDT = kC + 8;
+__device__ __forceinline__ int tix(int row, int tok) {
+  return row * kLDT + ((((tok >> 3) ^ (row >> 4)) & 7) << 3) + (tok & 7);
+}
+
+// ---- LDS of intra_chunk_kernel (bytes) ----------------------------------------
+struct ALds {
+  static constexpr int LDA = kC + 4;                  // fp32 A / T rows
+  static constexpr int LDB = kC + 8;                  // fp16 T diag(beta) rows
+  static constexpr int TOT = 0;                       // [4][128] fp32: sum of g over each tile
+  static constexpr int BETA = TOT + 4 * kD * 4;       // [64] fp32
+  static constexpr int FLAG = BETA + kC * 4;          // int
+  static constexpr int R1 = FLAG + 16;
+  // R1, until the A / P products: column operands of tiles 0..2 and (K e^{G_C-G})^T
+  static constexpr int CC = R1;                       // [3 tiles][4 k] fragments
+  static constexpr int KBT = CC + 3 * 4 * kFrag;      // [128][kLDT] fp16
+  static constexpr int R1_A = KBT + kD * kLDT * 2;
+  // R1, afterwards: A (then T on its diagonal blocks) and T diag(beta)
+  static constexpr int AM = R1;                       // [64][LDA] fp32
+  static constexpr int TB = AM + kC * LDA * 4;        // [64][LDB] fp16
+  static constexpr int R1_B = TB + kC * LDB * 2;
+  static constexpr int R2 = ((R1_A > R1_B ? R1_A : R1_B) + 15) / 16 * 16;
+  // R2, until the A / P products: conv taps and per-channel decay factors
+  static constexpr int CW = R2;                       // [384] float4
+  static constexpr int ERHO = CW + kNCh * 16;         // [4][128] e^{rho_a}
+  static constexpr int ETOT = ERHO + 4 * kD * 4;      // [4][128] e^{tot_a}
+  static constexpr int EKB = ETOT + 4 * kD * 4;       // [4][128] e^{G_C - rho_a - tot_a}
+  static constexpr int FOFF = EKB + 4 * kD * 4;       // [3][128] e^{rho_a - rho_{b+1}}: (2,0) (3,0) (3,1)
+  static constexpr int R2_A = FOFF + 3 * kD * 4;
+  // R2, afterwards: (K e^G)^T and V^T
+  static constexpr int KGT = R2;                      // [128][kLDT] fp16
+  static constexpr int VT = KGT + kD * kLDT * 2;      // [128][kLDT] fp16
+  static constexpr int R2_B = VT + kD * kLDT * 2;
+  static constexpr int BYTES = R2_A > R2_B ? R2_A : R2_B;
+};
+
+// ---------------------------------------------------------------------------
+// intra_chunk_kernel: grid n_chunks * B * H, block 256
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
+  using L = ALds;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  float* sTot = reinterpret_cast<float*>(smem + L::TOT);
+  float* sBeta = reinterpret_cast<float*>(smem + L::BETA);
+  int* sFlag = reinterpret_cast<int*>(smem + L::FLAG);
+  float4* sCW = reinterpret_cast<float4*>(smem + L::CW);
+  float* sERho = reinterpret_cast<float*>(smem + L::ERHO);
+  float* sETot = reinterpret_cast<float*>(smem + L::ETOT);
+  float* sEKb = reinterpret_cast<float*>(smem + L::EKB);
+  float* sFoff = reinterpret_cast<float*>(smem + L::FOFF);
+  half8* sCC = reinterpret_cast<half8*>(smem + L::CC);
+  _Float16* sKBT = reinterpret_cast<_Float16*>(smem + L::KBT);
+  float* sAM = reinterpret_cast<float*>(smem + L::AM);
+  _Float16* sTB = reinterpret_cast<_Float16*>(smem + L::TB);
+  _Float16* sKGT = reinterpret_cast<_Float16*>(smem + L::KGT);
+  _Float16* sVT = reinterpret_cast<_Float16*>(smem + L::VT);
+  constexpr int LDA = L::LDA, LDB = L::LDB;
+
+  const int H = p.H, T = p.T;
+  const int nc = p.n_chunks;
+  const int bh = blockIdx.x / nc;
+  const int c = p.c_begin + (blockIdx.x - bh * nc);
+  const int b = bh / H, h = bh - b * H;
+  const int c0 = c * kC;
+  const int n_valid = min(kC, T - c0);
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // token tile
+  const int lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int tok = 16 * wave + i;
+  const bool valid = tok < n_valid;
+  unsigned char* wsb = p.ws + (size_t)blockIdx.x * WS_CHUNK;
+
+  // ---- loads: this lane's token (clamped) and the tile's halo ------------------
+  const size_t cch = (size_t)H * kNCh;
+  const size_t row = ((size_t)b * T + c0 + min(tok, n_valid - 1)) * H + h;
+  const int th = c0 + 16 * wave - 16 + max(i, 13);  // lanes 13..15: tokens before the tile
+  const bool h_in = th >= 0;
+  const bool hok = i >= 13 && (h_in || p.conv_in != nullptr);
+  const size_t hrow = ((size_t)b * T + min(max(th, 0), T - 1)) * H + h;
+  const size_t hist = ((size_t)b * 3 + (3 + max(th, -3))) * cch;  // conv_in row when th < 0
+  const bool from_hist = !h_in && p.conv_in != nullptr;
+  uint4 rq[4], rk[4], rv[4], rg[4], hq[4], hk[4], hv[4];
+  {
+    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
+    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(p.k);
+    const uint16_t* v16 = reinterpret_cast<const uint16_t*>(p.v);
+    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.g);
+    const uint16_t* ci16 = reinterpret_cast<const uint16_t*>(p.conv_in);
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      const int cl = 32 * kp + 8 * g;
+      rq[kp] = *reinterpret_cast<const uint4*>(q16 + row * kD + cl);
+      rk[kp] = *reinterpret_cast<const uint4*>(k16 + row * kD + cl);
+      rv[kp] = *reinterpret_cast<const uint4*>(v16 + row * kD + cl);
+      rg[kp] = *reinterpret_cast<const uint4*>(g16 + row * kD + cl);
+      const uint16_t* pq = from_hist ? ci16 + hist + (size_t)h * kD + cl : q16 + hrow * kD + cl;
+      const uint16_t* pk = from_hist ? ci16 + hist + (size_t)H * kD + (size_t)h * kD + cl : k16 + hrow * kD + cl;
+      const uint16_t* pv = from_hist ? ci16 + hist + (size_t)2 * H * kD + (size_t)h * kD + cl : v16 + hrow * kD + cl;
+      hq[kp] = *reinterpret_cast<const uint4*>(pq);
+      hk[kp] = *reinterpret_cast<const uint4*>(pk);
+      hv[kp] = *reinterpret_cast<const uint4*>(pv);
+    }
+  }
+  const float beta_v = valid ? bf16_to_f(reinterpret_cast<const uint16_t*>(p.beta)[row]) : 0.f;
+
+  // conv taps of this head, per-token beta, fp16-range flag
+  for (int ch = tid; ch < kNCh; ch += 256) {
+    const size_t gch = ch < kD ? (size_t)h * kD + ch
+                     : ch < 2 * kD ? (size_t)H * kD + (size_t)h * kD + (ch - kD)
+                                   : (size_t)2 * H * kD + (size_t)h * kD + (ch - 2 * kD);
+    sCW[ch] = *reinterpret_cast<const float4*>(p.conv_w + gch * 4);
+  }
+  if (g == 0) sBeta[tok] = beta_v;
+  if (tid == 0) *sFlag = 0;
+
+  // ---- chunk-local cumulative sum of g: DPP scan over the tile, tile sums -----
+  float s[32];
+#pragma unroll
+  for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      float x = valid ? bf16_at(rg[kp], e) : 0.f;
+      x += dppf<0x111, 0xF>(x);
+      x += dppf<0x112, 0xF>(x);
+      x += dppf<0x114, 0xF>(x);
+      x += dppf<0x118, 0xF>(x);
+      s[8 * kp + e] = x;   // G - rho_a at this token
+    }
+  if (i == 15) {
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      float* d = sTot + wave * kD + 32 * kp + 8 * g;
+      *reinterpret_cast<float4*>(d) = make_float4(s[8 * kp], s[8 * kp + 1], s[8 * kp + 2], s[8 * kp + 3]);
+      *reinterpret_cast<float4*>(d + 4) = make_float4(s[8 * kp + 4], s[8 * kp + 5], s[8 * kp + 6], s[8 * kp + 7]);
+    }
+  }
+  lds_barrier();
+
+  // ---- per-channel decay factors of the chunk -----------------------------------
+  {
+    bool wide = false;
+    for (int idx = tid; idx < 4 * kD; idx += 256) {
+      const int a = idx >> 7, ch = idx & (kD - 1);
+      const float t0 = sTot[ch], t1 = sTot[kD + ch], t2 = sTot[2 * kD + ch], t3 = sTot[3 * kD + ch];
+      const float ta = a == 0 ? t0 : a == 1 ? t1 : a == 2 ? t2 : t3;
+      const float rho = (a > 0 ? t0 : 0.f) + (a > 1 ? t1 : 0.f) + (a > 2 ? t2 : 0.f);
+      const float gc = t0 + t1 + t2 + t3;
+      sERho[idx] = fast_exp(rho);
+      sETot[idx] = fast_exp(ta);
+      sEKb[idx] = fast_exp(gc - rho - ta);
+      wide |= -ta > kSpanF16;
+    }
+    for (int idx = tid; idx < 3 * kD; idx += 256) {
+      const int pr = idx >> 7, ch = idx & (kD - 1);
+      const float t1 = sTot[kD + ch], t2 = sTot[2 * kD + ch];
+      sFoff[idx] = fast_exp(pr == 0 ? t1 : pr == 1 ? t1 + t2 : t2);
+    }
+    if (tid < kD) {
+      const int ch = perm_row(tid);
+      const float gc = sTot[ch] + sTot[kD + ch] + sTot[2 * kD + ch] + sTot[3 * kD + ch];
+      reinterpret_cast<float*>(wsb + WS_GAM)[tid] = fast_exp(gc);
+    }
+    if (__any(wide) && lane == 0) atomicOr(sFlag, 1);
+  }
+  lds_barrier();
+  const bool bf = *sFlag != 0;  // decay-weighted A / P operands in bf16 for this chunk
+
+  // e^{G - rho_a} of this lane's channels
+  float E[32];
+#pragma unroll
+  for (int c2 = 0; c2 < 32; ++c2) E[c2] = fast_exp(s[c2]);
+
+  // ---- q: rows of P and Q e^G -----------------------------------------------------
+  half8 QrowF[4];
+  {
+    float x[32];
+    conv_silu(rq, hq, hok, valid, sCW + 8 * g, x);
+    l2norm128(x, fast_rsq((float)kD));
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      float er[8], qr[8], qg[8];
+      ld8f(sERho + wave * kD + 32 * kp + 8 * g, er);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        qr[e] = x[8 * kp + e] * E[8 * kp + e];
+        qg[e] = qr[e] * er[e];
+      }
+      QrowF[kp] = to_op8(qr, bf);
+      *reinterpret_cast<half8*>(wsb + WS_QG + ((wave * 4 + kp) * 64 + lane) * 16) = to_half8(qg);
+    }
+  }
+  // ---- k: rows and columns of A / P, K e^G, K e^{G_C - G} ---------------------------
+  half8 KrowF[4], CdiagF[4], KGf[4];
+  {
+    float x[32];
+    conv_silu(rk, hk, hok, valid, sCW + kD + 8 * g, x);
+    l2norm128(x, 1.0f);
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      float er[8], et[8], ek[8], kr[8], cd[8], cc[8], kb[8], kg[8];
+      ld8f(sERho + wave * kD + 32 * kp + 8 * g, er);
+      ld8f(sETot + wave * kD + 32 * kp + 8 * g, et);
+      ld8f(sEKb + wave * kD + 32 * kp + 8 * g, ek);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xe = x[8 * kp + e], ee = E[8 * kp + e];
+        kr[e] = xe * ee;                 // k e^{G - rho_a}
+        cd[e] = xe * fast_rcp(ee);       // k e^{rho_a - G}
+        cc[e] = cd[e] * et[e];           // k e^{rho_{a+1} - G}
+        kb[e] = cc[e] * ek[e];           // k e^{G_C - G}
+        kg[e] = kr[e] * er[e];           // k e^{G}
+      }
+      KrowF[kp] = to_op8(kr, bf);
+      CdiagF[kp] = to_op8(cd, bf);
+      KGf[kp] = to_half8(kg);
+      if (wave < 3) sCC[(wave * 4 + kp) * 64 + lane] = to_op8(cc, bf);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sKBT[tix(32 * kp + 8 * g + e, tok)] = (_Float16)kb[e];
+    }
+  }
+  // ---- v -----------------------------------------------------------------------------
+  half8 Vf[4];
+  {
+    float x[32];
+    conv_silu(rv, hv, hok, valid, sCW + 2 * kD + 8 * g, x);
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) Vf[kp] = to_half8(x + 8 * kp);
+  }
+  lds_barrier();
+
+  // ---- A^T and P^T blocks (b, a), b <= a: D[j][r] = sum_c col_b[j][c] row_a[r][c] --
+  // The column operand of an earlier tile b is scaled by e^{rho_a - rho_{b+1}} <= 1
+  // (exact 1 for b = a - 1).
+  f4 accA[4], accP[4];
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    accA[bb] = f4{0.f, 0.f, 0.f, 0.f};
+    accP[bb] = f4{0.f, 0.f, 0.f, 0.f};
+    if (bb <= wave) {
+#pragma unroll
+      for (int kp = 0; kp < 4; ++kp) {
+        half8 fa;
+        if (bb == wave) {
+          fa = CdiagF[kp];
+        } else {
+          fa = sCC[(bb * 4 + kp) * 64 + lane];
+          if (bb < wave - 1) {
+            const int pr = wave == 2 ? 0 : 1 + bb;
+            float xv[8], fv[8];
+            from_op8(fa, bf, xv);
+            ld8f(sFoff + pr * kD + 32 * kp + 8 * g, fv);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) xv[e] *= fv[e];
+            fa = to_op8(xv, bf);
+          }
+        }
+        accA[bb] = mma16(fa, KrowF[kp], accA[bb], bf);
+        accP[bb] = mma16(fa, QrowF[kp], accP[bb], bf);
+      }
+    }
+  }
+  // (K e^{G_C - G})^T fragments (m, k'): wave w takes m = 2w, 2w + 1
+#pragma unroll
+  for (int mm = 0; mm < 2; ++mm) {
+    const int m = 2 * wave + mm;
+    const int rw = perm_row(16 * m + i);
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      const half4 lo = *reinterpret_cast<const half4*>(sKBT + tix(rw, 32 * kp + 4 * g));
+      const half4 hi = *reinterpret_cast<const half4*>(sKBT + tix(rw, 32 * kp + 16 + 4 * g));
+      *reinterpret_cast<half8*>(wsb + WS_KB + ((m * 2 + kp) * 64 + lane) * 16) =
+          half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
+  }
+  lds_barrier();  // R1 and R2 are rewritten from here on
+
+  // A (beta_r scaled, strictly lower) into AM; P fragments to the workspace
+#pragma unroll
+  for (int bb = 0; bb < 4; ++bb) {
+    if (bb <= wave) {
+      float4 w4;
+      w4.x = 16 * bb + 4 * g + 0 < tok ? beta_v * accA[bb][0] : 0.f;
+      w4.y = 16 * bb + 4 * g + 1 < tok ? beta_v * accA[bb][1] : 0.f;
+      w4.z = 16 * bb + 4 * g + 2 < tok ? beta_v * accA[bb][2] : 0.f;
+      w4.w = 16 * bb + 4 * g + 3 < tok ? beta_v * accA[bb][3] : 0.f;
+      *reinterpret_cast<float4*>(sAM + tok * LDA + 16 * bb + 4 * g) = w4;
+    }
+  }
+#pragma unroll
+  for (int kp = 0; kp < 2; ++kp) {
+    if (2 * kp <= wave) {
+      float pv[8];
+#pragma unroll
+      for (int sh = 0; sh < 2; ++sh) {
+        const int bb = 2 * kp + sh;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float v = bb == 0 ? accP[0][e] : bb == 1 ? accP[1][e] : bb == 2 ? accP[2][e] : accP[3][e];
+          pv[4 * sh + e] = (bb <= wave && 16 * bb + 4 * g + e <= tok) ? v : 0.f;
+        }
+      }
+      *reinterpret_cast<half8*>(wsb + WS_P + (p_frag(wave, kp) * 64 + lane) * 16) = to_half8(pv);
+    }
+  }
+  // (K e^G)^T and V^T for the W / U~ products
+#pragma unroll
+  for (int kp = 0; kp < 4; ++kp)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      sKGT[tix(32 * kp + 8 * g + e, tok)] = KGf[kp][e];
+      sVT[tix(32 * kp + 8 * g + e, tok)] = Vf[kp][e];
+    }
+  lds_barrier();
+
+  // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution --------------
+  // wave 0, lane = (block g, column i); T_aa replaces A_aa in AM
+  if (wave == 0) {
+    const int a = g, j = i;
+    float col[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      float s0 = 0.f, s1 = 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) {
+        const float t = sAM[(16 * a + r) * LDA + 16 * a + m] * col[m];
+        if (m & 1) s1 += t; else s0 += t;
+      }
+      col[r] = r == j ? 1.f : (r > j ? -(s0 + s1) : 0.f);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sAM[(16 * a + r) * LDA + 16 * a + j] = col[r];
+  }
+  lds_barrier();
+  // off-diagonal blocks, wave bb = block column (fp32 matrix cores):
+  //   T_ab = -T_aa sum_{m=b}^{a-1} A_am T_mb, a = b+1 .. 3; stored as T diag(beta) in fp16.
+  // Wave 3 writes the diagonal blocks of T diag(beta) and the zero blocks the
+  // W / U~ products read.
+  if (wave < 3) {
+    const int bb = wave;
+    const float bcol = sBeta[16 * bb + i];
+    f4 Tcol[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) Tcol[0][e] = sAM[(16 * bb + 4 * g + e) * LDA + 16 * bb + i];
+#pragma unroll
+    for (int d = 1; d < 4; ++d) {
+      const int a = bb + d;
+      if (a < 4) {
+        f4 X = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int md = 0; md < d; ++md) {
+          const int m = bb + md;
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4)
+            X = __builtin_amdgcn_mfma_f32_16x16x4f32(sAM[(16 * a + i) * LDA + 16 * m + 4 * g + s4], Tcol[md][s4], X,
+                                                     0, 0, 0);
+        }
+        f4 Y = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4)
+          Y = __builtin_amdgcn_mfma_f32_16x16x4f32(sAM[(16 * a + i) * LDA + 16 * a + 4 * g + s4], X[s4], Y, 0, 0, 0);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          Tcol[d][e] = -Y[e];
+          sTB[(16 * a + 4 * g + e) * LDB + 16 * bb + i] = (_Float16)(-Y[e] * bcol);
+        }
+      }
+    }
+  } else {
+    for (int idx = lane; idx < 4 * 256; idx += 64) {
+      const int a = idx >> 8, r = (idx >> 4) & 15, cc = idx & 15;
+      sTB[(16 * a + r) * LDB + 16 * a + cc] =
+          (_Float16)(sAM[(16 * a + r) * LDA + 16 * a + cc] * sBeta[16 * a + cc]);
+    }
+    for (int idx = lane; idx < 2 * 256; idx += 64) {
+      const int a = 2 * (idx >> 8), r = (idx >> 4) & 15, cc = idx & 15;  // blocks (0,1), (2,3)
+      sTB[(16 * a + r) * LDB + 16 * (a + 1) + cc] = (_Float16)0.f;
+    }
+  }
+  lds_barrier();
+
+  // ---- W^T = (K e^G)^T (T diag(beta))^T and U~ = T diag(beta) V -------------------
+  // wave w: state rows 16(2w + s) + r (channels 32w + 8g + 4s + r) of W^T and
+  // dv column tiles 2w + s of U~.
+  f4 accW[2][4], accU[2][4];
+#pragma unroll
+  for (int sh = 0; sh < 2; ++sh)
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      accW[sh][rt] = f4{0.f, 0.f, 0.f, 0.f};
+      accU[sh][rt] = f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+    for (int kp = 0; kp < 2; ++kp) {
+      if (2 * kp <= rt) {
+        const half8 tb = *reinterpret_cast<const half8*>(sTB + (16 * rt + i) * LDB + 32 * kp + 8 * g);
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh) {
+          const int mc = 2 * wave + sh;
+          const half8 kg = *reinterpret_cast<const half8*>(sKGT + tix(perm_row(16 * mc + i), 32 * kp + 8 * g));
+          accW[sh][rt] = mma_f16(kg, tb, accW[sh][rt]);
+          const half8 vv = *reinterpret_cast<const half8*>(sVT + tix(16 * mc + i, 32 * kp + 8 * g));
+          accU[sh][rt] = mma_f16(tb, vv, accU[sh][rt]);
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const float wv[8] = {-accW[0][rt][0], -accW[0][rt][1], -accW[0][rt][2], -accW[0][rt][3],
+                         -accW[1][rt][0], -accW[1][rt][1], -accW[1][rt][2], -accW[1][rt][3]};
+    *reinterpret_cast<half8*>(wsb + WS_W + ((rt * 4 + wave) * 64 + lane) * 16) = to_half8(wv);
+    float4* up = reinterpret_cast<float4*>(wsb + WS_U + ((rt * 4 + wave) * 64 + lane) * 32);
+    up[0] = make_float4(accU[0][rt][0], accU[0][rt][1], accU[0][rt][2], accU[0][rt][3]);
+    up[1] = make_float4(accU[1][rt][0], accU[1][rt][1], accU[1][rt][2], accU[1][rt][3]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// inter_chunk_kernel: grid B * H, block 512 (8 waves), one workgroup per (b, h)
+//
+//   waves 0..3 ("math"): wave w owns dv columns 32w .. 32w+31 and the state
+//     columns with them; per chunk it runs U = U~ - W S, O = (Q e^G) S + P U and
+//     S <- e^{G_C} S + (K e^{G_C-G})^T U on the matrix cores and leaves O in LDS.
+//   waves 4..7 ("epilogue"): wave 4 + r takes token tile r of the previous
+//     chunk's O: RMSNorm over its rows * sigmoid(gate), stores; and copies the
+//     next chunk's operands into LDS.  O passes through LDS in fp16: it
+//     is only normalised and gated afterwards, so its rounding (2^-11 relative)
+//     stays far below the tolerance.
+// The epilogue of chunk j-1 runs beside the products of chunk j.  Two barriers
+// per chunk: B1 (chunk j's operands have landed; O(j-1) is complete) and B2
+// (the epilogue waves have read O(j-1), so the math waves may overwrite it).
+// ---------------------------------------------------------------------------
+constexpr int kStageQ = WS_STAGE / kFrag / 4;  // fragments each copying wave moves per chunk
+static_assert(WS_STAGE % (4 * kFrag) == 0, "staged part must split evenly over four waves");
+constexpr int B_O = 2 * WS_STAGE;              // two staging buffers, then O: [rt][w][lane][8] fp16
+constexpr int B_BYTES = B_O + 16 * kFrag;      // 128 KiB
+static_assert(B_BYTES <= 160 * 1024, "inter-chunk LDS exceeds 160 KiB");
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Copy one chunk's staged operands (56 fragments of 1 KiB) from the workspace
+// into an LDS buffer with direct-to-LDS loads (no registers): wave w moves
+// fragments w, w + 4, ...; lane l's 16 bytes land at offset 16 l of the
+// fragment.  Completion is tracked by the vector memory counter only, so the
+// consumer waits with s_waitcnt vmcnt(0) and a barrier.
+__device__ __forceinline__ void stage_dma(const unsigned char* chunk, unsigned char* buf, int w, int lane) {
+#pragma unroll
+  for (int q = 0; q < kStageQ; ++q) {
+    const int f = w + 4 * q;
+    __builtin_amdgcn_global_load_lds(chunk + f * kFrag + lane * 16, (lds_void*)(buf + f * kFrag), 16, 0, 0);
+  }
+}
+
+template <bool OUT_BF16>
+__global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int H = p.H, T = p.T;
+  const int bh = blockIdx.x;
+  const int b = bh / H, h = bh - b * H;
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const bool math = wave < 4;
+  const int w = wave & 3;
+  const int lane = tid & 63, g = lane >> 4, i = lane & 15;
+  const int nc = p.n_chunks;
+  const unsigned char* wsh = p.ws + (size_t)bh * nc * WS_CHUNK;
+  const int col0 = 32 * w;
+  half8* sO = reinterpret_cast<half8*>(smem + B_O);
+
+  // math waves: S[m][ct] element e = S[channel perm_row(16m + 4g + e)][col0 + 16ct + i]
+  f4 S[8][2];
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+#pragma unroll
+    for (int ct = 0; ct < 2; ++ct) S[m][ct] = f4{0.f, 0.f, 0.f, 0.f};
+  if (math) {
+    if (p.S_in != nullptr) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            S[m][ct][e] = p.S_in[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i];
+    }
+  } else if (nc > 0) {
+    stage_dma(wsh, smem, w, lane);
+  }
+
+  // Two loops with the same barriers, one per role, so that the state is live
+  // only in the math waves' loop.
+  // B1 (top of each iteration): chunk j's operands are in LDS (the copying
+  // waves waited for their copies), O(j-1) is complete, and nobody reads the
+  // buffer copied next.
+  if (math) {
+    // U~ of this wave's columns, loaded one chunk ahead (C layout)
+    float4 utn[4][2];
+    if (nc > 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const float4* up = reinterpret_cast<const float4*>(wsh + WS_U + ((rt * 4 + w) * 64 + lane) * 32);
+        utn[rt][0] = up[0];
+        utn[rt][1] = up[1];
+      }
+    }
+    for (int j = 0; j <= nc; ++j) {
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();  // B1
+      f4 O[4][2], U[4][2];
+      const unsigned char* sb = smem + (j & 1) * WS_STAGE;
+      if (j < nc) {
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            U[rt][ct] = f4{utn[rt][ct].x, utn[rt][ct].y, utn[rt][ct].z, utn[rt][ct].w};
+            O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+          }
+        if (j + 1 < nc) {
+          const unsigned char* wn = wsh + (size_t)(j + 1) * WS_CHUNK;
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const float4* up = reinterpret_cast<const float4*>(wn + WS_U + ((rt * 4 + w) * 64 + lane) * 32);
+            utn[rt][0] = up[0];
+            utn[rt][1] = up[1];
+          }
+        }
+        // U = U~ + (-W) S and (Q e^G) S, one 32-row step of S at a time: its B
+        // operands are rows 16(2k + s) + 4g + e, s = 0, 1
+#pragma unroll
+        for (int kp = 0; kp < 4; ++kp) {
+          half8 Sb[2];
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const float x[8] = {S[2 * kp][ct][0], S[2 * kp][ct][1], S[2 * kp][ct][2], S[2 * kp][ct][3],
+                                S[2 * kp + 1][ct][0], S[2 * kp + 1][ct][1], S[2 * kp + 1][ct][2], S[2 * kp + 1][ct][3]};
+            Sb[ct] = to_half8(x);
+          }
+#pragma unroll
+          for (int rt = 0; rt < 4; ++rt) {
+            const half8 wf = *reinterpret_cast<const half8*>(sb + WS_W + ((rt * 4 + kp) * 64 + lane) * 16);
+            const half8 qf = *reinterpret_cast<const half8*>(sb + WS_QG + ((rt * 4 + kp) * 64 + lane) * 16);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) {
+              U[rt][ct] = mma_f16(wf, Sb[ct], U[rt][ct]);
+              O[rt][ct] = mma_f16(qf, Sb[ct], O[rt][ct]);
+            }
+          }
+        }
+      }
+      lds_barrier();  // B2
+      if (j < nc) {
+        // U as B operands over tokens 32k' + 16s + 4g + e
+        half8 Ub[2][2];
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const float x[8] = {U[2 * kp][ct][0], U[2 * kp][ct][1], U[2 * kp][ct][2], U[2 * kp][ct][3],
+                                U[2 * kp + 1][ct][0], U[2 * kp + 1][ct][1], U[2 * kp + 1][ct][2], U[2 * kp + 1][ct][3]};
+            Ub[kp][ct] = to_half8(x);
+          }
+        // O += P U, then O to LDS for the epilogue waves
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp)
+            if (2 * kp <= rt) {
+              const half8 pf = *reinterpret_cast<const half8*>(sb + WS_P + (p_frag(rt, kp) * 64 + lane) * 16);
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) O[rt][ct] = mma_f16(pf, Ub[kp][ct], O[rt][ct]);
+            }
+          const float ox[8] = {O[rt][0][0], O[rt][0][1], O[rt][0][2], O[rt][0][3],
+                               O[rt][1][0], O[rt][1][1], O[rt][1][2], O[rt][1][3]};
+          sO[(rt * 4 + w) * 64 + lane] = to_half8(ox);
+        }
+        // S <- e^{G_C} S + (K e^{G_C - G})^T U
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+          const float4 gm = *reinterpret_cast<const float4*>(sb + WS_GAM + (16 * m + 4 * g) * 4);
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            S[m][ct][0] *= gm.x;
+            S[m][ct][1] *= gm.y;
+            S[m][ct][2] *= gm.z;
+            S[m][ct][3] *= gm.w;
+          }
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp) {
+            const half8 kf = *reinterpret_cast<const half8*>(sb + WS_KB + ((m * 2 + kp) * 64 + lane) * 16);
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) S[m][ct] = mma_f16(kf, Ub[kp][ct], S[m][ct]);
+          }
+        }
+      }
+    }
+  } else {
+    for (int j = 0; j <= nc; ++j) {
+      __builtin_amdgcn_s_waitcnt(0);
+      lds_barrier();  // B1
+      // ---- epilogue of chunk j-1: token tile r = w ----------------------------
+      // element [e][w'][ct]: token 16w + 4g + e, column 32w' + 16ct + i
+      float ov[4][4][2];
+      uint16_t gt[4][4][2];
+      const int c0 = (p.c_begin + j - 1) * kC;
+      const int nv = min(kC, T - c0);
+      if (j >= 1) {
+#pragma unroll
+        for (int w2 = 0; w2 < 4; ++w2) {
+          const half8 o8 = sO[(w * 4 + w2) * 64 + lane];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            ov[e][w2][0] = (float)o8[e];
+            ov[e][w2][1] = (float)o8[4 + e];
+          }
+        }
+        const uint16_t* gb = reinterpret_cast<const uint16_t*>(p.gate) + (((size_t)b * T + c0) * H + h) * kD + i;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint16_t* ge = gb + (size_t)min(16 * w + 4 * g + e, nv - 1) * H * kD;
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+            for (int ct = 0; ct < 2; ++ct) gt[e][w2][ct] = ge[32 * w2 + 16 * ct];
+        }
+      }
+      if (j + 1 < nc) stage_dma(wsh + (size_t)(j + 1) * WS_CHUNK, smem + ((j + 1) & 1) * WS_STAGE, w, lane);
+      lds_barrier();  // B2: O(j-1) is in registers
+      if (j >= 1) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float ss = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < 4; ++w2) ss += ov[e][w2][0] * ov[e][w2][0] + ov[e][w2][1] * ov[e][w2][1];
+          ss = group_sum<16>(ss);
+          const float rs = fast_rsq(ss * (1.0f / kD) + kRmsEps);
+          const int tk = 16 * w + 4 * g + e;
+          if (tk < nv) {
+            const size_t ob = (((size_t)b * T + c0 + tk) * H + h) * kD + i;
+#pragma unroll
+            for (int w2 = 0; w2 < 4; ++w2)
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct)
+                store1<OUT_BF16>(p.o, ob + 32 * w2 + 16 * ct,
+                                 ov[e][w2][ct] * rs * sigmoidf_(bf16_to_f(gt[e][w2][ct])));
+          }
+        }
+      }
+    }
+  }
+
+  // ---- state and conv history out -------------------------------------------------
+  if (math && p.S_out != nullptr) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+#pragma unroll
+      for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          p.S_out[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i] = S[m][ct][e];
+  }
+  if (p.conv_out != nullptr) {
+    const size_t cch = (size_t)H * kNCh;
+    for (int cl = tid; cl < kNCh; cl += 512) {
+      const void* src = cl < kD ? p.q : cl < 2 * kD ? p.k : p.v;
+      const int cc = cl & (kD - 1);
+      const size_t chb = cl < kD ? (size_t)h * kD + cc
+                       : cl < 2 * kD ? (size_t)H * kD + (size_t)h * kD + cc
+                                     : (size_t)2 * H * kD + (size_t)h * kD + cc;
+      float v3[3];
+#pragma unroll
+      for (int r = 0; r < 3; ++r) {
+        const int t = T - 3 + r;
+        if (t >= 0) v3[r] = load1<true>(src, (((size_t)b * T + t) * H + h) * kD + cc);
+        else if (p.conv_in != nullptr) v3[r] = load1<true>(p.conv_in, ((size_t)b * 3 + (3 + t)) * cch + chb);
+        else v3[r] = 0.f;
+      }
+#pragma unroll
+      for (int r = 0; r < 3; ++r) store1<true>(p.conv_out, ((size_t)b * 3 + r) * cch + chb, v3[r]);
+    }
+  }
+}
+
+// How the chunks of one call are split into launches ("slabs") that fit the
+// workspace: one slab when all chunk blocks fit (and stay under the cap), else
+// as many chunks per slab as fit next to a state carry buffer.
+struct SlabPlan {
+  int nchunks, per_slab, nslabs;
+  size_t chunk_bytes, carry_bytes;
+};
+
+size_t per_chunk_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * WS_CHUNK; }
+size_t carry_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * kD * kD * 4; }
+
+SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail) {
+  SlabPlan s{};
+  s.nchunks = (a.T + kC - 1) / kC;
+  const size_t pc = per_chunk_bytes(a);
+  const size_t room = avail < kSlabBytesMax ? avail : kSlabBytesMax;
+  if ((size_t)s.nchunks * pc <= room) {
+    s.per_slab = s.nchunks > 0 ? s.nchunks : 1;
+    s.nslabs = 1;
+    s.carry_bytes = 0;
+  } else {
+    const size_t cb = carry_bytes(a);
+    const size_t room2 = avail < kSlabBytesMax + cb ? avail : kSlabBytesMax + cb;
+    const size_t per = room2 > cb + pc ? (room2 - cb) / pc : 1;
+    const int most = (int)(per < (size_t)s.nchunks ? per : (size_t)s.nchunks);
+    s.nslabs = (s.nchunks + most - 1) / most;
+    s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;  // balanced slabs, no small tail
+    s.carry_bytes = s.nslabs > 1 ? cb : 0;
+  }
+  s.chunk_bytes = (size_t)s.per_slab * pc;
+  return s;
+}
+
+template <bool OB>
+int run_split(const kda_prefill_args& a, hipStream_t st) {
+  const SlabPlan pl = plan_slabs(a, a.workspace_bytes);
+  const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, ALds::BYTES);
+  const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&inter_chunk_kernel<OB>),
+                                            hipFuncAttributeMaxDynamicSharedMemorySize, B_BYTES);
+  if (e1 != hipSuccess || e2 != hipSuccess) {
+    set_error("prefill: hipFuncSetAttribute failed: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+    return KDA_E_HIP;
+  }
+  unsigned char* ws = static_cast<unsigned char*>(a.workspace);
+  float* carry = pl.carry_bytes ? reinterpret_cast<float*>(ws + pl.chunk_bytes) : nullptr;
+  for (int sl = 0; sl < pl.nslabs; ++sl) {
+    SplitParams p{};
+    p.B = a.B; p.T = a.T; p.H = a.H;
+    p.c_begin = sl * pl.per_slab;
+    p.n_chunks = pl.nchunks - p.c_begin < pl.per_slab ? pl.nchunks - p.c_begin : pl.per_slab;
+    if (p.n_chunks < 0) p.n_chunks = 0;
+    p.q = a.q; p.k = a.k; p.v = a.v; p.conv_w = a.conv_w; p.g = a.g; p.beta = a.beta; p.gate = a.gate;
+    const bool first = sl == 0, last = sl == pl.nslabs - 1;
+    p.S_in = first ? a.S0 : carry;
+    p.conv_in = a.conv_in;
+    p.o = a.o;
+    p.S_out = last ? a.S_T : carry;
+    p.conv_out = last ? a.conv_out : nullptr;
+    p.ws = ws;
+    if (p.n_chunks > 0) {
+      const size_t grid = (size_t)p.n_chunks * a.B * a.H;
+      hipLaunchKernelGGL(intra_chunk_kernel, dim3((unsigned)grid), dim3(256), ALds::BYTES, st, p);
+      const hipError_t e = hipGetLastError();
+      if (e != hipSuccess) {
+        set_error("prefill: intra-chunk launch failed: %s", hipGetErrorString(e));
+        return KDA_E_HIP;
+      }
+    }
+    hipLaunchKernelGGL((inter_chunk_kernel<OB>), dim3((unsigned)(a.B * a.H)), dim3(512), B_BYTES, st, p);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) {
+      set_error("prefill: inter-chunk launch failed: %s", hipGetErrorString(e));
+      return KDA_E_HIP;
+    }
+  }
+  return KDA_OK;
+}
+
+}  // namespace
+
+bool prefill_split_eligible(const kda_prefill_args& a) {
+  return a.in_dtype == KDA_BF16 && a.chunk == kC && a.dk == kD && a.dv == kD;
+}
+
+size_t prefill_split_workspace_bytes(const kda_prefill_args& a) {
+  if (!prefill_split_eligible(a)) return 0;
+  const SlabPlan pl = plan_slabs(a, ~(size_t)0);
+  return pl.chunk_bytes + pl.carry_bytes;
+}
+
+size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a) {
+  if (!prefill_split_eligible(a)) return 0;
+  const int nchunks = (a.T + kC - 1) / kC;
+  if (nchunks <= 1) return (size_t)nchunks * per_chunk_bytes(a);
+  return per_chunk_bytes(a) + carry_bytes(a);
+}
+
+int launch_prefill_split(const kda_prefill_args& a, hipStream_t s) {
+  return a.out_dtype == KDA_BF16 ? run_split<true>(a, s) : run_split<false>(a, s);
+}
+
+}  // namespace kda

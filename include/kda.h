@@ -62,8 +62,8 @@ enum {
   KDA_E_SHAPE = -2,       /* a size is out of range (negative, zero, too large)  */
   KDA_E_DTYPE = -3,       /* in_dtype / out_dtype not one of the enum values     */
   KDA_E_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
-  KDA_E_UNSUPPORTED = -5, /* dk, dv not in {16,32,64,128}, or chunk not in {16,32,64} */
-  KDA_E_WORKSPACE = -6,   /* workspace smaller than kda_prefill_workspace_bytes  */
+  KDA_E_UNSUPPORTED = -5, /* dk != dv, dk not in {16,32,64,128}, or chunk not in {16,32,64} */
+  KDA_E_WORKSPACE = -6,   /* workspace given but smaller than kda_prefill_workspace_min_bytes */
   KDA_E_HIP = -7          /* a HIP runtime call failed (text in kda_last_error)  */
 };
 
@@ -75,6 +75,18 @@ enum {
  * conv_out may alias conv_in, so a long sequence can be processed as
  * consecutive segments carrying both in place.  T = 0 is allowed (copies the
  * carry).  T need not be a multiple of `chunk`.
+ *
+ * Two execution paths, same results within the stated tolerance:
+ *  - workspace != NULL (kda_prefill_workspace_bytes, or at least
+ *    kda_prefill_workspace_min_bytes): for bf16 inputs
+ *    with chunk 64 and dk = dv = 128 the work runs as two kernels, one over
+ *    all chunks of all heads at once (prep and intra-chunk products) and one
+ *    per (b, h) walking the chunks (state recurrence and output), which meet
+ *    in the workspace.  For other sizes the workspace is unused.
+ *  - workspace == NULL: one kernel per (b, h) walks the chunks and keeps every
+ *    intermediate on chip (no device memory beyond the arguments).
+ * The library owns no device memory: the caller allocates the workspace and
+ * may reuse it once the call's work on `stream` has finished.
  */
 typedef struct kda_prefill_args {
   int B, T, H, dk, dv;
@@ -93,14 +105,23 @@ typedef struct kda_prefill_args {
   void* o;
   float* S_T;             /* may be NULL */
   void* conv_out;         /* may be NULL */
-  void* workspace;        /* may be NULL when the workspace size is 0 */
+  void* workspace;        /* NULL, or >= kda_prefill_workspace_min_bytes bytes, 16-byte aligned */
   size_t workspace_bytes;
 } kda_prefill_args;
 
 int kda_prefill(const kda_prefill_args* args, void* stream);
 
-/* Device scratch kda_prefill needs for these sizes (0 when none). */
+/* Device workspace the two-kernel path prefers for these sizes: 88 KiB per
+ * (b, h, chunk of 64 tokens), capped near 16 GiB (plus B*H*dk*dv*4 bytes to
+ * carry the state) by processing long sequences in slabs of chunks.  0 when
+ * the sizes have no two-kernel path or the arguments are invalid.  The fields
+ * B, T, H, dk, dv, chunk, in_dtype and out_dtype are read; pointers are not. */
 size_t kda_prefill_workspace_bytes(const kda_prefill_args* args);
+
+/* Smallest workspace the two-kernel path accepts (one chunk per slab): any size
+ * from this up to kda_prefill_workspace_bytes works, a smaller one in more
+ * slabs.  A non-NULL workspace below it is rejected with KDA_E_WORKSPACE. */
+size_t kda_prefill_workspace_min_bytes(const kda_prefill_args* args);
 
 /*
  * One decode step for N sequences of one new token each: the definition above

@@ -117,6 +117,42 @@ def test_prefill_null_args_and_empty(kda):
     assert L.kda_prefill_workspace_bytes(ctypes.byref(a)) == 0
 
 
+def test_prefill_workspace_sizes_and_check(kda):
+    """Workspace sizes (no device needed) and the too-small check, which runs
+    before anything is launched."""
+    L = kda.lib()
+    # sizes with a two-kernel path: bf16 inputs, chunk 64, dk = dv = 128
+    a = _prefill_args(kda, B=2, T=300, H=3, dk=128, dv=128, chunk=64)
+    per_chunk = 2 * 3 * 88 * 1024
+    carry = 2 * 3 * 128 * 128 * 4
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(a)) == 5 * per_chunk   # all 5 chunks, one launch
+    assert L.kda_prefill_workspace_min_bytes(ctypes.byref(a)) == per_chunk + carry
+    one = _prefill_args(kda, B=2, T=64, H=3, dk=128, dv=128, chunk=64)
+    assert L.kda_prefill_workspace_min_bytes(ctypes.byref(one)) == per_chunk
+    # no two-kernel path: fp32 inputs, other chunk or head dims
+    for over in (dict(in_dtype=kda.KDA_F32), dict(chunk=32), dict(dk=64, dv=64)):
+        b = _prefill_args(kda, **{**dict(B=2, T=300, H=3, dk=128, dv=128, chunk=64), **over})
+        assert L.kda_prefill_workspace_bytes(ctypes.byref(b)) == 0
+        assert L.kda_prefill_workspace_min_bytes(ctypes.byref(b)) == 0
+    # invalid arguments: 0
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(_prefill_args(kda, B=0))) == 0
+    # a workspace below the minimum is rejected; misaligned too
+    small = _prefill_args(kda, B=2, T=300, H=3, dk=128, dv=128, chunk=64, workspace=0x100000,
+                          workspace_bytes=per_chunk + carry - 1)
+    assert L.kda_prefill(ctypes.byref(small), None) == -6
+    mis = _prefill_args(kda, B=2, T=300, H=3, dk=128, dv=128, chunk=64, workspace=0x100008,
+                        workspace_bytes=10 * per_chunk)
+    assert L.kda_prefill(ctypes.byref(mis), None) == -4
+    # 1M tokens at K3 width in one call: balanced slabs keep the workspace under 16 GiB
+    big = _prefill_args(kda, B=1, T=1 << 20, H=96, dk=128, dv=128, chunk=64)
+    nb = L.kda_prefill_workspace_bytes(ctypes.byref(big))
+    nslabs = -(-16384 * 96 * 88 * 1024 // (16 << 30))
+    assert nb == -(-16384 // nslabs) * 96 * 88 * 1024 + 96 * 128 * 128 * 4 and nb - 96 * 128 * 128 * 4 <= 16 << 30
+    # K3 width (65536 tokens, 8.6 GB of chunk blocks) fits one launch
+    k3 = _prefill_args(kda, B=1, T=1 << 16, H=96, dk=128, dv=128, chunk=64)
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(k3)) == 1024 * 96 * 88 * 1024
+
+
 def test_decode_validation_codes(kda):
     L = kda.lib()
     base = dict(N=2, H=2, dk=16, dv=16, in_dtype=kda.KDA_BF16, out_dtype=kda.KDA_F32, q=0x1000,

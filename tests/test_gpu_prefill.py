@@ -1,4 +1,8 @@
-"""Prefill on the GPU (kda_prefill, kda_prep) against the fp64 oracle."""
+"""Prefill on the GPU (kda_prefill, kda_prep) against the fp64 oracle.
+
+Sizes with a two-kernel path (bf16 inputs, chunk 64, dk = dv = 128) run both
+paths: "split" passes the workspace kda_prefill_workspace_bytes asks for,
+"fused" passes none (the single-kernel path)."""
 from __future__ import annotations
 
 import numpy as np
@@ -9,6 +13,9 @@ from gpu_util import assert_rms_close, gather_heads, need_gpu, to_dev, tol_for
 from kda_synth import Workload
 
 pytestmark = pytest.mark.gpu
+
+PATHS = {"split": "auto", "fused": None}
+path = pytest.mark.parametrize("path", list(PATHS))
 
 
 def _gpu_prefill(kda, dev, chunk, **kw):
@@ -72,14 +79,15 @@ def test_tiny_fp32(oracle_mod):
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="tiny")
 
 
+@path
 @pytest.mark.parametrize("T", [1, 3, 15, 17, 63, 64, 65, 130])
-def test_ragged_lengths_bf16_d128(oracle_mod, T):
+def test_ragged_lengths_bf16_d128(oracle_mod, T, path):
     torch, kda = need_gpu()
     w = Workload("r", 1, T, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=40 + T)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, w.dtype)
-    o, S_T, c = _gpu_prefill(kda, dev, 64)
-    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"T={T}")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} T={T}")
 
 
 @pytest.mark.parametrize("dtype,d,chunk", [("bf16", 32, 64), ("bf16", 64, 32), ("bf16", 128, 16),
@@ -94,7 +102,8 @@ def test_dims_chunks_dtypes(oracle_mod, dtype, d, chunk):
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{dtype} d={d} C={chunk}")
 
 
-def test_split_in_place_carry(oracle_mod):
+@path
+def test_split_in_place_carry(oracle_mod, path):
     """Two calls with S and the conv history carried in place (S_T aliases S0,
     conv_out aliases conv_in) match the oracle over the whole sequence."""
     torch, kda = need_gpu()
@@ -109,15 +118,47 @@ def test_split_in_place_carry(oracle_mod):
         part["conv_w"] = dev["conv_w"]
         o, _, _ = kda.prefill(part["q"], part["k"], part["v"], part["conv_w"], part["g"],
                               part["beta"], part["gate"], S0=S, conv_in=conv, chunk=64, S_T=S,
-                              conv_out=conv)
+                              conv_out=conv, workspace=PATHS[path])
         outs.append(o)
     o = torch.cat(outs, 1)
-    _check_vs_oracle(oracle_mod, w, inp, o, S, conv, what="split")
+    _check_vs_oracle(oracle_mod, w, inp, o, S, conv, what=f"{path} carried")
 
 
-def test_empty_sequence_copies_carry():
+@pytest.mark.parametrize("per_slab", [1, 3])
+def test_slabs_of_a_small_workspace(oracle_mod, per_slab):
+    """A workspace smaller than the preferred size runs the chunks in several
+    launches with the state carried in the workspace: 5 chunks (T = 300) with
+    room for 1 or 3 chunks per launch."""
     torch, kda = need_gpu()
-    w = Workload("e", 2, 0, 2, 64, 64, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=2)
+    w = Workload("sl", 2, 300, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=9)
+    inp = syn.prefill_inputs_np(w)
+    dev = to_dev(inp, "bf16")
+    per_chunk = w.B * w.H * 88 * 1024
+    nbytes = per_slab * per_chunk + w.B * w.H * w.dk * w.dv * 4
+    assert nbytes >= kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, minimum=True)
+    assert nbytes < kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=ws)
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{per_slab} chunk(s) per launch")
+
+
+def test_paths_agree(oracle_mod):
+    """Both paths on the same inputs agree to well within the tolerance."""
+    torch, kda = need_gpu()
+    w = Workload("pa", 2, 256, 3, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=21)
+    dev = to_dev(syn.prefill_inputs_np(w), "bf16")
+    a = _gpu_prefill(kda, dev, 64, workspace="auto")
+    b = _gpu_prefill(kda, dev, 64, workspace=None)
+    torch.cuda.synchronize()
+    for x, y, what in zip(a, b, ("o", "S_T", "conv_out")):
+        x, y = x.float().cpu().numpy(), y.float().cpu().numpy()
+        assert_rms_close(x, y, 2e-2, f"split vs fused {what}")
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_empty_sequence_copies_carry(d):
+    torch, kda = need_gpu()
+    w = Workload("e", 2, 0, 2, d, d, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=2)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
     o, S_T, c = _gpu_prefill(kda, dev, 64)
@@ -126,16 +167,18 @@ def test_empty_sequence_copies_carry():
     assert torch.equal(S_T, dev["S0"]) and torch.equal(c, dev["conv_in"])
 
 
-def test_no_initial_state_is_zero_state(oracle_mod):
+@path
+def test_no_initial_state_is_zero_state(oracle_mod, path):
     torch, kda = need_gpu()
     w = Workload("z", 1, 100, 3, 128, 128, 64, "bf16", seed=12)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    o, S_T, c = _gpu_prefill(kda, dev, 64)
-    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="S0=None")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} S0=None")
 
 
-def test_strong_decay_takes_bf16_tiles(oracle_mod):
+@path
+def test_strong_decay_takes_bf16_tiles(oracle_mod, path):
     """g = -2 per token: a 16-token tile decays by e^32, beyond fp16's range, so the
     decay-weighted products of those chunks run on bf16 operands.  They are finite
     and correct to bf16 precision: the bound here is 3e-2 x RMS (bf16 operands on
@@ -147,36 +190,39 @@ def test_strong_decay_takes_bf16_tiles(oracle_mod):
     gbits[:, 64:128] = syn.bf16_bits_from_f64(np.full(inp["g"][:, 64:128].shape, -0.05))
     inp["g"] = gbits
     dev = to_dev(inp, "bf16")
-    o, S_T, c = _gpu_prefill(kda, dev, 64)
-    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="strong decay", tol=3e-2)
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} strong decay", tol=3e-2)
 
 
-def test_bf16_output(oracle_mod):
+@path
+def test_bf16_output(oracle_mod, path):
     torch, kda = need_gpu()
     w = Workload("bo", 1, 96, 2, 128, 128, 64, "bf16", s0_sigma=0.05, seed=13)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    o32, _, _ = _gpu_prefill(kda, dev, 64)
-    o16, _, _ = _gpu_prefill(kda, dev, 64, out_dtype=torch.bfloat16)
+    o32, _, _ = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    o16, _, _ = _gpu_prefill(kda, dev, 64, out_dtype=torch.bfloat16, workspace=PATHS[path])
     torch.cuda.synchronize()
     assert torch.equal(o16, o32.to(torch.bfloat16))
 
 
-def test_deterministic(oracle_mod):
+@path
+def test_deterministic(oracle_mod, path):
     torch, kda = need_gpu()
     w = Workload("det", 2, 300, 3, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=4)
     dev = to_dev(syn.prefill_inputs_np(w), "bf16")
-    runs = [_gpu_prefill(kda, dev, 64) for _ in range(3)]
+    runs = [_gpu_prefill(kda, dev, 64, workspace=PATHS[path]) for _ in range(3)]
     torch.cuda.synchronize()
     for o, S, c in runs[1:]:
         assert torch.equal(o, runs[0][0]) and torch.equal(S, runs[0][1]) and torch.equal(c, runs[0][2])
 
 
-def test_prefill_workload_b2_t4096_h32(oracle_mod):
+@path
+def test_prefill_workload_b2_t4096_h32(oracle_mod, path):
     """B2 T4096 H32 d128 bf16 chunk 64: every head against the oracle."""
     torch, kda = need_gpu()
     w = syn.WORKLOADS["prefill"]
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    o, S_T, c = _gpu_prefill(kda, dev, w.chunk)
-    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="B2 T4096 H32")
+    o, S_T, c = _gpu_prefill(kda, dev, w.chunk, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} B2 T4096 H32")
