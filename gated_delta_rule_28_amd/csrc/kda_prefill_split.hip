@@ -8,11 +8,15 @@
 //
 //   intra_chunk_kernel  one workgroup (4 waves) per (b, h, chunk); every chunk
 //     of every head at once.  Conv + SiLU + L2 normalisation + chunk-local
-//     cumulative sum of g, then A, P, T = (I + A)^-1, W = T diag(beta) (K e^G)
-//     and U~ = T diag(beta) V on the matrix cores.
-//   inter_chunk_kernel  one workgroup (4 waves) per (b, h) walks the chunks in
-//     order: U = U~ - W S, O = (Q e^G) S + P U, S <- e^{G_C} S + (K e^{G_C-G})^T U
-//     with the fp32 state in registers, then RMSNorm * sigmoid(gate).
+//     cumulative sum of g, then A, P and T = (I + A)^-1 on the matrix cores.
+//   inter_chunk_kernel  one workgroup (8 waves) per (b, h) walks the chunks in
+//     order with the fp32 state in registers:
+//       U = T diag(beta) (V - (K e^G) S)        (= U~ - W S of the WY form)
+//       O = (Q e^G) S + P U,   S <- e^{G_C} S + (K e^{G_C-G})^T U,
+//     then RMSNorm * sigmoid(gate).
+//   Taking V - (K e^G) S first keeps the cancellation between the new values
+//   and the state's prediction in fp32 accumulators, and hands over V and
+//   K e^G in fp16 instead of W and an fp32 U~.
 //
 // The first kernel hands the second its operands in a workspace laid out as
 // matrix-core fragments (64 lanes x 16 bytes, lane order), so every operand
@@ -35,9 +39,7 @@
 //
 // Precision as in kda_prefill.hip: fp16 operands (bf16 for the decay-weighted
 // A / P operands of a chunk in which some 16-token tile decays by more than
-// e^8), fp32 accumulation, fp32 state and output.  U~ is passed between the
-// kernels in fp32: U = U~ - W S can cancel (the state already predicts v), and
-// an fp16 U~ then puts the state's error at about 2e-2 of its RMS on some heads.
+// e^8), fp32 accumulation, fp32 state and output.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -52,14 +54,15 @@ constexpr float kSpanF16 = 8.0f;
 
 // ---- workspace block of one (b, h, chunk), bytes ------------------------------
 constexpr int kFrag = 1024;                  // 64 lanes x 16 bytes
-constexpr int WS_W = 0;                      // -W     fragments (rt, k)        16
-constexpr int WS_QG = WS_W + 16 * kFrag;     // Q e^G  fragments (rt, k)        16
+constexpr int WS_KG = 0;                     // -(K e^G) fragments (rt, k)      16
+constexpr int WS_QG = WS_KG + 16 * kFrag;    // Q e^G    fragments (rt, k)      16
 constexpr int WS_KB = WS_QG + 16 * kFrag;    // (K e^{G_C-G})^T fragments (m, k') 16
-constexpr int WS_P = WS_KB + 16 * kFrag;     // P      fragments (rt, k'), k' <= rt/2: 6
-constexpr int WS_GAM = WS_P + 6 * kFrag;     // e^{G_C} in state row order, 128 fp32 (+pad)
-constexpr int WS_STAGE = WS_GAM + 2 * kFrag; // bytes the second kernel stages through LDS (56 KiB)
-constexpr int WS_U = WS_STAGE;               // U~ (rt, w): 64 lanes x 8 fp32   32 KiB
-constexpr int WS_CHUNK = WS_U + 32 * kFrag;  // 88 KiB per chunk
+constexpr int WS_P = WS_KB + 16 * kFrag;     // P        fragments (rt, k'), k' <= rt/2: 6
+constexpr int WS_TB = WS_P + 6 * kFrag;      // T diag(beta) fragments, as P: 6
+constexpr int WS_GAM = WS_TB + 6 * kFrag;    // e^{G_C} in state row order, 128 fp32 (+pad)
+constexpr int WS_STAGE = WS_GAM + 4 * kFrag; // bytes the second kernel stages through LDS (64 KiB)
+constexpr int WS_V = WS_STAGE;               // V (rt, w): C layout, 64 lanes x 8 fp16   16 KiB
+constexpr int WS_CHUNK = WS_V + 16 * kFrag;  // 80 KiB per chunk
 constexpr size_t kSlabBytesMax = (size_t)16 << 30;  // workspace cap for the chunk blocks
 
 __device__ __forceinline__ int p_frag(int rt, int kp) { return rt < 2 ? rt : 2 * rt - 2 + kp; }
@@ -209,9 +212,8 @@ struct ALds {
   static constexpr int EKB = ETOT + 4 * kD * 4;       // [4][128] e^{G_C - rho_a - tot_a}
   static constexpr int FOFF = EKB + 4 * kD * 4;       // [3][128] e^{rho_a - rho_{b+1}}: (2,0) (3,0) (3,1)
   static constexpr int R2_A = FOFF + 3 * kD * 4;
-  // R2, afterwards: (K e^G)^T and V^T
-  static constexpr int KGT = R2;                      // [128][kLDT] fp16
-  static constexpr int VT = KGT + kD * kLDT * 2;      // [128][kLDT] fp16
+  // R2, afterwards: V^T
+  static constexpr int VT = R2;                       // [128][kLDT] fp16
   static constexpr int R2_B = VT + kD * kLDT * 2;
   static constexpr int BYTES = R2_A > R2_B ? R2_A : R2_B;
 };
@@ -219,7 +221,7 @@ struct ALds {
 // ---------------------------------------------------------------------------
 // intra_chunk_kernel: grid n_chunks * B * H, block 256
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
+__global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   using L = ALds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   float* sTot = reinterpret_cast<float*>(smem + L::TOT);
@@ -234,7 +236,6 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
   _Float16* sKBT = reinterpret_cast<_Float16*>(smem + L::KBT);
   float* sAM = reinterpret_cast<float*>(smem + L::AM);
   _Float16* sTB = reinterpret_cast<_Float16*>(smem + L::TB);
-  _Float16* sKGT = reinterpret_cast<_Float16*>(smem + L::KGT);
   _Float16* sVT = reinterpret_cast<_Float16*>(smem + L::VT);
   constexpr int LDA = L::LDA, LDB = L::LDB;
 
@@ -372,7 +373,7 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
     }
   }
   // ---- k: rows and columns of A / P, K e^G, K e^{G_C - G} ---------------------------
-  half8 KrowF[4], CdiagF[4], KGf[4];
+  half8 KrowF[4], CdiagF[4];
   {
     float x[32];
     conv_silu(rk, hk, hok, valid, sCW + kD + 8 * g, x);
@@ -390,11 +391,11 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
         cd[e] = xe * fast_rcp(ee);       // k e^{rho_a - G}
         cc[e] = cd[e] * et[e];           // k e^{rho_{a+1} - G}
         kb[e] = cc[e] * ek[e];           // k e^{G_C - G}
-        kg[e] = kr[e] * er[e];           // k e^{G}
+        kg[e] = -kr[e] * er[e];          // -k e^{G}
       }
       KrowF[kp] = to_op8(kr, bf);
       CdiagF[kp] = to_op8(cd, bf);
-      KGf[kp] = to_half8(kg);
+      *reinterpret_cast<half8*>(wsb + WS_KG + ((wave * 4 + kp) * 64 + lane) * 16) = to_half8(kg);
       if (wave < 3) sCC[(wave * 4 + kp) * 64 + lane] = to_op8(cc, bf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sKBT[tix(32 * kp + 8 * g + e, tok)] = (_Float16)kb[e];
@@ -484,14 +485,11 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
       *reinterpret_cast<half8*>(wsb + WS_P + (p_frag(wave, kp) * 64 + lane) * 16) = to_half8(pv);
     }
   }
-  // (K e^G)^T and V^T for the W / U~ products
+  // V^T, for V in the C layout of the second kernel
 #pragma unroll
   for (int kp = 0; kp < 4; ++kp)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      sKGT[tix(32 * kp + 8 * g + e, tok)] = KGf[kp][e];
-      sVT[tix(32 * kp + 8 * g + e, tok)] = Vf[kp][e];
-    }
+    for (int e = 0; e < 8; ++e) sVT[tix(32 * kp + 8 * g + e, tok)] = Vf[kp][e];
   lds_barrier();
 
   // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution --------------
@@ -560,42 +558,24 @@ __global__ __launch_bounds__(256, 2) void intra_chunk_kernel(SplitParams p) {
   }
   lds_barrier();
 
-  // ---- W^T = (K e^G)^T (T diag(beta))^T and U~ = T diag(beta) V -------------------
-  // wave w: state rows 16(2w + s) + r (channels 32w + 8g + 4s + r) of W^T and
-  // dv column tiles 2w + s of U~.
-  f4 accW[2][4], accU[2][4];
+  // ---- hand-over: T diag(beta) as row-operand fragments, V in C layout ------------
+  // T diag(beta) fragment (rt, k'), like P: lane (g, i) holds row 16rt + i at
+  // tokens 32k' + 4g + 0..3 and 32k' + 16 + 4g + 0..3; wave w writes fragments w, w + 4
 #pragma unroll
-  for (int sh = 0; sh < 2; ++sh)
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      accW[sh][rt] = f4{0.f, 0.f, 0.f, 0.f};
-      accU[sh][rt] = f4{0.f, 0.f, 0.f, 0.f};
-    }
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-#pragma unroll
-    for (int kp = 0; kp < 2; ++kp) {
-      if (2 * kp <= rt) {
-        const half8 tb = *reinterpret_cast<const half8*>(sTB + (16 * rt + i) * LDB + 32 * kp + 8 * g);
-#pragma unroll
-        for (int sh = 0; sh < 2; ++sh) {
-          const int mc = 2 * wave + sh;
-          const half8 kg = *reinterpret_cast<const half8*>(sKGT + tix(perm_row(16 * mc + i), 32 * kp + 8 * g));
-          accW[sh][rt] = mma_f16(kg, tb, accW[sh][rt]);
-          const half8 vv = *reinterpret_cast<const half8*>(sVT + tix(16 * mc + i, 32 * kp + 8 * g));
-          accU[sh][rt] = mma_f16(tb, vv, accU[sh][rt]);
-        }
-      }
-    }
+  for (int f = wave; f < 6; f += 4) {
+    const int rt = f < 2 ? f : (f - 2) / 2 + 2, kp = f < 2 ? 0 : (f - 2) & 1;
+    const half4 lo = *reinterpret_cast<const half4*>(sTB + (16 * rt + i) * LDB + 32 * kp + 4 * g);
+    const half4 hi = *reinterpret_cast<const half4*>(sTB + (16 * rt + i) * LDB + 32 * kp + 16 + 4 * g);
+    *reinterpret_cast<half8*>(wsb + WS_TB + (f * 64 + lane) * 16) = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
   }
+  // V fragment (rt, w): lane (g, i) holds tokens 16rt + 4g + 0..3 of dv columns
+  // 16(2w) + i and 16(2w + 1) + i
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) {
-    const float wv[8] = {-accW[0][rt][0], -accW[0][rt][1], -accW[0][rt][2], -accW[0][rt][3],
-                         -accW[1][rt][0], -accW[1][rt][1], -accW[1][rt][2], -accW[1][rt][3]};
-    *reinterpret_cast<half8*>(wsb + WS_W + ((rt * 4 + wave) * 64 + lane) * 16) = to_half8(wv);
-    float4* up = reinterpret_cast<float4*>(wsb + WS_U + ((rt * 4 + wave) * 64 + lane) * 32);
-    up[0] = make_float4(accU[0][rt][0], accU[0][rt][1], accU[0][rt][2], accU[0][rt][3]);
-    up[1] = make_float4(accU[1][rt][0], accU[1][rt][1], accU[1][rt][2], accU[1][rt][3]);
+    const half4 c0v = *reinterpret_cast<const half4*>(sVT + tix(32 * wave + i, 16 * rt + 4 * g));
+    const half4 c1v = *reinterpret_cast<const half4*>(sVT + tix(32 * wave + 16 + i, 16 * rt + 4 * g));
+    *reinterpret_cast<half8*>(wsb + WS_V + ((rt * 4 + wave) * 64 + lane) * 16) =
+        half8{c0v[0], c0v[1], c0v[2], c0v[3], c1v[0], c1v[1], c1v[2], c1v[3]};
   }
 }
 
@@ -677,40 +657,36 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   // waves waited for their copies), O(j-1) is complete, and nobody reads the
   // buffer copied next.
   if (math) {
-    // U~ of this wave's columns, loaded one chunk ahead (C layout)
-    float4 utn[4][2];
+    // V of this wave's columns, loaded one chunk ahead (C layout, fp16)
+    uint4 vtn[4];
     if (nc > 0) {
 #pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        const float4* up = reinterpret_cast<const float4*>(wsh + WS_U + ((rt * 4 + w) * 64 + lane) * 32);
-        utn[rt][0] = up[0];
-        utn[rt][1] = up[1];
-      }
+      for (int rt = 0; rt < 4; ++rt)
+        vtn[rt] = *reinterpret_cast<const uint4*>(wsh + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
     }
     for (int j = 0; j <= nc; ++j) {
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // B1
-      f4 O[4][2], U[4][2];
+      f4 O[4][2], X[4][2];
       const unsigned char* sb = smem + (j & 1) * WS_STAGE;
       if (j < nc) {
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt)
+        for (int rt = 0; rt < 4; ++rt) {
+          const half8 v8 = __builtin_bit_cast(half8, vtn[rt]);
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
-            U[rt][ct] = f4{utn[rt][ct].x, utn[rt][ct].y, utn[rt][ct].z, utn[rt][ct].w};
+            X[rt][ct] = f4{(float)v8[4 * ct], (float)v8[4 * ct + 1], (float)v8[4 * ct + 2], (float)v8[4 * ct + 3]};
             O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
           }
+        }
         if (j + 1 < nc) {
           const unsigned char* wn = wsh + (size_t)(j + 1) * WS_CHUNK;
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            const float4* up = reinterpret_cast<const float4*>(wn + WS_U + ((rt * 4 + w) * 64 + lane) * 32);
-            utn[rt][0] = up[0];
-            utn[rt][1] = up[1];
-          }
+          for (int rt = 0; rt < 4; ++rt)
+            vtn[rt] = *reinterpret_cast<const uint4*>(wn + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
         }
-        // U = U~ + (-W) S and (Q e^G) S, one 32-row step of S at a time: its B
-        // operands are rows 16(2k + s) + 4g + e, s = 0, 1
+        // X = V + (-(K e^G)) S and (Q e^G) S, one 32-row step of S at a time:
+        // its B operands are rows 16(2k + s) + 4g + e, s = 0, 1
 #pragma unroll
         for (int kp = 0; kp < 4; ++kp) {
           half8 Sb[2];
@@ -722,11 +698,11 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           }
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) {
-            const half8 wf = *reinterpret_cast<const half8*>(sb + WS_W + ((rt * 4 + kp) * 64 + lane) * 16);
+            const half8 wf = *reinterpret_cast<const half8*>(sb + WS_KG + ((rt * 4 + kp) * 64 + lane) * 16);
             const half8 qf = *reinterpret_cast<const half8*>(sb + WS_QG + ((rt * 4 + kp) * 64 + lane) * 16);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) {
-              U[rt][ct] = mma_f16(wf, Sb[ct], U[rt][ct]);
+              X[rt][ct] = mma_f16(wf, Sb[ct], X[rt][ct]);
               O[rt][ct] = mma_f16(qf, Sb[ct], O[rt][ct]);
             }
           }
@@ -734,6 +710,29 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       }
       lds_barrier();  // B2
       if (j < nc) {
+        // U = T diag(beta) X, with X as B operands over tokens 32k' + 16s + 4g + e
+        half8 Xb[2][2];
+#pragma unroll
+        for (int kp = 0; kp < 2; ++kp)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            const float x[8] = {X[2 * kp][ct][0], X[2 * kp][ct][1], X[2 * kp][ct][2], X[2 * kp][ct][3],
+                                X[2 * kp + 1][ct][0], X[2 * kp + 1][ct][1], X[2 * kp + 1][ct][2], X[2 * kp + 1][ct][3]};
+            Xb[kp][ct] = to_half8(x);
+          }
+        f4 U[4][2];
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) U[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kp = 0; kp < 2; ++kp)
+            if (2 * kp <= rt) {
+              const half8 tf = *reinterpret_cast<const half8*>(sb + WS_TB + (p_frag(rt, kp) * 64 + lane) * 16);
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) U[rt][ct] = mma_f16(tf, Xb[kp][ct], U[rt][ct]);
+            }
+        }
         // U as B operands over tokens 32k' + 16s + 4g + e
         half8 Ub[2][2];
 #pragma unroll

@@ -111,7 +111,7 @@ typedef struct kda_prefill_args {
 
 int kda_prefill(const kda_prefill_args* args, void* stream);
 
-/* Device workspace the two-kernel path prefers for these sizes: 88 KiB per
+/* Device workspace the two-kernel path prefers for these sizes: 80 KiB per
  * (b, h, chunk of 64 tokens), capped near 16 GiB (plus B*H*dk*dv*4 bytes to
  * carry the state) by processing long sequences in slabs of chunks.  0 when
  * the sizes have no two-kernel path or the arguments are invalid.  The fields

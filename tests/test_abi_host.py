@@ -123,7 +123,7 @@ def test_prefill_workspace_sizes_and_check(kda):
     L = kda.lib()
     # sizes with a two-kernel path: bf16 inputs, chunk 64, dk = dv = 128
     a = _prefill_args(kda, B=2, T=300, H=3, dk=128, dv=128, chunk=64)
-    per_chunk = 2 * 3 * 88 * 1024
+    per_chunk = 2 * 3 * 80 * 1024
     carry = 2 * 3 * 128 * 128 * 4
     assert L.kda_prefill_workspace_bytes(ctypes.byref(a)) == 5 * per_chunk   # all 5 chunks, one launch
     assert L.kda_prefill_workspace_min_bytes(ctypes.byref(a)) == per_chunk + carry
@@ -146,11 +146,11 @@ def test_prefill_workspace_sizes_and_check(kda):
     # 1M tokens at K3 width in one call: balanced slabs keep the workspace under 16 GiB
     big = _prefill_args(kda, B=1, T=1 << 20, H=96, dk=128, dv=128, chunk=64)
     nb = L.kda_prefill_workspace_bytes(ctypes.byref(big))
-    nslabs = -(-16384 * 96 * 88 * 1024 // (16 << 30))
-    assert nb == -(-16384 // nslabs) * 96 * 88 * 1024 + 96 * 128 * 128 * 4 and nb - 96 * 128 * 128 * 4 <= 16 << 30
+    nslabs = -(-16384 * 96 * 80 * 1024 // (16 << 30))
+    assert nb == -(-16384 // nslabs) * 96 * 80 * 1024 + 96 * 128 * 128 * 4 and nb - 96 * 128 * 128 * 4 <= 16 << 30
     # K3 width (65536 tokens, 8.6 GB of chunk blocks) fits one launch
     k3 = _prefill_args(kda, B=1, T=1 << 16, H=96, dk=128, dv=128, chunk=64)
-    assert L.kda_prefill_workspace_bytes(ctypes.byref(k3)) == 1024 * 96 * 88 * 1024
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(k3)) == 1024 * 96 * 80 * 1024
 
 
 def test_decode_validation_codes(kda):

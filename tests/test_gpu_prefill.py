@@ -133,7 +133,7 @@ def test_slabs_of_a_small_workspace(oracle_mod, per_slab):
     w = Workload("sl", 2, 300, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=9)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    per_chunk = w.B * w.H * 88 * 1024
+    per_chunk = w.B * w.H * 80 * 1024
     nbytes = per_slab * per_chunk + w.B * w.H * w.dk * w.dv * 4
     assert nbytes >= kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, minimum=True)
     assert nbytes < kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
