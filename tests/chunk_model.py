@@ -9,7 +9,7 @@ cumulative sum of g inside the chunk (G_{-1} = 0):
   A_rj = beta_r sum_c k_rc k_jc e^{G_rc - G_jc}     (j < r)
   T    = (I + A)^-1
   W    = T diag(beta) (K * e^G) ;  U~ = T diag(beta) V
-  U    = U~ - W S
+  U    = U~ - W S  ( = T diag(beta) (V - (K * e^G) S) )
   P_rj = sum_c q_rc k_jc e^{G_rc - G_jc}            (j <= r)
   O    = (Q * e^G) S + P U
   S'   = diag(e^{G_C}) S + (K * e^{G_C - G})^T U
@@ -42,13 +42,18 @@ def _id(x):
     return np.asarray(x, dtype=np.float64)
 
 
-def chunk_core(qn, kn, vn, g, beta, S0, C=64, operands=None, tile=TILE):
+def chunk_core(qn, kn, vn, g, beta, S0, C=64, operands=None, tile=TILE, form="wy", ut_rounded=False):
     """Chunkwise o_core [T,dv] and final state for one (b,h).
 
     qn, kn [T,dk] (q already scaled by dk^-1/2), vn [T,dv], g [T,dk], beta [T].
     operands = None (exact fp64), "bf16" or "fp16": every matrix-core operand is
     rounded to that type while accumulation, decay factors and the state stay in
     higher precision, as in the GPU kernels.
+    form = "wy": U = U~ - W S with W, U~ formed inside the chunk (single-kernel
+    path); "tx": U = (T diag(beta)) (V - (K e^G) S), the same product taken in
+    the other order (two-kernel path), with its operand rounding points.
+    ut_rounded: also round U~ to the operand type before U = U~ - W S (a
+    hand-over the kernels do not use: see test_chunk_algebra).
     """
     rnd = {None: _id, "bf16": _bf16, "fp16": _fp16}[operands]
     f32 = _id if operands is None else (lambda x: np.asarray(x, dtype=np.float32).astype(np.float64))
@@ -76,9 +81,13 @@ def chunk_core(qn, kn, vn, g, beta, S0, C=64, operands=None, tile=TILE):
         P = np.tril(P, 0)
         Tm = np.linalg.inv(np.eye(n) + A)
         Tb = rnd(Tm * b[None, :])
-        W = Tb @ rnd(K * np.exp(G))
-        Ut = Tb @ rnd(V)
-        U = Ut - rnd(W) @ rnd(S)
+        if form == "tx":
+            X = rnd(V) - rnd(K * np.exp(G)) @ rnd(S)
+            U = Tb @ rnd(X)
+        else:
+            W = Tb @ rnd(K * np.exp(G))
+            Ut = Tb @ rnd(V)
+            U = (rnd(Ut) if ut_rounded else Ut) - rnd(W) @ rnd(S)
         Ub = rnd(U)
         o[c0:c1] = rnd(Q * np.exp(G)) @ rnd(S) + rnd(P) @ Ub
         S = np.exp(G[-1])[:, None] * S + rnd(K * np.exp(G[-1] - G)).T @ Ub

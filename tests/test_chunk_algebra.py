@@ -23,16 +23,17 @@ def _case(T, dk, dv, dtype="f32", s0=0.2, seed=11, H=1):
     return w, syn.prefill_inputs_np(w)
 
 
+@pytest.mark.parametrize("form", ["wy", "tx"])
 @pytest.mark.parametrize("C", [1, 2, 16, 64])
 @pytest.mark.parametrize("T", [1, 15, 17, 64, 100])
-def test_chunk_algebra_exact(oracle_mod, C, T):
+def test_chunk_algebra_exact(oracle_mod, C, T, form):
     w, inp = _case(T, 16, 24)
     r = oracle_mod.prefill(inp, want_prep=True)
     prep = r["prep"][0]
     qn, kn, vn = prep[:, :16], prep[:, 16:32], prep[:, 32:]
     g = inp["g"][0, :, 0].astype(np.float64)
     beta = inp["beta"][0, :, 0].astype(np.float64)
-    oc, S = chunk_core(qn, kn, vn, g, beta, inp["S0"][0, 0].astype(np.float64), C=C)
+    oc, S = chunk_core(qn, kn, vn, g, beta, inp["S0"][0, 0].astype(np.float64), C=C, form=form)
     o = gated_rmsnorm(oc, inp["gate"][0, :, 0].astype(np.float64))
     np.testing.assert_allclose(S, r["S_T"][0], rtol=1e-11, atol=1e-13)
     np.testing.assert_allclose(o, r["o"][0], rtol=1e-9, atol=1e-11)
@@ -51,7 +52,7 @@ def test_tile_references_bound_factors():
     assert worst == 80.0 and np.isfinite(np.float32(np.exp(worst)))
 
 
-def _operand_error(oracle_mod, operands, T=512, d=128):
+def _operand_error(oracle_mod, operands, T=512, d=128, form="wy"):
     """max |err| / RMS for o and S_T with the given operand type, C = 64."""
     w, inp = _case(T, d, d, dtype="bf16", s0=0.01, seed=5, H=2)
     r = oracle_mod.prefill(inp, want_prep=True)
@@ -63,7 +64,7 @@ def _operand_error(oracle_mod, operands, T=512, d=128):
         beta = to_f64(inp["beta"], "bf16")[0, :, i]
         gate = to_f64(inp["gate"], "bf16")[0, :, i]
         oc, S = chunk_core(qn, kn, vn, g, beta, inp["S0"][0, i].astype(np.float64), C=64,
-                           operands=operands)
+                           operands=operands, form=form)
         o = gated_rmsnorm(oc, gate)
         errs_o.append(np.abs(o - r["o"][i]).max())
         errs_s.append(np.abs(S - r["S_T"][i]).max())
@@ -74,11 +75,37 @@ def _operand_error(oracle_mod, operands, T=512, d=128):
     return max(errs_o) / rms_o, max(errs_s) / rms_s
 
 
-def test_operand_precision_budget(oracle_mod):
+@pytest.mark.parametrize("form", ["wy", "tx"])
+def test_operand_precision_budget(oracle_mod, form):
     """fp16 operands (d = 128, C = 64, bf16 inputs, non-zero initial state) keep the
-    max error under 0.4 of the 2e-2 x RMS bound for o and S_T; bf16 operands
-    would not (their error is above half the bound)."""
-    eo, es = _operand_error(oracle_mod, "fp16")
+    max error under 0.4 of the 2e-2 x RMS bound for o and S_T, in both orders of
+    the U product; bf16 operands would not (their error is above half the bound)."""
+    eo, es = _operand_error(oracle_mod, "fp16", form=form)
     assert eo < 0.4 * 2e-2 and es < 0.4 * 2e-2, (eo, es)
+    if form == "tx":
+        return
     bo, bs = _operand_error(oracle_mod, "bf16")
     assert max(bo, bs) > 0.5 * 2e-2, (bo, bs)
+
+
+def test_cancellation_needs_full_precision_u(oracle_mod):
+    """On a head of the B2 T4096 H32 workload where the state predicts the new
+    values well (U = U~ - W S cancels), passing U~ in fp16 puts the state's max
+    error past the 2e-2 x RMS bound, while both orders the kernels use (fp32
+    U~ - W S in one kernel; T diag(beta) (V - (K e^G) S) with the difference
+    in fp32 accumulators in the other) stay well inside it."""
+    w = syn.WORKLOADS["prefill"]
+    inp = syn.prefill_inputs_np(w)
+    b, h = divmod(55, w.H)
+    r = oracle_mod.prefill(inp, heads=[55], want_prep=True)
+    d = w.dk
+    prep = r["prep"][0]
+    args = (prep[:, :d], prep[:, d:2 * d], prep[:, 2 * d:], syn.to_f64(inp["g"], "bf16")[b, :, h],
+            syn.to_f64(inp["beta"], "bf16")[b, :, h], np.zeros((d, d)))
+    rms_s = np.sqrt(np.mean(r["S_T"][0] ** 2))
+    err = {}
+    for name, kw in [("wy", {}), ("tx", {"form": "tx"}), ("ut16", {"ut_rounded": True})]:
+        _, S = chunk_core(*args, C=64, operands="fp16", **kw)
+        err[name] = np.abs(S - r["S_T"][0]).max() / rms_s
+    assert err["ut16"] > 2e-2, err
+    assert err["wy"] < 0.6 * 2e-2 and err["tx"] < 0.6 * 2e-2, err
