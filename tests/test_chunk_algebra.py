@@ -102,7 +102,7 @@ def test_cancellation_needs_full_precision_u(oracle_mod):
     prep = r["prep"][0]
     args = (prep[:, :d], prep[:, d:2 * d], prep[:, 2 * d:], syn.to_f64(inp["g"], "bf16")[b, :, h],
             syn.to_f64(inp["beta"], "bf16")[b, :, h], np.zeros((d, d)))
-    rms_s = np.sqrt(np.mean(r["S_T"][0] ** 2))
+    rms_s = np.sqrt(np.mean(oracle_mod.prefill(inp, want_o=False)["S_T"] ** 2))  # over the workload
     err = {}
     for name, kw in [("wy", {}), ("tx", {"form": "tx"}), ("ut16", {"ut_rounded": True})]:
         _, S = chunk_core(*args, C=64, operands="fp16", **kw)
