@@ -194,8 +194,11 @@ def main():
     nbytes = prefill_bytes_per_launch(w.B, seg, w.H, w.dk, w.dv)
     flops = prefill_flops(w.B, seg, w.H, w.dk, w.dv, w.chunk)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
-    src = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc", "kda_prefill.hip")
-    traffic = load_traffic("prefill_kernel", src)
+    # one kda_prefill call = the two kernels of the workspace path
+    src = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc", "kda_prefill_split.hip")
+    t_intra = load_traffic("intra_chunk_kernel", src)
+    t_inter = load_traffic("inter_chunk_kernel", src)
+    traffic = t_intra + t_inter if t_intra is not None and t_inter is not None else None
     log(f"[bench] prefill {ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic")
 
     out = {
@@ -217,8 +220,9 @@ def main():
                    "matrix_core_operands": "f16 with f32 accumulation"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "prefill_kernel<64,128,128,bf16 in,f32 out>",
-                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms},
+                     "kernel": "kda_prefill (intra_chunk_kernel + inter_chunk_kernel, bf16 in, f32 out)",
+                     "algorithmic_bytes_per_launch": nbytes, "launch_ms": launch_ms,
+                     "workspace_bytes": kda.workspace_bytes(w.B, seg, w.H, w.dk, w.dv, w.chunk)},
         "mfma": {"algorithmic_flops_per_launch": flops,
                  "tflops": flops / (launch_ms * 1e-3) / 1e12,
                  "frac_of_bf16_f16_peak": flops / (launch_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},

@@ -24,6 +24,8 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc")
 
 # kernel key -> (substring of the demangled name, source file)
 KERNELS = {
+    "intra_chunk_kernel": ("intra_chunk_kernel", "kda_prefill_split.hip"),
+    "inter_chunk_kernel": ("inter_chunk_kernel<false>", "kda_prefill_split.hip"),
     "prefill_kernel": ("prefill_kernel<64, 128, 128, true, false, false>", "kda_prefill.hip"),
     "decode_kernel": ("decode_kernel<128, 128, true, false>", "kda_decode.hip"),
 }
@@ -115,9 +117,8 @@ def traffic(fetch_csv, write_csv, cmd, out, json_out):
 
 
 def counters(path, cmd, out, simds=1024):
-    """Per-kernel means of the raw counters of one --pmc run, with the derived
-    utilisations that their definitions give (MFMA busy and VALU active cycles
-    over GPU-active cycles per SIMD / CU)."""
+    """Per-kernel means of the counters of one --pmc run (raw or derived, as
+    rocprofv3 reports them)."""
     d, _ = _per_kernel(path)
     lines = ["# Compute counters per dispatch (rocprofv3 --pmc)", "", "Command:", "", "```", cmd, "```", ""]
     for key, (sub, _src) in KERNELS.items():
@@ -129,12 +130,6 @@ def counters(path, cmd, out, simds=1024):
         lines.append("")
         for k in sorted(c):
             lines.append(f"- {k}: {c[k]:.6g}")
-        gui = c.get("GRBM_GUI_ACTIVE")
-        if gui:
-            if "SQ_VALU_MFMA_BUSY_CYCLES" in c:
-                lines.append(f"- MFMA busy: {100 * c['SQ_VALU_MFMA_BUSY_CYCLES'] / (gui * simds):.2f}% of SIMD cycles")
-            if "SQ_ACTIVE_INST_VALU" in c:
-                lines.append(f"- VALU active: {100 * c['SQ_ACTIVE_INST_VALU'] / (gui * simds / 4):.2f}% of CU cycles")
         lines.append("")
     open(out, "w").write("\n".join(lines) + "\n")
 
