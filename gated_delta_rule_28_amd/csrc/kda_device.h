@@ -21,6 +21,7 @@ namespace kda {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 hf2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
@@ -82,6 +83,23 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
     *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + idx) = u;
   } else {
     *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + idx) = make_float4(a, b, c, d);
+  }
+}
+
+// Store 8 consecutive outputs (fp32 or bf16) with 16-byte stores.
+template <bool BF16>
+__device__ __forceinline__ void store8(void* base, size_t idx, const float* x) {
+  if constexpr (BF16) {
+    uint4 u;
+    u.x = (uint32_t)f_to_bf16(x[0]) | ((uint32_t)f_to_bf16(x[1]) << 16);
+    u.y = (uint32_t)f_to_bf16(x[2]) | ((uint32_t)f_to_bf16(x[3]) << 16);
+    u.z = (uint32_t)f_to_bf16(x[4]) | ((uint32_t)f_to_bf16(x[5]) << 16);
+    u.w = (uint32_t)f_to_bf16(x[6]) | ((uint32_t)f_to_bf16(x[7]) << 16);
+    *reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(base) + idx) = u;
+  } else {
+    float* f = reinterpret_cast<float*>(base) + idx;
+    *reinterpret_cast<float4*>(f) = make_float4(x[0], x[1], x[2], x[3]);
+    *reinterpret_cast<float4*>(f + 4) = make_float4(x[4], x[5], x[6], x[7]);
   }
 }
 

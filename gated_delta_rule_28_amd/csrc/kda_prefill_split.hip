@@ -43,6 +43,8 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <type_traits>
+
 namespace kda {
 
 namespace {
@@ -583,41 +585,61 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 // inter_chunk_kernel: grid B * H, block 512 (8 waves), one workgroup per (b, h)
 //
 //   waves 0..3 ("math"): wave w owns dv columns 32w .. 32w+31 and the state
-//     columns with them; per chunk it runs U = U~ - W S, O = (Q e^G) S + P U and
-//     S <- e^{G_C} S + (K e^{G_C-G})^T U on the matrix cores and leaves O in LDS.
-//   waves 4..7 ("epilogue"): wave 4 + r takes token tile r of the previous
-//     chunk's O: RMSNorm over its rows * sigmoid(gate), stores; and copies the
-//     next chunk's operands into LDS.  O passes through LDS in fp16: it
-//     is only normalised and gated afterwards, so its rounding (2^-11 relative)
-//     stays far below the tolerance.
+//     columns with them; per chunk it runs U = T diag(beta) (V - (K e^G) S),
+//     O = (Q e^G) S + P U and S <- e^{G_C} S + (K e^{G_C-G})^T U on the matrix
+//     cores and leaves O in LDS.  Its only memory accesses are LDS reads and
+//     the V of the next chunk, so it never waits behind other traffic.
+//   waves 4..7 ("epilogue"): wave 4 + r copies a quarter of the next chunk's
+//     operands into LDS and takes token tile r of the previous chunk's O:
+//     RMSNorm over its rows * sigmoid(gate), stores (16-byte pieces; the gate
+//     is loaded a chunk ahead).  O passes through LDS in fp16: it is only
+//     normalised and gated afterwards, so its rounding (2^-11 relative) stays
+//     far below the tolerance.
 // The epilogue of chunk j-1 runs beside the products of chunk j.  Two barriers
 // per chunk: B1 (chunk j's operands have landed; O(j-1) is complete) and B2
 // (the epilogue waves have read O(j-1), so the math waves may overwrite it).
 // ---------------------------------------------------------------------------
 constexpr int kStageQ = WS_STAGE / kFrag / 4;  // fragments each copying wave moves per chunk
 static_assert(WS_STAGE % (4 * kFrag) == 0, "staged part must split evenly over four waves");
-constexpr int B_O = 2 * WS_STAGE;              // two staging buffers, then O: [rt][w][lane][8] fp16
-constexpr int B_BYTES = B_O + 16 * kFrag;      // 128 KiB
-static_assert(B_BYTES <= 160 * 1024, "inter-chunk LDS exceeds 160 KiB");
+
+// LDS of inter_chunk_kernel as three separate objects: the compiler then knows
+// that the direct-to-LDS copy into one staging buffer never aliases reads of
+// the other or of O, and waits for the copies only where the kernel says so.
+__shared__ __attribute__((aligned(16))) unsigned char g_stage0[WS_STAGE];  // operands of even chunks
+__shared__ __attribute__((aligned(16))) unsigned char g_stage1[WS_STAGE];  // operands of odd chunks
+// O of a chunk, fp16: block (rt, w) holds math wave w's accumulator tile rt in
+// C layout, lane (g, i) at g * kOGrp + i * 16 + (i / 8) * 16.  The padding makes
+// the epilogue's transposing 4-byte reads hit 64 different banks.
+constexpr int kOGrp = 288;
+constexpr int kOBlk = 4 * kOGrp;
+__shared__ __attribute__((aligned(16))) unsigned char g_O[16 * kOBlk];
+static_assert(2 * WS_STAGE + 16 * kOBlk <= 160 * 1024, "inter-chunk LDS exceeds 160 KiB");
+
+template <int P>
+__device__ __forceinline__ unsigned char* stage_buf() {
+  if constexpr (P == 0) return g_stage0;
+  else return g_stage1;
+}
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copy one chunk's staged operands (56 fragments of 1 KiB) from the workspace
-// into an LDS buffer with direct-to-LDS loads (no registers): wave w moves
+// Copy one chunk's staged operands (64 fragments of 1 KiB) from the workspace
+// into staging buffer P with direct-to-LDS loads (no registers): wave w moves
 // fragments w, w + 4, ...; lane l's 16 bytes land at offset 16 l of the
 // fragment.  Completion is tracked by the vector memory counter only, so the
 // consumer waits with s_waitcnt vmcnt(0) and a barrier.
-__device__ __forceinline__ void stage_dma(const unsigned char* chunk, unsigned char* buf, int w, int lane) {
+template <int P>
+__device__ __forceinline__ void stage_dma(const unsigned char* chunk, int w, int lane) {
 #pragma unroll
   for (int q = 0; q < kStageQ; ++q) {
     const int f = w + 4 * q;
-    __builtin_amdgcn_global_load_lds(chunk + f * kFrag + lane * 16, (lds_void*)(buf + f * kFrag), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(chunk + f * kFrag + lane * 16, (lds_void*)(stage_buf<P>() + f * kFrag), 16, 0,
+                                     0);
   }
 }
 
 template <bool OUT_BF16>
 __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int H = p.H, T = p.T;
   const int bh = blockIdx.x;
   const int b = bh / H, h = bh - b * H;
@@ -629,7 +651,6 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   const int nc = p.n_chunks;
   const unsigned char* wsh = p.ws + (size_t)bh * nc * WS_CHUNK;
   const int col0 = 32 * w;
-  half8* sO = reinterpret_cast<half8*>(smem + B_O);
 
   // math waves: S[m][ct] element e = S[channel perm_row(16m + 4g + e)][col0 + 16ct + i]
   f4 S[8][2];
@@ -648,7 +669,8 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
             S[m][ct][e] = p.S_in[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i];
     }
   } else if (nc > 0) {
-    stage_dma(wsh, smem, w, lane);
+    stage_dma<0>(wsh, w, lane);
+    __builtin_amdgcn_s_waitcnt(0);  // chunk 0's operands land before the first B1
   }
 
   // Two loops with the same barriers, one per role, so that the state is live
@@ -657,22 +679,25 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   // waves waited for their copies), O(j-1) is complete, and nobody reads the
   // buffer copied next.
   if (math) {
-    // V of this wave's columns, loaded one chunk ahead (C layout, fp16)
-    uint4 vtn[4];
+    // V of this wave's columns (C layout, fp16), loaded one chunk ahead into
+    // the register set of the chunk's parity
+    uint4 vt[2][4];
     if (nc > 0) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        vtn[rt] = *reinterpret_cast<const uint4*>(wsh + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
+        vt[0][rt] = *reinterpret_cast<const uint4*>(wsh + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
     }
-    for (int j = 0; j <= nc; ++j) {
+    // one chunk; P = j & 1 picks the staging buffer and the V registers
+    auto step = [&](auto parity, int j) {
+      constexpr int P = decltype(parity)::value;
       __builtin_amdgcn_s_waitcnt(0);
       lds_barrier();  // B1
       f4 O[4][2], X[4][2];
-      const unsigned char* sb = smem + (j & 1) * WS_STAGE;
+      const unsigned char* sb = stage_buf<P>();
       if (j < nc) {
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt) {
-          const half8 v8 = __builtin_bit_cast(half8, vtn[rt]);
+          const half8 v8 = __builtin_bit_cast(half8, vt[P][rt]);
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             X[rt][ct] = f4{(float)v8[4 * ct], (float)v8[4 * ct + 1], (float)v8[4 * ct + 2], (float)v8[4 * ct + 3]};
@@ -683,7 +708,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           const unsigned char* wn = wsh + (size_t)(j + 1) * WS_CHUNK;
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
-            vtn[rt] = *reinterpret_cast<const uint4*>(wn + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
+            vt[1 - P][rt] = *reinterpret_cast<const uint4*>(wn + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
         }
         // X = V + (-(K e^G)) S and (Q e^G) S, one 32-row step of S at a time:
         // its B operands are rows 16(2k + s) + 4g + e, s = 0, 1
@@ -755,7 +780,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
             }
           const float ox[8] = {O[rt][0][0], O[rt][0][1], O[rt][0][2], O[rt][0][3],
                                O[rt][1][0], O[rt][1][1], O[rt][1][2], O[rt][1][3]};
-          sO[(rt * 4 + w) * 64 + lane] = to_half8(ox);
+          *reinterpret_cast<half8*>(g_O + (rt * 4 + w) * kOBlk + g * kOGrp + i * 16 + (i >> 3) * 16) = to_half8(ox);
         }
         // S <- e^{G_C} S + (K e^{G_C - G})^T U
 #pragma unroll
@@ -776,59 +801,91 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           }
         }
       }
+    };
+    for (int j = 0; j <= nc; j += 2) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
     }
   } else {
-    for (int j = 0; j <= nc; ++j) {
-      __builtin_amdgcn_s_waitcnt(0);
-      lds_barrier();  // B1
-      // ---- epilogue of chunk j-1: token tile r = w ----------------------------
-      // element [e][w'][ct]: token 16w + 4g + e, column 32w' + 16ct + i
-      float ov[4][4][2];
-      uint16_t gt[4][4][2];
-      const int c0 = (p.c_begin + j - 1) * kC;
+    // lane (u, q) = (lane / 8, lane % 8) of epilogue wave r = w: tokens
+    // 16r + 2u + tt (tt = 0, 1) of the previous chunk, columns 64s + 8q + c
+    // (s = 0, 1; c = 0..7), so that gate and output move in 16-byte pieces.
+    const int u = lane >> 3, q = lane & 7;
+    const int tk0 = 16 * w + 2 * u;
+    // In g_O: block (w, 2s + q / 4); C-layout lane (u / 2, 8 (q % 2) + c),
+    // element 4 ((q / 2) % 2) + 2 (u % 2) + tt; one 4-byte read gives both tokens.
+    const int obase = (u >> 1) * kOGrp + (q & 1) * 144 + ((q >> 1) & 1) * 8 + (u & 1) * 4;
+    // gate of the chunk normalised next, loaded one chunk ahead: [tt][s], 8 bf16
+    uint4 gt[2][2];
+    auto load_gate = [&](int jc) {
+      const int c0 = (p.c_begin + jc) * kC;
       const int nv = min(kC, T - c0);
-      if (j >= 1) {
 #pragma unroll
-        for (int w2 = 0; w2 < 4; ++w2) {
-          const half8 o8 = sO[(w * 4 + w2) * 64 + lane];
+      for (int tt = 0; tt < 2; ++tt) {
+        const int tk = min(tk0 + tt, nv - 1);
+        const uint16_t* gr =
+            reinterpret_cast<const uint16_t*>(p.gate) + (((size_t)b * T + c0 + tk) * H + h) * kD + 8 * q;
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            ov[e][w2][0] = (float)o8[e];
-            ov[e][w2][1] = (float)o8[4 + e];
-          }
-        }
-        const uint16_t* gb = reinterpret_cast<const uint16_t*>(p.gate) + (((size_t)b * T + c0) * H + h) * kD + i;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint16_t* ge = gb + (size_t)min(16 * w + 4 * g + e, nv - 1) * H * kD;
-#pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-            for (int ct = 0; ct < 2; ++ct) gt[e][w2][ct] = ge[32 * w2 + 16 * ct];
-        }
+        for (int s2 = 0; s2 < 2; ++s2) gt[tt][s2] = *reinterpret_cast<const uint4*>(gr + 64 * s2);
       }
-      if (j + 1 < nc) stage_dma(wsh + (size_t)(j + 1) * WS_CHUNK, smem + ((j + 1) & 1) * WS_STAGE, w, lane);
-      lds_barrier();  // B2: O(j-1) is in registers
+    };
+    if (nc > 0) load_gate(0);
+    // one chunk; P = j & 1 picks the staging buffer the next chunk goes to
+    auto step = [&](auto parity, int j) {
+      constexpr int P = decltype(parity)::value;
+      // No memory wait before B1: this wave's copy of chunk j was waited for
+      // after B2 of the previous chunk, and its stores need no wait.
+      lds_barrier();  // B1
+      if (j + 1 < nc) stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
+      // ---- epilogue of chunk j-1 ----------------------------------------------------
+      float ov[2][2][8];
       if (j >= 1) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+          for (int c = 0; c < 8; ++c) {
+            const hf2 o2 = *reinterpret_cast<const hf2*>(g_O + (w * 4 + 2 * s2 + (q >> 2)) * kOBlk + obase + 16 * c);
+            ov[0][s2][c] = (float)o2[0];
+            ov[1][s2][c] = (float)o2[1];
+          }
+      }
+      lds_barrier();  // B2: O(j-1) is in registers
+      // The copy of chunk j + 1 (it must land before B1 of chunk j + 1), the
+      // gate loaded a chunk ago and the previous chunk's stores: one wait here,
+      // before this chunk's stores, so that those are never waited on.
+      __builtin_amdgcn_s_waitcnt(0);
+      if (j >= 1) {
+        const int c0 = (p.c_begin + j - 1) * kC;
+        const int nv = min(kC, T - c0);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
           float ss = 0.f;
 #pragma unroll
-          for (int w2 = 0; w2 < 4; ++w2) ss += ov[e][w2][0] * ov[e][w2][0] + ov[e][w2][1] * ov[e][w2][1];
-          ss = group_sum<16>(ss);
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) ss += ov[tt][s2][c] * ov[tt][s2][c];
+          ss = group_sum<8>(ss);
           const float rs = fast_rsq(ss * (1.0f / kD) + kRmsEps);
-          const int tk = 16 * w + 4 * g + e;
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2)
+#pragma unroll
+            for (int c = 0; c < 8; ++c) ov[tt][s2][c] *= rs * sigmoidf_(bf16_at(gt[tt][s2], c));
+        }
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+          const int tk = tk0 + tt;
           if (tk < nv) {
-            const size_t ob = (((size_t)b * T + c0 + tk) * H + h) * kD + i;
+            const size_t ob = (((size_t)b * T + c0 + tk) * H + h) * kD + 8 * q;
 #pragma unroll
-            for (int w2 = 0; w2 < 4; ++w2)
-#pragma unroll
-              for (int ct = 0; ct < 2; ++ct)
-                store1<OUT_BF16>(p.o, ob + 32 * w2 + 16 * ct,
-                                 ov[e][w2][ct] * rs * sigmoidf_(bf16_to_f(gt[e][w2][ct])));
+            for (int s2 = 0; s2 < 2; ++s2) store8<OUT_BF16>(p.o, ob + 64 * s2, ov[tt][s2]);
           }
         }
       }
+      if (j >= 1 && j < nc) load_gate(j);
+    };
+    for (int j = 0; j <= nc; j += 2) {
+      step(std::integral_constant<int, 0>{}, j);
+      if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
     }
   }
 
@@ -902,10 +959,8 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
   const SlabPlan pl = plan_slabs(a, a.workspace_bytes);
   const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, ALds::BYTES);
-  const hipError_t e2 = hipFuncSetAttribute(reinterpret_cast<const void*>(&inter_chunk_kernel<OB>),
-                                            hipFuncAttributeMaxDynamicSharedMemorySize, B_BYTES);
-  if (e1 != hipSuccess || e2 != hipSuccess) {
-    set_error("prefill: hipFuncSetAttribute failed: %s", hipGetErrorString(e1 != hipSuccess ? e1 : e2));
+  if (e1 != hipSuccess) {
+    set_error("prefill: hipFuncSetAttribute failed: %s", hipGetErrorString(e1));
     return KDA_E_HIP;
   }
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
@@ -933,7 +988,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
         return KDA_E_HIP;
       }
     }
-    hipLaunchKernelGGL((inter_chunk_kernel<OB>), dim3((unsigned)(a.B * a.H)), dim3(512), B_BYTES, st, p);
+    hipLaunchKernelGGL((inter_chunk_kernel<OB>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, st, p);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) {
       set_error("prefill: inter-chunk launch failed: %s", hipGetErrorString(e));
