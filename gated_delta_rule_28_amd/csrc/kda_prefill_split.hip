@@ -921,37 +921,126 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   }
 }
 
-// How the chunks of one call are split into launches ("slabs") that fit the
-// workspace: one slab when all chunk blocks fit (and stay under the cap), else
-// as many chunks per slab as fit next to a state carry buffer.
+// How the chunks of one call are split into launches ("slabs").
+//
+// Pipelined (a sequence of more than kPipeChunks chunks and B*H at most half
+// the compute units): slabs of about kPipeChunks chunks in kPipeBufs workspace
+// buffers.  The inter-chunk kernel (one workgroup per (b, h), the state carried
+// between slabs in a buffer) runs on a stream restricted to B*H compute units,
+// the intra-chunk kernel of the next slab on a stream restricted to the others,
+// so the two overlap without competing for compute units.
+// Otherwise: one slab when all chunk blocks fit the workspace (and stay under
+// the cap), else as many chunks per slab as fit next to the state carry, one
+// slab after the other on the caller's stream.
+constexpr int kPipeChunks = 64;
+constexpr int kPipeBufs = 3;  // the intra-chunk kernel runs up to two slabs ahead
+constexpr int kPlanCUs = 256;  // compute units the preferred workspace is planned for
+
 struct SlabPlan {
-  int nchunks, per_slab, nslabs;
-  size_t chunk_bytes, carry_bytes;
+  int nchunks, per_slab, nslabs, nbuf;
+  size_t region_bytes, carry_bytes;
 };
 
 size_t per_chunk_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * WS_CHUNK; }
 size_t carry_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * kD * kD * 4; }
+bool pipe_shape(const kda_prefill_args& a, int ncu) { return 2L * a.B * a.H <= ncu; }
 
 SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail) {
   SlabPlan s{};
   s.nchunks = (a.T + kC - 1) / kC;
+  s.nbuf = 1;
   const size_t pc = per_chunk_bytes(a);
-  const size_t room = avail < kSlabBytesMax ? avail : kSlabBytesMax;
-  if ((size_t)s.nchunks * pc <= room) {
-    s.per_slab = s.nchunks > 0 ? s.nchunks : 1;
-    s.nslabs = 1;
-    s.carry_bytes = 0;
-  } else {
-    const size_t cb = carry_bytes(a);
-    const size_t room2 = avail < kSlabBytesMax + cb ? avail : kSlabBytesMax + cb;
-    const size_t per = room2 > cb + pc ? (room2 - cb) / pc : 1;
-    const int most = (int)(per < (size_t)s.nchunks ? per : (size_t)s.nchunks);
+  const size_t cb = carry_bytes(a);
+  if (s.nchunks > kPipeChunks && pipe_shape(a, kPlanCUs) && avail >= cb + kPipeBufs * pc) {
+    const size_t fit = (avail - cb) / (kPipeBufs * pc);
+    const int most = (int)(fit < (size_t)kPipeChunks ? fit : (size_t)kPipeChunks);
     s.nslabs = (s.nchunks + most - 1) / most;
     s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;  // balanced slabs, no small tail
-    s.carry_bytes = s.nslabs > 1 ? cb : 0;
+    s.nbuf = s.nslabs < kPipeBufs ? s.nslabs : kPipeBufs;
+    s.carry_bytes = cb;
+  } else {
+    const size_t room = avail < kSlabBytesMax ? avail : kSlabBytesMax;
+    if ((size_t)s.nchunks * pc <= room) {
+      s.per_slab = s.nchunks > 0 ? s.nchunks : 1;
+      s.nslabs = 1;
+      s.carry_bytes = 0;
+    } else {
+      const size_t room2 = avail < kSlabBytesMax + cb ? avail : kSlabBytesMax + cb;
+      const size_t per = room2 > cb + pc ? (room2 - cb) / pc : 1;
+      const int most = (int)(per < (size_t)s.nchunks ? per : (size_t)s.nchunks);
+      s.nslabs = (s.nchunks + most - 1) / most;
+      s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;
+      s.carry_bytes = s.nslabs > 1 ? cb : 0;
+    }
   }
-  s.chunk_bytes = (size_t)s.per_slab * pc;
+  s.region_bytes = (size_t)s.per_slab * pc;
   return s;
+}
+
+// The compute-unit-restricted streams of the pipeline (default priority) and
+// the events that order them, per host thread and device, for one inter-chunk
+// width (B*H rounded up to a multiple of 8, so each of the eight accelerator
+// dies gets the same share: mask bits interleave over the dies).  Slabs
+// alternate between two intra-chunk streams, so the event recorded after one
+// slab's intra-chunk kernel never holds back the next one's start.  Created on
+// first use and kept for the life of the thread.
+struct Pipe {
+  int n_inter = 0;
+  hipStream_t intra[2] = {nullptr, nullptr}, inter = nullptr;
+  hipEvent_t fork = nullptr, a_done[2] = {nullptr, nullptr}, b_done[kPipeBufs] = {};
+  hipEvent_t join[3] = {nullptr, nullptr, nullptr};
+};
+
+// 0 and pp = nullptr when the device has too few compute units to split.
+int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
+  constexpr int kMaxDev = 64, kPerDev = 4;
+  static thread_local Pipe pipes[kMaxDev][kPerDev];
+  static thread_local int ncus[kMaxDev];
+  pp = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    set_error("prefill: hipGetDevice failed or device %d out of range", dev);
+    return KDA_E_HIP;
+  }
+  if (ncus[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0) {
+      set_error("prefill: compute unit count query failed: %s", hipGetErrorString(e));
+      return KDA_E_HIP;
+    }
+    ncus[dev] = n;
+  }
+  const int ncu = ncus[dev];
+  if (!pipe_shape(a, ncu)) return KDA_OK;
+  const int n_inter = (int)((a.B * a.H + 7) / 8 * 8);
+  if (n_inter >= ncu) return KDA_OK;
+  Pipe* slot = nullptr;
+  for (int k = 0; k < kPerDev && slot == nullptr; ++k)
+    if (pipes[dev][k].n_inter == n_inter) slot = &pipes[dev][k];
+  for (int k = 0; k < kPerDev && slot == nullptr; ++k)
+    if (pipes[dev][k].n_inter == 0) slot = &pipes[dev][k];
+  if (slot == nullptr) return KDA_OK;  // every slot holds another width: run unpipelined
+  if (slot->n_inter == 0) {
+    uint32_t m_inter[32] = {0}, m_intra[32] = {0};
+    const int nb = ncu < 32 * 32 ? ncu : 32 * 32;
+    for (int c = 0; c < nb; ++c) (c < n_inter ? m_inter : m_intra)[c / 32] |= 1u << (c % 32);
+    const uint32_t words = (uint32_t)((nb + 31) / 32);
+    e = hipExtStreamCreateWithCUMask(&slot->inter, words, m_inter);
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipExtStreamCreateWithCUMask(&slot->intra[k], words, m_intra);
+    hipEvent_t* evs[6 + kPipeBufs] = {&slot->fork, &slot->a_done[0], &slot->a_done[1],
+                                      &slot->join[0], &slot->join[1], &slot->join[2]};
+    for (int k = 0; k < kPipeBufs; ++k) evs[6 + k] = &slot->b_done[k];
+    for (int k = 0; k < 6 + kPipeBufs && e == hipSuccess; ++k) e = hipEventCreateWithFlags(evs[k], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      set_error("prefill: stream / event creation failed: %s", hipGetErrorString(e));
+      return KDA_E_HIP;
+    }
+    slot->n_inter = n_inter;
+  }
+  pp = slot;
+  return KDA_OK;
 }
 
 template <bool OB>
@@ -963,9 +1052,25 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
     set_error("prefill: hipFuncSetAttribute failed: %s", hipGetErrorString(e1));
     return KDA_E_HIP;
   }
+  Pipe* pp = nullptr;
+  if (pl.nbuf > 1) {
+    const int rc = get_pipe(a, pp);
+    if (rc != KDA_OK) return rc;
+  }
+  const bool piped = pp != nullptr;
+  hipStream_t sb = piped ? pp->inter : st;
   unsigned char* ws = static_cast<unsigned char*>(a.workspace);
-  float* carry = pl.carry_bytes ? reinterpret_cast<float*>(ws + pl.chunk_bytes) : nullptr;
-  for (int sl = 0; sl < pl.nslabs; ++sl) {
+  float* carry = pl.carry_bytes ? reinterpret_cast<float*>(ws + pl.nbuf * pl.region_bytes) : nullptr;
+  hipError_t e = hipSuccess;
+  const char* what = "event";
+  if (piped) {
+    // both streams start after everything already queued on the caller's
+    e = hipEventRecord(pp->fork, st);
+    if (e == hipSuccess) e = hipStreamWaitEvent(pp->intra[0], pp->fork, 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(pp->intra[1], pp->fork, 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(sb, pp->fork, 0);
+  }
+  for (int sl = 0; sl < pl.nslabs && e == hipSuccess; ++sl) {
     SplitParams p{};
     p.B = a.B; p.T = a.T; p.H = a.H;
     p.c_begin = sl * pl.per_slab;
@@ -978,22 +1083,47 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
     p.o = a.o;
     p.S_out = last ? a.S_T : carry;
     p.conv_out = last ? a.conv_out : nullptr;
-    p.ws = ws;
-    if (p.n_chunks > 0) {
+    const int buf = sl % pl.nbuf;
+    p.ws = ws + (size_t)buf * pl.region_bytes;
+    hipStream_t sa = piped ? pp->intra[sl & 1] : st;
+    // the buffer is free once the inter-chunk kernel of slab sl - nbuf is done
+    if (piped && sl >= pl.nbuf) e = hipStreamWaitEvent(sa, pp->b_done[buf], 0);
+    if (e == hipSuccess && p.n_chunks > 0) {
       const size_t grid = (size_t)p.n_chunks * a.B * a.H;
-      hipLaunchKernelGGL(intra_chunk_kernel, dim3((unsigned)grid), dim3(256), ALds::BYTES, st, p);
-      const hipError_t e = hipGetLastError();
-      if (e != hipSuccess) {
-        set_error("prefill: intra-chunk launch failed: %s", hipGetErrorString(e));
-        return KDA_E_HIP;
-      }
+      hipLaunchKernelGGL(intra_chunk_kernel, dim3((unsigned)grid), dim3(256), ALds::BYTES, sa, p);
+      e = hipGetLastError();
+      what = "intra-chunk launch";
     }
-    hipLaunchKernelGGL((inter_chunk_kernel<OB>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, st, p);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) {
-      set_error("prefill: inter-chunk launch failed: %s", hipGetErrorString(e));
-      return KDA_E_HIP;
+    if (e == hipSuccess && piped) {
+      what = "event";
+      e = hipEventRecord(pp->a_done[sl & 1], sa);
+      if (e == hipSuccess) e = hipStreamWaitEvent(sb, pp->a_done[sl & 1], 0);
     }
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((inter_chunk_kernel<OB>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, sb, p);
+      e = hipGetLastError();
+      what = "inter-chunk launch";
+    }
+    if (e == hipSuccess && piped) {
+      what = "event";
+      e = hipEventRecord(pp->b_done[buf], sb);
+    }
+  }
+  if (piped) {
+    // the caller's stream resumes after the three streams' work (also on an error
+    // above, so that nothing of this call is left unordered)
+    hipStream_t all[3] = {pp->intra[0], pp->intra[1], sb};
+    hipError_t j = hipSuccess;
+    for (int k = 0; k < 3 && j == hipSuccess; ++k) j = hipEventRecord(pp->join[k], all[k]);
+    for (int k = 0; k < 3 && j == hipSuccess; ++k) j = hipStreamWaitEvent(st, pp->join[k], 0);
+    if (e == hipSuccess && j != hipSuccess) {
+      e = j;
+      what = "event";
+    }
+  }
+  if (e != hipSuccess) {
+    set_error("prefill: %s failed: %s", what, hipGetErrorString(e));
+    return KDA_E_HIP;
   }
   return KDA_OK;
 }
@@ -1007,7 +1137,7 @@ bool prefill_split_eligible(const kda_prefill_args& a) {
 size_t prefill_split_workspace_bytes(const kda_prefill_args& a) {
   if (!prefill_split_eligible(a)) return 0;
   const SlabPlan pl = plan_slabs(a, ~(size_t)0);
-  return pl.chunk_bytes + pl.carry_bytes;
+  return pl.nbuf * pl.region_bytes + pl.carry_bytes;
 }
 
 size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a) {

@@ -85,6 +85,15 @@ enum {
  *    in the workspace.  For other sizes the workspace is unused.
  *  - workspace == NULL: one kernel per (b, h) walks the chunks and keeps every
  *    intermediate on chip (no device memory beyond the arguments).
+ *    A sequence of more than 64 chunks with 2*B*H at most the device's
+ *    compute units runs in slabs of up to 64 chunks through up to three
+ *    workspace buffers: the per-(b, h) kernel of one slab runs on a stream
+ *    restricted to B*H (rounded up to 8) compute units while the all-chunks
+ *    kernels of the next slabs run on two streams restricted to the others.
+ *    The library creates these three streams (default priority) and their
+ *    events once per host thread, device and B*H, keeps them for the life of
+ *    the thread, starts them after the work already queued on `stream` and
+ *    makes `stream` wait for all three before any later work.
  * The library owns no device memory: the caller allocates the workspace and
  * may reuse it once the call's work on `stream` has finished.
  */
@@ -112,10 +121,13 @@ typedef struct kda_prefill_args {
 int kda_prefill(const kda_prefill_args* args, void* stream);
 
 /* Device workspace the two-kernel path prefers for these sizes: 80 KiB per
- * (b, h, chunk of 64 tokens), capped near 16 GiB (plus B*H*dk*dv*4 bytes to
- * carry the state) by processing long sequences in slabs of chunks.  0 when
- * the sizes have no two-kernel path or the arguments are invalid.  The fields
- * B, T, H, dk, dv, chunk, in_dtype and out_dtype are read; pointers are not. */
+ * (b, h, chunk of 64 tokens) of one slab; for a pipelined sequence (more than
+ * 64 chunks, 2*B*H <= 256) three buffers of one slab of up to 64 chunks (two
+ * when there are two slabs) plus B*H*dk*dv*4 bytes to carry the state; otherwise all chunks in one slab,
+ * capped near 16 GiB (plus the carry) by running longer sequences in slabs
+ * one after the other.  0 when the sizes have no two-kernel path or the
+ * arguments are invalid.  The fields B, T, H, dk, dv, chunk, in_dtype and
+ * out_dtype are read; pointers are not. */
 size_t kda_prefill_workspace_bytes(const kda_prefill_args* args);
 
 /* Smallest workspace the two-kernel path accepts (one chunk per slab): any size

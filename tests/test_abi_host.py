@@ -143,14 +143,14 @@ def test_prefill_workspace_sizes_and_check(kda):
     mis = _prefill_args(kda, B=2, T=300, H=3, dk=128, dv=128, chunk=64, workspace=0x100008,
                         workspace_bytes=10 * per_chunk)
     assert L.kda_prefill(ctypes.byref(mis), None) == -4
-    # 1M tokens at K3 width in one call: balanced slabs keep the workspace under 16 GiB
-    big = _prefill_args(kda, B=1, T=1 << 20, H=96, dk=128, dv=128, chunk=64)
-    nb = L.kda_prefill_workspace_bytes(ctypes.byref(big))
-    nslabs = -(-16384 * 96 * 80 * 1024 // (16 << 30))
-    assert nb == -(-16384 // nslabs) * 96 * 80 * 1024 + 96 * 128 * 128 * 4 and nb - 96 * 128 * 128 * 4 <= 16 << 30
-    # K3 width (65536 tokens, 8.6 GB of chunk blocks) fits one launch
-    k3 = _prefill_args(kda, B=1, T=1 << 16, H=96, dk=128, dv=128, chunk=64)
-    assert L.kda_prefill_workspace_bytes(ctypes.byref(k3)) == 1024 * 96 * 80 * 1024
+    # longer sequences run in pipelined slabs of 64 chunks with three buffers and
+    # a state carry: the same size for 65,536 and 1,048,576 tokens at K3 width
+    for T in (1 << 16, 1 << 20):
+        big = _prefill_args(kda, B=1, T=T, H=96, dk=128, dv=128, chunk=64)
+        assert L.kda_prefill_workspace_bytes(ctypes.byref(big)) == 3 * 64 * 96 * 80 * 1024 + 96 * 128 * 128 * 4
+    # 65 chunks: two balanced slabs of 33, one buffer each
+    b65 = _prefill_args(kda, B=1, T=65 * 64, H=2, dk=128, dv=128, chunk=64)
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(b65)) == 2 * 33 * 2 * 80 * 1024 + 2 * 128 * 128 * 4
 
 
 def test_decode_validation_codes(kda):

@@ -142,6 +142,25 @@ def test_slabs_of_a_small_workspace(oracle_mod, per_slab):
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{per_slab} chunk(s) per launch")
 
 
+@pytest.mark.parametrize("per_buf", [None, 10])
+def test_pipelined_slabs(oracle_mod, per_buf):
+    """70 chunks (T = 4480) exceed one slab of 64 chunks: the preferred
+    workspace runs two slabs of 35 on streams restricted to disjoint compute
+    units, the state carried between them; a workspace with room for three
+    buffers of 10 chunks runs 7 slabs, so every buffer is reused."""
+    torch, kda = need_gpu()
+    w = Workload("pp", 1, 70 * 64, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=17)
+    inp = syn.prefill_inputs_np(w)
+    dev = to_dev(inp, "bf16")
+    per_chunk = w.B * w.H * 80 * 1024
+    carry = w.B * w.H * w.dk * w.dv * 4
+    assert kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv) == 2 * 35 * per_chunk + carry
+    ws = "auto" if per_buf is None else torch.empty(3 * per_buf * per_chunk + carry, dtype=torch.uint8,
+                                                     device="cuda")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=ws)
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"pipelined slabs, buffers of {per_buf or 35} chunks")
+
+
 def test_paths_agree(oracle_mod):
     """Both paths on the same inputs agree to well within the tolerance."""
     torch, kda = need_gpu()
