@@ -139,27 +139,49 @@ __device__ __forceinline__ f4 mma16(const half8& a, const half8& b, const f4& c,
   return mma_f16(a, b, c);
 }
 
+// a + w1 * t_{-1} + w2 * t_{-2} + w3 * t_{-3} for a causal conv along the
+// 16 lanes of a row: t_{-j} at lane i is z_j of lane (i - j) mod 16 (row
+// rotation by j), where z_j is the lane's halo value y in lanes 16 - j .. 15
+// and its own value x elsewhere.  The three selects come first so that each
+// rotated read is two instructions after the write of its source (the DPP
+// read-after-write wait), and each rotation is folded into its multiply-add,
+// so no rotated copy occupies a register.
+__device__ __forceinline__ float conv3_dpp(float a, float x, float y, float w1, float w2, float w3) {
+  float z1, z2, z3;
+  asm("v_cndmask_b32_e64 %0, %4, %5, %6\n\t"
+      "v_cndmask_b32_e64 %1, %4, %5, %7\n\t"
+      "v_cndmask_b32_e64 %2, %4, %5, %8\n\t"
+      "v_fmac_f32_dpp %3, %0, %9 row_ror:1 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %1, %10 row_ror:2 row_mask:0xf bank_mask:0xf\n\t"
+      "v_fmac_f32_dpp %3, %2, %11 row_ror:3 row_mask:0xf bank_mask:0xf"
+      : "=&v"(z1), "=&v"(z2), "=&v"(z3), "+v"(a)
+      : "v"(x), "v"(y), "s"(0x8000800080008000ull), "s"(0xC000C000C000C000ull), "s"(0xE000E000E000E000ull),
+        "v"(w1), "v"(w2), "v"(w3));
+  return a;
+}
+
 // Causal depthwise conv (kernel 4) + SiLU of one tensor for this lane's token
 // and 32 channels.  `cur` are the raw token's channels, `hal` the raw values of
-// the token 16 positions earlier (only lanes 13..15 carry them: the three
-// tokens before the tile), `cw` this lane's taps (32k + e indexing).
-__device__ __forceinline__ void conv_silu(const uint4 (&cur)[4], const uint4 (&hal)[4], bool hok, bool valid,
-                                          const float4* cw, float (&x)[32]) {
+// the token 16 positions earlier (used in lanes 13..15 only: the three tokens
+// before the tile; zero when there are none), `cw` this lane's taps (32k + e
+// indexing).  Token t - j is lane i - j of the row, or for i < j the halo of
+// lane 16 + i - j: a rotation by j of the row in which lanes 16 - j .. 15
+// offer their halo instead of their own token.
+// `sink(kp, x8)` takes the 8 outputs of channel group kp.
+template <typename Sink>
+__device__ __forceinline__ void conv_silu(const uint4 (&cur)[4], const uint4 (&hal)[4], const float4* cw,
+                                          Sink&& sink) {
 #pragma unroll
   for (int kp = 0; kp < 4; ++kp) {
+    float x[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const float xc = bf16_at(cur[kp], e);
-      const float y = hok ? bf16_at(hal[kp], e) : 0.f;
+      const float y = bf16_at(hal[kp], e);
       const float4 w = cw[32 * kp + e];
-      // token t-j: lane i-j of the row, or for i < j the halo in lane 16+i-j
-      // (a rotation written to lanes 0..3 only)
-      float a = w.w * xc;
-      a += w.z * (dppf<0x111, 0xF>(xc) + dppf<0x121, 0x1>(y));
-      a += w.y * (dppf<0x112, 0xF>(xc) + dppf<0x122, 0x1>(y));
-      a += w.x * (dppf<0x113, 0xF>(xc) + dppf<0x123, 0x1>(y));
-      x[8 * kp + e] = valid ? siluf_(a) : 0.f;
+      x[e] = siluf_(conv3_dpp(w.w * xc, xc, y, w.z, w.y, w.x));
     }
+    sink(kp, x);
   }
 }
 
@@ -260,32 +282,40 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   const size_t row = ((size_t)b * T + c0 + min(tok, n_valid - 1)) * H + h;
   const int th = c0 + 16 * wave - 16 + max(i, 13);  // lanes 13..15: tokens before the tile
   const bool h_in = th >= 0;
-  const bool hok = i >= 13 && (h_in || p.conv_in != nullptr);
+  // the tile has earlier tokens (the same for lanes 13..15: c0 + 16 wave is a
+  // multiple of 16), in the sequence or in the conv history
+  const bool hok = c0 + 16 * wave > 0 || p.conv_in != nullptr;
   const size_t hrow = ((size_t)b * T + min(max(th, 0), T - 1)) * H + h;
   const size_t hist = ((size_t)b * 3 + (3 + max(th, -3))) * cch;  // conv_in row when th < 0
   const bool from_hist = !h_in && p.conv_in != nullptr;
-  uint4 rq[4], rk[4], rv[4], rg[4], hq[4], hk[4], hv[4];
-  {
-    const uint16_t* q16 = reinterpret_cast<const uint16_t*>(p.q);
-    const uint16_t* k16 = reinterpret_cast<const uint16_t*>(p.k);
-    const uint16_t* v16 = reinterpret_cast<const uint16_t*>(p.v);
-    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.g);
-    const uint16_t* ci16 = reinterpret_cast<const uint16_t*>(p.conv_in);
+  // Raw q / k / v (this token and the halo) of one tensor, loaded while the
+  // previous tensor is processed: at most two tensors' raw values are live.
+  const uint16_t* ci16 = reinterpret_cast<const uint16_t*>(p.conv_in);
+  const uint32_t hm = hok ? ~0u : 0u;  // no earlier tokens: the halo is zero
+  auto load_raw = [&](const void* src, int part, uint4 (&r)[4], uint4 (&hr)[4]) {
+    const uint16_t* x16 = reinterpret_cast<const uint16_t*>(src);
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
       const int cl = 32 * kp + 8 * g;
-      rq[kp] = *reinterpret_cast<const uint4*>(q16 + row * kD + cl);
-      rk[kp] = *reinterpret_cast<const uint4*>(k16 + row * kD + cl);
-      rv[kp] = *reinterpret_cast<const uint4*>(v16 + row * kD + cl);
-      rg[kp] = *reinterpret_cast<const uint4*>(g16 + row * kD + cl);
-      const uint16_t* pq = from_hist ? ci16 + hist + (size_t)h * kD + cl : q16 + hrow * kD + cl;
-      const uint16_t* pk = from_hist ? ci16 + hist + (size_t)H * kD + (size_t)h * kD + cl : k16 + hrow * kD + cl;
-      const uint16_t* pv = from_hist ? ci16 + hist + (size_t)2 * H * kD + (size_t)h * kD + cl : v16 + hrow * kD + cl;
-      hq[kp] = *reinterpret_cast<const uint4*>(pq);
-      hk[kp] = *reinterpret_cast<const uint4*>(pk);
-      hv[kp] = *reinterpret_cast<const uint4*>(pv);
+      r[kp] = *reinterpret_cast<const uint4*>(x16 + row * kD + cl);
+      const uint16_t* ph =
+          from_hist ? ci16 + hist + (size_t)part * H * kD + (size_t)h * kD + cl : x16 + hrow * kD + cl;
+      hr[kp] = *reinterpret_cast<const uint4*>(ph);
     }
+  };
+  auto mask_halo = [&](uint4 (&hr)[4]) {
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) {
+      hr[kp].x &= hm; hr[kp].y &= hm; hr[kp].z &= hm; hr[kp].w &= hm;
+    }
+  };
+  uint4 rg[4], ra[4], ha[4], rb[4], hb[4];
+  {
+    const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.g);
+#pragma unroll
+    for (int kp = 0; kp < 4; ++kp) rg[kp] = *reinterpret_cast<const uint4*>(g16 + row * kD + 32 * kp + 8 * g);
   }
+  load_raw(p.q, 0, rb, hb);  // q's raw values land during the decay-factor phase
   const float beta_v = valid ? bf16_to_f(reinterpret_cast<const uint16_t*>(p.beta)[row]) : 0.f;
 
   // conv taps of this head, per-token beta, fp16-range flag
@@ -359,7 +389,11 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   half8 QrowF[4];
   {
     float x[32];
-    conv_silu(rq, hq, hok, valid, sCW + 8 * g, x);
+    mask_halo(hb);
+    conv_silu(rb, hb, sCW + 8 * g, [&](int kp, const float* x8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
+    });
     l2norm128(x, fast_rsq((float)kD));
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
@@ -374,11 +408,17 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       *reinterpret_cast<half8*>(wsb + WS_QG + ((wave * 4 + kp) * 64 + lane) * 16) = to_half8(qg);
     }
   }
+  load_raw(p.k, 1, ra, ha);
+  __builtin_amdgcn_sched_barrier(0);
   // ---- k: rows and columns of A / P, K e^G, K e^{G_C - G} ---------------------------
   half8 KrowF[4], CdiagF[4];
   {
     float x[32];
-    conv_silu(rk, hk, hok, valid, sCW + kD + 8 * g, x);
+    mask_halo(ha);
+    conv_silu(ra, ha, sCW + kD + 8 * g, [&](int kp, const float* x8) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
+    });
     l2norm128(x, 1.0f);
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
@@ -404,13 +444,11 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     }
   }
   // ---- v -----------------------------------------------------------------------------
+  load_raw(p.v, 2, ra, ha);
+  __builtin_amdgcn_sched_barrier(0);
   half8 Vf[4];
-  {
-    float x[32];
-    conv_silu(rv, hv, hok, valid, sCW + 2 * kD + 8 * g, x);
-#pragma unroll
-    for (int kp = 0; kp < 4; ++kp) Vf[kp] = to_half8(x + 8 * kp);
-  }
+  mask_halo(ha);
+  conv_silu(ra, ha, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
   lds_barrier();
 
   // ---- A^T and P^T blocks (b, a), b <= a: D[j][r] = sum_c col_b[j][c] row_a[r][c] --
