@@ -194,11 +194,9 @@ def main():
     nbytes = prefill_bytes_per_launch(w.B, seg, w.H, w.dk, w.dv)
     flops = prefill_flops(w.B, seg, w.H, w.dk, w.dv, w.chunk)
     achieved = nbytes / (launch_ms * 1e-3) / 1e9
-    # one kda_prefill call = the two kernels of the workspace path
+    # one kda_prefill call = every slab of the two kernels of the workspace path
     src = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc", "kda_prefill_split.hip")
-    t_intra = load_traffic("intra_chunk_kernel", src)
-    t_inter = load_traffic("inter_chunk_kernel", src)
-    traffic = t_intra + t_inter if t_intra is not None and t_inter is not None else None
+    traffic = load_traffic("prefill_call", src)
     log(f"[bench] prefill {ms:.3f} ms/step, {value / 1e6:.2f} M tokens/s, {achieved:.0f} GB/s algorithmic")
 
     out = {

@@ -1,8 +1,14 @@
 """Summaries of rocprofv3 CSV output for the KDA kernels.
 
-    python -m gated_delta_rule_28_amd.profsum stats  KERNEL_STATS_CSV --cmd "..." --out FILE.md
-    python -m gated_delta_rule_28_amd.profsum traffic FETCH_CSV WRITE_CSV --cmd "..." --out FILE.md
+    python -m gated_delta_rule_28_amd.profsum stats  KERNEL_STATS_CSV [--trace KERNEL_TRACE_CSV --prefill-calls N] --cmd "..." --out FILE.md
+    python -m gated_delta_rule_28_amd.profsum traffic FETCH_CSV WRITE_CSV [--prefill-calls N] --cmd "..." --out FILE.md
     python -m gated_delta_rule_28_amd.profsum counters COUNTER_CSV --cmd "..." --out FILE.md
+
+A kda_prefill call on the two-kernel path launches the intra-chunk and the
+inter-chunk kernel once per slab of chunks, partly at the same time; with
+--prefill-calls (the number of calls in the profiled run) `stats` adds the
+average span of a call (first start to last end of its kernels) and
+`traffic` the HBM bytes of a whole call.
 
 `traffic` scales FETCH_SIZE and WRITE_SIZE (KiB per dispatch) by what the same
 counters read for the largest `neg` elementwise kernel in the run (bench.py
@@ -41,7 +47,22 @@ def _short(name, n=90):
     return name if len(name) <= n else name[:n - 3] + "..."
 
 
-def stats(path, cmd, out):
+def call_spans(trace, calls):
+    """Spans (ns) of the prefill calls: the chunk kernels of the run, in start
+    order, split into `calls` equal groups (each call launches the same slabs)."""
+    ks = [r for r in csv.DictReader(open(trace)) if "chunk_kernel" in r["Kernel_Name"]]
+    ks.sort(key=lambda r: int(r["Start_Timestamp"]))
+    if calls <= 0 or len(ks) % calls:
+        raise SystemExit(f"{trace}: {len(ks)} chunk-kernel dispatches do not split into {calls} calls")
+    per = len(ks) // calls
+    spans = []
+    for c in range(calls):
+        g = ks[c * per:(c + 1) * per]
+        spans.append(max(int(r["End_Timestamp"]) for r in g) - min(int(r["Start_Timestamp"]) for r in g))
+    return spans, per
+
+
+def stats(path, cmd, out, trace=None, calls=0):
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["# Kernel time (rocprofv3 --kernel-trace --stats)", "", "Command:", "",
@@ -51,6 +72,11 @@ def stats(path, cmd, out):
     for r in rows[:8]:
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    if trace:
+        spans, per = call_spans(trace, calls)
+        lines += ["", f"kda_prefill calls: {calls}, {per} chunk-kernel launches each (intra-chunk and inter-chunk per "
+                  f"slab, overlapping); span of a call (first start to last end): average "
+                  f"{sum(spans) / len(spans) / 1e3:.1f} us, min {min(spans) / 1e3:.1f} us, max {max(spans) / 1e3:.1f} us."]
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -85,7 +111,7 @@ def _match(d, sub):
     return names[0] if names else None
 
 
-def traffic(fetch_csv, write_csv, cmd, out, json_out):
+def traffic(fetch_csv, write_csv, cmd, out, json_out, calls=0):
     f_d, _ = _per_kernel(fetch_csv)
     w_d, _ = _per_kernel(write_csv)
     f_cal = _calib(fetch_csv, "FETCH_SIZE")
@@ -112,6 +138,22 @@ def traffic(fetch_csv, write_csv, cmd, out, json_out):
         res[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                     "source_sha256_16": source_hash(os.path.join(CSRC, src)),
                     "fetch_scale": f_scale, "write_scale": w_scale}
+    if calls > 0:
+        # a whole kda_prefill call: every dispatch of both chunk kernels, per call
+        tot_r = tot_w = 0.0
+        for key in ("intra_chunk_kernel", "inter_chunk_kernel"):
+            sub = KERNELS[key][0]
+            nf, nw = _match(f_d, sub), _match(w_d, sub)
+            if nf is None or nw is None:
+                raise SystemExit(f"no dispatches of {key} in the counter runs")
+            tot_r += sum(f_d[nf]["FETCH_SIZE"]) * 1024 * f_scale
+            tot_w += sum(w_d[nw]["WRITE_SIZE"]) * 1024 * w_scale
+        rd, wr = tot_r / calls, tot_w / calls
+        lines += ["", f"Whole kda_prefill call ({calls} calls in the run, all slabs of both chunk kernels): "
+                  f"read {rd / 1e9:.3f} GB, written {wr / 1e9:.3f} GB, total {(rd + wr) / 1e9:.3f} GB per call."]
+        res["prefill_call"] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                               "source_sha256_16": source_hash(os.path.join(CSRC, "kda_prefill_split.hip")),
+                               "fetch_scale": f_scale, "write_scale": w_scale}
     open(out, "w").write("\n".join(lines) + "\n")
     json.dump(res, open(json_out, "w"), indent=1, sort_keys=True)
 
@@ -139,6 +181,7 @@ def main():
     sub = ap.add_subparsers(dest="what", required=True)
     a = sub.add_parser("stats")
     a.add_argument("csv")
+    a.add_argument("--trace", default=None)
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -148,11 +191,13 @@ def main():
     for p in (a, b, c):
         p.add_argument("--cmd", required=True)
         p.add_argument("--out", required=True)
+    for p in (a, b):
+        p.add_argument("--prefill-calls", type=int, default=0)
     args = ap.parse_args()
     if args.what == "stats":
-        stats(args.csv, args.cmd, args.out)
+        stats(args.csv, args.cmd, args.out, args.trace, args.prefill_calls)
     elif args.what == "traffic":
-        traffic(args.fetch_csv, args.write_csv, args.cmd, args.out, args.json)
+        traffic(args.fetch_csv, args.write_csv, args.cmd, args.out, args.json, args.prefill_calls)
     else:
         counters(args.csv, args.cmd, args.out)
 
