@@ -1,10 +1,11 @@
-"""The full-size workloads on the GPU, checked on sampled heads against the oracle.
+"""The full-size workloads on the GPU, checked against the oracle: every head
+at K3 width, sampled heads and pairs for the 1M-token and decode workloads.
 
 Inputs are drawn on the device (kda_synth's torch backend) at the exact
-shapes the benchmark times; the GPU runs the whole workload; the sampled
+shapes the benchmark times; the GPU runs the whole workload; the checked
 (batch, head) pairs' inputs are copied to the host and the fp64 oracle
 recomputes those pairs over the full sequence.  The tolerance RMS is taken
-over the sampled pairs' outputs.
+over the checked pairs' outputs.
 """
 from __future__ import annotations
 
@@ -54,24 +55,29 @@ def _compare_heads(oracle_mod, picks, per_head_inputs, what, tol):
     assert_rms_close(np.stack(s_got), np.stack(s_ref), tol, f"{what} S_T")
 
 
-def test_k3width_prefill_sampled_heads(oracle_mod):
-    """B1 T65536 H96 d128, S0 ~ N(0, 0.01^2), chunk 64: four sampled heads over all
-    65536 tokens."""
+@pytest.mark.timeout(600)
+def test_k3width_prefill_all_heads(oracle_mod):
+    """B1 T65536 H96 d128, S0 ~ N(0, 0.01^2), chunk 64, at the preferred
+    workspace (the pipelined two-kernel path): every head over all 65536
+    tokens against the oracle (which takes about 10 s on 16 threads).  The
+    tolerance RMS is over the whole output; the worst single head is printed."""
     torch, kda = need_gpu()
     w = syn.WORKLOADS["k3width"]
     dev = syn.prefill_inputs_torch(w, "cuda")
     o, S_T, _ = kda.prefill(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"],
                             dev["gate"], S0=dev["S0"], chunk=w.chunk)
     torch.cuda.synchronize()
-    heads = sorted(np.random.default_rng(7).choice(w.H, 4, replace=False).tolist())
-    print(f"  sampled heads {heads}", flush=True)
-    picks, inputs = [], []
-    for h in heads:
-        inp, _ = head_inputs(dev, h, w.H, w.dk, w.dv)
-        inp["S0"] = dev["S0"][0:1, h:h + 1].cpu().numpy()
-        inputs.append(inp)
-        picks.append((o[0, :, h].float().cpu().numpy(), S_T[0, h].cpu().numpy()))
-    _compare_heads(oracle_mod, picks, inputs, "k3width", TOL_BF16)
+    host = {x: syn.torch_to_np(dev[x]) for x in ("q", "k", "v", "g", "beta", "gate")}
+    host["conv_w"] = syn.torch_to_np(dev["conv_w"])
+    host["S0"] = dev["S0"].cpu().numpy()
+    r = oracle_mod.prefill(host)  # all (b, h) pairs: o [H, T, dv], S_T [H, dk, dv]
+    o_got = o[0].float().cpu().numpy().transpose(1, 0, 2)  # [H, T, dv]
+    s_got = S_T[0].cpu().numpy()
+    rms_o = float(np.sqrt(np.mean(r["o"] ** 2)))
+    per_head = np.abs(o_got - r["o"]).max(axis=(1, 2)) / rms_o
+    print(f"  worst head {int(per_head.argmax())}: max|err|/RMS(o) = {per_head.max():.3e}", flush=True)
+    assert_rms_close(o_got, r["o"], TOL_BF16, "k3width o, all heads")
+    assert_rms_close(s_got, r["S_T"], TOL_BF16, "k3width S_T, all heads")
 
 
 @pytest.mark.timeout(900)
