@@ -161,6 +161,29 @@ def test_pipelined_slabs(oracle_mod, per_buf):
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"pipelined slabs, buffers of {per_buf or 35} chunks")
 
 
+@pytest.mark.parametrize("B,H,T", [(2, 3, 70 * 64 + 17), (1, 130, 66 * 64 + 5)])
+def test_slab_plans_at_other_shapes(oracle_mod, B, H, T):
+    """Ragged last chunk, at the preferred workspace.  B*H = 6 pipelines two
+    slabs on 8 compute units (6 rounded up to a multiple of 8); B*H = 130 is
+    more than half the compute units, so its 67 chunks run in one slab on
+    the caller's stream.  Checked on a few pairs."""
+    torch, kda = need_gpu()
+    w = Workload("ps", B, T, H, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=23)
+    inp = syn.prefill_inputs_np(w)
+    dev = to_dev(inp, "bf16")
+    nch = -(-T // 64)
+    per_chunk = B * H * 80 * 1024
+    carry = B * H * 128 * 128 * 4
+    if 2 * B * H <= 256:
+        want = 2 * (-(-nch // 2)) * per_chunk + carry
+    else:
+        want = nch * per_chunk
+    assert kda.workspace_bytes(B, T, H, 128, 128) == want
+    o, S_T, c = _gpu_prefill(kda, dev, 64)
+    pairs = sorted({0, B * H // 2, B * H - 1})
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, heads=pairs, what=f"B{B} H{H} T{T}")
+
+
 def test_paths_agree(oracle_mod):
     """Both paths on the same inputs agree to well within the tolerance."""
     torch, kda = need_gpu()
