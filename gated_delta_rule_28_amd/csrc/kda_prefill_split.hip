@@ -394,6 +394,8 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
     });
+    load_raw(p.k, 1, ra, ha);  // k's raw values land during the rest of q's work
+    __builtin_amdgcn_sched_barrier(0);
     l2norm128(x, fast_rsq((float)kD));
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
@@ -408,8 +410,6 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       *reinterpret_cast<half8*>(wsb + WS_QG + ((wave * 4 + kp) * 64 + lane) * 16) = to_half8(qg);
     }
   }
-  load_raw(p.k, 1, ra, ha);
-  __builtin_amdgcn_sched_barrier(0);
   // ---- k: rows and columns of A / P, K e^G, K e^{G_C - G} ---------------------------
   half8 KrowF[4], CdiagF[4];
   {
@@ -419,6 +419,8 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
     });
+    load_raw(p.v, 2, rb, hb);  // v's raw values land during the rest of k's work
+    __builtin_amdgcn_sched_barrier(0);
     l2norm128(x, 1.0f);
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
@@ -444,11 +446,9 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     }
   }
   // ---- v -----------------------------------------------------------------------------
-  load_raw(p.v, 2, ra, ha);
-  __builtin_amdgcn_sched_barrier(0);
   half8 Vf[4];
-  mask_halo(ha);
-  conv_silu(ra, ha, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
+  mask_halo(hb);
+  conv_silu(rb, hb, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
   lds_barrier();
 
   // ---- A^T and P^T blocks (b, a), b <= a: D[j][r] = sum_c col_b[j][c] row_a[r][c] --
