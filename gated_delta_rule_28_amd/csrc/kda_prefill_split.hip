@@ -637,8 +637,9 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 // per chunk: B1 (chunk j's operands have landed; O(j-1) is complete) and B2
 // (the epilogue waves have read O(j-1), so the math waves may overwrite it).
 // ---------------------------------------------------------------------------
-constexpr int kStageQ = WS_STAGE / kFrag / 4;  // fragments each copying wave moves per chunk
+constexpr int kStageQ = WS_STAGE / kFrag / 4;  // fragment slots of each copying wave per chunk
 static_assert(WS_STAGE % (4 * kFrag) == 0, "staged part must split evenly over four waves");
+constexpr int kStageFrags = WS_GAM / kFrag + 1;  // fragments holding data: up to e^{G_C}, not its padding
 
 // LDS of inter_chunk_kernel as three separate objects: the compiler then knows
 // that the direct-to-LDS copy into one staging buffer never aliases reads of
@@ -661,7 +662,7 @@ __device__ __forceinline__ unsigned char* stage_buf() {
 
 typedef __attribute__((address_space(3))) void lds_void;
 
-// Copy one chunk's staged operands (64 fragments of 1 KiB) from the workspace
+// Copy one chunk's staged operands (61 fragments of 1 KiB) from the workspace
 // into staging buffer P with direct-to-LDS loads (no registers): wave w moves
 // fragments w, w + 4, ...; lane l's 16 bytes land at offset 16 l of the
 // fragment.  Completion is tracked by the vector memory counter only, so the
@@ -671,8 +672,9 @@ __device__ __forceinline__ void stage_dma(const unsigned char* chunk, int w, int
 #pragma unroll
   for (int q = 0; q < kStageQ; ++q) {
     const int f = w + 4 * q;
-    __builtin_amdgcn_global_load_lds(chunk + f * kFrag + lane * 16, (lds_void*)(stage_buf<P>() + f * kFrag), 16, 0,
-                                     0);
+    if (f < kStageFrags)
+      __builtin_amdgcn_global_load_lds(chunk + f * kFrag + lane * 16, (lds_void*)(stage_buf<P>() + f * kFrag), 16,
+                                       0, 0);
   }
 }
 
