@@ -965,7 +965,8 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 //
 // Pipelined (a sequence of more than kPipeChunks chunks and B*H at most half
 // the compute units): slabs of about kPipeChunks chunks in kPipeBufs workspace
-// buffers.  The inter-chunk kernel (one workgroup per (b, h), the state carried
+// buffers.  From 2 * kPipeChunks chunks on, the first slab has half as many
+// chunks, so the inter-chunk kernel (the slower stage) starts sooner.  The inter-chunk kernel (one workgroup per (b, h), the state carried
 // between slabs in a buffer) runs on a stream restricted to B*H compute units,
 // the intra-chunk kernel of the next slab on a stream restricted to the others,
 // so the two overlap without competing for compute units.
@@ -978,8 +979,18 @@ constexpr int kPlanCUs = 256;  // compute units the preferred workspace is plann
 
 struct SlabPlan {
   int nchunks, per_slab, nslabs, nbuf;
+  int first;  // chunks of slab 0 when it differs from per_slab, else 0
   size_t region_bytes, carry_bytes;
 };
+
+// Chunks [c0, c0 + n) of slab sl.
+void slab_range(const SlabPlan& pl, int sl, int& c0, int& n) {
+  if (pl.first > 0) c0 = sl == 0 ? 0 : pl.first + (sl - 1) * pl.per_slab;
+  else c0 = sl * pl.per_slab;
+  const int len = pl.first > 0 && sl == 0 ? pl.first : pl.per_slab;
+  n = pl.nchunks - c0 < len ? pl.nchunks - c0 : len;
+  if (n < 0) n = 0;
+}
 
 size_t per_chunk_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * WS_CHUNK; }
 size_t carry_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * kD * kD * 4; }
@@ -994,8 +1005,16 @@ SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail) {
   if (s.nchunks > kPipeChunks && pipe_shape(a, kPlanCUs) && avail >= cb + kPipeBufs * pc) {
     const size_t fit = (avail - cb) / (kPipeBufs * pc);
     const int most = (int)(fit < (size_t)kPipeChunks ? fit : (size_t)kPipeChunks);
-    s.nslabs = (s.nchunks + most - 1) / most;
-    s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;  // balanced slabs, no small tail
+    if (most == kPipeChunks && s.nchunks >= 2 * kPipeChunks) {
+      s.first = kPipeChunks / 2;
+      const int rest = s.nchunks - s.first;
+      const int k = (rest + most - 1) / most;
+      s.per_slab = (rest + k - 1) / k;  // balanced slabs after the first
+      s.nslabs = 1 + k;
+    } else {
+      s.nslabs = (s.nchunks + most - 1) / most;
+      s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;  // balanced slabs, no small tail
+    }
     s.nbuf = s.nslabs < kPipeBufs ? s.nslabs : kPipeBufs;
     s.carry_bytes = cb;
   } else {
@@ -1013,7 +1032,8 @@ SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail) {
       s.carry_bytes = s.nslabs > 1 ? cb : 0;
     }
   }
-  s.region_bytes = (size_t)s.per_slab * pc;
+  s.region_bytes = (size_t)(s.first > s.per_slab ? s.first : s.per_slab) * pc;
+  if (s.first > 0) s.region_bytes = (size_t)kPipeChunks * pc;  // the same preferred size for any length
   return s;
 }
 
@@ -1113,9 +1133,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
   for (int sl = 0; sl < pl.nslabs && e == hipSuccess; ++sl) {
     SplitParams p{};
     p.B = a.B; p.T = a.T; p.H = a.H;
-    p.c_begin = sl * pl.per_slab;
-    p.n_chunks = pl.nchunks - p.c_begin < pl.per_slab ? pl.nchunks - p.c_begin : pl.per_slab;
-    if (p.n_chunks < 0) p.n_chunks = 0;
+    slab_range(pl, sl, p.c_begin, p.n_chunks);
     p.q = a.q; p.k = a.k; p.v = a.v; p.conv_w = a.conv_w; p.g = a.g; p.beta = a.beta; p.gate = a.gate;
     const bool first = sl == 0, last = sl == pl.nslabs - 1;
     p.S_in = first ? a.S0 : carry;

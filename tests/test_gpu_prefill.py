@@ -161,6 +161,19 @@ def test_pipelined_slabs(oracle_mod, per_buf):
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"pipelined slabs, buffers of {per_buf or 35} chunks")
 
 
+def test_pipelined_half_first_slab(oracle_mod):
+    """131 chunks (T = 8393, ragged): slabs of 32, 50 and 49 chunks (the first
+    one half-size), three buffers of 64 chunks at the preferred workspace."""
+    torch, kda = need_gpu()
+    w = Workload("pf", 1, 131 * 64 - 55, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=29)
+    inp = syn.prefill_inputs_np(w)
+    dev = to_dev(inp, "bf16")
+    per_chunk = w.B * w.H * 80 * 1024
+    assert kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv) == 3 * 64 * per_chunk + w.B * w.H * w.dk * w.dv * 4
+    o, S_T, c = _gpu_prefill(kda, dev, 64)
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="half-size first slab")
+
+
 @pytest.mark.parametrize("B,H,T", [(2, 3, 70 * 64 + 17), (1, 130, 66 * 64 + 5)])
 def test_slab_plans_at_other_shapes(oracle_mod, B, H, T):
     """Ragged last chunk, at the preferred workspace.  B*H = 6 pipelines two
