@@ -86,6 +86,37 @@ __device__ __forceinline__ void store4(void* base, size_t idx, float a, float b,
   }
 }
 
+// Non-temporal 16-byte accesses (data used once: the memory system keeps it
+// out of its caches, which measured up to 18% more bandwidth per CU on
+// streams that every CU runs at once).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_nt(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+template <typename V16>
+__device__ __forceinline__ void st_nt(void* p, const V16& v) {
+  static_assert(sizeof(V16) == 16, "16-byte value");
+  __builtin_nontemporal_store(__builtin_bit_cast(u32x4, v), reinterpret_cast<u32x4*>(p));
+}
+
+// Store 8 consecutive outputs (fp32 or bf16) with 16-byte non-temporal stores.
+template <bool BF16>
+__device__ __forceinline__ void store8_nt(void* base, size_t idx, const float* x) {
+  if constexpr (BF16) {
+    uint4 u;
+    u.x = (uint32_t)f_to_bf16(x[0]) | ((uint32_t)f_to_bf16(x[1]) << 16);
+    u.y = (uint32_t)f_to_bf16(x[2]) | ((uint32_t)f_to_bf16(x[3]) << 16);
+    u.z = (uint32_t)f_to_bf16(x[4]) | ((uint32_t)f_to_bf16(x[5]) << 16);
+    u.w = (uint32_t)f_to_bf16(x[6]) | ((uint32_t)f_to_bf16(x[7]) << 16);
+    st_nt(reinterpret_cast<uint16_t*>(base) + idx, u);
+  } else {
+    float* f = reinterpret_cast<float*>(base) + idx;
+    st_nt(f, make_float4(x[0], x[1], x[2], x[3]));
+    st_nt(f + 4, make_float4(x[4], x[5], x[6], x[7]));
+  }
+}
+
 // Store 8 consecutive outputs (fp32 or bf16) with 16-byte stores.
 template <bool BF16>
 __device__ __forceinline__ void store8(void* base, size_t idx, const float* x) {

@@ -297,7 +297,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
       const int cl = 32 * kp + 8 * g;
-      r[kp] = *reinterpret_cast<const uint4*>(x16 + row * kD + cl);
+      r[kp] = ld_nt(x16 + row * kD + cl);
       const uint16_t* ph =
           from_hist ? ci16 + hist + (size_t)part * H * kD + (size_t)h * kD + cl : x16 + hrow * kD + cl;
       hr[kp] = *reinterpret_cast<const uint4*>(ph);
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   {
     const uint16_t* g16 = reinterpret_cast<const uint16_t*>(p.g);
 #pragma unroll
-    for (int kp = 0; kp < 4; ++kp) rg[kp] = *reinterpret_cast<const uint4*>(g16 + row * kD + 32 * kp + 8 * g);
+    for (int kp = 0; kp < 4; ++kp) rg[kp] = ld_nt(g16 + row * kD + 32 * kp + 8 * g);
   }
   load_raw(p.q, 0, rb, hb);  // q's raw values land during the decay-factor phase
   const float beta_v = valid ? bf16_to_f(reinterpret_cast<const uint16_t*>(p.beta)[row]) : 0.f;
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
         qg[e] = qr[e] * er[e];
       }
       QrowF[kp] = to_op8(qr, bf);
-      *reinterpret_cast<half8*>(wsb + WS_QG + ((wave * 4 + kp) * 64 + lane) * 16) = to_half8(qg);
+      st_nt(wsb + WS_QG + ((wave * 4 + kp) * 64 + lane) * 16, to_half8(qg));
     }
   }
   // ---- k: rows and columns of A / P, K e^G, K e^{G_C - G} ---------------------------
@@ -439,7 +439,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       }
       KrowF[kp] = to_op8(kr, bf);
       CdiagF[kp] = to_op8(cd, bf);
-      *reinterpret_cast<half8*>(wsb + WS_KG + ((wave * 4 + kp) * 64 + lane) * 16) = to_half8(kg);
+      st_nt(wsb + WS_KG + ((wave * 4 + kp) * 64 + lane) * 16, to_half8(kg));
       if (wave < 3) sCC[(wave * 4 + kp) * 64 + lane] = to_op8(cc, bf);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sKBT[tix(32 * kp + 8 * g + e, tok)] = (_Float16)kb[e];
@@ -491,8 +491,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     for (int kp = 0; kp < 2; ++kp) {
       const half4 lo = *reinterpret_cast<const half4*>(sKBT + tix(rw, 32 * kp + 4 * g));
       const half4 hi = *reinterpret_cast<const half4*>(sKBT + tix(rw, 32 * kp + 16 + 4 * g));
-      *reinterpret_cast<half8*>(wsb + WS_KB + ((m * 2 + kp) * 64 + lane) * 16) =
-          half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      st_nt(wsb + WS_KB + ((m * 2 + kp) * 64 + lane) * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     }
   }
   lds_barrier();  // R1 and R2 are rewritten from here on
@@ -522,7 +521,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
           pv[4 * sh + e] = (bb <= wave && 16 * bb + 4 * g + e <= tok) ? v : 0.f;
         }
       }
-      *reinterpret_cast<half8*>(wsb + WS_P + (p_frag(wave, kp) * 64 + lane) * 16) = to_half8(pv);
+      st_nt(wsb + WS_P + (p_frag(wave, kp) * 64 + lane) * 16, to_half8(pv));
     }
   }
   // V^T, for V in the C layout of the second kernel
@@ -606,7 +605,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     const int rt = f < 2 ? f : (f - 2) / 2 + 2, kp = f < 2 ? 0 : (f - 2) & 1;
     const half4 lo = *reinterpret_cast<const half4*>(sTB + (16 * rt + i) * LDB + 32 * kp + 4 * g);
     const half4 hi = *reinterpret_cast<const half4*>(sTB + (16 * rt + i) * LDB + 32 * kp + 16 + 4 * g);
-    *reinterpret_cast<half8*>(wsb + WS_TB + (f * 64 + lane) * 16) = half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    st_nt(wsb + WS_TB + (f * 64 + lane) * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   }
   // V fragment (rt, w): lane (g, i) holds tokens 16rt + 4g + 0..3 of dv columns
   // 16(2w) + i and 16(2w + 1) + i
@@ -614,8 +613,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   for (int rt = 0; rt < 4; ++rt) {
     const half4 c0v = *reinterpret_cast<const half4*>(sVT + tix(32 * wave + i, 16 * rt + 4 * g));
     const half4 c1v = *reinterpret_cast<const half4*>(sVT + tix(32 * wave + 16 + i, 16 * rt + 4 * g));
-    *reinterpret_cast<half8*>(wsb + WS_V + ((rt * 4 + wave) * 64 + lane) * 16) =
-        half8{c0v[0], c0v[1], c0v[2], c0v[3], c1v[0], c1v[1], c1v[2], c1v[3]};
+    st_nt(wsb + WS_V + ((rt * 4 + wave) * 64 + lane) * 16, half8{c0v[0], c0v[1], c0v[2], c0v[3], c1v[0], c1v[1], c1v[2], c1v[3]});
   }
 }
 
@@ -674,7 +672,7 @@ __device__ __forceinline__ void stage_dma(const unsigned char* chunk, int w, int
     const int f = w + 4 * q;
     if (f < kStageFrags)
       __builtin_amdgcn_global_load_lds(chunk + f * kFrag + lane * 16, (lds_void*)(stage_buf<P>() + f * kFrag), 16,
-                                       0, 0);
+                                       0, 2);
   }
 }
 
@@ -725,7 +723,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
     if (nc > 0) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        vt[0][rt] = *reinterpret_cast<const uint4*>(wsh + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
+        vt[0][rt] = ld_nt(wsh + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
     }
     // one chunk; P = j & 1 picks the staging buffer and the V registers
     auto step = [&](auto parity, int j) {
@@ -748,7 +746,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           const unsigned char* wn = wsh + (size_t)(j + 1) * WS_CHUNK;
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt)
-            vt[1 - P][rt] = *reinterpret_cast<const uint4*>(wn + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
+            vt[1 - P][rt] = ld_nt(wn + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
         }
         // X = V + (-(K e^G)) S and (Q e^G) S, one 32-row step of S at a time:
         // its B operands are rows 16(2k + s) + 4g + e, s = 0, 1
@@ -866,7 +864,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         const uint16_t* gr =
             reinterpret_cast<const uint16_t*>(p.gate) + (((size_t)b * T + c0 + tk) * H + h) * kD + 8 * q;
 #pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) gt[tt][s2] = *reinterpret_cast<const uint4*>(gr + 64 * s2);
+        for (int s2 = 0; s2 < 2; ++s2) gt[tt][s2] = ld_nt(gr + 64 * s2);
       }
     };
     if (nc > 0) load_gate(0);
@@ -917,7 +915,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           if (tk < nv) {
             const size_t ob = (((size_t)b * T + c0 + tk) * H + h) * kD + 8 * q;
 #pragma unroll
-            for (int s2 = 0; s2 < 2; ++s2) store8<OUT_BF16>(p.o, ob + 64 * s2, ov[tt][s2]);
+            for (int s2 = 0; s2 < 2; ++s2) store8_nt<OUT_BF16>(p.o, ob + 64 * s2, ov[tt][s2]);
           }
         }
       }
