@@ -250,6 +250,36 @@ def test_strong_decay_takes_bf16_tiles(oracle_mod, path):
 
 
 @path
+def test_beta_zero_state_only_decays(oracle_mod, path):
+    """beta = 0: no token writes the state, which only decays from S0 (the
+    outputs read the decayed S0).  Also checks S_T = Diag(e^{sum g}) S0 row by
+    row, which holds exactly in this case."""
+    torch, kda = need_gpu()
+    w = Workload("b0", 1, 130, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=41)
+    inp = syn.prefill_inputs_np(w)
+    inp["beta"] = syn.bf16_bits_from_f64(np.zeros(inp["beta"].shape))
+    dev = to_dev(inp, "bf16")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} beta=0")
+    g = syn.bf16_bits_to_f64(inp["g"]).reshape(w.B, w.T, w.H, w.dk).sum(axis=1)  # [B, H, dk]
+    want = inp["S0"].astype(np.float64).reshape(w.B, w.H, w.dk, w.dv) * np.exp(g)[..., None]
+    got = S_T.cpu().numpy().astype(np.float64).reshape(w.B, w.H, w.dk, w.dv)
+    assert_rms_close(got, want, 1e-5, f"{path} beta=0 S_T = decayed S0")
+
+
+@path
+def test_no_decay(oracle_mod, path):
+    """g = 0: nothing is forgotten, every decay factor is exactly 1."""
+    torch, kda = need_gpu()
+    w = Workload("g0", 1, 130, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=43)
+    inp = syn.prefill_inputs_np(w)
+    inp["g"] = syn.bf16_bits_from_f64(np.zeros(inp["g"].shape))
+    dev = to_dev(inp, "bf16")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} g=0")
+
+
+@path
 def test_bf16_output(oracle_mod, path):
     torch, kda = need_gpu()
     w = Workload("bo", 1, 96, 2, 128, 128, 64, "bf16", s0_sigma=0.05, seed=13)
