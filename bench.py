@@ -15,6 +15,8 @@ Prints one JSON line.  Options:
   --decode-steps  decode steps timed back to back (default 1000; 0 skips decode)
   --no-cpu        skip the oracle leg
   --calibrate     also run a plain 1 GiB read + 1 GiB write kernel (for HBM counter scaling)
+  --decay-form    direct (default: g and beta given) | k3 (g and beta given as K3's
+                  logits, g = -5 sigmoid(e^A z) and beta = sigmoid(b) computed in the kernels)
 """
 from __future__ import annotations
 
@@ -118,6 +120,8 @@ def cpu_baseline(w, dev_inp, seconds_target=15.0):
     host = {x: syn.torch_to_np(t) for x, t in sl.items()}
     if dev_inp.get("S0") is not None:
         host["S0"] = syn.torch_to_np(dev_inp["S0"][:, :nheads].contiguous())
+    if dev_inp.get("A") is not None:
+        host["A"] = syn.torch_to_np(dev_inp["A"][:nheads].contiguous())
     t0 = time.perf_counter()
     oracle.prefill(host)
     el = time.perf_counter() - t0
@@ -137,6 +141,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
+    ap.add_argument("--decay-form", default="direct", choices=["direct", "k3"])
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU path only; run it with --gpus 1 "
@@ -156,6 +161,9 @@ def main():
 
     t0 = time.perf_counter()
     inp = syn.prefill_inputs_torch(w, dev)
+    if args.decay_form == "k3":
+        inp = syn.with_k3_logits_torch(inp, w, dev)
+    A = inp.get("A")
     torch.cuda.synchronize()
     log(f"[bench] inputs generated on device in {time.perf_counter() - t0:.1f} s")
     o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device=dev)
@@ -166,7 +174,7 @@ def main():
     def step():
         if w.segments == 1:
             kda.prefill(inp["q"], inp["k"], inp["v"], inp["conv_w"], inp["g"], inp["beta"], inp["gate"],
-                        S0=S0, conv_in=None, chunk=w.chunk, o=o, S_T=S, conv_out=conv)
+                        S0=S0, conv_in=None, chunk=w.chunk, o=o, S_T=S, conv_out=conv, A=A)
             return
         S.zero_()
         conv.zero_()
@@ -174,7 +182,7 @@ def main():
             t0_, t1_ = s * seg, (s + 1) * seg
             kda.prefill(inp["q"][:, t0_:t1_], inp["k"][:, t0_:t1_], inp["v"][:, t0_:t1_], inp["conv_w"],
                         inp["g"][:, t0_:t1_], inp["beta"][:, t0_:t1_], inp["gate"][:, t0_:t1_],
-                        S0=S, conv_in=conv, chunk=w.chunk, o=o[:, t0_:t1_], S_T=S, conv_out=conv)
+                        S0=S, conv_in=conv, chunk=w.chunk, o=o[:, t0_:t1_], S_T=S, conv_out=conv, A=A)
 
     if w.segments > 1:
         # segment views must be contiguous for the ABI: [B=1, seg, H, d] slices are
@@ -211,10 +219,13 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
-        "data": "synthetic (seeded device draws; q,k,v,gate ~ N(0,1), g = -softplus(N(-3,1)), beta = sigmoid(N(0,1)))",
+        "data": ("synthetic (seeded device draws; q,k,v,gate ~ N(0,1), g = -softplus(N(-3,1)), beta = sigmoid(N(0,1)))"
+                 if A is None else
+                 "synthetic (seeded device draws; q,k,v,gate ~ N(0,1); g, beta as K3 logits: z ~ N(-4.7,1), "
+                 "b ~ N(0,1), A ~ N(0,0.1))"),
         "config": {"workload": f"{w.name}: KDA prefill B{w.B} T{w.T} H{w.H} dk=dv={w.dk} chunk {w.chunk}"
                                + (f", {w.segments} segments of {seg} with state carried" if w.segments > 1 else ""),
-                   "inputs": "bf16", "state": "f32", "output": "f32",
+                   "inputs": "bf16", "state": "f32", "output": "f32", "decay_form": args.decay_form,
                    "matrix_core_operands": "f16 with f32 accumulation"},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

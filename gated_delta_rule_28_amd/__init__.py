@@ -9,6 +9,10 @@ works, but every call raises (there is no fallback implementation).
     nbytes = workspace_bytes(B, T, H, dk, dv, chunk, in_dtype)  # what prefill allocates
     o = decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state)   # S, conv_state in place
     qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
+
+Every call also takes A=None: given an fp32 [H, dk] tensor, g and beta are K3's
+logits (g = -5 sigmoid(e^A z), beta = sigmoid(b), KDA_DECAY_K3) instead of the
+log-decay and beta themselves.
 """
 from __future__ import annotations
 
@@ -16,14 +20,17 @@ import ctypes
 import os
 
 __all__ = ["prefill", "decode_step", "prep", "workspace_bytes", "library_path", "lib", "KDAError",
-           "KDA_F32", "KDA_BF16", "PrefillArgs", "DecodeArgs", "PrepArgs"]
+           "KDA_F32", "KDA_BF16", "KDA_DECAY_DIRECT", "KDA_DECAY_K3", "PrefillArgs", "DecodeArgs",
+           "PrepArgs"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
 
 KDA_F32 = 0
 KDA_BF16 = 1
-ABI_VERSION = 1
+KDA_DECAY_DIRECT = 0
+KDA_DECAY_K3 = 1
+ABI_VERSION = 2
 
 
 class KDAError(RuntimeError):
@@ -41,14 +48,16 @@ class PrefillArgs(ctypes.Structure):
                 ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P), ("g", _P), ("beta", _P),
                 ("gate", _P), ("S0", _P), ("conv_in", _P), ("o", _P), ("S_T", _P),
-                ("conv_out", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t)]
+                ("conv_out", _P), ("workspace", _P), ("workspace_bytes", ctypes.c_size_t),
+                ("decay_form", ctypes.c_int), ("A", _P)]
 
 
 class DecodeArgs(ctypes.Structure):
     _fields_ = [("N", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
                 ("dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
                 ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P), ("g", _P), ("beta", _P),
-                ("gate", _P), ("S", _P), ("conv_state", _P), ("o", _P)]
+                ("gate", _P), ("S", _P), ("conv_state", _P), ("o", _P),
+                ("decay_form", ctypes.c_int), ("A", _P)]
 
 
 class PrepArgs(ctypes.Structure):
@@ -56,7 +65,7 @@ class PrepArgs(ctypes.Structure):
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
                 ("in_dtype", ctypes.c_int), ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P),
                 ("g", _P), ("conv_in", _P), ("q_out", _P), ("k_out", _P), ("v_out", _P),
-                ("G_out", _P)]
+                ("G_out", _P), ("decay_form", ctypes.c_int), ("A", _P)]
 
 
 _lib = None
@@ -117,13 +126,18 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _decay(A):
+    """(decay_form, A pointer): K3's logits when A is given, else g and beta themselves."""
+    return (KDA_DECAY_DIRECT, None) if A is None else (KDA_DECAY_K3, _ptr(A))
+
+
 def _stream(device):
     torch = _torch()
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out_dtype=None,
-            o=None, S_T=None, conv_out=None, want_state=True, want_conv=True, workspace="auto"):
+            o=None, S_T=None, conv_out=None, want_state=True, want_conv=True, workspace="auto", A=None):
     """Chunkwise KDA prefill (kda_prefill).  Shapes as in include/kda.h.
 
     Returns (o, S_T, conv_out); S_T / conv_out are None when not wanted.
@@ -145,7 +159,7 @@ def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out
         conv_out = torch.empty((B, 3, H * (2 * dk + dv)), dtype=q.dtype, device=dev)
     a = PrefillArgs(B, T, H, dk, dv, chunk, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
                     _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in),
-                    _ptr(o), _ptr(S_T), _ptr(conv_out), None, 0)
+                    _ptr(o), _ptr(S_T), _ptr(conv_out), None, 0, *_decay(A))
     if isinstance(workspace, str):
         if workspace != "auto":
             raise ValueError("workspace must be 'auto', None or a uint8 tensor")
@@ -165,7 +179,7 @@ def workspace_bytes(B, T, H, dk, dv, chunk=64, in_dtype=KDA_BF16, out_dtype=KDA_
     return int(fn(ctypes.byref(a)))
 
 
-def decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype=None):
+def decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype=None, A=None):
     """One KDA decode step (kda_decode_step); S and conv_state are updated in place."""
     torch = _torch()
     N, H, dk = q.shape
@@ -174,12 +188,12 @@ def decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype
     if o is None:
         o = torch.empty((N, H, dv), dtype=out_dtype, device=q.device)
     a = DecodeArgs(N, H, dk, dv, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w),
-                   _ptr(g), _ptr(beta), _ptr(gate), _ptr(S), _ptr(conv_state), _ptr(o))
+                   _ptr(g), _ptr(beta), _ptr(gate), _ptr(S), _ptr(conv_state), _ptr(o), *_decay(A))
     _check("kda_decode_step", lib().kda_decode_step(ctypes.byref(a), _stream(q.device)))
     return o
 
 
-def prep(q, k, v, conv_w, g, conv_in=None, chunk=64):
+def prep(q, k, v, conv_w, g, conv_in=None, chunk=64, A=None):
     """Stage 1 on its own (kda_prep): returns fp32 (q^, k^, v^, G)."""
     torch = _torch()
     B, T, H, dk = q.shape
@@ -188,6 +202,6 @@ def prep(q, k, v, conv_w, g, conv_in=None, chunk=64):
     qo, ko, vo = torch.empty((B, T, H, dk), **f), torch.empty((B, T, H, dk), **f), torch.empty((B, T, H, dv), **f)
     Go = torch.empty((B, T, H, dk), **f)
     a = PrepArgs(B, T, H, dk, dv, chunk, _dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w), _ptr(g),
-                 _ptr(conv_in), _ptr(qo), _ptr(ko), _ptr(vo), _ptr(Go))
+                 _ptr(conv_in), _ptr(qo), _ptr(ko), _ptr(vo), _ptr(Go), *_decay(A))
     _check("kda_prep", lib().kda_prep(ctypes.byref(a), _stream(q.device)))
     return qo, ko, vo, Go

@@ -44,6 +44,16 @@ int check_common(int B, int T, int H, int dk, int dv, int in_dtype, int out_dtyp
   if ((long long)B * H > 0x7fffffffLL) return fail(KDA_E_SHAPE, "B*H=%lld too large", (long long)B * H);
   return KDA_OK;
 }
+
+int check_decay(int form, const float* A) {
+  if (form != KDA_DECAY_DIRECT && form != KDA_DECAY_K3)
+    return fail(KDA_E_UNSUPPORTED, "decay_form=%d not KDA_DECAY_DIRECT/KDA_DECAY_K3", form);
+  if (form == KDA_DECAY_K3) {
+    if (A == nullptr) return fail(KDA_E_NULL, "A is NULL (decay_form KDA_DECAY_K3)");
+    if (!aligned16(A)) return fail(KDA_E_ALIGN, "A is not 16-byte aligned");
+  }
+  return KDA_OK;
+}
 }  // namespace
 
 void set_error(const char* fmt, ...) {
@@ -96,6 +106,8 @@ int kda_prefill(const kda_prefill_args* a, void* stream) {
   if (rc != KDA_OK) return rc;
   if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64)
     return fail(KDA_E_UNSUPPORTED, "chunk=%d not in {16,32,64}", a->chunk);
+  rc = kda::check_decay(a->decay_form, a->A);
+  if (rc != KDA_OK) return rc;
   if (a->T > 0) {
     REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
     REQUIRE_PTR(a->g); REQUIRE_PTR(a->beta); REQUIRE_PTR(a->gate); REQUIRE_PTR(a->o);
@@ -118,6 +130,8 @@ int kda_decode_step(const kda_decode_args* a, void* stream) {
   REQUIRE_PTR(a);
   int rc = kda::check_common(a->N, 1, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype);
   if (rc != KDA_OK) return rc;
+  rc = kda::check_decay(a->decay_form, a->A);
+  if (rc != KDA_OK) return rc;
   REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
   REQUIRE_PTR(a->g); REQUIRE_PTR(a->beta); REQUIRE_PTR(a->gate); REQUIRE_PTR(a->S);
   REQUIRE_PTR(a->conv_state); REQUIRE_PTR(a->o);
@@ -133,6 +147,8 @@ int kda_prep(const kda_prep_args* a, void* stream) {
   kda::g_err[0] = '\0';
   REQUIRE_PTR(a);
   int rc = kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, KDA_F32);
+  if (rc != KDA_OK) return rc;
+  rc = kda::check_decay(a->decay_form, a->A);
   if (rc != KDA_OK) return rc;
   if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64)
     return fail(KDA_E_UNSUPPORTED, "chunk=%d not in {16,32,64}", a->chunk);

@@ -31,6 +31,7 @@ struct DecodeParams {
   float* S;
   void* conv_state;
   void* o;
+  const float* A;  // [H, dk]: g and beta are K3's logits (see k3_decay); null: given directly
 };
 
 constexpr int kDecodeThreads = 256;
@@ -113,7 +114,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
   if (tid < DK) {
-    const float a = fast_exp(load1<IN_BF16>(p.g, (size_t)nh * DK + tid));
+    float gv = load1<IN_BF16>(p.g, (size_t)nh * DK + tid);
+    if (p.A != nullptr) gv = k3_decay(gv, fast_exp(p.A[(size_t)h * DK + tid]));
+    const float a = fast_exp(gv);
     const float kq = xs[DK + tid] * scal[1];
     alpha[tid] = a;
     kn[tid] = kq;
@@ -152,7 +155,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
       y += red[0][r][tid];
       z += red[1][r][tid];
     }
-    const float beta = load1<IN_BF16>(p.beta, (size_t)nh);
+    float beta = load1<IN_BF16>(p.beta, (size_t)nh);
+    if (p.A != nullptr) beta = sigmoidf_(beta);
     const float u = beta * (xs[2 * DK + tid] - y);
     us[tid] = u;
     ocs[tid] = z + scal[2] * u;
@@ -184,7 +188,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
 
 template <int DK, int DV, bool IB, bool OB>
 int run(const kda_decode_args& a, hipStream_t s) {
-  DecodeParams p{a.H, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o};
+  DecodeParams p{a.H, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o,
+                 a.decay_form == KDA_DECAY_K3 ? a.A : nullptr};
   const unsigned grid = (unsigned)((size_t)a.N * a.H);
   hipLaunchKernelGGL((decode_kernel<DK, DV, IB, OB>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
   const hipError_t e = hipGetLastError();

@@ -36,6 +36,9 @@ __device__ __forceinline__ float fast_rcp(float x) { return __builtin_amdgcn_rcp
 __device__ __forceinline__ float fast_rsq(float x) { return __builtin_amdgcn_rsqf(x); }
 __device__ __forceinline__ float sigmoidf_(float x) { return fast_rcp(1.0f + fast_exp(-x)); }
 __device__ __forceinline__ float siluf_(float x) { return x * fast_rcp(1.0f + fast_exp(-x)); }
+// K3's bounded log-decay from its logit z, given e^A of the channel
+// ("Kimi K3.1 Pro vs gpt-oss-120b", component table, row "Gated DeltaNet / KDA")
+__device__ __forceinline__ float k3_decay(float z, float eA) { return -5.0f * sigmoidf_(eA * z); }
 
 // ---- bf16 / fp16 ---------------------------------------------------------------
 __device__ __forceinline__ float bf16lo(uint32_t u) { return __uint_as_float(u << 16); }

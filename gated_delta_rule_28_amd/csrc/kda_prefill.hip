@@ -76,6 +76,7 @@ struct PrefillParams {
   float* k_out;
   float* v_out;
   float* G_out;
+  const float* A;  // [H, dk]: g and beta are K3's logits (see k3_decay); null: given directly
 };
 
 // ---------------------------------------------------------------------------
@@ -486,11 +487,25 @@ __device__ __forceinline__ void l2norm(float* x, float extra) {
   for (int e = 0; e < 8; ++e) x[e] *= r;
 }
 
+// g of channels c8 .. c8+7 of head h from the loaded input: the input itself,
+// or K3's bounded log-decay of the logits in it (tokens that are not loaded
+// keep g = 0)
+__device__ __forceinline__ void g_from_input(const float* A, int h, int DK, int c8, bool loaded, float* gv) {
+  if (A != nullptr && loaded) {
+    const float4 a0 = *reinterpret_cast<const float4*>(A + (size_t)h * DK + c8);
+    const float4 a1 = *reinterpret_cast<const float4*>(A + (size_t)h * DK + c8 + 4);
+    const float av[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+#pragma unroll
+    for (int e = 0; e < 8; ++e) gv[e] = k3_decay(gv[e], fast_exp(av[e]));
+  }
+}
+
 template <bool IN_BF16>
 __device__ __forceinline__ void load_g(const PrefillParams& p, int b, int h, int t, int c8, int DK, bool valid,
                                        float* gv) {
   if (valid) {
     load8<IN_BF16>(p.g, ((size_t)b * p.T + t) * p.H * DK + (size_t)h * DK + c8, gv);
+    g_from_input(p.A, h, DK, c8, true, gv);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) gv[e] = 0.f;
@@ -716,7 +731,10 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int tt = 0; tt < TBQ; ++tt) load_g(tt);
       }
     }
-    if (tl < C) beta_v = load1<IN_BF16>(p.beta, ((size_t)b * T + cl + min(tl, nv - 1)) * H + h);
+    if (tl < C) {
+      beta_v = load1<IN_BF16>(p.beta, ((size_t)b * T + cl + min(tl, nv - 1)) * H + h);
+      if (p.A != nullptr) beta_v = sigmoidf_(beta_v);
+    }
   };
 
   if (nchunks > 0) issue_loads(0);
@@ -742,6 +760,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       for (int tt = 0; tt < TBK; ++tt) {
         float gv[8];
         raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
+        g_from_input(p.A, h, DK, c8, (gr_ok >> tt) & 1u, gv);
 #pragma unroll
         for (int e = 0; e < 8; ++e) s8[e] += gv[e];
       }
@@ -839,6 +858,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       const float* erho = sERho + bt * DK + c8;
       float gv[8];
       raw_unpack_if<IN_BF16>(gr[tt], (gr_ok >> tt) & 1u, gv);
+      g_from_input(p.A, h, DK, c8, (gr_ok >> tt) & 1u, gv);
       float er[8], rowv[8], xg[8];
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -1191,6 +1211,7 @@ PrefillParams make_params(const kda_prefill_args& a) {
   p.g = a.g; p.beta = a.beta; p.gate = a.gate;
   p.S0 = a.S0; p.conv_in = a.conv_in;
   p.o = a.o; p.S_T = a.S_T; p.conv_out = a.conv_out;
+  p.A = a.decay_form == KDA_DECAY_K3 ? a.A : nullptr;
   return p;
 }
 
@@ -1252,6 +1273,7 @@ int run_prep(const kda_prep_args& a, hipStream_t s) {
   p.B = a.B; p.T = a.T; p.H = a.H;
   p.q = a.q; p.k = a.k; p.v = a.v; p.conv_w = a.conv_w; p.g = a.g; p.conv_in = a.conv_in;
   p.q_out = a.q_out; p.k_out = a.k_out; p.v_out = a.v_out; p.G_out = a.G_out;
+  p.A = a.decay_form == KDA_DECAY_K3 ? a.A : nullptr;
   const int nchunks = (a.T + C - 1) / C;
   const size_t grid = (size_t)a.B * a.H * nchunks;
   hipLaunchKernelGGL((prep_kernel<C, D, D, IB>), dim3((unsigned)grid), dim3(kThreads), 0, s, p);

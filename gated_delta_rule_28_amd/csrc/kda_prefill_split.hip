@@ -91,6 +91,7 @@ struct SplitParams {
   float* S_out;           // state after the last chunk, or null
   void* conv_out;         // raw conv history after the last token, or null
   unsigned char* ws;      // n_chunks * B * H chunk blocks
+  const float* A;         // [H, dk]: g and beta are K3's logits (see k3_decay); null: given directly
 };
 
 // DPP move inside rows of 16 lanes; lanes with no source or outside the bank
@@ -245,6 +246,8 @@ struct ALds {
 // ---------------------------------------------------------------------------
 // intra_chunk_kernel: grid n_chunks * B * H, block 256
 // ---------------------------------------------------------------------------
+// K3: g and beta are K3's logits (p.A holds A), see k3_decay
+template <bool K3>
 __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   using L = ALds;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -316,7 +319,8 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     for (int kp = 0; kp < 4; ++kp) rg[kp] = ld_nt(g16 + row * kD + 32 * kp + 8 * g);
   }
   load_raw(p.q, 0, rb, hb);  // q's raw values land during the decay-factor phase
-  const float beta_v = valid ? bf16_to_f(reinterpret_cast<const uint16_t*>(p.beta)[row]) : 0.f;
+  float beta_v = valid ? bf16_to_f(reinterpret_cast<const uint16_t*>(p.beta)[row]) : 0.f;
+  if constexpr (K3) beta_v = valid ? sigmoidf_(beta_v) : 0.f;
 
   // conv taps of this head, per-token beta, fp16-range flag
   for (int ch = tid; ch < kNCh; ch += 256) {
@@ -331,16 +335,20 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   // ---- chunk-local cumulative sum of g: DPP scan over the tile, tile sums -----
   float s[32];
 #pragma unroll
-  for (int kp = 0; kp < 4; ++kp)
+  for (int kp = 0; kp < 4; ++kp) {
+    float av[8];  // K3's decay: A of this lane's channels 32kp + 8g + 0..7
+    if constexpr (K3) ld8f(p.A + (size_t)h * kD + 32 * kp + 8 * g, av);
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       float x = valid ? bf16_at(rg[kp], e) : 0.f;
+      if constexpr (K3) x = valid ? k3_decay(x, fast_exp(av[e])) : 0.f;
       x += dppf<0x111, 0xF>(x);
       x += dppf<0x112, 0xF>(x);
       x += dppf<0x114, 0xF>(x);
       x += dppf<0x118, 0xF>(x);
       s[8 * kp + e] = x;   // G - rho_a at this token
     }
+  }
   if (i == 15) {
 #pragma unroll
     for (int kp = 0; kp < 4; ++kp) {
@@ -1101,10 +1109,10 @@ int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
   return KDA_OK;
 }
 
-template <bool OB>
+template <bool OB, bool K3>
 int run_split(const kda_prefill_args& a, hipStream_t st) {
   const SlabPlan pl = plan_slabs(a, a.workspace_bytes);
-  const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel),
+  const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<K3>),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, ALds::BYTES);
   if (e1 != hipSuccess) {
     set_error("prefill: hipFuncSetAttribute failed: %s", hipGetErrorString(e1));
@@ -1133,6 +1141,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
     p.B = a.B; p.T = a.T; p.H = a.H;
     slab_range(pl, sl, p.c_begin, p.n_chunks);
     p.q = a.q; p.k = a.k; p.v = a.v; p.conv_w = a.conv_w; p.g = a.g; p.beta = a.beta; p.gate = a.gate;
+    p.A = a.decay_form == KDA_DECAY_K3 ? a.A : nullptr;
     const bool first = sl == 0, last = sl == pl.nslabs - 1;
     p.S_in = first ? a.S0 : carry;
     p.conv_in = a.conv_in;
@@ -1146,7 +1155,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st) {
     if (piped && sl >= pl.nbuf) e = hipStreamWaitEvent(sa, pp->b_done[buf], 0);
     if (e == hipSuccess && p.n_chunks > 0) {
       const size_t grid = (size_t)p.n_chunks * a.B * a.H;
-      hipLaunchKernelGGL(intra_chunk_kernel, dim3((unsigned)grid), dim3(256), ALds::BYTES, sa, p);
+      hipLaunchKernelGGL(intra_chunk_kernel<K3>, dim3((unsigned)grid), dim3(256), ALds::BYTES, sa, p);
       e = hipGetLastError();
       what = "intra-chunk launch";
     }
@@ -1204,7 +1213,9 @@ size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a) {
 }
 
 int launch_prefill_split(const kda_prefill_args& a, hipStream_t s) {
-  return a.out_dtype == KDA_BF16 ? run_split<true>(a, s) : run_split<false>(a, s);
+  const bool k3 = a.decay_form == KDA_DECAY_K3;
+  if (a.out_dtype == KDA_BF16) return k3 ? run_split<true, true>(a, s) : run_split<true, false>(a, s);
+  return k3 ? run_split<false, true>(a, s) : run_split<false, false>(a, s);
 }
 
 }  // namespace kda

@@ -31,8 +31,19 @@
  * fails validation returns a negative code and launches nothing.  The library
  * is reentrant; kda_last_error() is per calling thread.
  *
- * Preconditions not checked (for cost): g <= 0; 0 <= beta <= 1; inputs
- * finite; |v~| and the state below 6e4 (fp16 operand range).
+ * Decay and beta inputs (decay_form):
+ *   KDA_DECAY_DIRECT  g is the log-decay (g <= 0) and beta is beta in [0, 1].
+ *   KDA_DECAY_K3      g holds the decay logits z and beta the beta logits b:
+ *                     g = -5 sigmoid(e^A z) with A [H, dk] fp32 (one value per
+ *                     head and key channel), beta = sigmoid(b).  K3's bounded
+ *                     log-decay ("Kimi K3.1 Pro vs gpt-oss-120b" and "Gemma 4
+ *                     31B vs Kimi K3", component tables, row "Gated DeltaNet /
+ *                     KDA"; the pages give A's shape nowhere, and beta's form
+ *                     only as a value in (0, 1)), computed in the kernels where
+ *                     they load g and beta.
+ *
+ * Preconditions not checked (for cost): g <= 0 and 0 <= beta <= 1 in the
+ * direct form; inputs finite; |v~| and the state below 6e4 (fp16 operand range).
  * Precision: the prefill's matrix-core operands are fp16 with fp32
  * accumulation and an fp32 state.  Decay factors inside a 16-token tile are
  * formed relative to a per-tile reference; when a tile's summed log-decay in
@@ -50,10 +61,13 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 1
+#define KDA_ABI_VERSION 2
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
+
+/* how g and beta are given (see above) */
+enum { KDA_DECAY_DIRECT = 0, KDA_DECAY_K3 = 1 };
 
 /* status codes */
 enum {
@@ -62,7 +76,8 @@ enum {
   KDA_E_SHAPE = -2,       /* a size is out of range (negative, zero, too large)  */
   KDA_E_DTYPE = -3,       /* in_dtype / out_dtype not one of the enum values     */
   KDA_E_ALIGN = -4,       /* a pointer is not 16-byte aligned                    */
-  KDA_E_UNSUPPORTED = -5, /* dk != dv, dk not in {16,32,64,128}, or chunk not in {16,32,64} */
+  KDA_E_UNSUPPORTED = -5, /* dk != dv, dk not in {16,32,64,128}, chunk not in {16,32,64},
+                             or decay_form not one of the enum values */
   KDA_E_WORKSPACE = -6,   /* workspace given but smaller than kda_prefill_workspace_min_bytes */
   KDA_E_HIP = -7          /* a HIP runtime call failed (text in kda_last_error)  */
 };
@@ -116,6 +131,8 @@ typedef struct kda_prefill_args {
   void* conv_out;         /* may be NULL */
   void* workspace;        /* NULL, or >= kda_prefill_workspace_min_bytes bytes, 16-byte aligned */
   size_t workspace_bytes;
+  int decay_form;         /* KDA_DECAY_DIRECT (0) or KDA_DECAY_K3 */
+  const float* A;         /* [H, dk] fp32 for KDA_DECAY_K3 (required, 16-byte aligned); else unused */
 } kda_prefill_args;
 
 int kda_prefill(const kda_prefill_args* args, void* stream);
@@ -155,6 +172,8 @@ typedef struct kda_decode_args {
   float* S;               /* in/out */
   void* conv_state;       /* in/out */
   void* o;
+  int decay_form;         /* as in kda_prefill_args */
+  const float* A;         /* as in kda_prefill_args */
 } kda_decode_args;
 
 int kda_decode_step(const kda_decode_args* args, void* stream);
@@ -180,6 +199,8 @@ typedef struct kda_prep_args {
   float* k_out;
   float* v_out;
   float* G_out;
+  int decay_form;         /* as in kda_prefill_args (G sums the g it implies) */
+  const float* A;
 } kda_prep_args;
 
 int kda_prep(const kda_prep_args* args, void* stream);

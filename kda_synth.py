@@ -17,7 +17,15 @@ component tables give for KDA):
 Value recipe (all workloads): q, k, v ~ N(0,1); conv_w ~ U(-1/2, 1/2) per
 (channel, tap); g = -softplus(z), z ~ N(-3, 1) per channel; beta = sigmoid(N(0,1))
 per (token, head); gate ~ N(0,1).  The second parameter of N(., .) is the
-standard deviation.  Draws are fp64 (numpy backend) or fp32 (torch backend,
+standard deviation.
+
+K3-logit inputs (`with_k3_logits`, for the KDA_DECAY_K3 form): the same
+tensors, except that g holds decay logits z ~ N(z_mean, 1) per channel, beta
+holds beta logits ~ N(0, 1) per (token, head) (so beta has the distribution
+above), and A ~ N(0, 0.1) fp32 per (head, key channel).  The default
+z_mean = -4.7 gives the log-decay -5 sigmoid(e^A z) the same mean as the
+recipe above (-0.075 per token; 0.7% of values below -0.5 against 0.5%).
+With z_mean = 6 nearly every log-decay sits at K3's bound of -5 per token.  Draws are fp64 (numpy backend) or fp32 (torch backend,
 used for the large workloads on the device), then rounded once to the
 workload's dtype.
 """
@@ -139,6 +147,17 @@ def prefill_inputs_np(w: Workload, T: int | None = None, seed: int | None = None
     return out
 
 
+def with_k3_logits(inp: dict, w: Workload, seed: int | None = None, z_mean: float = -4.7) -> dict:
+    """Copy of prefill or decode inputs whose g and beta are K3's logits, plus A [H, dk]."""
+    seed = (w.seed if seed is None else seed) + 0x1000
+    rz, rb, ra = _streams(seed, 3)
+    out = dict(inp)
+    out["g"] = _round(rz.normal(z_mean, 1.0, inp["g"].shape), w.dtype)
+    out["beta"] = _round(rb.standard_normal(inp["beta"].shape), w.dtype)
+    out["A"] = (ra.standard_normal((w.H, w.dk)) * 0.1).astype(np.float32)
+    return out
+
+
 def decode_inputs_np(w: Workload, steps: int, seed: int | None = None) -> dict:
     """Decode inputs for `steps` consecutive steps (numpy backend).
 
@@ -243,6 +262,19 @@ def prefill_inputs_torch(w: Workload, device, T: int | None = None, seed: int | 
     if w.conv_hist == "normal":
         out["conv_in"] = _normal_fill(torch.empty((B, 3, w.cch), dtype=dt, device=device),
                                       _gen(device, seed * 16 + 8))
+    return out
+
+
+def with_k3_logits_torch(inp: dict, w: Workload, device, seed: int | None = None,
+                         z_mean: float = -4.7) -> dict:
+    """Device-side twin of `with_k3_logits`: g and beta replaced by K3's logits, plus A."""
+    torch = _torch()
+    seed = w.seed if seed is None else seed
+    out = dict(inp)
+    out["g"] = _normal_fill(torch.empty_like(inp["g"]), _gen(device, seed * 16 + 9), mean=z_mean)
+    out["beta"] = _normal_fill(torch.empty_like(inp["beta"]), _gen(device, seed * 16 + 10))
+    out["A"] = _normal_fill(torch.empty((w.H, w.dk), dtype=torch.float32, device=device),
+                            _gen(device, seed * 16 + 11), std=0.1)
     return out
 
 

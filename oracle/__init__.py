@@ -18,6 +18,12 @@ rms_norm_eps from the "Kimi K3" model card config):
 
 Inputs are numpy arrays: float32, or uint16 holding bf16 bits.  All
 arithmetic is fp64 on the exact input values.
+
+K3's gate parameterisation ("Kimi K3.1 Pro vs gpt-oss-120b" and "Gemma 4 31B
+vs Kimi K3", component tables, row "Gated DeltaNet / KDA"): when `inp` holds
+"A" (fp32 [H, dk]), g and beta are logits z and b, and the recurrence uses the
+bounded log-decay g = -5 sigmoid(e^A z) and beta = sigmoid(b) (`k3_log_decay`,
+`k3_beta`).
 """
 from __future__ import annotations
 
@@ -50,7 +56,8 @@ class _Inputs(ctypes.Structure):
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("in_dtype", ctypes.c_int),
                 ("q", ctypes.c_void_p), ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
                 ("conv_w", ctypes.c_void_p), ("g", ctypes.c_void_p),
-                ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p)]
+                ("beta", ctypes.c_void_p), ("gate", ctypes.c_void_p),
+                ("decay_form", ctypes.c_int), ("A", ctypes.c_void_p)]
 
 
 _lib_handle = None
@@ -78,6 +85,25 @@ def _lib():
 
 def max_threads() -> int:
     return int(_lib().kdao_max_threads())
+
+
+def k3_log_decay(z, A):
+    """K3's bounded log-decay -5 sigmoid(e^A z) (fp64), z [..., dk], A broadcast over it."""
+    return -5.0 / (1.0 + np.exp(-np.exp(A) * z))
+
+
+def k3_beta(b):
+    """beta = sigmoid(b) of a beta logit (fp64)."""
+    return 1.0 / (1.0 + np.exp(-b))
+
+
+def decay_and_beta(inp: dict):
+    """fp64 log-decay g [B,T,H,dk] and beta [B,T,H] that `prefill` uses for these inputs."""
+    g, beta = _f64(inp["g"]), _f64(inp["beta"])
+    if inp.get("A") is None:
+        return g, beta
+    A = np.asarray(inp["A"], dtype=np.float32).astype(np.float64)
+    return k3_log_decay(g, A[None, None]), k3_beta(beta)
 
 
 def _dtype_of(a) -> str:
@@ -156,9 +182,14 @@ def prefill(inp: dict, heads=None, S=None, hist=None, want_o=True, want_prep=Fal
     assert hist.dtype == np.float64 and hist.flags.c_contiguous
     o = np.zeros((len(bh), T, dv)) if want_o else None
     prep = np.zeros((len(bh), T, 2 * dk + dv)) if want_prep else None
+    A = inp.get("A")
+    if A is not None:
+        A = np.ascontiguousarray(A, dtype=np.float32)
+        if A.shape != (H, dk):
+            raise ValueError(f"A must be [H, dk] = [{H}, {dk}], got {A.shape}")
     st = _Inputs(B, T, H, dk, dv, 1 if dt == "bf16" else 0, q.ctypes.data, k.ctypes.data,
                  v.ctypes.data, conv_w.ctypes.data, g.ctypes.data, beta.ctypes.data,
-                 gate.ctypes.data)
+                 gate.ctypes.data, 0 if A is None else 1, None if A is None else A.ctypes.data)
     rc = (lib or _lib()).kdao_prefill(ctypes.byref(st), _ptr(bh), len(bh), _ptr(S), _ptr(hist),
                              _ptr(o) if o is not None else None,
                              _ptr(prep) if prep is not None else None, int(nthreads))
@@ -173,6 +204,7 @@ def decode_step(step_inp: dict, S: np.ndarray, hist: np.ndarray, heads=None,
     (fp64, per listed pair) are updated in place; returns o [n, dv]."""
     one = {x: step_inp[x][:, None] for x in ("q", "k", "v", "g", "beta", "gate")}
     one["conv_w"] = step_inp["conv_w"]
+    one["A"] = step_inp.get("A")
     r = prefill(one, heads=heads, S=S, hist=hist, nthreads=nthreads)
     return r["o"][:, 0, :]
 
@@ -202,7 +234,12 @@ def prep_matrix_form(x_raw, hist, w):
 def prefill_matrix_form(inp: dict, heads=None, S=None, hist=None) -> dict:
     """Same outputs as `prefill`, with the state update as an explicit matrix product."""
     q, k, v = _f64(inp["q"]), _f64(inp["k"]), _f64(inp["v"])
-    g, beta, gate = _f64(inp["g"]), _f64(inp["beta"]), _f64(inp["gate"])
+    gate = _f64(inp["gate"])
+    g, beta = _f64(inp["g"]), _f64(inp["beta"])
+    if inp.get("A") is not None:  # K3's logits, mapped here with NumPy's own exp
+        A = np.asarray(inp["A"], dtype=np.float32).astype(np.float64)
+        g = -5.0 * (1.0 / (1.0 + np.exp(-(np.exp(A)[None, None] * g))))
+        beta = 1.0 / (1.0 + np.exp(-beta))
     conv_w = np.asarray(inp["conv_w"], dtype=np.float64)
     B, T, H, dk = q.shape
     dv = v.shape[3]

@@ -40,6 +40,9 @@ static double load(const void* p, int dtype, size_t i) {
 static double silu(double x) { return x / (1.0 + exp(-x)); }
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
+/* K3's bounded log-decay of a decay logit z in a channel with parameter A */
+static double k3_log_decay(double z, double A) { return -5.0 * sigmoid(exp(A) * z); }
+
 /* One (b,h) pair over all T tokens.  S: dk*dv (row = key channel),
  * hist: 3 rows of nc = 2dk+dv raw values (row 0 oldest). */
 static void run_head(const kdao_inputs* in, int b, int h, double* S, double* hist,
@@ -91,11 +94,14 @@ static void run_head(const kdao_inputs* in, int b, int h, double* S, double* his
     /* 4: per-channel decay of the state rows */
     const size_t base_g = base_qk;
     for (int i = 0; i < dk; ++i) {
-      const double a = exp(load(in->g, in->in_dtype, base_g + i));
+      double gi = load(in->g, in->in_dtype, base_g + i);
+      if (in->decay_form == KDAO_DECAY_K3) gi = k3_log_decay(gi, (double)in->A[(size_t)h * dk + i]);
+      const double a = exp(gi);
       for (int j = 0; j < dv; ++j) S[(size_t)i * dv + j] *= a;
     }
     /* 5: delta rule  y = S^T k ; S += beta k (v - y)^T */
-    const double beta = load(in->beta, in->in_dtype, tok * H + h);
+    double beta = load(in->beta, in->in_dtype, tok * H + h);
+    if (in->decay_form == KDAO_DECAY_K3) beta = sigmoid(beta);
     for (int j = 0; j < dv; ++j) y[j] = 0.0;
     for (int i = 0; i < dk; ++i)
       for (int j = 0; j < dv; ++j) y[j] += S[(size_t)i * dv + j] * kh[i];
@@ -125,6 +131,8 @@ int kdao_prefill(const kdao_inputs* in, const int32_t* bh, int n_bh, double* S_i
   if (in->B < 1 || in->T < 0 || in->H < 1 || in->dk < 1 || in->dv < 1) return -1;
   if (!in->q || !in->k || !in->v || !in->conv_w || !in->g || !in->beta || !in->gate) return -1;
   if (in->in_dtype != KDAO_F32 && in->in_dtype != KDAO_BF16) return -1;
+  if (in->decay_form != KDAO_DECAY_DIRECT && in->decay_form != KDAO_DECAY_K3) return -1;
+  if (in->decay_form == KDAO_DECAY_K3 && !in->A) return -1;
   for (int i = 0; i < n_bh; ++i)
     if (bh[i] < 0 || bh[i] >= in->B * in->H) return -1;
   const int dk = in->dk, dv = in->dv, nc = 2 * dk + dv, T = in->T;

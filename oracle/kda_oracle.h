@@ -16,6 +16,11 @@
  *   2. SiLU  x / (1 + e^-x)
  *   3. q^ = q~ (sum q~^2 + 1e-6)^-1/2 dk^-1/2 ;  k^ = k~ (sum k~^2 + 1e-6)^-1/2
  *   4. S <- diag(exp g_t) S                       (per-channel decay, g <= 0)
+ *      With decay_form KDAO_DECAY_K3 the inputs g and beta hold logits z and
+ *      b instead: g = -5 sigmoid(e^A z) (K3's bounded log-decay, "Kimi K3.1
+ *      Pro vs gpt-oss-120b" and "Gemma 4 31B vs Kimi K3", component tables,
+ *      row "Gated DeltaNet / KDA"; A per head and key channel) and
+ *      beta = sigmoid(b).
  *   5. y = S^T k^ ;  S <- S + beta_t k^ (v^ - y)^T   (delta rule)
  *   6. o_core = S^T q^                             (post-update state)
  *   7. o = o_core / sqrt(mean(o_core^2) + 1e-5) * sigmoid(gate)
@@ -37,6 +42,7 @@ extern "C" {
 #endif
 
 enum { KDAO_F32 = 0, KDAO_BF16 = 1 };
+enum { KDAO_DECAY_DIRECT = 0, KDAO_DECAY_K3 = 1 };
 
 typedef struct {
   int B, T, H, dk, dv;
@@ -48,6 +54,8 @@ typedef struct {
   const void* g;         /* [B,T,H,dk] log-decay, g <= 0 */
   const void* beta;      /* [B,T,H] */
   const void* gate;      /* [B,T,H,dv] */
+  int decay_form;        /* KDAO_DECAY_DIRECT: g, beta as given; KDAO_DECAY_K3: logits (step 4) */
+  const float* A;        /* [H,dk] fp32, KDAO_DECAY_K3 only */
 } kdao_inputs;
 
 /*

@@ -42,7 +42,7 @@ def to_dev(inp: dict, dtype: str, device="cuda") -> dict:
     for kk, a in inp.items():
         if a is None:
             out[kk] = None
-        elif kk in ("conv_w", "S0", "S"):
+        elif kk in ("conv_w", "S0", "S", "A"):
             out[kk] = syn.np_to_torch(np.ascontiguousarray(a, dtype=np.float32), "f32", device)
         else:
             out[kk] = syn.np_to_torch(np.ascontiguousarray(a), dtype, device)

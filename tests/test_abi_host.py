@@ -96,6 +96,9 @@ CASES = [
     (dict(k=0x2008), -4), (dict(o=0x8004), -4), (dict(S0=0x9002), -4), (dict(beta=0x6001), -4),
     (dict(dk=48, dv=48), -5), (dict(dk=16, dv=32), -5), (dict(dk=256, dv=256), -5),
     (dict(chunk=48), -5), (dict(chunk=128), -5),
+    # decay form: unknown value, K3's logits without A, A misaligned
+    (dict(decay_form=2), -5), (dict(decay_form=-1), -5), (dict(decay_form=1), -1),
+    (dict(decay_form=1, A=0xb008), -4),
 ]
 
 
@@ -159,7 +162,9 @@ def test_decode_validation_codes(kda):
                 k=0x2000, v=0x3000, conv_w=0x4000, g=0x5000, beta=0x6000, gate=0x7000, S=0x8000,
                 conv_state=0x9000, o=0xa000)
     for over, code in [(dict(S=None), -1), (dict(conv_state=None), -1), (dict(N=0), -2),
-                       (dict(in_dtype=3), -3), (dict(S=0x8008), -4), (dict(dk=24, dv=24), -5)]:
+                       (dict(in_dtype=3), -3), (dict(S=0x8008), -4), (dict(dk=24, dv=24), -5),
+                       (dict(decay_form=5), -5), (dict(decay_form=1), -1),
+                       (dict(decay_form=1, A=0xb004), -4)]:
         a = kda.DecodeArgs(**{**base, **over})
         assert L.kda_decode_step(ctypes.byref(a), None) == code, over
     assert L.kda_decode_step(None, None) == -1
@@ -171,7 +176,8 @@ def test_prep_validation_codes(kda):
                 v=0x3000, conv_w=0x4000, g=0x5000, conv_in=None, q_out=0x6000, k_out=0x7000,
                 v_out=0x8000, G_out=0x9000)
     for over, code in [(dict(G_out=None), -1), (dict(T=-2), -2), (dict(in_dtype=9), -3),
-                       (dict(q_out=0x6004), -4), (dict(chunk=8), -5)]:
+                       (dict(q_out=0x6004), -4), (dict(chunk=8), -5), (dict(decay_form=3), -5),
+                       (dict(decay_form=1), -1)]:
         a = kda.PrepArgs(**{**base, **over})
         assert L.kda_prep(ctypes.byref(a), None) == code, over
 
@@ -180,4 +186,4 @@ def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 1
+    assert L.kda_abi_version() == 2

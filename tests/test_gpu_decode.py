@@ -11,7 +11,7 @@ from kda_synth import Workload
 pytestmark = pytest.mark.gpu
 
 
-def _run_steps(oracle_mod, w: Workload, steps: int, heads=None, device_gen=False):
+def _run_steps(oracle_mod, w: Workload, steps: int, heads=None, device_gen=False, k3=False):
     torch, kda = need_gpu()
     bh = np.arange(w.B * w.H) if heads is None else np.asarray(heads)
     if device_gen:
@@ -25,6 +25,8 @@ def _run_steps(oracle_mod, w: Workload, steps: int, heads=None, device_gen=False
         _, h_o = oracle_mod.initial_carry(w.B, w.H, w.dk, w.dv, heads, None, inp["conv_state"])
     else:
         inp = syn.decode_inputs_np(w, steps)
+        if k3:  # g and beta as K3's logits, with A
+            inp = syn.with_k3_logits(inp, w)
         dev = to_dev(inp, w.dtype)
         S_o, h_o = oracle_mod.initial_carry(w.B, w.H, w.dk, w.dv, heads, inp["S"], inp["conv_state"])
     S = dev["S"].clone()
@@ -33,9 +35,10 @@ def _run_steps(oracle_mod, w: Workload, steps: int, heads=None, device_gen=False
     for s in range(steps):
         step = {x: inp[x][s] for x in ("q", "k", "v", "g", "beta", "gate")}
         step["conv_w"] = inp["conv_w"]
+        step["A"] = inp.get("A")
         o_ref = oracle_mod.decode_step(step, S_o, h_o, heads=heads)
         o = kda.decode_step(dev["q"][s], dev["k"][s], dev["v"][s], dev["conv_w"], dev["g"][s],
-                            dev["beta"][s], dev["gate"][s], S, conv)
+                            dev["beta"][s], dev["gate"][s], S, conv, A=dev.get("A"))
         torch.cuda.synchronize()
         o_np = o.cpu().numpy().reshape(w.B * w.H, w.dv)[bh]
         assert_rms_close(o_np, o_ref, tol, f"decode o step {s}")
@@ -54,6 +57,13 @@ def _run_steps(oracle_mod, w: Workload, steps: int, heads=None, device_gen=False
 def test_decode_small(oracle_mod, d, dtype):
     w = Workload("dec", 3, 1, 2, d, d, 1, dtype, s0_sigma=0.05, conv_hist="normal", seed=17 + d)
     _run_steps(oracle_mod, w, steps=6)
+
+
+@pytest.mark.parametrize("d,dtype", [(16, "f32"), (128, "bf16")])
+def test_decode_k3_logits(oracle_mod, d, dtype):
+    """g and beta given as K3's logits (KDA_DECAY_K3, A per head and channel)."""
+    w = Workload("dk3", 3, 1, 2, d, d, 1, dtype, s0_sigma=0.05, conv_hist="normal", seed=29 + d)
+    _run_steps(oracle_mod, w, steps=6, k3=True)
 
 
 def test_decode_k3_batch_sampled(oracle_mod):

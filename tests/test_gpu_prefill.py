@@ -20,7 +20,8 @@ path = pytest.mark.parametrize("path", list(PATHS))
 
 def _gpu_prefill(kda, dev, chunk, **kw):
     return kda.prefill(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"],
-                       dev["gate"], S0=dev.get("S0"), conv_in=dev.get("conv_in"), chunk=chunk, **kw)
+                       dev["gate"], S0=dev.get("S0"), conv_in=dev.get("conv_in"), chunk=chunk,
+                       A=dev.get("A"), **kw)
 
 
 def _check_vs_oracle(oracle_mod, w: Workload, inp, o, S_T, conv_out, heads=None, what="", tol=None):
@@ -277,6 +278,76 @@ def test_no_decay(oracle_mod, path):
     dev = to_dev(inp, "bf16")
     o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} g=0")
+
+
+# -- K3's gate parameterisation (KDA_DECAY_K3) ----------------------------------------------
+
+@path
+@pytest.mark.parametrize("T", [17, 130])
+def test_k3_logits(oracle_mod, path, T):
+    """g and beta given as K3's logits: g = -5 sigmoid(e^A z), beta = sigmoid(b),
+    computed in the kernels where they load g and beta."""
+    torch, kda = need_gpu()
+    w = Workload("k3", 2, T, 3, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=47)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w)
+    dev = to_dev(inp, "bf16")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} K3 logits")
+
+
+@path
+def test_k3_logits_at_the_bound(oracle_mod, path):
+    """Decay logits around +6: nearly every channel decays by K3's bound of -5 per
+    token, so a 16-token tile spans e^-80.  The pages' claim is that this stays
+    inside bf16 range, and every chunk's decay-weighted products then run on bf16
+    operands (8-bit significands) as in the pages' own design.  This is not one of
+    the workloads the 2e-2 bound is stated for; the bound here follows from the
+    bf16 arithmetic: the state forgets nearly everything each token, o_core is
+    mostly the token's own beta (k.q) v term, and the per-token RMSNorm scales a
+    token whose o_core nearly cancels back up to unit size, together with the
+    bf16 rounding of its terms.  Measured worst case 4.7e-2 x RMS(o); the bounds
+    are 6e-2 on the largest error and 1e-2 on the RMS error, for o and S_T."""
+    torch, kda = need_gpu()
+    w = Workload("k3b", 1, 160, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=53)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w, z_mean=6.0)
+    dev = to_dev(inp, "bf16")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=PATHS[path])
+    torch.cuda.synchronize()
+    assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
+    r = oracle_mod.prefill(inp)
+    for got, want, what in ((gather_heads(o, r["heads"], w.H), r["o"], "o"),
+                            (S_T.cpu().numpy().reshape(w.B * w.H, w.dk, w.dv), r["S_T"], "S_T")):
+        assert_rms_close(got, want, 6e-2, f"{path} K3 bound {what}")
+        err = np.asarray(got, dtype=np.float64) - want
+        rms_err = float(np.sqrt(np.mean(err * err)) / np.sqrt(np.mean(want * want)))
+        print(f"  {path} K3 bound {what}: RMS(err)/RMS = {rms_err:.3e}", flush=True)
+        assert rms_err <= 1e-2, f"{path} K3 bound {what}: RMS error {rms_err:.3e} > 1e-2"
+
+
+@pytest.mark.parametrize("dtype,d,chunk", [("f32", 16, 16), ("bf16", 64, 32)])
+def test_k3_logits_other_sizes(oracle_mod, dtype, d, chunk):
+    """The single-kernel path's other instantiations with K3's logits."""
+    torch, kda = need_gpu()
+    w = Workload("k3s", 1, 45, 2, d, d, chunk, dtype, s0_sigma=0.1, conv_hist="normal", seed=59 + d)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w)
+    dev = to_dev(inp, dtype)
+    o, S_T, c = _gpu_prefill(kda, dev, chunk)
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"K3 logits {dtype} d{d} C{chunk}")
+
+
+def test_k3_prep_cumsum(oracle_mod):
+    """kda_prep with K3's logits: G is the chunk-local cumulative sum of the
+    bounded log-decay the oracle derives from the same logits."""
+    torch, kda = need_gpu()
+    w = Workload("k3p", 1, 100, 2, 128, 128, 64, "bf16", conv_hist="normal", seed=61)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w)
+    dev = to_dev(inp, "bf16")
+    _, _, _, G = kda.prep(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"],
+                          conv_in=dev["conv_in"], chunk=64, A=dev["A"])
+    torch.cuda.synchronize()
+    g, _ = oracle_mod.decay_and_beta(inp)
+    want = np.concatenate([np.cumsum(g[:, c0:c0 + 64], axis=1) for c0 in range(0, w.T, 64)], axis=1)
+    assert_rms_close(G.cpu().numpy(), want, 1e-5, "K3 G")
 
 
 @path

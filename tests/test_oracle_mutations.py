@@ -15,6 +15,7 @@ import pytest
 
 import kda_synth as syn
 from kda_synth import Workload, to_f64
+import k3_checks
 from ref_math import bruteforce_core, gated_rmsnorm, head_channels, prep_numpy
 
 SRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "oracle",
@@ -27,7 +28,7 @@ MUTANTS = {
     "dk^-1/2 on k": ("const double rk = 1.0 / sqrt(sk + L2_EPS);",
                      "const double rk = 1.0 / sqrt(sk + L2_EPS) / sqrt((double)dk);"),
     "L2 eps": ("L2_EPS = 1e-6", "L2_EPS = 1e-4"),
-    "decay sign": ("const double a = exp(load(", "const double a = exp(-load("),
+    "decay sign": ("const double a = exp(gi);", "const double a = exp(-gi);"),
     "correction sign": ("(vh[j] - y[j])", "(vh[j] + y[j])"),
     "beta dropped": ("const double bk = beta * kh[i];", "const double bk = kh[i];"),
     "y from q": ("y[j] += S[(size_t)i * dv + j] * kh[i];", "y[j] += S[(size_t)i * dv + j] * qh[i];"),
@@ -38,6 +39,13 @@ MUTANTS = {
                               "ch = (size_t)h * dk + (c - dk);"),
     "v channel offset": ("ch = (size_t)2 * H * dk + (size_t)h * dv + (c - 2 * dk);",
                          "ch = (size_t)2 * H * dk + (c - 2 * dk);"),
+    # K3's gate parameterisation
+    "K3 decay sign": ("-5.0 * sigmoid(exp(A) * z)", "-5.0 * sigmoid(-exp(A) * z)"),
+    "K3 bound": ("-5.0 * sigmoid(exp(A) * z)", "-4.0 * sigmoid(exp(A) * z)"),
+    "K3 A not exponentiated": ("-5.0 * sigmoid(exp(A) * z)", "-5.0 * sigmoid(A * z)"),
+    "K3 A of head 0 for all": ("in->A[(size_t)h * dk + i]", "in->A[i]"),
+    "K3 beta logit not mapped": ("if (in->decay_form == KDAO_DECAY_K3) beta = sigmoid(beta);", ""),
+    "K3 decay not mapped": ("if (in->decay_form == KDAO_DECAY_K3) gi = ", "if (0) gi = "),
 }
 
 
@@ -66,7 +74,7 @@ def _checks_fail(oracle_mod, lib) -> bool:
             [inp["q"][b, :, h], inp["k"][b, :, h], inp["v"][b, :, h]], 1).astype(np.float64)])[-3:]
         if not np.array_equal(r["conv_out"][i], want_hist):
             return True
-    return False
+    return bool(k3_checks.failures(oracle_mod, lib))
 
 
 def test_unmutated_oracle_passes_checks(oracle_mod):

@@ -14,6 +14,7 @@ import pytest
 
 import kda_synth as syn
 from kda_synth import Workload, to_f64
+import k3_checks
 from ref_math import (bruteforce_core, conv_numpy, gated_rmsnorm, head_channels, prep_numpy,
                       raw_head, silu)
 
@@ -145,6 +146,27 @@ def test_beta_zero_only_decays(oracle_mod):
         qn, _, _ = prep_numpy(inp, "f32", b, h, conv_in[b][:, head_channels(w.H, w.dk, w.dv, h)])
         oc = (qn * np.exp(G)) @ S0
         np.testing.assert_allclose(r["o"][i], gated_rmsnorm(oc, gate[b, :, h]), rtol=1e-10)
+
+
+# -- K3's gate parameterisation --------------------------------------------------------
+
+def test_k3_decay_and_beta_properties(oracle_mod):
+    """The KDA_DECAY_K3 form: the bound, its limits, z = 0, the symmetry, e^A scaling,
+    A per head and beta = sigmoid(b) (tests/k3_checks.py says what each pins).
+    Catches a flipped sign, a wrong bound, A used without exp, head 0's A for
+    every head, and an unmapped beta or decay logit."""
+    assert k3_checks.failures(oracle_mod) == []
+
+
+def test_k3_matrix_form_twin_agrees(oracle_mod):
+    """The NumPy matrix-form route maps the logits with its own code; the C
+    recurrence agrees with it on K3-form inputs."""
+    w = Workload("t", 1, 20, 2, 8, 12, 16, "f32", s0_sigma=0.3, conv_hist="normal", seed=9)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w)
+    a = oracle_mod.prefill(inp)
+    b = oracle_mod.prefill_matrix_form(inp)
+    np.testing.assert_allclose(a["o"], b["o"], rtol=1e-10, atol=1e-13)
+    np.testing.assert_allclose(a["S_T"], b["S_T"], rtol=1e-10, atol=1e-13)
 
 
 # -- P4 / P6: carry -----------------------------------------------------------------------
