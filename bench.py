@@ -15,6 +15,8 @@ Prints one JSON line.  Options:
   --decode-steps  decode steps timed back to back (default 1000; 0 skips decode)
   --no-cpu        skip the oracle leg
   --calibrate     also run a plain 1 GiB read + 1 GiB write kernel (for HBM counter scaling)
+  --verify-tokens M tokens per sequence per kda_decode_multi call on the decode shape
+                  (default 4; 0 skips): tokens/s and HBM GB/s
   --decay-form    direct (default: g and beta given) | k3 (g and beta given as K3's
                   logits, g = -5 sigmoid(e^A z) and beta = sigmoid(b) computed in the kernels)
 """
@@ -61,6 +63,14 @@ def prefill_flops(B, T, H, dk, dv, C=64):
                + tri_incl * dv)         # P U
         return 2 * mac
     return B * H * (n_full * chunk(C) + (chunk(tail) if tail else 0))
+
+
+def decode_multi_bytes_per_call(N, M, H, dk, dv, in_bytes=2, out_bytes=4):
+    """kda_decode_multi: the state once, M tokens of activations and outputs."""
+    per = (4 * dk * dv * 2
+           + M * (in_bytes * (2 * dk + dv + dk + dv) + in_bytes + out_bytes * dv)
+           + 2 * 3 * (2 * dk + dv) * in_bytes)
+    return N * H * per + H * (2 * dk + dv) * 4 * 4
 
 
 def decode_bytes_per_step(N, H, dk, dv, in_bytes=2, out_bytes=4):
@@ -142,6 +152,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--decay-form", default="direct", choices=["direct", "k3"])
+    ap.add_argument("--verify-tokens", type=int, default=4)
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU path only; run it with --gpus 1 "
@@ -273,6 +284,49 @@ def main():
                                       "algorithmic_bytes_per_launch": dbytes}}
         log(f"[bench] decode {dms * 1e3:.1f} us/step, {gbs:.0f} GB/s")
         del d
+
+    if args.decode_steps > 0 and args.verify_tokens > 0:
+        wd = syn.WORKLOADS["decode"]
+        M = args.verify_tokens
+        ncalls = max(1, args.decode_steps // M)
+        t0 = time.perf_counter()
+        # ncalls sets of M tokens for N sequences: [ncalls * N, M, H, .]
+        wm = syn.Workload("verify", ncalls * wd.B, M, wd.H, wd.dk, wd.dv, 1, "bf16", seed=wd.seed + 16)
+        dm = syn.prefill_inputs_torch(wm, dev)
+        st = syn.decode_inputs_torch(wd, dev, 1)
+        om = torch.empty((wd.B, M, wd.H, wd.dv), dtype=torch.float32, device=dev)
+        torch.cuda.synchronize()
+        log(f"[bench] multi-token decode inputs ({ncalls} calls x {M} tokens) generated in "
+            f"{time.perf_counter() - t0:.1f} s")
+
+        def mstep(c):
+            r = slice(c * wd.B, (c + 1) * wd.B)
+            kda.decode_multi(dm["q"][r], dm["k"][r], dm["v"][r], dm["conv_w"], dm["g"][r], dm["beta"][r],
+                             dm["gate"][r], st["S"], st["conv_state"], o=om)
+
+        for c in range(min(5, ncalls)):
+            mstep(c)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for c in range(ncalls):
+            mstep(c)
+        e1.record()
+        torch.cuda.synchronize()
+        mms = e0.elapsed_time(e1) / ncalls
+        mbytes = decode_multi_bytes_per_call(wd.B, M, wd.H, wd.dk, wd.dv)
+        mgbs = mbytes / (mms * 1e-3) / 1e9
+        out["decode_multi"] = {"metric": "multi-token decode tokens/s", "value": wd.B * M / (mms * 1e-3),
+                               "unit": "tokens/s", "tokens_per_call": M, "ms_per_call": mms,
+                               "calls_timed": ncalls,
+                               "config": f"kda_decode_multi N{wd.B} M{M} H{wd.H} dk=dv={wd.dk}, bf16 inputs, "
+                                         "f32 state, all tokens committed",
+                               "roofline": {"bound": "hbm", "achieved": mgbs, "peak": HBM_PEAK_GBS,
+                                            "unit": "GB/s", "frac": mgbs / HBM_PEAK_GBS,
+                                            "algorithmic_bytes_per_launch": mbytes}}
+        log(f"[bench] multi-token decode M={M}: {mms * 1e3:.1f} us/call, "
+            f"{wd.B * M / (mms * 1e-3) / 1e6:.2f} M tokens/s, {mgbs:.0f} GB/s")
+        del dm, st
 
     if args.calibrate:
         # an elementwise kernel that reads 1 GiB and writes 1 GiB: the known-size

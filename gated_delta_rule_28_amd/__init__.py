@@ -8,6 +8,7 @@ works, but every call raises (there is no fallback implementation).
     o, S_T, conv_out = prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64)
     nbytes = workspace_bytes(B, T, H, dk, dv, chunk, in_dtype)  # what prefill allocates
     o = decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state)   # S, conv_state in place
+    o = decode_multi(q, k, v, conv_w, g, beta, gate, S, conv_state, accept=None)  # [N, M, H, .]
     qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
 
 Every call also takes A=None: given an fp32 [H, dk] tensor, g and beta are K3's
@@ -19,9 +20,9 @@ from __future__ import annotations
 import ctypes
 import os
 
-__all__ = ["prefill", "decode_step", "prep", "workspace_bytes", "library_path", "lib", "KDAError",
+__all__ = ["prefill", "decode_step", "decode_multi", "prep", "workspace_bytes", "library_path", "lib", "KDAError",
            "KDA_F32", "KDA_BF16", "KDA_DECAY_DIRECT", "KDA_DECAY_K3", "PrefillArgs", "DecodeArgs",
-           "PrepArgs"]
+           "PrepArgs", "DecodeMultiArgs", "MAX_DECODE_TOKENS"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -31,6 +32,7 @@ KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
 ABI_VERSION = 2
+MAX_DECODE_TOKENS = 16
 
 
 class KDAError(RuntimeError):
@@ -60,6 +62,14 @@ class DecodeArgs(ctypes.Structure):
                 ("decay_form", ctypes.c_int), ("A", _P)]
 
 
+class DecodeMultiArgs(ctypes.Structure):
+    _fields_ = [("N", ctypes.c_int), ("M", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("out_dtype", ctypes.c_int),
+                ("q", _P), ("k", _P), ("v", _P), ("conv_w", _P), ("g", _P), ("beta", _P),
+                ("gate", _P), ("S", _P), ("conv_state", _P), ("o", _P), ("accept", _P),
+                ("decay_form", ctypes.c_int), ("A", _P)]
+
+
 class PrepArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("chunk", ctypes.c_int),
@@ -86,6 +96,8 @@ def lib():
         L.kda_prefill_workspace_min_bytes.restype = ctypes.c_size_t
         L.kda_decode_step.argtypes = [ctypes.POINTER(DecodeArgs), _P]
         L.kda_decode_step.restype = ctypes.c_int
+        L.kda_decode_multi.argtypes = [ctypes.POINTER(DecodeMultiArgs), _P]
+        L.kda_decode_multi.restype = ctypes.c_int
         L.kda_prep.argtypes = [ctypes.POINTER(PrepArgs), _P]
         L.kda_prep.restype = ctypes.c_int
         L.kda_status_string.argtypes = [ctypes.c_int]
@@ -190,6 +202,28 @@ def decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype
     a = DecodeArgs(N, H, dk, dv, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w),
                    _ptr(g), _ptr(beta), _ptr(gate), _ptr(S), _ptr(conv_state), _ptr(o), *_decay(A))
     _check("kda_decode_step", lib().kda_decode_step(ctypes.byref(a), _stream(q.device)))
+    return o
+
+
+def decode_multi(q, k, v, conv_w, g, beta, gate, S, conv_state, o=None, out_dtype=None, accept=None,
+                 A=None):
+    """M tokens per sequence in one call (kda_decode_multi): inputs [N, M, H, .].
+
+    Returns o [N, M, H, dv] for every token.  S and conv_state are updated in place
+    to the state after the first accept[n] tokens (accept: int32 [N] device tensor,
+    or None for all M)."""
+    torch = _torch()
+    N, M, H, dk = q.shape
+    dv = v.shape[-1]
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((N, M, H, dv), dtype=out_dtype, device=q.device)
+    if accept is not None and accept.dtype != torch.int32:
+        raise TypeError("accept must be an int32 tensor")
+    a = DecodeMultiArgs(N, M, H, dk, dv, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w),
+                        _ptr(g), _ptr(beta), _ptr(gate), _ptr(S), _ptr(conv_state), _ptr(o),
+                        _ptr(accept), *_decay(A))
+    _check("kda_decode_multi", lib().kda_decode_multi(ctypes.byref(a), _stream(q.device)))
     return o
 
 

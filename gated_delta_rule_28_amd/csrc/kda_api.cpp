@@ -143,6 +143,30 @@ int kda_decode_step(const kda_decode_args* a, void* stream) {
   return kda::launch_decode(*a, reinterpret_cast<hipStream_t>(stream));
 }
 
+int kda_decode_multi(const kda_decode_multi_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(a);
+  int rc = kda::check_common(a->N, 1, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype);
+  if (rc != KDA_OK) return rc;
+  if (a->M < 1 || a->M > KDA_MAX_DECODE_TOKENS)
+    return fail(KDA_E_SHAPE, "M=%d not in [1, %d]", a->M, KDA_MAX_DECODE_TOKENS);
+  if ((long long)a->N * a->M * a->H > 0x7fffffffLL)
+    return fail(KDA_E_SHAPE, "N*M*H too large");
+  rc = kda::check_decay(a->decay_form, a->A);
+  if (rc != KDA_OK) return rc;
+  REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
+  REQUIRE_PTR(a->g); REQUIRE_PTR(a->beta); REQUIRE_PTR(a->gate); REQUIRE_PTR(a->S);
+  REQUIRE_PTR(a->conv_state); REQUIRE_PTR(a->o);
+  REQUIRE_A16(a->q); REQUIRE_A16(a->k); REQUIRE_A16(a->v); REQUIRE_A16(a->conv_w);
+  REQUIRE_A16(a->g); REQUIRE_A16(a->gate); REQUIRE_A16(a->S); REQUIRE_A16(a->conv_state);
+  REQUIRE_A16(a->o);
+  if (!kda::aligned_n(a->beta, kda::esize(a->in_dtype)))
+    return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
+  if (a->accept != nullptr && !kda::aligned_n(a->accept, 4))
+    return fail(KDA_E_ALIGN, "accept is not 4-byte aligned");
+  return kda::launch_decode_multi(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
 int kda_prep(const kda_prep_args* a, void* stream) {
   kda::g_err[0] = '\0';
   REQUIRE_PTR(a);

@@ -186,6 +186,227 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// decode_multi_kernel: M consecutive tokens per sequence (speculative decoding:
+// verify M drafted tokens in one pass), one workgroup per (n, h).  The same
+// recurrence as M calls of decode_kernel, but the state is read once, kept in
+// registers for the M tokens and written once, after token accept[n] - 1 (not
+// at all when accept[n] = 0): its traffic is that of one step.  The conv
+// history is replaced by the last three raw tokens of the accepted prefix.
+// ---------------------------------------------------------------------------
+struct DecodeMultiParams {
+  int H, M;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  float* S;
+  void* conv_state;
+  void* o;
+  const int32_t* accept;  // [N] tokens whose updates are kept, or null (all M)
+  const float* A;         // [H, dk]: g and beta are K3's logits; null: given directly
+};
+
+constexpr int kMaxTokens = 16;
+
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16>
+__global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(DecodeMultiParams p) {
+  constexpr int NC = 2 * DK + DV;
+  constexpr int CG = DV / 4;
+  constexpr int RG0 = kDecodeThreads / CG;
+  constexpr int RG = RG0 < DK ? RG0 : DK;
+  constexpr int RPT = DK / RG;
+
+  const int tid = threadIdx.x;
+  const int nh = blockIdx.x;
+  const int H = p.H, M = p.M;
+  const int n = nh / H;
+  const int h = nh - n * H;
+  const size_t cch = (size_t)H * NC;
+  const int acc_n = p.accept != nullptr ? min(max(p.accept[n], 0), M) : M;
+
+  __shared__ float xs[kMaxTokens][NC];     // conv + SiLU, then q^ | k^ | v^
+  __shared__ float alpha[kMaxTokens][DK];  // e^g
+  __shared__ float betas[kMaxTokens];
+  __shared__ float scal[kMaxTokens][3];    // q scale, k scale, k^ . q^
+  __shared__ float red[2][RG][DV];
+  __shared__ float us[DV];
+  __shared__ float ocs[DV];
+  __shared__ float rs_s;
+
+  // row of token t of this (n, h) in the [N, M, H, .] inputs
+  auto tok = [&](int t) { return ((size_t)n * M + t) * H + h; };
+
+  // 1. conv + SiLU of every token; the new raw history is the accepted
+  //    prefix's last three tokens (from the old history where it is shorter)
+  for (int c = tid; c < NC; c += kDecodeThreads) {
+    size_t ch;
+    const void* src;
+    int D, cc;
+    if (c < DK) {
+      ch = (size_t)h * DK + c; src = p.q; D = DK; cc = c;
+    } else if (c < 2 * DK) {
+      ch = (size_t)H * DK + (size_t)h * DK + (c - DK); src = p.k; D = DK; cc = c - DK;
+    } else {
+      ch = (size_t)2 * H * DK + (size_t)h * DV + (c - 2 * DK); src = p.v; D = DV; cc = c - 2 * DK;
+    }
+    const size_t r0 = ((size_t)n * 3 + 0) * cch + ch;
+    const float h0 = load1<IN_BF16>(p.conv_state, r0);
+    const float h1 = load1<IN_BF16>(p.conv_state, r0 + cch);
+    const float h2 = load1<IN_BF16>(p.conv_state, r0 + 2 * cch);
+    const float4 w = *reinterpret_cast<const float4*>(p.conv_w + ch * 4);
+    // new history rows R(a-3), R(a-2), R(a-1), with R(i) = history row 3 + i for i < 0
+    float n0 = acc_n == 0 ? h0 : acc_n == 1 ? h1 : h2;
+    float n1 = acc_n == 0 ? h1 : h2;
+    float n2 = h2;
+    float xm3 = h0, xm2 = h1, xm1 = h2;
+    for (int t = 0; t < M; ++t) {
+      const float x = load1<IN_BF16>(src, tok(t) * D + cc);
+      xs[t][c] = siluf_(w.x * xm3 + w.y * xm2 + w.z * xm1 + w.w * x);
+      xm3 = xm2; xm2 = xm1; xm1 = x;
+      if (t == acc_n - 3) n0 = x;
+      if (t == acc_n - 2) n1 = x;
+      if (t == acc_n - 1) n2 = x;
+    }
+    // exact in the history dtype: every value came from it or from the input
+    if (acc_n > 0) {
+      store1<IN_BF16>(p.conv_state, r0, n0);
+      store1<IN_BF16>(p.conv_state, r0 + cch, n1);
+      store1<IN_BF16>(p.conv_state, r0 + 2 * cch, n2);
+    }
+  }
+  // decay factors and beta of every token
+  for (int idx = tid; idx < M * DK; idx += kDecodeThreads) {
+    const int t = idx / DK, c = idx - t * DK;
+    float gv = load1<IN_BF16>(p.g, tok(t) * DK + c);
+    if (p.A != nullptr) gv = k3_decay(gv, fast_exp(p.A[(size_t)h * DK + c]));
+    alpha[t][c] = fast_exp(gv);
+  }
+  if (tid < M) {
+    float b = load1<IN_BF16>(p.beta, tok(tid));
+    if (p.A != nullptr) b = sigmoidf_(b);
+    betas[tid] = b;
+  }
+  __syncthreads();
+
+  // 2. L2 norms of q and k per token, one wave per token
+  {
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int t = wv; t < M; t += kDecodeThreads / 64) {
+      float sq = 0.f, sk = 0.f, sqk = 0.f;
+      for (int c = ln; c < DK; c += 64) {
+        const float a = xs[t][c], b = xs[t][DK + c];
+        sq += a * a;
+        sk += b * b;
+        sqk += a * b;
+      }
+      sq = group_sum<64>(sq);
+      sk = group_sum<64>(sk);
+      sqk = group_sum<64>(sqk);
+      if (ln == 0) {
+        const float rq = fast_rsq(sq + kL2Eps) * fast_rsq((float)DK);
+        const float rk = fast_rsq(sk + kL2Eps);
+        scal[t][0] = rq;
+        scal[t][1] = rk;
+        scal[t][2] = sqk * rq * rk;
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = tid; idx < M * 2 * DK; idx += kDecodeThreads) {
+    const int t = idx / (2 * DK), c = idx - t * 2 * DK;
+    xs[t][c] *= c < DK ? scal[t][0] : scal[t][1];
+  }
+  __syncthreads();
+
+  // 3. the tokens in order, the state in registers
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  const bool active = rg < RG;
+  f4* Sp = reinterpret_cast<f4*>(p.S + (size_t)nh * DK * DV);
+  f4 s[RPT];
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + RG * i) * CG + cg);
+  }
+  for (int t = 0; t < M; ++t) {
+    // S' = diag(e^g) S;  S'^T k^ and S'^T q^
+    if (active) {
+      f4 y = f4{0.f, 0.f, 0.f, 0.f}, z = y;
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int r = rg + RG * i;
+        s[i] *= alpha[t][r];
+        y += s[i] * xs[t][DK + r];
+        z += s[i] * xs[t][r];
+      }
+      *reinterpret_cast<f4*>(&red[0][rg][4 * cg]) = y;
+      *reinterpret_cast<f4*>(&red[1][rg][4 * cg]) = z;
+    }
+    __syncthreads();
+    // u = beta (v^ - y);  o_core = S'^T q^ + (k^ . q^) u
+    if (tid < DV) {
+      float y = 0.f, z = 0.f;
+#pragma unroll
+      for (int r = 0; r < RG; ++r) {
+        y += red[0][r][tid];
+        z += red[1][r][tid];
+      }
+      const float u = betas[t] * (xs[t][2 * DK + tid] - y);
+      us[tid] = u;
+      ocs[tid] = z + scal[t][2] * u;
+    }
+    __syncthreads();
+    // S <- S' + k^ u^T; the state after the accepted prefix goes to memory
+    if (active) {
+      const f4 u = *reinterpret_cast<const f4*>(&us[4 * cg]);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) s[i] += u * xs[t][DK + rg + RG * i];
+      if (t == acc_n - 1) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(s[i], Sp + (size_t)(rg + RG * i) * CG + cg);
+      }
+    }
+    if (tid < 64) {
+      float ss = 0.f;
+      for (int j = tid; j < DV; j += 64) ss += ocs[j] * ocs[j];
+      ss = group_sum<64>(ss);
+      if (tid == 0) rs_s = fast_rsq(ss * (1.0f / DV) + kRmsEps);
+    }
+    __syncthreads();
+    if (tid < DV) {
+      const float gt = load1<IN_BF16>(p.gate, tok(t) * DV + tid);
+      store1<OUT_BF16>(p.o, tok(t) * DV + tid, ocs[tid] * rs_s * sigmoidf_(gt));
+    }
+  }
+}
+
+template <int DK, int DV, bool IB, bool OB>
+int run_multi(const kda_decode_multi_args& a, hipStream_t s) {
+  DecodeMultiParams p{a.H, a.M, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o,
+                      a.accept, a.decay_form == KDA_DECAY_K3 ? a.A : nullptr};
+  const unsigned grid = (unsigned)((size_t)a.N * a.H);
+  hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("multi-token decode launch failed: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  return KDA_OK;
+}
+
+template <int DK, int DV>
+int run_multi_dt(const kda_decode_multi_args& a, hipStream_t s) {
+  const bool ib = a.in_dtype == KDA_BF16, ob = a.out_dtype == KDA_BF16;
+  if (ib && ob) return run_multi<DK, DV, true, true>(a, s);
+  if (ib) return run_multi<DK, DV, true, false>(a, s);
+  if (ob) return run_multi<DK, DV, false, true>(a, s);
+  return run_multi<DK, DV, false, false>(a, s);
+}
+
 template <int DK, int DV, bool IB, bool OB>
 int run(const kda_decode_args& a, hipStream_t s) {
   DecodeParams p{a.H, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o,
@@ -210,6 +431,18 @@ int run_dt(const kda_decode_args& a, hipStream_t s) {
 }
 
 }  // namespace
+
+int launch_decode_multi(const kda_decode_multi_args& a, hipStream_t s) {
+  switch (a.dk) {
+    case 16: return run_multi_dt<16, 16>(a, s);
+    case 32: return run_multi_dt<32, 32>(a, s);
+    case 64: return run_multi_dt<64, 64>(a, s);
+    case 128: return run_multi_dt<128, 128>(a, s);
+    default:
+      set_error("multi-token decode: head dim %d not in {16,32,64,128}", a.dk);
+      return KDA_E_UNSUPPORTED;
+  }
+}
 
 int launch_decode(const kda_decode_args& a, hipStream_t s) {
   if (a.dk != a.dv) {

@@ -10,6 +10,7 @@
 namespace kda {
 
 int launch_decode(const kda_decode_args& a, hipStream_t s);
+int launch_decode_multi(const kda_decode_multi_args& a, hipStream_t s);
 int launch_prefill(const kda_prefill_args& a, hipStream_t s);
 int launch_prep(const kda_prep_args& a, hipStream_t s);
 

@@ -179,6 +179,47 @@ typedef struct kda_decode_args {
 int kda_decode_step(const kda_decode_args* args, void* stream);
 
 /*
+ * M consecutive tokens per sequence in one call (1 <= M <= KDA_MAX_DECODE_TOKENS),
+ * for speculative decoding: drafted tokens are verified in one pass (the pages
+ * name MTP self-drafting and an EAGLE-3 drafter for K3: "Kimi K3.1 Pro vs
+ * gpt-oss-120b" and "Gemma 4 31B vs Kimi K3", component tables, rows "Speculative
+ * decoding" and "MTP layer turned EAGLE-3 drafter").
+ *
+ * Inputs are [N, M, H, .] (token t of sequence n at row n*M + t): q, k [N,M,H,dk],
+ * v, gate, o [N,M,H,dv], g [N,M,H,dk], beta [N,M,H].  o is written for all M
+ * tokens, each from the state after the tokens before it -- exactly a prefill
+ * of the M tokens from (S, conv_state).  S and conv_state are then replaced by
+ * the state and raw history after the first accept[n] tokens of sequence n
+ * (accept: int32 [N] in device memory, values clamped to [0, M]; NULL means M;
+ * 0 leaves both unchanged).  Typical use: one call with accept[n] = 0 to verify
+ * (outputs only), then one with the accepted counts to commit.
+ * The state is read and written once per call, whatever M is.
+ * Errors as kda_decode_step; M outside [1, KDA_MAX_DECODE_TOKENS] is
+ * KDA_E_SHAPE; accept must be 4-byte aligned (KDA_E_ALIGN).
+ */
+#define KDA_MAX_DECODE_TOKENS 16
+typedef struct kda_decode_multi_args {
+  int N, M, H, dk, dv;
+  int in_dtype;
+  int out_dtype;
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  float* S;               /* in/out */
+  void* conv_state;       /* in/out */
+  void* o;
+  const int32_t* accept;  /* [N] device, or NULL (all M tokens) */
+  int decay_form;         /* as in kda_prefill_args */
+  const float* A;         /* as in kda_prefill_args */
+} kda_decode_multi_args;
+
+int kda_decode_multi(const kda_decode_multi_args* args, void* stream);
+
+/*
  * The first stage of the prefill on its own: conv + SiLU + L2 normalisation
  * (q scaled by dk^-1/2) and the chunk-local inclusive cumulative sum of g.
  * Writes fp32 q^, k^ [B,T,H,dk], v^ [B,T,H,dv] and G [B,T,H,dk], where

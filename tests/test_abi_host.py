@@ -35,7 +35,7 @@ def declared_functions():
 
 def test_header_declares_the_abi():
     names = declared_functions()
-    for must in ("kda_prefill", "kda_decode_step", "kda_prefill_workspace_bytes", "kda_prep",
+    for must in ("kda_prefill", "kda_decode_step", "kda_decode_multi", "kda_prefill_workspace_bytes", "kda_prep",
                  "kda_status_string", "kda_last_error", "kda_abi_version"):
         assert must in names
 
@@ -67,12 +67,12 @@ def _c_offsets(struct, fields):
     return vals[0], vals[1:]
 
 
-@pytest.mark.parametrize("name", ["PrefillArgs", "DecodeArgs", "PrepArgs"])
+@pytest.mark.parametrize("name", ["PrefillArgs", "DecodeArgs", "PrepArgs", "DecodeMultiArgs"])
 def test_ctypes_layout_matches_header(name):
     import gated_delta_rule_28_amd as kda
     cls = getattr(kda, name)
     struct = {"PrefillArgs": "kda_prefill_args", "DecodeArgs": "kda_decode_args",
-              "PrepArgs": "kda_prep_args"}[name]
+              "PrepArgs": "kda_prep_args", "DecodeMultiArgs": "kda_decode_multi_args"}[name]
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_offsets(struct, fields)
     assert ctypes.sizeof(cls) == size
@@ -168,6 +168,20 @@ def test_decode_validation_codes(kda):
         a = kda.DecodeArgs(**{**base, **over})
         assert L.kda_decode_step(ctypes.byref(a), None) == code, over
     assert L.kda_decode_step(None, None) == -1
+
+
+def test_decode_multi_validation_codes(kda):
+    L = kda.lib()
+    base = dict(N=2, M=4, H=2, dk=16, dv=16, in_dtype=kda.KDA_BF16, out_dtype=kda.KDA_F32, q=0x1000,
+                k=0x2000, v=0x3000, conv_w=0x4000, g=0x5000, beta=0x6000, gate=0x7000, S=0x8000,
+                conv_state=0x9000, o=0xa000, accept=None)
+    for over, code in [(dict(S=None), -1), (dict(o=None), -1), (dict(N=0), -2), (dict(M=0), -2),
+                       (dict(M=17), -2), (dict(in_dtype=3), -3), (dict(S=0x8008), -4),
+                       (dict(accept=0xb002), -4), (dict(dk=24, dv=24), -5),
+                       (dict(decay_form=4), -5), (dict(decay_form=1), -1)]:
+        a = kda.DecodeMultiArgs(**{**base, **over})
+        assert L.kda_decode_multi(ctypes.byref(a), None) == code, over
+    assert L.kda_decode_multi(None, None) == -1
 
 
 def test_prep_validation_codes(kda):

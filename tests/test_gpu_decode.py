@@ -5,7 +5,7 @@ import numpy as np
 import pytest
 
 import kda_synth as syn
-from gpu_util import assert_rms_close, need_gpu, to_dev, tol_for
+from gpu_util import assert_rms_close, gather_heads, need_gpu, to_dev, tol_for
 from kda_synth import Workload
 
 pytestmark = pytest.mark.gpu
@@ -94,3 +94,102 @@ def test_decode_equals_prefill_gpu(oracle_mod):
     assert_rms_close(o_d.cpu().numpy(), o_p.cpu().numpy(), 1e-2, "decode vs prefill o")
     assert_rms_close(S.cpu().numpy(), S_p.cpu().numpy(), 1e-2, "decode vs prefill S")
     assert torch.equal(conv, c_p)
+
+
+# -- M tokens per call (kda_decode_multi) ---------------------------------------------------
+
+def _multi_case(N, M, H, d, dtype, seed, k3=False):
+    """Inputs of M tokens for N sequences ([N, M, H, .], a prefill of T = M tokens),
+    with an initial state and raw conv history."""
+    w = Workload("dm", N, M, H, d, d, 1, dtype, s0_sigma=0.05, conv_hist="normal", seed=seed)
+    inp = syn.prefill_inputs_np(w)
+    if k3:
+        inp = syn.with_k3_logits(inp, w)
+    return w, inp
+
+
+def _decode_multi(kda, dev, S, conv, accept=None):
+    return kda.decode_multi(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"],
+                            dev["gate"], S, conv, accept=accept, A=dev.get("A"))
+
+
+def _expect_carry(oracle_mod, w, inp, n, a):
+    """State and raw history of sequence n after its first a tokens (the oracle)."""
+    one = {x: inp[x][n:n + 1, :a] for x in ("q", "k", "v", "g", "beta", "gate")}
+    one["conv_w"] = inp["conv_w"]
+    one["S0"] = inp["S0"][n:n + 1]
+    one["conv_in"] = inp["conv_in"][n:n + 1]
+    one["A"] = inp.get("A")
+    S, hist = oracle_mod.initial_carry(1, w.H, w.dk, w.dv, None, one["S0"], one["conv_in"])
+    if a > 0:
+        oracle_mod.prefill(one, S=S, hist=hist)
+    return S, hist
+
+
+@pytest.mark.parametrize("d,dtype,M", [(16, "f32", 3), (128, "bf16", 1), (128, "bf16", 5),
+                                       (128, "bf16", 16), (64, "bf16", 8), (128, "f32", 4)])
+def test_decode_multi_matches_oracle(oracle_mod, d, dtype, M):
+    """All M tokens committed: o for every token, the state and the raw history after
+    the last one, equal to the oracle's prefill of the M tokens."""
+    torch, kda = need_gpu()
+    w, inp = _multi_case(3, M, 2, d, dtype, seed=71 + d + M)
+    dev = to_dev(inp, dtype)
+    S, conv = dev["S0"].clone(), dev["conv_in"].clone()
+    o = _decode_multi(kda, dev, S, conv)
+    torch.cuda.synchronize()
+    r = oracle_mod.prefill(inp)
+    tol = tol_for(dtype)
+    assert_rms_close(gather_heads(o, r["heads"], w.H), r["o"], tol, f"multi M={M} o")
+    assert_rms_close(S.cpu().numpy().reshape(w.B * w.H, d, d), r["S_T"], tol, f"multi M={M} S")
+    conv_np = syn.torch_to_np(conv)
+    want = syn.bf16_bits_from_f64(r["conv_out"]) if dtype == "bf16" else r["conv_out"].astype(np.float32)
+    for i, p in enumerate(r["heads"]):
+        n, h = divmod(int(p), w.H)
+        assert np.array_equal(conv_np[n][:, oracle_mod._head_channels(w.H, d, d, h)], want[i])
+
+
+@pytest.mark.parametrize("k3", [False, True])
+def test_decode_multi_accept_counts(oracle_mod, k3):
+    """Per-sequence accept counts 0, 1, 2, 4 and M = 6: o still covers all M tokens;
+    S and the raw history are those after each sequence's accepted prefix
+    (unchanged at 0)."""
+    torch, kda = need_gpu()
+    M = 6
+    w, inp = _multi_case(5, M, 2, 128, "bf16", seed=83, k3=k3)
+    dev = to_dev(inp, "bf16")
+    acc = [0, 1, 2, 4, M]
+    S, conv = dev["S0"].clone(), dev["conv_in"].clone()
+    o = _decode_multi(kda, dev, S, conv, accept=torch.tensor(acc, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    r = oracle_mod.prefill(inp)
+    tol = tol_for("bf16")
+    assert_rms_close(gather_heads(o, r["heads"], w.H), r["o"], tol, "accept o")
+    S_np = S.cpu().numpy()
+    conv_np = syn.torch_to_np(conv)
+    for n, a in enumerate(acc):
+        S_ref, h_ref = _expect_carry(oracle_mod, w, inp, n, a)
+        assert_rms_close(S_np[n], S_ref, tol, f"accept {a}: S")
+        for h in range(w.H):
+            ch = oracle_mod._head_channels(w.H, 128, 128, h)
+            assert np.array_equal(conv_np[n][:, ch], syn.bf16_bits_from_f64(h_ref[h])), f"accept {a}: history"
+
+
+def test_decode_multi_equals_single_steps(oracle_mod):
+    """M tokens in one call and M single-token steps give the same outputs and state
+    (the single steps read and write the state M times)."""
+    torch, kda = need_gpu()
+    M = 4
+    w, inp = _multi_case(4, M, 3, 128, "bf16", seed=89)
+    dev = to_dev(inp, "bf16")
+    S1, c1 = dev["S0"].clone(), dev["conv_in"].clone()
+    o1 = _decode_multi(kda, dev, S1, c1)
+    S2, c2 = dev["S0"].clone(), dev["conv_in"].clone()
+    o2 = torch.stack([kda.decode_step(dev["q"][:, t].contiguous(), dev["k"][:, t].contiguous(),
+                                      dev["v"][:, t].contiguous(), dev["conv_w"], dev["g"][:, t].contiguous(),
+                                      dev["beta"][:, t].contiguous(), dev["gate"][:, t].contiguous(), S2, c2)
+                      for t in range(M)], dim=1)
+    torch.cuda.synchronize()
+    rms = o2.float().pow(2).mean().sqrt().item()
+    assert (o1 - o2).abs().max().item() <= 1e-4 * rms
+    assert (S1 - S2).abs().max().item() <= 1e-4 * S2.pow(2).mean().sqrt().item()
+    assert torch.equal(c1, c2)
