@@ -323,6 +323,8 @@ def main():
                                          "f32 state, all tokens committed",
                                "roofline": {"bound": "hbm", "achieved": mgbs, "peak": HBM_PEAK_GBS,
                                             "unit": "GB/s", "frac": mgbs / HBM_PEAK_GBS,
+                                            "traffic": load_traffic("decode_multi_kernel", os.path.join(
+                                                ROOT, "gated_delta_rule_28_amd", "csrc", "kda_decode.hip")),
                                             "algorithmic_bytes_per_launch": mbytes}}
         log(f"[bench] multi-token decode M={M}: {mms * 1e3:.1f} us/call, "
             f"{wd.B * M / (mms * 1e-3) / 1e6:.2f} M tokens/s, {mgbs:.0f} GB/s")
