@@ -210,9 +210,9 @@ struct DecodeMultiParams {
   const float* A;         // [H, dk]: g and beta are K3's logits; null: given directly
 };
 
-constexpr int kMaxTokens = 16;
-
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16>
+// MT: tokens the LDS arrays hold (M <= MT); a smaller MT for short drafts
+// leaves room for more workgroups per compute unit
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, int MT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(DecodeMultiParams p) {
   constexpr int NC = 2 * DK + DV;
   constexpr int CG = DV / 4;
@@ -228,10 +228,10 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(DecodeMult
   const size_t cch = (size_t)H * NC;
   const int acc_n = p.accept != nullptr ? min(max(p.accept[n], 0), M) : M;
 
-  __shared__ float xs[kMaxTokens][NC];     // conv + SiLU, then q^ | k^ | v^
-  __shared__ float alpha[kMaxTokens][DK];  // e^g
-  __shared__ float betas[kMaxTokens];
-  __shared__ float scal[kMaxTokens][3];    // q scale, k scale, k^ . q^
+  __shared__ float xs[MT][NC];             // conv + SiLU, then q^ | k^ | v^
+  __shared__ float alpha[MT][DK];          // e^g
+  __shared__ float betas[MT];
+  __shared__ float scal[MT][3];            // q scale, k scale, k^ . q^
   __shared__ float red[2][RG][DV];
   __shared__ float us[DV];
   __shared__ float ocs[DV];
@@ -389,7 +389,13 @@ int run_multi(const kda_decode_multi_args& a, hipStream_t s) {
   DecodeMultiParams p{a.H, a.M, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o,
                       a.accept, a.decay_form == KDA_DECAY_K3 ? a.A : nullptr};
   const unsigned grid = (unsigned)((size_t)a.N * a.H);
-  hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  if (a.M <= 4)
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 4>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  else if (a.M <= 8)
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 8>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, KDA_MAX_DECODE_TOKENS>), dim3(grid),
+                       dim3(kDecodeThreads), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("multi-token decode launch failed: %s", hipGetErrorString(e));
