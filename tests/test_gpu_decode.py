@@ -193,3 +193,40 @@ def test_decode_multi_equals_single_steps(oracle_mod):
     assert (o1 - o2).abs().max().item() <= 1e-4 * rms
     assert (S1 - S2).abs().max().item() <= 1e-4 * S2.pow(2).mean().sqrt().item()
     assert torch.equal(c1, c2)
+
+
+def test_decode_multi_bf16_output(oracle_mod):
+    """bf16 output is the fp32 output rounded once (same kernel arithmetic)."""
+    torch, kda = need_gpu()
+    w, inp = _multi_case(2, 7, 3, 128, "bf16", seed=97)
+    dev = to_dev(inp, "bf16")
+    S1, c1 = dev["S0"].clone(), dev["conv_in"].clone()
+    o32 = _decode_multi(kda, dev, S1, c1)
+    S2, c2 = dev["S0"].clone(), dev["conv_in"].clone()
+    o16 = kda.decode_multi(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"],
+                           S2, c2, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(o16, o32.to(torch.bfloat16))
+    assert torch.equal(S1, S2) and torch.equal(c1, c2)
+
+
+def test_decode_multi_fp32_k3_accept(oracle_mod):
+    """fp32 inputs (bound 1e-4 x RMS) with K3's logits and accept counts 3, 0, 16."""
+    torch, kda = need_gpu()
+    M = 16
+    w, inp = _multi_case(3, M, 2, 32, "f32", seed=101, k3=True)
+    dev = to_dev(inp, "f32")
+    acc = [3, 0, M]
+    S, conv = dev["S0"].clone(), dev["conv_in"].clone()
+    o = _decode_multi(kda, dev, S, conv, accept=torch.tensor(acc, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    r = oracle_mod.prefill(inp)
+    tol = tol_for("f32")
+    assert_rms_close(gather_heads(o, r["heads"], w.H), r["o"], tol, "fp32 K3 o")
+    S_np, conv_np = S.cpu().numpy(), conv.cpu().numpy()
+    for n, a in enumerate(acc):
+        S_ref, h_ref = _expect_carry(oracle_mod, w, inp, n, a)
+        assert_rms_close(S_np[n], S_ref, tol, f"fp32 K3 accept {a}: S")
+        for h in range(w.H):
+            ch = oracle_mod._head_channels(w.H, 32, 32, h)
+            assert np.array_equal(conv_np[n][:, ch], h_ref[h].astype(np.float32)), f"accept {a}: history"
