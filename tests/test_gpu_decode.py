@@ -127,7 +127,8 @@ def _expect_carry(oracle_mod, w, inp, n, a):
 
 
 @pytest.mark.parametrize("d,dtype,M", [(16, "f32", 3), (128, "bf16", 1), (128, "bf16", 5),
-                                       (128, "bf16", 16), (64, "bf16", 8), (128, "f32", 4)])
+                                       (128, "bf16", 16), (64, "bf16", 8), (128, "f32", 4),
+                                       (128, "f32", 12)])
 def test_decode_multi_matches_oracle(oracle_mod, d, dtype, M):
     """All M tokens committed: o for every token, the state and the raw history after
     the last one, equal to the oracle's prefill of the M tokens."""
