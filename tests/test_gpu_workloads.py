@@ -80,6 +80,32 @@ def test_k3width_prefill_all_heads(oracle_mod):
     assert_rms_close(s_got, r["S_T"], TOL_BF16, "k3width S_T, all heads")
 
 
+@pytest.mark.timeout(600)
+def test_k3width_prefill_k3_logits_all_heads(oracle_mod):
+    """The same workload with g and beta given as K3's logits (z ~ N(-4.7, 1),
+    b ~ N(0, 1), A ~ N(0, 0.1^2) per head and channel), so the kernels compute
+    g = -5 sigmoid(e^A z) and beta = sigmoid(b) over all 17 pipelined slabs:
+    every head over all 65536 tokens against the oracle."""
+    torch, kda = need_gpu()
+    w = syn.WORKLOADS["k3width"]
+    dev = syn.with_k3_logits_torch(syn.prefill_inputs_torch(w, "cuda"), w, "cuda")
+    o, S_T, _ = kda.prefill(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"],
+                            dev["gate"], S0=dev["S0"], chunk=w.chunk, A=dev["A"])
+    torch.cuda.synchronize()
+    host = {x: syn.torch_to_np(dev[x]) for x in ("q", "k", "v", "g", "beta", "gate")}
+    host["conv_w"] = syn.torch_to_np(dev["conv_w"])
+    host["S0"] = dev["S0"].cpu().numpy()
+    host["A"] = dev["A"].cpu().numpy()
+    r = oracle_mod.prefill(host)
+    o_got = o[0].float().cpu().numpy().transpose(1, 0, 2)
+    s_got = S_T[0].cpu().numpy()
+    rms_o = float(np.sqrt(np.mean(r["o"] ** 2)))
+    per_head = np.abs(o_got - r["o"]).max(axis=(1, 2)) / rms_o
+    print(f"  worst head {int(per_head.argmax())}: max|err|/RMS(o) = {per_head.max():.3e}", flush=True)
+    assert_rms_close(o_got, r["o"], TOL_BF16, "k3width K3 logits o, all heads")
+    assert_rms_close(s_got, r["S_T"], TOL_BF16, "k3width K3 logits S_T, all heads")
+
+
 @pytest.mark.timeout(900)
 def test_long1m_prefill_sampled_head(oracle_mod):
     """B1 T1048576 H96 d128 in 16 segments of 65536 with S and the conv history
