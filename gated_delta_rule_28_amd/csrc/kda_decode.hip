@@ -211,14 +211,30 @@ struct DecodeMultiParams {
 };
 
 // MT: tokens the LDS arrays hold (M <= MT); a smaller MT for short drafts
-// leaves room for more workgroups per compute unit
-template <int DK, int DV, bool IN_BF16, bool OUT_BF16, int MT>
-__global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(DecodeMultiParams p) {
+// leaves room for more workgroups per compute unit.
+// LANE_SUM: how the threads share the state in the token loop.
+//   false  thread (cg = tid % CG, rg = tid / CG) holds rows rg + RG i of column
+//          group cg.  A wave's state accesses are 512-byte row pieces; the
+//          read-outs S'^T k^ and S'^T q^ are summed over row groups through
+//          LDS, three barriers per token.
+//   true   thread (rg = tid % RG, cg = tid / RG): the RG threads of a column
+//          group are consecutive lanes of one wave, so the read-outs are lane
+//          sums and the token loop has no barrier; the state accesses become
+//          128-byte row pieces, and the outputs are normalised after the loop.
+//          Fewer instructions per token, worse memory access: the better
+//          choice for long drafts.
+template <int DK, int DV, bool IN_BF16, bool OUT_BF16, int MT, bool LANE_SUM>
+__global__ __launch_bounds__(kDecodeThreads) __attribute__((amdgpu_waves_per_eu(LANE_SUM ? 4 : 1)))
+void decode_multi_kernel(DecodeMultiParams p) {
   constexpr int NC = 2 * DK + DV;
   constexpr int CG = DV / 4;
   constexpr int RG0 = kDecodeThreads / CG;
   constexpr int RG = RG0 < DK ? RG0 : DK;
   constexpr int RPT = DK / RG;
+  // LDS of the row-group reduction and of one token's u and o_core; unused
+  // with LANE_SUM, where o_core replaces v^ in xs
+  constexpr int RED = LANE_SUM ? 1 : RG;
+  constexpr int RDV = LANE_SUM ? 1 : DV;
 
   const int tid = threadIdx.x;
   const int nh = blockIdx.x;
@@ -232,9 +248,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(DecodeMult
   __shared__ float alpha[MT][DK];          // e^g
   __shared__ float betas[MT];
   __shared__ float scal[MT][3];            // q scale, k scale, k^ . q^
-  __shared__ float red[2][RG][DV];
-  __shared__ float us[DV];
-  __shared__ float ocs[DV];
+  __shared__ float red[2][RED][RDV];
+  __shared__ float us[RDV];
+  __shared__ float ocs[RDV];
   __shared__ float rs_s;
 
   // row of token t of this (n, h) in the [N, M, H, .] inputs
@@ -323,63 +339,124 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_multi_kernel(DecodeMult
   __syncthreads();
 
   // 3. the tokens in order, the state in registers
-  const int cg = tid % CG;
-  const int rg = tid / CG;
-  const bool active = rg < RG;
+  const int cg = LANE_SUM ? tid / RG : tid % CG;
+  const int rg = LANE_SUM ? tid % RG : tid / CG;
+  const bool active = LANE_SUM ? cg < CG : rg < RG;
   f4* Sp = reinterpret_cast<f4*>(p.S + (size_t)nh * DK * DV);
   f4 s[RPT];
   if (active) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) s[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + RG * i) * CG + cg);
   }
-  for (int t = 0; t < M; ++t) {
-    // S' = diag(e^g) S;  S'^T k^ and S'^T q^
+  if constexpr (LANE_SUM) {
     if (active) {
-      f4 y = f4{0.f, 0.f, 0.f, 0.f}, z = y;
+      auto step = [&](int t) {
+        // S' = diag(e^g) S;  S'^T k^ and S'^T q^ as sums over the RG lanes
+        f4 y = f4{0.f, 0.f, 0.f, 0.f}, z = y;
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int r = rg + RG * i;
-        s[i] *= alpha[t][r];
-        y += s[i] * xs[t][DK + r];
-        z += s[i] * xs[t][r];
-      }
-      *reinterpret_cast<f4*>(&red[0][rg][4 * cg]) = y;
-      *reinterpret_cast<f4*>(&red[1][rg][4 * cg]) = z;
-    }
-    __syncthreads();
-    // u = beta (v^ - y);  o_core = S'^T q^ + (k^ . q^) u
-    if (tid < DV) {
-      float y = 0.f, z = 0.f;
+        for (int i = 0; i < RPT; ++i) {
+          const int r = rg + RG * i;
+          s[i] *= alpha[t][r];
+          y += s[i] * xs[t][DK + r];
+          z += s[i] * xs[t][r];
+        }
 #pragma unroll
-      for (int r = 0; r < RG; ++r) {
-        y += red[0][r][tid];
-        z += red[1][r][tid];
-      }
-      const float u = betas[t] * (xs[t][2 * DK + tid] - y);
-      us[tid] = u;
-      ocs[tid] = z + scal[t][2] * u;
-    }
-    __syncthreads();
-    // S <- S' + k^ u^T; the state after the accepted prefix goes to memory
-    if (active) {
-      const f4 u = *reinterpret_cast<const f4*>(&us[4 * cg]);
+        for (int e = 0; e < 4; ++e) {
+          y[e] = group_sum<RG>(y[e]);
+          z[e] = group_sum<RG>(z[e]);
+        }
+        // u = beta (v^ - y);  S <- S' + k^ u^T;  o_core = S'^T q^ + (k^ . q^) u
+        const f4 u = betas[t] * (*reinterpret_cast<const f4*>(&xs[t][2 * DK + 4 * cg]) - y);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) s[i] += u * xs[t][DK + rg + RG * i];
-      if (t == acc_n - 1) {
+        for (int i = 0; i < RPT; ++i) s[i] += u * xs[t][DK + rg + RG * i];
+        // o_core over v^ of this column group: only this wave's lanes read it,
+        // and they have (LDS accesses of a wave complete in order)
+        if (rg == 0) *reinterpret_cast<f4*>(&xs[t][2 * DK + 4 * cg]) = z + scal[t][2] * u;
+      };
+      // the accepted prefix, its state to memory, then the rest of the tokens
+      // (their outputs only).  Storing between the two loops keeps the store
+      // addresses out of the registers the loops hold.
+      for (int t = 0; t < acc_n; ++t) step(t);
+      if (acc_n > 0) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(s[i], Sp + (size_t)(rg + RG * i) * CG + cg);
       }
-    }
-    if (tid < 64) {
-      float ss = 0.f;
-      for (int j = tid; j < DV; j += 64) ss += ocs[j] * ocs[j];
-      ss = group_sum<64>(ss);
-      if (tid == 0) rs_s = fast_rsq(ss * (1.0f / DV) + kRmsEps);
+      for (int t = acc_n; t < M; ++t) step(t);
     }
     __syncthreads();
-    if (tid < DV) {
-      const float gt = load1<IN_BF16>(p.gate, tok(t) * DV + tid);
-      store1<OUT_BF16>(p.o, tok(t) * DV + tid, ocs[tid] * rs_s * sigmoidf_(gt));
+    // RMSNorm * sigmoid(gate) of every token, one wave per token
+    const int wv = tid >> 6, ln = tid & 63;
+    for (int t = wv; t < M; t += kDecodeThreads / 64) {
+      float ss = 0.f;
+      const float* oc = &xs[t][2 * DK];
+      for (int j = ln; j < DV; j += 64) ss += oc[j] * oc[j];
+      const float rs = fast_rsq(group_sum<64>(ss) * (1.0f / DV) + kRmsEps);
+      for (int j = ln; j < DV; j += 64) {
+        const float gt = load1<IN_BF16>(p.gate, tok(t) * DV + j);
+        store1<OUT_BF16>(p.o, tok(t) * DV + j, oc[j] * rs * sigmoidf_(gt));
+      }
+    }
+  } else {
+    auto step = [&](int t, bool store) {
+      // S' = diag(e^g) S;  S'^T k^ and S'^T q^
+      if (active) {
+        f4 y = f4{0.f, 0.f, 0.f, 0.f}, z = y;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          const int r = rg + RG * i;
+          s[i] *= alpha[t][r];
+          y += s[i] * xs[t][DK + r];
+          z += s[i] * xs[t][r];
+        }
+        *reinterpret_cast<f4*>(&red[0][rg][4 * cg]) = y;
+        *reinterpret_cast<f4*>(&red[1][rg][4 * cg]) = z;
+      }
+      __syncthreads();
+      // u = beta (v^ - y);  o_core = S'^T q^ + (k^ . q^) u
+      if (tid < DV) {
+        float y = 0.f, z = 0.f;
+#pragma unroll
+        for (int r = 0; r < RG; ++r) {
+          y += red[0][r][tid];
+          z += red[1][r][tid];
+        }
+        const float u = betas[t] * (xs[t][2 * DK + tid] - y);
+        us[tid] = u;
+        ocs[tid] = z + scal[t][2] * u;
+      }
+      __syncthreads();
+      // S <- S' + k^ u^T; after the accepted prefix, the state goes to memory
+      if (active) {
+        const f4 u = *reinterpret_cast<const f4*>(&us[4 * cg]);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) s[i] += u * xs[t][DK + rg + RG * i];
+        if (store) {
+#pragma unroll
+          for (int i = 0; i < RPT; ++i) __builtin_nontemporal_store(s[i], Sp + (size_t)(rg + RG * i) * CG + cg);
+        }
+      }
+      if (tid < 64) {
+        float ss = 0.f;
+        for (int j = tid; j < DV; j += 64) ss += ocs[j] * ocs[j];
+        ss = group_sum<64>(ss);
+        if (tid == 0) rs_s = fast_rsq(ss * (1.0f / DV) + kRmsEps);
+      }
+      __syncthreads();
+      if (tid < DV) {
+        const float gt = load1<IN_BF16>(p.gate, tok(t) * DV + tid);
+        store1<OUT_BF16>(p.o, tok(t) * DV + tid, ocs[tid] * rs_s * sigmoidf_(gt));
+      }
+    };
+    if constexpr (MT <= 2) {
+      // one or two tokens: one loop, the store under a condition (faster here,
+      // measured, though it holds the store addresses through the loop)
+      for (int t = 0; t < M; ++t) step(t, t == acc_n - 1);
+    } else {
+      // as above, with the last accepted token's step on its own: its state
+      // stores are issued before its output is normalised
+      for (int t = 0; t < acc_n - 1; ++t) step(t, false);
+      if (acc_n > 0) step(acc_n - 1, true);
+      for (int t = acc_n; t < M; ++t) step(t, false);
     }
   }
 }
@@ -389,12 +466,14 @@ int run_multi(const kda_decode_multi_args& a, hipStream_t s) {
   DecodeMultiParams p{a.H, a.M, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S, a.conv_state, a.o,
                       a.accept, a.decay_form == KDA_DECAY_K3 ? a.A : nullptr};
   const unsigned grid = (unsigned)((size_t)a.N * a.H);
-  if (a.M <= 4)
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 4>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  if (a.M <= 2)
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 2, false>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+  else if (a.M <= 4)
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 4, false>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
   else if (a.M <= 8)
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 8>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, 8, false>), dim3(grid), dim3(kDecodeThreads), 0, s, p);
   else
-    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, KDA_MAX_DECODE_TOKENS>), dim3(grid),
+    hipLaunchKernelGGL((decode_multi_kernel<DK, DV, IB, OB, KDA_MAX_DECODE_TOKENS, true>), dim3(grid),
                        dim3(kDecodeThreads), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {

@@ -34,7 +34,7 @@ KERNELS = {
     "inter_chunk_kernel": ("inter_chunk_kernel<false>", "kda_prefill_split.hip"),
     "prefill_kernel": ("prefill_kernel<64, 128, 128, true, false, false>", "kda_prefill.hip"),
     "decode_kernel": ("decode_kernel<128, 128, true, false>", "kda_decode.hip"),
-    "decode_multi_kernel": ("decode_multi_kernel<128, 128, true, false, 4>", "kda_decode.hip"),
+    "decode_multi_kernel": ("decode_multi_kernel<128, 128, true, false, 4, false>", "kda_decode.hip"),
 }
 CALIB_BYTES = 1 << 30   # bytes read, and bytes written, by the calibration kernel
 

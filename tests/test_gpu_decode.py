@@ -126,12 +126,15 @@ def _expect_carry(oracle_mod, w, inp, n, a):
     return S, hist
 
 
-@pytest.mark.parametrize("d,dtype,M", [(16, "f32", 3), (128, "bf16", 1), (128, "bf16", 5),
+@pytest.mark.parametrize("d,dtype,M", [(16, "f32", 3), (128, "bf16", 1), (128, "bf16", 2), (128, "bf16", 5),
                                        (128, "bf16", 16), (64, "bf16", 8), (128, "f32", 4),
-                                       (128, "f32", 12)])
+                                       (128, "f32", 12), (16, "f32", 10), (32, "bf16", 9),
+                                       (64, "bf16", 13)])
 def test_decode_multi_matches_oracle(oracle_mod, d, dtype, M):
     """All M tokens committed: o for every token, the state and the raw history after
-    the last one, equal to the oracle's prefill of the M tokens."""
+    the last one, equal to the oracle's prefill of the M tokens.  M > 8 runs the
+    lane-sum layout of the token loop, smaller M the row-group layout (one loop
+    up to 2 tokens, split at the accept point from 3)."""
     torch, kda = need_gpu()
     w, inp = _multi_case(3, M, 2, d, dtype, seed=71 + d + M)
     dev = to_dev(inp, dtype)
@@ -149,16 +152,15 @@ def test_decode_multi_matches_oracle(oracle_mod, d, dtype, M):
         assert np.array_equal(conv_np[n][:, oracle_mod._head_channels(w.H, d, d, h)], want[i])
 
 
-@pytest.mark.parametrize("k3", [False, True])
-def test_decode_multi_accept_counts(oracle_mod, k3):
-    """Per-sequence accept counts 0, 1, 2, 4 and M = 6: o still covers all M tokens;
-    S and the raw history are those after each sequence's accepted prefix
-    (unchanged at 0)."""
+@pytest.mark.parametrize("k3,M", [(False, 2), (False, 3), (False, 6), (True, 6), (False, 12), (True, 15)])
+def test_decode_multi_accept_counts(oracle_mod, k3, M):
+    """Per-sequence accept counts 0, 1, 2, 4, M - 1 and M, and one above M (taken
+    as M): o still covers all M tokens; S and the raw history are those after each
+    sequence's accepted prefix (unchanged at 0)."""
     torch, kda = need_gpu()
-    M = 6
-    w, inp = _multi_case(5, M, 2, 128, "bf16", seed=83, k3=k3)
+    w, inp = _multi_case(7, M, 2, 128, "bf16", seed=83 + M, k3=k3)
     dev = to_dev(inp, "bf16")
-    acc = [0, 1, 2, 4, M]
+    acc = [0, 1, 2, 4, M - 1, M, M + 3]
     S, conv = dev["S0"].clone(), dev["conv_in"].clone()
     o = _decode_multi(kda, dev, S, conv, accept=torch.tensor(acc, dtype=torch.int32, device="cuda"))
     torch.cuda.synchronize()
@@ -168,19 +170,19 @@ def test_decode_multi_accept_counts(oracle_mod, k3):
     S_np = S.cpu().numpy()
     conv_np = syn.torch_to_np(conv)
     for n, a in enumerate(acc):
-        S_ref, h_ref = _expect_carry(oracle_mod, w, inp, n, a)
+        S_ref, h_ref = _expect_carry(oracle_mod, w, inp, n, min(a, M))
         assert_rms_close(S_np[n], S_ref, tol, f"accept {a}: S")
         for h in range(w.H):
             ch = oracle_mod._head_channels(w.H, 128, 128, h)
             assert np.array_equal(conv_np[n][:, ch], syn.bf16_bits_from_f64(h_ref[h])), f"accept {a}: history"
 
 
-def test_decode_multi_equals_single_steps(oracle_mod):
+@pytest.mark.parametrize("M", [4, 11])
+def test_decode_multi_equals_single_steps(oracle_mod, M):
     """M tokens in one call and M single-token steps give the same outputs and state
     (the single steps read and write the state M times)."""
     torch, kda = need_gpu()
-    M = 4
-    w, inp = _multi_case(4, M, 3, 128, "bf16", seed=89)
+    w, inp = _multi_case(4, M, 3, 128, "bf16", seed=85 + M)
     dev = to_dev(inp, "bf16")
     S1, c1 = dev["S0"].clone(), dev["conv_in"].clone()
     o1 = _decode_multi(kda, dev, S1, c1)
@@ -196,10 +198,11 @@ def test_decode_multi_equals_single_steps(oracle_mod):
     assert torch.equal(c1, c2)
 
 
-def test_decode_multi_bf16_output(oracle_mod):
+@pytest.mark.parametrize("M", [7, 14])
+def test_decode_multi_bf16_output(oracle_mod, M):
     """bf16 output is the fp32 output rounded once (same kernel arithmetic)."""
     torch, kda = need_gpu()
-    w, inp = _multi_case(2, 7, 3, 128, "bf16", seed=97)
+    w, inp = _multi_case(2, M, 3, 128, "bf16", seed=90 + M)
     dev = to_dev(inp, "bf16")
     S1, c1 = dev["S0"].clone(), dev["conv_in"].clone()
     o32 = _decode_multi(kda, dev, S1, c1)
