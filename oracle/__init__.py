@@ -16,6 +16,12 @@ rms_norm_eps from the "Kimi K3" model card config):
   matrix product S_t = (I - beta k k^T) Diag(alpha_t) S_{t-1} + beta k v^T with
   an explicit dk x dk transition.  Slow; for small shapes.
 
+Context parallelism ("Kimi K3, previewed", long-context row): a segment maps its
+entering state S to M S + N.  `segment_transition` builds M as the ordered
+product of the per-token maps, `segment_fragments` returns (M, N),
+`compose_segments` the entering states, and `prefill_context_parallel` the
+whole prefill computed segment by segment.
+
 Inputs are numpy arrays: float32, or uint16 holding bf16 bits.  All
 arithmetic is fp64 on the exact input values.
 
@@ -272,3 +278,112 @@ def prefill_matrix_form(inp: dict, heads=None, S=None, hist=None) -> dict:
         full = np.concatenate([hist[i], x_raw], axis=0)
         hist_out[i] = full[-3:]
     return {"o": o, "S_T": S_T, "conv_out": hist_out, "heads": bh}
+
+
+# ----------------------------------------------------------------------------
+# Context parallelism ("Kimi K3, previewed", long-context row: ranks exchange
+# only fixed-size state fragments).  Plainest reading: the state update is
+# affine in the state, so a segment acts on the state entering it as
+# S_out = M S_in + N; each rank forms (M, N) for its segment, the fragments are
+# gathered, and a prefix composition gives every segment its entering state.
+# ----------------------------------------------------------------------------
+
+def segment_transition(inp: dict, heads=None, hist=None) -> np.ndarray:
+    """M [n, dk, dk] per (b, h) pair: the product, over the tokens in order, of the
+    per-token maps (I - beta k^ k^T) Diag(e^g) -- the linear part of the update,
+    so that S_T = M S_0 + N for every initial state S_0.
+
+    k^ (conv + SiLU + L2 norm from the raw history `hist`, default from
+    inp["conv_in"] or zeros) comes from the C oracle's prep output; g and beta
+    as the recurrence takes them.  Each token is applied as the rank-1 form
+    D M - beta k^ (k^T D M) of the same product."""
+    q = inp["q"]
+    B, T, H, dk = q.shape
+    dv = inp["v"].shape[3]
+    bh = _pairs(B, H, heads)
+    S0, h0 = initial_carry(B, H, dk, dv, bh, None, inp.get("conv_in"))
+    r = prefill(inp, heads=bh, S=S0, hist=h0 if hist is None else hist.copy(), want_o=False,
+                want_prep=True)
+    g, beta = decay_and_beta(inp)
+    M = np.zeros((len(bh), dk, dk))
+    for i, p in enumerate(bh):
+        b, h = divmod(int(p), H)
+        Mi = np.eye(dk)
+        kn = r["prep"][i][:, dk:2 * dk]
+        for t in range(T):
+            DM = np.exp(g[b, t, h])[:, None] * Mi
+            Mi = DM - beta[b, t, h] * np.outer(kn[t], kn[t] @ DM)
+        M[i] = Mi
+    return M
+
+
+def segment_fragments(inp: dict, heads=None, hist=None) -> tuple:
+    """(M, N) of each listed pair for one segment: N is the state after the
+    segment from S = 0 (the C recurrence), M its `segment_transition`."""
+    q = inp["q"]
+    B, T, H, dk = q.shape
+    dv = inp["v"].shape[3]
+    bh = _pairs(B, H, heads)
+    S, h0 = initial_carry(B, H, dk, dv, bh, None, inp.get("conv_in"))
+    h0 = h0 if hist is None else hist.copy()
+    M = segment_transition(inp, heads=bh, hist=h0)
+    prefill(inp, heads=bh, S=S, hist=h0.copy(), want_o=False)
+    return M, S
+
+
+def compose_segments(M: np.ndarray, N: np.ndarray, S0: np.ndarray) -> tuple:
+    """Prefix composition: M, N [R, n, dk, .] per segment, S0 [n, dk, dv] entering
+    segment 0.  Returns (S_start [R, n, dk, dv], S_end [n, dk, dv]) with
+    S_start[0] = S0 and S_start[r + 1] = M[r] S_start[r] + N[r] (fp64)."""
+    R = M.shape[0]
+    S_start = np.zeros((R,) + S0.shape)
+    S = np.array(S0, dtype=np.float64)
+    for r in range(R):
+        S_start[r] = S
+        S = np.einsum("nij,njk->nik", M[r], S) + N[r]
+    return S_start, S
+
+
+def _segment_inputs(inp: dict, t0: int, t1: int) -> tuple:
+    """Inputs of tokens [t0, t1) and the raw conv history [B, 3, Cch] entering them
+    (the caller's conv_in before token 0, zeros before that)."""
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[3]
+    seg = {x: inp[x][:, t0:t1] for x in ("q", "k", "v", "g", "beta", "gate")}
+    seg["conv_w"] = inp["conv_w"]
+    seg["A"] = inp.get("A")
+    raw = np.concatenate([_f64(inp["q"]).reshape(B, T, H * dk), _f64(inp["k"]).reshape(B, T, H * dk),
+                          _f64(inp["v"]).reshape(B, T, H * dv)], axis=2)
+    ci = np.zeros((B, 3, raw.shape[2]))
+    if inp.get("conv_in") is not None:
+        ci = _f64(inp["conv_in"])
+    full = np.concatenate([ci, raw], axis=1)  # row t + 3 holds token t
+    return seg, full[:, t0:t0 + 3]
+
+
+def prefill_context_parallel(inp: dict, segments: int) -> dict:
+    """`prefill` of the whole sequence computed the context-parallel way: the T
+    tokens cut into `segments` equal segments, each segment's (M, N) formed from
+    S = 0 with its own 3-token raw history, the entering states by
+    `compose_segments` from S0, then every segment run from its entering state.
+    Returns o [B*H, T, dv] and S_T [B*H, dk, dv] like `prefill`."""
+    B, T, H, dk = inp["q"].shape
+    dv = inp["v"].shape[3]
+    if T % segments:
+        raise ValueError("T must be a multiple of the segment count")
+    L = T // segments
+    n = B * H
+    Ms, Ns, hists = np.zeros((segments, n, dk, dk)), np.zeros((segments, n, dk, dv)), []
+    for r in range(segments):
+        seg, ci = _segment_inputs(inp, r * L, (r + 1) * L)
+        _, h = initial_carry(B, H, dk, dv, None, None, ci)
+        hists.append(h)
+        Ms[r], Ns[r] = segment_fragments(seg, hist=h)
+    S0, _ = initial_carry(B, H, dk, dv, None, inp.get("S0"), None)
+    S_start, S_end = compose_segments(Ms, Ns, S0)
+    o = np.zeros((n, T, dv))
+    for r in range(segments):
+        seg, _ = _segment_inputs(inp, r * L, (r + 1) * L)
+        res = prefill(seg, S=S_start[r].copy(), hist=hists[r].copy())
+        o[:, r * L:(r + 1) * L] = res["o"]
+    return {"o": o, "S_T": S_end, "S_start": S_start, "M": Ms, "N": Ns}
