@@ -142,6 +142,67 @@ def cpu_baseline(w, dev_inp, seconds_target=15.0):
                       f"({head_tokens} head-tokens, {el:.1f} s); tokens/s = head-tokens/s / {H}"}
 
 
+def time_context_parallel(torch, kda, w, inp, R, A, steps):
+    """kda_prefill_cp of the whole workload (all T tokens of each sequence, whatever
+    segmentation the workload's own timing uses) in R segments on this GPU (three prefill
+    passes over all segments and the composition), and one rank's share of it at
+    the rank's shape: its segment from S = 0 and from S = I, the composition of
+    the R gathered fragments, and its segment again from the entering state (the
+    exchange itself needs R GPUs and is not timed)."""
+    if w.T % R or w.T // R < 3:
+        raise SystemExit(f"--cp-segments {R} does not split workload {w.name}")
+    dev = inp["q"].device
+    L = w.T // R
+    o = torch.empty((w.B, w.T, w.H, w.dv), dtype=torch.float32, device=dev)
+    S = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    conv = torch.empty((w.B, 3, w.cch), dtype=torch.bfloat16, device=dev)
+    nbytes = kda.cp_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, R, w.chunk)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    args = [inp[x] for x in ("q", "k", "v", "conv_w", "g", "beta", "gate")]
+
+    def call():
+        kda.prefill_cp(*args, R, S0=inp["S0"], chunk=w.chunk, o=o, S_T=S, conv_out=conv, workspace=ws, A=A)
+
+    call()
+    torch.cuda.synchronize()
+    per = timed_launches(torch, call, steps)
+    ms = sum(per) / len(per)
+    del ws, o
+    log(f"[bench] context-parallel prefill, {R} segments on one GPU: {ms:.3f} ms/call")
+
+    # one rank's share (segment 0's inputs; every segment has the same shape)
+    seg = [t if t is inp["conv_w"] else t[:, :L].contiguous() for t in args]
+    BH = w.B * w.H
+    eye = torch.eye(w.dk, device=dev).expand(w.B, w.H, w.dk, w.dv).contiguous()
+    N1, P1 = torch.empty_like(eye), torch.empty_like(eye)
+    NR = torch.randn((w.B * R, w.H, w.dk, w.dv), device=dev) * 0.01
+    PR = NR + torch.randn_like(NR) * 0.01
+    Sst = torch.empty_like(NR)
+    o_r = torch.empty((w.B, L, w.H, w.dv), dtype=torch.float32, device=dev)
+    ws_r = torch.empty(max(kda.workspace_bytes(w.B, L, w.H, w.dk, w.dv, w.chunk), 1), dtype=torch.uint8,
+                       device=dev)
+
+    def rank():
+        kda.prefill(*seg, S0=None, chunk=w.chunk, o=o_r, S_T=N1, want_conv=False, workspace=ws_r, A=A)
+        kda.prefill(*seg, S0=eye, chunk=w.chunk, o=o_r, S_T=P1, want_conv=False, workspace=ws_r, A=A)
+        kda.cp_compose(NR, PR, S0=inp["S0"], B=w.B, S_start=Sst, want_state=False)
+        kda.prefill(*seg, S0=Sst[:w.B], chunk=w.chunk, o=o_r, S_T=N1, want_conv=False, workspace=ws_r, A=A)
+
+    rank()
+    torch.cuda.synchronize()
+    rper = timed_launches(torch, rank, steps)
+    rms = sum(rper) / len(rper)
+    log(f"[bench] one rank's share ({L} tokens, {R} fragments composed): {rms:.3f} ms")
+    return {"segments": R, "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "calls_timed": steps,
+            "config": f"kda_prefill_cp of the {w.name} workload in {R} segments of {L} tokens on one GPU: "
+                      "three prefill passes over all segments and the composition",
+            "rank_share_ms": rms,
+            "rank_share": f"one segment of B{w.B} T{L} H{w.H} from S = 0 and from S = I, kda_cp_compose of "
+                          f"{R} fragments, the segment again; the all-gather of the fragments "
+                          f"({2 * BH * w.dk * w.dv * 4} bytes per rank) needs {R} GPUs and is not timed",
+            "workspace_bytes": nbytes}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -153,6 +214,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--decay-form", default="direct", choices=["direct", "k3"])
     ap.add_argument("--verify-tokens", type=int, default=4)
+    ap.add_argument("--cp-segments", type=int, default=0,
+                    help="also time the context-parallel prefill (kda_prefill_cp) with this many segments")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures the single-GPU path only; run it with --gpus 1 "
@@ -248,6 +311,10 @@ def main():
                  "frac_of_bf16_f16_peak": flops / (launch_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
     }
     del o
+
+    if args.cp_segments > 0:
+        out["context_parallel"] = time_context_parallel(torch, kda, w, inp, args.cp_segments, A,
+                                                        min(args.steps, 5))
 
     if args.decode_steps > 0:
         wd = syn.WORKLOADS["decode"]

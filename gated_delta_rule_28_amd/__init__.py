@@ -10,6 +10,8 @@ works, but every call raises (there is no fallback implementation).
     o = decode_step(q, k, v, conv_w, g, beta, gate, S, conv_state)   # S, conv_state in place
     o = decode_multi(q, k, v, conv_w, g, beta, gate, S, conv_state, accept=None)  # [N, M, H, .]
     qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
+    o, S_T, conv_out = prefill_cp(q, k, v, conv_w, g, beta, gate, segments=R, ...)  # context-parallel
+    S_start, S_T = cp_compose(N, P, S0=None, B=1)   # the composition step alone
 
 Every call also takes A=None: given an fp32 [H, dk] tensor, g and beta are K3's
 logits (g = -5 sigmoid(e^A z), beta = sigmoid(b), KDA_DECAY_K3) instead of the
@@ -22,7 +24,8 @@ import os
 
 __all__ = ["prefill", "decode_step", "decode_multi", "prep", "workspace_bytes", "library_path", "lib", "KDAError",
            "KDA_F32", "KDA_BF16", "KDA_DECAY_DIRECT", "KDA_DECAY_K3", "PrefillArgs", "DecodeArgs",
-           "PrepArgs", "DecodeMultiArgs", "MAX_DECODE_TOKENS"]
+           "PrepArgs", "DecodeMultiArgs", "MAX_DECODE_TOKENS", "prefill_cp", "cp_compose",
+           "cp_workspace_bytes", "CpComposeArgs", "PrefillCpArgs"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -31,7 +34,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
-ABI_VERSION = 2
+ABI_VERSION = 3
 MAX_DECODE_TOKENS = 16
 
 
@@ -78,6 +81,16 @@ class PrepArgs(ctypes.Structure):
                 ("G_out", _P), ("decay_form", ctypes.c_int), ("A", _P)]
 
 
+class CpComposeArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("R", ctypes.c_int), ("H", ctypes.c_int), ("d", ctypes.c_int),
+                ("N", _P), ("P", _P), ("S0", _P), ("S_start", _P), ("S_T", _P)]
+
+
+class PrefillCpArgs(ctypes.Structure):
+    _fields_ = [("prefill", PrefillArgs), ("segments", ctypes.c_int), ("workspace", _P),
+                ("workspace_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 
@@ -100,6 +113,12 @@ def lib():
         L.kda_decode_multi.restype = ctypes.c_int
         L.kda_prep.argtypes = [ctypes.POINTER(PrepArgs), _P]
         L.kda_prep.restype = ctypes.c_int
+        L.kda_cp_compose.argtypes = [ctypes.POINTER(CpComposeArgs), _P]
+        L.kda_cp_compose.restype = ctypes.c_int
+        L.kda_prefill_cp.argtypes = [ctypes.POINTER(PrefillCpArgs), _P]
+        L.kda_prefill_cp.restype = ctypes.c_int
+        L.kda_prefill_cp_workspace_bytes.argtypes = [ctypes.POINTER(PrefillCpArgs)]
+        L.kda_prefill_cp_workspace_bytes.restype = ctypes.c_size_t
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.restype = ctypes.c_char_p
@@ -239,3 +258,58 @@ def prep(q, k, v, conv_w, g, conv_in=None, chunk=64, A=None):
                  _ptr(conv_in), _ptr(qo), _ptr(ko), _ptr(vo), _ptr(Go), *_decay(A))
     _check("kda_prep", lib().kda_prep(ctypes.byref(a), _stream(q.device)))
     return qo, ko, vo, Go
+
+
+def prefill_cp(q, k, v, conv_w, g, beta, gate, segments, S0=None, conv_in=None, chunk=64, out_dtype=None,
+               o=None, S_T=None, conv_out=None, want_state=True, want_conv=True, workspace=None, A=None):
+    """Context-parallel prefill on one device (kda_prefill_cp): the results of
+    `prefill`, computed from `segments` equal segments per sequence, each formed
+    from S = 0 and S = I, composed, and run again from its entering state.
+    workspace: None allocates kda_prefill_cp_workspace_bytes, or a uint8 tensor."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    out_dtype = torch.float32 if out_dtype is None else out_dtype
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_out is None and want_conv:
+        conv_out = torch.empty((B, 3, H * (2 * dk + dv)), dtype=q.dtype, device=dev)
+    pa = PrefillArgs(B, T, H, dk, dv, chunk, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
+                     _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in),
+                     _ptr(o), _ptr(S_T), _ptr(conv_out), None, 0, *_decay(A))
+    a = PrefillCpArgs(pa, int(segments), None, 0)
+    if workspace is None:
+        nbytes = lib().kda_prefill_cp_workspace_bytes(ctypes.byref(a))
+        if nbytes == 0 and T > 0:
+            raise ValueError(f"no context-parallel split of T={T} into {segments} segments for these sizes")
+        workspace = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("kda_prefill_cp", lib().kda_prefill_cp(ctypes.byref(a), _stream(dev)))
+    return o, S_T, conv_out
+
+
+def cp_workspace_bytes(B, T, H, dk, dv, segments, chunk=64, in_dtype=KDA_BF16, out_dtype=KDA_F32):
+    """kda_prefill_cp_workspace_bytes for these sizes (0: invalid)."""
+    a = PrefillCpArgs(PrefillArgs(B, T, H, dk, dv, chunk, in_dtype, out_dtype), int(segments), None, 0)
+    return int(lib().kda_prefill_cp_workspace_bytes(ctypes.byref(a)))
+
+
+def cp_compose(N, P, S0=None, B=1, S_start=None, S_T=None, want_state=True):
+    """Prefix composition of segment fragments (kda_cp_compose).  N, P: fp32
+    [B*R, H, d, d] final states of each segment from S = 0 and from S = I;
+    S0 [B, H, d, d] or None.  Returns (S_start [B*R, H, d, d], S_T [B, H, d, d])."""
+    torch = _torch()
+    BR, H, d, _ = N.shape
+    if BR % B:
+        raise ValueError("N's first dimension must be B * R")
+    if S_start is None:
+        S_start = torch.empty_like(N)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, d, d), dtype=torch.float32, device=N.device)
+    a = CpComposeArgs(B, BR // B, H, d, _ptr(N), _ptr(P), _ptr(S0), _ptr(S_start), _ptr(S_T))
+    _check("kda_cp_compose", lib().kda_cp_compose(ctypes.byref(a), _stream(N.device)))
+    return S_start, S_T

@@ -45,6 +45,38 @@ int check_common(int B, int T, int H, int dk, int dv, int in_dtype, int out_dtyp
   return KDA_OK;
 }
 
+// Workspace of kda_prefill_cp, in order: the segments' raw conv histories,
+// then the final states from S = 0 (N), from S = I (P), the entering states
+// (first the identity), and the segment prefills' own workspace.
+size_t round256(size_t x) { return (x + 255) / 256 * 256; }
+
+struct CpLayout {
+  size_t n, p, s, pf, total;
+};
+
+kda_prefill_args cp_segment_args(const kda_prefill_cp_args& c) {
+  kda_prefill_args s = c.prefill;
+  s.B = c.prefill.B * c.segments;
+  s.T = c.prefill.T / c.segments;
+  s.workspace = nullptr;
+  s.workspace_bytes = 0;
+  return s;
+}
+
+CpLayout cp_layout(const kda_prefill_cp_args& c) {
+  const kda_prefill_args& a = c.prefill;
+  const size_t bs = (size_t)a.B * c.segments;
+  const size_t cch = (size_t)a.H * (2 * a.dk + a.dv);
+  const size_t states = round256(bs * a.H * a.dk * a.dv * sizeof(float));
+  CpLayout l{};
+  l.n = round256(bs * 3 * cch * esize(a.in_dtype));
+  l.p = l.n + states;
+  l.s = l.p + states;
+  l.pf = l.s + states;
+  l.total = l.pf + prefill_split_workspace_bytes(cp_segment_args(c));
+  return l;
+}
+
 int check_decay(int form, const float* A) {
   if (form != KDA_DECAY_DIRECT && form != KDA_DECAY_K3)
     return fail(KDA_E_UNSUPPORTED, "decay_form=%d not KDA_DECAY_DIRECT/KDA_DECAY_K3", form);
@@ -123,6 +155,110 @@ int kda_prefill(const kda_prefill_args* a, void* stream) {
                 kda_prefill_workspace_min_bytes(a));
   if (a->T == 0 && a->S_T == nullptr && a->conv_out == nullptr) return KDA_OK;
   return kda::launch_prefill(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int kda_cp_compose(const kda_cp_compose_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(a);
+  if (a->B < 1 || a->R < 1 || a->H < 1) return fail(KDA_E_SHAPE, "B=%d R=%d H=%d out of range", a->B, a->R, a->H);
+  if ((long long)a->B * a->R * a->H > 0x7fffffffLL) return fail(KDA_E_SHAPE, "B*R*H too large");
+  if (!kda::dim_ok(a->d)) return fail(KDA_E_UNSUPPORTED, "d=%d not in {16,32,64,128}", a->d);
+  REQUIRE_PTR(a->N); REQUIRE_PTR(a->P); REQUIRE_PTR(a->S_start);
+  REQUIRE_A16(a->N); REQUIRE_A16(a->P); REQUIRE_A16(a->S0); REQUIRE_A16(a->S_start); REQUIRE_A16(a->S_T);
+  return kda::launch_cp_compose(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
+size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* c) {
+  if (c == nullptr) return 0;
+  const kda_prefill_args& a = c->prefill;
+  if (kda::check_common(a.B, a.T, a.H, a.dk, a.dv, a.in_dtype, a.out_dtype) != KDA_OK) return 0;
+  if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64) return 0;
+  if (c->segments < 1 || a.T % c->segments != 0 || a.T / c->segments < 3) return 0;
+  if ((long long)a.B * c->segments * a.H > 0x7fffffffLL) return 0;
+  return kda::cp_layout(*c).total;
+}
+
+int kda_prefill_cp(const kda_prefill_cp_args* c, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(c);
+  const kda_prefill_args& a = c->prefill;
+  int rc = kda::check_common(a.B, a.T, a.H, a.dk, a.dv, a.in_dtype, a.out_dtype);
+  if (rc != KDA_OK) return rc;
+  if (a.chunk != 16 && a.chunk != 32 && a.chunk != 64)
+    return fail(KDA_E_UNSUPPORTED, "chunk=%d not in {16,32,64}", a.chunk);
+  rc = kda::check_decay(a.decay_form, a.A);
+  if (rc != KDA_OK) return rc;
+  const int R = c->segments;
+  if (R < 1) return fail(KDA_E_SHAPE, "segments=%d < 1", R);
+  if (a.T == 0) {  // nothing to split: the carry copies of kda_prefill
+    kda_prefill_args z = a;
+    z.workspace = nullptr;
+    z.workspace_bytes = 0;
+    return kda_prefill(&z, stream);
+  }
+  if (a.T % R != 0 || a.T / R < 3)
+    return fail(KDA_E_SHAPE, "T=%d is not a multiple of segments=%d with at least 3 tokens each", a.T, R);
+  if ((long long)a.B * R * a.H > 0x7fffffffLL) return fail(KDA_E_SHAPE, "B*segments*H too large");
+  REQUIRE_PTR(a.q); REQUIRE_PTR(a.k); REQUIRE_PTR(a.v); REQUIRE_PTR(a.conv_w);
+  REQUIRE_PTR(a.g); REQUIRE_PTR(a.beta); REQUIRE_PTR(a.gate); REQUIRE_PTR(a.o);
+  REQUIRE_A16(a.q); REQUIRE_A16(a.k); REQUIRE_A16(a.v); REQUIRE_A16(a.conv_w);
+  REQUIRE_A16(a.g); REQUIRE_A16(a.gate); REQUIRE_A16(a.o); REQUIRE_A16(a.S0);
+  REQUIRE_A16(a.S_T); REQUIRE_A16(a.conv_in); REQUIRE_A16(a.conv_out);
+  if (!kda::aligned_n(a.beta, kda::esize(a.in_dtype)))
+    return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
+  if (c->workspace == nullptr) return fail(KDA_E_NULL, "workspace is NULL (kda_prefill_cp_workspace_bytes)");
+  REQUIRE_A16(c->workspace);
+  const kda::CpLayout l = kda::cp_layout(*c);
+  if (c->workspace_bytes < l.total)
+    return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", c->workspace_bytes, l.total);
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  unsigned char* ws = static_cast<unsigned char*>(c->workspace);
+  float* Nb = reinterpret_cast<float*>(ws + l.n);
+  float* Pb = reinterpret_cast<float*>(ws + l.p);
+  float* Sb = reinterpret_cast<float*>(ws + l.s);
+  const int L = a.T / R;
+  const size_t bs = (size_t)a.B * R;
+  // 1. every segment's raw conv history
+  rc = kda::launch_cp_history(a, R, 0, L, ws, s);
+  if (rc != KDA_OK) return rc;
+  // 2. the fragments: all segments from S = 0 (N) and from S = I (P)
+  kda_prefill_args sa = kda::cp_segment_args(*c);
+  sa.conv_in = ws;
+  sa.conv_out = nullptr;
+  if (l.total > l.pf) {
+    sa.workspace = ws + l.pf;
+    sa.workspace_bytes = l.total - l.pf;
+  }
+  sa.S0 = nullptr;
+  sa.S_T = Nb;
+  rc = kda_prefill(&sa, stream);
+  if (rc != KDA_OK) return rc;
+  rc = kda::launch_cp_identity(Sb, bs * a.H, a.dk, s);
+  if (rc != KDA_OK) return rc;
+  sa.S0 = Sb;
+  sa.S_T = Pb;
+  rc = kda_prefill(&sa, stream);
+  if (rc != KDA_OK) return rc;
+  // 3. the entering state of every segment
+  const kda_cp_compose_args ca{a.B, R, a.H, a.dk, Nb, Pb, a.S0, Sb, nullptr};
+  rc = kda::launch_cp_compose(ca, s);
+  if (rc != KDA_OK) return rc;
+  // 4. every segment from its entering state; the last segment's final state
+  sa.S0 = Sb;
+  sa.S_T = a.S_T != nullptr ? Pb : nullptr;
+  rc = kda_prefill(&sa, stream);
+  if (rc != KDA_OK) return rc;
+  if (a.S_T != nullptr) {
+    const size_t per = (size_t)a.H * a.dk * a.dv;
+    for (int b = 0; b < a.B; ++b) {
+      const hipError_t e = hipMemcpyAsync(a.S_T + (size_t)b * per, Pb + ((size_t)b * R + R - 1) * per,
+                                          per * sizeof(float), hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return fail(KDA_E_HIP, "state copy failed: %s", hipGetErrorString(e));
+    }
+  }
+  if (a.conv_out != nullptr) return kda::launch_cp_history(a, 1, R, L, a.conv_out, s);
+  return KDA_OK;
 }
 
 int kda_decode_step(const kda_decode_args* a, void* stream) {

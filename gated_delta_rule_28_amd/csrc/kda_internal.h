@@ -20,6 +20,14 @@ size_t prefill_split_workspace_bytes(const kda_prefill_args& a);
 size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a);
 int launch_prefill_split(const kda_prefill_args& a, hipStream_t s);
 
+// Context-parallel helpers: the prefix composition; the raw conv history of
+// `nblk` blocks per sequence (the three raw tokens before token (first + j) * L
+// of block j, from conv_in before token 0) into dst [B * nblk, 3, Cch]; the
+// identity in `count` d x d fp32 matrices.
+int launch_cp_compose(const kda_cp_compose_args& a, hipStream_t s);
+int launch_cp_history(const kda_prefill_args& a, int nblk, int first, int L, void* dst, hipStream_t s);
+int launch_cp_identity(float* S, size_t count, int d, hipStream_t s);
+
 // Set the calling thread's last-error text (printf-style).
 void set_error(const char* fmt, ...);
 

@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 2
+#define KDA_ABI_VERSION 3
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -245,6 +245,73 @@ typedef struct kda_prep_args {
 } kda_prep_args;
 
 int kda_prep(const kda_prep_args* args, void* stream);
+
+/*
+ * Context-parallel prefill.  The long-context training row of "Gemma 4 31B vs
+ * Kimi K3" (component table) says that ranks exchange only fixed-size state
+ * fragments.  The update above is affine in the state, so a segment of tokens
+ * maps the state S entering it to M S + N (M: dk x dk, N: dk x dv), whatever S
+ * is.  With dk = dv, two prefills
+ * of a segment give both: from S = 0 its final state is N, from S = I it is
+ * P = M + N.  Each rank forms (N, P) for its segment, the ranks exchange them
+ * (dk*(dk+dv)*4 bytes per head each), each composes the state entering its own
+ * segment, and runs its segment again from that state for the outputs.
+ *
+ * kda_cp_compose: the composition, for every (b, h):
+ *   S_start[b*R]         = S0[b]                          (zeros if S0 is NULL)
+ *   S_start[b*R + r + 1] = (P[b*R + r] - N[b*R + r]) S_start[b*R + r] + N[b*R + r]
+ *   S_T[b]               = the same map applied after the last segment r = R - 1
+ * N, P, S_start: [B*R, H, d, d] fp32 (the R segments of sequence b consecutive,
+ * as in a prefill batch of B*R segments); S0, S_T: [B, H, d, d] fp32, may be
+ * NULL; S_T may alias S0.  S_start must not overlap N, P or S0.  d in {16, 32,
+ * 64, 128}; all pointers 16-byte aligned.  Errors: KDA_E_NULL (N, P or
+ * S_start NULL), KDA_E_SHAPE (B, R or H < 1, or too large), KDA_E_UNSUPPORTED
+ * (d), KDA_E_ALIGN.
+ */
+typedef struct kda_cp_compose_args {
+  int B, R, H, d;
+  const float* N;         /* [B*R, H, d, d] final states from S = 0 */
+  const float* P;         /* [B*R, H, d, d] final states from S = I */
+  const float* S0;        /* [B, H, d, d] state entering segment 0, or NULL */
+  float* S_start;         /* [B*R, H, d, d] out: state entering each segment */
+  float* S_T;             /* [B, H, d, d] out: state after the last segment, or NULL */
+} kda_cp_compose_args;
+
+int kda_cp_compose(const kda_cp_compose_args* args, void* stream);
+
+/*
+ * kda_prefill_cp: the whole context-parallel prefill on one device, the R
+ * segments of each sequence standing in for R ranks.  Same arguments and
+ * results as kda_prefill (o, S_T, conv_out; S_T may alias S0 and conv_out
+ * conv_in), computed as
+ *   1. the raw conv history of every segment: the three raw tokens before it
+ *      (from conv_in, or zeros, before the first);
+ *   2. all B*R segments as one prefill batch from S = 0, then from S = I
+ *      (their outputs o are overwritten by step 4);
+ *   3. kda_cp_compose of the two final-state batches, from S0;
+ *   4. all B*R segments again from their entering states: o, and the last
+ *      segment's final state as S_T; conv_out from the last three raw tokens.
+ * Requires T a multiple of `segments` with at least 3 tokens per segment (T = 0
+ * is passed to kda_prefill), dk = dv.  Every step runs on `stream` in the
+ * caller's workspace (kda_prefill_cp_workspace_bytes, 16-byte aligned): the
+ * segment histories, the N / P / entering-state batches and the segment
+ * prefills' own workspace.  The workspace fields inside `prefill` are ignored.
+ * Errors: those of kda_prefill, KDA_E_SHAPE (segments < 1, T not a multiple,
+ * fewer than 3 tokens per segment), KDA_E_NULL (no workspace),
+ * KDA_E_WORKSPACE (workspace too small).
+ */
+typedef struct kda_prefill_cp_args {
+  kda_prefill_args prefill;  /* the whole sequences, as for kda_prefill */
+  int segments;              /* R >= 1 segments per sequence */
+  void* workspace;
+  size_t workspace_bytes;
+} kda_prefill_cp_args;
+
+int kda_prefill_cp(const kda_prefill_cp_args* args, void* stream);
+
+/* Workspace kda_prefill_cp needs for these sizes (fields B, T, H, dk, dv,
+ * chunk, in_dtype, out_dtype and segments are read); 0 if they are invalid. */
+size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* args);
 
 /* Static text of a status code. */
 const char* kda_status_string(int code);

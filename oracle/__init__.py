@@ -16,11 +16,11 @@ rms_norm_eps from the "Kimi K3" model card config):
   matrix product S_t = (I - beta k k^T) Diag(alpha_t) S_{t-1} + beta k v^T with
   an explicit dk x dk transition.  Slow; for small shapes.
 
-Context parallelism ("Kimi K3, previewed", long-context row): a segment maps its
-entering state S to M S + N.  `segment_transition` builds M as the ordered
-product of the per-token maps, `segment_fragments` returns (M, N),
-`compose_segments` the entering states, and `prefill_context_parallel` the
-whole prefill computed segment by segment.
+Context parallelism ("Gemma 4 31B vs Kimi K3", component table, long-context
+training row): a segment maps its entering state S to M S + N.
+`segment_transition` builds M as the ordered product of the per-token maps,
+`segment_fragments` returns (M, N), `compose_segments` the entering states, and
+`prefill_context_parallel` the whole prefill computed segment by segment.
 
 Inputs are numpy arrays: float32, or uint16 holding bf16 bits.  All
 arithmetic is fp64 on the exact input values.
@@ -281,9 +281,10 @@ def prefill_matrix_form(inp: dict, heads=None, S=None, hist=None) -> dict:
 
 
 # ----------------------------------------------------------------------------
-# Context parallelism ("Kimi K3, previewed", long-context row: ranks exchange
-# only fixed-size state fragments).  Plainest reading: the state update is
-# affine in the state, so a segment acts on the state entering it as
+# Context parallelism ("Gemma 4 31B vs Kimi K3", component table, long-context
+# training row: ranks exchange only fixed-size state fragments).  Plainest
+# reading: the state update is affine in the state, so a segment acts on the
+# state entering it as
 # S_out = M S_in + N; each rank forms (M, N) for its segment, the fragments are
 # gathered, and a prefix composition gives every segment its entering state.
 # ----------------------------------------------------------------------------

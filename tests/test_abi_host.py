@@ -36,7 +36,8 @@ def declared_functions():
 def test_header_declares_the_abi():
     names = declared_functions()
     for must in ("kda_prefill", "kda_decode_step", "kda_decode_multi", "kda_prefill_workspace_bytes", "kda_prep",
-                 "kda_status_string", "kda_last_error", "kda_abi_version"):
+                 "kda_status_string", "kda_last_error", "kda_abi_version", "kda_cp_compose", "kda_prefill_cp",
+                 "kda_prefill_cp_workspace_bytes"):
         assert must in names
 
 
@@ -67,12 +68,14 @@ def _c_offsets(struct, fields):
     return vals[0], vals[1:]
 
 
-@pytest.mark.parametrize("name", ["PrefillArgs", "DecodeArgs", "PrepArgs", "DecodeMultiArgs"])
+@pytest.mark.parametrize("name", ["PrefillArgs", "DecodeArgs", "PrepArgs", "DecodeMultiArgs", "CpComposeArgs",
+                                  "PrefillCpArgs"])
 def test_ctypes_layout_matches_header(name):
     import gated_delta_rule_28_amd as kda
     cls = getattr(kda, name)
     struct = {"PrefillArgs": "kda_prefill_args", "DecodeArgs": "kda_decode_args",
-              "PrepArgs": "kda_prep_args", "DecodeMultiArgs": "kda_decode_multi_args"}[name]
+              "PrepArgs": "kda_prep_args", "DecodeMultiArgs": "kda_decode_multi_args",
+              "CpComposeArgs": "kda_cp_compose_args", "PrefillCpArgs": "kda_prefill_cp_args"}[name]
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_offsets(struct, fields)
     assert ctypes.sizeof(cls) == size
@@ -196,8 +199,47 @@ def test_prep_validation_codes(kda):
         assert L.kda_prep(ctypes.byref(a), None) == code, over
 
 
+def test_cp_compose_validation_codes(kda):
+    L = kda.lib()
+    base = dict(B=2, R=3, H=2, d=32, N=0x1000, P=0x2000, S0=None, S_start=0x3000, S_T=None)
+    for over, code in [(dict(N=None), -1), (dict(P=None), -1), (dict(S_start=None), -1), (dict(B=0), -2),
+                       (dict(R=0), -2), (dict(H=-1), -2), (dict(d=48), -5), (dict(d=256), -5),
+                       (dict(S0=0x4008), -4), (dict(S_T=0x5004), -4), (dict(P=0x2002), -4)]:
+        a = kda.CpComposeArgs(**{**base, **over})
+        assert L.kda_cp_compose(ctypes.byref(a), None) == code, over
+    assert L.kda_cp_compose(None, None) == -1
+
+
+def _cp_args(kda, segments=4, ws=0x100000, ws_bytes=1 << 40, **over):
+    return kda.PrefillCpArgs(_prefill_args(kda, **{**dict(B=2, T=256, H=3, dk=128, dv=128, chunk=64), **over}),
+                             segments, ws, ws_bytes)
+
+
+def test_prefill_cp_validation_and_workspace(kda):
+    """Context-parallel prefill: segment count, split, workspace; nothing launched."""
+    L = kda.lib()
+    for a, code in [(_cp_args(kda, segments=0), -2), (_cp_args(kda, segments=3), -2),
+                    (_cp_args(kda, segments=128), -2),   # 2 tokens per segment
+                    (_cp_args(kda, ws=None), -1), (_cp_args(kda, ws=0x100008), -4),
+                    (_cp_args(kda, ws_bytes=1000), -6), (_cp_args(kda, q=None), -1),
+                    (_cp_args(kda, dk=64, dv=128), -5), (_cp_args(kda, chunk=8), -5),
+                    (_cp_args(kda, decay_form=1), -1)]:
+        assert L.kda_prefill_cp(ctypes.byref(a), None) == code
+    assert L.kda_prefill_cp(None, None) == -1
+    # workspace: histories + three state batches + the segment prefills' workspace
+    a = _cp_args(kda, segments=4)
+    seg = _prefill_args(kda, B=8, T=64, H=3, dk=128, dv=128, chunk=64)
+    cch = 3 * 3 * 128
+    r256 = lambda x: (x + 255) // 256 * 256
+    want = (r256(8 * 3 * cch * 2) + 3 * r256(8 * 3 * 128 * 128 * 4)
+            + L.kda_prefill_workspace_bytes(ctypes.byref(seg)))
+    assert L.kda_prefill_cp_workspace_bytes(ctypes.byref(a)) == want
+    assert L.kda_prefill_cp_workspace_bytes(ctypes.byref(_cp_args(kda, segments=3))) == 0
+    assert L.kda_prefill_cp_workspace_bytes(None) == 0
+
+
 def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 2
+    assert L.kda_abi_version() == 3

@@ -1,8 +1,9 @@
 """Pins of the oracle's context-parallel algebra (segment fragments and their
 prefix composition) against results that do not come from that algebra.
 
-The long-context row of "Kimi K3, previewed" says only that ranks exchange
-fixed-size state fragments.  The reading taken: the update is affine in the
+The long-context training row of "Gemma 4 31B vs Kimi K3" (component table)
+says only that ranks exchange fixed-size state fragments.  The reading taken:
+the update is affine in the
 state, a segment maps its entering state S to M S + N, and composing the
 segments' (M, N) in order gives each segment its entering state.  M is built
 from the per-token product definition, not from the recurrence, so agreement
