@@ -142,6 +142,49 @@ def cpu_baseline(w, dev_inp, seconds_target=15.0):
                       f"({head_tokens} head-tokens, {el:.1f} s); tokens/s = head-tokens/s / {H}"}
 
 
+FP32_VALU_PEAK_TFS = 157.3
+
+
+def backward_flops_per_head_token(d):
+    """Algorithmic FLOP of the prefill gradient per (head, token), state side:
+    one forward step (decay d^2, y 2d^2, rank-1 update 2d^2, read-out 2d^2 = 7d^2)
+    and the reverse step (decay of the state and of its gradient 2d^2, S_t 2d^2,
+    S_t dz 2d^2, q^ dz^T 2d^2, dS^T k^ 2d^2, dS u + S' dy 4d^2, k^ dy^T 2d^2,
+    rowsum(dS' S') 2d^2 = 18d^2); the O(d) vector work is not counted."""
+    return 25 * d * d
+
+
+def time_backward(torch, kda, w, inp, steps):
+    """kda_prefill_backward over the whole workload (all T tokens of each
+    sequence), random fp32 output and final-state gradients."""
+    dev = inp["q"].device
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    go = torch.randn((w.B, w.T, w.H, w.dv), generator=gen, device=dev)
+    gs = torch.randn((w.B, w.H, w.dk, w.dv), generator=gen, device=dev)
+    ws = torch.empty(kda.backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+    args = [inp[x] for x in ("q", "k", "v", "conv_w", "g", "beta", "gate")]
+    holder = {}
+
+    def call():
+        holder["g"] = kda.prefill_backward(*args, go, S0=inp["S0"], grad_S_T=gs, workspace=ws)
+
+    call()
+    torch.cuda.synchronize()
+    per = timed_launches(torch, call, steps)
+    ms = sum(per) / len(per)
+    flops = backward_flops_per_head_token(w.dk) * w.B * w.T * w.H
+    tfs = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] backward: {ms:.1f} ms/call, {w.B * w.T / (ms * 1e-3) / 1e6:.3f} M tokens/s, {tfs:.2f} TFLOP/s")
+    return {"metric": "prefill backward tokens/s", "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s",
+            "ms_per_call": ms, "calls_timed": steps,
+            "config": f"kda_prefill_backward B{w.B} T{w.T} H{w.H} dk=dv={w.dk}, bf16 inputs, fp32 gradients",
+            "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": None,
+                         "algorithmic_flops_per_launch": flops},
+            "workspace_bytes": ws.numel()}
+
+
 def time_context_parallel(torch, kda, w, inp, R, A, steps):
     """kda_prefill_cp of the whole workload (all T tokens of each sequence, whatever
     segmentation the workload's own timing uses) in R segments on this GPU (three prefill
@@ -214,6 +257,8 @@ def main():
     ap.add_argument("--calibrate", action="store_true")
     ap.add_argument("--decay-form", default="direct", choices=["direct", "k3"])
     ap.add_argument("--verify-tokens", type=int, default=4)
+    ap.add_argument("--backward-steps", type=int, default=0,
+                    help="also time kda_prefill_backward over the workload (this many calls)")
     ap.add_argument("--cp-segments", type=int, default=0,
                     help="also time the context-parallel prefill (kda_prefill_cp) with this many segments")
     args = ap.parse_args()
@@ -311,6 +356,9 @@ def main():
                  "frac_of_bf16_f16_peak": flops / (launch_ms * 1e-3) / 1e12 / BF16_MFMA_PEAK_TFS},
     }
     del o
+
+    if args.backward_steps > 0:
+        out["backward"] = time_backward(torch, kda, w, inp, args.backward_steps)
 
     if args.cp_segments > 0:
         out["context_parallel"] = time_context_parallel(torch, kda, w, inp, args.cp_segments, A,

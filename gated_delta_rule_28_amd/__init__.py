@@ -12,6 +12,7 @@ works, but every call raises (there is no fallback implementation).
     qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
     o, S_T, conv_out = prefill_cp(q, k, v, conv_w, g, beta, gate, segments=R, ...)  # context-parallel
     S_start, S_T = cp_compose(N, P, S0=None, B=1)   # the composition step alone
+    grads = prefill_backward(q, k, v, conv_w, g, beta, gate, grad_o, S0=None, conv_in=None, grad_S_T=None)
 
 Every call also takes A=None: given an fp32 [H, dk] tensor, g and beta are K3's
 logits (g = -5 sigmoid(e^A z), beta = sigmoid(b), KDA_DECAY_K3) instead of the
@@ -25,7 +26,8 @@ import os
 __all__ = ["prefill", "decode_step", "decode_multi", "prep", "workspace_bytes", "library_path", "lib", "KDAError",
            "KDA_F32", "KDA_BF16", "KDA_DECAY_DIRECT", "KDA_DECAY_K3", "PrefillArgs", "DecodeArgs",
            "PrepArgs", "DecodeMultiArgs", "MAX_DECODE_TOKENS", "prefill_cp", "cp_compose",
-           "cp_workspace_bytes", "CpComposeArgs", "PrefillCpArgs"]
+           "cp_workspace_bytes", "CpComposeArgs", "PrefillCpArgs", "prefill_backward", "PrefillBackwardArgs",
+           "backward_workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -34,7 +36,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
-ABI_VERSION = 3
+ABI_VERSION = 4
 MAX_DECODE_TOKENS = 16
 
 
@@ -91,6 +93,16 @@ class PrefillCpArgs(ctypes.Structure):
                 ("workspace_bytes", ctypes.c_size_t)]
 
 
+class PrefillBackwardArgs(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
+                ("dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("q", _P), ("k", _P), ("v", _P),
+                ("conv_w", _P), ("g", _P), ("beta", _P), ("gate", _P), ("S0", _P), ("conv_in", _P),
+                ("grad_o", _P), ("grad_S_T", _P), ("grad_q", _P), ("grad_k", _P), ("grad_v", _P),
+                ("grad_g", _P), ("grad_beta", _P), ("grad_gate", _P), ("grad_S0", _P), ("grad_conv_in", _P),
+                ("workspace", _P), ("workspace_bytes", ctypes.c_size_t), ("decay_form", ctypes.c_int),
+                ("A", _P)]
+
+
 _lib = None
 
 
@@ -119,6 +131,10 @@ def lib():
         L.kda_prefill_cp.restype = ctypes.c_int
         L.kda_prefill_cp_workspace_bytes.argtypes = [ctypes.POINTER(PrefillCpArgs)]
         L.kda_prefill_cp_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_prefill_backward.argtypes = [ctypes.POINTER(PrefillBackwardArgs), _P]
+        L.kda_prefill_backward.restype = ctypes.c_int
+        L.kda_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(PrefillBackwardArgs)]
+        L.kda_prefill_backward_workspace_bytes.restype = ctypes.c_size_t
         L.kda_status_string.argtypes = [ctypes.c_int]
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.restype = ctypes.c_char_p
@@ -313,3 +329,37 @@ def cp_compose(N, P, S0=None, B=1, S_start=None, S_T=None, want_state=True):
     a = CpComposeArgs(B, BR // B, H, d, _ptr(N), _ptr(P), _ptr(S0), _ptr(S_start), _ptr(S_T))
     _check("kda_cp_compose", lib().kda_cp_compose(ctypes.byref(a), _stream(N.device)))
     return S_start, S_T
+
+
+def backward_workspace_bytes(B, T, H, dk, dv, in_dtype=KDA_BF16):
+    """kda_prefill_backward_workspace_bytes for these sizes (0: invalid)."""
+    a = PrefillBackwardArgs(B, T, H, dk, dv, in_dtype)
+    return int(lib().kda_prefill_backward_workspace_bytes(ctypes.byref(a)))
+
+
+def prefill_backward(q, k, v, conv_w, g, beta, gate, grad_o, S0=None, conv_in=None, grad_S_T=None,
+                     want_state_grad=True, want_conv_grad=True, workspace=None):
+    """Gradients of <grad_o, o> + <grad_S_T, S_T> of `prefill` (kda_prefill_backward).
+    Returns a dict of fp32 tensors: q, k, v, g, beta, gate (the inputs' shapes),
+    S0 [B,H,dk,dv] and conv_in [B,3,Cch] (None when not wanted)."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    f = dict(dtype=torch.float32, device=dev)
+    out = {x: torch.empty(t.shape, **f) for x, t in (("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta),
+                                                     ("gate", gate))}
+    out["S0"] = torch.empty((B, H, dk, dv), **f) if want_state_grad else None
+    out["conv_in"] = torch.empty((B, 3, H * (2 * dk + dv)), **f) if want_conv_grad else None
+    a = PrefillBackwardArgs(B, T, H, dk, dv, _dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w), _ptr(g),
+                            _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in), _ptr(grad_o), _ptr(grad_S_T),
+                            _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["g"]), _ptr(out["beta"]),
+                            _ptr(out["gate"]), _ptr(out["S0"]), _ptr(out["conv_in"]), None, 0, KDA_DECAY_DIRECT,
+                            None)
+    if workspace is None:
+        workspace = torch.empty(max(int(lib().kda_prefill_backward_workspace_bytes(ctypes.byref(a))), 16),
+                                dtype=torch.uint8, device=dev)
+    a.workspace = _ptr(workspace)
+    a.workspace_bytes = workspace.numel() * workspace.element_size()
+    _check("kda_prefill_backward", lib().kda_prefill_backward(ctypes.byref(a), _stream(dev)))
+    return out

@@ -16,7 +16,8 @@ OUT = os.path.join(HERE, "libkda.so")
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
-SOURCES = ["kda_api.cpp", "kda_cp.hip", "kda_decode.hip", "kda_prefill.hip", "kda_prefill_split.hip"]
+SOURCES = ["kda_api.cpp", "kda_backward.hip", "kda_cp.hip", "kda_decode.hip", "kda_prefill.hip",
+           "kda_prefill_split.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",

@@ -261,6 +261,42 @@ int kda_prefill_cp(const kda_prefill_cp_args* c, void* stream) {
   return KDA_OK;
 }
 
+size_t kda_prefill_backward_workspace_bytes(const kda_prefill_backward_args* a) {
+  if (a == nullptr) return 0;
+  if (kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, KDA_F32) != KDA_OK) return 0;
+  return kda::prefill_backward_workspace_bytes(*a);
+}
+
+int kda_prefill_backward(const kda_prefill_backward_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  REQUIRE_PTR(a);
+  int rc = kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, KDA_F32);
+  if (rc != KDA_OK) return rc;
+  if (a->decay_form != KDA_DECAY_DIRECT)
+    return fail(KDA_E_UNSUPPORTED, "backward: decay_form=%d; only KDA_DECAY_DIRECT", a->decay_form);
+  if ((long long)a->B * a->T * a->H > 0x7fffffffLL) return fail(KDA_E_SHAPE, "B*T*H too large");
+  if (a->T > 0) {
+    REQUIRE_PTR(a->q); REQUIRE_PTR(a->k); REQUIRE_PTR(a->v); REQUIRE_PTR(a->conv_w);
+    REQUIRE_PTR(a->g); REQUIRE_PTR(a->beta); REQUIRE_PTR(a->gate); REQUIRE_PTR(a->grad_o);
+    REQUIRE_PTR(a->grad_q); REQUIRE_PTR(a->grad_k); REQUIRE_PTR(a->grad_v); REQUIRE_PTR(a->grad_g);
+    REQUIRE_PTR(a->grad_beta); REQUIRE_PTR(a->grad_gate);
+  }
+  REQUIRE_A16(a->q); REQUIRE_A16(a->k); REQUIRE_A16(a->v); REQUIRE_A16(a->conv_w);
+  REQUIRE_A16(a->g); REQUIRE_A16(a->gate); REQUIRE_A16(a->S0); REQUIRE_A16(a->conv_in);
+  REQUIRE_A16(a->grad_o); REQUIRE_A16(a->grad_S_T); REQUIRE_A16(a->grad_q); REQUIRE_A16(a->grad_k);
+  REQUIRE_A16(a->grad_v); REQUIRE_A16(a->grad_g); REQUIRE_A16(a->grad_gate); REQUIRE_A16(a->grad_S0);
+  REQUIRE_A16(a->grad_conv_in);
+  if (a->beta != nullptr && !kda::aligned_n(a->beta, kda::esize(a->in_dtype)))
+    return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
+  if (a->grad_beta != nullptr && !kda::aligned_n(a->grad_beta, 4))
+    return fail(KDA_E_ALIGN, "grad_beta is not 4-byte aligned");
+  if (a->workspace == nullptr) return fail(KDA_E_NULL, "workspace is NULL (kda_prefill_backward_workspace_bytes)");
+  REQUIRE_A16(a->workspace);
+  const size_t need = kda::prefill_backward_workspace_bytes(*a);
+  if (a->workspace_bytes < need) return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", a->workspace_bytes, need);
+  return kda::launch_prefill_backward(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
 int kda_decode_step(const kda_decode_args* a, void* stream) {
   kda::g_err[0] = '\0';
   REQUIRE_PTR(a);

@@ -28,6 +28,10 @@ int launch_cp_compose(const kda_cp_compose_args& a, hipStream_t s);
 int launch_cp_history(const kda_prefill_args& a, int nblk, int first, int L, void* dst, hipStream_t s);
 int launch_cp_identity(float* S, size_t count, int d, hipStream_t s);
 
+// Prefill gradients (fp32, one workgroup per (b, h)) and their workspace.
+size_t prefill_backward_workspace_bytes(const kda_prefill_backward_args& a);
+int launch_prefill_backward(const kda_prefill_backward_args& a, hipStream_t s);
+
 // Set the calling thread's last-error text (printf-style).
 void set_error(const char* fmt, ...);
 

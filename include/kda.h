@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 3
+#define KDA_ABI_VERSION 4
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -312,6 +312,57 @@ int kda_prefill_cp(const kda_prefill_cp_args* args, void* stream);
 /* Workspace kda_prefill_cp needs for these sizes (fields B, T, H, dk, dv,
  * chunk, in_dtype, out_dtype and segments are read); 0 if they are invalid. */
 size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* args);
+
+/*
+ * kda_prefill_backward: gradients of the prefill for training (the long
+ * contexts of "Gemma 4 31B vs Kimi K3", component table, long-context training
+ * row), for the loss <grad_o, o> + <grad_S_T, S_T> of kda_prefill with the
+ * same inputs: grad_q, grad_k, grad_v, grad_g, grad_beta, grad_gate (fp32, the
+ * layouts of q, k, v, g, beta, gate), grad_S0 [B,H,dk,dv] and grad_conv_in
+ * [B,3,Cch] (fp32, each may be NULL).
+ * Gradients are with respect to the input values (bf16 inputs: their bf16
+ * values).  Direct decay form only (decay_form KDA_DECAY_DIRECT), dk = dv.
+ * Computed in fp32, one workgroup per (b, h): the forward recurrence again
+ * with the state stored every 64 tokens in the workspace, then each 64-token
+ * stretch recomputed and walked back token by token.  Workspace
+ * (kda_prefill_backward_workspace_bytes, 16-byte aligned, required):
+ * B*H*((ceil(T/64) + 64)*dk*dv + 64*(11*dk + 8))*4 bytes.
+ * Errors as kda_prefill; KDA_E_NULL (grad_o, a required gradient output or the
+ * workspace NULL), KDA_E_UNSUPPORTED (KDA_DECAY_K3), KDA_E_WORKSPACE.
+ */
+typedef struct kda_prefill_backward_args {
+  int B, T, H, dk, dv;
+  int in_dtype;           /* KDA_F32 or KDA_BF16 (q, k, v, g, beta, gate, conv_in) */
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* conv_w;
+  const void* g;
+  const void* beta;
+  const void* gate;
+  const float* S0;        /* may be NULL */
+  const void* conv_in;    /* may be NULL */
+  const float* grad_o;    /* dL/do [B,T,H,dv] fp32 */
+  const float* grad_S_T;  /* dL/dS_T [B,H,dk,dv] fp32, or NULL (no loss on S_T) */
+  float* grad_q;
+  float* grad_k;
+  float* grad_v;
+  float* grad_g;
+  float* grad_beta;
+  float* grad_gate;
+  float* grad_S0;         /* may be NULL */
+  float* grad_conv_in;    /* may be NULL */
+  void* workspace;
+  size_t workspace_bytes;
+  int decay_form;         /* KDA_DECAY_DIRECT */
+  const float* A;         /* unused */
+} kda_prefill_backward_args;
+
+int kda_prefill_backward(const kda_prefill_backward_args* args, void* stream);
+
+/* Workspace kda_prefill_backward needs (fields B, T, H, dk, dv, in_dtype read);
+ * 0 if they are invalid. */
+size_t kda_prefill_backward_workspace_bytes(const kda_prefill_backward_args* args);
 
 /* Static text of a status code. */
 const char* kda_status_string(int code);

@@ -37,7 +37,7 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for must in ("kda_prefill", "kda_decode_step", "kda_decode_multi", "kda_prefill_workspace_bytes", "kda_prep",
                  "kda_status_string", "kda_last_error", "kda_abi_version", "kda_cp_compose", "kda_prefill_cp",
-                 "kda_prefill_cp_workspace_bytes"):
+                 "kda_prefill_cp_workspace_bytes", "kda_prefill_backward", "kda_prefill_backward_workspace_bytes"):
         assert must in names
 
 
@@ -69,13 +69,14 @@ def _c_offsets(struct, fields):
 
 
 @pytest.mark.parametrize("name", ["PrefillArgs", "DecodeArgs", "PrepArgs", "DecodeMultiArgs", "CpComposeArgs",
-                                  "PrefillCpArgs"])
+                                  "PrefillCpArgs", "PrefillBackwardArgs"])
 def test_ctypes_layout_matches_header(name):
     import gated_delta_rule_28_amd as kda
     cls = getattr(kda, name)
     struct = {"PrefillArgs": "kda_prefill_args", "DecodeArgs": "kda_decode_args",
               "PrepArgs": "kda_prep_args", "DecodeMultiArgs": "kda_decode_multi_args",
-              "CpComposeArgs": "kda_cp_compose_args", "PrefillCpArgs": "kda_prefill_cp_args"}[name]
+              "CpComposeArgs": "kda_cp_compose_args", "PrefillCpArgs": "kda_prefill_cp_args",
+              "PrefillBackwardArgs": "kda_prefill_backward_args"}[name]
     fields = [f for f, _ in cls._fields_]
     size, offs = _c_offsets(struct, fields)
     assert ctypes.sizeof(cls) == size
@@ -238,8 +239,29 @@ def test_prefill_cp_validation_and_workspace(kda):
     assert L.kda_prefill_cp_workspace_bytes(None) == 0
 
 
+def test_prefill_backward_validation_and_workspace(kda):
+    L = kda.lib()
+    base = dict(B=2, T=100, H=3, dk=32, dv=32, in_dtype=kda.KDA_BF16, q=0x1000, k=0x2000, v=0x3000,
+                conv_w=0x4000, g=0x5000, beta=0x6000, gate=0x7000, S0=None, conv_in=None, grad_o=0x8000,
+                grad_S_T=None, grad_q=0x9000, grad_k=0xa000, grad_v=0xb000, grad_g=0xc000, grad_beta=0xd000,
+                grad_gate=0xe000, grad_S0=None, grad_conv_in=None, workspace=0x100000, workspace_bytes=1 << 40,
+                decay_form=0, A=None)
+    for over, code in [(dict(grad_o=None), -1), (dict(grad_k=None), -1), (dict(workspace=None), -1),
+                       (dict(B=0), -2), (dict(in_dtype=5), -3), (dict(grad_q=0x9008), -4),
+                       (dict(workspace=0x100004), -4), (dict(grad_beta=0xd002), -4), (dict(dk=32, dv=64), -5),
+                       (dict(decay_form=1, A=0xf000), -5), (dict(workspace_bytes=100), -6)]:
+        a = kda.PrefillBackwardArgs(**{**base, **over})
+        assert L.kda_prefill_backward(ctypes.byref(a), None) == code, over
+    assert L.kda_prefill_backward(None, None) == -1
+    # ((ceil(T/64) + 64) d^2 + 64 (11 d + 8)) floats per (b, h)
+    a = kda.PrefillBackwardArgs(**base)
+    want = 2 * 3 * ((2 + 64) * 32 * 32 + 64 * (11 * 32 + 8)) * 4
+    assert L.kda_prefill_backward_workspace_bytes(ctypes.byref(a)) == want
+    assert L.kda_prefill_backward_workspace_bytes(None) == 0
+
+
 def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 3
+    assert L.kda_abi_version() == 4

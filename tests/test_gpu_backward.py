@@ -1,0 +1,86 @@
+"""kda_prefill_backward on the GPU against the fp64 autograd reference
+(oracle/backward.py, itself pinned by finite differences).
+
+The kernel computes in fp32 throughout, so the bound is the fp32 one of the
+forward (1e-4 x RMS of each reference gradient), for f32 and bf16 inputs alike
+(bf16 inputs are exact values; only the arithmetic rounds).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import kda_synth as syn
+from kda_synth import Workload
+from gpu_util import assert_rms_close, need_gpu, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL_GRAD = 1e-4
+NAMES = ("q", "k", "v", "g", "beta", "gate", "S0", "conv_in")
+
+
+def _run(kda, torch, inp, dtype, dO, dS):
+    dev = to_dev(inp, dtype)
+    go = torch.from_numpy(dO.astype(np.float32)).cuda()
+    gs = None if dS is None else torch.from_numpy(dS.astype(np.float32)).cuda()
+    out = kda.prefill_backward(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"],
+                               go, S0=dev.get("S0"), conv_in=dev.get("conv_in"), grad_S_T=gs)
+    torch.cuda.synchronize()
+    return {x: out[x].cpu().numpy() for x in NAMES}
+
+
+CASES = [
+    # B, T, H, d, dtype
+    (1, 200, 2, 128, "bf16"),   # 4 stretches of 64 (ragged last)
+    (2, 150, 2, 32, "f32"),
+    (2, 70, 3, 16, "bf16"),
+    (1, 64, 2, 64, "f32"),      # exactly one stretch
+    (2, 2, 2, 16, "f32"),       # fewer tokens than the conv history
+]
+
+
+@pytest.mark.parametrize("B,T,H,d,dtype", CASES)
+def test_backward_matches_autograd(B, T, H, d, dtype):
+    torch, kda = need_gpu()
+    ob = pytest.importorskip("oracle.backward")
+    w = Workload("bwd", B, T, H, d, d, 64, dtype, s0_sigma=0.05, conv_hist="normal", seed=120 + T + d)
+    inp = syn.prefill_inputs_np(w)
+    rng = np.random.default_rng(T + d)
+    dO = rng.standard_normal((B, T, H, d))
+    dS = rng.standard_normal((B, H, d, d))
+    print(f"  case B{B} T{T} H{H} d{d} {dtype}", flush=True)
+    got = _run(kda, torch, inp, dtype, dO, dS)
+    ref = ob.backward(inp, dO, dS)
+    for x in NAMES:
+        assert_rms_close(got[x], ref[x], TOL_GRAD, f"d{x}")
+
+
+def test_backward_without_state_loss():
+    """grad_S_T = NULL: the loss is <dO, o> only (S0 = NULL, conv_in = NULL too)."""
+    torch, kda = need_gpu()
+    ob = pytest.importorskip("oracle.backward")
+    w = Workload("bwd0", 1, 90, 2, 32, 32, 64, "bf16", s0_sigma=0.0, conv_hist="zero", seed=131)
+    inp = syn.prefill_inputs_np(w)
+    inp["S0"] = None
+    inp["conv_in"] = None
+    dO = np.random.default_rng(7).standard_normal((1, 90, 2, 32))
+    got = _run(kda, torch, inp, "bf16", dO, None)
+    ref = ob.backward(inp, dO, None)
+    for x in NAMES:
+        assert_rms_close(got[x], ref[x], TOL_GRAD, f"d{x} (no state loss)")
+
+
+def test_backward_empty_sequence():
+    """T = 0: the state gradient passes through, the history gradient is zero."""
+    torch, kda = need_gpu()
+    B, H, d = 2, 2, 32
+    dev = {x: torch.zeros((B, 0, H, d), dtype=torch.bfloat16, device="cuda") for x in ("q", "k", "v", "g", "gate")}
+    beta = torch.zeros((B, 0, H), dtype=torch.bfloat16, device="cuda")
+    conv_w = torch.zeros((3 * H * d, 4), dtype=torch.float32, device="cuda")
+    go = torch.zeros((B, 0, H, d), dtype=torch.float32, device="cuda")
+    gs = torch.randn((B, H, d, d), device="cuda")
+    out = kda.prefill_backward(dev["q"], dev["k"], dev["v"], conv_w, dev["g"], beta, dev["gate"], go, grad_S_T=gs)
+    torch.cuda.synchronize()
+    assert torch.equal(out["S0"], gs)
+    assert torch.count_nonzero(out["conv_in"]).item() == 0
