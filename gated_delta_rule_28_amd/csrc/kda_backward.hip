@@ -54,29 +54,36 @@ struct BwdParams {
   float* ws;
 };
 
-// floats of one token's vectors in the workspace: a, x~ (3d each), q^, k^, y,
-// u, z (d each), then scalars nq, nk, rq, rk, r, beta (8 slots)
+// One token's record in the workspace (floats): a, x~ (3d each), q^, k^, y,
+// u, z, alpha = e^g, sigmoid(gate), dL/do (d each), then scalars nq, nk, rq,
+// rk, -, beta (8 slots).  The same layout serves as the token's LDS image.
 template <int D>
-struct Vec {
+struct Rec {
   static constexpr int A = 0, X = 3 * D, QN = 6 * D, KN = 7 * D, Y = 8 * D, U = 9 * D, Z = 10 * D;
-  static constexpr int SC = 11 * D;
-  static constexpr int SIZE = 11 * D + 8;
+  static constexpr int AL = 11 * D, SG = 12 * D, DO = 13 * D, SC = 14 * D;
+  static constexpr int SIZE = 14 * D + 8;
 };
 
 template <int D>
 __host__ __device__ constexpr size_t bwd_head_floats(int T) {
   const size_t nch = (size_t)(T + kBwdChunk - 1) / kBwdChunk;
-  return (nch + kBwdChunk) * D * D + (size_t)kBwdChunk * Vec<D>::SIZE;
+  return (nch + kBwdChunk) * D * D + (size_t)kBwdChunk * Rec<D>::SIZE;
 }
 
+// Barriers are LDS-only (lds_barrier): threads exchange data through LDS only,
+// and each thread reads back only the workspace data it wrote itself, so
+// global loads issued ahead (the next token's raw inputs and record) stay in
+// flight across them.
 template <int D, bool IB>
 __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
   constexpr int NC = 3 * D;
+  constexpr int NCT = (NC + kBwdThreads - 1) / kBwdThreads;  // conv channels per thread
   constexpr int CG = D / 4;
   constexpr int RG0 = kBwdThreads / CG;
   constexpr int RG = RG0 < D ? RG0 : D;
   constexpr int RPT = D / RG;
-  using V = Vec<D>;
+  using V = Rec<D>;
+  constexpr int NPRE = (V::SIZE + kBwdThreads - 1) / kBwdThreads;  // record floats per thread
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -89,39 +96,80 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
 
   float* ckpt = p.ws + (size_t)bh * bwd_head_floats<D>(T);     // [nch][D][D]
   float* st = ckpt + (size_t)nch * D * D;                      // [kBwdChunk][D][D]
-  float* vec = st + (size_t)kBwdChunk * D * D;                 // [kBwdChunk][V::SIZE]
+  float* rec = st + (size_t)kBwdChunk * D * D;                 // [kBwdChunk][V::SIZE]
 
-  // (16-byte aligned: rows of these are read as float4)
-  __shared__ float xa[NC], xs[NC];                 // pre-SiLU a, x~ of the current token
-  __shared__ float al[D], qn[D], kn[D], yv[D], zv[D];
-  __shared__ __attribute__((aligned(16))) float uv[D];
+  __shared__ __attribute__((aligned(16))) float R[V::SIZE];   // the current token's record
   __shared__ __attribute__((aligned(16))) float dzs[D];
   __shared__ __attribute__((aligned(16))) float dus[D];
   __shared__ __attribute__((aligned(16))) float dys[D];
   __shared__ float dqn[D], dkn[D];
-  __shared__ __attribute__((aligned(16))) float red[2][RG][D];
-  __shared__ float ring[3][NC];                    // da of tokens t+1, t+2, t+3
-  __shared__ float sc[16];  // nq, nk, rq, rk, -, beta, -, -, q~.dq^, k~.dk^
+  __shared__ __attribute__((aligned(16))) float red[RG][D];
+  float* const xa = R + V::A;
+  float* const xs = R + V::X;
+  float* const qn = R + V::QN;
+  float* const kn = R + V::KN;
+  float* const yv = R + V::Y;
+  float* const uv = R + V::U;
+  float* const zv = R + V::Z;
+  float* const al = R + V::AL;
+  float* const sc = R + V::SC;  // nq, nk, rq, rk, -, beta; [6], [7]: q~.dq^, k~.dk^
 
   auto rowidx = [&](int t) { return ((size_t)b * T + t) * H + h; };
   // global conv channel of head-local channel c (q | k | v)
   auto gch = [&](int c) { return c < D ? h * D + c : c < 2 * D ? H * D + h * D + (c - D) : 2 * H * D + h * D + (c - 2 * D); };
   auto raw = [&](int t, int c) -> float {
+    if (t >= T) return 0.f;
     if (t < 0) return p.conv_in != nullptr ? load1<IB>(p.conv_in, ((size_t)b * 3 + (size_t)(3 + t)) * cch + gch(c)) : 0.f;
     const void* src = c < D ? p.q : c < 2 * D ? p.k : p.v;
     return load1<IB>(src, rowidx(t) * D + (c % D));
   };
 
-  // per-token vectors of token t into LDS (xa, xs, al, qn, kn, sc[0..5])
-  auto token_vectors = [&](int t) {
-    for (int c = tid; c < NC; c += kBwdThreads) {
-      const float4 w = *reinterpret_cast<const float4*>(p.conv_w + (size_t)gch(c) * 4);
-      const float a = w.x * raw(t - 3, c) + w.y * raw(t - 2, c) + w.z * raw(t - 1, c) + w.w * raw(t, c);
-      xa[c] = a;
-      xs[c] = a * sigmoidf_(a);
+  // this thread's conv channels c = tid + 256 j: taps, raw window t-3..t-1, raw t
+  float4 wch[NCT];
+  float win[NCT][3], rnext[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    const int c = tid + kBwdThreads * j;
+    wch[j] = c < NC ? *reinterpret_cast<const float4*>(p.conv_w + (size_t)gch(c) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
+  }
+  float gnext = 0.f, bnext = 0.f;  // g(t) of channel tid, beta(t)
+  auto start_window = [&](int t) {  // the raw window and the prefetch for token t
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + kBwdThreads * j;
+      if (c < NC) {
+        win[j][0] = raw(t - 3, c);
+        win[j][1] = raw(t - 2, c);
+        win[j][2] = raw(t - 1, c);
+        rnext[j] = raw(t, c);
+      }
     }
-    for (int c = tid; c < D; c += kBwdThreads) al[c] = __expf(load1<IB>(p.g, rowidx(t) * D + c));
-    __syncthreads();
+    gnext = tid < D && t < T ? load1<IB>(p.g, rowidx(t) * D + tid) : 0.f;
+    bnext = tid == 0 && t < T ? load1<IB>(p.beta, rowidx(t)) : 0.f;
+  };
+
+  // token t's vectors into R (xa, xs, al, qn, kn, sc[0..5]); the raw inputs of
+  // token t + 1 are requested before the first barrier
+  auto token_vectors = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + kBwdThreads * j;
+      if (c < NC) {
+        const float4 w = wch[j];
+        const float a = w.x * win[j][0] + w.y * win[j][1] + w.z * win[j][2] + w.w * rnext[j];
+        xa[c] = a;
+        xs[c] = a * sigmoidf_(a);
+        win[j][0] = win[j][1];
+        win[j][1] = win[j][2];
+        win[j][2] = rnext[j];
+        rnext[j] = raw(t + 1, c);
+      }
+    }
+    if (tid < D) al[tid] = __expf(gnext);
+    if (tid == 0) sc[5] = bnext;
+    gnext = tid < D && t + 1 < T ? load1<IB>(p.g, rowidx(t + 1) * D + tid) : 0.f;
+    bnext = tid == 0 && t + 1 < T ? load1<IB>(p.beta, rowidx(t + 1)) : 0.f;
+    lds_barrier();
     if (tid < 64) {
       float sq = 0.f, sk = 0.f;
       for (int c = tid; c < D; c += 64) {
@@ -136,38 +184,30 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         sc[1] = nk;
         sc[2] = rsqrtf(nq) * rsqrtf((float)D);
         sc[3] = rsqrtf(nk);
-        sc[5] = load1<IB>(p.beta, rowidx(t));
       }
     }
-    __syncthreads();
+    lds_barrier();
     for (int c = tid; c < D; c += kBwdThreads) {
       qn[c] = xs[c] * sc[2];
       kn[c] = xs[D + c] * sc[3];
     }
-    __syncthreads();
+    lds_barrier();
   };
 
-  // column sums over the rows: partial[4] of this thread's column group -> out[D]
-  auto colsum2 = [&](const f4& pa, const f4& pb, float* outa, float* outb) {
-    if (active) {
-      *reinterpret_cast<f4*>(&red[0][rg][4 * cg]) = pa;
-      *reinterpret_cast<f4*>(&red[1][rg][4 * cg]) = pb;
-    }
-    __syncthreads();
+  // column sums over the rows of this thread's column group: part -> out[D]
+  auto colsum = [&](const f4& part, float* out) {
+    if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = part;
+    lds_barrier();
     for (int c = tid; c < D; c += kBwdThreads) {
-      float sa = 0.f, sb = 0.f;
-      for (int r = 0; r < RG; ++r) {
-        sa += red[0][r][c];
-        sb += red[1][r][c];
-      }
-      outa[c] = sa;
-      if (outb != nullptr) outb[c] = sb;
+      float sum = 0.f;
+      for (int r = 0; r < RG; ++r) sum += red[r][c];
+      out[c] = sum;
     }
-    __syncthreads();
+    lds_barrier();
   };
 
   // one forward token on the register state s[]: S' = Diag(al) S, y, u, S_t
-  // (and z when want_z); leaves yv, uv (and zv) in LDS
+  // (and z when want_z); leaves yv, uv (and zv) in R
   f4 s[RPT];
   auto forward_token = [&](bool want_z) {
     f4 yp = f4{0.f, 0.f, 0.f, 0.f};
@@ -179,9 +219,9 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         yp += s[i] * kn[r];
       }
     }
-    colsum2(yp, yp, yv, nullptr);
+    colsum(yp, yv);
     for (int c = tid; c < D; c += kBwdThreads) uv[c] = sc[5] * (xs[2 * D + c] - yv[c]);
-    __syncthreads();
+    lds_barrier();
     f4 zp = f4{0.f, 0.f, 0.f, 0.f};
     if (active) {
       const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
@@ -192,7 +232,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         zp += s[i] * qn[r];
       }
     }
-    if (want_z) colsum2(zp, zp, zv, nullptr);
+    if (want_z) colsum(zp, zv);
   };
 
   // ---- 1. forward over the sequence, the state at every chunk start ----------
@@ -204,6 +244,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
                              : f4{0.f, 0.f, 0.f, 0.f};
     }
   }
+  start_window(0);
   for (int t = 0; t < T; ++t) {
     if (t % kBwdChunk == 0 && active) {
       float* dst = ckpt + (size_t)(t / kBwdChunk) * D * D;
@@ -224,57 +265,69 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
                                 : f4{0.f, 0.f, 0.f, 0.f};
     }
   }
-  for (int c = tid; c < 3 * NC; c += kBwdThreads) (&ring[0][0])[c] = 0.f;
-  __syncthreads();
+  float ring[NCT][3];  // da of tokens t+1, t+2, t+3 for this thread's channels
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) ring[j][0] = ring[j][1] = ring[j][2] = 0.f;
 
   for (int ch = nch - 1; ch >= 0; --ch) {
     const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
-    // recompute: the state entering each token and the token's vectors
+    // recompute: the state entering each token, and each token's record
     if (active) {
       const float* src = ckpt + (size_t)ch * D * D;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
     }
+    start_window(t0);
     for (int t = t0; t < t1; ++t) {
       if (active) {
         float* dst = st + (size_t)(t - t0) * D * D;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) *reinterpret_cast<f4*>(dst + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
       }
+      const float gt = tid < D ? load1<IB>(p.gate, rowidx(t) * D + tid) : 0.f;
+      const float dov = tid < D ? p.dO[rowidx(t) * D + tid] : 0.f;
       token_vectors(t);
       forward_token(true);
-      float* vt = vec + (size_t)(t - t0) * V::SIZE;
-      for (int c = tid; c < NC; c += kBwdThreads) {
-        vt[V::A + c] = xa[c];
-        vt[V::X + c] = xs[c];
+      if (tid < D) {
+        R[V::SG + tid] = sigmoidf_(gt);
+        R[V::DO + tid] = dov;
       }
-      for (int c = tid; c < D; c += kBwdThreads) {
-        vt[V::QN + c] = qn[c];
-        vt[V::KN + c] = kn[c];
-        vt[V::Y + c] = yv[c];
-        vt[V::U + c] = uv[c];
-        vt[V::Z + c] = zv[c];
-      }
-      if (tid < 6) vt[V::SC + tid] = sc[tid];
-      __syncthreads();
+      lds_barrier();
+      float* vt = rec + (size_t)(t - t0) * V::SIZE;
+      for (int i = tid; i < V::SIZE; i += kBwdThreads) vt[i] = R[i];
+      lds_barrier();  // R is rewritten by the next token
     }
-    // reverse
+    // reverse, the next token's record requested one token ahead
+    float pre[NPRE];
+    {
+      const float* vt = rec + (size_t)(t1 - 1 - t0) * V::SIZE;
+#pragma unroll
+      for (int j = 0; j < NPRE; ++j) {
+        const int i = tid + kBwdThreads * j;
+        pre[j] = i < V::SIZE ? vt[i] : 0.f;
+      }
+    }
     for (int t = t1 - 1; t >= t0; --t) {
-      const float* vt = vec + (size_t)(t - t0) * V::SIZE;
-      for (int c = tid; c < NC; c += kBwdThreads) {
-        xa[c] = vt[V::A + c];
-        xs[c] = vt[V::X + c];
+#pragma unroll
+      for (int j = 0; j < NPRE; ++j) {
+        const int i = tid + kBwdThreads * j;
+        if (i < V::SIZE) R[i] = pre[j];
       }
-      for (int c = tid; c < D; c += kBwdThreads) {
-        qn[c] = vt[V::QN + c];
-        kn[c] = vt[V::KN + c];
-        yv[c] = vt[V::Y + c];
-        uv[c] = vt[V::U + c];
-        zv[c] = vt[V::Z + c];
-        al[c] = __expf(load1<IB>(p.g, rowidx(t) * D + c));
+      f4 prev[RPT];
+      if (active) {
+        const float* src = st + (size_t)(t - t0) * D * D;
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) prev[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
       }
-      if (tid < 6) sc[tid] = vt[V::SC + tid];
-      __syncthreads();
+      if (t > t0) {
+        const float* vt = rec + (size_t)(t - 1 - t0) * V::SIZE;
+#pragma unroll
+        for (int j = 0; j < NPRE; ++j) {
+          const int i = tid + kBwdThreads * j;
+          pre[j] = i < V::SIZE ? vt[i] : 0.f;
+        }
+      }
+      lds_barrier();
       // output side: r, dgate, dz
       if (tid < 64) {
         float zz = 0.f;
@@ -284,19 +337,14 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         float dd = 0.f;
         for (int c = tid; c < D; c += 64) {
           const float n = zv[c] / r;
-          const float sg = sigmoidf_(load1<IB>(p.gate, rowidx(t) * D + c));
-          const float dov = p.dO[rowidx(t) * D + c];
+          const float sg = R[V::SG + c], dov = R[V::DO + c];
           p.dgate[rowidx(t) * D + c] = dov * n * sg * (1.f - sg);
           dd += dov * sg * n;
         }
         dd = group_sum<64>(dd) * (1.0f / D);
-        for (int c = tid; c < D; c += 64) {
-          const float n = zv[c] / r;
-          const float sg = sigmoidf_(load1<IB>(p.gate, rowidx(t) * D + c));
-          dzs[c] = (p.dO[rowidx(t) * D + c] * sg - n * dd) / r;
-        }
+        for (int c = tid; c < D; c += 64) dzs[c] = (R[V::DO + c] * R[V::SG + c] - zv[c] / r * dd) / r;
       }
-      __syncthreads();
+      lds_barrier();
       // state side
       f4 sp[RPT];
       float rq_part[RPT];
@@ -304,12 +352,10 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
       if (active) {
         const f4 dz = *reinterpret_cast<const f4*>(&dzs[4 * cg]);
         const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
-        const float* src = st + (size_t)(t - t0) * D * D;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
-          const f4 prev = *reinterpret_cast<const f4*>(src + (size_t)r * D + 4 * cg);
-          sp[i] = prev * al[r];
+          sp[i] = prev[i] * al[r];
           const f4 stt = sp[i] + u * kn[r];
           rq_part[i] = stt.x * dz.x + stt.y * dz.y + stt.z * dz.z + stt.w * dz.w;  // (S_t dz)_r partial
           dS[i] += dz * qn[r];
@@ -322,8 +368,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         const float v = group_sum<CG>(active ? rq_part[i] : 0.f);
         if (active && cg == 0) dqn[rg + RG * i] = v;
       }
-      colsum2(dup, dup, dus, nullptr);  // du = dS^T k^
-      // dbeta, dv^, dy
+      colsum(dup, dus);  // du = dS^T k^
+      // dbeta, dy
       if (tid < 64) {
         float db = 0.f;
         for (int c = tid; c < D; c += 64) db += dus[c] * (xs[2 * D + c] - yv[c]);
@@ -331,7 +377,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         if (tid == 0) p.dbeta[rowidx(t)] = db;
       }
       for (int c = tid; c < D; c += kBwdThreads) dys[c] = -sc[5] * dus[c];
-      __syncthreads();
+      lds_barrier();
       if (active) {
         const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
         const f4 dy = *reinterpret_cast<const f4*>(&dys[4 * cg]);
@@ -352,7 +398,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
           dS[i] *= al[r];  // dS_{t-1}
         }
       }
-      __syncthreads();
+      lds_barrier();
       // L2 norms, SiLU, conv transpose
       if (tid < 64) {
         float a = 0.f, bb = 0.f;
@@ -363,28 +409,32 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         a = group_sum<64>(a);
         bb = group_sum<64>(bb);
         if (tid == 0) {
-          sc[8] = a;
-          sc[9] = bb;
+          sc[6] = a;
+          sc[7] = bb;
         }
       }
-      __syncthreads();
-      for (int c = tid; c < NC; c += kBwdThreads) {
-        float dx;
-        if (c < D) dx = sc[2] * (dqn[c] - xs[c] * sc[8] / sc[0]);
-        else if (c < 2 * D) dx = sc[3] * (dkn[c - D] - xs[c] * sc[9] / sc[1]);
-        else dx = sc[5] * dus[c - 2 * D];
-        const float a = xa[c];
-        const float sa = sigmoidf_(a);
-        const float da = dx * sa * (1.f + a * (1.f - sa));
-        const float4 w = *reinterpret_cast<const float4*>(p.conv_w + (size_t)gch(c) * 4);
-        const float dr = w.w * da + w.z * ring[0][c] + w.y * ring[1][c] + w.x * ring[2][c];
-        float* dst = c < D ? p.dq : c < 2 * D ? p.dk : p.dv;
-        dst[rowidx(t) * D + (c % D)] = dr;
-        ring[2][c] = ring[1][c];
-        ring[1][c] = ring[0][c];
-        ring[0][c] = da;
+      lds_barrier();
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        const int c = tid + kBwdThreads * j;
+        if (c < NC) {
+          float dx;
+          if (c < D) dx = sc[2] * (dqn[c] - xs[c] * sc[6] / sc[0]);
+          else if (c < 2 * D) dx = sc[3] * (dkn[c - D] - xs[c] * sc[7] / sc[1]);
+          else dx = sc[5] * dus[c - 2 * D];
+          const float a = xa[c];
+          const float sa = sigmoidf_(a);
+          const float da = dx * sa * (1.f + a * (1.f - sa));
+          const float4 w = wch[j];
+          const float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
+          float* dst = c < D ? p.dq : c < 2 * D ? p.dk : p.dv;
+          dst[rowidx(t) * D + (c % D)] = dr;
+          ring[j][2] = ring[j][1];
+          ring[j][1] = ring[j][0];
+          ring[j][0] = da;
+        }
       }
-      __syncthreads();
+      lds_barrier();  // R, dqn, dkn, dus are rewritten by the next token
     }
   }
 
@@ -396,13 +446,17 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
   }
   if (p.dconv_in != nullptr) {
     // history row s + 3 (token s = -3..-1): sum over t = 0 .. s + 3 of w_{s-t+3} da_t
-    for (int c = tid; c < NC; c += kBwdThreads) {
-      const float4 w = *reinterpret_cast<const float4*>(p.conv_w + (size_t)gch(c) * 4);
-      const float wj[4] = {w.x, w.y, w.z, w.w};
-      for (int s = -3; s < 0; ++s) {
-        float acc = 0.f;
-        for (int t = 0; t <= s + 3 && t < 3; ++t) acc += wj[s - t + 3] * ring[t][c];
-        p.dconv_in[((size_t)b * 3 + (size_t)(s + 3)) * cch + gch(c)] = acc;
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + kBwdThreads * j;
+      if (c < NC) {
+        const float4 w = wch[j];
+        const float wj[4] = {w.x, w.y, w.z, w.w};
+        for (int s3 = 0; s3 < 3; ++s3) {  // s = s3 - 3
+          float acc = 0.f;
+          for (int t = 0; t <= s3 && t < 3; ++t) acc += wj[s3 - t] * ring[j][t];
+          p.dconv_in[((size_t)b * 3 + (size_t)s3) * cch + gch(c)] = acc;
+        }
       }
     }
   }

@@ -136,7 +136,10 @@ int run_compose(const ComposeParams& p, hipStream_t s) {
 // Raw conv history rows: block j of `nblk` per sequence b takes the three raw
 // tokens before token (first + j) * L of q, k and v, in the packed channel
 // order of conv_in; tokens before 0 come from conv_in (zeros if NULL).
-// Elements are copied bit for bit (E: element type of in_dtype).
+// Elements are copied bit for bit (E: element type of in_dtype).  Grid:
+// x over b * nblk + j, y over pieces of kHistPiece elements of the 3 x Cch rows.
+constexpr int kHistPiece = 4 * kThreads;
+
 template <typename E>
 __global__ __launch_bounds__(kThreads) void cp_history_kernel(const E* q, const E* k, const E* v, const E* conv_in,
                                                               E* dst, int nblk, int first, int L, int T, int H,
@@ -146,7 +149,10 @@ __global__ __launch_bounds__(kThreads) void cp_history_kernel(const E* q, const 
   const int hd = H * d;
   const int cch = 3 * hd;
   const long long t0 = (long long)(first + j) * L - 3;
-  for (int idx = threadIdx.x; idx < 3 * cch; idx += kThreads) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int idx = blockIdx.y * kHistPiece + e * kThreads + threadIdx.x;
+    if (idx >= 3 * cch) break;
     const int row = idx / cch, c = idx - row * cch;
     const long long t = t0 + row;
     E val;
@@ -185,14 +191,20 @@ int launch_cp_compose(const kda_cp_compose_args& a, hipStream_t s) {
 }
 
 int launch_cp_history(const kda_prefill_args& a, int nblk, int first, int L, void* dst, hipStream_t s) {
-  const unsigned grid = (unsigned)((size_t)a.B * nblk);
+  const size_t rows = 3 * (size_t)a.H * (2 * a.dk + a.dv);
+  const size_t pieces = (rows + kHistPiece - 1) / kHistPiece;
+  if (pieces > 65535) {
+    set_error("context-parallel history: %zu channels too many", rows / 3);
+    return KDA_E_SHAPE;
+  }
+  const dim3 grid((unsigned)((size_t)a.B * nblk), (unsigned)pieces);
   if (a.in_dtype == KDA_BF16)
-    hipLaunchKernelGGL(cp_history_kernel<uint16_t>, dim3(grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(cp_history_kernel<uint16_t>, grid, dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                        static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.conv_in),
                        static_cast<uint16_t*>(dst), nblk, first, L, a.T, a.H, a.dk);
   else
-    hipLaunchKernelGGL(cp_history_kernel<uint32_t>, dim3(grid), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(cp_history_kernel<uint32_t>, grid, dim3(kThreads), 0, s,
                        static_cast<const uint32_t*>(a.q), static_cast<const uint32_t*>(a.k),
                        static_cast<const uint32_t*>(a.v), static_cast<const uint32_t*>(a.conv_in),
                        static_cast<uint32_t*>(dst), nblk, first, L, a.T, a.H, a.dk);
