@@ -1,6 +1,6 @@
 """Summaries of rocprofv3 CSV output for the KDA kernels.
 
-    python -m gated_delta_rule_28_amd.profsum stats  KERNEL_STATS_CSV [--trace KERNEL_TRACE_CSV --prefill-calls N] --cmd "..." --out FILE.md
+    python -m gated_delta_rule_28_amd.profsum stats  KERNEL_STATS_CSV [--trace KERNEL_TRACE_CSV --prefill-calls N] [--top K] --cmd "..." --out FILE.md
     python -m gated_delta_rule_28_amd.profsum traffic FETCH_CSV WRITE_CSV [--prefill-calls N] --cmd "..." --out FILE.md
     python -m gated_delta_rule_28_amd.profsum counters COUNTER_CSV --cmd "..." --out FILE.md
 
@@ -63,14 +63,14 @@ def call_spans(trace, calls):
     return spans, per
 
 
-def stats(path, cmd, out, trace=None, calls=0):
+def stats(path, cmd, out, trace=None, calls=0, top=8):
     rows = list(csv.DictReader(open(path)))
     rows.sort(key=lambda r: -float(r["TotalDurationNs"]))
     lines = ["# Kernel time (rocprofv3 --kernel-trace --stats)", "", "Command:", "",
              "```", cmd, "```", "",
              "| kernel | calls | average (us) | min (us) | max (us) | share of GPU time |",
              "|---|---:|---:|---:|---:|---:|"]
-    for r in rows[:8]:
+    for r in rows[:top]:
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     if trace:
@@ -183,6 +183,7 @@ def main():
     a = sub.add_parser("stats")
     a.add_argument("csv")
     a.add_argument("--trace", default=None)
+    a.add_argument("--top", type=int, default=8, help="kernels listed (by total time)")
     b = sub.add_parser("traffic")
     b.add_argument("fetch_csv")
     b.add_argument("write_csv")
@@ -196,7 +197,7 @@ def main():
         p.add_argument("--prefill-calls", type=int, default=0)
     args = ap.parse_args()
     if args.what == "stats":
-        stats(args.csv, args.cmd, args.out, args.trace, args.prefill_calls)
+        stats(args.csv, args.cmd, args.out, args.trace, args.prefill_calls, args.top)
     elif args.what == "traffic":
         traffic(args.fetch_csv, args.write_csv, args.cmd, args.out, args.json, args.prefill_calls)
     else:
