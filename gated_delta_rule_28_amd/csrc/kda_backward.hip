@@ -3,7 +3,7 @@
 // row), for the definition of "Kimi K3, previewed", section "Kimi Delta
 // Attention - the workhorse" and the KDA rows of the component tables.
 //
-// One workgroup per (b, h), token by token, all in fp32:
+// One workgroup per (b, h) (256 or 512 threads by head dim), token by token, all in fp32:
 //   1. forward: the recurrence over the whole sequence, storing the state at
 //      every chunk start (kBwdChunk tokens) in the workspace;
 //   2. the chunks in reverse: each is recomputed from its stored state (the
@@ -27,8 +27,15 @@ namespace kda {
 
 namespace {
 
-constexpr int kBwdThreads = 256;
 constexpr int kBwdChunk = 64;  // tokens between stored states
+
+// Threads per workgroup: eight state rows per thread at d = 128 (512 threads,
+// 8 waves), so each SIMD has two waves to hide latency with (1024 threads
+// would need more than the 128 registers four waves allow).
+template <int D>
+constexpr int bwd_threads() {
+  return D >= 64 ? 512 : 256;
+}
 
 struct BwdParams {
   int B, T, H;
@@ -70,20 +77,23 @@ __host__ __device__ constexpr size_t bwd_head_floats(int T) {
   return (nch + kBwdChunk) * D * D + (size_t)kBwdChunk * Rec<D>::SIZE;
 }
 
-// Barriers are LDS-only (lds_barrier): threads exchange data through LDS only,
-// and each thread reads back only the workspace data it wrote itself, so
-// global loads issued ahead (the next token's raw inputs and record) stay in
-// flight across them.
+// Barriers are LDS-only (lds_barrier) wherever threads exchange data through
+// LDS only, so global loads issued ahead (the next token's raw inputs and
+// record) stay in flight across them.  The one exchange through the workspace
+// (each token's record, written by the threads that hold each value and read
+// back in another mapping) is ordered by a full barrier after each stretch's
+// recompute.
 template <int D, bool IB>
-__global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
+__global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p) {
+  constexpr int NT = bwd_threads<D>();
   constexpr int NC = 3 * D;
-  constexpr int NCT = (NC + kBwdThreads - 1) / kBwdThreads;  // conv channels per thread
+  constexpr int NCT = (NC + NT - 1) / NT;  // conv channels per thread
   constexpr int CG = D / 4;
-  constexpr int RG0 = kBwdThreads / CG;
+  constexpr int RG0 = NT / CG;
   constexpr int RG = RG0 < D ? RG0 : D;
   constexpr int RPT = D / RG;
   using V = Rec<D>;
-  constexpr int NPRE = (V::SIZE + kBwdThreads - 1) / kBwdThreads;  // record floats per thread
+  constexpr int NPRE = (V::SIZE + NT - 1) / NT;  // record floats per thread
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -124,115 +134,174 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
     return load1<IB>(src, rowidx(t) * D + (c % D));
   };
 
-  // this thread's conv channels c = tid + 256 j: taps, raw window t-3..t-1, raw t
+  // this thread's conv channels c = tid + NT j: taps, the raw window t-3..t-1,
+  // and a FIFO of the raw values, g (channel tid) and beta of tokens t..t+PF-1,
+  // requested PF tokens before they are used (deeper measured slower)
+  constexpr int PF = 1;
   float4 wch[NCT];
-  float win[NCT][3], rnext[NCT];
+  float win[NCT][3], rq[PF][NCT], gq[PF], bq[PF];
 #pragma unroll
   for (int j = 0; j < NCT; ++j) {
-    const int c = tid + kBwdThreads * j;
+    const int c = tid + NT * j;
     wch[j] = c < NC ? *reinterpret_cast<const float4*>(p.conv_w + (size_t)gch(c) * 4) : make_float4(0.f, 0.f, 0.f, 0.f);
   }
-  float gnext = 0.f, bnext = 0.f;  // g(t) of channel tid, beta(t)
-  auto start_window = [&](int t) {  // the raw window and the prefetch for token t
+  auto request = [&](int t, int k) {  // FIFO slot k <- token t
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
-      const int c = tid + kBwdThreads * j;
+      const int c = tid + NT * j;
+      if (c < NC) rq[k][j] = raw(t, c);
+    }
+    gq[k] = tid < D && t < T ? load1<IB>(p.g, rowidx(t) * D + tid) : 0.f;
+    bq[k] = t < T ? load1<IB>(p.beta, rowidx(t)) : 0.f;
+  };
+  auto start_window = [&](int t) {  // the raw window and the FIFO for token t
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + NT * j;
       if (c < NC) {
         win[j][0] = raw(t - 3, c);
         win[j][1] = raw(t - 2, c);
         win[j][2] = raw(t - 1, c);
-        rnext[j] = raw(t, c);
       }
     }
-    gnext = tid < D && t < T ? load1<IB>(p.g, rowidx(t) * D + tid) : 0.f;
-    bnext = tid == 0 && t < T ? load1<IB>(p.beta, rowidx(t)) : 0.f;
-  };
-
-  // token t's vectors into R (xa, xs, al, qn, kn, sc[0..5]); the raw inputs of
-  // token t + 1 are requested before the first barrier
-  auto token_vectors = [&](int t) {
 #pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int c = tid + kBwdThreads * j;
-      if (c < NC) {
-        const float4 w = wch[j];
-        const float a = w.x * win[j][0] + w.y * win[j][1] + w.z * win[j][2] + w.w * rnext[j];
-        xa[c] = a;
-        xs[c] = a * sigmoidf_(a);
-        win[j][0] = win[j][1];
-        win[j][1] = win[j][2];
-        win[j][2] = rnext[j];
-        rnext[j] = raw(t + 1, c);
-      }
-    }
-    if (tid < D) al[tid] = __expf(gnext);
-    if (tid == 0) sc[5] = bnext;
-    gnext = tid < D && t + 1 < T ? load1<IB>(p.g, rowidx(t + 1) * D + tid) : 0.f;
-    bnext = tid == 0 && t + 1 < T ? load1<IB>(p.beta, rowidx(t + 1)) : 0.f;
-    lds_barrier();
-    if (tid < 64) {
-      float sq = 0.f, sk = 0.f;
-      for (int c = tid; c < D; c += 64) {
-        sq += xs[c] * xs[c];
-        sk += xs[D + c] * xs[D + c];
-      }
-      sq = group_sum<64>(sq);
-      sk = group_sum<64>(sk);
-      if (tid == 0) {
-        const float nq = sq + kL2Eps, nk = sk + kL2Eps;
-        sc[0] = nq;
-        sc[1] = nk;
-        sc[2] = rsqrtf(nq) * rsqrtf((float)D);
-        sc[3] = rsqrtf(nk);
-      }
-    }
-    lds_barrier();
-    for (int c = tid; c < D; c += kBwdThreads) {
-      qn[c] = xs[c] * sc[2];
-      kn[c] = xs[D + c] * sc[3];
-    }
-    lds_barrier();
+    for (int k = 0; k < PF; ++k) request(t + k, k);
   };
 
   // column sums over the rows of this thread's column group: part -> out[D]
   auto colsum = [&](const f4& part, float* out) {
     if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = part;
     lds_barrier();
-    for (int c = tid; c < D; c += kBwdThreads) {
+    for (int c = tid; c < D; c += NT) {
       float sum = 0.f;
+#pragma unroll 4
       for (int r = 0; r < RG; ++r) sum += red[r][c];
       out[c] = sum;
     }
     lds_barrier();
   };
 
-  // one forward token on the register state s[]: S' = Diag(al) S, y, u, S_t
-  // (and z when want_z); leaves yv, uv (and zv) in R
+  // Forward-pass exchange buffers, double-buffered by token parity: a token
+  // has at least two barriers, so token t + 2 rewrites a buffer only after
+  // every thread has passed token t + 1's first barrier, i.e. has finished
+  // reading token t's.
+  __shared__ float fx[2][NC];                                   // x~
+  __shared__ float fal[2][D];                                   // alpha = e^g
+  __shared__ float fn[2][NT / 64][2];                  // per-wave |q~|^2, |k~|^2
+  __shared__ __attribute__((aligned(16))) float fy[2][RG][D];   // row-group partials of y
+  __shared__ __attribute__((aligned(16))) float fz[2][RG][D];   // row-group partials of z
+
+  // One forward token t on the register state s[]: conv + SiLU, the L2 norms,
+  // S' = Diag(alpha) S, y = S'^T k^, u = beta (v^ - y), S_t = S' + k^ u^T.
+  // Every thread derives the norms from the per-wave partials and sums y (and
+  // z) for its own columns, so a token needs two barriers (three with z).
+  // With vt, the token's record is written straight from the threads that
+  // hold each value.
   f4 s[RPT];
-  auto forward_token = [&](bool want_z) {
+  auto forward_step = [&](int t, float* vt) {
+    const int u = t & 1;
+    float pq = 0.f, pk = 0.f;
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + NT * j;
+      if (c < NC) {
+        const float4 w = wch[j];
+        const float a = w.x * win[j][0] + w.y * win[j][1] + w.z * win[j][2] + w.w * rq[0][j];
+        const float x = a * sigmoidf_(a);
+        fx[u][c] = x;
+        if (vt != nullptr) {
+          vt[V::A + c] = a;
+          vt[V::X + c] = x;
+        }
+        if (c < D) pq += x * x;
+        else if (c < 2 * D) pk += x * x;
+        win[j][0] = win[j][1];
+        win[j][1] = win[j][2];
+        win[j][2] = rq[0][j];
+      }
+    }
+    if (tid < D) fal[u][tid] = __expf(gq[0]);
+    const float beta_t = bq[0];
+#pragma unroll
+    for (int k = 0; k + 1 < PF; ++k) {
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) rq[k][j] = rq[k + 1][j];
+      gq[k] = gq[k + 1];
+      bq[k] = bq[k + 1];
+    }
+    request(t + PF, PF - 1);
+    pq = group_sum<64>(pq);
+    pk = group_sum<64>(pk);
+    if ((tid & 63) == 0) {
+      fn[u][tid >> 6][0] = pq;
+      fn[u][tid >> 6][1] = pk;
+    }
+    lds_barrier();
+    float nq = kL2Eps, nk = kL2Eps;
+#pragma unroll
+    for (int wv = 0; wv < NT / 64; ++wv) {
+      nq += fn[u][wv][0];
+      nk += fn[u][wv][1];
+    }
+    const float rq = rsqrtf(nq) * rsqrtf((float)D), rk = rsqrtf(nk);
     f4 yp = f4{0.f, 0.f, 0.f, 0.f};
     if (active) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        s[i] *= al[r];
-        yp += s[i] * kn[r];
+        s[i] *= fal[u][r];
+        yp += s[i] * (fx[u][D + r] * rk);
       }
+      *reinterpret_cast<f4*>(&fy[u][rg][4 * cg]) = yp;
     }
-    colsum(yp, yv);
-    for (int c = tid; c < D; c += kBwdThreads) uv[c] = sc[5] * (xs[2 * D + c] - yv[c]);
     lds_barrier();
-    f4 zp = f4{0.f, 0.f, 0.f, 0.f};
     if (active) {
-      const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
+      f4 y = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+      for (int r = 0; r < RG; ++r) y += *reinterpret_cast<const f4*>(&fy[u][r][4 * cg]);
+      const f4 v4 = f4{fx[u][2 * D + 4 * cg], fx[u][2 * D + 4 * cg + 1], fx[u][2 * D + 4 * cg + 2],
+                       fx[u][2 * D + 4 * cg + 3]};
+      const f4 uu = beta_t * (v4 - y);
+      f4 zp = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const int r = rg + RG * i;
-        s[i] += u * kn[r];
-        zp += s[i] * qn[r];
+        s[i] += uu * (fx[u][D + r] * rk);
+        zp += s[i] * (fx[u][r] * rq);
+      }
+      if (vt != nullptr) {
+        *reinterpret_cast<f4*>(&fz[u][rg][4 * cg]) = zp;
+        if (rg == 0) {
+          *reinterpret_cast<f4*>(vt + V::Y + 4 * cg) = y;
+          *reinterpret_cast<f4*>(vt + V::U + 4 * cg) = uu;
+        }
+        if (cg == 0) {
+#pragma unroll
+          for (int i = 0; i < RPT; ++i) {
+            const int r = rg + RG * i;
+            vt[V::QN + r] = fx[u][r] * rq;
+            vt[V::KN + r] = fx[u][D + r] * rk;
+            vt[V::AL + r] = fal[u][r];
+          }
+        }
       }
     }
-    if (want_z) colsum(zp, zv);
+    if (vt != nullptr) {
+      if (tid == 0) {
+        vt[V::SC + 0] = nq;
+        vt[V::SC + 1] = nk;
+        vt[V::SC + 2] = rq;
+        vt[V::SC + 3] = rk;
+        vt[V::SC + 5] = beta_t;
+      }
+      lds_barrier();
+      if (active && rg == 0) {
+        f4 z = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int r = 0; r < RG; ++r) z += *reinterpret_cast<const f4*>(&fz[u][r][4 * cg]);
+        *reinterpret_cast<f4*>(vt + V::Z + 4 * cg) = z;
+      }
+    }
   };
 
   // ---- 1. forward over the sequence, the state at every chunk start ----------
@@ -251,8 +320,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i) *reinterpret_cast<f4*>(dst + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
     }
-    token_vectors(t);
-    forward_token(false);
+    forward_step(t, nullptr);
   }
 
   // ---- 2. the chunks in reverse ---------------------------------------------------
@@ -278,39 +346,68 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
       for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
     }
     start_window(t0);
+    // gate and dL/do are requested a token ahead: loads and stores share one
+    // in-order counter, so a load waited for right after stores waits for them
+    float gate_n = tid < D ? load1<IB>(p.gate, rowidx(t0) * D + tid) : 0.f;
+    float do_n = tid < D ? p.dO[rowidx(t0) * D + tid] : 0.f;
     for (int t = t0; t < t1; ++t) {
+      float* vt = rec + (size_t)(t - t0) * V::SIZE;
+      const float gate_t = gate_n, do_t = do_n;
+      if (tid < D && t + 1 < t1) {
+        gate_n = load1<IB>(p.gate, rowidx(t + 1) * D + tid);
+        do_n = p.dO[rowidx(t + 1) * D + tid];
+      }
       if (active) {
         float* dst = st + (size_t)(t - t0) * D * D;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) *reinterpret_cast<f4*>(dst + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
       }
-      const float gt = tid < D ? load1<IB>(p.gate, rowidx(t) * D + tid) : 0.f;
-      const float dov = tid < D ? p.dO[rowidx(t) * D + tid] : 0.f;
-      token_vectors(t);
-      forward_token(true);
       if (tid < D) {
-        R[V::SG + tid] = sigmoidf_(gt);
-        R[V::DO + tid] = dov;
+        vt[V::SG + tid] = sigmoidf_(gate_t);
+        vt[V::DO + tid] = do_t;
       }
-      lds_barrier();
-      float* vt = rec + (size_t)(t - t0) * V::SIZE;
-      for (int i = tid; i < V::SIZE; i += kBwdThreads) vt[i] = R[i];
-      lds_barrier();  // R is rewritten by the next token
+      forward_step(t, vt);
     }
+    // The records were written by the threads that hold each value, and are
+    // read below in another mapping: a full barrier (with its memory fence).
+    __syncthreads();
     // reverse, the next token's record requested one token ahead
     float pre[NPRE];
     {
       const float* vt = rec + (size_t)(t1 - 1 - t0) * V::SIZE;
 #pragma unroll
       for (int j = 0; j < NPRE; ++j) {
-        const int i = tid + kBwdThreads * j;
+        const int i = tid + NT * j;
         pre[j] = i < V::SIZE ? vt[i] : 0.f;
       }
     }
+    // A token's gradients are stored after the next token's loads are issued
+    // (the counter is in order), so the store latency stays off the chain.
+    int t_def = -1;
+    float dgate_def[(D + 63) / 64], dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
+    auto flush = [&]() {
+      if (t_def < 0) return;
+      const size_t rw = rowidx(t_def);
+      if (tid < 64) {
+#pragma unroll
+        for (int k2 = 0; k2 < (D + 63) / 64; ++k2)
+          if (tid + 64 * k2 < D) p.dgate[rw * D + tid + 64 * k2] = dgate_def[k2];
+      }
+      if (tid == 0) p.dbeta[rw] = dbeta_def;
+      if (active && cg == 0) {
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
+      }
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        const int c = tid + NT * j;
+        if (c < NC) (c < D ? p.dq : c < 2 * D ? p.dk : p.dv)[rw * D + (c % D)] = dx_def[j];
+      }
+    };
     for (int t = t1 - 1; t >= t0; --t) {
 #pragma unroll
       for (int j = 0; j < NPRE; ++j) {
-        const int i = tid + kBwdThreads * j;
+        const int i = tid + NT * j;
         if (i < V::SIZE) R[i] = pre[j];
       }
       f4 prev[RPT];
@@ -323,10 +420,12 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         const float* vt = rec + (size_t)(t - 1 - t0) * V::SIZE;
 #pragma unroll
         for (int j = 0; j < NPRE; ++j) {
-          const int i = tid + kBwdThreads * j;
+          const int i = tid + NT * j;
           pre[j] = i < V::SIZE ? vt[i] : 0.f;
         }
       }
+      flush();  // token t + 1's gradients
+      t_def = t;
       lds_barrier();
       // output side: r, dgate, dz
       if (tid < 64) {
@@ -335,11 +434,15 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         zz = group_sum<64>(zz);
         const float r = sqrtf(zz * (1.0f / D) + kRmsEps);
         float dd = 0.f;
-        for (int c = tid; c < D; c += 64) {
-          const float n = zv[c] / r;
-          const float sg = R[V::SG + c], dov = R[V::DO + c];
-          p.dgate[rowidx(t) * D + c] = dov * n * sg * (1.f - sg);
-          dd += dov * sg * n;
+#pragma unroll
+        for (int k2 = 0; k2 < (D + 63) / 64; ++k2) {
+          const int c = tid + 64 * k2;
+          if (c < D) {
+            const float n = zv[c] / r;
+            const float sg = R[V::SG + c], dov = R[V::DO + c];
+            dgate_def[k2] = dov * n * sg * (1.f - sg);
+            dd += dov * sg * n;
+          }
         }
         dd = group_sum<64>(dd) * (1.0f / D);
         for (int c = tid; c < D; c += 64) dzs[c] = (R[V::DO + c] * R[V::SG + c] - zv[c] / r * dd) / r;
@@ -374,9 +477,9 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
         float db = 0.f;
         for (int c = tid; c < D; c += 64) db += dus[c] * (xs[2 * D + c] - yv[c]);
         db = group_sum<64>(db);
-        if (tid == 0) p.dbeta[rowidx(t)] = db;
+        dbeta_def = db;
       }
-      for (int c = tid; c < D; c += kBwdThreads) dys[c] = -sc[5] * dus[c];
+      for (int c = tid; c < D; c += NT) dys[c] = -sc[5] * dus[c];
       lds_barrier();
       if (active) {
         const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
@@ -391,10 +494,8 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
           float gp = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
           kp = group_sum<CG>(kp);
           gp = group_sum<CG>(gp);
-          if (cg == 0) {
-            dkn[r] = kp;
-            p.dg[rowidx(t) * D + r] = gp;  // rowsum(dS' * S'): alpha is inside S'
-          }
+          if (cg == 0) dkn[r] = kp;
+          dg_def[i] = gp;  // rowsum(dS' * S'): alpha is inside S'
           dS[i] *= al[r];  // dS_{t-1}
         }
       }
@@ -416,7 +517,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
       lds_barrier();
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
-        const int c = tid + kBwdThreads * j;
+        const int c = tid + NT * j;
         if (c < NC) {
           float dx;
           if (c < D) dx = sc[2] * (dqn[c] - xs[c] * sc[6] / sc[0]);
@@ -427,8 +528,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
           const float da = dx * sa * (1.f + a * (1.f - sa));
           const float4 w = wch[j];
           const float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
-          float* dst = c < D ? p.dq : c < 2 * D ? p.dk : p.dv;
-          dst[rowidx(t) * D + (c % D)] = dr;
+          dx_def[j] = dr;
           ring[j][2] = ring[j][1];
           ring[j][1] = ring[j][0];
           ring[j][0] = da;
@@ -436,6 +536,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
       }
       lds_barrier();  // R, dqn, dkn, dus are rewritten by the next token
     }
+    flush();
   }
 
   // ---- 3. state and history gradients ------------------------------------------------
@@ -448,7 +549,7 @@ __global__ __launch_bounds__(kBwdThreads) void backward_kernel(BwdParams p) {
     // history row s + 3 (token s = -3..-1): sum over t = 0 .. s + 3 of w_{s-t+3} da_t
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
-      const int c = tid + kBwdThreads * j;
+      const int c = tid + NT * j;
       if (c < NC) {
         const float4 w = wch[j];
         const float wj[4] = {w.x, w.y, w.z, w.w};
@@ -469,9 +570,9 @@ int run_backward(const kda_prefill_backward_args& a, hipStream_t s) {
               a.grad_conv_in, static_cast<float*>(a.workspace)};
   const unsigned grid = (unsigned)((size_t)a.B * a.H);
   if (a.in_dtype == KDA_BF16)
-    hipLaunchKernelGGL((backward_kernel<D, true>), dim3(grid), dim3(kBwdThreads), 0, s, p);
+    hipLaunchKernelGGL((backward_kernel<D, true>), dim3(grid), dim3(bwd_threads<D>()), 0, s, p);
   else
-    hipLaunchKernelGGL((backward_kernel<D, false>), dim3(grid), dim3(kBwdThreads), 0, s, p);
+    hipLaunchKernelGGL((backward_kernel<D, false>), dim3(grid), dim3(bwd_threads<D>()), 0, s, p);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) {
     set_error("backward launch failed: %s", hipGetErrorString(e));
