@@ -236,7 +236,14 @@ def time_context_parallel(torch, kda, w, inp, R, A, steps):
     rper = timed_launches(torch, rank, steps)
     rms = sum(rper) / len(rper)
     log(f"[bench] one rank's share ({L} tokens, {R} fragments composed): {rms:.3f} ms")
+    nbytes_alg = prefill_bytes_per_launch(w.B, w.T, w.H, w.dk, w.dv)
+    gbs = nbytes_alg / (ms * 1e-3) / 1e9
     return {"segments": R, "ms_per_call": ms, "tokens_per_s": w.B * w.T / (ms * 1e-3), "calls_timed": steps,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "algorithmic_bytes_per_launch": nbytes_alg,
+                         "note": "the prefill's algorithmic bytes; on one GPU the call runs all three passes "
+                                 "of every segment"},
             "config": f"kda_prefill_cp of the {w.name} workload in {R} segments of {L} tokens on one GPU: "
                       "three prefill passes over all segments and the composition",
             "rank_share_ms": rms,

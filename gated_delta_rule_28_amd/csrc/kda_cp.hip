@@ -68,6 +68,21 @@ __global__ __launch_bounds__(ComposeShape<D>::THREADS) void cp_compose_kernel(Co
                                      : make_float4(0.f, 0.f, 0.f, 0.f);
     *reinterpret_cast<float4*>(sX + i * LDX + j) = x;
   }
+  // P and N of segment r + 1 are requested while segment r's product runs
+  constexpr int NQ = (D * D / 4 + NT - 1) / NT;  // float4 pieces per thread
+  float4 pv[NQ], nv[NQ];
+  auto request = [&](int r) {
+    const size_t seg = ((size_t)(b * p.R + r) * p.H + h) * DD;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int idx = tid + NT * q;
+      if (idx < D * D / 4) {
+        pv[q] = *reinterpret_cast<const float4*>(p.P + seg + 4 * (size_t)idx);
+        nv[q] = *reinterpret_cast<const float4*>(p.N + seg + 4 * (size_t)idx);
+      }
+    }
+  };
+  request(0);
   for (int r = 0; r < p.R; ++r) {
     const size_t seg = ((size_t)(b * p.R + r) * p.H + h) * DD;
     __syncthreads();  // X complete
@@ -76,14 +91,17 @@ __global__ __launch_bounds__(ComposeShape<D>::THREADS) void cp_compose_kernel(Co
       *reinterpret_cast<float4*>(p.S_start + seg + (size_t)i * D + c0 + j) =
           *reinterpret_cast<const float4*>(sX + i * LDX + j);
     }
-    for (int idx = tid; idx < D * D / 4; idx += NT) {
-      const int i = (4 * idx) / D, j = 4 * idx - i * D;
-      const float4 pv = *reinterpret_cast<const float4*>(p.P + seg + 4 * (size_t)idx);
-      const float4 nv = *reinterpret_cast<const float4*>(p.N + seg + 4 * (size_t)idx);
-      float* m = sM + i * LDM + j;
-      m[0] = pv.x - nv.x; m[1] = pv.y - nv.y; m[2] = pv.z - nv.z; m[3] = pv.w - nv.w;
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      const int idx = tid + NT * q;
+      if (idx < D * D / 4) {
+        const int i = (4 * idx) / D, j = 4 * idx - i * D;
+        float* m = sM + i * LDM + j;
+        m[0] = pv[q].x - nv[q].x; m[1] = pv[q].y - nv[q].y; m[2] = pv[q].z - nv[q].z; m[3] = pv[q].w - nv[q].w;
+      }
     }
     __syncthreads();  // map complete
+    if (r + 1 < p.R) request(r + 1);
     float acc[TR][TB];
 #pragma unroll
     for (int u = 0; u < TR; ++u)
