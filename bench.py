@@ -158,6 +158,13 @@ def time_backward(torch, kda, w, inp, steps):
     """kda_prefill_backward over the whole workload (all T tokens of each
     sequence), random fp32 output and final-state gradients."""
     dev = inp["q"].device
+    # fp32 gradients of q, k, v, g, gate, grad_o, and the workspace
+    need = 6 * w.B * w.T * w.H * w.dk * 4 + kda.backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
+    free, _ = torch.cuda.mem_get_info(dev)
+    if need > 0.9 * free:
+        log(f"[bench] backward skipped: needs {need / 2**30:.0f} GiB, {free / 2**30:.0f} GiB free "
+            "(a sequence this long takes segment-wise backward calls)")
+        return {"skipped": f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} GiB free"}
     gen = torch.Generator(device=dev)
     gen.manual_seed(7)
     go = torch.randn((w.B, w.T, w.H, w.dv), generator=gen, device=dev)
