@@ -16,7 +16,9 @@ gpt-oss-120b" and "Gemma 4 31B vs Kimi K3", rows "Gated DeltaNet / KDA" and
 
 `prefill_torch` must equal `oracle.prefill` (pinned), so autograd differentiates
 the same function.  Gradients are taken with respect to the exact input values
-(bf16 inputs are their bf16 values), for a loss <dO, o> + <dS_T, S_T>.
+(bf16 inputs are their bf16 values), for a loss <dO, o> + <dS_T, S_T> +
+<dconv_out, conv_out>: the last two terms carry a later segment's gradient
+into this one when a long sequence is processed in segments.
 Direct decay form only (g is the log-decay, beta in [0, 1]).
 """
 from __future__ import annotations
@@ -44,9 +46,10 @@ def _head_channels(H, dk, dv, h):
                            2 * H * dk + h * dv + np.arange(dv)])
 
 
-def prefill_torch(q, k, v, conv_w, g, beta, gate, S0, conv_in):
+def prefill_torch(q, k, v, conv_w, g, beta, gate, S0, conv_in, want_conv_out=False):
     """The prefill in float64 torch ops on [B,T,H,.] tensors; conv_w [Cch,4],
-    S0 [B,H,dk,dv], conv_in [B,3,Cch].  Returns (o [B,T,H,dv], S_T [B,H,dk,dv])."""
+    S0 [B,H,dk,dv], conv_in [B,3,Cch].  Returns (o [B,T,H,dv], S_T [B,H,dk,dv]),
+    and conv_out [B,3,Cch] (the last three raw rows) when want_conv_out."""
     torch = _torch()
     B, T, H, dk = q.shape
     dv = v.shape[3]
@@ -71,7 +74,15 @@ def prefill_torch(q, k, v, conv_w, g, beta, gate, S0, conv_in):
         z = torch.einsum("bhij,bhi->bhj", S, qn[:, t])
         rms = torch.sqrt((z * z).mean(-1, keepdim=True) + RMS_EPS)
         outs.append(z / rms * torch.sigmoid(gate[:, t]))
-    return torch.stack(outs, dim=1), S
+    if not want_conv_out:
+        return torch.stack(outs, dim=1), S
+    # last three raw rows of history + tokens, back in the packed channel order
+    last = full[:, T:T + 3]                                       # [B,3,H,nc]
+    cch = H * nc
+    conv_out = torch.zeros((B, 3, cch), dtype=last.dtype)
+    for h in range(H):
+        conv_out = conv_out.index_add(2, torch.as_tensor(_head_channels(H, dk, dv, h)), last[:, :, h])
+    return torch.stack(outs, dim=1), S, conv_out
 
 
 def _leaves(inp, B, H, dk, dv):
@@ -96,35 +107,42 @@ def forward(inp: dict) -> dict:
     if inp.get("A") is not None:
         raise ValueError("the backward reference covers the direct decay form only")
     vals = _leaves(inp, B, H, dk, dv)
-    o, S_T = prefill_torch(vals["q"], vals["k"], vals["v"], vals["conv_w"], vals["g"], vals["beta"],
-                           vals["gate"], vals["S0"], vals["conv_in"])
-    return {"o": o.detach().numpy(), "S_T": S_T.detach().numpy()}
+    o, S_T, conv_out = prefill_torch(vals["q"], vals["k"], vals["v"], vals["conv_w"], vals["g"], vals["beta"],
+                                     vals["gate"], vals["S0"], vals["conv_in"], want_conv_out=True)
+    return {"o": o.detach().numpy(), "S_T": S_T.detach().numpy(), "conv_out": conv_out.detach().numpy()}
 
 
-def backward(inp: dict, dO, dS_T=None) -> dict:
-    """Gradients of <dO, o> + <dS_T, S_T> with respect to q, k, v, g, beta, gate,
-    S0 and conv_in (all float64, shapes of the inputs)."""
+def backward(inp: dict, dO, dS_T=None, dconv_out=None) -> dict:
+    """Gradients of <dO, o> + <dS_T, S_T> + <dconv_out, conv_out> with respect to
+    q, k, v, g, beta, gate, S0 and conv_in (all float64, shapes of the inputs);
+    conv_out is the last three raw rows [B, 3, Cch]."""
     torch = _torch()
     B, T, H, dk = inp["q"].shape
     dv = inp["v"].shape[3]
     if inp.get("A") is not None:
         raise ValueError("the backward reference covers the direct decay form only")
     vals = _leaves(inp, B, H, dk, dv)
-    o, S_T = prefill_torch(vals["q"], vals["k"], vals["v"], vals["conv_w"], vals["g"], vals["beta"],
-                           vals["gate"], vals["S0"], vals["conv_in"])
+    o, S_T, conv_out = prefill_torch(vals["q"], vals["k"], vals["v"], vals["conv_w"], vals["g"], vals["beta"],
+                                     vals["gate"], vals["S0"], vals["conv_in"], want_conv_out=True)
     outs, gouts = [o], [torch.tensor(np.asarray(dO, dtype=np.float64))]
     if dS_T is not None:
         outs.append(S_T)
         gouts.append(torch.tensor(np.asarray(dS_T, dtype=np.float64)))
+    if dconv_out is not None:
+        outs.append(conv_out)
+        gouts.append(torch.tensor(np.asarray(dconv_out, dtype=np.float64)))
     names = ["q", "k", "v", "g", "beta", "gate", "S0", "conv_in"]
     grads = torch.autograd.grad(outs, [vals[x] for x in names], gouts, allow_unused=True)
     return {x: (np.zeros(vals[x].shape) if gr is None else gr.numpy()) for x, gr in zip(names, grads)}
 
 
-def loss(inp: dict, dO, dS_T=None) -> float:
-    """<dO, o> + <dS_T, S_T> at these inputs (float64), for finite differences."""
+def loss(inp: dict, dO, dS_T=None, dconv_out=None) -> float:
+    """<dO, o> + <dS_T, S_T> + <dconv_out, conv_out> at these inputs (float64),
+    for finite differences."""
     r = forward(inp)
     val = float(np.sum(np.asarray(dO, dtype=np.float64) * r["o"]))
     if dS_T is not None:
         val += float(np.sum(np.asarray(dS_T, dtype=np.float64) * r["S_T"]))
+    if dconv_out is not None:
+        val += float(np.sum(np.asarray(dconv_out, dtype=np.float64) * r["conv_out"]))
     return val
