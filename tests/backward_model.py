@@ -33,9 +33,10 @@ def _sig(x):
     return 1.0 / (1.0 + np.exp(-x))
 
 
-def backward_pair(raw, hist, w, g, beta, gate, S0, dO, dS_T, chunk=64):
+def backward_pair(raw, hist, w, g, beta, gate, S0, dO, dS_T, chunk=64, dC=None):
     """One (b, h): raw [T, 3d] raw q|k|v, hist [3, 3d], w [3d, 4], g [T, d],
-    beta [T], gate [T, d], S0 [d, d], dO [T, d], dS_T [d, d] (all float64).
+    beta [T], gate [T, d], S0 [d, d], dO [T, d], dS_T [d, d], dC [3, 3d] the
+    gradient of the last three raw rows (all float64).
     Returns (draw [T, 3d], dhist [3, 3d], dg, dbeta, dgate, dS0)."""
     T, nc = raw.shape
     d = nc // 3
@@ -112,14 +113,20 @@ def backward_pair(raw, hist, w, g, beta, gate, S0, dO, dS_T, chunk=64):
             sa = _sig(tv["a"])
             da = dx * sa * (1 + tv["a"] * (1 - sa))
             draw[t] = w[:, 3] * da + w[:, 2] * ring[0] + w[:, 1] * ring[1] + w[:, 0] * ring[2]
+            if dC is not None and t >= T - 3:
+                draw[t] += dC[t - (T - 3)]
             ring = np.stack([da, ring[0], ring[1]])
     # history rows 0..2 are tokens -3..-1: dx_s = sum over t = 0 .. s + 3 of w_{s-t+3} da_t
     for s in (-1, -2, -3):
         dhist[s + 3] = sum(w[:, s - t + 3] * ring[t] for t in range(0, s + 4))
+    if dC is not None:  # rows of conv_out that are history rows (T < 3)
+        for kk in range(3):
+            if T - 3 + kk < 0:
+                dhist[T + kk] += dC[kk]
     return draw, dhist, dg, dbeta, dgate, dS
 
 
-def backward(inp: dict, dO, dS_T, chunk=64) -> dict:
+def backward(inp: dict, dO, dS_T, chunk=64, dconv_out=None) -> dict:
     """All (b, h) pairs; gradients in the layouts of the inputs (float64)."""
     def f64(a):
         a = np.asarray(a)
@@ -141,9 +148,10 @@ def backward(inp: dict, dO, dS_T, chunk=64) -> dict:
         for h in range(H):
             ch = np.concatenate([h * d + np.arange(d), H * d + h * d + np.arange(d), 2 * H * d + h * d + np.arange(d)])
             raw = np.concatenate([q[b, :, h], k[b, :, h], v[b, :, h]], axis=1)
+            dC = None if dconv_out is None else np.asarray(dconv_out, dtype=np.float64)[b][:, ch]
             draw, dhist, dg, dbeta, dgate, dS0 = backward_pair(raw, ci[b][:, ch], conv_w[ch], g[b, :, h],
                                                                beta[b, :, h], gate[b, :, h], S0[b, h],
-                                                               dO[b, :, h], dS_T[b, h], chunk)
+                                                               dO[b, :, h], dS_T[b, h], chunk, dC)
             out["q"][b, :, h], out["k"][b, :, h], out["v"][b, :, h] = draw[:, :d], draw[:, d:2 * d], draw[:, 2 * d:]
             out["conv_in"][b][:, ch] = dhist
             out["g"][b, :, h], out["beta"][b, :, h], out["gate"][b, :, h] = dg, dbeta, dgate

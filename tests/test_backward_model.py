@@ -22,7 +22,8 @@ def test_reverse_model_equals_autograd(T, chunk, dtype):
     f = ob.forward(inp)
     dO = rng.standard_normal(f["o"].shape)
     dS = rng.standard_normal(f["S_T"].shape)
-    ref = ob.backward(inp, dO, dS)
-    got = bm.backward(inp, dO, dS, chunk=chunk)
+    dC = rng.standard_normal(f["conv_out"].shape)
+    ref = ob.backward(inp, dO, dS, dC)
+    got = bm.backward(inp, dO, dS, chunk=chunk, dconv_out=dC)
     for x in ref:
         assert np.abs(got[x] - ref[x]).max() <= 1e-12 * max(1.0, np.abs(ref[x]).max()), x
