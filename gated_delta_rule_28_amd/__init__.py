@@ -36,7 +36,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
-ABI_VERSION = 4
+ABI_VERSION = 5
 MAX_DECODE_TOKENS = 16
 
 
@@ -97,7 +97,8 @@ class PrefillBackwardArgs(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int), ("dk", ctypes.c_int),
                 ("dv", ctypes.c_int), ("in_dtype", ctypes.c_int), ("q", _P), ("k", _P), ("v", _P),
                 ("conv_w", _P), ("g", _P), ("beta", _P), ("gate", _P), ("S0", _P), ("conv_in", _P),
-                ("grad_o", _P), ("grad_S_T", _P), ("grad_q", _P), ("grad_k", _P), ("grad_v", _P),
+                ("grad_o", _P), ("grad_S_T", _P), ("grad_conv_out", _P), ("grad_q", _P), ("grad_k", _P),
+                ("grad_v", _P),
                 ("grad_g", _P), ("grad_beta", _P), ("grad_gate", _P), ("grad_S0", _P), ("grad_conv_in", _P),
                 ("workspace", _P), ("workspace_bytes", ctypes.c_size_t), ("decay_form", ctypes.c_int),
                 ("A", _P)]
@@ -338,8 +339,9 @@ def backward_workspace_bytes(B, T, H, dk, dv, in_dtype=KDA_BF16):
 
 
 def prefill_backward(q, k, v, conv_w, g, beta, gate, grad_o, S0=None, conv_in=None, grad_S_T=None,
-                     want_state_grad=True, want_conv_grad=True, workspace=None):
-    """Gradients of <grad_o, o> + <grad_S_T, S_T> of `prefill` (kda_prefill_backward).
+                     grad_conv_out=None, want_state_grad=True, want_conv_grad=True, workspace=None):
+    """Gradients of <grad_o, o> + <grad_S_T, S_T> + <grad_conv_out, conv_out> of
+    `prefill` (kda_prefill_backward).
     Returns a dict of fp32 tensors: q, k, v, g, beta, gate (the inputs' shapes),
     S0 [B,H,dk,dv] and conv_in [B,3,Cch] (None when not wanted)."""
     torch = _torch()
@@ -353,9 +355,9 @@ def prefill_backward(q, k, v, conv_w, g, beta, gate, grad_o, S0=None, conv_in=No
     out["conv_in"] = torch.empty((B, 3, H * (2 * dk + dv)), **f) if want_conv_grad else None
     a = PrefillBackwardArgs(B, T, H, dk, dv, _dt(q), _ptr(q), _ptr(k), _ptr(v), _ptr(conv_w), _ptr(g),
                             _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in), _ptr(grad_o), _ptr(grad_S_T),
-                            _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["g"]), _ptr(out["beta"]),
-                            _ptr(out["gate"]), _ptr(out["S0"]), _ptr(out["conv_in"]), None, 0, KDA_DECAY_DIRECT,
-                            None)
+                            _ptr(grad_conv_out), _ptr(out["q"]), _ptr(out["k"]), _ptr(out["v"]), _ptr(out["g"]),
+                            _ptr(out["beta"]), _ptr(out["gate"]), _ptr(out["S0"]), _ptr(out["conv_in"]), None, 0,
+                            KDA_DECAY_DIRECT, None)
     if workspace is None:
         workspace = torch.empty(max(int(lib().kda_prefill_backward_workspace_bytes(ctypes.byref(a))), 16),
                                 dtype=torch.uint8, device=dev)

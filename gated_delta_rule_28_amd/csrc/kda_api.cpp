@@ -283,7 +283,8 @@ int kda_prefill_backward(const kda_prefill_backward_args* a, void* stream) {
   }
   REQUIRE_A16(a->q); REQUIRE_A16(a->k); REQUIRE_A16(a->v); REQUIRE_A16(a->conv_w);
   REQUIRE_A16(a->g); REQUIRE_A16(a->gate); REQUIRE_A16(a->S0); REQUIRE_A16(a->conv_in);
-  REQUIRE_A16(a->grad_o); REQUIRE_A16(a->grad_S_T); REQUIRE_A16(a->grad_q); REQUIRE_A16(a->grad_k);
+  REQUIRE_A16(a->grad_o); REQUIRE_A16(a->grad_S_T); REQUIRE_A16(a->grad_conv_out);
+  REQUIRE_A16(a->grad_q); REQUIRE_A16(a->grad_k);
   REQUIRE_A16(a->grad_v); REQUIRE_A16(a->grad_g); REQUIRE_A16(a->grad_gate); REQUIRE_A16(a->grad_S0);
   REQUIRE_A16(a->grad_conv_in);
   if (a->beta != nullptr && !kda::aligned_n(a->beta, kda::esize(a->in_dtype)))

@@ -50,6 +50,7 @@ struct BwdParams {
   const void* conv_in;
   const float* dO;
   const float* dS_T;
+  const float* dconv_out;  // gradient of the last three raw rows, or null
   float* dq;
   float* dk;
   float* dv;
@@ -527,7 +528,9 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           const float sa = sigmoidf_(a);
           const float da = dx * sa * (1.f + a * (1.f - sa));
           const float4 w = wch[j];
-          const float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
+          float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
+          // the last three tokens are also conv_out's rows
+          if (p.dconv_out != nullptr && t >= T - 3) dr += p.dconv_out[((size_t)b * 3 + (t - (T - 3))) * cch + gch(c)];
           dx_def[j] = dr;
           ring[j][2] = ring[j][1];
           ring[j][1] = ring[j][0];
@@ -556,6 +559,8 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         for (int s3 = 0; s3 < 3; ++s3) {  // s = s3 - 3
           float acc = 0.f;
           for (int t = 0; t <= s3 && t < 3; ++t) acc += wj[s3 - t] * ring[j][t];
+          // with fewer than three tokens, conv_out row s3 - T is this history row
+          if (p.dconv_out != nullptr && s3 - T >= 0) acc += p.dconv_out[((size_t)b * 3 + (s3 - T)) * cch + gch(c)];
           p.dconv_in[((size_t)b * 3 + (size_t)s3) * cch + gch(c)] = acc;
         }
       }
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
 template <int D>
 int run_backward(const kda_prefill_backward_args& a, hipStream_t s) {
   BwdParams p{a.B, a.T, a.H, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S0, a.conv_in, a.grad_o,
-              a.grad_S_T, a.grad_q, a.grad_k, a.grad_v, a.grad_g, a.grad_beta, a.grad_gate, a.grad_S0,
+              a.grad_S_T, a.grad_conv_out, a.grad_q, a.grad_k, a.grad_v, a.grad_g, a.grad_beta, a.grad_gate, a.grad_S0,
               a.grad_conv_in, static_cast<float*>(a.workspace)};
   const unsigned grid = (unsigned)((size_t)a.B * a.H);
   if (a.in_dtype == KDA_BF16)

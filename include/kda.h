@@ -61,7 +61,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 4
+#define KDA_ABI_VERSION 5
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -316,10 +316,14 @@ size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* args);
 /*
  * kda_prefill_backward: gradients of the prefill for training (the long
  * contexts of "Gemma 4 31B vs Kimi K3", component table, long-context training
- * row), for the loss <grad_o, o> + <grad_S_T, S_T> of kda_prefill with the
- * same inputs: grad_q, grad_k, grad_v, grad_g, grad_beta, grad_gate (fp32, the
- * layouts of q, k, v, g, beta, gate), grad_S0 [B,H,dk,dv] and grad_conv_in
- * [B,3,Cch] (fp32, each may be NULL).
+ * row), for the loss <grad_o, o> + <grad_S_T, S_T> + <grad_conv_out, conv_out>
+ * of kda_prefill with the same inputs: grad_q, grad_k, grad_v, grad_g,
+ * grad_beta, grad_gate (fp32, the layouts of q, k, v, g, beta, gate), grad_S0
+ * [B,H,dk,dv] and grad_conv_in [B,3,Cch] (fp32, each may be NULL).  A long
+ * sequence run as carried segments is differentiated segment by segment, the
+ * last first: a segment's grad_S0 and grad_conv_in are the grad_S_T and
+ * grad_conv_out of the segment before it (its S0 and conv_in being that
+ * segment's S_T and conv_out from the forward pass).
  * Gradients are with respect to the input values (bf16 inputs: their bf16
  * values).  Direct decay form only (decay_form KDA_DECAY_DIRECT), dk = dv.
  * Computed in fp32, one workgroup per (b, h): the forward recurrence again
@@ -344,6 +348,8 @@ typedef struct kda_prefill_backward_args {
   const void* conv_in;    /* may be NULL */
   const float* grad_o;    /* dL/do [B,T,H,dv] fp32 */
   const float* grad_S_T;  /* dL/dS_T [B,H,dk,dv] fp32, or NULL (no loss on S_T) */
+  const float* grad_conv_out;  /* dL/dconv_out [B,3,Cch] fp32 (conv_out: the last three raw
+                                  tokens, as kda_prefill writes them), or NULL */
   float* grad_q;
   float* grad_k;
   float* grad_v;

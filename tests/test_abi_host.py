@@ -243,12 +243,13 @@ def test_prefill_backward_validation_and_workspace(kda):
     L = kda.lib()
     base = dict(B=2, T=100, H=3, dk=32, dv=32, in_dtype=kda.KDA_BF16, q=0x1000, k=0x2000, v=0x3000,
                 conv_w=0x4000, g=0x5000, beta=0x6000, gate=0x7000, S0=None, conv_in=None, grad_o=0x8000,
-                grad_S_T=None, grad_q=0x9000, grad_k=0xa000, grad_v=0xb000, grad_g=0xc000, grad_beta=0xd000,
+                grad_S_T=None, grad_conv_out=None, grad_q=0x9000, grad_k=0xa000, grad_v=0xb000, grad_g=0xc000, grad_beta=0xd000,
                 grad_gate=0xe000, grad_S0=None, grad_conv_in=None, workspace=0x100000, workspace_bytes=1 << 40,
                 decay_form=0, A=None)
     for over, code in [(dict(grad_o=None), -1), (dict(grad_k=None), -1), (dict(workspace=None), -1),
                        (dict(B=0), -2), (dict(in_dtype=5), -3), (dict(grad_q=0x9008), -4),
-                       (dict(workspace=0x100004), -4), (dict(grad_beta=0xd002), -4), (dict(dk=32, dv=64), -5),
+                       (dict(workspace=0x100004), -4), (dict(grad_beta=0xd002), -4),
+                       (dict(grad_conv_out=0xf008), -4), (dict(dk=32, dv=64), -5),
                        (dict(decay_form=1, A=0xf000), -5), (dict(workspace_bytes=100), -6)]:
         a = kda.PrefillBackwardArgs(**{**base, **over})
         assert L.kda_prefill_backward(ctypes.byref(a), None) == code, over
@@ -264,4 +265,4 @@ def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 4
+    assert L.kda_abi_version() == 5

@@ -84,3 +84,81 @@ def test_backward_empty_sequence():
     torch.cuda.synchronize()
     assert torch.equal(out["S0"], gs)
     assert torch.count_nonzero(out["conv_in"]).item() == 0
+
+
+def _carry_to_input(a, dtype):
+    """Raw rows carried from the reference forward (exact input values) in the
+    input encoding: uint16 bits for bf16, float32 otherwise."""
+    a = np.asarray(a, dtype=np.float64)
+    if dtype == "bf16":
+        bits = a.astype(np.float32).view(np.uint32)
+        assert np.all(bits & 0xFFFF == 0), "carried rows are not bf16 values"
+        return (bits >> 16).astype(np.uint16)
+    return a.astype(np.float32)
+
+
+@pytest.mark.parametrize("B,T,H,d,dtype", [(1, 100, 2, 32, "bf16"), (2, 2, 2, 16, "f32"), (1, 3, 2, 16, "bf16")])
+def test_backward_with_conv_out_loss(B, T, H, d, dtype):
+    """A loss on conv_out (the last three raw rows) as well as on o and S_T;
+    T = 2 also sends one row of that gradient into the history."""
+    torch, kda = need_gpu()
+    ob = pytest.importorskip("oracle.backward")
+    w = Workload("bwdc", B, T, H, d, d, 64, dtype, s0_sigma=0.05, conv_hist="normal", seed=140 + T)
+    inp = syn.prefill_inputs_np(w)
+    rng = np.random.default_rng(40 + T)
+    dO = rng.standard_normal((B, T, H, d))
+    dS = rng.standard_normal((B, H, d, d))
+    dC = rng.standard_normal((B, 3, 3 * H * d))
+    print(f"  case B{B} T{T} H{H} d{d} {dtype} with grad_conv_out", flush=True)
+    dev = to_dev(inp, dtype)
+    out = kda.prefill_backward(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"],
+                               torch.from_numpy(dO.astype(np.float32)).cuda(), S0=dev["S0"],
+                               conv_in=dev["conv_in"], grad_S_T=torch.from_numpy(dS.astype(np.float32)).cuda(),
+                               grad_conv_out=torch.from_numpy(dC.astype(np.float32)).cuda())
+    torch.cuda.synchronize()
+    ref = ob.backward(inp, dO, dS, dC)
+    for x in NAMES:
+        assert_rms_close(out[x].cpu().numpy(), ref[x], TOL_GRAD, f"d{x}")
+
+
+def test_segment_chain_equals_whole_sequence():
+    """A sequence differentiated as three carried segments, the last first: each
+    segment's grad_S0 and grad_conv_in are the grad_S_T and grad_conv_out of
+    the one before it.  The concatenated gradients match the reference's
+    whole-sequence gradients (the carries S0 and conv_in of each segment come
+    from the reference forward of the segments before it)."""
+    torch, kda = need_gpu()
+    ob = pytest.importorskip("oracle.backward")
+    B, T, H, d, dtype = 1, 300, 2, 64, "bf16"
+    w = Workload("bwds", B, T, H, d, d, 64, dtype, s0_sigma=0.05, conv_hist="normal", seed=151)
+    inp = syn.prefill_inputs_np(w)
+    rng = np.random.default_rng(52)
+    dO = rng.standard_normal((B, T, H, d))
+    dS = rng.standard_normal((B, H, d, d))
+    whole = ob.backward(inp, dO, dS)
+    cuts = [0, 70, 129, T]  # segments of 70, 59 and 171 tokens
+    seq = ("q", "k", "v", "g", "beta", "gate")
+    segs, S0, ci = [], inp["S0"], inp["conv_in"]
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        seg = {x: inp[x][:, a:b] for x in seq}
+        seg.update(conv_w=inp["conv_w"], S0=S0, conv_in=ci)
+        segs.append(seg)
+        f = ob.forward(seg)
+        S0, ci = f["S_T"], _carry_to_input(f["conv_out"], dtype)
+    gS = torch.from_numpy(dS.astype(np.float32)).cuda()
+    gC = None
+    got = [None] * len(segs)
+    for i in range(len(segs) - 1, -1, -1):
+        a, b = cuts[i], cuts[i + 1]
+        print(f"  segment {i}: tokens {a}..{b}", flush=True)
+        dev = to_dev(segs[i], dtype)
+        out = kda.prefill_backward(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"],
+                                   torch.from_numpy(dO[:, a:b].astype(np.float32)).cuda(), S0=dev["S0"],
+                                   conv_in=dev["conv_in"], grad_S_T=gS, grad_conv_out=gC)
+        torch.cuda.synchronize()
+        got[i] = {x: out[x].cpu().numpy() for x in NAMES}
+        gS, gC = out["S0"], out["conv_in"]
+    for x in seq:
+        assert_rms_close(np.concatenate([g[x] for g in got], axis=1), whole[x], TOL_GRAD, f"d{x} (3 segments)")
+    for x in ("S0", "conv_in"):
+        assert_rms_close(got[0][x], whole[x], TOL_GRAD, f"d{x} (3 segments)")
