@@ -327,10 +327,10 @@ size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* args);
  * Gradients are with respect to the input values (bf16 inputs: their bf16
  * values).  Direct decay form only (decay_form KDA_DECAY_DIRECT), dk = dv.
  * Computed in fp32, one workgroup per (b, h): the forward recurrence again
- * with the state stored every 64 tokens in the workspace, then each 64-token
+ * with the state stored every 16 tokens in the workspace, then each 16-token
  * stretch recomputed and walked back token by token.  Workspace
  * (kda_prefill_backward_workspace_bytes, 16-byte aligned, required):
- * B*H*((ceil(T/64) + 64)*dk*dv + 64*(14*dk + 8))*4 bytes.
+ * B*H*((ceil(T/16) + 16)*dk*dv + 16*(14*dk + 8))*4 bytes.
  * Errors as kda_prefill; KDA_E_NULL (grad_o, a required gradient output or the
  * workspace NULL), KDA_E_UNSUPPORTED (KDA_DECAY_K3), KDA_E_WORKSPACE.
  */

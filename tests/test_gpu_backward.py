@@ -32,10 +32,10 @@ def _run(kda, torch, inp, dtype, dO, dS):
 
 CASES = [
     # B, T, H, d, dtype
-    (1, 200, 2, 128, "bf16"),   # 4 stretches of 64 (ragged last)
+    (1, 200, 2, 128, "bf16"),   # 13 stretches of 16 (ragged last)
     (2, 150, 2, 32, "f32"),
     (2, 70, 3, 16, "bf16"),
-    (1, 64, 2, 64, "f32"),      # exactly one stretch
+    (1, 64, 2, 64, "f32"),      # a whole number of stretches
     (2, 2, 2, 16, "f32"),       # fewer tokens than the conv history
 ]
 
