@@ -3,13 +3,17 @@
 // row), for the definition of "Kimi K3, previewed", section "Kimi Delta
 // Attention - the workhorse" and the KDA rows of the component tables.
 //
-// One workgroup per (b, h) (256 or 512 threads by head dim), token by token, all in fp32:
-//   1. forward: the recurrence over the whole sequence, storing the state at
-//      every chunk start (kBwdChunk tokens) in the workspace;
-//   2. the chunks in reverse: each is recomputed from its stored state (the
-//      state entering every token and the token's vectors go to the
-//      workspace), then walked back token by token with the state gradient dS
-//      in registers.
+// Token by token, all in fp32, three launch kinds (256 or 512 threads by head dim):
+//   1. forward, one workgroup per (b, h): the recurrence over the whole
+//      sequence, storing the state at every stretch start (kBwdChunk tokens);
+//   2. recompute, one workgroup per (b, h, stretch) of a slab of stretches:
+//      from the stretch's stored state, the state entering every token and
+//      the token's vectors go to the slab buffer (all stretches at once, on
+//      every compute unit);
+//   3. reverse, one workgroup per (b, h): the slab's tokens walked back with
+//      the state gradient dS in registers; dS and the conv ring are carried
+//      to the next (earlier) slab through the workspace.
+// Slabs run from the last to the first, recompute then reverse.
 // Reverse step of token t (dS = dL/dS_t, do = dL/do_t; s = sigmoid(gate)):
 //   dgate = do n s (1 - s);  dz = (do s - n mean(do s n)) / r
 //   dq^ = S_t dz;  dS += q^ dz^T;  du = dS^T k^;  dk^ = dS u
@@ -28,6 +32,9 @@ namespace kda {
 namespace {
 
 constexpr int kBwdChunk = 16;  // tokens between stored states (16 measured faster than 4, 8, 32 and 64)
+constexpr int kBwdSlab = 64;   // stretches recomputed per launch
+
+enum : int { kModeForward = 1, kModeRecompute = 2, kModeReverse = 3 };
 
 // Threads per workgroup: eight state rows per thread at d = 128 (512 threads,
 // 8 waves), so each SIMD has two waves to hide latency with (1024 threads
@@ -60,6 +67,8 @@ struct BwdParams {
   float* dS0;
   float* dconv_in;
   float* ws;
+  int ch_lo, ch_hi;  // the slab's stretches (recompute, reverse)
+  int buf;           // the slab buffer (0 or 1) they go through
 };
 
 // One token's record in the workspace (floats): a, x~ (3d each), q^, k^, y,
@@ -72,11 +81,20 @@ struct Rec {
   static constexpr int SIZE = 14 * D + 8;
 };
 
+// Workspace, in floats: the stored states [BH][nch][D][D], the carry
+// [BH][D*D + 9D] (dS, then the conv ring [3][3D]), and two slab buffers
+// [2][BH][slab stretches][kBwdChunk][D*D] states + [kBwdChunk][Rec SIZE]
+// records (one is recomputed into while the other is walked back).
 template <int D>
-__host__ __device__ constexpr size_t bwd_head_floats(int T) {
-  const size_t nch = (size_t)(T + kBwdChunk - 1) / kBwdChunk;
-  return (nch + kBwdChunk) * D * D + (size_t)kBwdChunk * Rec<D>::SIZE;
-}
+struct BwdLayout {
+  static constexpr size_t CARRY = (size_t)D * D + 9 * D;
+  static constexpr size_t STRETCH = (size_t)kBwdChunk * ((size_t)D * D + Rec<D>::SIZE);
+  __host__ __device__ static int nch(int T) { return (T + kBwdChunk - 1) / kBwdChunk; }
+  __host__ __device__ static int slab(int T) { return nch(T) < kBwdSlab ? nch(T) : kBwdSlab; }
+  __host__ __device__ static size_t ckpt(int T) { return (size_t)nch(T) * D * D; }
+  // per (b, h)
+  __host__ __device__ static size_t head_floats(int T) { return ckpt(T) + CARRY + 2 * (size_t)slab(T) * STRETCH; }
+};
 
 // Barriers are LDS-only (lds_barrier) wherever threads exchange data through
 // LDS only, so global loads issued ahead (the next token's raw inputs and
@@ -84,7 +102,7 @@ __host__ __device__ constexpr size_t bwd_head_floats(int T) {
 // (each token's record, written by the threads that hold each value and read
 // back in another mapping) is ordered by a full barrier after each stretch's
 // recompute.
-template <int D, bool IB>
+template <int D, bool IB, int MODE>
 __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p) {
   constexpr int NT = bwd_threads<D>();
   constexpr int NC = 3 * D;
@@ -103,11 +121,16 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   const int cch = H * NC;
   const int cg = tid % CG, rg = tid / CG;
   const bool active = rg < RG;
-  const int nch = (T + kBwdChunk - 1) / kBwdChunk;
+  using L = BwdLayout<D>;
+  const int nch = L::nch(T);
+  const size_t BH = (size_t)p.B * H;
 
-  float* ckpt = p.ws + (size_t)bh * bwd_head_floats<D>(T);     // [nch][D][D]
-  float* st = ckpt + (size_t)nch * D * D;                      // [kBwdChunk][D][D]
-  float* rec = st + (size_t)kBwdChunk * D * D;                 // [kBwdChunk][V::SIZE]
+  float* ckpt = p.ws + (size_t)bh * L::ckpt(T);                           // [nch][D][D]
+  float* carry = p.ws + BH * L::ckpt(T) + (size_t)bh * L::CARRY;          // dS, ring
+  float* slab = p.ws + BH * (L::ckpt(T) + L::CARRY) + ((size_t)p.buf * BH + bh) * L::slab(T) * L::STRETCH;
+  // stretch l of the slab: states [kBwdChunk][D][D], then records [kBwdChunk][V::SIZE]
+  auto slot_st = [&](int l) { return slab + (size_t)l * L::STRETCH; };
+  auto slot_rec = [&](int l) { return slab + (size_t)l * L::STRETCH + (size_t)kBwdChunk * D * D; };
 
   __shared__ __attribute__((aligned(16))) float R[V::SIZE];   // the current token's record
   __shared__ __attribute__((aligned(16))) float dzs[D];
@@ -305,7 +328,8 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     }
   };
 
-  // ---- 1. forward over the sequence, the state at every chunk start ----------
+  // ---- 1. forward over the sequence, the state at every stretch start --------
+  if constexpr (MODE == kModeForward) {
   if (active) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -323,24 +347,16 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     }
     forward_step(t, nullptr);
   }
-
-  // ---- 2. the chunks in reverse ---------------------------------------------------
-  f4 dS[RPT];
-  if (active) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + RG * i;
-      dS[i] = p.dS_T != nullptr ? *reinterpret_cast<const f4*>(p.dS_T + (size_t)bh * D * D + (size_t)r * D + 4 * cg)
-                                : f4{0.f, 0.f, 0.f, 0.f};
-    }
+  return;
   }
-  float ring[NCT][3];  // da of tokens t+1, t+2, t+3 for this thread's channels
-#pragma unroll
-  for (int j = 0; j < NCT; ++j) ring[j][0] = ring[j][1] = ring[j][2] = 0.f;
 
-  for (int ch = nch - 1; ch >= 0; --ch) {
+  // ---- 2. recompute one stretch: the state entering each token, each token's record
+  if constexpr (MODE == kModeRecompute) {
+    const int l = blockIdx.y;
+    const int ch = p.ch_lo + l;
     const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
-    // recompute: the state entering each token, and each token's record
+    float* st = slot_st(l);
+    float* rec = slot_rec(l);
     if (active) {
       const float* src = ckpt + (size_t)ch * D * D;
 #pragma unroll
@@ -369,10 +385,34 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       }
       forward_step(t, vt);
     }
-    // The records were written by the threads that hold each value, and are
-    // read below in another mapping: a full barrier (with its memory fence).
-    __syncthreads();
-    // reverse, the next token's record requested one token ahead
+    return;
+  }
+
+  // ---- 3. reverse over the slab's stretches (the records come from the recompute launch)
+  f4 dS[RPT];
+  float ring[NCT][3];  // da of tokens t+1, t+2, t+3 for this thread's channels
+  const bool first_slab = p.ch_hi >= nch;  // the slab holding the last token
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = rg + RG * i;
+      const float* src = first_slab ? p.dS_T + (size_t)bh * D * D : carry;
+      dS[i] = first_slab && p.dS_T == nullptr ? f4{0.f, 0.f, 0.f, 0.f}
+                                              : *reinterpret_cast<const f4*>(src + (size_t)r * D + 4 * cg);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    const int c = tid + NT * j;
+#pragma unroll
+    for (int k = 0; k < 3; ++k) ring[j][k] = !first_slab && c < NC ? carry[(size_t)D * D + (size_t)k * NC + c] : 0.f;
+  }
+
+  for (int ch = p.ch_hi - 1; ch >= p.ch_lo; --ch) {
+    const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
+    const float* st = slot_st(ch - p.ch_lo);
+    const float* rec = slot_rec(ch - p.ch_lo);
+    // the next token's record requested one token ahead
     float pre[NPRE];
     {
       const float* vt = rec + (size_t)(t1 - 1 - t0) * V::SIZE;
@@ -541,8 +581,24 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     }
     flush();
   }
+  if (p.ch_lo > 0) {  // carry dS and the ring to the earlier slab
+    if (active) {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i)
+        *reinterpret_cast<f4*>(carry + (size_t)(rg + RG * i) * D + 4 * cg) = dS[i];
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + NT * j;
+      if (c < NC) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) carry[(size_t)D * D + (size_t)k * NC + c] = ring[j][k];
+      }
+    }
+    return;
+  }
 
-  // ---- 3. state and history gradients ------------------------------------------------
+  // ---- 4. state and history gradients (after the first stretch) ----------------------
   if (p.dS0 != nullptr && active) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
@@ -568,22 +624,146 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   }
 }
 
-template <int D>
-int run_backward(const kda_prefill_backward_args& a, hipStream_t s) {
+// The streams of the slab pipeline (default priority) and the events that
+// order them, per host thread and device, for one reverse width (B*H rounded
+// up to a multiple of 8, so each of the eight accelerator dies gets the same
+// share: mask bits interleave over the dies).  The reverse launches run on
+// that many compute units, the recompute launches on the others, alternating
+// between two streams.  Created on first use and kept for the life of the thread.
+struct BwdPipe {
+  int n_rev = 0;
+  hipStream_t rev = nullptr, rec[2] = {nullptr, nullptr};
+  hipEvent_t fork = nullptr, rec_done[2] = {nullptr, nullptr}, rev_done[2] = {nullptr, nullptr};
+  hipEvent_t join[3] = {nullptr, nullptr, nullptr};
+};
+
+// pp = nullptr (and KDA_OK) when the device is too small to split for this width.
+int get_bwd_pipe(int heads, BwdPipe*& pp) {
+  constexpr int kMaxDev = 64, kPerDev = 4;
+  static thread_local BwdPipe pipes[kMaxDev][kPerDev];
+  static thread_local int ncus[kMaxDev];
+  pp = nullptr;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    set_error("backward: hipGetDevice failed or device %d out of range", dev);
+    return KDA_E_HIP;
+  }
+  if (ncus[dev] == 0) {
+    int n = 0;
+    e = hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess || n <= 0) {
+      set_error("backward: compute unit count query failed: %s", hipGetErrorString(e));
+      return KDA_E_HIP;
+    }
+    ncus[dev] = n;
+  }
+  const int ncu = ncus[dev];
+  const int n_rev = (heads + 7) / 8 * 8;
+  if (n_rev + 32 > ncu) return KDA_OK;  // too few compute units left for the recompute
+  BwdPipe* slot = nullptr;
+  for (int k = 0; k < kPerDev && slot == nullptr; ++k)
+    if (pipes[dev][k].n_rev == n_rev) slot = &pipes[dev][k];
+  for (int k = 0; k < kPerDev && slot == nullptr; ++k)
+    if (pipes[dev][k].n_rev == 0) slot = &pipes[dev][k];
+  if (slot == nullptr) return KDA_OK;  // every slot holds another width: run on one stream
+  if (slot->n_rev == 0) {
+    uint32_t m_rev[32] = {0}, m_rec[32] = {0};
+    const int nb = ncu < 32 * 32 ? ncu : 32 * 32;
+    for (int c = 0; c < nb; ++c) (c < n_rev ? m_rev : m_rec)[c / 32] |= 1u << (c % 32);
+    const uint32_t words = (uint32_t)((nb + 31) / 32);
+    e = hipExtStreamCreateWithCUMask(&slot->rev, words, m_rev);
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipExtStreamCreateWithCUMask(&slot->rec[k], words, m_rec);
+    hipEvent_t* evs[8] = {&slot->fork, &slot->rec_done[0], &slot->rec_done[1], &slot->rev_done[0],
+                          &slot->rev_done[1], &slot->join[0], &slot->join[1], &slot->join[2]};
+    for (int k = 0; k < 8 && e == hipSuccess; ++k) e = hipEventCreateWithFlags(evs[k], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      set_error("backward: stream / event creation failed: %s", hipGetErrorString(e));
+      return KDA_E_HIP;
+    }
+    slot->n_rev = n_rev;
+  }
+  pp = slot;
+  return KDA_OK;
+}
+
+template <int D, bool IB>
+int run_backward_typed(const kda_prefill_backward_args& a, hipStream_t st) {
   BwdParams p{a.B, a.T, a.H, a.q, a.k, a.v, a.conv_w, a.g, a.beta, a.gate, a.S0, a.conv_in, a.grad_o,
               a.grad_S_T, a.grad_conv_out, a.grad_q, a.grad_k, a.grad_v, a.grad_g, a.grad_beta, a.grad_gate, a.grad_S0,
-              a.grad_conv_in, static_cast<float*>(a.workspace)};
-  const unsigned grid = (unsigned)((size_t)a.B * a.H);
-  if (a.in_dtype == KDA_BF16)
-    hipLaunchKernelGGL((backward_kernel<D, true>), dim3(grid), dim3(bwd_threads<D>()), 0, s, p);
-  else
-    hipLaunchKernelGGL((backward_kernel<D, false>), dim3(grid), dim3(bwd_threads<D>()), 0, s, p);
-  const hipError_t e = hipGetLastError();
+              a.grad_conv_in, static_cast<float*>(a.workspace), 0, 0, 0};
+  using L = BwdLayout<D>;
+  const unsigned heads = (unsigned)((size_t)a.B * a.H);
+  const int nch = L::nch(a.T), sl = L::slab(a.T);
+  const dim3 block(bwd_threads<D>());
+  // slabs from the last to the first; with no tokens, one reverse launch writes dS0 and dconv_in
+  const int nslab = nch > 0 ? (nch + sl - 1) / sl : 1;
+  BwdPipe* pp = nullptr;
+  if (nslab > 1) {
+    const int rc = get_bwd_pipe((int)heads, pp);
+    if (rc != KDA_OK) return rc;
+  }
+  const bool piped = pp != nullptr;
+  hipLaunchKernelGGL((backward_kernel<D, IB, kModeForward>), dim3(heads), block, 0, st, p);
+  hipError_t e = hipGetLastError();
+  const char* what = "forward launch";
+  if (e == hipSuccess && piped) {
+    // the pipeline's streams start after the forward launch
+    what = "event";
+    e = hipEventRecord(pp->fork, st);
+    for (int k = 0; k < 2 && e == hipSuccess; ++k) e = hipStreamWaitEvent(pp->rec[k], pp->fork, 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(pp->rev, pp->fork, 0);
+  }
+  for (int i = 0; i < nslab && e == hipSuccess; ++i) {
+    const int k = nslab - 1 - i;
+    p.ch_lo = k * sl;
+    p.ch_hi = nch < p.ch_lo + sl ? nch : p.ch_lo + sl;
+    p.buf = i & 1;
+    hipStream_t sa = piped ? pp->rec[i & 1] : st, sb = piped ? pp->rev : st;
+    // the buffer is free once the reverse launch of slab i - 2 is done
+    if (piped && i >= 2) e = hipStreamWaitEvent(sa, pp->rev_done[p.buf], 0);
+    if (e == hipSuccess && p.ch_hi > p.ch_lo) {
+      hipLaunchKernelGGL((backward_kernel<D, IB, kModeRecompute>), dim3(heads, (unsigned)(p.ch_hi - p.ch_lo)), block,
+                         0, sa, p);
+      e = hipGetLastError();
+      what = "recompute launch";
+    }
+    if (e == hipSuccess && piped) {
+      what = "event";
+      e = hipEventRecord(pp->rec_done[i & 1], sa);
+      if (e == hipSuccess) e = hipStreamWaitEvent(sb, pp->rec_done[i & 1], 0);
+    }
+    if (e == hipSuccess) {
+      hipLaunchKernelGGL((backward_kernel<D, IB, kModeReverse>), dim3(heads), block, 0, sb, p);
+      e = hipGetLastError();
+      what = "reverse launch";
+    }
+    if (e == hipSuccess && piped) {
+      what = "event";
+      e = hipEventRecord(pp->rev_done[p.buf], sb);
+    }
+  }
+  if (piped) {
+    // the caller's stream resumes after the pipeline's work (also on an error above)
+    hipStream_t all[3] = {pp->rec[0], pp->rec[1], pp->rev};
+    hipError_t j = hipSuccess;
+    for (int k = 0; k < 3 && j == hipSuccess; ++k) j = hipEventRecord(pp->join[k], all[k]);
+    for (int k = 0; k < 3 && j == hipSuccess; ++k) j = hipStreamWaitEvent(st, pp->join[k], 0);
+    if (e == hipSuccess && j != hipSuccess) {
+      e = j;
+      what = "event";
+    }
+  }
   if (e != hipSuccess) {
-    set_error("backward launch failed: %s", hipGetErrorString(e));
+    set_error("backward: %s failed: %s", what, hipGetErrorString(e));
     return KDA_E_HIP;
   }
   return KDA_OK;
+}
+
+template <int D>
+int run_backward(const kda_prefill_backward_args& a, hipStream_t s) {
+  return a.in_dtype == KDA_BF16 ? run_backward_typed<D, true>(a, s) : run_backward_typed<D, false>(a, s);
 }
 
 }  // namespace
@@ -591,10 +771,10 @@ int run_backward(const kda_prefill_backward_args& a, hipStream_t s) {
 size_t prefill_backward_workspace_bytes(const kda_prefill_backward_args& a) {
   size_t per = 0;
   switch (a.dk) {
-    case 16: per = bwd_head_floats<16>(a.T); break;
-    case 32: per = bwd_head_floats<32>(a.T); break;
-    case 64: per = bwd_head_floats<64>(a.T); break;
-    case 128: per = bwd_head_floats<128>(a.T); break;
+    case 16: per = BwdLayout<16>::head_floats(a.T); break;
+    case 32: per = BwdLayout<32>::head_floats(a.T); break;
+    case 64: per = BwdLayout<64>::head_floats(a.T); break;
+    case 128: per = BwdLayout<128>::head_floats(a.T); break;
     default: return 0;
   }
   return per * sizeof(float) * (size_t)a.B * a.H;

@@ -37,6 +37,7 @@ CASES = [
     (2, 70, 3, 16, "bf16"),
     (1, 64, 2, 64, "f32"),      # a whole number of stretches
     (2, 2, 2, 16, "f32"),       # fewer tokens than the conv history
+    (1, 1100, 1, 32, "f32"),    # 69 stretches: two slabs of recompute (64 + 5), dS and the ring carried
 ]
 
 
