@@ -72,13 +72,15 @@ struct BwdParams {
 };
 
 // One token's record in the workspace (floats): a, x~ (3d each), q^, k^, y,
-// u, z, alpha = e^g, sigmoid(gate), dL/do (d each), then scalars nq, nk, rq,
-// rk, -, beta (8 slots).  The same layout serves as the token's LDS image.
+// u, dz = dL/dz, alpha = e^g, dq^ = S_t dz (d each), then scalars nq, nk, rq,
+// rk, -, beta (8 slots).  dz and dq^ need only forward values and dL/do, so
+// the recompute computes them (and dgate) off the reverse's serial path.  The
+// same layout serves as the token's LDS image.
 template <int D>
 struct Rec {
-  static constexpr int A = 0, X = 3 * D, QN = 6 * D, KN = 7 * D, Y = 8 * D, U = 9 * D, Z = 10 * D;
-  static constexpr int AL = 11 * D, SG = 12 * D, DO = 13 * D, SC = 14 * D;
-  static constexpr int SIZE = 14 * D + 8;
+  static constexpr int A = 0, X = 3 * D, QN = 6 * D, KN = 7 * D, Y = 8 * D, U = 9 * D, DZ = 10 * D;
+  static constexpr int AL = 11 * D, DQ = 12 * D, SC = 13 * D;
+  static constexpr int SIZE = 13 * D + 8;
 };
 
 // Workspace, in floats: the stored states [BH][nch][D][D], the carry
@@ -133,10 +135,9 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   auto slot_rec = [&](int l) { return slab + (size_t)l * L::STRETCH + (size_t)kBwdChunk * D * D; };
 
   __shared__ __attribute__((aligned(16))) float R[V::SIZE];   // the current token's record
-  __shared__ __attribute__((aligned(16))) float dzs[D];
   __shared__ __attribute__((aligned(16))) float dus[D];
   __shared__ __attribute__((aligned(16))) float dys[D];
-  __shared__ float dqn[D], dkn[D];
+  __shared__ float dkn[D];
   __shared__ __attribute__((aligned(16))) float red[RG][D];
   float* const xa = R + V::A;
   float* const xs = R + V::X;
@@ -144,7 +145,6 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   float* const kn = R + V::KN;
   float* const yv = R + V::Y;
   float* const uv = R + V::U;
-  float* const zv = R + V::Z;
   float* const al = R + V::AL;
   float* const sc = R + V::SC;  // nq, nk, rq, rk, -, beta; [6], [7]: q~.dq^, k~.dk^
 
@@ -214,15 +214,19 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   __shared__ float fn[2][NT / 64][2];                  // per-wave |q~|^2, |k~|^2
   __shared__ __attribute__((aligned(16))) float fy[2][RG][D];   // row-group partials of y
   __shared__ __attribute__((aligned(16))) float fz[2][RG][D];   // row-group partials of z
+  __shared__ __attribute__((aligned(16))) float fdz[D];         // dz of the token (recompute)
 
   // One forward token t on the register state s[]: conv + SiLU, the L2 norms,
   // S' = Diag(alpha) S, y = S'^T k^, u = beta (v^ - y), S_t = S' + k^ u^T.
   // Every thread derives the norms from the per-wave partials and sums y (and
   // z) for its own columns, so a token needs two barriers (three with z).
   // With vt, the token's record is written straight from the threads that
-  // hold each value.
+  // hold each value, and the output side of the reverse step is taken here
+  // (gate4, do4: the gate and dL/do of this thread's 4 columns, row group 0):
+  //   r = rms(z), n = z / r, dgate = do n s (1 - s), dz = (do s - n mean(do s n)) / r,
+  //   dq^ = S_t dz  (s = sigmoid(gate)).
   f4 s[RPT];
-  auto forward_step = [&](int t, float* vt) {
+  auto forward_step = [&](int t, float* vt, const f4& gate4, const f4& do4) {
     const int u = t & 1;
     float pq = 0.f, pk = 0.f;
 #pragma unroll
@@ -319,11 +323,32 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         vt[V::SC + 5] = beta_t;
       }
       lds_barrier();
-      if (active && rg == 0) {
-        f4 z = f4{0.f, 0.f, 0.f, 0.f};
+      const bool lead = active && rg == 0;  // the CG lanes of row group 0 hold z, 4 columns each
+      f4 z = f4{0.f, 0.f, 0.f, 0.f};
+      if (lead) {
 #pragma unroll 4
         for (int r = 0; r < RG; ++r) z += *reinterpret_cast<const f4*>(&fz[u][r][4 * cg]);
-        *reinterpret_cast<f4*>(vt + V::Z + 4 * cg) = z;
+      }
+      const float zz = group_sum<CG>(lead ? z.x * z.x + z.y * z.y + z.z * z.z + z.w * z.w : 0.f);
+      const float rr = sqrtf(zz * (1.0f / D) + kRmsEps);
+      const f4 n = z * (1.0f / rr);
+      const f4 sg = f4{sigmoidf_(gate4.x), sigmoidf_(gate4.y), sigmoidf_(gate4.z), sigmoidf_(gate4.w)};
+      const f4 dos = do4 * sg;
+      const float dd =
+          group_sum<CG>(lead ? dos.x * n.x + dos.y * n.y + dos.z * n.z + dos.w * n.w : 0.f) * (1.0f / D);
+      if (lead) {
+        *reinterpret_cast<f4*>(p.dgate + rowidx(t) * D + 4 * cg) = dos * n * (1.f - sg);
+        const f4 dz = (dos - n * dd) * (1.0f / rr);
+        *reinterpret_cast<f4*>(vt + V::DZ + 4 * cg) = dz;
+        *reinterpret_cast<f4*>(&fdz[4 * cg]) = dz;
+      }
+      lds_barrier();
+      const f4 dz = *reinterpret_cast<const f4*>(&fdz[4 * cg]);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const float part = active ? s[i].x * dz.x + s[i].y * dz.y + s[i].z * dz.z + s[i].w * dz.w : 0.f;
+        const float v = group_sum<CG>(part);  // (S_t dz)_r
+        if (active && cg == 0) vt[V::DQ + rg + RG * i] = v;
       }
     }
   };
@@ -345,7 +370,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
 #pragma unroll
       for (int i = 0; i < RPT; ++i) *reinterpret_cast<f4*>(dst + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
     }
-    forward_step(t, nullptr);
+    forward_step(t, nullptr, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f});
   }
   return;
   }
@@ -363,27 +388,30 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       for (int i = 0; i < RPT; ++i) s[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
     }
     start_window(t0);
-    // gate and dL/do are requested a token ahead: loads and stores share one
-    // in-order counter, so a load waited for right after stores waits for them
-    float gate_n = tid < D ? load1<IB>(p.gate, rowidx(t0) * D + tid) : 0.f;
-    float do_n = tid < D ? p.dO[rowidx(t0) * D + tid] : 0.f;
+    // gate and dL/do (4 columns per lane of row group 0) are requested a token
+    // ahead: loads and stores share one in-order counter, so a load waited for
+    // right after stores waits for them
+    auto gate4_of = [&](int t) {
+      const size_t i = rowidx(t) * D + 4 * cg;
+      return f4{load1<IB>(p.gate, i), load1<IB>(p.gate, i + 1), load1<IB>(p.gate, i + 2), load1<IB>(p.gate, i + 3)};
+    };
+    auto do4_of = [&](int t) { return *reinterpret_cast<const f4*>(p.dO + rowidx(t) * D + 4 * cg); };
+    const bool lead = tid < CG;
+    f4 gate_n = lead ? gate4_of(t0) : f4{0.f, 0.f, 0.f, 0.f};
+    f4 do_n = lead ? do4_of(t0) : f4{0.f, 0.f, 0.f, 0.f};
     for (int t = t0; t < t1; ++t) {
       float* vt = rec + (size_t)(t - t0) * V::SIZE;
-      const float gate_t = gate_n, do_t = do_n;
-      if (tid < D && t + 1 < t1) {
-        gate_n = load1<IB>(p.gate, rowidx(t + 1) * D + tid);
-        do_n = p.dO[rowidx(t + 1) * D + tid];
+      const f4 gate_t = gate_n, do_t = do_n;
+      if (lead && t + 1 < t1) {
+        gate_n = gate4_of(t + 1);
+        do_n = do4_of(t + 1);
       }
       if (active) {
         float* dst = st + (size_t)(t - t0) * D * D;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) *reinterpret_cast<f4*>(dst + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
       }
-      if (tid < D) {
-        vt[V::SG + tid] = sigmoidf_(gate_t);
-        vt[V::DO + tid] = do_t;
-      }
-      forward_step(t, vt);
+      forward_step(t, vt, gate_t, do_t);
     }
     return;
   }
@@ -425,15 +453,10 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     // A token's gradients are stored after the next token's loads are issued
     // (the counter is in order), so the store latency stays off the chain.
     int t_def = -1;
-    float dgate_def[(D + 63) / 64], dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
+    float dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
     auto flush = [&]() {
       if (t_def < 0) return;
       const size_t rw = rowidx(t_def);
-      if (tid < 64) {
-#pragma unroll
-        for (int k2 = 0; k2 < (D + 63) / 64; ++k2)
-          if (tid + 64 * k2 < D) p.dgate[rw * D + tid + 64 * k2] = dgate_def[k2];
-      }
       if (tid == 0) p.dbeta[rw] = dbeta_def;
       if (active && cg == 0) {
 #pragma unroll
@@ -468,49 +491,18 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       flush();  // token t + 1's gradients
       t_def = t;
       lds_barrier();
-      // output side: r, dgate, dz
-      if (tid < 64) {
-        float zz = 0.f;
-        for (int c = tid; c < D; c += 64) zz += zv[c] * zv[c];
-        zz = group_sum<64>(zz);
-        const float r = sqrtf(zz * (1.0f / D) + kRmsEps);
-        float dd = 0.f;
-#pragma unroll
-        for (int k2 = 0; k2 < (D + 63) / 64; ++k2) {
-          const int c = tid + 64 * k2;
-          if (c < D) {
-            const float n = zv[c] / r;
-            const float sg = R[V::SG + c], dov = R[V::DO + c];
-            dgate_def[k2] = dov * n * sg * (1.f - sg);
-            dd += dov * sg * n;
-          }
-        }
-        dd = group_sum<64>(dd) * (1.0f / D);
-        for (int c = tid; c < D; c += 64) dzs[c] = (R[V::DO + c] * R[V::SG + c] - zv[c] / r * dd) / r;
-      }
-      lds_barrier();
       // state side
       f4 sp[RPT];
-      float rq_part[RPT];
       f4 dup = f4{0.f, 0.f, 0.f, 0.f};
       if (active) {
-        const f4 dz = *reinterpret_cast<const f4*>(&dzs[4 * cg]);
-        const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
+        const f4 dz = *reinterpret_cast<const f4*>(&R[V::DZ + 4 * cg]);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
           sp[i] = prev[i] * al[r];
-          const f4 stt = sp[i] + u * kn[r];
-          rq_part[i] = stt.x * dz.x + stt.y * dz.y + stt.z * dz.z + stt.w * dz.w;  // (S_t dz)_r partial
           dS[i] += dz * qn[r];
           dup += dS[i] * kn[r];
         }
-      }
-      // dq^ = S_t dz: row sums over the CG lanes of a row group
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const float v = group_sum<CG>(active ? rq_part[i] : 0.f);
-        if (active && cg == 0) dqn[rg + RG * i] = v;
       }
       colsum(dup, dus);  // du = dS^T k^
       // dbeta, dy
@@ -545,7 +537,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       if (tid < 64) {
         float a = 0.f, bb = 0.f;
         for (int c = tid; c < D; c += 64) {
-          a += xs[c] * dqn[c];
+          a += xs[c] * R[V::DQ + c];
           bb += xs[D + c] * dkn[c];
         }
         a = group_sum<64>(a);
@@ -561,7 +553,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         const int c = tid + NT * j;
         if (c < NC) {
           float dx;
-          if (c < D) dx = sc[2] * (dqn[c] - xs[c] * sc[6] / sc[0]);
+          if (c < D) dx = sc[2] * (R[V::DQ + c] - xs[c] * sc[6] / sc[0]);
           else if (c < 2 * D) dx = sc[3] * (dkn[c - D] - xs[c] * sc[7] / sc[1]);
           else dx = sc[5] * dus[c - 2 * D];
           const float a = xa[c];
@@ -577,7 +569,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           ring[j][0] = da;
         }
       }
-      lds_barrier();  // R, dqn, dkn, dus are rewritten by the next token
+      lds_barrier();  // R, dkn, dus are rewritten by the next token
     }
     flush();
   }

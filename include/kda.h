@@ -335,7 +335,7 @@ size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* args);
  * already on `stream`, which in turn waits for them).  Workspace
  * (kda_prefill_backward_workspace_bytes, 16-byte aligned, required), with
  * n = ceil(T/16):
- * B*H*(n*dk*dv + dk*dv + 9*dk + 2*min(n, 64)*16*(dk*dv + 14*dk + 8))*4 bytes.
+ * B*H*(n*dk*dv + dk*dv + 9*dk + 2*min(n, 64)*16*(dk*dv + 13*dk + 8))*4 bytes.
  * Errors as kda_prefill; KDA_E_NULL (grad_o, a required gradient output or the
  * workspace NULL), KDA_E_UNSUPPORTED (KDA_DECAY_K3), KDA_E_WORKSPACE.
  */
