@@ -73,8 +73,9 @@ struct BwdParams {
 
 // One token's record in the workspace (floats): a, x~ (3d each), q^, k^, y,
 // u, dz = dL/dz, alpha = e^g, dq^ = S_t dz (d each), then scalars nq, nk, rq,
-// rk, -, beta (8 slots).  dz and dq^ need only forward values and dL/do, so
-// the recompute computes them (and dgate) off the reverse's serial path.  The
+// rk, -, beta, q~ . dq^ (and a slot the reverse uses for k~ . dk^).  dz, dq^
+// and q~ . dq^ need only forward values and dL/do, so the recompute computes
+// them (and dgate) off the reverse's serial path.  The
 // same layout serves as the token's LDS image.
 template <int D>
 struct Rec {
@@ -136,7 +137,6 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
 
   __shared__ __attribute__((aligned(16))) float R[V::SIZE];   // the current token's record
   __shared__ __attribute__((aligned(16))) float dus[D];
-  __shared__ __attribute__((aligned(16))) float dys[D];
   __shared__ float dkn[D];
   __shared__ __attribute__((aligned(16))) float red[RG][D];
   float* const xa = R + V::A;
@@ -215,6 +215,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   __shared__ __attribute__((aligned(16))) float fy[2][RG][D];   // row-group partials of y
   __shared__ __attribute__((aligned(16))) float fz[2][RG][D];   // row-group partials of z
   __shared__ __attribute__((aligned(16))) float fdz[D];         // dz of the token (recompute)
+  __shared__ float fqa[RG];                                     // row-group partials of q~ . dq^
 
   // One forward token t on the register state s[]: conv + SiLU, the L2 norms,
   // S' = Diag(alpha) S, y = S'^T k^, u = beta (v^ - y), S_t = S' + k^ u^T.
@@ -344,11 +345,23 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       }
       lds_barrier();
       const f4 dz = *reinterpret_cast<const f4*>(&fdz[4 * cg]);
+      float qa = 0.f;
 #pragma unroll
       for (int i = 0; i < RPT; ++i) {
         const float part = active ? s[i].x * dz.x + s[i].y * dz.y + s[i].z * dz.z + s[i].w * dz.w : 0.f;
         const float v = group_sum<CG>(part);  // (S_t dz)_r
-        if (active && cg == 0) vt[V::DQ + rg + RG * i] = v;
+        if (active && cg == 0) {
+          const int r = rg + RG * i;
+          vt[V::DQ + r] = v;
+          qa += fx[u][r] * v;
+        }
+      }
+      if (active && cg == 0) fqa[rg] = qa;
+      lds_barrier();
+      if (tid == 0) {
+        float a = 0.f;
+        for (int r = 0; r < RG; ++r) a += fqa[r];
+        vt[V::SC + 6] = a;  // q~ . dq^
       }
     }
   };
@@ -504,19 +517,17 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           dup += dS[i] * kn[r];
         }
       }
-      colsum(dup, dus);  // du = dS^T k^
-      // dbeta, dy
+      colsum(dup, dus);  // du = dS^T k^, visible to all after colsum's last barrier
+      // dbeta
       if (tid < 64) {
         float db = 0.f;
         for (int c = tid; c < D; c += 64) db += dus[c] * (xs[2 * D + c] - yv[c]);
         db = group_sum<64>(db);
         dbeta_def = db;
       }
-      for (int c = tid; c < D; c += NT) dys[c] = -sc[5] * dus[c];
-      lds_barrier();
       if (active) {
         const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
-        const f4 dy = *reinterpret_cast<const f4*>(&dys[4 * cg]);
+        const f4 dy = -sc[5] * *reinterpret_cast<const f4*>(&dus[4 * cg]);  // dy = -beta du
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
@@ -533,19 +544,12 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         }
       }
       lds_barrier();
-      // L2 norms, SiLU, conv transpose
+      // L2 norms (q~ . dq^ comes with the record), SiLU, conv transpose
       if (tid < 64) {
-        float a = 0.f, bb = 0.f;
-        for (int c = tid; c < D; c += 64) {
-          a += xs[c] * R[V::DQ + c];
-          bb += xs[D + c] * dkn[c];
-        }
-        a = group_sum<64>(a);
+        float bb = 0.f;
+        for (int c = tid; c < D; c += 64) bb += xs[D + c] * dkn[c];
         bb = group_sum<64>(bb);
-        if (tid == 0) {
-          sc[6] = a;
-          sc[7] = bb;
-        }
+        if (tid == 0) sc[7] = bb;
       }
       lds_barrier();
 #pragma unroll
