@@ -116,6 +116,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   constexpr int RPT = D / RG;
   using V = Rec<D>;
   constexpr int NPRE = (V::SIZE + NT - 1) / NT;  // record floats per thread
+  constexpr int kDbetaWave = NT > 64 ? 1 : 0;     // the wave that reduces dbeta
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -192,18 +193,6 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     for (int k = 0; k < PF; ++k) request(t + k, k);
   };
 
-  // column sums over the rows of this thread's column group: part -> out[D]
-  auto colsum = [&](const f4& part, float* out) {
-    if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = part;
-    lds_barrier();
-    for (int c = tid; c < D; c += NT) {
-      float sum = 0.f;
-#pragma unroll 4
-      for (int r = 0; r < RG; ++r) sum += red[r][c];
-      out[c] = sum;
-    }
-    lds_barrier();
-  };
 
   // Forward-pass exchange buffers, double-buffered by token parity: a token
   // has at least two barriers, so token t + 2 rewrites a buffer only after
@@ -470,7 +459,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     auto flush = [&]() {
       if (t_def < 0) return;
       const size_t rw = rowidx(t_def);
-      if (tid == 0) p.dbeta[rw] = dbeta_def;
+      if (tid == kDbetaWave * 64) p.dbeta[rw] = dbeta_def;
       if (active && cg == 0) {
 #pragma unroll
         for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
@@ -517,17 +506,17 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           dup += dS[i] * kn[r];
         }
       }
-      colsum(dup, dus);  // du = dS^T k^, visible to all after colsum's last barrier
-      // dbeta
-      if (tid < 64) {
-        float db = 0.f;
-        for (int c = tid; c < D; c += 64) db += dus[c] * (xs[2 * D + c] - yv[c]);
-        db = group_sum<64>(db);
-        dbeta_def = db;
-      }
+      // du = dS^T k^: every thread sums the row groups' partials of its own
+      // columns (no second barrier); row group 0 keeps du for the later steps
+      if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = dup;
+      lds_barrier();
       if (active) {
+        f4 du = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int r = 0; r < RG; ++r) du += *reinterpret_cast<const f4*>(&red[r][4 * cg]);
+        if (rg == 0) *reinterpret_cast<f4*>(&dus[4 * cg]) = du;
         const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
-        const f4 dy = -sc[5] * *reinterpret_cast<const f4*>(&dus[4 * cg]);  // dy = -beta du
+        const f4 dy = -sc[5] * du;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
@@ -544,12 +533,18 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         }
       }
       lds_barrier();
-      // L2 norms (q~ . dq^ comes with the record), SiLU, conv transpose
+      // L2 norms (q~ . dq^ comes with the record) on wave 0, dbeta on wave 1 (or
+      // wave 0 after it with a single wave), SiLU, conv transpose
       if (tid < 64) {
         float bb = 0.f;
         for (int c = tid; c < D; c += 64) bb += xs[D + c] * dkn[c];
         bb = group_sum<64>(bb);
         if (tid == 0) sc[7] = bb;
+      }
+      if (tid >= kDbetaWave * 64 && tid < kDbetaWave * 64 + 64) {
+        float db = 0.f;
+        for (int c = tid - kDbetaWave * 64; c < D; c += 64) db += dus[c] * (xs[2 * D + c] - yv[c]);
+        dbeta_def = group_sum<64>(db);
       }
       lds_barrier();
 #pragma unroll
