@@ -154,9 +154,72 @@ def backward_flops_per_head_token(d):
     return 25 * d * d
 
 
+def time_backward_segments(torch, kda, w, inp, steps):
+    """kda_prefill_backward of a workload run as carried segments (long1m: 16 x
+    65536 tokens), segment by segment from the last: each call's grad_S0 and
+    grad_conv_in are the earlier segment's grad_S_T and grad_conv_out.  Each
+    segment's entering state and conv rows come from a segment-wise forward
+    before the timed region; one random segment-sized grad_o serves every
+    segment (the whole sequence's would not fit beside the inputs)."""
+    dev = inp["q"].device
+    R = w.segments
+    L = w.T // R
+    need = 6 * w.B * L * w.H * w.dk * 4 + kda.backward_workspace_bytes(w.B, L, w.H, w.dk, w.dv)
+    free, _ = torch.cuda.mem_get_info(dev)
+    if need > 0.9 * free:
+        log(f"[bench] segment-wise backward skipped: needs {need / 2**30:.0f} GiB, {free / 2**30:.0f} GiB free")
+        return {"skipped": f"needs {need / 2**30:.0f} GiB of device memory, {free / 2**30:.0f} GiB free"}
+    seq = ("q", "k", "v", "g", "beta", "gate")
+    part = [{x: inp[x][:, r * L:(r + 1) * L] for x in seq} for r in range(R)]
+    # the carries entering each segment
+    S = inp["S0"].clone() if inp.get("S0") is not None else torch.zeros((w.B, w.H, w.dk, w.dv), device=dev)
+    conv = torch.zeros((w.B, 3, w.cch), dtype=inp["q"].dtype, device=dev)
+    S_in, conv_in = [], []
+    for r in range(R):
+        S_in.append(S.clone())
+        conv_in.append(conv.clone())
+        pr = part[r]
+        kda.prefill(pr["q"], pr["k"], pr["v"], inp["conv_w"], pr["g"], pr["beta"], pr["gate"], S0=S,
+                    conv_in=conv, chunk=w.chunk, S_T=S, conv_out=conv)
+    torch.cuda.synchronize()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(7)
+    go = torch.randn((w.B, L, w.H, w.dv), generator=gen, device=dev)
+    gs_T = torch.randn((w.B, w.H, w.dk, w.dv), generator=gen, device=dev)
+    ws = torch.empty(kda.backward_workspace_bytes(w.B, L, w.H, w.dk, w.dv), dtype=torch.uint8, device=dev)
+
+    def call():
+        gS, gC = gs_T, None
+        for r in range(R - 1, -1, -1):
+            pr = part[r]
+            g = kda.prefill_backward(pr["q"], pr["k"], pr["v"], inp["conv_w"], pr["g"], pr["beta"], pr["gate"], go,
+                                     S0=S_in[r], conv_in=conv_in[r], grad_S_T=gS, grad_conv_out=gC, workspace=ws)
+            gS, gC = g["S0"], g["conv_in"]
+            del g  # this segment's 16 GB of input gradients go back before the next call allocates its own
+
+    call()
+    torch.cuda.synchronize()
+    per = timed_launches(torch, call, steps)
+    ms = sum(per) / len(per)
+    flops = backward_flops_per_head_token(w.dk) * w.B * w.T * w.H
+    tfs = flops / (ms * 1e-3) / 1e12
+    log(f"[bench] backward, {R} segments of {L}: {ms:.1f} ms/call, {w.B * w.T / (ms * 1e-3) / 1e6:.3f} M tokens/s, "
+        f"{tfs:.2f} TFLOP/s")
+    return {"metric": "prefill backward tokens/s", "value": w.B * w.T / (ms * 1e-3), "unit": "tokens/s",
+            "ms_per_call": ms, "calls_timed": steps,
+            "config": f"kda_prefill_backward of B{w.B} T{w.T} H{w.H} dk=dv={w.dk} as {R} carried segments of "
+                      f"{L} tokens (last first, state and conv gradients chained), bf16 inputs, fp32 gradients",
+            "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
+                         "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": None,
+                         "algorithmic_flops_per_launch": flops},
+            "workspace_bytes": ws.numel()}
+
+
 def time_backward(torch, kda, w, inp, steps):
     """kda_prefill_backward over the whole workload (all T tokens of each
     sequence), random fp32 output and final-state gradients."""
+    if w.segments > 1:
+        return time_backward_segments(torch, kda, w, inp, steps)
     dev = inp["q"].device
     # fp32 gradients of q, k, v, g, gate, grad_o, and the workspace
     need = 6 * w.B * w.T * w.H * w.dk * 4 + kda.backward_workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
