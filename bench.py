@@ -211,7 +211,8 @@ def time_backward_segments(torch, kda, w, inp, steps):
                       f"{L} tokens (last first, state and conv gradients chained), bf16 inputs, fp32 gradients",
             "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": None,
-                         "algorithmic_flops_per_launch": flops},
+                         "algorithmic_flops_per_launch": flops,
+                         "launches": f"{R} calls, each " + backward_launches(L, w.dk)},
             "workspace_bytes": ws.numel()}
 
 
@@ -251,8 +252,16 @@ def time_backward(torch, kda, w, inp, steps):
             "config": f"kda_prefill_backward B{w.B} T{w.T} H{w.H} dk=dv={w.dk}, bf16 inputs, fp32 gradients",
             "roofline": {"bound": "alu", "achieved": tfs, "peak": FP32_VALU_PEAK_TFS, "unit": "TFLOP/s",
                          "frac": tfs / FP32_VALU_PEAK_TFS, "traffic": None,
-                         "algorithmic_flops_per_launch": flops},
+                         "algorithmic_flops_per_launch": flops, "launches": backward_launches(w.T, w.dk)},
             "workspace_bytes": ws.numel()}
+
+
+def backward_launches(T, d):
+    """What one kda_prefill_backward call of T tokens launches (16-token stretches, 64 per slab)."""
+    stretches = -(-T // 16)
+    slabs = max(1, -(-stretches // 64))
+    return (f"backward_kernel<{d}, ., 1> (forward) once, then {slabs} x (mode 2: recompute of a slab, "
+            "on the compute units the reverse leaves free, overlapping mode 3: the reverse walk of the previous slab)")
 
 
 def time_context_parallel(torch, kda, w, inp, R, A, steps):
