@@ -163,3 +163,34 @@ def test_segment_chain_equals_whole_sequence():
         assert_rms_close(np.concatenate([g[x] for g in got], axis=1), whole[x], TOL_GRAD, f"d{x} (3 segments)")
     for x in ("S0", "conv_in"):
         assert_rms_close(got[0][x], whole[x], TOL_GRAD, f"d{x} (3 segments)")
+
+
+def test_unpipelined_fallback_equals_pipelined():
+    """232 heads leave too few compute units to split (the slabs then run one
+    after the other on the caller's stream); heads are independent, so batch 0
+    of that call equals, bit for bit, a 29-head call on batch 0's inputs, which
+    takes the pipelined path (two slabs: 1100 tokens)."""
+    torch, kda = need_gpu()
+    B, T, H, d = 8, 1100, 29, 16
+    w = Workload("bwdp", B, T, H, d, d, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=171)
+    inp = syn.prefill_inputs_np(w)
+    rng = np.random.default_rng(71)
+    dO = rng.standard_normal((B, T, H, d)).astype(np.float32)
+    dS = rng.standard_normal((B, H, d, d)).astype(np.float32)
+    dC = rng.standard_normal((B, 3, 3 * H * d)).astype(np.float32)
+
+    def run(sl):
+        part = {x: (a if x == "conv_w" else a[sl]) for x, a in inp.items() if a is not None}
+        dev = to_dev(part, "bf16")
+        out = kda.prefill_backward(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"],
+                                   torch.from_numpy(np.ascontiguousarray(dO[sl])).cuda(), S0=dev["S0"],
+                                   conv_in=dev["conv_in"], grad_S_T=torch.from_numpy(np.ascontiguousarray(dS[sl])).cuda(),
+                                   grad_conv_out=torch.from_numpy(np.ascontiguousarray(dC[sl])).cuda())
+        torch.cuda.synchronize()
+        return {x: out[x].cpu().numpy() for x in NAMES}
+
+    print(f"  B{B} T{T} H{H} d{d}: all heads, then batch 0 alone", flush=True)
+    whole = run(slice(0, B))
+    first = run(slice(0, 1))
+    for x in NAMES:
+        assert np.array_equal(whole[x][:1], first[x]), x
