@@ -547,6 +547,7 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, inp)
         log(f"[bench] oracle {out['cpu_baseline']['value']:.1f} tokens/s on {out['cpu_baseline']['cores']} threads")
 
+    kda.release()  # the pipeline's streams, before the runtime's teardown
     print(json.dumps(out), flush=True)
 
 

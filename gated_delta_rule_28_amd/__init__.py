@@ -13,6 +13,7 @@ works, but every call raises (there is no fallback implementation).
     o, S_T, conv_out = prefill_cp(q, k, v, conv_w, g, beta, gate, segments=R, ...)  # context-parallel
     S_start, S_T = cp_compose(N, P, S0=None, B=1)   # the composition step alone
     grads = prefill_backward(q, k, v, conv_w, g, beta, gate, grad_o, S0=None, conv_in=None, grad_S_T=None)
+    release()   # destroy the streams the library keeps between calls (kda_release)
 
 Every call also takes A=None: given an fp32 [H, dk] tensor, g and beta are K3's
 logits (g = -5 sigmoid(e^A z), beta = sigmoid(b), KDA_DECAY_K3) instead of the
@@ -27,7 +28,7 @@ __all__ = ["prefill", "decode_step", "decode_multi", "prep", "workspace_bytes", 
            "KDA_F32", "KDA_BF16", "KDA_DECAY_DIRECT", "KDA_DECAY_K3", "PrefillArgs", "DecodeArgs",
            "PrepArgs", "DecodeMultiArgs", "MAX_DECODE_TOKENS", "prefill_cp", "cp_compose",
            "cp_workspace_bytes", "CpComposeArgs", "PrefillCpArgs", "prefill_backward", "PrefillBackwardArgs",
-           "backward_workspace_bytes"]
+           "backward_workspace_bytes", "release"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -36,7 +37,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
-ABI_VERSION = 5
+ABI_VERSION = 6
 MAX_DECODE_TOKENS = 16
 
 
@@ -140,6 +141,7 @@ def lib():
         L.kda_status_string.restype = ctypes.c_char_p
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_abi_version.restype = ctypes.c_int
+        L.kda_release.restype = ctypes.c_int
         if L.kda_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libkda ABI {L.kda_abi_version()} != binding ABI {ABI_VERSION}")
         _lib = L
@@ -150,6 +152,12 @@ def _check(fn, rc):
     if rc != 0:
         L = lib()
         raise KDAError(fn, rc, f"{L.kda_status_string(rc).decode()} ({L.kda_last_error().decode()})")
+
+
+def release():
+    """kda_release: destroy the streams and events the library keeps between
+    calls (all devices and threads; call with no library call in flight)."""
+    _check("kda_release", lib().kda_release())
 
 
 def _torch():

@@ -4,9 +4,13 @@
 // Every check happens before any HIP call, so a call that fails validation
 // launches nothing and touches no device state (and can be made on a machine
 // without a GPU).
+#include <atomic>
 #include <cstdarg>
 #include <cstdint>
 #include <cstdio>
+#include <cstdlib>
+#include <mutex>
+#include <vector>
 
 #include "kda_internal.h"
 
@@ -95,6 +99,69 @@ void set_error(const char* fmt, ...) {
   va_end(ap);
 }
 
+// ---- streams and events kept between calls -------------------------------------
+// Handles are heap-held in a leaked registry, so they are still reachable when
+// the exit handler runs, whatever order static objects are destroyed in.
+namespace {
+struct Kept {
+  std::mutex mu;
+  std::vector<hipStream_t> streams;
+  std::vector<hipEvent_t> events;
+};
+Kept& kept() {
+  static Kept* k = new Kept;
+  return *k;
+}
+std::atomic<unsigned> g_generation{1};
+std::once_flag g_at_exit;
+
+// Destroy everything registered; the first failure is returned (the rest are
+// still destroyed).
+hipError_t release_all() {
+  Kept& k = kept();
+  std::lock_guard<std::mutex> lock(k.mu);
+  g_generation.fetch_add(1);
+  hipError_t first = hipSuccess;
+  for (hipStream_t s : k.streams) {
+    hipError_t e = hipStreamSynchronize(s);
+    if (e == hipSuccess) e = hipStreamDestroy(s);
+    if (first == hipSuccess) first = e;
+  }
+  for (hipEvent_t ev : k.events) {
+    const hipError_t e = hipEventDestroy(ev);
+    if (first == hipSuccess) first = e;
+  }
+  k.streams.clear();
+  k.events.clear();
+  return first;
+}
+
+// Registered with atexit() when the first handle is kept, which is after the
+// HIP runtime (and any tool loaded with it) registered its own teardown, so
+// this runs before that teardown.
+void release_at_exit() { (void)release_all(); }
+
+void arm_exit_release() {
+  std::call_once(g_at_exit, [] { std::atexit(release_at_exit); });
+}
+}  // namespace
+
+void keep(hipStream_t s) {
+  arm_exit_release();
+  Kept& k = kept();
+  std::lock_guard<std::mutex> lock(k.mu);
+  k.streams.push_back(s);
+}
+
+void keep(hipEvent_t e) {
+  arm_exit_release();
+  Kept& k = kept();
+  std::lock_guard<std::mutex> lock(k.mu);
+  k.events.push_back(e);
+}
+
+unsigned release_generation() { return g_generation.load(); }
+
 }  // namespace kda
 
 using kda::fail;
@@ -102,6 +169,12 @@ using kda::fail;
 extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
+
+int kda_release(void) {
+  const hipError_t e = kda::release_all();
+  if (e != hipSuccess) return fail(KDA_E_HIP, "release: %s", hipGetErrorString(e));
+  return KDA_OK;
+}
 
 const char* kda_last_error(void) { return kda::g_err; }
 

@@ -620,9 +620,11 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
 // up to a multiple of 8, so each of the eight accelerator dies gets the same
 // share: mask bits interleave over the dies).  The reverse launches run on
 // that many compute units, the recompute launches on the others, alternating
-// between two streams.  Created on first use and kept for the life of the thread.
+// between two streams.  Created on first use and kept until kda_release() or
+// process exit.
 struct BwdPipe {
   int n_rev = 0;
+  unsigned gen = 0;  // release_generation() when created
   hipStream_t rev = nullptr, rec[2] = {nullptr, nullptr};
   hipEvent_t fork = nullptr, rec_done[2] = {nullptr, nullptr}, rev_done[2] = {nullptr, nullptr};
   hipEvent_t join[3] = {nullptr, nullptr, nullptr};
@@ -652,6 +654,10 @@ int get_bwd_pipe(int heads, BwdPipe*& pp) {
   const int ncu = ncus[dev];
   const int n_rev = (heads + 7) / 8 * 8;
   if (n_rev + 32 > ncu) return KDA_OK;  // too few compute units left for the recompute
+  // slots made before the last kda_release() hold destroyed handles
+  const unsigned gen = release_generation();
+  for (int k = 0; k < kPerDev; ++k)
+    if (pipes[dev][k].n_rev != 0 && pipes[dev][k].gen != gen) pipes[dev][k] = BwdPipe{};
   BwdPipe* slot = nullptr;
   for (int k = 0; k < kPerDev && slot == nullptr; ++k)
     if (pipes[dev][k].n_rev == n_rev) slot = &pipes[dev][k];
@@ -668,11 +674,19 @@ int get_bwd_pipe(int heads, BwdPipe*& pp) {
     hipEvent_t* evs[8] = {&slot->fork, &slot->rec_done[0], &slot->rec_done[1], &slot->rev_done[0],
                           &slot->rev_done[1], &slot->join[0], &slot->join[1], &slot->join[2]};
     for (int k = 0; k < 8 && e == hipSuccess; ++k) e = hipEventCreateWithFlags(evs[k], hipEventDisableTiming);
+    // everything created is registered, so kda_release() (or process exit) frees it
+    if (slot->rev != nullptr) keep(slot->rev);
+    for (int k = 0; k < 2; ++k)
+      if (slot->rec[k] != nullptr) keep(slot->rec[k]);
+    for (int k = 0; k < 8; ++k)
+      if (*evs[k] != nullptr) keep(*evs[k]);
     if (e != hipSuccess) {
+      *slot = BwdPipe{};
       set_error("backward: stream / event creation failed: %s", hipGetErrorString(e));
       return KDA_E_HIP;
     }
     slot->n_rev = n_rev;
+    slot->gen = gen;
   }
   pp = slot;
   return KDA_OK;

@@ -35,4 +35,12 @@ int launch_prefill_backward(const kda_prefill_backward_args& a, hipStream_t s);
 // Set the calling thread's last-error text (printf-style).
 void set_error(const char* fmt, ...);
 
+// Streams and events kept between calls (kda_api.cpp).  keep() registers one
+// for kda_release(); the first registration also arranges the release at
+// process exit.  A cached handle is valid while release_generation() still
+// returns the value read when it was created.
+void keep(hipStream_t s);
+void keep(hipEvent_t e);
+unsigned release_generation();
+
 }  // namespace kda

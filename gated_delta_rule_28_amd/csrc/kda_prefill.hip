@@ -24,11 +24,16 @@
 //
 // Precision: matrix-core operands are fp16 (bf16 would put the max error at
 // several 1e-2 of RMS; fp16 has the same rate and three more mantissa bits),
-// accumulation fp32, state fp32, output fp32 by default.  When some tile's
-// span exceeds what fp16 holds at full precision (e^8), that chunk's
-// decay-weighted operands are bf16 instead (finite up to e^88, but with
-// bf16's 8-bit precision on those products).  fp32 inputs use fp32
-// operands on the fp32 matrix-core instruction throughout.
+// accumulation fp32, state fp32, output fp32 by default.  The exceptions are
+// where a factor can leave fp16's range or a single rounding shows:
+//   * the column operand of the A and P tiles, k e^{rho_b - G} (up to e^80 at
+//     K3's bound of -5 per token), is kept in fp32 and those products run on
+//     the fp32 matrix-core instruction, with the fp16 row operands widened;
+//   * in a chunk where some 16-token tile decays by more than e^8 ("wide":
+//     the state then forgets nearly everything per token, so S_T and o are
+//     dominated by the last tokens' U), U enters the P U and
+//     (K e^{G_C-G})^T U products as an fp16 pair hi + lo (about 22 bits).
+// fp32 inputs use fp32 operands on the fp32 matrix-core instruction throughout.
 //
 // Work decomposition: one workgroup (8 waves) per (b, h) walks the chunks in
 // order; the fp32 state stays in VGPRs as matrix-core accumulators, each wave
@@ -51,10 +56,8 @@ namespace {
 
 constexpr int kThreads = 512;  // 8 waves
 constexpr int kWaves = kThreads / 64;
-// Largest decay span of a 16-token tile (per channel, in nats) for which the
-// decay-weighted operands stay fp16: column factors reach e^span and row
-// factors e^-span, and both must stay in fp16's normal range (6e-5 .. 6.5e4)
-// after multiplying a normalised key component.
+// Largest decay span of a 16-token tile (per channel, in nats) below which a
+// chunk is not "wide" (see the precision notes above).
 constexpr float kF16SpanMax = 8.0f;
 
 struct PrefillParams {
@@ -153,9 +156,7 @@ __device__ __forceinline__ void raw_unpack_if(const Raw8<BF16>& r, bool ok, floa
 __device__ __forceinline__ uint16_t to_f16_bits(float x) {
   return __builtin_bit_cast(uint16_t, (_Float16)x);
 }
-__device__ __forceinline__ uint16_t to_op16(float x, bool bf) {
-  return bf ? f_to_bf16(x) : to_f16_bits(x);
-}
+__device__ __forceinline__ uint16_t to_op16(float x) { return to_f16_bits(x); }
 
 template <bool F32>
 __device__ __forceinline__ void frag_zero(Frag<F32>& f) {
@@ -217,35 +218,34 @@ __device__ __forceinline__ void frag_perm(Frag<F32>& f, const OpT<F32>* buf, int
 
 // c += A(16x32) * B(32x16) with the lane layout of kda_device.h.
 template <bool F32>
-__device__ __forceinline__ f4 mma(const Frag<F32>& a, const Frag<F32>& b, f4 c, bool bf = false) {
+__device__ __forceinline__ f4 mma(const Frag<F32>& a, const Frag<F32>& b, f4 c) {
   if constexpr (F32) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.v[e], b.v[e], c, 0, 0, 0);
     return c;
   } else {
-    if (bf) return mma_bf16(__builtin_bit_cast(bf16x8, a.v), __builtin_bit_cast(bf16x8, b.v), c);
     return mma_f16(a.v, b.v, c);
   }
 }
 
 template <bool F32>
-__device__ __forceinline__ void st_op(OpT<F32>* p, float x, bool bf) {
+__device__ __forceinline__ void st_op(OpT<F32>* p, float x) {
   if constexpr (F32) *p = x;
-  else *p = to_op16(x, bf);
+  else *p = to_op16(x);
 }
 
 // 8 consecutive operand elements from 8 fp32 values.
 template <bool F32>
-__device__ __forceinline__ void st_op8(OpT<F32>* p, const float* x, bool bf) {
+__device__ __forceinline__ void st_op8(OpT<F32>* p, const float* x) {
   if constexpr (F32) {
     *reinterpret_cast<float4*>(p) = make_float4(x[0], x[1], x[2], x[3]);
     *reinterpret_cast<float4*>(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
   } else {
     uint4 u;
-    u.x = (uint32_t)to_op16(x[0], bf) | ((uint32_t)to_op16(x[1], bf) << 16);
-    u.y = (uint32_t)to_op16(x[2], bf) | ((uint32_t)to_op16(x[3], bf) << 16);
-    u.z = (uint32_t)to_op16(x[4], bf) | ((uint32_t)to_op16(x[5], bf) << 16);
-    u.w = (uint32_t)to_op16(x[6], bf) | ((uint32_t)to_op16(x[7], bf) << 16);
+    u.x = (uint32_t)to_op16(x[0]) | ((uint32_t)to_op16(x[1]) << 16);
+    u.y = (uint32_t)to_op16(x[2]) | ((uint32_t)to_op16(x[3]) << 16);
+    u.z = (uint32_t)to_op16(x[4]) | ((uint32_t)to_op16(x[5]) << 16);
+    u.w = (uint32_t)to_op16(x[6]) | ((uint32_t)to_op16(x[7]) << 16);
     *reinterpret_cast<uint4*>(p) = u;
   }
 }
@@ -253,18 +253,13 @@ __device__ __forceinline__ void st_op8(OpT<F32>* p, const float* x, bool bf) {
 // Scale the 8 elements of a fragment by f[0..7] (fp32, 16-byte aligned),
 // rounding back to the operand type.
 template <bool F32>
-__device__ __forceinline__ void frag_scale(Frag<F32>& fr, const float* f, bool bf) {
+__device__ __forceinline__ void frag_scale(Frag<F32>& fr, const float* f) {
   const float4 a = *reinterpret_cast<const float4*>(f);
   const float4 c = *reinterpret_cast<const float4*>(f + 4);
   const float s[8] = {a.x, a.y, a.z, a.w, c.x, c.y, c.z, c.w};
   if constexpr (F32) {
 #pragma unroll
     for (int e = 0; e < 8; ++e) fr.v[e] *= s[e];
-  } else if (bf) {
-    bf16x8 v = __builtin_bit_cast(bf16x8, fr.v);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) v[e] = (__bf16)((float)v[e] * s[e]);
-    fr.v = __builtin_bit_cast(half8, v);
   } else {
 #pragma unroll
     for (int e = 0; e < 8; ++e) fr.v[e] = (_Float16)((float)fr.v[e] * s[e]);
@@ -304,23 +299,32 @@ struct Smem {
   static constexpr int LDC = C + PAD;                // rows of chunk-wide operands
   static constexpr int LDT = C + PAD;                // rows of transposed operands
   static constexpr int LDA = C + 4;                  // fp32 A and T
+  // region X, phase 0 (stage 1a/1b only): sums of g per 4-token k block
+  static constexpr int BTOT = 0;                            // [16][DK] fp32
+  static constexpr int BTOT_BYTES = 16 * DK * 4;
   // region X, phase 1: decay-weighted A/P operands
+  static constexpr int LDRF = DK + 4;                       // rows of the fp32 column operand
   static constexpr int QR = 0;                              // [C][LDR]  q^ e^{G - rho_tile}
   static constexpr int KR = QR + C * LDR * E;               // [C][LDR]  k^ e^{G - rho_tile}
-  static constexpr int KC = KR + C * LDR * E;               // [C][LDR]  k^ e^{rho_tile - G}
-  static constexpr int X1 = KC + C * LDR * E;
+  static constexpr int KC = KR + C * LDR * E;               // [C][LDRF] k^ e^{rho_tile - G}, fp32
+  static constexpr int X1 = KC + C * LDRF * 4;
+  // wide chunks (16-bit operands): the A/P rows in fp32 instead, q's over QR
+  // and KR, k's over QG and KGT (rebuilt from these rows after the products)
+  static constexpr int QRF = QR;                            // [C][LDRF] fp32
   // region X, phase 2 (after the A/P products)
   static constexpr int AS = 0;                              // [C][LDA] fp32
   static constexpr int TS = AS + C * LDA * 4;               // [C][LDA] fp32
   static constexpr int TB = TS + C * LDA * 4;               // [C][LDC] T diag(beta)
   static constexpr int PS = TB + C * LDC * E;               // [C][LDC] P
   static constexpr int X2 = PS + C * LDC * E;
-  static constexpr int XE = X1 > X2 ? X1 : X2;
+  static constexpr int XE0 = X1 > X2 ? X1 : X2;
+  static constexpr int XE = XE0 > BTOT_BYTES ? XE0 : BTOT_BYTES;
   // region Y: operands of the W / U~ / inter-chunk products
   static constexpr int QG = (XE + 15) / 16 * 16;            // [C][LDR]   q^ e^G
   static constexpr int KGT = QG + C * LDR * E;              // [DK][LDT]  (k^ e^G)^T, later W [C][LDR]
   static constexpr int KGT_BYTES = (DK * LDT > C * LDR ? DK * LDT : C * LDR) * E;
   static constexpr int KBT = KGT + KGT_BYTES;               // [DK][LDT]  (k^ e^{G_C-G})^T
+  static constexpr int KRF = QG;                            // [C][LDRF] fp32, wide chunks
   static constexpr int VT = KBT + DK * LDT * E;             // [DV][LDT]  v^T
   // small fp32 arrays
   static constexpr int BETA = VT + DV * LDT * E;            // [C]
@@ -329,9 +333,7 @@ struct Smem {
   static constexpr int RHO = GC + DK * 4;                   // [NT][DK]  rho_a
   static constexpr int ERHO = RHO + NT * DK * 4;            // [NT][DK]  e^{rho_a}
   static constexpr int FAB = ERHO + NT * DK * 4;            // [NOFF][DK] e^{rho_a - rho_b}, b < a
-  static constexpr int BTOT = FAB + (NOFF > 0 ? NOFF : 1) * DK * 4;  // [16][DK] sums of g per k block
-  static constexpr int BTOT_BYTES = 16 * DK * 4;
-  static constexpr int CW = BTOT + BTOT_BYTES;              // [2dk+dv][4] conv taps of the head
+  static constexpr int CW = FAB + (NOFF > 0 ? NOFF : 1) * DK * 4;  // [2dk+dv][4] conv taps of the head
   static constexpr int FLAG = CW + (2 * DK + DV) * 16;      // [4] ints
   // O of a chunk, staged for the epilogue: [C][DV+4] fp32, in A / T's space
   // (dead by then) when it fits, else after everything else
@@ -339,6 +341,8 @@ struct Smem {
   static constexpr int OS_BYTES = C * LDO * 4;
   static constexpr int OS = OS_BYTES <= TB ? 0 : FLAG + 16;
   static constexpr int BYTES = OS_BYTES <= TB ? FLAG + 16 : FLAG + 16 + OS_BYTES;
+  static_assert(F32 || QRF + C * LDRF * 4 <= KC, "wide-chunk q rows overlap the column operand");
+  static_assert(F32 || KRF + C * LDRF * 4 <= KBT, "wide-chunk k rows overlap (k e^{G_C-G})^T");
 };
 
 // index of the pair (a, b), b < a, among the strictly-lower tile pairs
@@ -597,12 +601,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   Op* sQR = reinterpret_cast<Op*>(smem + L::QR);
   Op* sKR = reinterpret_cast<Op*>(smem + L::KR);
-  Op* sKC = reinterpret_cast<Op*>(smem + L::KC);
+  float* sKC = reinterpret_cast<float*>(smem + L::KC);
   float* sA = reinterpret_cast<float*>(smem + L::AS);
   float* sT = reinterpret_cast<float*>(smem + L::TS);
   Op* sTB = reinterpret_cast<Op*>(smem + L::TB);
   Op* sP = reinterpret_cast<Op*>(smem + L::PS);
   Op* sQG = reinterpret_cast<Op*>(smem + L::QG);
+  float* sQRf = reinterpret_cast<float*>(smem + L::QRF);  // wide chunks (16-bit operands)
+  float* sKRf = reinterpret_cast<float*>(smem + L::KRF);
   Op* sKGT = reinterpret_cast<Op*>(smem + L::KGT);
   Op* sW = reinterpret_cast<Op*>(smem + L::KGT);   // W replaces (k e^G)^T after stage 4
   Op* sKBT = reinterpret_cast<Op*>(smem + L::KBT);
@@ -807,7 +813,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           sGC[c8 + e] = rho[NT][e];
           sGam[c8 + e] = fast_exp(rho[NT][e]);
         }
-      } else if constexpr (!F32) {
+      } else {
         float mx = 0.f;
 #pragma unroll
         for (int a = 0; a < NT; ++a)
@@ -825,7 +831,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int e = 0; e < 8; ++e) G[e] += sBtot[q * DK + c8 + e];
     }
     lds_barrier();
-    const bool bfAP = sFlag[0] != 0;  // decay-weighted operands in bf16 for this chunk
+    const bool wide = __builtin_amdgcn_readfirstlane(sFlag[0]) != 0;  // U split in two fp16 parts
 
     // ---- stage 1c: conv + SiLU + L2, then the decay-scaled operands -----------
     auto token_work = [&](int tt, bool is_k) {
@@ -849,7 +855,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
       }
       if (it.role == 2) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) st_op<F32>(sVT + tidx<C, LDT>(c8 + e, tau), x[e], false);
+        for (int e = 0; e < 8; ++e) st_op<F32>(sVT + tidx<C, LDT>(c8 + e, tau), x[e]);
         return;
       }
       l2norm<DK>(x, is_k ? 1.0f : fast_rsq((float)DK));
@@ -867,19 +873,28 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         rowv[e] = x[e] * er[e];
         xg[e] = rowv[e] * erho[e];         // x e^{G}
       }
+      // A wide chunk keeps the rows in fp32 (the in-tile column factor can make
+      // up for a row factor below fp16's range); q e^G and (k e^G)^T are then
+      // rebuilt from those rows after the A / P products.
+      const bool rows32 = !F32 && wide;
       if (!is_k) {
-        st_op8<F32>(sQR + tau * LDR + c8, rowv, bfAP);
-        st_op8<F32>(sQG + tau * LDR + c8, xg, false);
+        if (rows32) {
+          st_op8<true>(sQRf + tau * L::LDRF + c8, rowv);
+        } else {
+          st_op8<F32>(sQR + tau * LDR + c8, rowv);
+          st_op8<F32>(sQG + tau * LDR + c8, xg);
+        }
       } else {
-        st_op8<F32>(sKR + tau * LDR + c8, rowv, bfAP);
+        if (rows32) st_op8<true>(sKRf + tau * L::LDRF + c8, rowv);
+        else st_op8<F32>(sKR + tau * LDR + c8, rowv);
         float cv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           cv[e] = x[e] * fast_rcp(er[e]);  // k e^{rho_bt - G}
-          st_op<F32>(sKGT + tidx<C, LDT>(c8 + e, tau), xg[e], false);
-          st_op<F32>(sKBT + tidx<C, LDT>(c8 + e, tau), x[e] * fast_exp(sGC[c8 + e] - G[e]), false);
+          if (!rows32) st_op<F32>(sKGT + tidx<C, LDT>(c8 + e, tau), xg[e]);
+          st_op<F32>(sKBT + tidx<C, LDT>(c8 + e, tau), x[e] * fast_exp(sGC[c8 + e] - G[e]));
         }
-        st_op8<F32>(sKC + tau * LDR + c8, cv, bfAP);
+        st_op8<true>(sKC + tau * L::LDRF + c8, cv);
       }
     };
     if (it.role == 1) {
@@ -912,15 +927,50 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int ks = 0; ks < KSD; ++ks) {
           const int k0 = 32 * ks + 8 * gq;
-          Frag<F32> fa, fb;
-          frag_std<F32>(fa, rowb, 16 * a + li, LDR, k0, k0 < DK);
-          frag_std<F32>(fb, sKC, 16 * bcol + li, LDR, k0, k0 < DK);
-          if (bcol < a && k0 < DK) frag_scale<F32>(fb, sFab + off_pair(a, bcol) * DK + k0, bfAP);
-          acc[jj] = mma<F32>(fa, fb, acc[jj], bfAP);
+          Frag<true> fa, fb;  // fp32 instruction: the column factor needs fp32's range
+          if constexpr (F32) {
+            frag_std<true>(fa, rowb, 16 * a + li, LDR, k0, k0 < DK);
+          } else if (wide) {
+            frag_std<true>(fa, isP ? sQRf : sKRf, 16 * a + li, L::LDRF, k0, k0 < DK);
+          } else {
+            Frag<false> f16;
+            frag_std<false>(f16, rowb, 16 * a + li, LDR, k0, k0 < DK);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) fa.v[e] = (float)f16.v[e];
+          }
+          frag_std<true>(fb, sKC, 16 * bcol + li, L::LDRF, k0, k0 < DK);
+          if (bcol < a && k0 < DK) frag_scale<true>(fb, sFab + off_pair(a, bcol) * DK + k0);
+          acc[jj] = mma<true>(fa, fb, acc[jj]);
         }
       }
     }
+    // wide chunks: q e^G and k e^G from the fp32 rows (x e^{G - rho_tile} times
+    // e^{rho_tile}, the same products the plain path stores), read before the
+    // barrier since the k rows sit where they go
+    constexpr int NRB = (C * DK + kThreads - 1) / kThreads;
+    float qgv[NRB], kgv[NRB];
+    if (!F32 && wide) {
+#pragma unroll
+      for (int j = 0; j < NRB; ++j) {
+        const int idx = tid + kThreads * j;
+        const int r = min(idx / DK, C - 1), c = idx % DK;
+        const float er = sERho[(r >> 4) * DK + c];
+        qgv[j] = sQRf[r * L::LDRF + c] * er;
+        kgv[j] = sKRf[r * L::LDRF + c] * er;
+      }
+    }
     lds_barrier();  // region X (A/P operands) is dead from here on
+    if (!F32 && wide) {
+#pragma unroll
+      for (int j = 0; j < NRB; ++j) {
+        const int idx = tid + kThreads * j;
+        if (idx < C * DK) {
+          const int r = idx / DK, c = idx % DK;
+          st_op<F32>(sQG + r * LDR + c, qgv[j]);
+          st_op<F32>(sKGT + tidx<C, LDT>(c, r), kgv[j]);
+        }
+      }
+    }
 #pragma unroll
     for (int jj = 0; jj < JPW; ++jj) {
       const int job = wave + kWaves * jj;
@@ -934,7 +984,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         for (int r = 0; r < 4; ++r) {
           const int row = 16 * a + 4 * gq + r;
           const int col = 16 * bcol + li;
-          if (isP) st_op<F32>(sP + row * LDC + col, row >= col ? acc[jj][r] : 0.f, false);
+          if (isP) st_op<F32>(sP + row * LDC + col, row >= col ? acc[jj][r] : 0.f);
           else sA[row * LDA + col] = row > col ? sBeta[row] * acc[jj][r] : 0.f;
         }
       }
@@ -942,7 +992,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     // upper tiles of P are zero (P.U runs over whole 32-token steps)
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int row = idx / C, col = idx - row * C;
-      if ((col >> 4) > (row >> 4)) st_op<F32>(sP + row * LDC + col, 0.f, false);
+      if ((col >> 4) > (row >> 4)) st_op<F32>(sP + row * LDC + col, 0.f);
     }
     lds_barrier();
 
@@ -1009,7 +1059,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
     for (int idx = tid; idx < C * C; idx += kThreads) {
       const int row = idx / C, col = idx - row * C;
       const float v = (col >> 4) > (row >> 4) ? 0.f : sT[row * LDA + col] * sBeta[col];
-      st_op<F32>(sTB + row * LDC + col, v, false);
+      st_op<F32>(sTB + row * LDC + col, v);
     }
     lds_barrier();
 
@@ -1050,7 +1100,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
 #pragma unroll
       for (int rt = 0; rt < NT; ++rt)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) st_op<F32>(sW + (16 * rt + 4 * gq + r) * LDR + 16 * wave + li, Wt[rt][r], false);
+        for (int r = 0; r < 4; ++r) st_op<F32>(sW + (16 * rt + 4 * gq + r) * LDR + 16 * wave + li, Wt[rt][r]);
     }
     lds_barrier();
 
@@ -1091,7 +1141,9 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         U[rt] = U[rt] - ws;
       }
       // U as B operand over tokens, same permutation
-      Frag<F32> Ub[KSC];
+      // (wide chunks, 16-bit operands: also the remainder U - Ub in fp16)
+      const bool split = !F32 && wide;
+      Frag<F32> Ub[KSC], Ul[KSC];
 #pragma unroll
       for (int kt = 0; kt < KSC; ++kt) {
         float x[8];
@@ -1101,6 +1153,12 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           x[4 + r] = (2 * kt + 1 < NT) ? U[2 * kt + 1][r] : 0.f;
         }
         frag_from_f<F32>(Ub[kt], x);
+        if constexpr (!F32) {
+          if (split) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) Ul[kt].v[e] = (_Float16)(x[e] - (float)Ub[kt].v[e]);
+          }
+        }
       }
       // O = (Q e^G) S + P U
 #pragma unroll
@@ -1118,6 +1176,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
             Frag<F32> fa;
             frag_perm<F32>(fa, sP, 16 * rt + li, LDC, 32 * kt, gq, true, 32 * kt + 16 < C);
             o = mma<F32>(fa, Ub[kt], o);
+            if (split) o = mma<F32>(fa, Ul[kt], o);
           }
         }
         O[rt] = o;
@@ -1133,6 +1192,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
           Frag<F32> fa;
           frag_perm_t<F32, C, LDT>(fa, sKBT, 16 * t + li, 32 * kt, gq, 32 * kt + 16 < C);
           s = mma<F32>(fa, Ub[kt], s);
+          if (split) s = mma<F32>(fa, Ul[kt], s);
         }
         S[t] = s;
       }

@@ -37,9 +37,18 @@
 // 32k + 8g + 0..7: W and Q e^G fragments are then plain row-major pieces.
 // S0 and S_T stay in natural order in memory.
 //
-// Precision as in kda_prefill.hip: fp16 operands (bf16 for the decay-weighted
-// A / P operands of a chunk in which some 16-token tile decays by more than
-// e^8), fp32 accumulation, fp32 state and output.
+// Precision: fp16 matrix-core operands, fp32 accumulation, fp32 state and
+// output.  A chunk in which some 16-token tile decays by more than e^8 in some
+// channel ("wide" chunk: the in-tile column factors e^{rho_a - G} leave fp16's
+// range, reaching e^80 at K3's bound of -5 per token) takes two extra steps:
+//   * the diagonal 16x16 blocks of A and P run on the fp32 matrix-core
+//     instruction with fp32 column factors (fp32 holds e^{+-80});
+//   * U enters the P U and (K e^{G_C-G})^T U products as an fp16 pair
+//     hi + lo (about 22 significant bits): when the state forgets nearly
+//     everything per token, S_T and o are dominated by the last tokens' U
+//     and a single fp16 rounding of U is visible at the 2e-2 x RMS bound.
+// Every other operand keeps fp16: all other decay factors are <= 1, so their
+// rounding is relative to entries of at most unit size.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -61,7 +70,8 @@ constexpr int WS_QG = WS_KG + 16 * kFrag;    // Q e^G    fragments (rt, k)      
 constexpr int WS_KB = WS_QG + 16 * kFrag;    // (K e^{G_C-G})^T fragments (m, k') 16
 constexpr int WS_P = WS_KB + 16 * kFrag;     // P        fragments (rt, k'), k' <= rt/2: 6
 constexpr int WS_TB = WS_P + 6 * kFrag;      // T diag(beta) fragments, as P: 6
-constexpr int WS_GAM = WS_TB + 6 * kFrag;    // e^{G_C} in state row order, 128 fp32 (+pad)
+constexpr int WS_GAM = WS_TB + 6 * kFrag;    // e^{G_C} in state row order, 128 fp32; int "wide" flag at +512
+constexpr int WS_WIDE = WS_GAM + 512;        // int: the chunk is wide (see the file header)
 constexpr int WS_STAGE = WS_GAM + 4 * kFrag; // bytes the second kernel stages through LDS (64 KiB)
 constexpr int WS_V = WS_STAGE;               // V (rt, w): C layout, 64 lanes x 8 fp16   16 KiB
 constexpr int WS_CHUNK = WS_V + 16 * kFrag;  // 80 KiB per chunk
@@ -111,33 +121,6 @@ __device__ __forceinline__ half8 to_half8(const float* x) {
 #pragma unroll
   for (int e = 0; e < 8; ++e) h[e] = (_Float16)x[e];
   return h;
-}
-
-// Eight fp32 values as a matrix-core operand: fp16, or bf16 bits when `bf`.
-__device__ __forceinline__ half8 to_op8(const float* x, bool bf) {
-  if (bf) {
-    bf16x8 t;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) t[e] = (__bf16)x[e];
-    return __builtin_bit_cast(half8, t);
-  }
-  return to_half8(x);
-}
-
-__device__ __forceinline__ void from_op8(const half8& h, bool bf, float* x) {
-  if (bf) {
-    const bf16x8 t = __builtin_bit_cast(bf16x8, h);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)t[e];
-  } else {
-#pragma unroll
-    for (int e = 0; e < 8; ++e) x[e] = (float)h[e];
-  }
-}
-
-__device__ __forceinline__ f4 mma16(const half8& a, const half8& b, const f4& c, bool bf) {
-  if (bf) return mma_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c);
-  return mma_f16(a, b, c);
 }
 
 // a + w1 * t_{-1} + w2 * t_{-2} + w3 * t_{-3} for a causal conv along the
@@ -361,7 +344,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 
   // ---- per-channel decay factors of the chunk -----------------------------------
   {
-    bool wide = false;
+    bool span_big = false;
     for (int idx = tid; idx < 4 * kD; idx += 256) {
       const int a = idx >> 7, ch = idx & (kD - 1);
       const float t0 = sTot[ch], t1 = sTot[kD + ch], t2 = sTot[2 * kD + ch], t3 = sTot[3 * kD + ch];
@@ -371,7 +354,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       sERho[idx] = fast_exp(rho);
       sETot[idx] = fast_exp(ta);
       sEKb[idx] = fast_exp(gc - rho - ta);
-      wide |= -ta > kSpanF16;
+      span_big |= -ta > kSpanF16;
     }
     for (int idx = tid; idx < 3 * kD; idx += 256) {
       const int pr = idx >> 7, ch = idx & (kD - 1);
@@ -383,10 +366,12 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       const float gc = sTot[ch] + sTot[kD + ch] + sTot[2 * kD + ch] + sTot[3 * kD + ch];
       reinterpret_cast<float*>(wsb + WS_GAM)[tid] = fast_exp(gc);
     }
-    if (__any(wide) && lane == 0) atomicOr(sFlag, 1);
+    if (__any(span_big) && lane == 0) atomicOr(sFlag, 1);
   }
   lds_barrier();
-  const bool bf = *sFlag != 0;  // decay-weighted A / P operands in bf16 for this chunk
+  // wide chunk: fp32 diagonal blocks of A and P here, split U in the recurrence
+  const bool wide = __builtin_amdgcn_readfirstlane(*sFlag) != 0;
+  if (tid == 0) *reinterpret_cast<int*>(wsb + WS_WIDE) = wide ? 1 : 0;
 
   // e^{G - rho_a} of this lane's channels
   float E[32];
@@ -414,12 +399,26 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
         qr[e] = x[8 * kp + e] * E[8 * kp + e];
         qg[e] = qr[e] * er[e];
       }
-      QrowF[kp] = to_op8(qr, bf);
+      // a wide chunk keeps q's normalised value here: the k phase applies the
+      // factor in fp32 for the diagonal blocks (it may underflow fp16 while the
+      // in-tile column factor makes up for it), then forms the fp16 operand
+      if (wide) {
+        QrowF[kp] = to_half8(&x[8 * kp]);
+      } else {
+        QrowF[kp] = to_half8(qr);
+      }
       st_nt(wsb + WS_QG + ((wave * 4 + kp) * 64 + lane) * 16, to_half8(qg));
     }
   }
   // ---- k: rows and columns of A / P, K e^G, K e^{G_C - G} ---------------------------
-  half8 KrowF[4], CdiagF[4];
+  // Wide chunks form the diagonal blocks (D[j][r], j, r in this wave's tile) here
+  // on the fp32 instruction: column k e^{rho_a - G}, rows k e^{G - rho_a} and
+  // q e^{G - rho_a} in fp32 (q from its fp16 normalised value).  Instruction
+  // (kp, e) contracts over channels 32kp + 8g + e, g = 0..3.
+  // Other chunks form them here too, on the fp16 instruction, so the column
+  // operand k e^{rho_a - G} is never held.
+  half8 KrowF[4];
+  f4 diagA = f4{0.f, 0.f, 0.f, 0.f}, diagP = f4{0.f, 0.f, 0.f, 0.f};
   {
     float x[32];
     mask_halo(ha);
@@ -427,7 +426,6 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
     });
-    load_raw(p.v, 2, rb, hb);  // v's raw values land during the rest of k's work
     __builtin_amdgcn_sched_barrier(0);
     l2norm128(x, 1.0f);
 #pragma unroll
@@ -445,18 +443,38 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
         kb[e] = cc[e] * ek[e];           // k e^{G_C - G}
         kg[e] = -kr[e] * er[e];          // -k e^{G}
       }
-      KrowF[kp] = to_op8(kr, bf);
-      CdiagF[kp] = to_op8(cd, bf);
+      KrowF[kp] = to_half8(kr);
+      if (wide) {
+        float qr[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qr[e] = (float)QrowF[kp][e] * E[8 * kp + e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          diagA = __builtin_amdgcn_mfma_f32_16x16x4f32(cd[e], kr[e], diagA, 0, 0, 0);
+          diagP = __builtin_amdgcn_mfma_f32_16x16x4f32(cd[e], qr[e], diagP, 0, 0, 0);
+        }
+        QrowF[kp] = to_half8(qr);
+      } else {
+        const half8 cdf = to_half8(cd);
+        diagA = mma_f16(cdf, KrowF[kp], diagA);
+        diagP = mma_f16(cdf, QrowF[kp], diagP);
+      }
       st_nt(wsb + WS_KG + ((wave * 4 + kp) * 64 + lane) * 16, to_half8(kg));
-      if (wave < 3) sCC[(wave * 4 + kp) * 64 + lane] = to_op8(cc, bf);
+      if (wave < 3) sCC[(wave * 4 + kp) * 64 + lane] = to_half8(cc);
 #pragma unroll
       for (int e = 0; e < 8; ++e) sKBT[tix(32 * kp + 8 * g + e, tok)] = (_Float16)kb[e];
     }
   }
+  // v's raw values are requested only now: issued during k's work they held 32
+  // more registers at its peak and the kernel spilled (measured slower)
+  load_raw(p.v, 2, rb, hb);
   // ---- v -----------------------------------------------------------------------------
   half8 Vf[4];
   mask_halo(hb);
   conv_silu(rb, hb, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
+  // v's conv completes here rather than being sunk past the barrier into the
+  // products below (where its raw values would stay live)
+  asm volatile("" : "+v"(Vf[0]), "+v"(Vf[1]), "+v"(Vf[2]), "+v"(Vf[3]));
   lds_barrier();
 
   // ---- A^T and P^T blocks (b, a), b <= a: D[j][r] = sum_c col_b[j][c] row_a[r][c] --
@@ -467,26 +485,22 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   for (int bb = 0; bb < 4; ++bb) {
     accA[bb] = f4{0.f, 0.f, 0.f, 0.f};
     accP[bb] = f4{0.f, 0.f, 0.f, 0.f};
-    if (bb <= wave) {
+    if (bb == wave) {
+      accA[bb] = diagA;
+      accP[bb] = diagP;
+    } else if (bb < wave) {
 #pragma unroll
       for (int kp = 0; kp < 4; ++kp) {
-        half8 fa;
-        if (bb == wave) {
-          fa = CdiagF[kp];
-        } else {
-          fa = sCC[(bb * 4 + kp) * 64 + lane];
-          if (bb < wave - 1) {
-            const int pr = wave == 2 ? 0 : 1 + bb;
-            float xv[8], fv[8];
-            from_op8(fa, bf, xv);
-            ld8f(sFoff + pr * kD + 32 * kp + 8 * g, fv);
+        half8 fa = sCC[(bb * 4 + kp) * 64 + lane];
+        if (bb < wave - 1) {
+          const int pr = wave == 2 ? 0 : 1 + bb;
+          float fv[8];
+          ld8f(sFoff + pr * kD + 32 * kp + 8 * g, fv);
 #pragma unroll
-            for (int e = 0; e < 8; ++e) xv[e] *= fv[e];
-            fa = to_op8(xv, bf);
-          }
+          for (int e = 0; e < 8; ++e) fa[e] = (_Float16)((float)fa[e] * fv[e]);
         }
-        accA[bb] = mma16(fa, KrowF[kp], accA[bb], bf);
-        accP[bb] = mma16(fa, QrowF[kp], accP[bb], bf);
+        accA[bb] = mma_f16(fa, KrowF[kp], accA[bb]);
+        accP[bb] = mma_f16(fa, QrowF[kp], accP[bb]);
       }
     }
   }
@@ -804,8 +818,11 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
               for (int ct = 0; ct < 2; ++ct) U[rt][ct] = mma_f16(tf, Xb[kp][ct], U[rt][ct]);
             }
         }
-        // U as B operands over tokens 32k' + 16s + 4g + e
-        half8 Ub[2][2];
+        // U as B operands over tokens 32k' + 16s + 4g + e; in a wide chunk also
+        // the fp16 remainder U - Ub, so the two products below see U to about
+        // 22 bits
+        const bool wide = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(sb + WS_WIDE)) != 0;
+        half8 Ub[2][2], Ul[2][2];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
 #pragma unroll
@@ -813,6 +830,10 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
             const float x[8] = {U[2 * kp][ct][0], U[2 * kp][ct][1], U[2 * kp][ct][2], U[2 * kp][ct][3],
                                 U[2 * kp + 1][ct][0], U[2 * kp + 1][ct][1], U[2 * kp + 1][ct][2], U[2 * kp + 1][ct][3]};
             Ub[kp][ct] = to_half8(x);
+            if (wide) {
+#pragma unroll
+              for (int e = 0; e < 8; ++e) Ul[kp][ct][e] = (_Float16)(x[e] - (float)Ub[kp][ct][e]);
+            }
           }
         // O += P U, then O to LDS for the epilogue waves
 #pragma unroll
@@ -823,6 +844,10 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
               const half8 pf = *reinterpret_cast<const half8*>(sb + WS_P + (p_frag(rt, kp) * 64 + lane) * 16);
 #pragma unroll
               for (int ct = 0; ct < 2; ++ct) O[rt][ct] = mma_f16(pf, Ub[kp][ct], O[rt][ct]);
+              if (wide) {
+#pragma unroll
+                for (int ct = 0; ct < 2; ++ct) O[rt][ct] = mma_f16(pf, Ul[kp][ct], O[rt][ct]);
+              }
             }
           const float ox[8] = {O[rt][0][0], O[rt][0][1], O[rt][0][2], O[rt][0][3],
                                O[rt][1][0], O[rt][1][1], O[rt][1][2], O[rt][1][3]};
@@ -844,6 +869,10 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
             const half8 kf = *reinterpret_cast<const half8*>(sb + WS_KB + ((m * 2 + kp) * 64 + lane) * 16);
 #pragma unroll
             for (int ct = 0; ct < 2; ++ct) S[m][ct] = mma_f16(kf, Ub[kp][ct], S[m][ct]);
+            if (wide) {
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) S[m][ct] = mma_f16(kf, Ul[kp][ct], S[m][ct]);
+            }
           }
         }
       }
@@ -1049,9 +1078,10 @@ SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail) {
 // dies gets the same share: mask bits interleave over the dies).  Slabs
 // alternate between two intra-chunk streams, so the event recorded after one
 // slab's intra-chunk kernel never holds back the next one's start.  Created on
-// first use and kept for the life of the thread.
+// first use and kept until kda_release() or process exit.
 struct Pipe {
   int n_inter = 0;
+  unsigned gen = 0;  // release_generation() when created
   hipStream_t intra[2] = {nullptr, nullptr}, inter = nullptr;
   hipEvent_t fork = nullptr, a_done[2] = {nullptr, nullptr}, b_done[kPipeBufs] = {};
   hipEvent_t join[3] = {nullptr, nullptr, nullptr};
@@ -1082,6 +1112,10 @@ int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
   if (!pipe_shape(a, ncu)) return KDA_OK;
   const int n_inter = (int)((a.B * a.H + 7) / 8 * 8);
   if (n_inter >= ncu) return KDA_OK;
+  // slots made before the last kda_release() hold destroyed handles
+  const unsigned gen = release_generation();
+  for (int k = 0; k < kPerDev; ++k)
+    if (pipes[dev][k].n_inter != 0 && pipes[dev][k].gen != gen) pipes[dev][k] = Pipe{};
   Pipe* slot = nullptr;
   for (int k = 0; k < kPerDev && slot == nullptr; ++k)
     if (pipes[dev][k].n_inter == n_inter) slot = &pipes[dev][k];
@@ -1099,11 +1133,19 @@ int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
                                       &slot->join[0], &slot->join[1], &slot->join[2]};
     for (int k = 0; k < kPipeBufs; ++k) evs[6 + k] = &slot->b_done[k];
     for (int k = 0; k < 6 + kPipeBufs && e == hipSuccess; ++k) e = hipEventCreateWithFlags(evs[k], hipEventDisableTiming);
+    // everything created is registered, so kda_release() (or process exit) frees it
+    if (slot->inter != nullptr) keep(slot->inter);
+    for (int k = 0; k < 2; ++k)
+      if (slot->intra[k] != nullptr) keep(slot->intra[k]);
+    for (int k = 0; k < 6 + kPipeBufs; ++k)
+      if (*evs[k] != nullptr) keep(*evs[k]);
     if (e != hipSuccess) {
+      *slot = Pipe{};
       set_error("prefill: stream / event creation failed: %s", hipGetErrorString(e));
       return KDA_E_HIP;
     }
     slot->n_inter = n_inter;
+    slot->gen = gen;
   }
   pp = slot;
   return KDA_OK;

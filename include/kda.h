@@ -25,7 +25,11 @@
  * conv_w are always fp32.
  *
  * Ownership: the caller owns every buffer (device memory).  The library keeps
- * no device allocations and no global device state; inputs are never written.
+ * no device allocations; inputs are never written.  Long prefill and backward
+ * calls fork onto compute-unit-restricted streams (default priority) that the
+ * library creates on first use, keeps for later calls, and destroys in
+ * kda_release() or, failing that, at process exit, before the HIP runtime
+ * tears itself down.
  * Calls are asynchronous on `stream` (a hipStream_t; NULL = the null stream);
  * execution faults surface at the caller's next synchronisation.  A call that
  * fails validation returns a negative code and launches nothing.  The library
@@ -43,13 +47,17 @@
  *                     they load g and beta.
  *
  * Preconditions not checked (for cost): g <= 0 and 0 <= beta <= 1 in the
- * direct form; inputs finite; |v~| and the state below 6e4 (fp16 operand range).
+ * direct form; inputs finite; |v~| and the state below 6e4 (fp16 operand
+ * range); the summed log-decay of any 16 consecutive tokens of a chunk at
+ * least -80 per channel (g >= -5 per token suffices, which K3's bounded decay
+ * g = -5 sigmoid(.) guarantees: the pages' 16-token tile bound), so that the
+ * in-tile decay factors stay finite in fp32.
  * Precision: the prefill's matrix-core operands are fp16 with fp32
  * accumulation and an fp32 state.  Decay factors inside a 16-token tile are
- * formed relative to a per-tile reference; when a tile's summed log-decay in
- * some channel is below -8 the chunk's decay-weighted products switch to bf16
- * operands (finite for any tile with g >= -5 per token, as K3's bounded decay
- * g = -5 sigmoid(.) guarantees), at bf16 precision for those products.
+ * formed relative to a per-tile reference.  A chunk in which some tile's
+ * summed log-decay in some channel is below -8 ("wide") computes its in-tile
+ * blocks with fp32 operands and passes U to its state and output products as
+ * a pair of fp16 parts (about 22 significant bits).
  */
 #ifndef KDA_H
 #define KDA_H
@@ -61,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 5
+#define KDA_ABI_VERSION 6
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -383,6 +391,15 @@ const char* kda_last_error(void);
 
 /* KDA_ABI_VERSION of the loaded library. */
 int kda_abi_version(void);
+
+/* Destroy the streams and events the library keeps between calls (the
+ * compute-unit-restricted streams of pipelined prefill and backward calls),
+ * on every device and for every host thread; later calls create them again.
+ * Call it with no library call in flight (it waits for those streams first).
+ * The library also does this at process exit, before the HIP runtime's own
+ * teardown (streams still alive then have crashed profiled runs at exit).
+ * Returns KDA_OK, or KDA_E_HIP (text in kda_last_error) if a destroy failed. */
+int kda_release(void);
 
 #ifdef __cplusplus
 }

@@ -25,7 +25,10 @@ holds beta logits ~ N(0, 1) per (token, head) (so beta has the distribution
 above), and A ~ N(0, 0.1) fp32 per (head, key channel).  The default
 z_mean = -4.7 gives the log-decay -5 sigmoid(e^A z) the same mean as the
 recipe above (-0.075 per token; 0.7% of values below -0.5 against 0.5%).
-With z_mean = 6 nearly every log-decay sits at K3's bound of -5 per token.  Draws are fp64 (numpy backend) or fp32 (torch backend,
+With z_mean = 6 nearly every log-decay sits at K3's bound of -5 per token.
+`fast_channels` = n redraws the logits of n seeded key channels per head from
+N(6, 1) (the rest as above): a few fast-forgetting channels put every chunk of
+every head past fp16's in-tile decay range.  Draws are fp64 (numpy backend) or fp32 (torch backend,
 used for the large workloads on the device), then rounded once to the
 workload's dtype.
 """
@@ -147,12 +150,25 @@ def prefill_inputs_np(w: Workload, T: int | None = None, seed: int | None = None
     return out
 
 
-def with_k3_logits(inp: dict, w: Workload, seed: int | None = None, z_mean: float = -4.7) -> dict:
+def _fast_channel_sets(seed: int, H: int, dk: int, n: int) -> np.ndarray:
+    """n distinct key channels per head [H, n], seeded (shared by both backends)."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed + 0x2000))
+    return np.stack([rng.choice(dk, n, replace=False) for _ in range(H)])
+
+
+def with_k3_logits(inp: dict, w: Workload, seed: int | None = None, z_mean: float = -4.7,
+                   fast_channels: int = 0) -> dict:
     """Copy of prefill or decode inputs whose g and beta are K3's logits, plus A [H, dk]."""
-    seed = (w.seed if seed is None else seed) + 0x1000
-    rz, rb, ra = _streams(seed, 3)
+    seed0 = w.seed if seed is None else seed
+    seed = seed0 + 0x1000
+    rz, rb, ra, rf = _streams(seed, 4)
     out = dict(inp)
-    out["g"] = _round(rz.normal(z_mean, 1.0, inp["g"].shape), w.dtype)
+    z = rz.normal(z_mean, 1.0, inp["g"].shape)
+    if fast_channels:
+        chans = _fast_channel_sets(seed0, w.H, w.dk, fast_channels)
+        for h in range(w.H):
+            z[..., h, chans[h]] = rf.normal(6.0, 1.0, z[..., h, chans[h]].shape)
+    out["g"] = _round(z, w.dtype)
     out["beta"] = _round(rb.standard_normal(inp["beta"].shape), w.dtype)
     out["A"] = (ra.standard_normal((w.H, w.dk)) * 0.1).astype(np.float32)
     return out
@@ -266,12 +282,19 @@ def prefill_inputs_torch(w: Workload, device, T: int | None = None, seed: int | 
 
 
 def with_k3_logits_torch(inp: dict, w: Workload, device, seed: int | None = None,
-                         z_mean: float = -4.7) -> dict:
+                         z_mean: float = -4.7, fast_channels: int = 0) -> dict:
     """Device-side twin of `with_k3_logits`: g and beta replaced by K3's logits, plus A."""
     torch = _torch()
     seed = w.seed if seed is None else seed
     out = dict(inp)
     out["g"] = _normal_fill(torch.empty_like(inp["g"]), _gen(device, seed * 16 + 9), mean=z_mean)
+    if fast_channels:
+        chans = _fast_channel_sets(seed, w.H, w.dk, fast_channels)
+        gen = _gen(device, seed * 16 + 12)
+        for h in range(w.H):
+            idx = torch.as_tensor(chans[h], device=device)
+            sel = out["g"][..., h, :].index_select(-1, idx)
+            out["g"][..., h, :].index_copy_(-1, idx, _normal_fill(torch.empty_like(sel), gen, mean=6.0))
     out["beta"] = _normal_fill(torch.empty_like(inp["beta"]), _gen(device, seed * 16 + 10))
     out["A"] = _normal_fill(torch.empty((w.H, w.dk), dtype=torch.float32, device=device),
                             _gen(device, seed * 16 + 11), std=0.1)

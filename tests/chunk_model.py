@@ -42,6 +42,86 @@ def _id(x):
     return np.asarray(x, dtype=np.float64)
 
 
+def _f32(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+
+
+def _fp16_fin(x):
+    with np.errstate(over="ignore"):
+        return np.asarray(x, dtype=np.float16).astype(np.float64)
+
+
+WIDE_SPAN = 8.0  # a chunk is "wide" when some tile decays by more than e^8 in some channel
+
+
+def chunk_core_kernel(qn, kn, vn, g, beta, S0, wide_scheme="split", C=64, span=WIDE_SPAN):
+    """The two-kernel path's rounding points, chunk by chunk (C = 64, 16-token tiles).
+
+    fp16 operands everywhere, fp32 accumulation and state, as the kernels do:
+    row factors e^{G - rho_a} <= 1; off-diagonal column factors referenced to
+    the end of the column tile (<= 1); the diagonal column factor
+    e^{rho_a - G} (up to e^{span} of the tile).  A chunk is wide when some
+    tile's span exceeds e^8.  wide_scheme decides what a wide chunk does:
+      "bf16":  every decay-weighted A / P operand in bf16 (an earlier design);
+      "split": diagonal blocks of A and P from fp32 operands (q's row as its
+               fp16 normalised value times the fp32 factor: the factor may
+               underflow fp16 while the column factor makes up for it), and U
+               passed to the P U and (K e^{G_C-G})^T U products as fp16 hi + lo.
+    Returns (o_core [T, dv], S_T, number of wide chunks).
+    """
+    T, dk = qn.shape
+    S = np.array(S0, dtype=np.float64)
+    o = np.zeros((T, vn.shape[1]))
+    nwide = 0
+    for c0 in range(0, T, C):
+        c1 = min(T, c0 + C)
+        n = c1 - c0
+        Q, K, V, b = _f32(qn[c0:c1]), _f32(kn[c0:c1]), _f32(vn[c0:c1]), _f32(beta[c0:c1])
+        G = _f32(np.cumsum(g[c0:c1], axis=0))
+        tiles = list(range(0, n, TILE))
+        refs = [G[a0 - 1] if a0 > 0 else np.zeros(dk) for a0 in tiles]
+        wide = any(np.any(refs[i] - G[min(n, a0 + TILE) - 1] > span) for i, a0 in enumerate(tiles))
+        nwide += wide
+        op = _bf16 if (wide and wide_scheme == "bf16") else _fp16_fin
+        A = np.zeros((n, n))
+        P = np.zeros((n, n))
+        for ai, a0 in enumerate(tiles):
+            a1 = min(n, a0 + TILE)
+            rho = refs[ai]
+            rowf = np.exp(G[a0:a1] - rho)
+            Kr, Qr = K[a0:a1] * rowf, Q[a0:a1] * rowf
+            Kc = K[a0:a1] * np.exp(rho - G[a0:a1])
+            with np.errstate(over="ignore", invalid="ignore"):
+                if wide and wide_scheme == "split":
+                    # q's fp32 row: its fp16 normalised value times the fp32 factor
+                    Ad, Pd = _f32(Kr) @ _f32(Kc).T, _f32(_fp16(Q[a0:a1]) * rowf) @ _f32(Kc).T
+                else:
+                    Ad, Pd = op(Kr) @ op(Kc).T, op(Qr) @ op(Kc).T
+            A[a0:a1, a0:a1] = np.where(np.isfinite(Ad), Ad, 0.0)   # upper part is discarded below
+            P[a0:a1, a0:a1] = np.where(np.isfinite(Pd), Pd, 0.0)
+            for bi in range(ai):
+                b0 = tiles[bi]
+                rb1 = G[b0 + TILE - 1]                              # end of column tile b
+                cc = op(K[b0:b0 + TILE] * np.exp(rb1 - G[b0:b0 + TILE]))
+                if bi < ai - 1:
+                    cc = op(cc * np.exp(rho - rb1))
+                A[a0:a1, b0:b0 + TILE] = op(Kr) @ cc.T
+                P[a0:a1, b0:b0 + TILE] = op(Qr) @ cc.T
+        A = np.tril(A, -1) * b[:, None]
+        P = np.tril(P, 0)
+        Tm = np.linalg.inv(np.eye(n) + A)
+        Tb = _fp16(Tm * b[None, :])
+        X = _fp16(V) - _fp16(K * np.exp(G)) @ _fp16(S)
+        U = Tb @ _fp16(X)
+        Ub = _fp16(U)
+        if wide and wide_scheme == "split":
+            Ub = Ub + _fp16(U - Ub)
+        o[c0:c1] = _fp16(_fp16(Q * np.exp(G)) @ _fp16(S) + _fp16(P) @ Ub)
+        S = np.exp(G[-1])[:, None] * S + _fp16(K * np.exp(G[-1] - G)).T @ Ub
+    return o, S, nwide
+
+
 def chunk_core(qn, kn, vn, g, beta, S0, C=64, operands=None, tile=TILE, form="wy", ut_rounded=False):
     """Chunkwise o_core [T,dv] and final state for one (b,h).
 

@@ -37,7 +37,8 @@ def test_header_declares_the_abi():
     names = declared_functions()
     for must in ("kda_prefill", "kda_decode_step", "kda_decode_multi", "kda_prefill_workspace_bytes", "kda_prep",
                  "kda_status_string", "kda_last_error", "kda_abi_version", "kda_cp_compose", "kda_prefill_cp",
-                 "kda_prefill_cp_workspace_bytes", "kda_prefill_backward", "kda_prefill_backward_workspace_bytes"):
+                 "kda_prefill_cp_workspace_bytes", "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
+                 "kda_release"):
         assert must in names
 
 
@@ -265,4 +266,11 @@ def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 5
+    assert L.kda_abi_version() == 6
+
+
+def test_release_with_nothing_kept(kda):
+    """kda_release with no streams created makes no HIP call (safe without a GPU)
+    and can be repeated."""
+    L = kda.lib()
+    assert L.kda_release() == 0 and L.kda_release() == 0

@@ -5,7 +5,10 @@
   put the max error at several times 1e-2 x RMS, too close to (or past) the
   2e-2 x RMS bound, while fp16 operands (same matrix-core rate, three more
   mantissa bits) stay under 0.4 of it.  That fixes the kernels' scheme:
-  fp16 operands, fp32 accumulation, fp32 state, fp32 output.
+  fp16 operands, fp32 accumulation, fp32 state, fp32 output;
+* strong decay ("wide" chunks, a tile decaying by more than e^8): the scheme
+  the kernels take there (fp32 in-tile blocks, U as an fp16 pair) against the
+  bf16 operands of an earlier design, at K3's -5 bound and on mixed inputs.
 """
 from __future__ import annotations
 
@@ -13,7 +16,7 @@ import numpy as np
 import pytest
 
 import kda_synth as syn
-from chunk_model import chunk_core
+from chunk_model import chunk_core, chunk_core_kernel
 from kda_synth import Workload, to_f64
 from ref_math import gated_rmsnorm, head_channels, prep_numpy
 
@@ -109,3 +112,55 @@ def test_cancellation_needs_full_precision_u(oracle_mod):
         err[name] = np.abs(S - r["S_T"][0]).max() / rms_s
     assert err["ut16"] > 2e-2, err
     assert err["wy"] < 0.6 * 2e-2 and err["tx"] < 0.6 * 2e-2, err
+
+
+def _wide_case_error(oracle_mod, w, inp, scheme):
+    """max |err| / RMS for o and S_T of the kernels' rounding model, and the
+    number of wide chunks, over every head of the case."""
+    r = oracle_mod.prefill(inp, want_prep=True)
+    g_all, beta_all = oracle_mod.decay_and_beta(inp)
+    d = w.dk
+    eo, es, ro, rs, nwide = 0.0, 0.0, [], [], 0
+    for p in range(w.B * w.H):
+        b, h = divmod(p, w.H)
+        prep = r["prep"][p]
+        S0 = inp["S0"][b, h].astype(np.float64)
+        oc, S, nw = chunk_core_kernel(prep[:, :d], prep[:, d:2 * d], prep[:, 2 * d:], g_all[b, :, h],
+                                      beta_all[b, :, h], S0, wide_scheme=scheme)
+        o = gated_rmsnorm(oc, to_f64(inp["gate"], "bf16")[b, :, h])
+        eo, es = max(eo, np.abs(o - r["o"][p]).max()), max(es, np.abs(S - r["S_T"][p]).max())
+        ro.append(r["o"][p])
+        rs.append(r["S_T"][p])
+        nwide += nw
+    return eo / np.sqrt(np.mean(np.square(ro))), es / np.sqrt(np.mean(np.square(rs))), nwide
+
+
+def test_wide_chunks_precision_design(oracle_mod):
+    """Strong decay, modelled with the kernels' rounding points.  At K3's bound
+    (every channel at -5 per token, tiles spanning e^80) bf16 decay-weighted
+    operands put the largest o error past the 2e-2 x RMS bound; fp32 diagonal
+    blocks plus U as an fp16 pair keep o and S_T under 0.6 of it.  The same
+    scheme holds a few fast channels among normal ones, and g = -2 per token,
+    under half of it."""
+    w = Workload("k3b", 1, 160, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=53)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w, z_mean=6.0)
+    bo, bs, nb = _wide_case_error(oracle_mod, w, inp, "bf16")
+    so, ss, ns = _wide_case_error(oracle_mod, w, inp, "split")
+    assert nb == ns == 2 * 3, (nb, ns)  # every chunk of both heads is wide
+    assert bo > 2e-2, bo
+    assert so < 0.6 * 2e-2 and ss < 0.6 * 2e-2, (so, ss)
+
+    w = Workload("k3m", 1, 256, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=57)
+    inp = syn.with_k3_logits(syn.prefill_inputs_np(w), w, fast_channels=8)
+    so, ss, ns = _wide_case_error(oracle_mod, w, inp, "split")
+    assert ns == 2 * 4, ns
+    assert so < 0.5 * 2e-2 and ss < 0.5 * 2e-2, (so, ss)
+
+    w = Workload("sd", 1, 160, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=31)
+    inp = syn.prefill_inputs_np(w)
+    gbits = syn.bf16_bits_from_f64(np.full(inp["g"].shape, -2.0))
+    gbits[:, 64:128] = syn.bf16_bits_from_f64(np.full(inp["g"][:, 64:128].shape, -0.05))
+    inp["g"] = gbits
+    so, ss, ns = _wide_case_error(oracle_mod, w, inp, "split")
+    assert ns == 2 * 2, ns  # the middle chunk decays slowly
+    assert so < 0.5 * 2e-2 and ss < 0.5 * 2e-2, (so, ss)

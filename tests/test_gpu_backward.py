@@ -38,6 +38,7 @@ CASES = [
     (1, 64, 2, 64, "f32"),      # a whole number of stretches
     (2, 2, 2, 16, "f32"),       # fewer tokens than the conv history
     (1, 1100, 1, 32, "f32"),    # 69 stretches: two slabs of recompute (64 + 5), dS and the ring carried
+    (1, 1100, 2, 128, "bf16"),  # the K3-width shape's kernels: 512 threads, two pipelined slabs
 ]
 
 
@@ -172,6 +173,11 @@ def test_unpipelined_fallback_equals_pipelined():
     takes the pipelined path (two slabs: 1100 tokens)."""
     torch, kda = need_gpu()
     B, T, H, d = 8, 1100, 29, 16
+    # the library pipelines a call when its reverse width (heads rounded up to
+    # 8) leaves at least 32 compute units: 232 + 32 > CUs >= 32 + 32 makes the
+    # 232-head call run unpipelined and the 29-head call pipelined
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    assert 64 <= ncu < 264, f"{ncu} compute units: this test's two calls would take the same path"
     w = Workload("bwdp", B, T, H, d, d, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=171)
     inp = syn.prefill_inputs_np(w)
     rng = np.random.default_rng(71)
