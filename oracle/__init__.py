@@ -151,12 +151,15 @@ def initial_carry(B, H, dk, dv, heads=None, S0=None, conv_in=None):
     n = len(bh)
     S = np.zeros((n, dk, dv))
     hist = np.zeros((n, 3, 2 * dk + dv))
+    S0a = None if S0 is None else np.asarray(S0)
+    ci = None
+    if conv_in is not None:
+        ci = _f64(conv_in) if conv_in.dtype in (np.uint16, np.float32) else conv_in
     for i, p in enumerate(bh):
         b, h = divmod(int(p), H)
-        if S0 is not None:
-            S[i] = np.asarray(S0, dtype=np.float64)[b, h]
-        if conv_in is not None:
-            ci = _f64(conv_in) if conv_in.dtype in (np.uint16, np.float32) else conv_in
+        if S0a is not None:
+            S[i] = S0a[b, h]
+        if ci is not None:
             hist[i] = ci[b][:, _head_channels(H, dk, dv, h)]
     return S, hist
 
