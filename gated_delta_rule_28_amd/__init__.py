@@ -39,6 +39,7 @@ KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
 ABI_VERSION = 6
 MAX_DECODE_TOKENS = 16
+NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
 
 class KDAError(RuntimeError):
@@ -142,6 +143,8 @@ def lib():
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_abi_version.restype = ctypes.c_int
         L.kda_release.restype = ctypes.c_int
+        L.kda_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _P]
+        L.kda_prefill_noalloc.restype = ctypes.c_int
         if L.kda_abi_version() != ABI_VERSION:
             raise RuntimeError(f"libkda ABI {L.kda_abi_version()} != binding ABI {ABI_VERSION}")
         _lib = L
@@ -200,7 +203,9 @@ def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out
     Passing S_T=S0 / conv_out=conv_in updates the carry in place.
     workspace: "auto" allocates what kda_prefill_workspace_bytes asks for (the
     two-kernel path where the sizes have one), None passes no workspace (the
-    single-kernel path), or a uint8 device tensor to use.
+    single-kernel path), a uint8 device tensor to use, or "noalloc": call
+    kda_prefill_noalloc, whose workspace is the library's own device scratch
+    (pass o / S_T / conv_out as well for a call that allocates nothing).
     """
     torch = _torch()
     B, T, H, dk = q.shape
@@ -216,9 +221,12 @@ def prefill(q, k, v, conv_w, g, beta, gate, S0=None, conv_in=None, chunk=64, out
     a = PrefillArgs(B, T, H, dk, dv, chunk, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
                     _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in),
                     _ptr(o), _ptr(S_T), _ptr(conv_out), None, 0, *_decay(A))
+    if isinstance(workspace, str) and workspace == "noalloc":
+        _check("kda_prefill_noalloc", lib().kda_prefill_noalloc(ctypes.byref(a), _stream(dev)))
+        return o, S_T, conv_out
     if isinstance(workspace, str):
         if workspace != "auto":
-            raise ValueError("workspace must be 'auto', None or a uint8 tensor")
+            raise ValueError("workspace must be 'auto', 'noalloc', None or a uint8 tensor")
         nbytes = lib().kda_prefill_workspace_bytes(ctypes.byref(a))
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=dev) if nbytes else None
     if workspace is not None:

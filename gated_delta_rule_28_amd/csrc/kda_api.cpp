@@ -204,8 +204,10 @@ size_t kda_prefill_workspace_min_bytes(const kda_prefill_args* a) {
   return kda::prefill_split_workspace_min_bytes(*a);
 }
 
-int kda_prefill(const kda_prefill_args* a, void* stream) {
-  kda::g_err[0] = '\0';
+namespace kda {
+namespace {
+// Argument checks of kda_prefill and kda_prefill_noalloc (all but the workspace).
+int check_prefill(const kda_prefill_args* a) {
   REQUIRE_PTR(a);
   int rc = kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype);
   if (rc != KDA_OK) return rc;
@@ -222,12 +224,29 @@ int kda_prefill(const kda_prefill_args* a, void* stream) {
   REQUIRE_A16(a->S_T); REQUIRE_A16(a->conv_in); REQUIRE_A16(a->conv_out);
   if (a->beta != nullptr && !kda::aligned_n(a->beta, kda::esize(a->in_dtype)))
     return fail(KDA_E_ALIGN, "beta is not aligned to its element size");
+  return KDA_OK;
+}
+}  // namespace
+}  // namespace kda
+
+int kda_prefill(const kda_prefill_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  const int rc = kda::check_prefill(a);
+  if (rc != KDA_OK) return rc;
   REQUIRE_A16(a->workspace);
   if (a->workspace != nullptr && a->workspace_bytes < kda_prefill_workspace_min_bytes(a))
     return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", a->workspace_bytes,
                 kda_prefill_workspace_min_bytes(a));
   if (a->T == 0 && a->S_T == nullptr && a->conv_out == nullptr) return KDA_OK;
   return kda::launch_prefill(*a, reinterpret_cast<hipStream_t>(stream));
+}
+
+int kda_prefill_noalloc(const kda_prefill_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  const int rc = kda::check_prefill(a);
+  if (rc != KDA_OK) return rc;
+  if (a->T == 0 && a->S_T == nullptr && a->conv_out == nullptr) return KDA_OK;
+  return kda::launch_prefill_noalloc(*a, reinterpret_cast<hipStream_t>(stream));
 }
 
 int kda_cp_compose(const kda_cp_compose_args* a, void* stream) {

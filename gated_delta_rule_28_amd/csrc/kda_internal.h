@@ -19,6 +19,9 @@ bool prefill_split_eligible(const kda_prefill_args& a);
 size_t prefill_split_workspace_bytes(const kda_prefill_args& a);
 size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a);
 int launch_prefill_split(const kda_prefill_args& a, hipStream_t s);
+// kda_prefill without a caller workspace or any allocation: the two-kernel
+// path's workspace is a file-scope device array (kda_prefill_split.hip).
+int launch_prefill_noalloc(const kda_prefill_args& a, hipStream_t s);
 
 // Context-parallel helpers: the prefix composition; the raw conv history of
 // `nblk` blocks per sequence (the three raw tokens before token (first + j) * L

@@ -52,6 +52,7 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <mutex>
 #include <type_traits>
 
 namespace kda {
@@ -1031,13 +1032,14 @@ size_t per_chunk_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * W
 size_t carry_bytes(const kda_prefill_args& a) { return (size_t)a.B * a.H * kD * kD * 4; }
 bool pipe_shape(const kda_prefill_args& a, int ncu) { return 2L * a.B * a.H <= ncu; }
 
-SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail) {
+// pipe_ok = false plans the slabs one after the other on the caller's stream.
+SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail, bool pipe_ok = true) {
   SlabPlan s{};
   s.nchunks = (a.T + kC - 1) / kC;
   s.nbuf = 1;
   const size_t pc = per_chunk_bytes(a);
   const size_t cb = carry_bytes(a);
-  if (s.nchunks > kPipeChunks && pipe_shape(a, kPlanCUs) && avail >= cb + kPipeBufs * pc) {
+  if (pipe_ok && s.nchunks > kPipeChunks && pipe_shape(a, kPlanCUs) && avail >= cb + kPipeBufs * pc) {
     const size_t fit = (avail - cb) / (kPipeBufs * pc);
     const int most = (int)(fit < (size_t)kPipeChunks ? fit : (size_t)kPipeChunks);
     if (most == kPipeChunks && s.nchunks >= 2 * kPipeChunks) {
@@ -1152,8 +1154,8 @@ int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
 }
 
 template <bool OB, bool K3>
-int run_split(const kda_prefill_args& a, hipStream_t st) {
-  const SlabPlan pl = plan_slabs(a, a.workspace_bytes);
+int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
+  const SlabPlan pl = plan_slabs(a, a.workspace_bytes, pipe_ok);
   const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<K3>),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, ALds::BYTES);
   if (e1 != hipSuccess) {
@@ -1254,10 +1256,70 @@ size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a) {
   return per_chunk_bytes(a) + carry_bytes(a);
 }
 
-int launch_prefill_split(const kda_prefill_args& a, hipStream_t s) {
+int launch_split(const kda_prefill_args& a, hipStream_t s, bool pipe_ok) {
   const bool k3 = a.decay_form == KDA_DECAY_K3;
-  if (a.out_dtype == KDA_BF16) return k3 ? run_split<true, true>(a, s) : run_split<true, false>(a, s);
-  return k3 ? run_split<false, true>(a, s) : run_split<false, false>(a, s);
+  if (a.out_dtype == KDA_BF16) return k3 ? run_split<true, true>(a, s, pipe_ok) : run_split<true, false>(a, s, pipe_ok);
+  return k3 ? run_split<false, true>(a, s, pipe_ok) : run_split<false, false>(a, s, pipe_ok);
+}
+
+int launch_prefill_split(const kda_prefill_args& a, hipStream_t s) { return launch_split(a, s, true); }
+
+// ---- allocation-free prefill (kda_prefill_noalloc) ---------------------------------
+// For callers that cannot allocate, the two-kernel path's workspace is this
+// file-scope device array instead of a caller buffer.  Each GPU the library
+// runs on holds its own copy until the process ends; its address differs per
+// device and is looked up once per device.  In host code `scratch` names only
+// a host-side stand-in: every host use goes through the looked-up address.
+// Nothing in it has to start at zero (each slab's blocks and the state carry
+// are written before they are read).  Calls that overlap on one GPU share it
+// and race.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+// Device address of `scratch` on the current device (looked up on first use).
+int scratch_address(unsigned char*& ptr) {
+  constexpr int kMaxDev = 64;
+  static std::mutex mu;
+  static unsigned char* addr[kMaxDev] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDev) {
+    set_error("prefill (no allocation): hipGetDevice failed or device %d out of range", dev);
+    return KDA_E_HIP;
+  }
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr) {
+      set_error("prefill (no allocation): hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+      return KDA_E_HIP;
+    }
+    addr[dev] = static_cast<unsigned char*>(p);
+  }
+  ptr = addr[dev];
+  return KDA_OK;
+}
+}  // namespace
+
+int launch_prefill_noalloc(const kda_prefill_args& a, hipStream_t s) {
+  kda_prefill_args b = a;
+  b.workspace = nullptr;
+  b.workspace_bytes = 0;
+  if (!prefill_split_eligible(a)) return launch_prefill(b, s);  // the single-kernel path: no workspace
+  const size_t need = prefill_split_workspace_min_bytes(a);
+  if (need > KDA_NOALLOC_SCRATCH_BYTES) {
+    set_error("prefill (no allocation): B*H = %lld heads need %zu bytes of workspace, more than the %zu-byte "
+              "scratch (at most %zu bytes per head)", (long long)a.B * a.H, need, (size_t)KDA_NOALLOC_SCRATCH_BYTES,
+              (size_t)(WS_CHUNK + kD * kD * 4));
+    return KDA_E_WORKSPACE;
+  }
+  unsigned char* ws = nullptr;
+  const int rc = scratch_address(ws);
+  if (rc != KDA_OK) return rc;
+  b.workspace = ws;
+  b.workspace_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+  return launch_split(b, s, false);  // slabs in turn on the caller's stream: no streams created
 }
 
 }  // namespace kda

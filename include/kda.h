@@ -392,6 +392,23 @@ const char* kda_last_error(void);
 /* KDA_ABI_VERSION of the loaded library. */
 int kda_abi_version(void);
 
+/* kda_prefill for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments and results as kda_prefill; args->workspace and workspace_bytes
+ * are ignored.  Where kda_prefill would take its two-kernel path (bf16
+ * inputs, chunk 64, dk = dv = 128) the workspace is instead a device array of
+ * KDA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends; its slabs run one after the other on `stream` (no
+ * streams are created).  Other shapes take the single-kernel path, which
+ * needs no workspace.  The call makes no hipMalloc / hipFree or other
+ * allocating call.  Limit: B*H * (80 KiB + 64 KiB) must fit the scratch, i.e.
+ * at most 910 heads (B*H) for sequences longer than one chunk; beyond that it
+ * returns KDA_E_WORKSPACE and launches nothing.  Every call on one GPU uses
+ * the same scratch: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be ordered by the caller. */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)128 << 20)
+int kda_prefill_noalloc(const kda_prefill_args* args, void* stream);
+
 /* Destroy the streams and events the library keeps between calls (the
  * compute-unit-restricted streams of pipelined prefill and backward calls),
  * on every device and for every host thread; later calls create them again.

@@ -274,3 +274,16 @@ def test_release_with_nothing_kept(kda):
     and can be repeated."""
     L = kda.lib()
     assert L.kda_release() == 0 and L.kda_release() == 0
+
+
+def test_noalloc_rejects_heads_beyond_its_scratch(kda):
+    """kda_prefill_noalloc validates on the host: B*H whose minimum workspace
+    (80 KiB + 64 KiB per head) exceeds the 128 MiB scratch is refused with
+    KDA_E_WORKSPACE before any HIP call (so this runs without a GPU)."""
+    L = kda.lib()
+    fake = 1 << 20  # a 16-byte aligned stand-in address; nothing is launched
+    a = kda.PrefillArgs(1, 128, 1000, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32, fake, fake, fake, fake, fake,
+                        fake, fake, None, None, fake, fake, fake, None, 0, kda.KDA_DECAY_DIRECT, None)
+    assert L.kda_prefill_noalloc(ctypes.byref(a), None) == -6
+    assert b"scratch" in L.kda_last_error()
+    assert kda.NOALLOC_SCRATCH_BYTES == 128 << 20
