@@ -137,9 +137,78 @@ def cpu_baseline(w, dev_inp, seconds_target=15.0):
     el = time.perf_counter() - t0
     head_tokens = w.B * Ts * nheads
     tok_s = head_tokens / el / H  # whole-token (all H heads) rate
-    return {"value": tok_s, "unit": "tokens/s", "cores": nthr, "kind": "oracle",
+    return {"value": tok_s, "unit": "tokens/s", "cores": nthr, "kind": "oracle", "cpu": cpu_model(),
             "sample": f"fp64 C oracle, first {nheads} of {H} heads x first {Ts} tokens "
                       f"({head_tokens} head-tokens, {el:.1f} s); tokens/s = head-tokens/s / {H}"}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def measured_peaks(torch):
+    """This GPU's own peaks (libkda_peaks.so): a fetch-modify-write of 1.61 GB of
+    fp32 with the decode step's access pattern (the decode state's size), swept
+    over workgroups per compute unit, and loops of fp16 16x16x32 matrix-core
+    instructions on register operands, swept over grid size and independent
+    chains.  The best of each sweep is reported; every point is listed."""
+    import ctypes
+    path = os.path.join(ROOT, "gated_delta_rule_28_amd", "libkda_peaks.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: run `python -m gated_delta_rule_28_amd.build`")
+    L = ctypes.CDLL(path)
+    L.kda_peak_fmw.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.kda_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    nbytes = 256 * 96 * 128 * 128 * 4
+    buf = torch.zeros(nbytes // 4, dtype=torch.float32, device="cuda")
+    fmw = {}
+    for lds in (0, 24 << 10, 32 << 10, 40 << 10, 54 << 10, 80 << 10):
+        def run():
+            assert L.kda_peak_fmw(ctypes.c_void_p(buf.data_ptr()), nbytes, lds, stream) == 0
+        for _ in range(3):
+            run()
+        ms = sorted(timed_launches(torch, run, 15))[7]
+        fmw[f"lds{lds >> 10}k"] = 2 * nbytes / (ms * 1e-3) / 1e9
+    L.kda_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    buf.zero_()
+    one_way = {}
+    for direction, name in ((0, "read"), (1, "write")):
+        def run():
+            assert L.kda_peak_stream(ctypes.c_void_p(buf.data_ptr()), nbytes, direction, stream) == 0
+        for _ in range(3):
+            run()
+        ms = sorted(timed_launches(torch, run, 15))[7]
+        one_way[name] = nbytes / (ms * 1e-3) / 1e9
+    del buf
+    # a mix of X bytes read and X written at the two directions' own rates
+    mix = 2.0 / (1.0 / one_way["read"] + 1.0 / one_way["write"])
+    iters = 20000
+    out = torch.empty(4096 * 256, dtype=torch.float32, device="cuda")
+    mfma = {}
+    for blocks in (1024, 2048, 4096):
+        for chains in (4, 8):
+            it = iters * 4 // chains
+            def run():
+                assert L.kda_peak_mfma(ctypes.c_void_p(out.data_ptr()), blocks, it, chains, stream) == 0
+            run()
+            ms = sorted(timed_launches(torch, run, 3))[1]
+            mfma[f"b{blocks}c{chains}"] = blocks * 4 * chains * it * 16 * 16 * 32 * 2 / (ms * 1e-3) / 1e12
+    return {"hbm_fetch_modify_write_gbs": max(fmw.values()), "hbm_fmw_sweep_gbs": fmw,
+            "hbm_read_gbs": one_way["read"], "hbm_write_gbs": one_way["write"],
+            "hbm_read_write_mix_gbs": mix,
+            "hbm_peak_gbs": max(max(fmw.values()), mix),
+            "mfma_f16_tflops": max(mfma.values()), "mfma_sweep_tflops": mfma,
+            "how": "median launch time with HIP events: kda_peak_fmw over 1.61 GB (decode access pattern; "
+                   "dynamic LDS caps workgroups per CU); kda_peak_stream read-only and write-only over the same "
+                   "blocks, combined as 2 / (1/read + 1/write) for an equal mix; kda_peak_mfma (workgroups x "
+                   "chains); hbm_peak_gbs is the larger of the fetch-modify-write and the mix"}
 
 
 FP32_VALU_PEAK_TFS = 157.3
@@ -541,6 +610,22 @@ def main():
             torch.neg(a, out=b)
         torch.cuda.synchronize()
         out["calibration_copy_bytes"] = 2 * 4 * n
+
+    peaks = measured_peaks(torch)
+    out["measured_peaks"] = peaks
+    mh, mm = peaks["hbm_peak_gbs"], peaks["mfma_f16_tflops"]
+    out["roofline"]["measured_peak"] = mh
+    out["roofline"]["frac_of_measured"] = out["roofline"]["achieved"] / mh
+    out["mfma"]["frac_of_measured_f16_peak"] = out["mfma"]["tflops"] / mm
+    if "decode" in out:
+        out["decode"]["roofline"]["measured_peak"] = mh
+        out["decode"]["roofline"]["frac_of_measured"] = out["decode"]["roofline"]["achieved"] / mh
+    if "decode_multi" in out:
+        out["decode_multi"]["roofline"]["measured_peak"] = mh
+        out["decode_multi"]["roofline"]["frac_of_measured"] = out["decode_multi"]["roofline"]["achieved"] / mh
+    log(f"[bench] measured peaks: fetch-modify-write {peaks['hbm_fetch_modify_write_gbs']:.0f} GB/s, read "
+        f"{peaks['hbm_read_gbs']:.0f}, write {peaks['hbm_write_gbs']:.0f}, read+write mix {peaks['hbm_read_write_mix_gbs']:.0f}"
+        f" GB/s; fp16 matrix cores {mm:.0f} TFLOP/s")
 
     if not args.no_cpu:
         log("[bench] timing the oracle on a bounded sample ...")

@@ -13,11 +13,13 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libkda.so")
+PEAKS_OUT = os.path.join(HERE, "libkda_peaks.so")  # measured-peak microbenchmarks (bench only)
 BUILD_DIR = os.path.join(HERE, "_build")
 ARCH = "gfx950"
 
 SOURCES = ["kda_api.cpp", "kda_backward.hip", "kda_cp.hip", "kda_decode.hip", "kda_prefill.hip",
            "kda_prefill_split.hip"]
+PEAKS_SOURCES = ["kda_peaks.hip"]
 
 COMMON = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17",
@@ -43,19 +45,26 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every HIP source for gfx950 and link libkda.so next to this file."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = OUT + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [_hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr[-8000:]}")
-    os.replace(tmp, OUT)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every HIP source for gfx950 and link libkda.so (and the
+    measured-peak library libkda_peaks.so) next to this file."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PEAKS_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = dict(zip(srcs, ex.map(_compile, srcs)))
+    _link([objs[s] for s in SOURCES], OUT)
+    _link([objs[s] for s in PEAKS_SOURCES], PEAKS_OUT)
     if verbose:
-        print(f"built {OUT}")
+        print(f"built {OUT} and {PEAKS_OUT}")
     return OUT
 
 

@@ -61,34 +61,73 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   __shared__ float ocs[DV];                // o_core
   __shared__ float scal[4];
 
-  // 1. conv step on the raw history + SiLU; shift the history in place.
-  for (int c = tid; c < NC; c += kDecodeThreads) {
+  // This thread's conv channels (c = tid, tid + 256) are requested first, then
+  // the state block, which is the step's traffic: the state's loads are in
+  // flight while the conv step and the norms run, and the conv inputs, being
+  // older, are waited for without waiting for the state.  Every load here is
+  // unconditional from a clamped, in-bounds address (a load under a branch
+  // makes the wait after the branch a wait for everything in flight); which
+  // values are real is decided at use.
+  constexpr int NCH = (NC + kDecodeThreads - 1) / kDecodeThreads;
+  float xr[NCH], hr[NCH][3];
+  float4 wr[NCH];
+  size_t chr[NCH];
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = min(tid + kDecodeThreads * j, NC - 1);
     size_t ch;
-    float x;
+    const void* src;
+    size_t idx;
     if (c < DK) {
       ch = (size_t)h * DK + c;
-      x = load1<IN_BF16>(p.q, (size_t)nh * DK + c);
+      src = p.q;
+      idx = (size_t)nh * DK + c;
     } else if (c < 2 * DK) {
       ch = (size_t)H * DK + (size_t)h * DK + (c - DK);
-      x = load1<IN_BF16>(p.k, (size_t)nh * DK + (c - DK));
+      src = p.k;
+      idx = (size_t)nh * DK + (c - DK);
     } else {
       ch = (size_t)2 * H * DK + (size_t)h * DV + (c - 2 * DK);
-      x = load1<IN_BF16>(p.v, (size_t)nh * DV + (c - 2 * DK));
+      src = p.v;
+      idx = (size_t)nh * DV + (c - 2 * DK);
     }
-    const size_t r0 = ((size_t)n * 3 + 0) * cch + ch;
-    const size_t r1 = r0 + cch;
-    const size_t r2 = r1 + cch;
-    const float h0 = load1<IN_BF16>(p.conv_state, r0);
-    const float h1 = load1<IN_BF16>(p.conv_state, r1);
-    const float h2 = load1<IN_BF16>(p.conv_state, r2);
-    const float4 w = *reinterpret_cast<const float4*>(p.conv_w + ch * 4);
-    const float acc = w.x * h0 + w.y * h1 + w.z * h2 + w.w * x;
-    xs[c] = siluf_(acc);
-    // h1, h2 and x are exact in the history dtype (they came from it or from
-    // the input, which has the same dtype), so the shift is lossless.
-    store1<IN_BF16>(p.conv_state, r0, h1);
-    store1<IN_BF16>(p.conv_state, r1, h2);
-    store1<IN_BF16>(p.conv_state, r2, x);
+    xr[j] = load1<IN_BF16>(src, idx);
+    chr[j] = ch;
+    const size_t r0 = (size_t)n * 3 * cch + ch;
+#pragma unroll
+    for (int r = 0; r < 3; ++r) hr[j][r] = load1<IN_BF16>(p.conv_state, r0 + r * cch);
+    wr[j] = *reinterpret_cast<const float4*>(p.conv_w + ch * 4);
+  }
+  // the per-channel decay (and K3's A), beta and gate: also requested before the state
+  const int tk = min(tid, DK - 1), tv = min(tid, DV - 1);
+  const float g_raw = load1<IN_BF16>(p.g, (size_t)nh * DK + tk);
+  const float a_log = (p.A != nullptr ? p.A : p.conv_w)[(size_t)h * DK + tk];  // used only with p.A
+  const float beta_raw = load1<IN_BF16>(p.beta, (size_t)nh);
+  const float gate_raw = load1<IN_BF16>(p.gate, (size_t)nh * DV + tv);
+  const int cg = tid % CG;
+  const int rg = tid / CG;
+  // every thread holds state rows when the row groups fit (no branch around
+  // the loads then, so the conv inputs can be waited for on their own)
+  constexpr bool kAllActive = kDecodeThreads / CG <= DK;
+  const bool active = kAllActive || rg < RG;
+  f4* Sp = reinterpret_cast<f4*>(p.S + (size_t)nh * DK * DV);
+  f4 s[RPT];
+  if (active) {
+#pragma unroll
+    for (int i = 0; i < RPT; ++i)
+      s[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + RG * i) * CG + cg);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep the conv work after the state requests
+
+  // 1. conv step on the raw history + SiLU; shift the history in place.
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    const int c = tid + kDecodeThreads * j;
+    if (c < NC) {
+      const float4 w = wr[j];
+      const float acc = w.x * hr[j][0] + w.y * hr[j][1] + w.z * hr[j][2] + w.w * xr[j];
+      xs[c] = siluf_(acc);
+    }
   }
   __syncthreads();
 
@@ -114,8 +153,8 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
   if (tid < DK) {
-    float gv = load1<IN_BF16>(p.g, (size_t)nh * DK + tid);
-    if (p.A != nullptr) gv = k3_decay(gv, fast_exp(p.A[(size_t)h * DK + tid]));
+    float gv = g_raw;
+    if (p.A != nullptr) gv = k3_decay(gv, fast_exp(a_log));
     const float a = fast_exp(gv);
     const float kq = xs[DK + tid] * scal[1];
     alpha[tid] = a;
@@ -125,16 +164,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
   }
   __syncthreads();
 
-  // 3. one pass over S: keep this thread's rows, accumulate S'^T k and S'^T q.
-  const int cg = tid % CG;
-  const int rg = tid / CG;
-  const bool active = rg < RG;
-  f4* Sp = reinterpret_cast<f4*>(p.S + (size_t)nh * DK * DV);
-  f4 s[RPT];
+  // 3. one pass over S (requested at the start): keep this thread's rows,
+  // accumulate S'^T k and S'^T q.
   if (active) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i)
-      s[i] = __builtin_nontemporal_load(Sp + (size_t)(rg + RG * i) * CG + cg);
     f4 y = f4{0.f, 0.f, 0.f, 0.f}, z = y;
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
@@ -155,7 +187,7 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
       y += red[0][r][tid];
       z += red[1][r][tid];
     }
-    float beta = load1<IN_BF16>(p.beta, (size_t)nh);
+    float beta = beta_raw;
     if (p.A != nullptr) beta = sigmoidf_(beta);
     const float u = beta * (xs[2 * DK + tid] - y);
     us[tid] = u;
@@ -180,9 +212,19 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(DecodeParams p) 
       __builtin_nontemporal_store(t, Sp + (size_t)r * CG + cg);
     }
   }
-  if (tid < DV) {
-    const float gt = load1<IN_BF16>(p.gate, (size_t)nh * DV + tid);
-    store1<OUT_BF16>(p.o, (size_t)nh * DV + tid, ocs[tid] * scal[3] * sigmoidf_(gt));
+  if (tid < DV) store1<OUT_BF16>(p.o, (size_t)nh * DV + tid, ocs[tid] * scal[3] * sigmoidf_(gate_raw));
+  // The conv history shifted by one token, stored last: a store issued earlier
+  // would make the state's loads be waited for at once (loads and stores share
+  // one counter).  The shifted values are exact in the history dtype (they came
+  // from it or from the input, which has the same dtype).
+#pragma unroll
+  for (int j = 0; j < NCH; ++j) {
+    if (tid + kDecodeThreads * j < NC) {
+      const size_t r0 = (size_t)n * 3 * cch + chr[j];
+      store1<IN_BF16>(p.conv_state, r0, hr[j][1]);
+      store1<IN_BF16>(p.conv_state, r0 + cch, hr[j][2]);
+      store1<IN_BF16>(p.conv_state, r0 + 2 * cch, xr[j]);
+    }
   }
 }
 

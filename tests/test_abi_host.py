@@ -287,3 +287,27 @@ def test_noalloc_rejects_heads_beyond_its_scratch(kda):
     assert L.kda_prefill_noalloc(ctypes.byref(a), None) == -6
     assert b"scratch" in L.kda_last_error()
     assert kda.NOALLOC_SCRATCH_BYTES == 128 << 20
+
+
+def test_peaks_library_exports_its_header():
+    """libkda_peaks.so (the measured-peak microbenchmarks the benchmark reports
+    beside the vendor peaks) exports every function include/kda_peaks.h declares."""
+    path = os.path.join(os.path.dirname(HEADER), "..", "gated_delta_rule_28_amd", "libkda_peaks.so")
+    if not os.path.exists(path):
+        pytest.skip("libkda_peaks.so not built")
+    text = re.sub(r"/\*.*?\*/", "", open(os.path.join(os.path.dirname(HEADER), "kda_peaks.h")).read(), flags=re.S)
+    names = set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kda_\w+)\s*\(", text, flags=re.M))
+    assert names == {"kda_peak_fmw", "kda_peak_stream", "kda_peak_mfma"}
+    out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
+    assert names <= set(re.findall(r" T (kda_\w+)", out))
+    L = ctypes.CDLL(path)
+    L.kda_peak_fmw.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    L.kda_peak_mfma.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    # argument checks run before any HIP call
+    assert L.kda_peak_fmw(None, 65536, 0, None) == -1
+    assert L.kda_peak_fmw(1 << 20, 1000, 0, None) == -2
+    assert L.kda_peak_fmw((1 << 20) + 4, 65536, 0, None) == -3
+    L.kda_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    assert L.kda_peak_stream(1 << 20, 65536, 2, None) == -2
+    assert L.kda_peak_mfma(None, 1, 1, 4, None) == -1
+    assert L.kda_peak_mfma(1 << 20, 1, 1, 5, None) == -2
