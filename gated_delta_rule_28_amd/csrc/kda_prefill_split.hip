@@ -153,7 +153,11 @@ __device__ __forceinline__ float conv3_dpp(float a, float x, float y, float w1, 
 // lane 16 + i - j: a rotation by j of the row in which lanes 16 - j .. 15
 // offer their halo instead of their own token.
 // `sink(kp, x8)` takes the 8 outputs of channel group kp.
-template <typename Sink>
+// LOG2E: the taps are pre-multiplied by log2(e), so the conv gives
+// t = log2(e) a and SiLU(a) = a / (1 + 2^-t) is returned as log2(e) SiLU(a)
+// = t / (1 + 2^-t), one multiply fewer; the L2 normalisation that follows for
+// q and k removes the constant factor (its epsilon is scaled to match).
+template <bool LOG2E, typename Sink>
 __device__ __forceinline__ void conv_silu(const uint4 (&cur)[4], const uint4 (&hal)[4], const float4* cw,
                                           Sink&& sink) {
 #pragma unroll
@@ -164,21 +168,24 @@ __device__ __forceinline__ void conv_silu(const uint4 (&cur)[4], const uint4 (&h
       const float xc = bf16_at(cur[kp], e);
       const float y = bf16_at(hal[kp], e);
       const float4 w = cw[32 * kp + e];
-      x[e] = siluf_(conv3_dpp(w.w * xc, xc, y, w.z, w.y, w.x));
+      const float a = conv3_dpp(w.w * xc, xc, y, w.z, w.y, w.x);
+      if constexpr (LOG2E) x[e] = a * fast_rcp(1.0f + __builtin_amdgcn_exp2f(-a));
+      else x[e] = siluf_(a);
     }
     sink(kp, x);
   }
 }
 
 // Scale x[32] to unit L2 norm over the token's 128 channels (held by lanes
-// i, i+16, i+32, i+48), times `extra`.
+// i, i+16, i+32, i+48), times `extra`; x holds log2(e) times the SiLU outputs
+// (see conv_silu), so the epsilon is log2(e)^2 times the definition's.
 __device__ __forceinline__ void l2norm128(float (&x)[32], float extra) {
   float ss = 0.f;
 #pragma unroll
   for (int c = 0; c < 32; ++c) ss += x[c] * x[c];
   ss += __shfl_xor(ss, 16, 64);
   ss += __shfl_xor(ss, 32, 64);
-  const float r = fast_rsq(ss + kL2Eps) * extra;
+  const float r = fast_rsq(ss + kL2Eps * kLog2e * kLog2e) * extra;
 #pragma unroll
   for (int c = 0; c < 32; ++c) x[c] *= r;
 }
@@ -278,7 +285,6 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   // Raw q / k / v (this token and the halo) of one tensor, loaded while the
   // previous tensor is processed: at most two tensors' raw values are live.
   const uint16_t* ci16 = reinterpret_cast<const uint16_t*>(p.conv_in);
-  const uint32_t hm = hok ? ~0u : 0u;  // no earlier tokens: the halo is zero
   auto load_raw = [&](const void* src, int part, uint4 (&r)[4], uint4 (&hr)[4]) {
     const uint16_t* x16 = reinterpret_cast<const uint16_t*>(src);
 #pragma unroll
@@ -290,10 +296,11 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       hr[kp] = *reinterpret_cast<const uint4*>(ph);
     }
   };
+  // no earlier tokens (a wave-uniform case): the halo is zero
   auto mask_halo = [&](uint4 (&hr)[4]) {
+    if (!hok) {
 #pragma unroll
-    for (int kp = 0; kp < 4; ++kp) {
-      hr[kp].x &= hm; hr[kp].y &= hm; hr[kp].z &= hm; hr[kp].w &= hm;
+      for (int kp = 0; kp < 4; ++kp) hr[kp] = make_uint4(0u, 0u, 0u, 0u);
     }
   };
   uint4 rg[4], ra[4], ha[4], rb[4], hb[4];
@@ -311,7 +318,9 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     const size_t gch = ch < kD ? (size_t)h * kD + ch
                      : ch < 2 * kD ? (size_t)H * kD + (size_t)h * kD + (ch - kD)
                                    : (size_t)2 * H * kD + (size_t)h * kD + (ch - 2 * kD);
-    sCW[ch] = *reinterpret_cast<const float4*>(p.conv_w + gch * 4);
+    float4 w = *reinterpret_cast<const float4*>(p.conv_w + gch * 4);
+    if (ch < 2 * kD) w = make_float4(w.x * kLog2e, w.y * kLog2e, w.z * kLog2e, w.w * kLog2e);  // q, k: see conv_silu
+    sCW[ch] = w;
   }
   if (g == 0) sBeta[tok] = beta_v;
   if (tid == 0) *sFlag = 0;
@@ -384,7 +393,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   {
     float x[32];
     mask_halo(hb);
-    conv_silu(rb, hb, sCW + 8 * g, [&](int kp, const float* x8) {
+    conv_silu<true>(rb, hb, sCW + 8 * g, [&](int kp, const float* x8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
     });
@@ -423,7 +432,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   {
     float x[32];
     mask_halo(ha);
-    conv_silu(ra, ha, sCW + kD + 8 * g, [&](int kp, const float* x8) {
+    conv_silu<true>(ra, ha, sCW + kD + 8 * g, [&](int kp, const float* x8) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) x[8 * kp + e] = x8[e];
     });
@@ -472,7 +481,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   // ---- v -----------------------------------------------------------------------------
   half8 Vf[4];
   mask_halo(hb);
-  conv_silu(rb, hb, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
+  conv_silu<false>(rb, hb, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
   // v's conv completes here rather than being sunk past the barrier into the
   // products below (where its raw values would stay live)
   asm volatile("" : "+v"(Vf[0]), "+v"(Vf[1]), "+v"(Vf[2]), "+v"(Vf[3]));
