@@ -7,16 +7,19 @@
 // work stops being parallel:
 //
 //   intra_chunk_kernel  one workgroup (4 waves) per (b, h, chunk); every chunk
-//     of every head at once.  Conv + SiLU + L2 normalisation + chunk-local
-//     cumulative sum of g, then A, P and T = (I + A)^-1 on the matrix cores.
+//     of every head at once.  Conv + SiLU + L2 normalisation of q and k,
+//     chunk-local cumulative sum of g, then A, P and T = (I + A)^-1 on the
+//     matrix cores.
 //   inter_chunk_kernel  one workgroup (8 waves) per (b, h) walks the chunks in
-//     order with the fp32 state in registers:
+//     order with the fp32 state in registers: v's conv + SiLU, then
 //       U = T diag(beta) (V - (K e^G) S)        (= U~ - W S of the WY form)
 //       O = (Q e^G) S + P U,   S <- e^{G_C} S + (K e^{G_C-G})^T U,
 //     then RMSNorm * sigmoid(gate).
 //   Taking V - (K e^G) S first keeps the cancellation between the new values
-//   and the state's prediction in fp32 accumulators, and hands over V and
-//   K e^G in fp16 instead of W and an fp32 U~.
+//   and the state's prediction in fp32 accumulators, and hands over K e^G in
+//   fp16 instead of W and an fp32 U~.  V itself is not handed over: the
+//   second kernel reads raw v (as many bytes as fp16 V) and convolves it, so
+//   the first kernel never touches v.
 //
 // The first kernel hands the second its operands in a workspace laid out as
 // matrix-core fragments (64 lanes x 16 bytes, lane order), so every operand
@@ -74,8 +77,7 @@ constexpr int WS_TB = WS_P + 6 * kFrag;      // T diag(beta) fragments, as P: 6
 constexpr int WS_GAM = WS_TB + 6 * kFrag;    // e^{G_C} in state row order, 128 fp32; int "wide" flag at +512
 constexpr int WS_WIDE = WS_GAM + 512;        // int: the chunk is wide (see the file header)
 constexpr int WS_STAGE = WS_GAM + 4 * kFrag; // bytes the second kernel stages through LDS (64 KiB)
-constexpr int WS_V = WS_STAGE;               // V (rt, w): C layout, 64 lanes x 8 fp16   16 KiB
-constexpr int WS_CHUNK = WS_V + 16 * kFrag;  // 80 KiB per chunk
+constexpr int WS_CHUNK = WS_STAGE;           // 64 KiB per chunk
 constexpr size_t kSlabBytesMax = (size_t)16 << 30;  // workspace cap for the chunk blocks
 
 __device__ __forceinline__ int p_frag(int rt, int kp) { return rt < 2 ? rt : 2 * rt - 2 + kp; }
@@ -221,17 +223,13 @@ struct ALds {
   static constexpr int TB = AM + kC * LDA * 4;        // [64][LDB] fp16
   static constexpr int R1_B = TB + kC * LDB * 2;
   static constexpr int R2 = ((R1_A > R1_B ? R1_A : R1_B) + 15) / 16 * 16;
-  // R2, until the A / P products: conv taps and per-channel decay factors
-  static constexpr int CW = R2;                       // [384] float4
-  static constexpr int ERHO = CW + kNCh * 16;         // [4][128] e^{rho_a}
+  // R2: conv taps of q and k and per-channel decay factors
+  static constexpr int CW = R2;                       // [256] float4
+  static constexpr int ERHO = CW + 2 * kD * 16;       // [4][128] e^{rho_a}
   static constexpr int ETOT = ERHO + 4 * kD * 4;      // [4][128] e^{tot_a}
   static constexpr int EKB = ETOT + 4 * kD * 4;       // [4][128] e^{G_C - rho_a - tot_a}
   static constexpr int FOFF = EKB + 4 * kD * 4;       // [3][128] e^{rho_a - rho_{b+1}}: (2,0) (3,0) (3,1)
-  static constexpr int R2_A = FOFF + 3 * kD * 4;
-  // R2, afterwards: V^T
-  static constexpr int VT = R2;                       // [128][kLDT] fp16
-  static constexpr int R2_B = VT + kD * kLDT * 2;
-  static constexpr int BYTES = R2_A > R2_B ? R2_A : R2_B;
+  static constexpr int BYTES = FOFF + 3 * kD * 4;
 };
 
 // ---------------------------------------------------------------------------
@@ -254,7 +252,6 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   _Float16* sKBT = reinterpret_cast<_Float16*>(smem + L::KBT);
   float* sAM = reinterpret_cast<float*>(smem + L::AM);
   _Float16* sTB = reinterpret_cast<_Float16*>(smem + L::TB);
-  _Float16* sVT = reinterpret_cast<_Float16*>(smem + L::VT);
   constexpr int LDA = L::LDA, LDB = L::LDB;
 
   const int H = p.H, T = p.T;
@@ -282,8 +279,8 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   const size_t hrow = ((size_t)b * T + min(max(th, 0), T - 1)) * H + h;
   const size_t hist = ((size_t)b * 3 + (3 + max(th, -3))) * cch;  // conv_in row when th < 0
   const bool from_hist = !h_in && p.conv_in != nullptr;
-  // Raw q / k / v (this token and the halo) of one tensor, loaded while the
-  // previous tensor is processed: at most two tensors' raw values are live.
+  // Raw q / k (this token and the halo) of one tensor; k's are loaded while q
+  // is processed.
   const uint16_t* ci16 = reinterpret_cast<const uint16_t*>(p.conv_in);
   auto load_raw = [&](const void* src, int part, uint4 (&r)[4], uint4 (&hr)[4]) {
     const uint16_t* x16 = reinterpret_cast<const uint16_t*>(src);
@@ -313,14 +310,13 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   float beta_v = valid ? bf16_to_f(reinterpret_cast<const uint16_t*>(p.beta)[row]) : 0.f;
   if constexpr (K3) beta_v = valid ? sigmoidf_(beta_v) : 0.f;
 
-  // conv taps of this head, per-token beta, fp16-range flag
-  for (int ch = tid; ch < kNCh; ch += 256) {
-    const size_t gch = ch < kD ? (size_t)h * kD + ch
-                     : ch < 2 * kD ? (size_t)H * kD + (size_t)h * kD + (ch - kD)
-                                   : (size_t)2 * H * kD + (size_t)h * kD + (ch - 2 * kD);
-    float4 w = *reinterpret_cast<const float4*>(p.conv_w + gch * 4);
-    if (ch < 2 * kD) w = make_float4(w.x * kLog2e, w.y * kLog2e, w.z * kLog2e, w.w * kLog2e);  // q, k: see conv_silu
-    sCW[ch] = w;
+  // conv taps of this head's q and k (times log2(e), see conv_silu), per-token
+  // beta, fp16-range flag
+  {
+    const int ch = tid;  // 256 threads: q channels, then k channels
+    const size_t gch = ch < kD ? (size_t)h * kD + ch : (size_t)H * kD + (size_t)h * kD + (ch - kD);
+    const float4 w = *reinterpret_cast<const float4*>(p.conv_w + gch * 4);
+    sCW[ch] = make_float4(w.x * kLog2e, w.y * kLog2e, w.z * kLog2e, w.w * kLog2e);
   }
   if (g == 0) sBeta[tok] = beta_v;
   if (tid == 0) *sFlag = 0;
@@ -475,16 +471,6 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       for (int e = 0; e < 8; ++e) sKBT[tix(32 * kp + 8 * g + e, tok)] = (_Float16)kb[e];
     }
   }
-  // v's raw values are requested only now: issued during k's work they held 32
-  // more registers at its peak and the kernel spilled (measured slower)
-  load_raw(p.v, 2, rb, hb);
-  // ---- v -----------------------------------------------------------------------------
-  half8 Vf[4];
-  mask_halo(hb);
-  conv_silu<false>(rb, hb, sCW + 2 * kD + 8 * g, [&](int kp, const float* x8) { Vf[kp] = to_half8(x8); });
-  // v's conv completes here rather than being sunk past the barrier into the
-  // products below (where its raw values would stay live)
-  asm volatile("" : "+v"(Vf[0]), "+v"(Vf[1]), "+v"(Vf[2]), "+v"(Vf[3]));
   lds_barrier();
 
   // ---- A^T and P^T blocks (b, a), b <= a: D[j][r] = sum_c col_b[j][c] row_a[r][c] --
@@ -526,7 +512,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       st_nt(wsb + WS_KB + ((m * 2 + kp) * 64 + lane) * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
     }
   }
-  lds_barrier();  // R1 and R2 are rewritten from here on
+  lds_barrier();  // R1 is rewritten from here on
 
   // A (beta_r scaled, strictly lower) into AM; P fragments to the workspace
 #pragma unroll
@@ -556,11 +542,6 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
       st_nt(wsb + WS_P + (p_frag(wave, kp) * 64 + lane) * 16, to_half8(pv));
     }
   }
-  // V^T, for V in the C layout of the second kernel
-#pragma unroll
-  for (int kp = 0; kp < 4; ++kp)
-#pragma unroll
-    for (int e = 0; e < 8; ++e) sVT[tix(32 * kp + 8 * g + e, tok)] = Vf[kp][e];
   lds_barrier();
 
   // ---- T = (I + A)^-1: diagonal 16x16 blocks by forward substitution --------------
@@ -629,7 +610,7 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   }
   lds_barrier();
 
-  // ---- hand-over: T diag(beta) as row-operand fragments, V in C layout ------------
+  // ---- hand-over: T diag(beta) as row-operand fragments ------------------------------
   // T diag(beta) fragment (rt, k'), like P: lane (g, i) holds row 16rt + i at
   // tokens 32k' + 4g + 0..3 and 32k' + 16 + 4g + 0..3; wave w writes fragments w, w + 4
 #pragma unroll
@@ -639,24 +620,17 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
     const half4 hi = *reinterpret_cast<const half4*>(sTB + (16 * rt + i) * LDB + 32 * kp + 16 + 4 * g);
     st_nt(wsb + WS_TB + (f * 64 + lane) * 16, half8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]});
   }
-  // V fragment (rt, w): lane (g, i) holds tokens 16rt + 4g + 0..3 of dv columns
-  // 16(2w) + i and 16(2w + 1) + i
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    const half4 c0v = *reinterpret_cast<const half4*>(sVT + tix(32 * wave + i, 16 * rt + 4 * g));
-    const half4 c1v = *reinterpret_cast<const half4*>(sVT + tix(32 * wave + 16 + i, 16 * rt + 4 * g));
-    st_nt(wsb + WS_V + ((rt * 4 + wave) * 64 + lane) * 16, half8{c0v[0], c0v[1], c0v[2], c0v[3], c1v[0], c1v[1], c1v[2], c1v[3]});
-  }
 }
 
 // ---------------------------------------------------------------------------
 // inter_chunk_kernel: grid B * H, block 512 (8 waves), one workgroup per (b, h)
 //
 //   waves 0..3 ("math"): wave w owns dv columns 32w .. 32w+31 and the state
-//     columns with them; per chunk it runs U = T diag(beta) (V - (K e^G) S),
-//     O = (Q e^G) S + P U and S <- e^{G_C} S + (K e^{G_C-G})^T U on the matrix
-//     cores and leaves O in LDS.  Its only memory accesses are LDS reads and
-//     the V of the next chunk, so it never waits behind other traffic.
+//     columns with them; per chunk it forms V = SiLU(conv(v)) of its columns,
+//     runs U = T diag(beta) (V - (K e^G) S), O = (Q e^G) S + P U and
+//     S <- e^{G_C} S + (K e^{G_C-G})^T U on the matrix cores and leaves O in
+//     LDS.  Its only memory accesses are LDS reads and the raw v of the next
+//     chunk, so it never waits behind other traffic.
 //   waves 4..7 ("epilogue"): wave 4 + r copies a quarter of the next chunk's
 //     operands into LDS and takes token tile r of the previous chunk's O:
 //     RMSNorm over its rows * sigmoid(gate), stores (16-byte pieces; the gate
@@ -682,7 +656,19 @@ __shared__ __attribute__((aligned(16))) unsigned char g_stage1[WS_STAGE];  // op
 constexpr int kOGrp = 288;
 constexpr int kOBlk = 4 * kOGrp;
 __shared__ __attribute__((aligned(16))) unsigned char g_O[16 * kOBlk];
-static_assert(2 * WS_STAGE + 16 * kOBlk <= 160 * 1024, "inter-chunk LDS exceeds 160 KiB");
+// conv taps of the head's v channels
+__shared__ float4 g_vw[kD];
+static_assert(2 * WS_STAGE + 16 * kOBlk + kD * 16 <= 160 * 1024, "inter-chunk LDS exceeds 160 KiB");
+
+// B operand of the 16x16x32 instruction that moves columns 16ct .. 16ct + 15
+// of a row-operand tile into the C layout: lane (g, i) holds rows 8g .. 8g + 7
+// of column i of the 32 x 16 matrix [k == i + 16 ct].
+__device__ __forceinline__ half8 ident_frag(int g, int i, int ct) {
+  half8 f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) f[e] = 8 * g + e == i + 16 * ct ? (_Float16)1.0f : (_Float16)0.0f;
+  return f;
+}
 
 template <int P>
 __device__ __forceinline__ unsigned char* stage_buf() {
@@ -729,6 +715,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) S[m][ct] = f4{0.f, 0.f, 0.f, 0.f};
   if (math) {
+    if (tid < kD) g_vw[tid] = *reinterpret_cast<const float4*>(p.conv_w + ((size_t)2 * H * kD + (size_t)h * kD + tid) * 4);
     if (p.S_in != nullptr) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
@@ -749,15 +736,38 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   // waves waited for their copies), O(j-1) is complete, and nobody reads the
   // buffer copied next.
   if (math) {
-    // V of this wave's columns (C layout, fp16), loaded one chunk ahead into
-    // the register set of the chunk's parity
-    uint4 vt[2][4];
-    if (nc > 0) {
+    // Raw v of this wave's columns in the row-operand layout: register rt of
+    // lane (g, i) holds token 16 rt + i (clamped to the sequence) and channels
+    // col0 + 8g .. col0 + 8g + 7, loaded one chunk ahead into the register set
+    // of the chunk's parity.
+    const uint16_t* v16 = reinterpret_cast<const uint16_t*>(p.v);
+    auto load_v = [&](int jc, uint4 (&r)[4]) {
+      const int c0 = (p.c_begin + jc) * kC;
+      const int last = min(kC, T - c0) - 1;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        vt[0][rt] = ld_nt(wsh + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
+        r[rt] = ld_nt(v16 + (((size_t)b * T + c0 + min(16 * rt + i, last)) * H + h) * kD + col0 + 8 * g);
+    };
+    uint4 rv[2][4];
+    if (nc > 0) {
+      load_v(0, rv[0]);
+      // The conv's halo of the first chunk goes where the previous chunk's last
+      // tile would be: lanes 13..15 take the three raw tokens before the chunk,
+      // from the sequence, the conv history, or zeros at the sequence start.
+      const int c0 = p.c_begin * kC;
+      const int th = c0 - 16 + max(i, 13);
+      if (c0 > 0) {
+        rv[1][3] = *reinterpret_cast<const uint4*>(v16 + (((size_t)b * T + th) * H + h) * kD + col0 + 8 * g);
+      } else if (p.conv_in != nullptr) {
+        const size_t cch = (size_t)H * kNCh;
+        rv[1][3] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(p.conv_in) +
+                                                   ((size_t)b * 3 + (3 + th)) * cch + (size_t)2 * H * kD +
+                                                   (size_t)h * kD + col0 + 8 * g);
+      } else {
+        rv[1][3] = make_uint4(0u, 0u, 0u, 0u);
+      }
     }
-    // one chunk; P = j & 1 picks the staging buffer and the V registers
+    // one chunk; P = j & 1 picks the staging buffer and the raw v registers
     auto step = [&](auto parity, int j) {
       constexpr int P = decltype(parity)::value;
       __builtin_amdgcn_s_waitcnt(0);
@@ -765,21 +775,29 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       f4 O[4][2], X[4][2];
       const unsigned char* sb = stage_buf<P>();
       if (j < nc) {
+        // V = SiLU(conv(v)) in fp16 (the causal conv along the tokens of each
+        // 16-lane row, the previous tile's raw values as the halo: for tile 0
+        // the previous chunk's tile 3), moved into the C layout of X by a
+        // product with the identity
+        half8 vh[4];
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
-          const half8 v8 = __builtin_bit_cast(half8, vt[P][rt]);
+        for (int e = 0; e < 8; ++e) {
+          const float4 wv = g_vw[col0 + 8 * g + e];
 #pragma unroll
-          for (int ct = 0; ct < 2; ++ct) {
-            X[rt][ct] = f4{(float)v8[4 * ct], (float)v8[4 * ct + 1], (float)v8[4 * ct + 2], (float)v8[4 * ct + 3]};
-            O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+          for (int rt = 0; rt < 4; ++rt) {
+            const float xc = bf16_at(rv[P][rt], e);
+            const float y = bf16_at(rt == 0 ? rv[1 - P][3] : rv[P][rt - 1], e);
+            vh[rt][e] = (_Float16)siluf_(conv3_dpp(wv.w * xc, xc, y, wv.z, wv.y, wv.x));
           }
         }
-        if (j + 1 < nc) {
-          const unsigned char* wn = wsh + (size_t)(j + 1) * WS_CHUNK;
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt)
-            vt[1 - P][rt] = ld_nt(wn + WS_V + ((rt * 4 + w) * 64 + lane) * 16);
-        }
+        for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) {
+            X[rt][ct] = mma_f16(vh[rt], ident_frag(g, i, ct), f4{0.f, 0.f, 0.f, 0.f});
+            O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+          }
+        if (j + 1 < nc) load_v(j + 1, rv[1 - P]);
         // X = V + (-(K e^G)) S and (Q e^G) S, one 32-row step of S at a time:
         // its B operands are rows 16(2k + s) + 4g + e, s = 0, 1
 #pragma unroll
@@ -887,9 +905,12 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         }
       }
     };
-    for (int j = 0; j <= nc; j += 2) {
-      step(std::integral_constant<int, 0>{}, j);
-      if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
+    // both roles skip the loop (and its barriers) in a launch without chunks
+    if (nc > 0) {
+      for (int j = 0; j <= nc; j += 2) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
+      }
     }
   } else {
     // lane (u, q) = (lane / 8, lane % 8) of epilogue wave r = w: tokens
@@ -968,9 +989,12 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       }
       if (j >= 1 && j < nc) load_gate(j);
     };
-    for (int j = 0; j <= nc; j += 2) {
-      step(std::integral_constant<int, 0>{}, j);
-      if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
+    // both roles skip the loop (and its barriers) in a launch without chunks
+    if (nc > 0) {
+      for (int j = 0; j <= nc; j += 2) {
+        step(std::integral_constant<int, 0>{}, j);
+        if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
+      }
     }
   }
 

@@ -145,7 +145,7 @@ typedef struct kda_prefill_args {
 
 int kda_prefill(const kda_prefill_args* args, void* stream);
 
-/* Device workspace the two-kernel path prefers for these sizes: 80 KiB per
+/* Device workspace the two-kernel path prefers for these sizes: 64 KiB per
  * (b, h, chunk of 64 tokens) of one slab; for a pipelined sequence (more than
  * 64 chunks, 2*B*H <= 256) three buffers of one slab of up to 64 chunks (two
  * when there are two slabs) plus B*H*dk*dv*4 bytes to carry the state; otherwise all chunks in one slab,
@@ -401,8 +401,8 @@ int kda_abi_version(void);
  * until the process ends; its slabs run one after the other on `stream` (no
  * streams are created).  Other shapes take the single-kernel path, which
  * needs no workspace.  The call makes no hipMalloc / hipFree or other
- * allocating call.  Limit: B*H * (80 KiB + 64 KiB) must fit the scratch, i.e.
- * at most 910 heads (B*H) for sequences longer than one chunk; beyond that it
+ * allocating call.  Limit: B*H * (64 KiB + 64 KiB) must fit the scratch, i.e.
+ * at most 1024 heads (B*H) for sequences longer than one chunk; beyond that it
  * returns KDA_E_WORKSPACE and launches nothing.  Every call on one GPU uses
  * the same scratch: calls that overlap on one GPU (other streams, other host
  * threads) race and must be ordered by the caller. */

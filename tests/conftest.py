@@ -18,3 +18,19 @@ def oracle_mod():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+@pytest.fixture
+def progress(request):
+    """progress(msg): a line written to the terminal at once, past pytest's
+    output capture, so that a test running for minutes shows it is alive."""
+    capman = request.config.pluginmanager.getplugin("capturemanager")
+
+    def say(msg):
+        if capman is None:
+            print(msg, flush=True)
+            return
+        with capman.global_and_fixture_disabled():
+            print(msg, flush=True)
+
+    return say

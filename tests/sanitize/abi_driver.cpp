@@ -67,7 +67,7 @@ int main() {
     a.workspace_bytes = 16;  // below the minimum
     EXPECT(kda_prefill(&a, nullptr) == KDA_E_WORKSPACE);
     // no-allocation entry: more heads than its scratch holds
-    a = prefill_base(1, 128, 1000, 128, 64, KDA_BF16);
+    a = prefill_base(1, 128, 1025, 128, 64, KDA_BF16);
     EXPECT(kda_prefill_noalloc(&a, nullptr) == KDA_E_WORKSPACE);
     EXPECT(std::strstr(kda_last_error(), "scratch") != nullptr);
     // T = 0 with nothing to write: a valid no-op

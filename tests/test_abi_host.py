@@ -131,7 +131,7 @@ def test_prefill_workspace_sizes_and_check(kda):
     L = kda.lib()
     # sizes with a two-kernel path: bf16 inputs, chunk 64, dk = dv = 128
     a = _prefill_args(kda, B=2, T=300, H=3, dk=128, dv=128, chunk=64)
-    per_chunk = 2 * 3 * 80 * 1024
+    per_chunk = 2 * 3 * 64 * 1024
     carry = 2 * 3 * 128 * 128 * 4
     assert L.kda_prefill_workspace_bytes(ctypes.byref(a)) == 5 * per_chunk   # all 5 chunks, one launch
     assert L.kda_prefill_workspace_min_bytes(ctypes.byref(a)) == per_chunk + carry
@@ -155,10 +155,10 @@ def test_prefill_workspace_sizes_and_check(kda):
     # a state carry: the same size for 65,536 and 1,048,576 tokens at K3 width
     for T in (1 << 16, 1 << 20):
         big = _prefill_args(kda, B=1, T=T, H=96, dk=128, dv=128, chunk=64)
-        assert L.kda_prefill_workspace_bytes(ctypes.byref(big)) == 3 * 64 * 96 * 80 * 1024 + 96 * 128 * 128 * 4
+        assert L.kda_prefill_workspace_bytes(ctypes.byref(big)) == 3 * 64 * 96 * 64 * 1024 + 96 * 128 * 128 * 4
     # 65 chunks: two balanced slabs of 33, one buffer each
     b65 = _prefill_args(kda, B=1, T=65 * 64, H=2, dk=128, dv=128, chunk=64)
-    assert L.kda_prefill_workspace_bytes(ctypes.byref(b65)) == 2 * 33 * 2 * 80 * 1024 + 2 * 128 * 128 * 4
+    assert L.kda_prefill_workspace_bytes(ctypes.byref(b65)) == 2 * 33 * 2 * 64 * 1024 + 2 * 128 * 128 * 4
 
 
 def test_decode_validation_codes(kda):
@@ -278,11 +278,11 @@ def test_release_with_nothing_kept(kda):
 
 def test_noalloc_rejects_heads_beyond_its_scratch(kda):
     """kda_prefill_noalloc validates on the host: B*H whose minimum workspace
-    (80 KiB + 64 KiB per head) exceeds the 128 MiB scratch is refused with
+    (64 KiB + 64 KiB per head) exceeds the 128 MiB scratch is refused with
     KDA_E_WORKSPACE before any HIP call (so this runs without a GPU)."""
     L = kda.lib()
     fake = 1 << 20  # a 16-byte aligned stand-in address; nothing is launched
-    a = kda.PrefillArgs(1, 128, 1000, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32, fake, fake, fake, fake, fake,
+    a = kda.PrefillArgs(1, 128, 1025, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32, fake, fake, fake, fake, fake,
                         fake, fake, None, None, fake, fake, fake, None, 0, kda.KDA_DECAY_DIRECT, None)
     assert L.kda_prefill_noalloc(ctypes.byref(a), None) == -6
     assert b"scratch" in L.kda_last_error()

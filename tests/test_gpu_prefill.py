@@ -134,7 +134,7 @@ def test_slabs_of_a_small_workspace(oracle_mod, per_slab):
     w = Workload("sl", 2, 300, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=9)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    per_chunk = w.B * w.H * 80 * 1024
+    per_chunk = w.B * w.H * 64 * 1024
     nbytes = per_slab * per_chunk + w.B * w.H * w.dk * w.dv * 4
     assert nbytes >= kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv, minimum=True)
     assert nbytes < kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv)
@@ -153,7 +153,7 @@ def test_pipelined_slabs(oracle_mod, per_buf):
     w = Workload("pp", 1, 70 * 64, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=17)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    per_chunk = w.B * w.H * 80 * 1024
+    per_chunk = w.B * w.H * 64 * 1024
     carry = w.B * w.H * w.dk * w.dv * 4
     assert kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv) == 2 * 35 * per_chunk + carry
     ws = "auto" if per_buf is None else torch.empty(3 * per_buf * per_chunk + carry, dtype=torch.uint8,
@@ -169,7 +169,7 @@ def test_pipelined_half_first_slab(oracle_mod):
     w = Workload("pf", 1, 131 * 64 - 55, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=29)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
-    per_chunk = w.B * w.H * 80 * 1024
+    per_chunk = w.B * w.H * 64 * 1024
     assert kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv) == 3 * 64 * per_chunk + w.B * w.H * w.dk * w.dv * 4
     o, S_T, c = _gpu_prefill(kda, dev, 64)
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="half-size first slab")
@@ -186,7 +186,7 @@ def test_slab_plans_at_other_shapes(oracle_mod, B, H, T):
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
     nch = -(-T // 64)
-    per_chunk = B * H * 80 * 1024
+    per_chunk = B * H * 64 * 1024
     carry = B * H * 128 * 128 * 4
     if 2 * B * H <= 256:
         want = 2 * (-(-nch // 2)) * per_chunk + carry

@@ -123,7 +123,7 @@ def test_k3width_mixed_fast_channels_all_heads(oracle_mod):
 
 
 @pytest.mark.timeout(1100)
-def test_long1m_prefill_all_heads(oracle_mod):
+def test_long1m_prefill_all_heads(oracle_mod, progress):
     """B1 T1048576 H96 d128 in 16 segments of 65536 with S and the conv history
     carried in place (the benchmark's calls): all 96 heads over all 1M tokens.
     The oracle follows segment by segment with its own fp64 carry; the RMS is
@@ -148,7 +148,7 @@ def test_long1m_prefill_all_heads(oracle_mod):
         r = oracle_mod.prefill(host, S=S_ref, hist=hist_ref)  # carries S_ref / hist_ref in place
         acc.add(got, r["o"])
         del r, host, got
-        print(f"  segment {s + 1}/{w.segments}: running max|err| {acc.err:.3e}", flush=True)
+        progress(f"  segment {s + 1}/{w.segments}: running max|err| {acc.err:.3e}")
     acc.check(TOL_BF16, "long1m o, all heads")
     assert_rms_close(S[0].cpu().numpy(), S_ref, TOL_BF16, "long1m S_T, all heads")
     conv_np = syn.torch_to_np(conv)
@@ -158,7 +158,7 @@ def test_long1m_prefill_all_heads(oracle_mod):
 
 
 @pytest.mark.timeout(600)
-def test_decode_1000_steps_all_pairs(oracle_mod):
+def test_decode_1000_steps_all_pairs(oracle_mod, progress):
     """256 sequences x 96 heads, 1000 consecutive decode steps: every (sequence,
     head) pair over all steps, the state carried in fp64 by the oracle (which
     runs each pair's 1000 tokens as one prefill: its pins show that equals
@@ -193,7 +193,7 @@ def test_decode_1000_steps_all_pairs(oracle_mod):
             n, h = divmod(i, w.H)
             ch = oracle_mod._head_channels(w.H, w.dk, w.dv, h)
             assert np.array_equal(conv_np[n][:, ch], syn.bf16_bits_from_f64(r["conv_out"][i])), "conv state"
-        print(f"  sequences {n0}..{n0 + nb - 1}: running max|err| o {acc_o.err:.3e}", flush=True)
+        progress(f"  sequences {n0}..{n0 + nb - 1}: running max|err| o {acc_o.err:.3e}")
         del r, host
     acc_o.check(TOL_DECODE, "decode x1000 o, all pairs")
     acc_s.check(TOL_DECODE, "decode x1000 S, all pairs")

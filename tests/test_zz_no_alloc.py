@@ -39,8 +39,8 @@ def _compare(kda, torch, w, seed_note):
 
 def test_noalloc_matches_prefill_twice():
     torch, kda = need_gpu()
-    # 64 chunks x 32 heads x 80 KiB = 160 MiB of chunk blocks: several slabs of the scratch
-    _compare(kda, torch, Workload("na1", 1, 4096, 32, 128, 128, 64, "bf16", s0_sigma=0.05,
+    # 128 chunks x 32 heads x 64 KiB = 256 MiB of chunk blocks: several slabs of the scratch
+    _compare(kda, torch, Workload("na1", 1, 8192, 32, 128, 128, 64, "bf16", s0_sigma=0.05,
                                   conv_hist="normal", seed=301), "first call")
     # smaller: one slab
     _compare(kda, torch, Workload("na2", 2, 300, 3, 128, 128, 64, "bf16", s0_sigma=0.05,
