@@ -337,8 +337,9 @@ def time_context_parallel(torch, kda, w, inp, R, A, steps):
     """kda_prefill_cp of the whole workload (all T tokens of each sequence, whatever
     segmentation the workload's own timing uses) in R segments on this GPU (three prefill
     passes over all segments and the composition), and one rank's share of it at
-    the rank's shape: its segment from S = 0 and from S = I, the composition of
-    the R gathered fragments, and its segment again from the entering state (the
+    the rank's shape: kda_cp_fragments of its segment (the intra-chunk work once,
+    the recurrence from S = 0 and from S = I side by side), the composition of
+    the R gathered fragments and kda_cp_finish from the entering state (the
     exchange itself needs R GPUs and is not timed)."""
     if w.T % R or w.T // R < 3:
         raise SystemExit(f"--cp-segments {R} does not split workload {w.name}")
@@ -364,20 +365,19 @@ def time_context_parallel(torch, kda, w, inp, R, A, steps):
     # one rank's share (segment 0's inputs; every segment has the same shape)
     seg = [t if t is inp["conv_w"] else t[:, :L].contiguous() for t in args]
     BH = w.B * w.H
-    eye = torch.eye(w.dk, device=dev).expand(w.B, w.H, w.dk, w.dv).contiguous()
-    N1, P1 = torch.empty_like(eye), torch.empty_like(eye)
+    N1 = torch.empty((w.B, w.H, w.dk, w.dv), dtype=torch.float32, device=dev)
+    P1 = torch.empty_like(N1)
     NR = torch.randn((w.B * R, w.H, w.dk, w.dv), device=dev) * 0.01
     PR = NR + torch.randn_like(NR) * 0.01
     Sst = torch.empty_like(NR)
     o_r = torch.empty((w.B, L, w.H, w.dv), dtype=torch.float32, device=dev)
-    ws_r = torch.empty(max(kda.workspace_bytes(w.B, L, w.H, w.dk, w.dv, w.chunk), 1), dtype=torch.uint8,
+    ws_r = torch.empty(max(kda.cp_rank_workspace_bytes(w.B, L, w.H, w.dk, w.dv, w.chunk), 16), dtype=torch.uint8,
                        device=dev)
 
     def rank():
-        kda.prefill(*seg, S0=None, chunk=w.chunk, o=o_r, S_T=N1, want_conv=False, workspace=ws_r, A=A)
-        kda.prefill(*seg, S0=eye, chunk=w.chunk, o=o_r, S_T=P1, want_conv=False, workspace=ws_r, A=A)
+        kda.cp_fragments(*seg, chunk=w.chunk, N=N1, P=P1, workspace=ws_r, o=o_r, A=A)
         kda.cp_compose(NR, PR, S0=inp["S0"], B=w.B, S_start=Sst, want_state=False)
-        kda.prefill(*seg, S0=Sst[:w.B], chunk=w.chunk, o=o_r, S_T=N1, want_conv=False, workspace=ws_r, A=A)
+        kda.cp_finish(ws_r, *seg, Sst[:w.B], chunk=w.chunk, o=o_r, S_T=N1, want_conv=False, A=A)
 
     rank()
     torch.cuda.synchronize()
@@ -395,8 +395,8 @@ def time_context_parallel(torch, kda, w, inp, R, A, steps):
             "config": f"kda_prefill_cp of the {w.name} workload in {R} segments of {L} tokens on one GPU: "
                       "three prefill passes over all segments and the composition",
             "rank_share_ms": rms,
-            "rank_share": f"one segment of B{w.B} T{L} H{w.H} from S = 0 and from S = I, kda_cp_compose of "
-                          f"{R} fragments, the segment again; the all-gather of the fragments "
+            "rank_share": f"kda_cp_fragments of one segment of B{w.B} T{L} H{w.H} (N from S = 0, P from S = I), "
+                          f"kda_cp_compose of {R} fragments, kda_cp_finish; the all-gather of the fragments "
                           f"({2 * BH * w.dk * w.dv * 4} bytes per rank) needs {R} GPUs and is not timed",
             "workspace_bytes": nbytes}
 

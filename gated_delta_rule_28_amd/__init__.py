@@ -12,6 +12,8 @@ works, but every call raises (there is no fallback implementation).
     qn, kn, vn, G = prep(q, k, v, conv_w, g, conv_in=None, chunk=64)
     o, S_T, conv_out = prefill_cp(q, k, v, conv_w, g, beta, gate, segments=R, ...)  # context-parallel
     S_start, S_T = cp_compose(N, P, S0=None, B=1)   # the composition step alone
+    ws, N, P = cp_fragments(q, k, v, conv_w, g, beta, gate, conv_in=None)   # one rank's share, part 1
+    o, S_T, conv_out = cp_finish(ws, q, k, v, conv_w, g, beta, gate, S_start, conv_in=None)  # part 2
     grads = prefill_backward(q, k, v, conv_w, g, beta, gate, grad_o, S0=None, conv_in=None, grad_S_T=None)
     release()   # destroy the streams the library keeps between calls (kda_release)
 
@@ -28,7 +30,7 @@ __all__ = ["prefill", "decode_step", "decode_multi", "prep", "workspace_bytes", 
            "KDA_F32", "KDA_BF16", "KDA_DECAY_DIRECT", "KDA_DECAY_K3", "PrefillArgs", "DecodeArgs",
            "PrepArgs", "DecodeMultiArgs", "MAX_DECODE_TOKENS", "prefill_cp", "cp_compose",
            "cp_workspace_bytes", "CpComposeArgs", "PrefillCpArgs", "prefill_backward", "PrefillBackwardArgs",
-           "backward_workspace_bytes", "release"]
+           "backward_workspace_bytes", "release", "cp_fragments", "cp_finish", "cp_rank_workspace_bytes"]
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 library_path = os.path.join(_HERE, "libkda.so")
@@ -37,7 +39,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
-ABI_VERSION = 6
+ABI_VERSION = 7
 MAX_DECODE_TOKENS = 16
 NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
@@ -134,6 +136,12 @@ def lib():
         L.kda_prefill_cp.restype = ctypes.c_int
         L.kda_prefill_cp_workspace_bytes.argtypes = [ctypes.POINTER(PrefillCpArgs)]
         L.kda_prefill_cp_workspace_bytes.restype = ctypes.c_size_t
+        L.kda_cp_fragments.argtypes = [ctypes.POINTER(PrefillArgs), _P, _P, _P]
+        L.kda_cp_fragments.restype = ctypes.c_int
+        L.kda_cp_finish.argtypes = [ctypes.POINTER(PrefillArgs), _P]
+        L.kda_cp_finish.restype = ctypes.c_int
+        L.kda_cp_rank_workspace_bytes.argtypes = [ctypes.POINTER(PrefillArgs)]
+        L.kda_cp_rank_workspace_bytes.restype = ctypes.c_size_t
         L.kda_prefill_backward.argtypes = [ctypes.POINTER(PrefillBackwardArgs), _P]
         L.kda_prefill_backward.restype = ctypes.c_int
         L.kda_prefill_backward_workspace_bytes.argtypes = [ctypes.POINTER(PrefillBackwardArgs)]
@@ -346,6 +354,66 @@ def cp_compose(N, P, S0=None, B=1, S_start=None, S_T=None, want_state=True):
     a = CpComposeArgs(B, BR // B, H, d, _ptr(N), _ptr(P), _ptr(S0), _ptr(S_start), _ptr(S_T))
     _check("kda_cp_compose", lib().kda_cp_compose(ctypes.byref(a), _stream(N.device)))
     return S_start, S_T
+
+
+def cp_rank_workspace_bytes(B, T, H, dk, dv, chunk=64, in_dtype=KDA_BF16, out_dtype=KDA_F32):
+    """kda_cp_rank_workspace_bytes for these sizes (0: invalid)."""
+    a = PrefillArgs(B, T, H, dk, dv, chunk, in_dtype, out_dtype)
+    return int(lib().kda_cp_rank_workspace_bytes(ctypes.byref(a)))
+
+
+def _rank_args(q, k, v, conv_w, g, beta, gate, S0, conv_in, chunk, o, S_T, conv_out, workspace, A):
+    B, T, H, dk = q.shape
+    a = PrefillArgs(B, T, H, dk, v.shape[-1], chunk, _dt(q), _dt(o), _ptr(q), _ptr(k), _ptr(v),
+                    _ptr(conv_w), _ptr(g), _ptr(beta), _ptr(gate), _ptr(S0), _ptr(conv_in),
+                    _ptr(o), _ptr(S_T), _ptr(conv_out), _ptr(workspace),
+                    workspace.numel() * workspace.element_size(), *_decay(A))
+    return a
+
+
+def cp_fragments(q, k, v, conv_w, g, beta, gate, conv_in=None, chunk=64, N=None, P=None, workspace=None,
+                 o=None, out_dtype=None, A=None):
+    """One rank's segment, part 1 (kda_cp_fragments): its final states from
+    S = 0 (N) and from S = I (P), fp32 [B, H, dk, dv].  conv_in: the three raw
+    tokens before the segment.  Returns (workspace, N, P); pass the workspace
+    unchanged to cp_finish.  o (the [B, T, H, dv] output buffer cp_finish will
+    fill) serves as scratch on sizes without the two-kernel path."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32 if out_dtype is None else out_dtype, device=dev)
+    if workspace is None:
+        nbytes = cp_rank_workspace_bytes(B, T, H, dk, dv, chunk, _dt(q), _dt(o))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    if N is None:
+        N = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if P is None:
+        P = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    a = _rank_args(q, k, v, conv_w, g, beta, gate, None, conv_in, chunk, o, None, None, workspace, A)
+    _check("kda_cp_fragments", lib().kda_cp_fragments(ctypes.byref(a), _ptr(N), _ptr(P), _stream(dev)))
+    return workspace, N, P
+
+
+def cp_finish(workspace, q, k, v, conv_w, g, beta, gate, S_start, conv_in=None, chunk=64, o=None,
+              S_T=None, conv_out=None, want_state=True, want_conv=True, out_dtype=None, A=None):
+    """One rank's segment, part 2 (kda_cp_finish): the segment from its
+    entering state S_start with the workspace of cp_fragments and the same
+    inputs.  Returns (o, S_T, conv_out) as prefill."""
+    torch = _torch()
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    dev = q.device
+    if o is None:
+        o = torch.empty((B, T, H, dv), dtype=torch.float32 if out_dtype is None else out_dtype, device=dev)
+    if S_T is None and want_state:
+        S_T = torch.empty((B, H, dk, dv), dtype=torch.float32, device=dev)
+    if conv_out is None and want_conv:
+        conv_out = torch.empty((B, 3, H * (2 * dk + dv)), dtype=q.dtype, device=dev)
+    a = _rank_args(q, k, v, conv_w, g, beta, gate, S_start, conv_in, chunk, o, S_T, conv_out, workspace, A)
+    _check("kda_cp_finish", lib().kda_cp_finish(ctypes.byref(a), _stream(dev)))
+    return o, S_T, conv_out
 
 
 def backward_workspace_bytes(B, T, H, dk, dv, in_dtype=KDA_BF16):

@@ -249,6 +249,60 @@ int kda_prefill_noalloc(const kda_prefill_args* a, void* stream) {
   return kda::launch_prefill_noalloc(*a, reinterpret_cast<hipStream_t>(stream));
 }
 
+size_t kda_cp_rank_workspace_bytes(const kda_prefill_args* a) {
+  if (a == nullptr) return 0;
+  if (kda::check_common(a->B, a->T, a->H, a->dk, a->dv, a->in_dtype, a->out_dtype) != KDA_OK) return 0;
+  if (a->chunk != 16 && a->chunk != 32 && a->chunk != 64) return 0;
+  const size_t split = kda::cp_rank_split_bytes(*a);
+  if (split > 0) return split;
+  // other sizes: three single-kernel prefills; the workspace holds the identity
+  return kda::round256((size_t)a->B * a->H * a->dk * a->dv * sizeof(float));
+}
+
+int kda_cp_fragments(const kda_prefill_args* a, float* N, float* P, void* stream) {
+  kda::g_err[0] = '\0';
+  int rc = kda::check_prefill(a);
+  if (rc != KDA_OK) return rc;
+  REQUIRE_PTR(N); REQUIRE_PTR(P); REQUIRE_A16(N); REQUIRE_A16(P);
+  REQUIRE_PTR(a->workspace); REQUIRE_A16(a->workspace);
+  const size_t need = kda_cp_rank_workspace_bytes(a);
+  if (a->workspace_bytes < need) return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", a->workspace_bytes, need);
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const size_t nstate = (size_t)a->B * a->H;
+  if (a->T > 0 && kda::cp_rank_split_bytes(*a) > 0) return kda::launch_cp_fragments_split(*a, N, P, s);
+  // T = 0 or sizes without the two-kernel path: plain prefills from S = 0 and
+  // S = I (o serves as scratch; the finishing call overwrites it)
+  float* eye = static_cast<float*>(a->workspace);
+  rc = kda::launch_cp_identity(eye, nstate, a->dk, s);
+  if (rc != KDA_OK) return rc;
+  kda_prefill_args z = *a;
+  z.workspace = nullptr;
+  z.workspace_bytes = 0;
+  z.conv_out = nullptr;
+  z.S0 = nullptr;
+  z.S_T = N;
+  rc = kda_prefill(&z, stream);
+  if (rc != KDA_OK) return rc;
+  z.S0 = eye;
+  z.S_T = P;
+  return kda_prefill(&z, stream);
+}
+
+int kda_cp_finish(const kda_prefill_args* a, void* stream) {
+  kda::g_err[0] = '\0';
+  const int rc = kda::check_prefill(a);
+  if (rc != KDA_OK) return rc;
+  REQUIRE_PTR(a->workspace); REQUIRE_A16(a->workspace);
+  const size_t need = kda_cp_rank_workspace_bytes(a);
+  if (a->workspace_bytes < need) return fail(KDA_E_WORKSPACE, "workspace %zu bytes < %zu", a->workspace_bytes, need);
+  if (a->T > 0 && kda::cp_rank_split_bytes(*a) > 0)
+    return kda::launch_cp_finish_split(*a, reinterpret_cast<hipStream_t>(stream));
+  kda_prefill_args z = *a;
+  z.workspace = nullptr;
+  z.workspace_bytes = 0;
+  return kda_prefill(&z, stream);
+}
+
 int kda_cp_compose(const kda_cp_compose_args* a, void* stream) {
   kda::g_err[0] = '\0';
   REQUIRE_PTR(a);

@@ -23,6 +23,14 @@ int launch_prefill_split(const kda_prefill_args& a, hipStream_t s);
 // path's workspace is a file-scope device array (kda_prefill_split.hip).
 int launch_prefill_noalloc(const kda_prefill_args& a, hipStream_t s);
 
+// One rank's share of context-parallel prefill on the two-kernel path: the
+// workspace that keeps every chunk block between the two calls (0 when the
+// sizes have no two-kernel path), the fragments N (from S = 0) and P (from
+// S = I), and the finishing pass from the entering state a.S0.
+size_t cp_rank_split_bytes(const kda_prefill_args& a);
+int launch_cp_fragments_split(const kda_prefill_args& a, float* N, float* P, hipStream_t s);
+int launch_cp_finish_split(const kda_prefill_args& a, hipStream_t s);
+
 // Context-parallel helpers: the prefix composition; the raw conv history of
 // `nblk` blocks per sequence (the three raw tokens before token (first + j) * L
 // of block j, from conv_in before token 0) into dst [B * nblk, 3, Cch]; the

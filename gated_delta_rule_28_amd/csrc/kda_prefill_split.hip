@@ -105,6 +105,10 @@ struct SplitParams {
   void* conv_out;         // raw conv history after the last token, or null
   unsigned char* ws;      // n_chunks * B * H chunk blocks
   const float* A;         // [H, dk]: g and beta are K3's logits (see k3_decay); null: given directly
+  // A second copy of the recurrence over the same chunk blocks (inter-chunk
+  // grid 2 * B * H, copy 1 in blocks B*H ..): it starts from the identity and
+  // writes only its final state to S_out2.  o may be null (no outputs).
+  float* S_out2;
 };
 
 // DPP move inside rows of 16 lanes; lanes with no source or outside the bank
@@ -694,10 +698,15 @@ __device__ __forceinline__ void stage_dma(const unsigned char* chunk, int w, int
   }
 }
 
-template <bool OUT_BF16>
+// WANT_O = false: no outputs (O is not formed, o not written), the final state
+// only.
+template <bool OUT_BF16, bool WANT_O>
 __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   const int H = p.H, T = p.T;
-  const int bh = blockIdx.x;
+  const int nbh = p.B * H;
+  const bool copy2 = (int)blockIdx.x >= nbh;  // the copy from the identity (see SplitParams)
+  const int bh = copy2 ? blockIdx.x - nbh : blockIdx.x;
+  float* const S_out = copy2 ? p.S_out2 : p.S_out;
   const int b = bh / H, h = bh - b * H;
   const int tid = threadIdx.x;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -716,7 +725,14 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
     for (int ct = 0; ct < 2; ++ct) S[m][ct] = f4{0.f, 0.f, 0.f, 0.f};
   if (math) {
     if (tid < kD) g_vw[tid] = *reinterpret_cast<const float4*>(p.conv_w + ((size_t)2 * H * kD + (size_t)h * kD + tid) * 4);
-    if (p.S_in != nullptr) {
+    if (copy2) {
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) S[m][ct][e] = perm_row(16 * m + 4 * g + e) == col0 + 16 * ct + i ? 1.f : 0.f;
+    } else if (p.S_in != nullptr) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -795,7 +811,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 #pragma unroll
           for (int ct = 0; ct < 2; ++ct) {
             X[rt][ct] = mma_f16(vh[rt], ident_frag(g, i, ct), f4{0.f, 0.f, 0.f, 0.f});
-            O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (WANT_O) O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
           }
         if (j + 1 < nc) load_v(j + 1, rv[1 - P]);
         // X = V + (-(K e^G)) S and (Q e^G) S, one 32-row step of S at a time:
@@ -812,11 +828,12 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 #pragma unroll
           for (int rt = 0; rt < 4; ++rt) {
             const half8 wf = *reinterpret_cast<const half8*>(sb + WS_KG + ((rt * 4 + kp) * 64 + lane) * 16);
-            const half8 qf = *reinterpret_cast<const half8*>(sb + WS_QG + ((rt * 4 + kp) * 64 + lane) * 16);
 #pragma unroll
-            for (int ct = 0; ct < 2; ++ct) {
-              X[rt][ct] = mma_f16(wf, Sb[ct], X[rt][ct]);
-              O[rt][ct] = mma_f16(qf, Sb[ct], O[rt][ct]);
+            for (int ct = 0; ct < 2; ++ct) X[rt][ct] = mma_f16(wf, Sb[ct], X[rt][ct]);
+            if constexpr (WANT_O) {
+              const half8 qf = *reinterpret_cast<const half8*>(sb + WS_QG + ((rt * 4 + kp) * 64 + lane) * 16);
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) O[rt][ct] = mma_f16(qf, Sb[ct], O[rt][ct]);
             }
           }
         }
@@ -865,7 +882,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           }
         // O += P U, then O to LDS for the epilogue waves
 #pragma unroll
-        for (int rt = 0; rt < 4; ++rt) {
+        for (int rt = 0; rt < 4 && WANT_O; ++rt) {
 #pragma unroll
           for (int kp = 0; kp < 2; ++kp)
             if (2 * kp <= rt) {
@@ -935,7 +952,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         for (int s2 = 0; s2 < 2; ++s2) gt[tt][s2] = ld_nt(gr + 64 * s2);
       }
     };
-    if (nc > 0) load_gate(0);
+    if (WANT_O && nc > 0) load_gate(0);
     // one chunk; P = j & 1 picks the staging buffer the next chunk goes to
     auto step = [&](auto parity, int j) {
       constexpr int P = decltype(parity)::value;
@@ -945,7 +962,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       if (j + 1 < nc) stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
       // ---- epilogue of chunk j-1 ----------------------------------------------------
       float ov[2][2][8];
-      if (j >= 1) {
+      if (WANT_O && j >= 1) {
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -960,7 +977,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       // gate loaded a chunk ago and the previous chunk's stores: one wait here,
       // before this chunk's stores, so that those are never waited on.
       __builtin_amdgcn_s_waitcnt(0);
-      if (j >= 1) {
+      if (WANT_O && j >= 1) {
         const int c0 = (p.c_begin + j - 1) * kC;
         const int nv = min(kC, T - c0);
 #pragma unroll
@@ -987,7 +1004,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           }
         }
       }
-      if (j >= 1 && j < nc) load_gate(j);
+      if (WANT_O && j >= 1 && j < nc) load_gate(j);
     };
     // both roles skip the loop (and its barriers) in a launch without chunks
     if (nc > 0) {
@@ -999,16 +1016,16 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   }
 
   // ---- state and conv history out -------------------------------------------------
-  if (math && p.S_out != nullptr) {
+  if (math && S_out != nullptr) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          p.S_out[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i] = S[m][ct][e];
+          S_out[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i] = S[m][ct][e];
   }
-  if (p.conv_out != nullptr) {
+  if (!copy2 && p.conv_out != nullptr) {
     const size_t cch = (size_t)H * kNCh;
     for (int cl = tid; cl < kNCh; cl += 512) {
       const void* src = cl < kD ? p.q : cl < 2 * kD ? p.k : p.v;
@@ -1242,7 +1259,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
       if (e == hipSuccess) e = hipStreamWaitEvent(sb, pp->a_done[sl & 1], 0);
     }
     if (e == hipSuccess) {
-      hipLaunchKernelGGL((inter_chunk_kernel<OB>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, sb, p);
+      hipLaunchKernelGGL((inter_chunk_kernel<OB, true>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, sb, p);
       e = hipGetLastError();
       what = "inter-chunk launch";
     }
@@ -1296,6 +1313,82 @@ int launch_split(const kda_prefill_args& a, hipStream_t s, bool pipe_ok) {
 }
 
 int launch_prefill_split(const kda_prefill_args& a, hipStream_t s) { return launch_split(a, s, true); }
+
+// ---- one rank's share of context-parallel prefill in two calls ------------------
+// Fragments: the intra-chunk kernel over every chunk once (all blocks kept in
+// the workspace), then two copies of the recurrence side by side, from S = 0
+// (final state N) and from S = I (final state P), without outputs.  Finish:
+// the recurrence again over the kept blocks from the entering state S0, with
+// outputs.  The inter-chunk kernel reads raw v and gate itself, so the kept
+// blocks are all that carries over between the calls.
+size_t cp_rank_split_bytes(const kda_prefill_args& a) {
+  if (!prefill_split_eligible(a)) return 0;
+  return (size_t)((a.T + kC - 1) / kC) * per_chunk_bytes(a);
+}
+
+namespace {
+SplitParams rank_params(const kda_prefill_args& a) {
+  SplitParams p{};
+  p.B = a.B; p.T = a.T; p.H = a.H;
+  p.c_begin = 0;
+  p.n_chunks = (a.T + kC - 1) / kC;
+  p.q = a.q; p.k = a.k; p.v = a.v; p.conv_w = a.conv_w; p.g = a.g; p.beta = a.beta; p.gate = a.gate;
+  p.A = a.decay_form == KDA_DECAY_K3 ? a.A : nullptr;
+  p.conv_in = a.conv_in;
+  p.ws = static_cast<unsigned char*>(a.workspace);
+  return p;
+}
+
+template <bool K3>
+int launch_intra_all(const SplitParams& p, hipStream_t s) {
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<K3>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, ALds::BYTES);
+  if (e == hipSuccess) {
+    hipLaunchKernelGGL(intra_chunk_kernel<K3>, dim3((unsigned)((size_t)p.n_chunks * p.B * p.H)), dim3(256),
+                       ALds::BYTES, s, p);
+    e = hipGetLastError();
+  }
+  if (e != hipSuccess) {
+    set_error("context-parallel fragments: intra-chunk launch failed: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  return KDA_OK;
+}
+}  // namespace
+
+int launch_cp_fragments_split(const kda_prefill_args& a, float* N, float* P, hipStream_t s) {
+  SplitParams p = rank_params(a);
+  p.S_in = nullptr;
+  p.S_out = N;
+  p.S_out2 = P;
+  const int rc = a.decay_form == KDA_DECAY_K3 ? launch_intra_all<true>(p, s) : launch_intra_all<false>(p, s);
+  if (rc != KDA_OK) return rc;
+  hipLaunchKernelGGL((inter_chunk_kernel<false, false>), dim3((unsigned)(2 * a.B * a.H)), dim3(512), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("context-parallel fragments: inter-chunk launch failed: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  return KDA_OK;
+}
+
+int launch_cp_finish_split(const kda_prefill_args& a, hipStream_t s) {
+  SplitParams p = rank_params(a);
+  p.S_in = a.S0;
+  p.S_out = a.S_T;
+  p.o = a.o;
+  p.conv_out = a.conv_out;
+  if (a.out_dtype == KDA_BF16)
+    hipLaunchKernelGGL((inter_chunk_kernel<true, true>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((inter_chunk_kernel<false, true>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, s, p);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) {
+    set_error("context-parallel finish: inter-chunk launch failed: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  return KDA_OK;
+}
 
 // ---- allocation-free prefill (kda_prefill_noalloc) ---------------------------------
 // For callers that cannot allocate, the two-kernel path's workspace is this

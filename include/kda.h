@@ -69,7 +69,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 6
+#define KDA_ABI_VERSION 7
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -320,6 +320,40 @@ int kda_prefill_cp(const kda_prefill_cp_args* args, void* stream);
 /* Workspace kda_prefill_cp needs for these sizes (fields B, T, H, dk, dv,
  * chunk, in_dtype, out_dtype and segments are read); 0 if they are invalid. */
 size_t kda_prefill_cp_workspace_bytes(const kda_prefill_cp_args* args);
+
+/*
+ * One rank's share of context-parallel prefill, in two calls around the
+ * exchange of fragments (the long-context training row of "Gemma 4 31B vs
+ * Kimi K3", component table: ranks exchange only fixed-size state fragments).
+ * `args` describes the rank's own segment as a kda_prefill call: its tokens,
+ * conv_in = the three raw tokens before the segment (the previous rank's last
+ * ones; NULL = zeros at the sequence start), and a workspace of at least
+ * kda_cp_rank_workspace_bytes bytes (16-byte aligned, required) that the
+ * caller leaves untouched between the two calls.
+ *   kda_cp_fragments(args, N, P): N = the segment's final state from S = 0,
+ *     P = from S = I ([B, H, dk, dv] fp32 each, caller-owned, 16-byte
+ *     aligned); args->S0, S_T and conv_out are ignored.  With bf16 inputs,
+ *     chunk 64 and dk = dv = 128 the intra-chunk work of every chunk runs once
+ *     into the workspace and the two recurrences run side by side without
+ *     forming outputs; other sizes run two plain prefills (args->o is then
+ *     used as scratch).
+ *   (exchange the fragments; kda_cp_compose gives the entering state)
+ *   kda_cp_finish(args): the segment from the entering state args->S0 with
+ *     the same inputs and workspace: o, S_T and conv_out as kda_prefill.  On
+ *     the two-kernel path it reruns only the recurrence over the kept chunk
+ *     blocks.
+ * Calls are asynchronous on `stream`; both must be ordered on one stream (or
+ * synchronised) with the workspace untouched between them.  Errors as
+ * kda_prefill; KDA_E_NULL (N, P or the workspace NULL), KDA_E_WORKSPACE.
+ */
+int kda_cp_fragments(const kda_prefill_args* args, float* N, float* P, void* stream);
+int kda_cp_finish(const kda_prefill_args* args, void* stream);
+
+/* Workspace of kda_cp_fragments / kda_cp_finish for these sizes: with the
+ * two-kernel path (bf16, chunk 64, dk = dv = 128) 64 KiB per (b, h, chunk of
+ * 64 tokens), B*H*ceil(T/64)*65536 bytes; otherwise B*H*dk*dv*4 bytes rounded
+ * up to 256.  0 when the sizes are invalid.  Pointers are not read. */
+size_t kda_cp_rank_workspace_bytes(const kda_prefill_args* args);
 
 /*
  * kda_prefill_backward: gradients of the prefill for training (the long

@@ -38,7 +38,7 @@ def test_header_declares_the_abi():
     for must in ("kda_prefill", "kda_decode_step", "kda_decode_multi", "kda_prefill_workspace_bytes", "kda_prep",
                  "kda_status_string", "kda_last_error", "kda_abi_version", "kda_cp_compose", "kda_prefill_cp",
                  "kda_prefill_cp_workspace_bytes", "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
-                 "kda_release"):
+                 "kda_release", "kda_cp_fragments", "kda_cp_finish", "kda_cp_rank_workspace_bytes"):
         assert must in names
 
 
@@ -266,7 +266,7 @@ def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 6
+    assert L.kda_abi_version() == 7
 
 
 def test_release_with_nothing_kept(kda):
@@ -311,3 +311,25 @@ def test_peaks_library_exports_its_header():
     assert L.kda_peak_stream(1 << 20, 65536, 2, None) == -2
     assert L.kda_peak_mfma(None, 1, 1, 4, None) == -1
     assert L.kda_peak_mfma(1 << 20, 1, 1, 5, None) == -2
+
+
+def test_cp_rank_workspace_and_validation(kda):
+    """kda_cp_rank_workspace_bytes: every 64-token chunk block (64 KiB per head)
+    on the two-kernel path, one identity state per head otherwise; the two
+    rank-share calls reject a missing fragment pointer or a short workspace
+    before any HIP call."""
+    L = kda.lib()
+    a = kda.PrefillArgs(2, 130, 3, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32)
+    assert L.kda_cp_rank_workspace_bytes(ctypes.byref(a)) == 2 * 3 * 3 * 64 * 1024
+    f = kda.PrefillArgs(2, 130, 3, 32, 32, 32, kda.KDA_F32, kda.KDA_F32)
+    assert L.kda_cp_rank_workspace_bytes(ctypes.byref(f)) == (2 * 3 * 32 * 32 * 4 + 255) // 256 * 256
+    bad = kda.PrefillArgs(2, 130, 3, 128, 64, 64, kda.KDA_BF16, kda.KDA_F32)
+    assert L.kda_cp_rank_workspace_bytes(ctypes.byref(bad)) == 0
+    fake = 1 << 20
+    r = kda.PrefillArgs(1, 128, 2, 128, 128, 64, kda.KDA_BF16, kda.KDA_F32, fake, fake, fake, fake, fake,
+                        fake, fake, None, None, fake, None, None, fake, 16, kda.KDA_DECAY_DIRECT, None)
+    assert L.kda_cp_fragments(ctypes.byref(r), None, fake, None) == -1
+    assert L.kda_cp_fragments(ctypes.byref(r), fake, fake, None) == -6
+    assert L.kda_cp_finish(ctypes.byref(r), None) == -6
+    r.workspace = None
+    assert L.kda_cp_finish(ctypes.byref(r), None) == -1

@@ -126,3 +126,63 @@ def test_prefill_cp_k3width_sixteen_segments(oracle_mod):
     o_got = o[0][:, heads].float().cpu().numpy().transpose(1, 0, 2)
     assert_rms_close(o_got, r["o"], TOL_BF16, "k3width 16 segments o")
     assert_rms_close(S_T[0, heads].cpu().numpy(), r["S_T"], TOL_BF16, "k3width 16 segments S_T")
+
+
+RANK_CASES = [
+    # B, T, H, d, dtype, chunk, K3 logits
+    (1, 4096 + 17, 2, 128, "bf16", 64, False),   # two-kernel path: kept chunk blocks, ragged last chunk
+    (2, 700, 3, 128, "bf16", 64, True),          # two-kernel path, K3's logits
+    (2, 96, 2, 32, "f32", 16, False),            # other sizes: plain prefills
+]
+
+
+@pytest.mark.parametrize("B,T,H,d,dtype,chunk,k3", RANK_CASES)
+def test_cp_rank_share_matches_oracle(oracle_mod, B, T, H, d, dtype, chunk, k3):
+    """One rank's share in two calls: kda_cp_fragments gives the segment's
+    final states from S = 0 and from S = I (against the oracle run from those
+    states), kda_cp_finish reruns it from an entering state with the kept
+    workspace (o, S_T, conv_out against the oracle's prefill from that state).
+    conv_in stands for the three raw tokens before the rank's segment."""
+    torch, kda = need_gpu()
+    w = Workload("rk", B, T, H, d, d, chunk, dtype, s0_sigma=0.05, conv_hist="normal", seed=90 + d + T)
+    inp = syn.prefill_inputs_np(w)
+    if k3:
+        inp = syn.with_k3_logits(inp, w)
+    dev = to_dev(inp, dtype)
+    print(f"  rank share B{B} T{T} H{H} d{d} {dtype} chunk {chunk} k3={k3}", flush=True)
+    args = [dev[x] for x in ("q", "k", "v", "conv_w", "g", "beta", "gate")]
+    ws, N, P = kda.cp_fragments(*args, conv_in=dev["conv_in"], chunk=chunk, A=dev.get("A"))
+    o, S_T, conv_out = kda.cp_finish(ws, *args, dev["S0"], conv_in=dev["conv_in"], chunk=chunk, A=dev.get("A"))
+    torch.cuda.synchronize()
+    tol = tol_for(dtype)
+    zero = dict(inp, S0=np.zeros((B, H, d, d), dtype=np.float32))
+    eye = dict(inp, S0=np.broadcast_to(np.eye(d, dtype=np.float32), (B, H, d, d)).copy())
+    rN = oracle_mod.prefill(zero, want_o=False)
+    rP = oracle_mod.prefill(eye, want_o=False)
+    assert_rms_close(N.cpu().numpy().reshape(B * H, d, d), rN["S_T"], tol, "fragment N (from S = 0)")
+    assert_rms_close(P.cpu().numpy().reshape(B * H, d, d), rP["S_T"], tol, "fragment P (from S = I)")
+    r = oracle_mod.prefill(inp)
+    assert_rms_close(gather_heads(o, r["heads"], H), r["o"], tol, "finish o")
+    assert_rms_close(S_T.cpu().numpy().reshape(B * H, d, d), r["S_T"], tol, "finish S_T")
+    conv_np = syn.torch_to_np(conv_out)
+    want = syn.bf16_bits_from_f64(r["conv_out"]) if dtype == "bf16" else r["conv_out"].astype(np.float32)
+    for i, p in enumerate(r["heads"]):
+        b, h = divmod(int(p), H)
+        assert np.array_equal(conv_np[b][:, oracle_mod._head_channels(H, d, d, h)], want[i])
+
+
+def test_cp_rank_share_finish_twice(oracle_mod):
+    """The kept workspace serves several finishing calls (here from two
+    entering states): each equals the oracle's prefill from its state."""
+    torch, kda = need_gpu()
+    w = Workload("rk2", 1, 1000, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=97)
+    inp = syn.prefill_inputs_np(w)
+    dev = to_dev(inp, "bf16")
+    args = [dev[x] for x in ("q", "k", "v", "conv_w", "g", "beta", "gate")]
+    ws, N, P = kda.cp_fragments(*args, conv_in=dev["conv_in"])
+    for s, S_in in enumerate((dev["S0"], torch.zeros_like(dev["S0"]))):
+        o, S_T, _ = kda.cp_finish(ws, *args, S_in, conv_in=dev["conv_in"], want_conv=False)
+        torch.cuda.synchronize()
+        r = oracle_mod.prefill(dict(inp, S0=S_in.cpu().numpy()))
+        assert_rms_close(gather_heads(o, r["heads"], 2), r["o"], TOL_BF16, f"finish {s} o")
+        assert_rms_close(S_T.cpu().numpy().reshape(2, 128, 128), r["S_T"], TOL_BF16, f"finish {s} S_T")
