@@ -161,6 +161,17 @@ __device__ __forceinline__ float group_sum(float x) {
   return x;
 }
 
+// Maximum over the 64 lanes of a wave (every lane gets it); all lanes active.
+__device__ __forceinline__ float wave_max(float x) {
+  x = fmaxf(x, dpp_mov<0xB1>(x));
+  x = fmaxf(x, dpp_mov<0x4E>(x));
+  x = fmaxf(x, dpp_mov<0x141>(x));
+  x = fmaxf(x, dpp_mov<0x140>(x));
+  x = fmaxf(x, __shfl_xor(x, 16, 64));
+  x = fmaxf(x, __shfl_xor(x, 32, 64));
+  return x;
+}
+
 // Workgroup barrier that waits only for this wave's LDS operations, not for its
 // outstanding global loads (which __syncthreads' release fence would drain):
 // loads issued for later stages stay in flight across it.  The memory clobber

@@ -662,6 +662,26 @@ constexpr int kOBlk = 4 * kOGrp;
 __shared__ __attribute__((aligned(16))) unsigned char g_O[16 * kOBlk];
 // conv taps of the head's v channels
 __shared__ float4 g_vw[kD];
+// scale of each math wave's columns of the O in g_O (see kRangeLimit)
+__shared__ float g_Osig[4];
+
+// Range of the fp16 operands.  Each math wave keeps its columns of V, S, X, U
+// and O divided by a power of two sigma (1 unless the values demand more):
+// before a chunk, |V| <= sum_j |w_j| max|raw v| + 0.3 (SiLU's negative lobe) is
+// bounded from the raw bf16 values, and sigma grows so that |V| / sigma and
+// |S| / sigma stay below kRangeLimit, which leaves fp16 (max 65504) a factor
+// 64 for X, U and O.  The recurrence is linear in (V, S), so the scaled state
+// follows the same update; RMSNorm is applied to O = sigma * O~ in fp32, and
+// S_T is written unscaled.  Sigma never shrinks within a launch.
+constexpr float kRangeLimit = 1024.0f;
+
+// Smallest power of two p with x / p <= kRangeLimit, at least `cur`.
+__device__ __forceinline__ float grow_scale(float cur, float x) {
+  if (!(x > kRangeLimit * cur)) return cur;
+  int e;
+  (void)__builtin_frexpf(x / kRangeLimit, &e);  // x / limit < 2^e
+  return __builtin_ldexpf(1.0f, e);
+}
 static_assert(2 * WS_STAGE + 16 * kOBlk + kD * 16 <= 160 * 1024, "inter-chunk LDS exceeds 160 KiB");
 
 // B operand of the 16x16x32 instruction that moves columns 16ct .. 16ct + 15
@@ -723,8 +743,21 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   for (int m = 0; m < 8; ++m)
 #pragma unroll
     for (int ct = 0; ct < 2; ++ct) S[m][ct] = f4{0.f, 0.f, 0.f, 0.f};
+  // math waves: the scale of this wave's columns (kRangeLimit) and the largest
+  // sum of |taps| over its v channels
+  float sig = 1.0f, tapsum = 0.0f;
   if (math) {
     if (tid < kD) g_vw[tid] = *reinterpret_cast<const float4*>(p.conv_w + ((size_t)2 * H * kD + (size_t)h * kD + tid) * 4);
+    {
+      float ts = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float4 t4 =
+            *reinterpret_cast<const float4*>(p.conv_w + ((size_t)2 * H * kD + (size_t)h * kD + col0 + 8 * g + e) * 4);
+        ts = fmaxf(ts, fabsf(t4.x) + fabsf(t4.y) + fabsf(t4.z) + fabsf(t4.w));
+      }
+      tapsum = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_max(ts))));
+    }
     if (copy2) {
 #pragma unroll
       for (int m = 0; m < 8; ++m)
@@ -740,6 +773,22 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             S[m][ct][e] = p.S_in[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i];
+      float sm = 0.0f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m)
+#pragma unroll
+        for (int ct = 0; ct < 2; ++ct)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) sm = fmaxf(sm, fabsf(S[m][ct][e]));
+      sm = __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, wave_max(sm))));
+      sig = grow_scale(1.0f, sm);
+      if (sig != 1.0f) {
+        const float r = 1.0f / sig;
+#pragma unroll
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+          for (int ct = 0; ct < 2; ++ct) S[m][ct] *= r;
+      }
     }
   } else if (nc > 0) {
     stage_dma<0>(wsh, w, lane);
@@ -795,17 +844,50 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         // 16-lane row, the previous tile's raw values as the halo: for tile 0
         // the previous chunk's tile 3), moved into the C layout of X by a
         // product with the identity
-        half8 vh[4];
+        // the chunk's bound on |V| from its raw values (and the halo's): the
+        // scale grows first if V or the state would leave fp16's range
+        {
+          // |bf16| as 16-bit integers (sign cleared), two per dword: packed maxima
+          typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+          us2 mb = us2{0, 0};
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float4 wv = g_vw[col0 + 8 * g + e];
+          for (int rt = 0; rt < 5; ++rt) {
+            const uint4 u = rt < 4 ? rv[P][rt] : rv[1 - P][3];
+            mb = __builtin_elementwise_max(mb, __builtin_bit_cast(us2, u.x & 0x7fff7fffu));
+            mb = __builtin_elementwise_max(mb, __builtin_bit_cast(us2, u.y & 0x7fff7fffu));
+            mb = __builtin_elementwise_max(mb, __builtin_bit_cast(us2, u.z & 0x7fff7fffu));
+            mb = __builtin_elementwise_max(mb, __builtin_bit_cast(us2, u.w & 0x7fff7fffu));
+          }
+          const uint32_t m1 = mb[0] > mb[1] ? mb[0] : mb[1];
+          const float mv = wave_max(__builtin_bit_cast(float, m1 << 16));
+          const float ns = grow_scale(sig, __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(
+                                                                       __builtin_bit_cast(int, mv))) * tapsum + 0.3f);
+          if (ns != sig) {
+            const float r = sig / ns;
 #pragma unroll
-          for (int rt = 0; rt < 4; ++rt) {
-            const float xc = bf16_at(rv[P][rt], e);
-            const float y = bf16_at(rt == 0 ? rv[1 - P][3] : rv[P][rt - 1], e);
-            vh[rt][e] = (_Float16)siluf_(conv3_dpp(wv.w * xc, xc, y, wv.z, wv.y, wv.x));
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+              for (int ct = 0; ct < 2; ++ct) S[m][ct] *= r;
+            sig = ns;
           }
         }
+        half8 vh[4];
+        auto conv_v = [&](auto scaled) {
+          const float isig = 1.0f / sig;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float4 wv = g_vw[col0 + 8 * g + e];
+#pragma unroll
+            for (int rt = 0; rt < 4; ++rt) {
+              const float xc = bf16_at(rv[P][rt], e);
+              const float y = bf16_at(rt == 0 ? rv[1 - P][3] : rv[P][rt - 1], e);
+              const float a = siluf_(conv3_dpp(wv.w * xc, xc, y, wv.z, wv.y, wv.x));
+              vh[rt][e] = (_Float16)(decltype(scaled)::value ? a * isig : a);
+            }
+          }
+        };
+        if (sig == 1.0f) conv_v(std::false_type{});
+        else conv_v(std::true_type{});
 #pragma unroll
         for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -898,6 +980,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
                                O[rt][1][0], O[rt][1][1], O[rt][1][2], O[rt][1][3]};
           *reinterpret_cast<half8*>(g_O + (rt * 4 + w) * kOBlk + g * kOGrp + i * 16 + (i >> 3) * 16) = to_half8(ox);
         }
+        if (WANT_O && lane == 0) g_Osig[w] = sig;
         // S <- e^{G_C} S + (K e^{G_C - G})^T U
 #pragma unroll
         for (int m = 0; m < 8; ++m) {
@@ -961,8 +1044,11 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       lds_barrier();  // B1
       if (j + 1 < nc) stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
       // ---- epilogue of chunk j-1 ----------------------------------------------------
-      float ov[2][2][8];
+      float ov[2][2][8], osig[2];
       if (WANT_O && j >= 1) {
+        // the scales of the two math waves whose columns this lane normalises
+        osig[0] = g_Osig[q >> 2];
+        osig[1] = g_Osig[2 + (q >> 2)];
 #pragma unroll
         for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
@@ -984,15 +1070,18 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         for (int tt = 0; tt < 2; ++tt) {
           float ss = 0.f;
 #pragma unroll
-          for (int s2 = 0; s2 < 2; ++s2)
+          for (int s2 = 0; s2 < 2; ++s2) {
+            float sp = 0.f;
 #pragma unroll
-            for (int c = 0; c < 8; ++c) ss += ov[tt][s2][c] * ov[tt][s2][c];
+            for (int c = 0; c < 8; ++c) sp += ov[tt][s2][c] * ov[tt][s2][c];
+            ss += sp * osig[s2] * osig[s2];
+          }
           ss = group_sum<8>(ss);
           const float rs = fast_rsq(ss * (1.0f / kD) + kRmsEps);
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2)
 #pragma unroll
-            for (int c = 0; c < 8; ++c) ov[tt][s2][c] *= rs * sigmoidf_(bf16_at(gt[tt][s2], c));
+            for (int c = 0; c < 8; ++c) ov[tt][s2][c] *= osig[s2] * rs * sigmoidf_(bf16_at(gt[tt][s2], c));
         }
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1023,7 +1112,8 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
         for (int e = 0; e < 4; ++e)
-          S_out[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i] = S[m][ct][e];
+          S_out[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i] =
+              S[m][ct][e] * sig;
   }
   if (!copy2 && p.conv_out != nullptr) {
     const size_t cch = (size_t)H * kNCh;

@@ -47,8 +47,12 @@
  *                     they load g and beta.
  *
  * Preconditions not checked (for cost): g <= 0 and 0 <= beta <= 1 in the
- * direct form; inputs finite; |v~| and the state below 6e4 (fp16 operand
- * range); the summed log-decay of any 16 consecutive tokens of a chunk at
+ * direct form; inputs finite; on the single-kernel path (no workspace, or
+ * sizes without the two-kernel path) |v~| and the state below 6e4 (fp16
+ * operand range) -- the two-kernel path scales each 32-column group of V, the
+ * state and the outputs by a power of two chosen per chunk from the raw v
+ * values and S0, so any finite bf16 v and fp32 S0 stay in range there; the
+ * summed log-decay of any 16 consecutive tokens of a chunk at
  * least -80 per channel (g >= -5 per token suffices, which K3's bounded decay
  * g = -5 sigmoid(.) guarantees: the pages' 16-token tile bound), so that the
  * in-tile decay factors stay finite in fp32.

@@ -391,3 +391,41 @@ def test_prefill_workload_b2_t4096_h32(oracle_mod, path):
     dev = to_dev(inp, "bf16")
     o, S_T, c = _gpu_prefill(kda, dev, w.chunk, workspace=PATHS[path])
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"{path} B2 T4096 H32")
+
+
+def _scale_bf16_bits(bits, factor_log2):
+    """bf16 bit patterns times 2^factor_log2 (exact: only the exponent moves)."""
+    f = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return syn.bf16_bits_from_f64(f * 2.0 ** factor_log2)
+
+
+def test_values_beyond_fp16_range(oracle_mod):
+    """v, S0 and the conv history times 2^15 (|v| up to about 1e5, the state
+    about 1e4): V, S and the recurrence's products would leave fp16's range
+    (65504).  The two-kernel path scales each math wave's columns by a power
+    of two (the state and outputs come back unscaled), so the result stays
+    within the workloads' 2e-2 x RMS of the oracle."""
+    torch, kda = need_gpu()
+    w = Workload("big", 1, 300, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=41)
+    inp = syn.prefill_inputs_np(w)
+    inp["v"] = _scale_bf16_bits(inp["v"], 15)
+    inp["conv_in"] = _scale_bf16_bits(inp["conv_in"], 15)
+    inp["S0"] = (inp["S0"] * 2.0 ** 15).astype(np.float32)
+    dev = to_dev(inp, "bf16")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace="auto")
+    assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="values x 2^15")
+
+
+def test_value_spike_mid_sequence(oracle_mod):
+    """Ordinary values except two chunks of v times 2^16 in the middle of a
+    pipelined 70-chunk sequence: the scale grows at the spike (the state is
+    rescaled in place) and stays for the rest of the launch."""
+    torch, kda = need_gpu()
+    w = Workload("spk", 1, 70 * 64, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=43)
+    inp = syn.prefill_inputs_np(w)
+    inp["v"][:, 40 * 64:42 * 64] = _scale_bf16_bits(inp["v"][:, 40 * 64:42 * 64], 16)
+    dev = to_dev(inp, "bf16")
+    o, S_T, c = _gpu_prefill(kda, dev, 64, workspace="auto")
+    assert torch.isfinite(o).all() and torch.isfinite(S_T).all()
+    _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="spike x 2^16")
