@@ -31,7 +31,7 @@ CSRC = os.path.join(ROOT, "gated_delta_rule_28_amd", "csrc")
 # kernel key -> (substring of the demangled name, source file)
 KERNELS = {
     "intra_chunk_kernel": ("intra_chunk_kernel<false>", "kda_prefill_split.hip"),
-    "inter_chunk_kernel": ("inter_chunk_kernel<false>", "kda_prefill_split.hip"),
+    "inter_chunk_kernel": ("inter_chunk_kernel<false, true>", "kda_prefill_split.hip"),
     "prefill_kernel": ("prefill_kernel<64, 128, 128, true, false, false>", "kda_prefill.hip"),
     "decode_kernel": ("decode_kernel<128, 128, true, false>", "kda_decode.hip"),
     "decode_multi_kernel": ("decode_multi_kernel<128, 128, true, false, 4, false>", "kda_decode.hip"),
