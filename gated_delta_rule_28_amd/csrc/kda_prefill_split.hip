@@ -1140,9 +1140,10 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 // How the chunks of one call are split into launches ("slabs").
 //
 // Pipelined (a sequence of more than kPipeChunks chunks and B*H at most half
-// the compute units): slabs of about kPipeChunks chunks in kPipeBufs workspace
-// buffers.  From 2 * kPipeChunks chunks on, the first slab has half as many
-// chunks, so the inter-chunk kernel (the slower stage) starts sooner.  The inter-chunk kernel (one workgroup per (b, h), the state carried
+// the compute units): slabs of at most kPipeChunks chunks in kPipeBufs
+// workspace buffers.  From 2 * kPipeChunks chunks on, the slabs ramp up from
+// kFirstChunks, each twice as long as the one before, so the inter-chunk kernel
+// (the slower stage) starts soon and later launches are few.  The inter-chunk kernel (one workgroup per (b, h), the state carried
 // between slabs in a buffer) runs on a stream restricted to B*H compute units,
 // the intra-chunk kernel of the next slab on a stream restricted to the others,
 // so the two overlap without competing for compute units.
@@ -1150,20 +1151,26 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 // the cap), else as many chunks per slab as fit next to the state carry, one
 // slab after the other on the caller's stream.
 constexpr int kPipeChunks = 64;
+constexpr int kFirstChunks = 32;
 constexpr int kPipeBufs = 3;  // the intra-chunk kernel runs up to two slabs ahead
 constexpr int kPlanCUs = 256;  // compute units the preferred workspace is planned for
 
 struct SlabPlan {
   int nchunks, per_slab, nslabs, nbuf;
-  int first;  // chunks of slab 0 when it differs from per_slab, else 0
+  int ramp;  // leading slabs of kFirstChunks, 2 kFirstChunks, ... chunks (0: none)
   size_t region_bytes, carry_bytes;
 };
 
 // Chunks [c0, c0 + n) of slab sl.
 void slab_range(const SlabPlan& pl, int sl, int& c0, int& n) {
-  if (pl.first > 0) c0 = sl == 0 ? 0 : pl.first + (sl - 1) * pl.per_slab;
-  else c0 = sl * pl.per_slab;
-  const int len = pl.first > 0 && sl == 0 ? pl.first : pl.per_slab;
+  int len;
+  if (sl < pl.ramp) {
+    c0 = kFirstChunks * ((1 << sl) - 1);
+    len = kFirstChunks << sl;
+  } else {
+    c0 = kFirstChunks * ((1 << pl.ramp) - 1) + (sl - pl.ramp) * pl.per_slab;
+    len = pl.per_slab;
+  }
   n = pl.nchunks - c0 < len ? pl.nchunks - c0 : len;
   if (n < 0) n = 0;
 }
@@ -1183,11 +1190,12 @@ SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail, bool pipe_ok = true
     const size_t fit = (avail - cb) / (kPipeBufs * pc);
     const int most = (int)(fit < (size_t)kPipeChunks ? fit : (size_t)kPipeChunks);
     if (most == kPipeChunks && s.nchunks >= 2 * kPipeChunks) {
-      s.first = kPipeChunks / 2;
-      const int rest = s.nchunks - s.first;
+      int done = 0;
+      while ((kFirstChunks << s.ramp) < kPipeChunks) done += kFirstChunks << s.ramp++;
+      const int rest = s.nchunks - done;
       const int k = (rest + most - 1) / most;
-      s.per_slab = (rest + k - 1) / k;  // balanced slabs after the first
-      s.nslabs = 1 + k;
+      s.per_slab = (rest + k - 1) / k;  // balanced slabs after the ramp
+      s.nslabs = s.ramp + k;
     } else {
       s.nslabs = (s.nchunks + most - 1) / most;
       s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;  // balanced slabs, no small tail
@@ -1209,8 +1217,8 @@ SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail, bool pipe_ok = true
       s.carry_bytes = s.nslabs > 1 ? cb : 0;
     }
   }
-  s.region_bytes = (size_t)(s.first > s.per_slab ? s.first : s.per_slab) * pc;
-  if (s.first > 0) s.region_bytes = (size_t)kPipeChunks * pc;  // the same preferred size for any length
+  s.region_bytes = (size_t)s.per_slab * pc;
+  if (s.ramp > 0) s.region_bytes = (size_t)kPipeChunks * pc;  // the same preferred size for any length
   return s;
 }
 
