@@ -326,11 +326,13 @@ def time_backward(torch, kda, w, inp, steps):
 
 
 def backward_launches(T, d):
-    """What one kda_prefill_backward call of T tokens launches (16-token stretches, 64 per slab)."""
-    stretches = -(-T // 16)
-    slabs = max(1, -(-stretches // 64))
-    return (f"backward_kernel<{d}, ., 1> (forward) once, then {slabs} x (mode 2: recompute of a slab, "
-            "on the compute units the reverse leaves free, overlapping mode 3: the reverse walk of the previous slab)")
+    """What one kda_prefill_backward call of T tokens launches (32-token stretches, 32 per slab)."""
+    stretches = -(-T // 32)
+    slabs = max(1, -(-stretches // 32))
+    return (f"prefill_kernel<32, {d}, {d}, ., false, true> (the chunkwise forward with fp32 operands, storing the "
+            f"state every 32 tokens) once, then {slabs} x (backward_kernel mode 2: recompute of a slab of 1,024 "
+            "tokens, on the compute units the reverse leaves free, overlapping mode 3: the reverse walk of the "
+            "previous slab)")
 
 
 def time_context_parallel(torch, kda, w, inp, R, A, steps):

@@ -3,9 +3,11 @@
 // row), for the definition of "Kimi K3, previewed", section "Kimi Delta
 // Attention - the workhorse" and the KDA rows of the component tables.
 //
-// Token by token, all in fp32, three launch kinds (256 or 512 threads by head dim):
-//   1. forward, one workgroup per (b, h): the recurrence over the whole
-//      sequence, storing the state at every stretch start (kBwdChunk tokens);
+// All in fp32, three launch kinds:
+//   1. forward, one workgroup per (b, h): the chunkwise prefill kernel with
+//      fp32 operands (kda_prefill.hip, launch_prefill_states), storing the
+//      state at every stretch start (kBwdChunk tokens, one chunk);
+//   then token by token (256 or 512 threads by head dim):
 //   2. recompute, one workgroup per (b, h, stretch) of a slab of stretches:
 //      from the stretch's stored state, the state entering every token and
 //      the token's vectors go to the slab buffer (all stretches at once, on
@@ -31,10 +33,12 @@ namespace kda {
 
 namespace {
 
-constexpr int kBwdChunk = 16;  // tokens between stored states (16 measured faster than 4, 8, 32 and 64)
-constexpr int kBwdSlab = 64;   // stretches recomputed per launch
+// Tokens between stored states: the chunk of the chunkwise forward that
+// stores them (kda_prefill.hip, fp32 operands).
+constexpr int kBwdChunk = kStateChunk;
+constexpr int kBwdSlab = 1024 / kBwdChunk;  // stretches recomputed per launch (1,024 tokens)
 
-enum : int { kModeForward = 1, kModeRecompute = 2, kModeReverse = 3 };
+enum : int { kModeRecompute = 2, kModeReverse = 3 };
 
 // Threads per workgroup: eight state rows per thread at d = 128 (512 threads,
 // 8 waves), so each SIMD has two waves to hide latency with (1024 threads
@@ -354,28 +358,6 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       }
     }
   };
-
-  // ---- 1. forward over the sequence, the state at every stretch start --------
-  if constexpr (MODE == kModeForward) {
-  if (active) {
-#pragma unroll
-    for (int i = 0; i < RPT; ++i) {
-      const int r = rg + RG * i;
-      s[i] = p.S0 != nullptr ? *reinterpret_cast<const f4*>(p.S0 + (size_t)bh * D * D + (size_t)r * D + 4 * cg)
-                             : f4{0.f, 0.f, 0.f, 0.f};
-    }
-  }
-  start_window(0);
-  for (int t = 0; t < T; ++t) {
-    if (t % kBwdChunk == 0 && active) {
-      float* dst = ckpt + (size_t)(t / kBwdChunk) * D * D;
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) *reinterpret_cast<f4*>(dst + (size_t)(rg + RG * i) * D + 4 * cg) = s[i];
-    }
-    forward_step(t, nullptr, f4{0.f, 0.f, 0.f, 0.f}, f4{0.f, 0.f, 0.f, 0.f});
-  }
-  return;
-  }
 
   // ---- 2. recompute one stretch: the state entering each token, each token's record
   if constexpr (MODE == kModeRecompute) {
@@ -709,8 +691,20 @@ int run_backward_typed(const kda_prefill_backward_args& a, hipStream_t st) {
     if (rc != KDA_OK) return rc;
   }
   const bool piped = pp != nullptr;
-  hipLaunchKernelGGL((backward_kernel<D, IB, kModeForward>), dim3(heads), block, 0, st, p);
-  hipError_t e = hipGetLastError();
+  // the state at every stretch start, from the chunkwise forward (fp32 operands)
+  {
+    kda_prefill_args f{};
+    f.B = a.B; f.T = a.T; f.H = a.H; f.dk = a.dk; f.dv = a.dv; f.chunk = kBwdChunk;
+    f.in_dtype = a.in_dtype; f.out_dtype = KDA_F32;
+    f.q = a.q; f.k = a.k; f.v = a.v; f.conv_w = a.conv_w; f.g = a.g; f.beta = a.beta; f.gate = a.gate;
+    f.S0 = a.S0; f.conv_in = a.conv_in;
+    f.decay_form = KDA_DECAY_DIRECT;
+    if (a.T > 0) {
+      const int rc = launch_prefill_states(f, kBwdChunk, static_cast<float*>(a.workspace), st);
+      if (rc != KDA_OK) return rc;
+    }
+  }
+  hipError_t e = hipSuccess;
   const char* what = "forward launch";
   if (e == hipSuccess && piped) {
     // the pipeline's streams start after the forward launch

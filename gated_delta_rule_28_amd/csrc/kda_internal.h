@@ -39,6 +39,12 @@ int launch_cp_compose(const kda_cp_compose_args& a, hipStream_t s);
 int launch_cp_history(const kda_prefill_args& a, int nblk, int first, int L, void* dst, hipStream_t s);
 int launch_cp_identity(float* S, size_t count, int d, hipStream_t s);
 
+// The state entering every kStateChunk-token chunk of a prefill ([B*H][chunks]
+// [dk][dv] fp32, natural order), computed chunkwise with fp32 operands and no
+// outputs (kda_prefill.hip): the backward's checkpoints.
+constexpr int kStateChunk = 32;
+int launch_prefill_states(const kda_prefill_args& a, int chunk, float* S_chunks, hipStream_t s);
+
 // Prefill gradients (fp32, one workgroup per (b, h)) and their workspace.
 size_t prefill_backward_workspace_bytes(const kda_prefill_backward_args& a);
 int launch_prefill_backward(const kda_prefill_backward_args& a, hipStream_t s);

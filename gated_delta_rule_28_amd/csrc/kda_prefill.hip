@@ -80,6 +80,9 @@ struct PrefillParams {
   float* v_out;
   float* G_out;
   const float* A;  // [H, dk]: g and beta are K3's logits (see k3_decay); null: given directly
+  // [B*H][chunks][dk][dv]: the state entering every chunk, or null (the
+  // backward's checkpoints); o may be null when only these are wanted
+  float* S_chunks;
 };
 
 // ---------------------------------------------------------------------------
@@ -748,6 +751,14 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
   for (int ci = 0; ci < nchunks; ++ci) {
     const int c0 = ci * C;
     const int n_valid = min(C, T - c0);
+    if (p.S_chunks != nullptr && owns_cols) {
+      float* sc = p.S_chunks + ((size_t)bh * nchunks + ci) * DK * DV;
+      const int sg = (threadIdx.x & 63) >> 4, sl = threadIdx.x & 15;
+#pragma unroll
+      for (int t = 0; t < RTK; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[(16 * t + 4 * sg + r) * DV + col0 + sl] = S[t][r];
+    }
     // per-lane indices, recomputed every chunk (see opaque())
     const int tid = opaque((int)threadIdx.x);
     const int lane = tid & 63;
@@ -1225,7 +1236,7 @@ __global__ __launch_bounds__(kThreads) void prefill_kernel(PrefillParams p) {
         raw_unpack<IN_BF16>(gt[j], gv);
 #pragma unroll
         for (int q = 0; q < 8; ++q) x[q] = x[q] * rs * sigmoidf_(gv[q]);
-        if (tok < n_valid) store8<OUT_BF16>(p.o, (((size_t)b * T + c0 + tok) * H + h) * DV + 8 * oc, x);
+        if (tok < n_valid && p.o != nullptr) store8<OUT_BF16>(p.o, (((size_t)b * T + c0 + tok) * H + h) * DV + 8 * oc, x);
       }
     }
     lds_barrier();  // LDS is rewritten by the next chunk
@@ -1302,6 +1313,27 @@ int run_prefill(const kda_prefill_args& a, hipStream_t s) {
   PrefillParams p = make_params(a);
   hipLaunchKernelGGL(kern, dim3((unsigned)(a.B * a.H)), dim3(kThreads), L::BYTES, s, p);
   return check_launch("prefill");
+}
+
+// The state entering every C-token chunk, fp32 operands throughout, no outputs.
+template <int C, int D, bool IB>
+int run_states(const kda_prefill_args& a, float* S_chunks, hipStream_t s) {
+  using L = Smem<C, D, D, true>;
+  static_assert(L::BYTES <= 160 * 1024, "fp32-operand chunk exceeds LDS");
+  auto kern = prefill_kernel<C, D, D, IB, false, true>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, L::BYTES);
+  if (e != hipSuccess) {
+    set_error("chunk states: hipFuncSetAttribute failed: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  PrefillParams p = make_params(a);
+  p.o = nullptr;
+  p.S_T = nullptr;
+  p.conv_out = nullptr;
+  p.S_chunks = S_chunks;
+  hipLaunchKernelGGL(kern, dim3((unsigned)(a.B * a.H)), dim3(kThreads), L::BYTES, s, p);
+  return check_launch("chunk states");
 }
 
 template <int C, int D>
@@ -1381,6 +1413,22 @@ int launch_prep(const kda_prep_args& a, hipStream_t s) {
     case 64: return prep_d<64>(a, s);
   }
   set_error("prep: chunk %d not in {16,32,64}", a.chunk);
+  return KDA_E_UNSUPPORTED;
+}
+
+int launch_prefill_states(const kda_prefill_args& a, int chunk, float* S_chunks, hipStream_t s) {
+  const bool ib = a.in_dtype == KDA_BF16;
+  if (chunk != kStateChunk) {
+    set_error("chunk states: chunk %d is not %d", chunk, kStateChunk);
+    return KDA_E_UNSUPPORTED;
+  }
+  switch (a.dk) {
+    case 16: return ib ? run_states<kStateChunk, 16, true>(a, S_chunks, s) : run_states<kStateChunk, 16, false>(a, S_chunks, s);
+    case 32: return ib ? run_states<kStateChunk, 32, true>(a, S_chunks, s) : run_states<kStateChunk, 32, false>(a, S_chunks, s);
+    case 64: return ib ? run_states<kStateChunk, 64, true>(a, S_chunks, s) : run_states<kStateChunk, 64, false>(a, S_chunks, s);
+    case 128: return ib ? run_states<kStateChunk, 128, true>(a, S_chunks, s) : run_states<kStateChunk, 128, false>(a, S_chunks, s);
+  }
+  set_error("chunk states: head dim %d not instantiated", a.dk);
   return KDA_E_UNSUPPORTED;
 }
 

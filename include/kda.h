@@ -372,16 +372,17 @@ size_t kda_cp_rank_workspace_bytes(const kda_prefill_args* args);
  * segment's S_T and conv_out from the forward pass).
  * Gradients are with respect to the input values (bf16 inputs: their bf16
  * values).  Direct decay form only (decay_form KDA_DECAY_DIRECT), dk = dv.
- * Computed in fp32: the forward recurrence again (one workgroup per (b, h))
- * with the state stored every 16 tokens in the workspace; then, for slabs of
- * up to 64 such stretches from the last to the first, every stretch of the
- * slab recomputed at once, and the slab walked back token by token (one
+ * Computed in fp32: the forward again, chunkwise with fp32 matrix-core
+ * operands (one workgroup per (b, h)), with the state stored every 32 tokens
+ * in the workspace; then, for slabs of up to 32 such stretches (1,024 tokens)
+ * from the last to the first, every stretch of the slab recomputed at once,
+ * and the slab walked back token by token (one
  * workgroup per (b, h)); the next slab's recompute runs on the other compute
  * units meanwhile (streams of the library's own, ordered after the work
  * already on `stream`, which in turn waits for them).  Workspace
  * (kda_prefill_backward_workspace_bytes, 16-byte aligned, required), with
- * n = ceil(T/16):
- * B*H*(n*dk*dv + dk*dv + 9*dk + 2*min(n, 64)*16*(dk*dv + 13*dk + 8))*4 bytes.
+ * n = ceil(T/32):
+ * B*H*(n*dk*dv + dk*dv + 9*dk + 2*min(n, 32)*32*(dk*dv + 13*dk + 8))*4 bytes.
  * Errors as kda_prefill; KDA_E_NULL (grad_o, a required gradient output or the
  * workspace NULL), KDA_E_UNSUPPORTED (KDA_DECAY_K3), KDA_E_WORKSPACE.
  */

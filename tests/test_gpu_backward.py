@@ -32,12 +32,12 @@ def _run(kda, torch, inp, dtype, dO, dS):
 
 CASES = [
     # B, T, H, d, dtype
-    (1, 200, 2, 128, "bf16"),   # 13 stretches of 16 (ragged last)
+    (1, 200, 2, 128, "bf16"),   # 7 stretches of 32 (ragged last)
     (2, 150, 2, 32, "f32"),
     (2, 70, 3, 16, "bf16"),
     (1, 64, 2, 64, "f32"),      # a whole number of stretches
     (2, 2, 2, 16, "f32"),       # fewer tokens than the conv history
-    (1, 1100, 1, 32, "f32"),    # 69 stretches: two slabs of recompute (64 + 5), dS and the ring carried
+    (1, 1100, 1, 32, "f32"),    # 35 stretches: two slabs of recompute (32 + 3), dS and the ring carried
     (1, 1100, 2, 128, "bf16"),  # the K3-width shape's kernels: 512 threads, two pipelined slabs
 ]
 
