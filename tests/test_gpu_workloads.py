@@ -1,7 +1,7 @@
 """The full-size workloads on the GPU, checked against the oracle over every
-output: all heads at K3 width (three input recipes), all 96 heads over all
-1,048,576 tokens of the 16-segment run, and all 256 x 96 (sequence, head)
-pairs over all 1000 decode steps.
+output: all heads at K3 width (three input recipes, and one context-parallel
+rank's share), all 96 heads over all 1,048,576 tokens of the 16-segment run,
+and all 256 x 96 (sequence, head) pairs over all 1000 decode steps.
 
 Inputs are drawn on the device (kda_synth's torch backend) at the exact
 shapes the benchmark times; the GPU runs the whole workload; the inputs are
@@ -120,6 +120,37 @@ def test_k3width_mixed_fast_channels_all_heads(oracle_mod):
     print(f"  worst head {int(per_head.argmax())}: max|err|/RMS(o) = {per_head.max():.3e}", flush=True)
     assert_rms_close(o_got, r["o"], TOL_BF16, "k3width fast channels o, all heads")
     assert_rms_close(s_got, r["S_T"], TOL_BF16, "k3width fast channels S_T, all heads")
+
+
+@pytest.mark.timeout(900)
+def test_k3width_cp_rank_share_all_heads(oracle_mod, progress):
+    """One rank's context-parallel share at the rank's full shape (65,536
+    tokens x 96 heads, the 1M-token run in 16 ranks): kda_cp_fragments' N and P
+    against the oracle run from S = 0 and from S = I, and kda_cp_finish's o and
+    S_T from an entering state against the oracle run from that state, every
+    head over every token.  conv_in stands for the previous rank's last tokens."""
+    torch, kda = need_gpu()
+    w = syn.WORKLOADS["k3width"]
+    dev = syn.prefill_inputs_torch(w, "cuda")
+    conv_in = (torch.randn((w.B, 3, w.cch), device="cuda", generator=torch.Generator("cuda").manual_seed(5))
+               .to(torch.bfloat16))
+    args = [dev[x] for x in ("q", "k", "v", "conv_w", "g", "beta", "gate")]
+    ws, N, P = kda.cp_fragments(*args, conv_in=conv_in, chunk=w.chunk)
+    o, S_T, _ = kda.cp_finish(ws, *args, dev["S0"], conv_in=conv_in, chunk=w.chunk, want_conv=False)
+    torch.cuda.synchronize()
+    del ws
+    host = {x: syn.torch_to_np(dev[x]) for x in ("q", "k", "v", "g", "beta", "gate")}
+    host["conv_w"] = syn.torch_to_np(dev["conv_w"])
+    host["conv_in"] = syn.torch_to_np(conv_in)
+    d = w.dk
+    for what, S0, got in (("N (from S = 0)", np.zeros((w.B, w.H, d, d), dtype=np.float32), N),
+                          ("P (from S = I)", np.broadcast_to(np.eye(d, dtype=np.float32), (w.B, w.H, d, d)).copy(), P)):
+        r = oracle_mod.prefill(dict(host, S0=S0), want_o=False)
+        assert_rms_close(got[0].cpu().numpy(), r["S_T"], TOL_BF16, f"rank share {what}, all heads")
+        progress(f"  {what}: checked")
+    r = oracle_mod.prefill(dict(host, S0=dev["S0"].cpu().numpy()))
+    assert_rms_close(o[0].cpu().numpy().transpose(1, 0, 2), r["o"], TOL_BF16, "rank share finish o, all heads")
+    assert_rms_close(S_T[0].cpu().numpy(), r["S_T"], TOL_BF16, "rank share finish S_T, all heads")
 
 
 @pytest.mark.timeout(1100)
