@@ -1140,8 +1140,9 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 // How the chunks of one call are split into launches ("slabs").
 //
 // Pipelined (a sequence of more than kPipeChunks chunks and B*H at most half
-// the compute units): slabs of at most kPipeChunks chunks in kPipeBufs
-// workspace buffers.  From 2 * kPipeChunks chunks on, the slabs ramp up from
+// the compute units): slabs of at most kPipeChunks chunks, each in its own
+// workspace region when all fit under kSlabBytesMax, else in kPipeBufs
+// buffers used in turn.  From 2 * kPipeChunks chunks on, the slabs ramp up from
 // kFirstChunks, each twice as long as the one before, so the inter-chunk kernel
 // (the slower stage) starts soon and later launches are few.  The inter-chunk kernel (one workgroup per (b, h), the state carried
 // between slabs in a buffer) runs on a stream restricted to B*H compute units,
@@ -1201,6 +1202,12 @@ SlabPlan plan_slabs(const kda_prefill_args& a, size_t avail, bool pipe_ok = true
       s.per_slab = (s.nchunks + s.nslabs - 1) / s.nslabs;  // balanced slabs, no small tail
     }
     s.nbuf = s.nslabs < kPipeBufs ? s.nslabs : kPipeBufs;
+    // Every slab its own region when they all fit (under the cap): the
+    // intra-chunk kernel then never waits for the inter-chunk kernel to free a
+    // buffer, and the inter-chunk stream records no per-slab event (measured
+    // 5.74 against 5.88 ms at K3 width).
+    const size_t all = (size_t)s.nslabs * kPipeChunks * pc;
+    if (all <= kSlabBytesMax && avail >= cb + all) s.nbuf = s.nslabs;
     s.carry_bytes = cb;
   } else {
     const size_t room = avail < kSlabBytesMax ? avail : kSlabBytesMax;
@@ -1361,7 +1368,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
       e = hipGetLastError();
       what = "inter-chunk launch";
     }
-    if (e == hipSuccess && piped) {
+    if (e == hipSuccess && piped && sl + pl.nbuf < pl.nslabs) {  // a later slab reuses the buffer
       what = "event";
       e = hipEventRecord(pp->b_done[buf], sb);
     }

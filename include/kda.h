@@ -151,8 +151,9 @@ int kda_prefill(const kda_prefill_args* args, void* stream);
 
 /* Device workspace the two-kernel path prefers for these sizes: 64 KiB per
  * (b, h, chunk of 64 tokens) of one slab; for a pipelined sequence (more than
- * 64 chunks, 2*B*H <= 256) three buffers of one slab of up to 64 chunks (two
- * when there are two slabs) plus B*H*dk*dv*4 bytes to carry the state; otherwise all chunks in one slab,
+ * 64 chunks, 2*B*H <= 256) one region of 64 chunks per slab while all of them
+ * fit 16 GiB (6.4 GB at K3 width for 65,536 tokens), else three such buffers
+ * used in turn, plus B*H*dk*dv*4 bytes to carry the state; otherwise all chunks in one slab,
  * capped near 16 GiB (plus the carry) by running longer sequences in slabs
  * one after the other.  0 when the sizes have no two-kernel path or the
  * arguments are invalid.  The fields B, T, H, dk, dv, chunk, in_dtype and
