@@ -472,6 +472,8 @@ def main():
     per = timed_launches(torch, step, args.steps)
     torch.cuda.synchronize()
     ms = sum(per) / len(per)
+    if kda.wait_timeouts() != 0:  # a per-slab wait expired: some outputs are wrong
+        raise RuntimeError("kda_wait_timeouts reports expired in-kernel waits; the timed prefill is invalid")
     tokens = w.B * w.T
     value = tokens / (ms * 1e-3)
     launch_ms = ms / w.segments

@@ -39,7 +39,7 @@ KDA_F32 = 0
 KDA_BF16 = 1
 KDA_DECAY_DIRECT = 0
 KDA_DECAY_K3 = 1
-ABI_VERSION = 7
+ABI_VERSION = 8
 MAX_DECODE_TOKENS = 16
 NOALLOC_SCRATCH_BYTES = 128 << 20  # KDA_NOALLOC_SCRATCH_BYTES
 
@@ -151,6 +151,8 @@ def lib():
         L.kda_last_error.restype = ctypes.c_char_p
         L.kda_abi_version.restype = ctypes.c_int
         L.kda_release.restype = ctypes.c_int
+        L.kda_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint)]
+        L.kda_wait_timeouts.restype = ctypes.c_int
         L.kda_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _P]
         L.kda_prefill_noalloc.restype = ctypes.c_int
         if L.kda_abi_version() != ABI_VERSION:
@@ -169,6 +171,15 @@ def release():
     """kda_release: destroy the streams and events the library keeps between
     calls (all devices and threads; call with no library call in flight)."""
     _check("kda_release", lib().kda_release())
+
+
+def wait_timeouts():
+    """kda_wait_timeouts: the bounded in-kernel waits that expired on the
+    current device since the library was loaded (nonzero: some prefill call's
+    outputs are wrong).  Waits for the device's work to finish."""
+    n = ctypes.c_uint(0)
+    _check("kda_wait_timeouts", lib().kda_wait_timeouts(ctypes.byref(n)))
+    return n.value
 
 
 def _torch():

@@ -170,6 +170,11 @@ extern "C" {
 
 int kda_abi_version(void) { return KDA_ABI_VERSION; }
 
+int kda_wait_timeouts(unsigned* count) {
+  if (count == nullptr) return fail(KDA_E_NULL, "wait_timeouts: count is NULL");
+  return kda::wait_timeouts(count);
+}
+
 int kda_release(void) {
   const hipError_t e = kda::release_all();
   if (e != hipSuccess) return fail(KDA_E_HIP, "release: %s", hipGetErrorString(e));

@@ -109,7 +109,29 @@ struct SplitParams {
   // grid 2 * B * H, copy 1 in blocks B*H ..): it starts from the identity and
   // writes only its final state to S_out2.  o may be null (no outputs).
   float* S_out2;
+  // Workspace addressing: the block of chunk c of head bh is block
+  // bh * ws_stride + (c - ws_first) (0, 0: ws_stride = n_chunks, ws_first =
+  // c_begin, the blocks of this launch alone).
+  int ws_stride, ws_first;
+  // One recurrence launch over every slab (see run_split): before copying the
+  // first chunk of slab s the copying waves wait for slab_ready[s] (set after
+  // that slab's intra-chunk kernel); slabs are laid out as slab_range does
+  // (ramp leading slabs of kFirstChunks << s chunks, then slab_per each).
+  const unsigned* slab_ready;
+  int slab_ramp, slab_per;
 };
+
+// Slab lengths of the pipeline (see plan_slabs).
+constexpr int kPipeChunks = 64;
+constexpr int kFirstChunks = 32;
+
+// Bounded waits on slab_ready: a copying wave that has waited this long (100
+// MHz real-time counter ticks, 10 s) counts the miss in g_wait_timeouts and
+// stops waiting, so the launch ends (with wrong results) instead of hanging.
+// The intra-chunk kernels are queued before the recurrence launch, on streams
+// of their own, so only other work holding their compute units can delay them.
+constexpr uint64_t kReadyWaitTicks = 1000000000ull;
+__device__ unsigned g_wait_timeouts;
 
 // DPP move inside rows of 16 lanes; lanes with no source or outside the bank
 // mask read 0.
@@ -270,7 +292,9 @@ __global__ __launch_bounds__(256, 3) void intra_chunk_kernel(SplitParams p) {
   const int lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int tok = 16 * wave + i;
   const bool valid = tok < n_valid;
-  unsigned char* wsb = p.ws + (size_t)blockIdx.x * WS_CHUNK;
+  const int wstride = p.ws_stride > 0 ? p.ws_stride : nc;
+  const int wfirst = p.ws_stride > 0 ? p.ws_first : p.c_begin;
+  unsigned char* wsb = p.ws + ((size_t)bh * wstride + (c - wfirst)) * WS_CHUNK;
 
   // ---- loads: this lane's token (clamped) and the tile's halo ------------------
   const size_t cch = (size_t)H * kNCh;
@@ -734,7 +758,38 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   const int w = wave & 3;
   const int lane = tid & 63, g = lane >> 4, i = lane & 15;
   const int nc = p.n_chunks;
-  const unsigned char* wsh = p.ws + (size_t)bh * nc * WS_CHUNK;
+  const unsigned char* wsh =
+      p.ws + ((size_t)bh * (p.ws_stride > 0 ? p.ws_stride : nc) + (p.ws_stride > 0 ? p.c_begin - p.ws_first : 0)) *
+                 WS_CHUNK;
+  // one launch over every slab: a copying wave waits for a slab's flag before
+  // copying the slab's first chunk (chunk jc of this launch)
+  bool dead = false;
+  auto wait_slab = [&](int jc) {
+    if (p.slab_ready == nullptr) return;
+    int sl;
+    const int ramp_end = kFirstChunks * ((1 << p.slab_ramp) - 1);
+    if (jc < ramp_end) {
+      int c0 = 0;
+      for (sl = 0; c0 + (kFirstChunks << sl) <= jc; ++sl) c0 += kFirstChunks << sl;
+      if (jc != c0) return;
+    } else {
+      if ((jc - ramp_end) % p.slab_per != 0) return;
+      sl = p.slab_ramp + (jc - ramp_end) / p.slab_per;
+    }
+    const unsigned* f = p.slab_ready + sl;
+    if (!dead && __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+      while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+        __builtin_amdgcn_s_sleep(8);
+        if (__builtin_amdgcn_s_memrealtime() - t0 > kReadyWaitTicks) {
+          dead = true;
+          if (lane == 0) atomicAdd(&g_wait_timeouts, 1u);
+          break;
+        }
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  };
   const int col0 = 32 * w;
 
   // math waves: S[m][ct] element e = S[channel perm_row(16m + 4g + e)][col0 + 16ct + i]
@@ -791,6 +846,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       }
     }
   } else if (nc > 0) {
+    wait_slab(0);
     stage_dma<0>(wsh, w, lane);
     __builtin_amdgcn_s_waitcnt(0);  // chunk 0's operands land before the first B1
   }
@@ -1042,7 +1098,10 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       // No memory wait before B1: this wave's copy of chunk j was waited for
       // after B2 of the previous chunk, and its stores need no wait.
       lds_barrier();  // B1
-      if (j + 1 < nc) stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
+      if (j + 1 < nc) {
+        wait_slab(j + 1);
+        stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
+      }
       // ---- epilogue of chunk j-1 ----------------------------------------------------
       float ov[2][2][8], osig[2];
       if (WANT_O && j >= 1) {
@@ -1151,8 +1210,6 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
 // Otherwise: one slab when all chunk blocks fit the workspace (and stay under
 // the cap), else as many chunks per slab as fit next to the state carry, one
 // slab after the other on the caller's stream.
-constexpr int kPipeChunks = 64;
-constexpr int kFirstChunks = 32;
 constexpr int kPipeBufs = 3;  // the intra-chunk kernel runs up to two slabs ahead
 constexpr int kPlanCUs = 256;  // compute units the preferred workspace is planned for
 
@@ -1308,6 +1365,15 @@ int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
   return KDA_OK;
 }
 
+// The flags of a one-launch recurrence: cleared on the caller's stream before
+// the pipeline forks, set one by one after each slab's intra-chunk kernel.
+__global__ void clear_flags_kernel(unsigned* f, int n) {
+  for (int i = threadIdx.x; i < n; i += blockDim.x) f[i] = 0u;
+}
+__global__ void set_flag_kernel(unsigned* f) {
+  if (threadIdx.x == 0) __hip_atomic_store(f, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 template <bool OB, bool K3>
 int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
   const SlabPlan pl = plan_slabs(a, a.workspace_bytes, pipe_ok);
@@ -1328,7 +1394,22 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
   float* carry = pl.carry_bytes ? reinterpret_cast<float*>(ws + pl.nbuf * pl.region_bytes) : nullptr;
   hipError_t e = hipSuccess;
   const char* what = "event";
-  if (piped) {
+  // Every slab resident at once: the chunk blocks of all slabs share one
+  // head-major layout, and a single recurrence launch walks them all, waiting
+  // on a flag per slab (kept where the state carry would be, which this mode
+  // does not use) instead of a stream event before each slab's launch.
+  // Not under stream capture: a graph may run its nodes in any order that
+  // keeps their dependencies, also the recurrence before the slabs it waits on.
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
+  const bool one_inter = piped && pl.nbuf == pl.nslabs && pl.nslabs > 1 &&
+                         hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone;
+  unsigned* flags = one_inter ? reinterpret_cast<unsigned*>(carry) : nullptr;
+  if (one_inter) {
+    hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, st, flags, pl.nslabs);
+    e = hipGetLastError();
+    what = "flag clear launch";
+  }
+  if (e == hipSuccess && piped) {
     // both streams start after everything already queued on the caller's
     e = hipEventRecord(pp->fork, st);
     if (e == hipSuccess) e = hipStreamWaitEvent(pp->intra[0], pp->fork, 0);
@@ -1349,6 +1430,11 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
     p.conv_out = last ? a.conv_out : nullptr;
     const int buf = sl % pl.nbuf;
     p.ws = ws + (size_t)buf * pl.region_bytes;
+    if (one_inter) {
+      p.ws = ws;
+      p.ws_stride = pl.nchunks;
+      p.ws_first = 0;
+    }
     hipStream_t sa = piped ? pp->intra[sl & 1] : st;
     // the buffer is free once the inter-chunk kernel of slab sl - nbuf is done
     if (piped && sl >= pl.nbuf) e = hipStreamWaitEvent(sa, pp->b_done[buf], 0);
@@ -1358,7 +1444,21 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
       e = hipGetLastError();
       what = "intra-chunk launch";
     }
-    if (e == hipSuccess && piped) {
+    if (one_inter) {
+      if (e == hipSuccess) {
+        hipLaunchKernelGGL(set_flag_kernel, dim3(1), dim3(64), 0, sa, flags + sl);
+        e = hipGetLastError();
+        what = "flag launch";
+      }
+      if (e != hipSuccess || !last) continue;
+      // every slab is queued: the one recurrence launch over all chunks
+      p.c_begin = 0;
+      p.n_chunks = pl.nchunks;
+      p.S_in = a.S0;
+      p.slab_ready = flags;
+      p.slab_ramp = pl.ramp;
+      p.slab_per = pl.per_slab;
+    } else if (e == hipSuccess && piped) {
       what = "event";
       e = hipEventRecord(pp->a_done[sl & 1], sa);
       if (e == hipSuccess) e = hipStreamWaitEvent(sb, pp->a_done[sl & 1], 0);
@@ -1393,6 +1493,16 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
 }
 
 }  // namespace
+
+int wait_timeouts(unsigned* count) {
+  const hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_wait_timeouts), sizeof(unsigned), 0,
+                                           hipMemcpyDeviceToHost);
+  if (e != hipSuccess) {
+    set_error("wait_timeouts: %s", hipGetErrorString(e));
+    return KDA_E_HIP;
+  }
+  return KDA_OK;
+}
 
 bool prefill_split_eligible(const kda_prefill_args& a) {
   return a.in_dtype == KDA_BF16 && a.chunk == kC && a.dk == kD && a.dv == kD;

@@ -73,7 +73,7 @@
 extern "C" {
 #endif
 
-#define KDA_ABI_VERSION 7
+#define KDA_ABI_VERSION 8
 
 /* element types */
 enum { KDA_F32 = 0, KDA_BF16 = 1 };
@@ -112,15 +112,22 @@ enum {
  *    in the workspace.  For other sizes the workspace is unused.
  *  - workspace == NULL: one kernel per (b, h) walks the chunks and keeps every
  *    intermediate on chip (no device memory beyond the arguments).
- *    A sequence of more than 64 chunks with 2*B*H at most the device's
- *    compute units runs in slabs of up to 64 chunks through up to three
- *    workspace buffers: the per-(b, h) kernel of one slab runs on a stream
- *    restricted to B*H (rounded up to 8) compute units while the all-chunks
- *    kernels of the next slabs run on two streams restricted to the others.
- *    The library creates these three streams (default priority) and their
- *    events once per host thread, device and B*H, keeps them for the life of
- *    the thread, starts them after the work already queued on `stream` and
- *    makes `stream` wait for all three before any later work.
+ * With a workspace, a sequence of more than 64 chunks with 2*B*H at most the
+ * device's compute units runs as a pipeline of slabs of up to 64 chunks: the
+ * per-(b, h) kernel runs on a stream restricted to B*H (rounded up to 8)
+ * compute units while the all-chunks kernels of the slabs run on two streams
+ * restricted to the others.  When every slab has a workspace region of its
+ * own (the size kda_prefill_workspace_bytes returns) and `stream` is not
+ * capturing a graph, the per-(b, h) kernel is one launch over all slabs that
+ * waits on a device flag per slab, set by a one-wave kernel queued after the
+ * slab's all-chunks kernel; such a wait gives up after 10 s (counted by
+ * kda_wait_timeouts; that call's outputs are then wrong), so the call always
+ * ends.  Otherwise the per-(b, h) kernel is launched once per slab, after a
+ * stream event, and the slabs go through up to three buffers in turn.
+ * The library creates these three streams (default priority) and their
+ * events once per host thread, device and B*H, keeps them for the life of
+ * the thread, starts them after the work already queued on `stream` and
+ * makes `stream` wait for all three before any later work.
  * The library owns no device memory: the caller allocates the workspace and
  * may reuse it once the call's work on `stream` has finished.
  */
@@ -431,6 +438,13 @@ const char* kda_last_error(void);
 
 /* KDA_ABI_VERSION of the loaded library. */
 int kda_abi_version(void);
+
+/* Bounded in-kernel waits that expired on the current device since the
+ * library was loaded: the per-slab flags of a pipelined kda_prefill (see
+ * there), whose producer did not run within 10 s, e.g. because other work held
+ * its compute units.  Nonzero means some call's outputs are wrong.  Waits for
+ * the device's work to finish.  Returns KDA_OK, KDA_E_NULL or KDA_E_HIP. */
+int kda_wait_timeouts(unsigned* count);
 
 /* kda_prefill for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same

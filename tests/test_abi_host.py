@@ -38,7 +38,8 @@ def test_header_declares_the_abi():
     for must in ("kda_prefill", "kda_decode_step", "kda_decode_multi", "kda_prefill_workspace_bytes", "kda_prep",
                  "kda_status_string", "kda_last_error", "kda_abi_version", "kda_cp_compose", "kda_prefill_cp",
                  "kda_prefill_cp_workspace_bytes", "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
-                 "kda_release", "kda_cp_fragments", "kda_cp_finish", "kda_cp_rank_workspace_bytes"):
+                 "kda_release", "kda_cp_fragments", "kda_cp_finish", "kda_cp_rank_workspace_bytes",
+                 "kda_wait_timeouts"):
         assert must in names
 
 
@@ -119,6 +120,7 @@ def test_prefill_validation_codes(kda, over, code):
 def test_prefill_null_args_and_empty(kda):
     L = kda.lib()
     assert L.kda_prefill(None, None) == -1
+    assert L.kda_wait_timeouts(None) == -1
     # T = 0 with nothing to carry: nothing to do, succeeds without a launch
     a = _prefill_args(kda, T=0, q=None, k=None, v=None, o=None)
     assert L.kda_prefill(ctypes.byref(a), None) == 0
@@ -269,7 +271,7 @@ def test_status_strings(kda):
     L = kda.lib()
     assert L.kda_status_string(0).decode() == "ok"
     assert L.kda_status_string(12345).decode() == "unknown status code"
-    assert L.kda_abi_version() == 7
+    assert L.kda_abi_version() == 8
 
 
 def test_release_with_nothing_kept(kda):

@@ -147,8 +147,10 @@ def test_slabs_of_a_small_workspace(oracle_mod, per_slab):
 def test_pipelined_slabs(oracle_mod, per_buf):
     """70 chunks (T = 4480) exceed one slab of 64 chunks: the preferred
     workspace runs two slabs of 35 on streams restricted to disjoint compute
-    units, the state carried between them; a workspace with room for three
-    buffers of 10 chunks runs 7 slabs, so every buffer is reused."""
+    units, each in a region of its own, and one recurrence launch that waits on
+    a flag per slab; a workspace with room for three buffers of 10 chunks runs
+    7 slabs, a recurrence launch each (the state carried between them), so
+    every buffer is reused."""
     torch, kda = need_gpu()
     w = Workload("pp", 1, 70 * 64, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=17)
     inp = syn.prefill_inputs_np(w)
@@ -160,11 +162,13 @@ def test_pipelined_slabs(oracle_mod, per_buf):
                                                      device="cuda")
     o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=ws)
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"pipelined slabs, buffers of {per_buf or 35} chunks")
+    assert kda.wait_timeouts() == 0
 
 
 def test_pipelined_half_first_slab(oracle_mod):
     """131 chunks (T = 8393, ragged): slabs of 32, 50 and 49 chunks (the first
-    one half-size), three buffers of 64 chunks at the preferred workspace."""
+    one half-size), three regions of 64 chunks at the preferred workspace, one
+    recurrence launch that finds each slab's first chunk from the slab plan."""
     torch, kda = need_gpu()
     w = Workload("pf", 1, 131 * 64 - 55, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=29)
     inp = syn.prefill_inputs_np(w)
@@ -173,6 +177,7 @@ def test_pipelined_half_first_slab(oracle_mod):
     assert kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv) == 3 * 64 * per_chunk + w.B * w.H * w.dk * w.dv * 4
     o, S_T, c = _gpu_prefill(kda, dev, 64)
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="half-size first slab")
+    assert kda.wait_timeouts() == 0
 
 
 @pytest.mark.parametrize("B,H,T", [(2, 3, 70 * 64 + 17), (1, 130, 66 * 64 + 5)])

@@ -49,6 +49,7 @@ def test_k3width_prefill_all_heads(oracle_mod):
     print(f"  worst head {int(per_head.argmax())}: max|err|/RMS(o) = {per_head.max():.3e}", flush=True)
     assert_rms_close(o_got, r["o"], TOL_BF16, "k3width o, all heads")
     assert_rms_close(s_got, r["S_T"], TOL_BF16, "k3width S_T, all heads")
+    assert kda.wait_timeouts() == 0
 
 
 @pytest.mark.timeout(600)
@@ -186,6 +187,7 @@ def test_long1m_prefill_all_heads(oracle_mod, progress):
     for h in range(w.H):
         ch = oracle_mod._head_channels(w.H, w.dk, w.dv, h)
         assert np.array_equal(conv_np[0][:, ch], syn.bf16_bits_from_f64(hist_ref[h])), "long1m conv history"
+    assert kda.wait_timeouts() == 0
 
 
 @pytest.mark.timeout(600)
