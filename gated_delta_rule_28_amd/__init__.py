@@ -153,6 +153,8 @@ def lib():
         L.kda_release.restype = ctypes.c_int
         L.kda_wait_timeouts.argtypes = [ctypes.POINTER(ctypes.c_uint)]
         L.kda_wait_timeouts.restype = ctypes.c_int
+        L.kda_debug_pipeline.argtypes = [ctypes.c_uint, ctypes.c_int]
+        L.kda_debug_pipeline.restype = ctypes.c_int
         L.kda_prefill_noalloc.argtypes = [ctypes.POINTER(PrefillArgs), _P]
         L.kda_prefill_noalloc.restype = ctypes.c_int
         if L.kda_abi_version() != ABI_VERSION:
@@ -174,12 +176,19 @@ def release():
 
 
 def wait_timeouts():
-    """kda_wait_timeouts: the bounded in-kernel waits that expired on the
-    current device since the library was loaded (nonzero: some prefill call's
-    outputs are wrong).  Waits for the device's work to finish."""
+    """kda_wait_timeouts: the bounded in-kernel waits of pipelined prefill
+    calls that expired on the current device since the library was loaded
+    (each stopped workgroup was finished by the call's second launch).  Waits
+    for the device's work to finish."""
     n = ctypes.c_uint(0)
     _check("kda_wait_timeouts", lib().kda_wait_timeouts(ctypes.byref(n)))
     return n.value
+
+
+def debug_pipeline(wait_limit_us=0, withhold_slab=-1):
+    """kda_debug_pipeline: test aid for the stop-and-resume path of pipelined
+    prefill (defaults restore normal operation)."""
+    _check("kda_debug_pipeline", lib().kda_debug_pipeline(wait_limit_us, withhold_slab))
 
 
 def _torch():

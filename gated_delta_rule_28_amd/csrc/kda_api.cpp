@@ -175,6 +175,12 @@ int kda_wait_timeouts(unsigned* count) {
   return kda::wait_timeouts(count);
 }
 
+int kda_debug_pipeline(unsigned wait_limit_us, int withhold_slab) {
+  if (withhold_slab < -1) return fail(KDA_E_SHAPE, "debug_pipeline: withhold_slab %d < -1", withhold_slab);
+  kda::debug_pipeline(wait_limit_us, withhold_slab);
+  return KDA_OK;
+}
+
 int kda_release(void) {
   const hipError_t e = kda::release_all();
   if (e != hipSuccess) return fail(KDA_E_HIP, "release: %s", hipGetErrorString(e));

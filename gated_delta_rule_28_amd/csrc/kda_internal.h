@@ -17,6 +17,8 @@ int launch_prep(const kda_prep_args& a, hipStream_t s);
 // Two-kernel prefill (bf16 inputs, chunk 64, dk = dv = 128) through a workspace.
 // Expired bounded waits of the one-launch recurrence on the current device.
 int wait_timeouts(unsigned* count);
+// Test settings of the one-launch recurrence (see kda_debug_pipeline).
+void debug_pipeline(unsigned wait_us, int withhold_slab);
 bool prefill_split_eligible(const kda_prefill_args& a);
 size_t prefill_split_workspace_bytes(const kda_prefill_args& a);
 size_t prefill_split_workspace_min_bytes(const kda_prefill_args& a);

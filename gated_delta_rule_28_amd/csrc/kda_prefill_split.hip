@@ -55,6 +55,8 @@
 #include "kda_device.h"
 #include "kda_internal.h"
 
+#include <algorithm>
+#include <atomic>
 #include <mutex>
 #include <type_traits>
 
@@ -115,22 +117,40 @@ struct SplitParams {
   int ws_stride, ws_first;
   // One recurrence launch over every slab (see run_split): before copying the
   // first chunk of slab s the copying waves wait for slab_ready[s] (set after
-  // that slab's intra-chunk kernel); slabs are laid out as slab_range does
-  // (ramp leading slabs of kFirstChunks << s chunks, then slab_per each).
+  // that slab's intra-chunk kernel), a sync block laid out as kSync* says;
+  // slabs are laid out as slab_range does (ramp leading slabs of kFirstChunks
+  // << s chunks, then slab_per each).  A workgroup whose wait expires stops
+  // before that chunk: it leaves its state after the chunks it finished in
+  // S_out (required; S_in, which S_out may alias, is no longer needed then), or
+  // nothing if it finished none, writes no conv_out, and records the chunks it
+  // finished in the block's progress entry.
   const unsigned* slab_ready;
   int slab_ramp, slab_per;
+  // Second launch after every slab is done: workgroup bh continues from chunk
+  // c_begin + resume[bh] (from the state left in S_out, or from S_in when
+  // resume[bh] == 0), or exits at once when resume[bh] == n_chunks.
+  const int* resume;
 };
 
 // Slab lengths of the pipeline (see plan_slabs).
 constexpr int kPipeChunks = 64;
 constexpr int kFirstChunks = 32;
 
-// Bounded waits on slab_ready: a copying wave that has waited this long (100
-// MHz real-time counter ticks, 10 s) counts the miss in g_wait_timeouts and
-// stops waiting, so the launch ends (with wrong results) instead of hanging.
-// The intra-chunk kernels are queued before the recurrence launch, on streams
-// of their own, so only other work holding their compute units can delay them.
-constexpr uint64_t kReadyWaitTicks = 1000000000ull;
+// Sync block of a one-launch recurrence (32-bit words): a flag per slab, the
+// bound of each wait (100 MHz real-time counter ticks), the chunks each (b, h)
+// finished.  Only pointers the kernel holds anyway lead to it.
+constexpr int kMaxSlabs = 4096;
+constexpr int kSyncBound = kMaxSlabs;
+constexpr int kSyncProgress = kMaxSlabs + 64;
+constexpr size_t sync_bytes(int nbh) { return ((size_t)kSyncProgress + nbh) * 4; }
+
+// Bounded waits on slab_ready (default 20 ms).  The intra-chunk kernels are
+// queued before the recurrence launch, on streams of their own, and normally
+// run ahead of it; a wait this long means they cannot run beside it (kernels
+// serialised, e.g. by a profiler collecting counters, or other work holding
+// their compute units).  The workgroup then stops, counts the miss in
+// g_wait_timeouts, and the resume launch finishes its work.
+constexpr unsigned kReadyWaitUs = 20000;
 __device__ unsigned g_wait_timeouts;
 
 // DPP move inside rows of 16 lanes; lanes with no source or outside the bank
@@ -688,6 +708,11 @@ __shared__ __attribute__((aligned(16))) unsigned char g_O[16 * kOBlk];
 __shared__ float4 g_vw[kD];
 // scale of each math wave's columns of the O in g_O (see kRangeLimit)
 __shared__ float g_Osig[4];
+// the chunk before which the first copying wave stopped (-1: none)
+__shared__ int g_dec;
+// In place of a chunk's wide flag (WS_WIDE) in a staging buffer: the chunk was
+// not copied, the workgroup stops before it.
+constexpr int kStopFlag = 2;
 
 // Range of the fp16 operands.  Each math wave keeps its columns of V, S, X, U
 // and O divided by a power of two sigma (1 unless the values demand more):
@@ -757,38 +782,46 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   const bool math = wave < 4;
   const int w = wave & 3;
   const int lane = tid & 63, g = lane >> 4, i = lane & 15;
-  const int nc = p.n_chunks;
-  const unsigned char* wsh =
-      p.ws + ((size_t)bh * (p.ws_stride > 0 ? p.ws_stride : nc) + (p.ws_stride > 0 ? p.c_begin - p.ws_first : 0)) *
-                 WS_CHUNK;
-  // one launch over every slab: a copying wave waits for a slab's flag before
-  // copying the slab's first chunk (chunk jc of this launch)
-  bool dead = false;
-  auto wait_slab = [&](int jc) {
-    if (p.slab_ready == nullptr) return;
-    int sl;
-    const int ramp_end = kFirstChunks * ((1 << p.slab_ramp) - 1);
-    if (jc < ramp_end) {
-      int c0 = 0;
-      for (sl = 0; c0 + (kFirstChunks << sl) <= jc; ++sl) c0 += kFirstChunks << sl;
-      if (jc != c0) return;
-    } else {
-      if ((jc - ramp_end) % p.slab_per != 0) return;
-      sl = p.slab_ramp + (jc - ramp_end) / p.slab_per;
-    }
+  // chunks [cb, cb + nc) of the sequence; a resume launch starts where the
+  // first launch stopped
+  int cb = p.c_begin, nc = p.n_chunks, done = 0;
+  if (p.resume != nullptr) {
+    done = p.resume[bh];
+    if (done >= nc) return;  // the first launch finished this (b, h)
+    cb += done;
+    nc -= done;
+  }
+  const int wstride = p.ws_stride > 0 ? p.ws_stride : p.n_chunks;
+  const int wfirst = p.ws_stride > 0 ? p.ws_first : p.c_begin;
+  const unsigned char* wsh = p.ws + ((size_t)bh * wstride + (cb - wfirst)) * WS_CHUNK;
+  // One launch over every slab (it starts at chunk 0): the copying waves wait
+  // before copying chunk next_jc, the first of slab next_sl; slab s is
+  // kFirstChunks << s chunks long while s < slab_ramp, then slab_per.
+  int next_sl = 0, next_jc = p.slab_ready != nullptr ? 0 : 0x7fffffff;
+  auto advance_slab = [&]() {
+    next_jc += next_sl < p.slab_ramp ? kFirstChunks << next_sl : p.slab_per;
+    ++next_sl;
+  };
+  // Each copying wave waits for slab sl's flag on its own (bounded); false: the
+  // wait expired.  The first copying wave's wait decides: the others wait 5 ms
+  // longer, so theirs expires only if the first wave's did (they start within
+  // microseconds of each other, after the same barrier).
+  auto slab_ready = [&](int sl) -> bool {
     const unsigned* f = p.slab_ready + sl;
-    if (!dead && __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+    const unsigned ticks = p.slab_ready[kSyncBound];
+    const unsigned bound = w == 0 ? ticks : ticks + 500000u;
+    if (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
       const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
       while (__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
         __builtin_amdgcn_s_sleep(8);
-        if (__builtin_amdgcn_s_memrealtime() - t0 > kReadyWaitTicks) {
-          dead = true;
-          if (lane == 0) atomicAdd(&g_wait_timeouts, 1u);
-          break;
+        if ((unsigned)(__builtin_amdgcn_s_memrealtime() - t0) > bound) {
+          if (w == 0 && lane == 0) atomicAdd(&g_wait_timeouts, 1u);
+          return false;
         }
       }
     }
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    return true;
   };
   const int col0 = 32 * w;
 
@@ -820,14 +853,15 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
           for (int e = 0; e < 4; ++e) S[m][ct][e] = perm_row(16 * m + 4 * g + e) == col0 + 16 * ct + i ? 1.f : 0.f;
-    } else if (p.S_in != nullptr) {
+    } else if (p.S_in != nullptr || done > 0) {
+      // a resumed (b, h) finds its state where the first launch left it
+      const float* src = (done > 0 ? S_out : p.S_in) + (size_t)bh * kD * kD;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int ct = 0; ct < 2; ++ct)
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            S[m][ct][e] = p.S_in[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i];
+          for (int e = 0; e < 4; ++e) S[m][ct][e] = src[(size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i];
       float sm = 0.0f;
 #pragma unroll
       for (int m = 0; m < 8; ++m)
@@ -845,9 +879,29 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           for (int ct = 0; ct < 2; ++ct) S[m][ct] *= r;
       }
     }
-  } else if (nc > 0) {
-    wait_slab(0);
-    stage_dma<0>(wsh, w, lane);
+  }
+  // Chunks this workgroup completes: nc, unless the first copying wave's wait
+  // for a slab expires.  It then puts kStopFlag in place of that chunk's wide
+  // flag (its own copy holds that flag) and posts the chunk in g_dec: the
+  // copying waves read it after the next barrier, the math waves see the flag
+  // in the step of that chunk, and all stop after that step.
+  int nce = nc;
+  if (!math && nc > 0) {
+    bool ok = true;
+    if (next_jc == 0) {
+      if (w == 0) ok = slab_ready(0);
+      advance_slab();
+    }
+    if (w == 0) {  // chunk 0: the first copying wave copies all of it
+      if (ok) {
+#pragma unroll
+        for (int ww = 0; ww < 4; ++ww) stage_dma<0>(wsh, ww, lane);
+      } else if (lane == 0) {
+        *reinterpret_cast<int*>(g_stage0 + WS_WIDE) = kStopFlag;
+      }
+      if (lane == 0) g_dec = ok ? -1 : 0;  // read by the others after the first B1
+    }
+    if (!ok) nce = 0;
     __builtin_amdgcn_s_waitcnt(0);  // chunk 0's operands land before the first B1
   }
 
@@ -863,7 +917,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
     // of the chunk's parity.
     const uint16_t* v16 = reinterpret_cast<const uint16_t*>(p.v);
     auto load_v = [&](int jc, uint4 (&r)[4]) {
-      const int c0 = (p.c_begin + jc) * kC;
+      const int c0 = (cb + jc) * kC;
       const int last = min(kC, T - c0) - 1;
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
@@ -875,7 +929,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       // The conv's halo of the first chunk goes where the previous chunk's last
       // tile would be: lanes 13..15 take the three raw tokens before the chunk,
       // from the sequence, the conv history, or zeros at the sequence start.
-      const int c0 = p.c_begin * kC;
+      const int c0 = cb * kC;
       const int th = c0 - 16 + max(i, 13);
       if (c0 > 0) {
         rv[1][3] = *reinterpret_cast<const uint4*>(v16 + (((size_t)b * T + th) * H + h) * kD + col0 + 8 * g);
@@ -895,7 +949,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       lds_barrier();  // B1
       f4 O[4][2], X[4][2];
       const unsigned char* sb = stage_buf<P>();
-      if (j < nc) {
+      if (j < nce) {
         // V = SiLU(conv(v)) in fp16 (the causal conv along the tokens of each
         // 16-lane row, the previous tile's raw values as the halo: for tile 0
         // the previous chunk's tile 3), moved into the C layout of X by a
@@ -951,7 +1005,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
             X[rt][ct] = mma_f16(vh[rt], ident_frag(g, i, ct), f4{0.f, 0.f, 0.f, 0.f});
             if constexpr (WANT_O) O[rt][ct] = f4{0.f, 0.f, 0.f, 0.f};
           }
-        if (j + 1 < nc) load_v(j + 1, rv[1 - P]);
+        if (j + 1 < nce) load_v(j + 1, rv[1 - P]);
         // X = V + (-(K e^G)) S and (Q e^G) S, one 32-row step of S at a time:
         // its B operands are rows 16(2k + s) + 4g + e, s = 0, 1
 #pragma unroll
@@ -977,7 +1031,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         }
       }
       lds_barrier();  // B2
-      if (j < nc) {
+      if (j < nce) {
         // U = T diag(beta) X, with X as B operands over tokens 32k' + 16s + 4g + e
         half8 Xb[2][2];
 #pragma unroll
@@ -1004,7 +1058,12 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
         // U as B operands over tokens 32k' + 16s + 4g + e; in a wide chunk also
         // the fp16 remainder U - Ub, so the two products below see U to about
         // 22 bits
-        const bool wide = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(sb + WS_WIDE)) != 0;
+        const int wflag = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const int*>(sb + WS_WIDE));
+        if (wflag == kStopFlag) {  // chunk j was not copied: stop before it
+          nce = j;
+          return;
+        }
+        const bool wide = wflag != 0;
         half8 Ub[2][2], Ul[2][2];
 #pragma unroll
         for (int kp = 0; kp < 2; ++kp)
@@ -1063,9 +1122,9 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
     };
     // both roles skip the loop (and its barriers) in a launch without chunks
     if (nc > 0) {
-      for (int j = 0; j <= nc; j += 2) {
+      for (int j = 0; j <= nce; j += 2) {
         step(std::integral_constant<int, 0>{}, j);
-        if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 1 <= nce) step(std::integral_constant<int, 1>{}, j + 1);
       }
     }
   } else {
@@ -1080,7 +1139,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
     // gate of the chunk normalised next, loaded one chunk ahead: [tt][s], 8 bf16
     uint4 gt[2][2];
     auto load_gate = [&](int jc) {
-      const int c0 = (p.c_begin + jc) * kC;
+      const int c0 = (cb + jc) * kC;
       const int nv = min(kC, T - c0);
 #pragma unroll
       for (int tt = 0; tt < 2; ++tt) {
@@ -1098,9 +1157,19 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       // No memory wait before B1: this wave's copy of chunk j was waited for
       // after B2 of the previous chunk, and its stores need no wait.
       lds_barrier();  // B1
-      if (j + 1 < nc) {
-        wait_slab(j + 1);
-        stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
+      if (j == 0 && w != 0 && __builtin_amdgcn_readfirstlane(g_dec) == 0) nce = 0;  // chunk 0 was not copied
+      if (j + 1 < nce) {
+        bool ok = true;
+        if (j + 1 == next_jc) {
+          ok = slab_ready(next_sl);
+          advance_slab();
+        }
+        if (ok) {
+          stage_dma<1 - P>(wsh + (size_t)(j + 1) * WS_CHUNK, w, lane);
+        } else if (w == 0 && lane == 0) {
+          *reinterpret_cast<int*>(stage_buf<1 - P>() + WS_WIDE) = kStopFlag;
+          g_dec = j + 1;
+        }
       }
       // ---- epilogue of chunk j-1 ----------------------------------------------------
       float ov[2][2][8], osig[2];
@@ -1118,12 +1187,13 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           }
       }
       lds_barrier();  // B2: O(j-1) is in registers
+      if (__builtin_amdgcn_readfirstlane(g_dec) == j + 1) nce = j + 1;  // the first copying wave stopped there
       // The copy of chunk j + 1 (it must land before B1 of chunk j + 1), the
       // gate loaded a chunk ago and the previous chunk's stores: one wait here,
       // before this chunk's stores, so that those are never waited on.
       __builtin_amdgcn_s_waitcnt(0);
       if (WANT_O && j >= 1) {
-        const int c0 = (p.c_begin + j - 1) * kC;
+        const int c0 = (cb + j - 1) * kC;
         const int nv = min(kC, T - c0);
 #pragma unroll
         for (int tt = 0; tt < 2; ++tt) {
@@ -1152,19 +1222,22 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           }
         }
       }
-      if (WANT_O && j >= 1 && j < nc) load_gate(j);
+      if (WANT_O && j >= 1 && j < nce) load_gate(j);
     };
     // both roles skip the loop (and its barriers) in a launch without chunks
     if (nc > 0) {
-      for (int j = 0; j <= nc; j += 2) {
+      for (int j = 0; j <= nce; j += 2) {
         step(std::integral_constant<int, 0>{}, j);
-        if (j + 1 <= nc) step(std::integral_constant<int, 1>{}, j + 1);
+        if (j + 1 <= nce) step(std::integral_constant<int, 1>{}, j + 1);
       }
     }
   }
 
   // ---- state and conv history out -------------------------------------------------
-  if (math && S_out != nullptr) {
+  // A workgroup that stopped early (nce < nc) leaves its state after chunk
+  // nce - 1 in S_out for the resume launch (none if it finished no chunk).
+  const bool stopped = nce < nc;
+  if (math && S_out != nullptr && (!stopped || nce > 0)) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
 #pragma unroll
@@ -1174,7 +1247,9 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
           S_out[(size_t)bh * kD * kD + (size_t)perm_row(16 * m + 4 * g + e) * kD + col0 + 16 * ct + i] =
               S[m][ct][e] * sig;
   }
-  if (!copy2 && p.conv_out != nullptr) {
+  if (p.slab_ready != nullptr && wave == 4 && lane == 0)  // a first launch (done = 0)
+    reinterpret_cast<int*>(const_cast<unsigned*>(p.slab_ready))[kSyncProgress + bh] = nce;
+  if (!copy2 && !stopped && p.conv_out != nullptr) {
     const size_t cch = (size_t)H * kNCh;
     for (int cl = tid; cl < kNCh; cl += 512) {
       const void* src = cl < kD ? p.q : cl < 2 * kD ? p.k : p.v;
@@ -1365,10 +1440,16 @@ int get_pipe(const kda_prefill_args& a, Pipe*& pp) {
   return KDA_OK;
 }
 
+// Test settings of the one-launch recurrence (kda_debug_pipeline): the bound
+// of its waits (0: kReadyWaitUs) and a slab whose flag is never set (-1: none).
+std::atomic<unsigned> g_dbg_wait_us{0};
+std::atomic<int> g_dbg_withhold{-1};
+
 // The flags of a one-launch recurrence: cleared on the caller's stream before
 // the pipeline forks, set one by one after each slab's intra-chunk kernel.
-__global__ void clear_flags_kernel(unsigned* f, int n) {
+__global__ void clear_flags_kernel(unsigned* f, int n, unsigned bound) {
   for (int i = threadIdx.x; i < n; i += blockDim.x) f[i] = 0u;
+  if (threadIdx.x == 0) f[kSyncBound] = bound;
 }
 __global__ void set_flag_kernel(unsigned* f) {
   if (threadIdx.x == 0) __hip_atomic_store(f, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
@@ -1396,16 +1477,25 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
   const char* what = "event";
   // Every slab resident at once: the chunk blocks of all slabs share one
   // head-major layout, and a single recurrence launch walks them all, waiting
-  // on a flag per slab (kept where the state carry would be, which this mode
-  // does not use) instead of a stream event before each slab's launch.
+  // on a flag per slab instead of a stream event before each slab's launch.
+  // The flags and each (b, h)'s count of finished chunks are kept where the
+  // state carry would be, which this mode does not use.  A resume launch after
+  // all slabs finishes what a workgroup left when its wait expired (at once
+  // when none did).
   // Not under stream capture: a graph may run its nodes in any order that
   // keeps their dependencies, also the recurrence before the slabs it waits on.
+  // S_T is where a stopped workgroup leaves its state for the resume launch.
   hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
-  const bool one_inter = piped && pl.nbuf == pl.nslabs && pl.nslabs > 1 &&
+  const bool one_inter = piped && pl.nbuf == pl.nslabs && pl.nslabs > 1 && pl.nslabs <= kMaxSlabs &&
+                         a.S_T != nullptr && pl.carry_bytes >= sync_bytes(a.B * a.H) &&
                          hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone;
   unsigned* flags = one_inter ? reinterpret_cast<unsigned*>(carry) : nullptr;
+  SplitParams resume{};
   if (one_inter) {
-    hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, st, flags, pl.nslabs);
+    const unsigned us = g_dbg_wait_us.load(std::memory_order_relaxed);
+    // the counter runs at 100 MHz; at most about 40 s
+    const unsigned ticks = 100u * std::min(us != 0 ? us : kReadyWaitUs, 40000000u);
+    hipLaunchKernelGGL(clear_flags_kernel, dim3(1), dim3(64), 0, st, flags, pl.nslabs, ticks);
     e = hipGetLastError();
     what = "flag clear launch";
   }
@@ -1445,7 +1535,7 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
       what = "intra-chunk launch";
     }
     if (one_inter) {
-      if (e == hipSuccess) {
+      if (e == hipSuccess && sl != g_dbg_withhold.load(std::memory_order_relaxed)) {
         hipLaunchKernelGGL(set_flag_kernel, dim3(1), dim3(64), 0, sa, flags + sl);
         e = hipGetLastError();
         what = "flag launch";
@@ -1455,9 +1545,11 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
       p.c_begin = 0;
       p.n_chunks = pl.nchunks;
       p.S_in = a.S0;
+      resume = p;
       p.slab_ready = flags;
       p.slab_ramp = pl.ramp;
       p.slab_per = pl.per_slab;
+      resume.resume = reinterpret_cast<const int*>(flags + kSyncProgress);
     } else if (e == hipSuccess && piped) {
       what = "event";
       e = hipEventRecord(pp->a_done[sl & 1], sa);
@@ -1485,6 +1577,12 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
       what = "event";
     }
   }
+  if (e == hipSuccess && one_inter) {
+    // after every slab: whatever a stopped workgroup left (nothing, normally)
+    hipLaunchKernelGGL((inter_chunk_kernel<OB, true>), dim3((unsigned)(a.B * a.H)), dim3(512), 0, st, resume);
+    e = hipGetLastError();
+    what = "resume launch";
+  }
   if (e != hipSuccess) {
     set_error("prefill: %s failed: %s", what, hipGetErrorString(e));
     return KDA_E_HIP;
@@ -1493,6 +1591,11 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
 }
 
 }  // namespace
+
+void debug_pipeline(unsigned wait_us, int withhold_slab) {
+  g_dbg_wait_us.store(wait_us, std::memory_order_relaxed);
+  g_dbg_withhold.store(withhold_slab, std::memory_order_relaxed);
+}
 
 int wait_timeouts(unsigned* count) {
   const hipError_t e = hipMemcpyFromSymbol(count, HIP_SYMBOL(g_wait_timeouts), sizeof(unsigned), 0,

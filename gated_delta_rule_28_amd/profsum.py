@@ -4,8 +4,9 @@
     python -m gated_delta_rule_28_amd.profsum traffic FETCH_CSV WRITE_CSV [--prefill-calls N] --cmd "..." --out FILE.md
     python -m gated_delta_rule_28_amd.profsum counters COUNTER_CSV --cmd "..." --out FILE.md
 
-A kda_prefill call on the two-kernel path launches the intra-chunk and the
-inter-chunk kernel once per slab of chunks, partly at the same time; with
+A kda_prefill call on the two-kernel path launches the intra-chunk kernel once
+per slab of chunks and the inter-chunk kernel once over all slabs (or once per
+slab when the slabs share buffers), partly at the same time; with
 --prefill-calls (the number of calls in the profiled run) `stats` adds the
 average span of a call (first start to last end of its kernels) and
 `traffic` the HBM bytes of a whole call.
@@ -75,8 +76,8 @@ def stats(path, cmd, out, trace=None, calls=0, top=8):
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     if trace:
         spans, per = call_spans(trace, calls)
-        lines += ["", f"kda_prefill calls: {calls}, {per} chunk-kernel launches each (intra-chunk and inter-chunk per "
-                  f"slab, overlapping); span of a call (first start to last end): average "
+        lines += ["", f"kda_prefill calls: {calls}, {per} chunk-kernel launches each (the intra-chunk kernel per slab and "
+                  f"the inter-chunk kernel, overlapping); span of a call (first start to last end): average "
                   f"{sum(spans) / len(spans) / 1e3:.1f} us, min {min(spans) / 1e3:.1f} us, max {max(spans) / 1e3:.1f} us."]
     open(out, "w").write("\n".join(lines) + "\n")
 

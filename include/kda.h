@@ -117,13 +117,17 @@ enum {
  * per-(b, h) kernel runs on a stream restricted to B*H (rounded up to 8)
  * compute units while the all-chunks kernels of the slabs run on two streams
  * restricted to the others.  When every slab has a workspace region of its
- * own (the size kda_prefill_workspace_bytes returns) and `stream` is not
- * capturing a graph, the per-(b, h) kernel is one launch over all slabs that
- * waits on a device flag per slab, set by a one-wave kernel queued after the
- * slab's all-chunks kernel; such a wait gives up after 10 s (counted by
- * kda_wait_timeouts; that call's outputs are then wrong), so the call always
- * ends.  Otherwise the per-(b, h) kernel is launched once per slab, after a
- * stream event, and the slabs go through up to three buffers in turn.
+ * own (the size kda_prefill_workspace_bytes returns), S_T is given and
+ * `stream` is not capturing a graph, the per-(b, h) kernel is one launch over
+ * all slabs that waits on a device flag per slab, set by a one-wave kernel
+ * queued after the slab's all-chunks kernel.  A wait is bounded (20 ms): a
+ * workgroup whose wait expires (the all-chunks kernels could not run beside
+ * it, e.g. kernels serialised by a profiler collecting counters) stops, leaves
+ * its state in S_T, and a second launch queued after every slab finishes its
+ * chunks, so the results do not depend on the timing (kda_wait_timeouts
+ * counts such stops).  Otherwise the per-(b, h) kernel is launched once per
+ * slab, after a stream event, and the slabs go through up to three buffers in
+ * turn.
  * The library creates these three streams (default priority) and their
  * events once per host thread, device and B*H, keeps them for the life of
  * the thread, starts them after the work already queued on `stream` and
@@ -441,10 +445,19 @@ int kda_abi_version(void);
 
 /* Bounded in-kernel waits that expired on the current device since the
  * library was loaded: the per-slab flags of a pipelined kda_prefill (see
- * there), whose producer did not run within 10 s, e.g. because other work held
- * its compute units.  Nonzero means some call's outputs are wrong.  Waits for
- * the device's work to finish.  Returns KDA_OK, KDA_E_NULL or KDA_E_HIP. */
+ * there) whose producer had not run within the bound.  Each one stopped a
+ * workgroup whose remaining chunks the call's second launch then ran (slower,
+ * same results).  Waits for the device's work to finish.  Returns KDA_OK,
+ * KDA_E_NULL or KDA_E_HIP. */
 int kda_wait_timeouts(unsigned* count);
+
+/* Test aid for that stop-and-resume path, for later kda_prefill calls from any
+ * thread: wait_limit_us replaces the 20 ms bound (0 restores it), and
+ * withhold_slab >= 0 makes the calls skip setting that slab's flag, so every
+ * workgroup's wait for it expires and the second launch finishes the work
+ * (-1: none).  (0, -1) restores normal operation.  Returns KDA_OK, or
+ * KDA_E_SHAPE for withhold_slab < -1. */
+int kda_debug_pipeline(unsigned wait_limit_us, int withhold_slab);
 
 /* kda_prefill for callers that cannot allocate device memory (code under HIP
  * graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same

@@ -39,7 +39,7 @@ def test_header_declares_the_abi():
                  "kda_status_string", "kda_last_error", "kda_abi_version", "kda_cp_compose", "kda_prefill_cp",
                  "kda_prefill_cp_workspace_bytes", "kda_prefill_backward", "kda_prefill_backward_workspace_bytes",
                  "kda_release", "kda_cp_fragments", "kda_cp_finish", "kda_cp_rank_workspace_bytes",
-                 "kda_wait_timeouts"):
+                 "kda_wait_timeouts", "kda_debug_pipeline"):
         assert must in names
 
 
@@ -121,6 +121,8 @@ def test_prefill_null_args_and_empty(kda):
     L = kda.lib()
     assert L.kda_prefill(None, None) == -1
     assert L.kda_wait_timeouts(None) == -1
+    assert L.kda_debug_pipeline(0, -2) == -2
+    assert L.kda_debug_pipeline(0, -1) == 0
     # T = 0 with nothing to carry: nothing to do, succeeds without a launch
     a = _prefill_args(kda, T=0, q=None, k=None, v=None, o=None)
     assert L.kda_prefill(ctypes.byref(a), None) == 0

@@ -152,6 +152,7 @@ def test_pipelined_slabs(oracle_mod, per_buf):
     7 slabs, a recurrence launch each (the state carried between them), so
     every buffer is reused."""
     torch, kda = need_gpu()
+    before = kda.wait_timeouts()
     w = Workload("pp", 1, 70 * 64, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=17)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
@@ -162,7 +163,7 @@ def test_pipelined_slabs(oracle_mod, per_buf):
                                                      device="cuda")
     o, S_T, c = _gpu_prefill(kda, dev, 64, workspace=ws)
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what=f"pipelined slabs, buffers of {per_buf or 35} chunks")
-    assert kda.wait_timeouts() == 0
+    assert kda.wait_timeouts() == before
 
 
 def test_pipelined_half_first_slab(oracle_mod):
@@ -170,6 +171,7 @@ def test_pipelined_half_first_slab(oracle_mod):
     one half-size), three regions of 64 chunks at the preferred workspace, one
     recurrence launch that finds each slab's first chunk from the slab plan."""
     torch, kda = need_gpu()
+    before = kda.wait_timeouts()
     w = Workload("pf", 1, 131 * 64 - 55, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=29)
     inp = syn.prefill_inputs_np(w)
     dev = to_dev(inp, "bf16")
@@ -177,7 +179,37 @@ def test_pipelined_half_first_slab(oracle_mod):
     assert kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv) == 3 * 64 * per_chunk + w.B * w.H * w.dk * w.dv * 4
     o, S_T, c = _gpu_prefill(kda, dev, 64)
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, what="half-size first slab")
-    assert kda.wait_timeouts() == 0
+    assert kda.wait_timeouts() == before
+
+
+@pytest.mark.parametrize("wait_us,withhold", [(200, 0), (200, 1), (200, 2), (1, -1)])
+def test_pipelined_stop_and_resume(oracle_mod, wait_us, withhold):
+    """The one-launch recurrence's stop-and-resume path, forced from the host
+    (kda_debug_pipeline).  With slab `withhold`'s flag never set, every
+    workgroup's bounded wait for it expires (after 200 us): the workgroup stops
+    before that slab, leaves its state in S_T, and the call's second launch
+    finishes from there.  With a 1 us bound and every flag set, the waits
+    expire wherever the intra-chunk kernel is not yet ahead.  131 chunks
+    (slabs of 32, 50 and 49, ragged), S and the conv history carried in place
+    (S_T aliases S0, conv_out aliases conv_in), against the oracle."""
+    torch, kda = need_gpu()
+    w = Workload("sr", 1, 131 * 64 - 55, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=31)
+    inp = syn.prefill_inputs_np(w)
+    dev = to_dev(inp, "bf16")
+    S = dev["S0"].clone()
+    conv = dev["conv_in"].clone()
+    before = kda.wait_timeouts()
+    kda.debug_pipeline(wait_us, withhold)
+    try:
+        o, _, _ = kda.prefill(dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"],
+                              S0=S, conv_in=conv, chunk=64, S_T=S, conv_out=conv)
+        torch.cuda.synchronize()
+    finally:
+        kda.debug_pipeline()
+    stops = kda.wait_timeouts() - before
+    if withhold >= 0:  # every workgroup waited for that slab in vain, once
+        assert stops == w.B * w.H, stops
+    _check_vs_oracle(oracle_mod, w, inp, o, S, conv, what=f"bound {wait_us} us, slab {withhold} withheld")
 
 
 @pytest.mark.parametrize("B,H,T", [(2, 3, 70 * 64 + 17), (1, 130, 66 * 64 + 5)])
