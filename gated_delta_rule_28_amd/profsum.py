@@ -51,17 +51,21 @@ def _short(name, n=90):
 
 def call_spans(trace, calls):
     """Spans (ns) of the prefill calls: the chunk kernels of the run, in start
-    order, split into `calls` equal groups (each call launches the same slabs)."""
+    order, split into `calls` equal groups (each call launches the same slabs);
+    and the durations (ns) of each call's inter-chunk dispatches in start order
+    (the recurrence launch, then the resume launch when there is one)."""
     ks = [r for r in csv.DictReader(open(trace)) if "chunk_kernel" in r["Kernel_Name"]]
     ks.sort(key=lambda r: int(r["Start_Timestamp"]))
     if calls <= 0 or len(ks) % calls:
         raise SystemExit(f"{trace}: {len(ks)} chunk-kernel dispatches do not split into {calls} calls")
     per = len(ks) // calls
-    spans = []
+    spans, inter = [], []
     for c in range(calls):
         g = ks[c * per:(c + 1) * per]
         spans.append(max(int(r["End_Timestamp"]) for r in g) - min(int(r["Start_Timestamp"]) for r in g))
-    return spans, per
+        inter.append([int(r["End_Timestamp"]) - int(r["Start_Timestamp"]) for r in g
+                      if "inter_chunk_kernel" in r["Kernel_Name"]])
+    return spans, per, inter
 
 
 def stats(path, cmd, out, trace=None, calls=0, top=8):
@@ -75,10 +79,18 @@ def stats(path, cmd, out, trace=None, calls=0, top=8):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f}% |")
     if trace:
-        spans, per = call_spans(trace, calls)
+        spans, per, inter = call_spans(trace, calls)
         lines += ["", f"kda_prefill calls: {calls}, {per} chunk-kernel launches each (the intra-chunk kernel per slab and "
                   f"the inter-chunk kernel, overlapping); span of a call (first start to last end): average "
                   f"{sum(spans) / len(spans) / 1e3:.1f} us, min {min(spans) / 1e3:.1f} us, max {max(spans) / 1e3:.1f} us."]
+        n_inter = {len(x) for x in inter}
+        if n_inter == {2}:
+            rec = [x[0] for x in inter]
+            res = [x[1] for x in inter]
+            lines += ["", "Inter-chunk dispatches of a call: the recurrence launch over all slabs, average "
+                      f"{sum(rec) / len(rec) / 1e3:.1f} us (min {min(rec) / 1e3:.1f}, max {max(rec) / 1e3:.1f}), "
+                      f"and the resume launch after the slabs, average {sum(res) / len(res) / 1e3:.1f} us (its "
+                      "workgroups exit at once when no wait expired); the per-kernel average above mixes the two."]
     open(out, "w").write("\n".join(lines) + "\n")
 
 
@@ -162,18 +174,29 @@ def traffic(fetch_csv, write_csv, cmd, out, json_out, calls=0):
 
 def counters(path, cmd, out, simds=1024):
     """Per-kernel means of the counters of one --pmc run (raw or derived, as
-    rocprofv3 reports them)."""
-    d, _ = _per_kernel(path)
+    rocprofv3 reports them), over the dispatches that did matrix-core work when
+    the run counts SQ_INSTS_VALU_MFMA_MOPS_F16 (counter collection serialises
+    kernels, so a one-launch recurrence stops at its first wait and its resume
+    launch does the work: the stopped dispatch would only dilute the means)."""
+    by = collections.defaultdict(lambda: collections.defaultdict(dict))
+    for r in csv.DictReader(open(path)):
+        by[r["Kernel_Name"]][r["Dispatch_Id"]][r["Counter_Name"]] = float(r["Counter_Value"])
     lines = ["# Compute counters per dispatch (rocprofv3 --pmc)", "", "Command:", "", "```", cmd, "```", ""]
     for key, (sub, _src) in KERNELS.items():
-        n = _match(d, sub)
+        n = _match(by, sub)
         if n is None:
             continue
-        c = {k: sum(v) / len(v) for k, v in d[n].items()}
+        disp = list(by[n].values())
+        mops = "SQ_INSTS_VALU_MFMA_MOPS_F16"
+        top = max((x.get(mops, 0.0) for x in disp), default=0.0)
+        used = [x for x in disp if top == 0.0 or x.get(mops, 0.0) > 0.01 * top]
+        names = sorted({k for x in used for k in x})
         lines.append(f"## `{_short(n)}`")
         lines.append("")
-        for k in sorted(c):
-            lines.append(f"- {k}: {c[k]:.6g}")
+        lines.append(f"- dispatches: {len(used)} of {len(disp)}")
+        for k in names:
+            v = [x[k] for x in used if k in x]
+            lines.append(f"- {k}: {sum(v) / len(v):.6g}")
         lines.append("")
     open(out, "w").write("\n".join(lines) + "\n")
 
