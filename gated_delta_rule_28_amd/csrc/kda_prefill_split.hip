@@ -806,7 +806,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   // wait expired.  The first copying wave's wait decides: the others wait 5 ms
   // longer, so theirs expires only if the first wave's did (they start within
   // microseconds of each other, after the same barrier).
-  auto slab_ready = [&](int sl) -> bool {
+  auto wait_for_slab = [&](int sl) -> bool {
     const unsigned* f = p.slab_ready + sl;
     const unsigned ticks = p.slab_ready[kSyncBound];
     const unsigned bound = w == 0 ? ticks : ticks + 500000u;
@@ -889,7 +889,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
   if (!math && nc > 0) {
     bool ok = true;
     if (next_jc == 0) {
-      if (w == 0) ok = slab_ready(0);
+      if (w == 0) ok = wait_for_slab(0);
       advance_slab();
     }
     if (w == 0) {  // chunk 0: the first copying wave copies all of it
@@ -1161,7 +1161,7 @@ __global__ __launch_bounds__(512, 1) void inter_chunk_kernel(SplitParams p) {
       if (j + 1 < nce) {
         bool ok = true;
         if (j + 1 == next_jc) {
-          ok = slab_ready(next_sl);
+          ok = wait_for_slab(next_sl);
           advance_slab();
         }
         if (ok) {
