@@ -165,6 +165,12 @@ def traffic(fetch_csv, write_csv, cmd, out, json_out, calls=0):
         rd, wr = tot_r / calls, tot_w / calls
         lines += ["", f"Whole kda_prefill call ({calls} calls in the run, all slabs of both chunk kernels): "
                   f"read {rd / 1e9:.3f} GB, written {wr / 1e9:.3f} GB, total {(rd + wr) / 1e9:.3f} GB per call."]
+        n_int = len(f_d[_match(f_d, KERNELS["inter_chunk_kernel"][0])]["FETCH_SIZE"])
+        if n_int == 2 * calls:
+            lines += ["", "Each call's two inter-chunk dispatches are the recurrence launch over all slabs and the "
+                      "resume launch. Counter collection serialises kernels, so the recurrence stops at its first "
+                      "slab wait and the resume launch does its work: the per-dispatch figures above are half a "
+                      "call's recurrence traffic; the per-call total is unaffected."]
         res["prefill_call"] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
                                "source_sha256_16": source_hash(os.path.join(CSRC, "kda_prefill_split.hip")),
                                "fetch_scale": f_scale, "write_scale": w_scale}
