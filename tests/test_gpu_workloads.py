@@ -53,6 +53,35 @@ def test_k3width_prefill_all_heads(oracle_mod):
     assert kda.wait_timeouts() == before
 
 
+@pytest.mark.timeout(300)
+def test_k3width_stop_and_resume_matches_uninterrupted():
+    """The K3-width call with the ninth slab's flag withheld (kda_debug_pipeline,
+    200 us bound): all 96 workgroups of the one recurrence launch stop before
+    that slab, park their state in S_T, and the resume launch finishes from
+    there.  Every output and the final state equal the uninterrupted call's to
+    1e-6 x RMS (the scale of each wave restarts at the resume, in powers of
+    two), which the oracle test above checks."""
+    torch, kda = need_gpu()
+    w = syn.WORKLOADS["k3width"]
+    dev = syn.prefill_inputs_torch(w, "cuda")
+    args = (dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"])
+    o1, S1, c1 = kda.prefill(*args, S0=dev["S0"], chunk=w.chunk)
+    before = kda.wait_timeouts()
+    kda.debug_pipeline(200, 8)
+    try:
+        o2, S2, c2 = kda.prefill(*args, S0=dev["S0"], chunk=w.chunk)
+        torch.cuda.synchronize()
+    finally:
+        kda.debug_pipeline()
+    assert kda.wait_timeouts() - before == w.B * w.H
+    rms = float(o1.float().pow(2).mean().sqrt())
+    d_o = float((o2 - o1).abs().max()) / rms
+    d_s = float((S2 - S1).abs().max()) / float(S1.pow(2).mean().sqrt())
+    print(f"  resumed vs uninterrupted: max|d o|/RMS {d_o:.2e}, max|d S_T|/RMS {d_s:.2e}", flush=True)
+    assert d_o <= 1e-6 and d_s <= 1e-6
+    assert torch.equal(c1, c2)
+
+
 @pytest.mark.timeout(600)
 def test_k3width_prefill_k3_logits_all_heads(oracle_mod):
     """The same workload with g and beta given as K3's logits (z ~ N(-4.7, 1),
