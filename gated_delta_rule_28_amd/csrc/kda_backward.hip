@@ -686,7 +686,11 @@ int run_backward_typed(const kda_prefill_backward_args& a, hipStream_t st) {
   // slabs from the last to the first; with no tokens, one reverse launch writes dS0 and dconv_in
   const int nslab = nch > 0 ? (nch + sl - 1) / sl : 1;
   BwdPipe* pp = nullptr;
-  if (nslab > 1) {
+  // under stream capture the slabs run on the caller's stream only (as for
+  // the prefill: no forks onto the compute-unit-restricted streams)
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
+  const bool capturing = hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+  if (nslab > 1 && !capturing) {
     const int rc = get_bwd_pipe((int)heads, pp);
     if (rc != KDA_OK) return rc;
   }

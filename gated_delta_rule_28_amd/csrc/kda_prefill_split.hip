@@ -1457,7 +1457,13 @@ __global__ void set_flag_kernel(unsigned* f) {
 
 template <bool OB, bool K3>
 int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
-  const SlabPlan pl = plan_slabs(a, a.workspace_bytes, pipe_ok);
+  // Under stream capture the slabs run one after the other on the caller's
+  // stream: no other streams, no events, no waits between kernels (a capture
+  // that forked onto the compute-unit-restricted streams crashed in the
+  // runtime's end of capture).
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
+  const bool capturing = hipStreamIsCapturing(st, &cap) != hipSuccess || cap != hipStreamCaptureStatusNone;
+  const SlabPlan pl = plan_slabs(a, a.workspace_bytes, pipe_ok && !capturing);
   const hipError_t e1 = hipFuncSetAttribute(reinterpret_cast<const void*>(&intra_chunk_kernel<K3>),
                                             hipFuncAttributeMaxDynamicSharedMemorySize, ALds::BYTES);
   if (e1 != hipSuccess) {
@@ -1482,13 +1488,9 @@ int run_split(const kda_prefill_args& a, hipStream_t st, bool pipe_ok) {
   // state carry would be, which this mode does not use.  A resume launch after
   // all slabs finishes what a workgroup left when its wait expired (at once
   // when none did).
-  // Not under stream capture: a graph may run its nodes in any order that
-  // keeps their dependencies, also the recurrence before the slabs it waits on.
   // S_T is where a stopped workgroup leaves its state for the resume launch.
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusActive;
   const bool one_inter = piped && pl.nbuf == pl.nslabs && pl.nslabs > 1 && pl.nslabs <= kMaxSlabs &&
-                         a.S_T != nullptr && pl.carry_bytes >= sync_bytes(a.B * a.H) &&
-                         hipStreamIsCapturing(st, &cap) == hipSuccess && cap == hipStreamCaptureStatusNone;
+                         a.S_T != nullptr && pl.carry_bytes >= sync_bytes(a.B * a.H);
   unsigned* flags = one_inter ? reinterpret_cast<unsigned*>(carry) : nullptr;
   SplitParams resume{};
   if (one_inter) {

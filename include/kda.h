@@ -127,7 +127,8 @@ enum {
  * chunks, so the results do not depend on the timing (kda_wait_timeouts
  * counts such stops).  Otherwise the per-(b, h) kernel is launched once per
  * slab, after a stream event, and the slabs go through up to three buffers in
- * turn.
+ * turn.  While `stream` is capturing a graph, nothing is forked: the slabs run
+ * one after the other on `stream` (as in kda_prefill_noalloc).
  * The library creates these three streams (default priority) and their
  * events once per host thread, device and B*H, keeps them for the life of
  * the thread, starts them after the work already queued on `stream` and
@@ -391,7 +392,8 @@ size_t kda_cp_rank_workspace_bytes(const kda_prefill_args* args);
  * and the slab walked back token by token (one
  * workgroup per (b, h)); the next slab's recompute runs on the other compute
  * units meanwhile (streams of the library's own, ordered after the work
- * already on `stream`, which in turn waits for them).  Workspace
+ * already on `stream`, which in turn waits for them; while `stream` is
+ * capturing a graph, everything runs on `stream`).  Workspace
  * (kda_prefill_backward_workspace_bytes, 16-byte aligned, required), with
  * n = ceil(T/32):
  * B*H*(n*dk*dv + dk*dv + 9*dk + 2*min(n, 32)*32*(dk*dv + 13*dk + 8))*4 bytes.

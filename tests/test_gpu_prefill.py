@@ -235,6 +235,42 @@ def test_slab_plans_at_other_shapes(oracle_mod, B, H, T):
     _check_vs_oracle(oracle_mod, w, inp, o, S_T, c, heads=pairs, what=f"B{B} H{H} T{T}")
 
 
+@pytest.mark.skip(reason="a capture that forked onto the library's CU-masked streams crashed (host "
+                         "segfault in the runtime's end of capture); the library now runs the slabs on the "
+                         "capturing stream alone, and capture stays off the GPU until that crash is understood")
+def test_prefill_in_captured_graph():
+    """kda_prefill captured in a HIP graph (torch.cuda.graph) at the preferred
+    workspace, 70 chunks (two pipelined slabs when not capturing).  Under
+    capture the slabs run one after the other on the capturing stream.  Three
+    replays, with eager work and a synchronisation between them, each equal
+    the eager call (one recurrence launch) bit for bit."""
+    torch, kda = need_gpu()
+    w = Workload("gr", 1, 70 * 64, 2, 128, 128, 64, "bf16", s0_sigma=0.05, conv_hist="normal", seed=51)
+    dev = to_dev(syn.prefill_inputs_np(w), "bf16")
+    args = (dev["q"], dev["k"], dev["v"], dev["conv_w"], dev["g"], dev["beta"], dev["gate"])
+    ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H, w.dk, w.dv), dtype=torch.uint8, device="cuda")
+    # the eager call also creates the library's streams before the capture
+    o_ref, S_ref, c_ref = kda.prefill(*args, S0=dev["S0"], conv_in=dev["conv_in"], workspace=ws)
+    torch.cuda.synchronize()
+    o, S, conv = torch.empty_like(o_ref), torch.empty_like(S_ref), torch.empty_like(c_ref)
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.graph(graph, stream=side):
+        kda.prefill(*args, S0=dev["S0"], conv_in=dev["conv_in"], o=o, S_T=S, conv_out=conv, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        o.zero_()
+        S.zero_()
+        conv.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o, o_ref), f"replay {rep}: o"
+        assert torch.equal(S, S_ref), f"replay {rep}: S_T"
+        assert torch.equal(conv, c_ref), f"replay {rep}: conv_out"
+
+
 def test_paths_agree(oracle_mod):
     """Both paths on the same inputs agree to well within the tolerance."""
     torch, kda = need_gpu()
