@@ -155,9 +155,11 @@ def cpu_model():
 def measured_peaks(torch):
     """This GPU's own peaks (libkda_peaks.so): a fetch-modify-write of 1.61 GB of
     fp32 with the decode step's access pattern (the decode state's size), swept
-    over workgroups per compute unit, and loops of fp16 16x16x32 matrix-core
-    instructions on register operands, swept over grid size and independent
-    chains.  The best of each sweep is reported; every point is listed."""
+    over workgroups per compute unit; the same blocks read and written in place
+    or copied to a second buffer by workgroups of 256, 512 or 1024 threads; and
+    loops of fp16 16x16x32 matrix-core instructions on register operands, swept
+    over grid size and independent chains.  The best of each sweep is reported;
+    every point is listed."""
     import ctypes
     path = os.path.join(ROOT, "gated_delta_rule_28_amd", "libkda_peaks.so")
     if not os.path.exists(path):
@@ -176,6 +178,20 @@ def measured_peaks(torch):
             run()
         ms = sorted(timed_launches(torch, run, 15))[7]
         fmw[f"lds{lds >> 10}k"] = 2 * nbytes / (ms * 1e-3) / 1e9
+    L.kda_peak_rw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    dst = torch.zeros_like(buf)
+    rw = {}
+    for mode in ("inplace", "copy"):
+        for threads in (256, 512, 1024):
+            d = buf if mode == "inplace" else dst
+            def run():
+                assert L.kda_peak_rw(ctypes.c_void_p(buf.data_ptr()), ctypes.c_void_p(d.data_ptr()), nbytes, threads,
+                                     stream) == 0
+            for _ in range(3):
+                run()
+            ms = sorted(timed_launches(torch, run, 15))[7]
+            rw[f"{mode}_t{threads}"] = 2 * nbytes / (ms * 1e-3) / 1e9
+    del dst
     L.kda_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     buf.zero_()
     one_way = {}
@@ -203,12 +219,15 @@ def measured_peaks(torch):
     return {"hbm_fetch_modify_write_gbs": max(fmw.values()), "hbm_fmw_sweep_gbs": fmw,
             "hbm_read_gbs": one_way["read"], "hbm_write_gbs": one_way["write"],
             "hbm_read_write_mix_gbs": mix,
-            "hbm_peak_gbs": max(max(fmw.values()), mix),
+            "hbm_read_write_gbs": max(rw.values()), "hbm_read_write_sweep_gbs": rw,
+            "hbm_peak_gbs": max(max(fmw.values()), mix, max(rw.values())),
             "mfma_f16_tflops": max(mfma.values()), "mfma_sweep_tflops": mfma,
             "how": "median launch time with HIP events: kda_peak_fmw over 1.61 GB (decode access pattern; "
                    "dynamic LDS caps workgroups per CU); kda_peak_stream read-only and write-only over the same "
-                   "blocks, combined as 2 / (1/read + 1/write) for an equal mix; kda_peak_mfma (workgroups x "
-                   "chains); hbm_peak_gbs is the larger of the fetch-modify-write and the mix"}
+                   "blocks, combined as 2 / (1/read + 1/write) for an equal mix; kda_peak_rw over the same blocks "
+                   "in place and as a copy to a second buffer, 256/512/1024-thread workgroups; kda_peak_mfma "
+                   "(workgroups x chains); hbm_peak_gbs is the largest of the fetch-modify-write, the mix and the "
+                   "read+write sweep"}
 
 
 FP32_VALU_PEAK_TFS = 157.3
@@ -630,6 +649,7 @@ def main():
         out["decode_multi"]["roofline"]["frac_of_measured"] = out["decode_multi"]["roofline"]["achieved"] / mh
     log(f"[bench] measured peaks: fetch-modify-write {peaks['hbm_fetch_modify_write_gbs']:.0f} GB/s, read "
         f"{peaks['hbm_read_gbs']:.0f}, write {peaks['hbm_write_gbs']:.0f}, read+write mix {peaks['hbm_read_write_mix_gbs']:.0f}"
+        f", read+write sweep {peaks['hbm_read_write_gbs']:.0f}"
         f" GB/s; fp16 matrix cores {mm:.0f} TFLOP/s")
 
     if not args.no_cpu:

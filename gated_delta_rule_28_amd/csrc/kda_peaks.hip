@@ -8,6 +8,10 @@
 //                     Bytes moved = 2 x block bytes per block.
 //   peak_read_kernel / peak_write_kernel  the same blocks read only (summed,
 //                     no store) or written only: each direction's ceiling.
+//   peak_rw_kernel    the same 64 KiB blocks with 256, 512 or 1024 threads per
+//                     block (16, 8 or 4 pieces per thread), either in place
+//                     (fetch-modify-write) or copied to a second buffer: the
+//                     read + write ceiling, swept over workgroup size.
 //   peak_mfma_kernel  back-to-back v_mfma_f32_16x16x32_f16 on register operands,
 //                     4 or 8 independent accumulators per wave, no memory
 //                     traffic inside the loop.  FLOP = blocks x 4 waves x iters
@@ -55,6 +59,21 @@ __global__ __launch_bounds__(kFmwThreads) void peak_write_kernel(float* buf, flo
   const f4 v = f4{a, a, a, a};
 #pragma unroll
   for (int i = 0; i < kFmwPieces; ++i) __builtin_nontemporal_store(v, p + i * kFmwThreads + threadIdx.x);
+}
+
+// One 64 KiB block per workgroup of NT threads: every thread requests its
+// 65536 / 16 / NT pieces first (non-temporal), then stores them, scaled in
+// place (src == dst) or unchanged into dst.
+template <int NT>
+__global__ __launch_bounds__(NT) void peak_rw_kernel(const float* src, float* dst, float a, float b) {
+  constexpr int NP = 65536 / 16 / NT;
+  const f4* p = reinterpret_cast<const f4*>(src) + (size_t)blockIdx.x * NT * NP;
+  f4* q = reinterpret_cast<f4*>(dst) + (size_t)blockIdx.x * NT * NP;
+  f4 s[NP];
+#pragma unroll
+  for (int i = 0; i < NP; ++i) s[i] = __builtin_nontemporal_load(p + i * NT + threadIdx.x);
+#pragma unroll
+  for (int i = 0; i < NP; ++i) __builtin_nontemporal_store(s[i] * a + b, q + i * NT + threadIdx.x);
 }
 
 constexpr int kMfmaThreads = 256;
@@ -110,6 +129,24 @@ int kda_peak_stream(float* buf, size_t bytes, int direction, void* stream) {
   const dim3 grid((unsigned)(bytes / block));
   if (direction == 0) hipLaunchKernelGGL(peak_read_kernel, grid, dim3(kFmwThreads), 0, s, buf, buf);
   else hipLaunchKernelGGL(peak_write_kernel, grid, dim3(kFmwThreads), 0, s, buf, 0.f);
+  return hipGetLastError() == hipSuccess ? 0 : -7;
+}
+
+int kda_peak_rw(const float* src, float* dst, size_t bytes, int threads, void* stream) {
+  const size_t block = 65536;
+  if (src == nullptr || dst == nullptr) return -1;
+  if (bytes == 0 || bytes % block != 0 || bytes / block > 0x7fffffffu) return -2;
+  if (threads != 256 && threads != 512 && threads != 1024) return -2;
+  if (((reinterpret_cast<uintptr_t>(src) | reinterpret_cast<uintptr_t>(dst)) & 15u) != 0) return -3;
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src), d0 = reinterpret_cast<uintptr_t>(dst);
+  if (s0 != d0 && s0 < d0 + bytes && d0 < s0 + bytes) return -2;  // partial overlap
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const dim3 grid((unsigned)(bytes / block));
+  // in place: the fetch-modify-write scale; copy: unchanged values
+  const float a = s0 == d0 ? 1.0000001f : 1.0f, b = s0 == d0 ? 1e-7f : 0.0f;
+  if (threads == 256) hipLaunchKernelGGL(peak_rw_kernel<256>, grid, dim3(256), 0, s, src, dst, a, b);
+  else if (threads == 512) hipLaunchKernelGGL(peak_rw_kernel<512>, grid, dim3(512), 0, s, src, dst, a, b);
+  else hipLaunchKernelGGL(peak_rw_kernel<1024>, grid, dim3(1024), 0, s, src, dst, a, b);
   return hipGetLastError() == hipSuccess ? 0 : -7;
 }
 

@@ -33,6 +33,15 @@ int kda_peak_fmw(float* buf, size_t bytes, int lds_bytes, void* stream);
  * bytes.  The two directions' rates bound any mix of reads and writes. */
 int kda_peak_stream(float* buf, size_t bytes, int direction, void* stream);
 
+/* Read + write ceiling: every 64 KiB block of `src` is read (sixteen 16-byte
+ * non-temporal loads per 256 threads) and written to the same offset of `dst`
+ * before its workgroup ends, by workgroups of `threads` threads (256, 512 or
+ * 1024).  src == dst: in place, dst[i] = src[i] * 1.0000001f + 1e-7f
+ * (fetch-modify-write); otherwise dst[i] = src[i] (copy), and the two buffers
+ * must not overlap.  Both device memory owned by the caller, 16-byte aligned;
+ * bytes a positive multiple of 65536.  HBM bytes moved: 2 * bytes. */
+int kda_peak_rw(const float* src, float* dst, size_t bytes, int threads, void* stream);
+
 /* `blocks` workgroups of four waves, each wave issuing chains * iters
  * v_mfma_f32_16x16x32_f16 in `chains` (4 or 8) independent accumulation chains
  * on register operands (no memory traffic in the loop); one fp32 per thread is

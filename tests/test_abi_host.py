@@ -304,7 +304,7 @@ def test_peaks_library_exports_its_header():
         pytest.skip("libkda_peaks.so not built")
     text = re.sub(r"/\*.*?\*/", "", open(os.path.join(os.path.dirname(HEADER), "kda_peaks.h")).read(), flags=re.S)
     names = set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(kda_\w+)\s*\(", text, flags=re.M))
-    assert names == {"kda_peak_fmw", "kda_peak_stream", "kda_peak_mfma"}
+    assert names == {"kda_peak_fmw", "kda_peak_stream", "kda_peak_rw", "kda_peak_mfma"}
     out = subprocess.run(["nm", "-D", "--defined-only", path], capture_output=True, text=True, check=True).stdout
     assert names <= set(re.findall(r" T (kda_\w+)", out))
     L = ctypes.CDLL(path)
@@ -316,6 +316,11 @@ def test_peaks_library_exports_its_header():
     assert L.kda_peak_fmw((1 << 20) + 4, 65536, 0, None) == -3
     L.kda_peak_stream.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
     assert L.kda_peak_stream(1 << 20, 65536, 2, None) == -2
+    L.kda_peak_rw.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int, ctypes.c_void_p]
+    assert L.kda_peak_rw(None, 1 << 20, 65536, 256, None) == -1
+    assert L.kda_peak_rw(1 << 20, 1 << 24, 65536, 128, None) == -2            # workgroup size
+    assert L.kda_peak_rw(1 << 20, (1 << 20) + 65536, 131072, 256, None) == -2  # partial overlap
+    assert L.kda_peak_rw((1 << 20) + 4, 1 << 24, 65536, 256, None) == -3
     assert L.kda_peak_mfma(None, 1, 1, 4, None) == -1
     assert L.kda_peak_mfma(1 << 20, 1, 1, 5, None) == -2
 
