@@ -140,18 +140,13 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   auto slot_st = [&](int l) { return slab + (size_t)l * L::STRETCH; };
   auto slot_rec = [&](int l) { return slab + (size_t)l * L::STRETCH + (size_t)kBwdChunk * D * D; };
 
-  __shared__ __attribute__((aligned(16))) float R[V::SIZE];   // the current token's record
-  __shared__ __attribute__((aligned(16))) float dus[D];
-  __shared__ float dkn[D];
+  // Reverse: token t's record in R[t % 3] (fields a, x~, q^, k^, y, u, dz,
+  // alpha, dq^ and the scalars nq, nk, rq, rk, -, beta, q~ . dq^), its du and
+  // dk^ in dus[t & 1] and dkn[t & 1]; red holds the row-group partials of du.
+  __shared__ __attribute__((aligned(16))) float R[3][V::SIZE];
+  __shared__ __attribute__((aligned(16))) float dus[2][D];
+  __shared__ float dkn[2][D];
   __shared__ __attribute__((aligned(16))) float red[RG][D];
-  float* const xa = R + V::A;
-  float* const xs = R + V::X;
-  float* const qn = R + V::QN;
-  float* const kn = R + V::KN;
-  float* const yv = R + V::Y;
-  float* const uv = R + V::U;
-  float* const al = R + V::AL;
-  float* const sc = R + V::SC;  // nq, nk, rq, rk, -, beta; [6], [7]: q~.dq^, k~.dk^
 
   auto rowidx = [&](int t) { return ((size_t)b * T + t) * H + h; };
   // global conv channel of head-local channel c (q | k | v)
@@ -401,6 +396,16 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   }
 
   // ---- 3. reverse over the slab's stretches (the records come from the recompute launch)
+  // Token t's step has a state side and a channel side.  The state side carries
+  // dS from token to token: dS += q^ dz^T, du = dS^T k^, dk^ = dS u + S' dy,
+  // dS' = dS + k^ dy^T, dg = rowsum(dS' * S'), dS <- Diag(alpha) dS'.  The
+  // channel side (the L2-norm, SiLU and conv-transpose backward of the token's
+  // q, k and v channels, and dbeta) needs only the token's record, du and dk^,
+  // and the conv ring, which it walks in token order.  So the loop runs the
+  // state side of token t and then the channel side of token t + 1: two
+  // barriers per token.  The buffers make that safe: R[t % 3] is rewritten
+  // two tokens after its channel side read it, dus / dkn[t & 1] one token
+  // after, each time with both barriers of a token in between.
   f4 dS[RPT];
   float ring[NCT][3];  // da of tokens t+1, t+2, t+3 for this thread's channels
   const bool first_slab = p.ch_hi >= nch;  // the slab holding the last token
@@ -420,6 +425,81 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     for (int k = 0; k < 3; ++k) ring[j][k] = !first_slab && c < NC ? carry[(size_t)D * D + (size_t)k * NC + c] : 0.f;
   }
 
+  // Gradients are stored one token late, after the next token's loads are
+  // issued (the counter is in order), so the store latency stays off the chain:
+  // dg of the token whose state side ran last (t_sd), and dq, dk, dv and dbeta
+  // of the token whose channel side ran last (t_cd).
+  int t_sd = -1, t_cd = -1;
+  float dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
+  // Each thread's gradient array, chosen once: chosen per store, the choice
+  // between the three kernel-argument pointers became a per-lane load of the
+  // argument block whose use waited for every memory operation in flight,
+  // the state loads just issued included.
+  float* dx_dst[NCT];
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) {
+    const int c = tid + NT * j;
+    dx_dst[j] = c < D ? p.dq + c : c < 2 * D ? p.dk + (c - D) : p.dv + (c - 2 * D);
+  }
+  auto flush = [&]() {
+    if (t_sd >= 0 && active && cg == 0) {
+      const size_t rw = rowidx(t_sd);
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
+    }
+    if (t_cd >= 0) {
+      const size_t rw = rowidx(t_cd);
+      if (tid == kDbetaWave * 64) p.dbeta[rw] = dbeta_def;
+#pragma unroll
+      for (int j = 0; j < NCT; ++j) {
+        const int c = tid + NT * j;
+        if (c < NC) dx_dst[j][rw * D] = dx_def[j];
+      }
+    }
+    t_sd = t_cd = -1;
+  };
+  const int wv = tid >> 6, ln = tid & 63;
+  // channel side of token tc (its state side has run and a barrier followed)
+  auto channel_side = [&](int tc) {
+    const float* Rc = R[tc % 3];
+    const float* dknc = dkn[tc & 1];
+    const float* dusc = dus[tc & 1];
+    const float* sc = Rc + V::SC;  // nq, nk, rq, rk, -, beta, q~ . dq^
+    // k~ . dk^, summed by every wave for itself
+    float bb = 0.f;
+    for (int c = ln; c < D; c += 64) bb += Rc[V::X + D + c] * dknc[c];
+    bb = group_sum<64>(bb);
+    if (wv == kDbetaWave) {
+      float db = 0.f;
+      for (int c = ln; c < D; c += 64) db += dusc[c] * (Rc[V::X + 2 * D + c] - Rc[V::Y + c]);
+      dbeta_def = group_sum<64>(db);
+    }
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      const int c = tid + NT * j;
+      if (c < NC) {
+        const float xc = Rc[V::X + c];
+        float dx;
+        if (c < D) dx = sc[2] * (Rc[V::DQ + c] - xc * sc[6] / sc[0]);
+        else if (c < 2 * D) dx = sc[3] * (dknc[c - D] - xc * bb / sc[1]);
+        else dx = sc[5] * dusc[c - 2 * D];
+        const float a = Rc[V::A + c];
+        const float sa = sigmoidf_(a);
+        const float da = dx * sa * (1.f + a * (1.f - sa));
+        const float4 w = wch[j];
+        float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
+        // the last three tokens are also conv_out's rows
+        if (p.dconv_out != nullptr && tc >= T - 3) dr += p.dconv_out[((size_t)b * 3 + (tc - (T - 3))) * cch + gch(c)];
+        dx_def[j] = dr;
+        ring[j][2] = ring[j][1];
+        ring[j][1] = ring[j][0];
+        ring[j][0] = da;
+      }
+    }
+    t_cd = tc;
+  };
+
+  int t_pend = -1;  // the token whose channel side comes next
   for (int ch = p.ch_hi - 1; ch >= p.ch_lo; --ch) {
     const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
     const float* st = slot_st(ch - p.ch_lo);
@@ -434,29 +514,12 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         pre[j] = i < V::SIZE ? vt[i] : 0.f;
       }
     }
-    // A token's gradients are stored after the next token's loads are issued
-    // (the counter is in order), so the store latency stays off the chain.
-    int t_def = -1;
-    float dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
-    auto flush = [&]() {
-      if (t_def < 0) return;
-      const size_t rw = rowidx(t_def);
-      if (tid == kDbetaWave * 64) p.dbeta[rw] = dbeta_def;
-      if (active && cg == 0) {
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
-      }
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const int c = tid + NT * j;
-        if (c < NC) (c < D ? p.dq : c < 2 * D ? p.dk : p.dv)[rw * D + (c % D)] = dx_def[j];
-      }
-    };
     for (int t = t1 - 1; t >= t0; --t) {
+      float* const Rt = R[t % 3];
 #pragma unroll
       for (int j = 0; j < NPRE; ++j) {
         const int i = tid + NT * j;
-        if (i < V::SIZE) R[i] = pre[j];
+        if (i < V::SIZE) Rt[i] = pre[j];
       }
       f4 prev[RPT];
       if (active) {
@@ -472,14 +535,16 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           pre[j] = i < V::SIZE ? vt[i] : 0.f;
         }
       }
-      flush();  // token t + 1's gradients
-      t_def = t;
+      flush();  // dg of token t + 1, the channel gradients of token t + 2
       lds_barrier();
+      const float* qn = Rt + V::QN;
+      const float* kn = Rt + V::KN;
+      const float* al = Rt + V::AL;
       // state side
       f4 sp[RPT];
       f4 dup = f4{0.f, 0.f, 0.f, 0.f};
       if (active) {
-        const f4 dz = *reinterpret_cast<const f4*>(&R[V::DZ + 4 * cg]);
+        const f4 dz = *reinterpret_cast<const f4*>(&Rt[V::DZ + 4 * cg]);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
@@ -489,16 +554,16 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         }
       }
       // du = dS^T k^: every thread sums the row groups' partials of its own
-      // columns (no second barrier); row group 0 keeps du for the later steps
+      // columns; row group 0 keeps du for the channel side
       if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = dup;
       lds_barrier();
       if (active) {
         f4 du = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
         for (int r = 0; r < RG; ++r) du += *reinterpret_cast<const f4*>(&red[r][4 * cg]);
-        if (rg == 0) *reinterpret_cast<f4*>(&dus[4 * cg]) = du;
-        const f4 u = *reinterpret_cast<const f4*>(&uv[4 * cg]);
-        const f4 dy = -sc[5] * du;
+        if (rg == 0) *reinterpret_cast<f4*>(&dus[t & 1][4 * cg]) = du;
+        const f4 u = *reinterpret_cast<const f4*>(&Rt[V::U + 4 * cg]);
+        const f4 dy = -Rt[V::SC + 5] * du;
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
@@ -509,51 +574,26 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           float gp = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
           kp = group_sum<CG>(kp);
           gp = group_sum<CG>(gp);
-          if (cg == 0) dkn[r] = kp;
+          if (cg == 0) dkn[t & 1][r] = kp;
           dg_def[i] = gp;  // rowsum(dS' * S'): alpha is inside S'
           dS[i] *= al[r];  // dS_{t-1}
         }
       }
-      lds_barrier();
-      // L2 norms (q~ . dq^ comes with the record) on wave 0, dbeta on wave 1 (or
-      // wave 0 after it with a single wave), SiLU, conv transpose
-      if (tid < 64) {
-        float bb = 0.f;
-        for (int c = tid; c < D; c += 64) bb += xs[D + c] * dkn[c];
-        bb = group_sum<64>(bb);
-        if (tid == 0) sc[7] = bb;
-      }
-      if (tid >= kDbetaWave * 64 && tid < kDbetaWave * 64 + 64) {
-        float db = 0.f;
-        for (int c = tid - kDbetaWave * 64; c < D; c += 64) db += dus[c] * (xs[2 * D + c] - yv[c]);
-        dbeta_def = group_sum<64>(db);
-      }
-      lds_barrier();
-#pragma unroll
-      for (int j = 0; j < NCT; ++j) {
-        const int c = tid + NT * j;
-        if (c < NC) {
-          float dx;
-          if (c < D) dx = sc[2] * (R[V::DQ + c] - xs[c] * sc[6] / sc[0]);
-          else if (c < 2 * D) dx = sc[3] * (dkn[c - D] - xs[c] * sc[7] / sc[1]);
-          else dx = sc[5] * dus[c - 2 * D];
-          const float a = xa[c];
-          const float sa = sigmoidf_(a);
-          const float da = dx * sa * (1.f + a * (1.f - sa));
-          const float4 w = wch[j];
-          float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
-          // the last three tokens are also conv_out's rows
-          if (p.dconv_out != nullptr && t >= T - 3) dr += p.dconv_out[((size_t)b * 3 + (t - (T - 3))) * cch + gch(c)];
-          dx_def[j] = dr;
-          ring[j][2] = ring[j][1];
-          ring[j][1] = ring[j][0];
-          ring[j][0] = da;
-        }
-      }
-      lds_barrier();  // R, dkn, dus are rewritten by the next token
+      t_sd = t;
+      // channel side of the later token (its du and dk^ were written before
+      // this token's first barrier)
+      if (t_pend >= 0) channel_side(t_pend);
+      t_pend = t;
     }
-    flush();
   }
+  // the channel side of the launch's last token, after the stores of the
+  // gradients still held (the channel side overwrites them)
+  if (t_pend >= 0) {
+    flush();
+    lds_barrier();
+    channel_side(t_pend);
+  }
+  flush();
   if (p.ch_lo > 0) {  // carry dS and the ring to the earlier slab
     if (active) {
 #pragma unroll
