@@ -431,6 +431,10 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   // of the token whose channel side ran last (t_cd).
   int t_sd = -1, t_cd = -1;
   float dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
+  // d = 128: the row sums of dk^ and dg are reduced together (see the state
+  // side), and lane cg ends with row rg + RG bfly_row of one of them
+  constexpr bool kButterfly = CG == 32 && RPT == 8;
+  const int bfly_row = 4 * ((cg >> 3) & 1) + 2 * ((cg >> 2) & 1) + ((cg >> 1) & 1);
   // Each thread's gradient array, chosen once: chosen per store, the choice
   // between the three kernel-argument pointers became a per-lane load of the
   // argument block whose use waited for every memory operation in flight,
@@ -442,10 +446,14 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     dx_dst[j] = c < D ? p.dq + c : c < 2 * D ? p.dk + (c - D) : p.dv + (c - 2 * D);
   }
   auto flush = [&]() {
-    if (t_sd >= 0 && active && cg == 0) {
+    if (t_sd >= 0 && active) {
       const size_t rw = rowidx(t_sd);
+      if constexpr (kButterfly) {
+        if ((cg & 17) == 16) p.dg[rw * D + rg + RG * bfly_row] = dg_def[0];
+      } else if (cg == 0) {
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
+        for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
+      }
     }
     if (t_cd >= 0) {
       const size_t rw = rowidx(t_cd);
@@ -500,9 +508,18 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   };
 
   int t_pend = -1;  // the token whose channel side comes next
+  // the state entering token t (stored by the recompute), requested a token
+  // ahead into prev_n
+  const int t_lo = p.ch_lo * kBwdChunk;
+  auto state_at = [&](int t) { return slot_st(t / kBwdChunk - p.ch_lo) + (size_t)(t % kBwdChunk) * D * D; };
+  f4 prev_n[RPT];
+  if (active && p.ch_hi > p.ch_lo) {
+    const float* src = state_at(min(T, p.ch_hi * kBwdChunk) - 1);
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
+  }
   for (int ch = p.ch_hi - 1; ch >= p.ch_lo; --ch) {
     const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
-    const float* st = slot_st(ch - p.ch_lo);
     const float* rec = slot_rec(ch - p.ch_lo);
     // the next token's record requested one token ahead
     float pre[NPRE];
@@ -522,10 +539,12 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         if (i < V::SIZE) Rt[i] = pre[j];
       }
       f4 prev[RPT];
-      if (active) {
-        const float* src = st + (size_t)(t - t0) * D * D;
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) prev[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
+      for (int i = 0; i < RPT; ++i) prev[i] = prev_n[i];
+      if (active && t - 1 >= t_lo) {
+        const float* src = state_at(t - 1);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
       }
       if (t > t0) {
         const float* vt = rec + (size_t)(t - 1 - t0) * V::SIZE;
@@ -564,6 +583,9 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         if (rg == 0) *reinterpret_cast<f4*>(&dus[t & 1][4 * cg]) = du;
         const f4 u = *reinterpret_cast<const f4*>(&Rt[V::U + 4 * cg]);
         const f4 dy = -Rt[V::SC + 5] * du;
+        // this thread's 4-column parts of dk^ and of rowsum(dS' * S') (alpha is
+        // inside S') for its rows, summed over the CG threads of the row group
+        float kps[RPT], gps[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
           const int r = rg + RG * i;
@@ -571,12 +593,36 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           float kp = dS[i].x * u.x + dS[i].y * u.y + dS[i].z * u.z + dS[i].w * u.w;
           kp += sp[i].x * dy.x + sp[i].y * dy.y + sp[i].z * dy.z + sp[i].w * dy.w;
           dS[i] += dy * kn[r];  // dS'
-          float gp = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
-          kp = group_sum<CG>(kp);
-          gp = group_sum<CG>(gp);
-          if (cg == 0) dkn[t & 1][r] = kp;
-          dg_def[i] = gp;  // rowsum(dS' * S'): alpha is inside S'
+          kps[i] = kp;
+          gps[i] = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
           dS[i] *= al[r];  // dS_{t-1}
+        }
+        if constexpr (kButterfly) {
+          // 16 sums over 32 lanes by recursive halving: at each exchange a lane
+          // keeps half of its values and adds its partner's copy of that half
+          // (partners lane ^ 16, ^ 15, ^ 7, ^ 2, then ^ 1 for the last value).
+          // Lane cg ends with the sum of value 8 b4 + bfly_row (bits b4..b1 of
+          // cg; value k < 8 is row k's dk^ part, k >= 8 row k - 8's dg part).
+          const bool b4 = cg & 16, b3 = cg & 8, b2 = cg & 4, b1 = cg & 2;
+          float a8[8], a4[4], a2[2];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            a8[k] = (b4 ? gps[k] : kps[k]) + __shfl_xor(b4 ? kps[k] : gps[k], 16, 64);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a4[k] = (b3 ? a8[k + 4] : a8[k]) + dpp_mov<0x140>(b3 ? a8[k] : a8[k + 4]);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) a2[k] = (b2 ? a4[k + 2] : a4[k]) + dpp_mov<0x141>(b2 ? a4[k] : a4[k + 2]);
+          float e = (b1 ? a2[1] : a2[0]) + dpp_mov<0x4E>(b1 ? a2[0] : a2[1]);
+          e += dpp_mov<0xB1>(e);
+          if (!b4 && !(cg & 1)) dkn[t & 1][rg + RG * bfly_row] = e;
+          dg_def[0] = e;
+        } else {
+#pragma unroll
+          for (int i = 0; i < RPT; ++i) {
+            const float kp = group_sum<CG>(kps[i]);
+            dg_def[i] = group_sum<CG>(gps[i]);
+            if (cg == 0) dkn[t & 1][rg + RG * i] = kp;
+          }
         }
       }
       t_sd = t;
