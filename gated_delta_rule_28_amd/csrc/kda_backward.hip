@@ -573,13 +573,23 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         }
       }
       // du = dS^T k^: every thread sums the row groups' partials of its own
-      // columns; row group 0 keeps du for the channel side
-      if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = dup;
+      // columns; row group 0 keeps du for the channel side.  With 32 column
+      // groups a wave holds two row groups of the same columns (lanes l and
+      // l + 32): they are added in the wave first, so half as many partials go
+      // through LDS.
+      constexpr int NRED = CG == 32 ? RG / 2 : RG;
+      if constexpr (CG == 32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dup[e] += __shfl_xor(dup[e], 32, 64);
+        if (active && (rg & 1) == 0) *reinterpret_cast<f4*>(&red[rg >> 1][4 * cg]) = dup;
+      } else {
+        if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = dup;
+      }
       lds_barrier();
       if (active) {
         f4 du = f4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 4
-        for (int r = 0; r < RG; ++r) du += *reinterpret_cast<const f4*>(&red[r][4 * cg]);
+        for (int r = 0; r < NRED; ++r) du += *reinterpret_cast<const f4*>(&red[r][4 * cg]);
         if (rg == 0) *reinterpret_cast<f4*>(&dus[t & 1][4 * cg]) = du;
         const f4 u = *reinterpret_cast<const f4*>(&Rt[V::U + 4 * cg]);
         const f4 dy = -Rt[V::SC + 5] * du;
