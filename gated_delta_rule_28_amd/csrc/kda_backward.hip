@@ -24,8 +24,8 @@
 // then the L2-norm, SiLU and conv backward (conv transpose over a 3-token ring
 // of the pre-SiLU gradients).  The state uses the decode kernel's layout:
 // thread (cg = tid % CG, rg = tid / CG) holds rows rg + RG i of the 4 columns
-// 4cg..4cg+3, so row sums are lane sums over the CG lanes of a row group and
-// column sums go through LDS.
+// 4cg..4cg+3 (the reverse's dS: rows RPT rg + i, consecutive), so row sums are
+// lane sums over the CG lanes of a row group and column sums go through LDS.
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -120,7 +120,8 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   constexpr int RPT = D / RG;
   using V = Rec<D>;
   constexpr int NPRE = (V::SIZE + NT - 1) / NT;  // record floats per thread
-  constexpr int kDbetaWave = NT > 64 ? 1 : 0;     // the wave that reduces dbeta
+  // the wave that reduces dbeta: the last one when it holds no conv channel
+  constexpr int kDbetaWave = NC <= NT - 64 ? NT / 64 - 1 : (NT > 64 ? 1 : 0);
 
   const int tid = threadIdx.x;
   const int bh = blockIdx.x;
@@ -412,7 +413,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   if (active) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i) {
-      const int r = rg + RG * i;
+      const int r = RPT * rg + i;
       const float* src = first_slab ? p.dS_T + (size_t)bh * D * D : carry;
       dS[i] = first_slab && p.dS_T == nullptr ? f4{0.f, 0.f, 0.f, 0.f}
                                               : *reinterpret_cast<const f4*>(src + (size_t)r * D + 4 * cg);
@@ -432,7 +433,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   int t_sd = -1, t_cd = -1;
   float dbeta_def = 0.f, dg_def[RPT], dx_def[NCT];
   // d = 128: the row sums of dk^ and dg are reduced together (see the state
-  // side), and lane cg ends with row rg + RG bfly_row of one of them
+  // side), and lane cg ends with row RPT rg + bfly_row of one of them
   constexpr bool kButterfly = CG == 32 && RPT == 8;
   const int bfly_row = 4 * ((cg >> 3) & 1) + 2 * ((cg >> 2) & 1) + ((cg >> 1) & 1);
   // Each thread's gradient array, chosen once: chosen per store, the choice
@@ -449,10 +450,10 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     if (t_sd >= 0 && active) {
       const size_t rw = rowidx(t_sd);
       if constexpr (kButterfly) {
-        if ((cg & 17) == 16) p.dg[rw * D + rg + RG * bfly_row] = dg_def[0];
+        if ((cg & 17) == 16) p.dg[rw * D + RPT * rg + bfly_row] = dg_def[0];
       } else if (cg == 0) {
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) p.dg[rw * D + rg + RG * i] = dg_def[i];
+        for (int i = 0; i < RPT; ++i) p.dg[rw * D + RPT * rg + i] = dg_def[i];
       }
     }
     if (t_cd >= 0) {
@@ -467,16 +468,22 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     t_sd = t_cd = -1;
   };
   const int wv = tid >> 6, ln = tid & 63;
+  // the wave holds k channels (channel c = tid + NT j)
+  bool kwave = false;
+#pragma unroll
+  for (int j = 0; j < NCT; ++j) kwave |= 64 * wv + NT * j < 2 * D && 64 * wv + NT * j + 64 > D;
   // channel side of token tc (its state side has run and a barrier followed)
   auto channel_side = [&](int tc) {
     const float* Rc = R[tc % 3];
     const float* dknc = dkn[tc & 1];
     const float* dusc = dus[tc & 1];
     const float* sc = Rc + V::SC;  // nq, nk, rq, rk, -, beta, q~ . dq^
-    // k~ . dk^, summed by every wave for itself
+    // k~ . dk^, summed by each wave that holds k channels, for itself
     float bb = 0.f;
-    for (int c = ln; c < D; c += 64) bb += Rc[V::X + D + c] * dknc[c];
-    bb = group_sum<64>(bb);
+    if (kwave) {
+      for (int c = ln; c < D; c += 64) bb += Rc[V::X + D + c] * dknc[c];
+      bb = group_sum<64>(bb);
+    }
     if (wv == kDbetaWave) {
       float db = 0.f;
       for (int c = ln; c < D; c += 64) db += dusc[c] * (Rc[V::X + 2 * D + c] - Rc[V::Y + c]);
@@ -507,6 +514,20 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     t_cd = tc;
   };
 
+  // The reverse holds rows RPT rg .. RPT rg + RPT - 1 of dS (consecutive, so
+  // the per-row values of a token come in 16-byte LDS reads).
+  auto rows_of = [&](const float* base, float (&out)[RPT]) {
+    if constexpr (RPT % 4 == 0) {
+#pragma unroll
+      for (int q4 = 0; q4 < RPT / 4; ++q4) {
+        const f4 v = *reinterpret_cast<const f4*>(base + RPT * rg + 4 * q4);
+        out[4 * q4] = v.x; out[4 * q4 + 1] = v.y; out[4 * q4 + 2] = v.z; out[4 * q4 + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) out[i] = base[RPT * rg + i];
+    }
+  };
   int t_pend = -1;  // the token whose channel side comes next
   // the state entering token t (stored by the recompute), requested a token
   // ahead into prev_n
@@ -516,7 +537,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   if (active && p.ch_hi > p.ch_lo) {
     const float* src = state_at(min(T, p.ch_hi * kBwdChunk) - 1);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
+    for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(RPT * rg + i) * D + 4 * cg);
   }
   for (int ch = p.ch_hi - 1; ch >= p.ch_lo; --ch) {
     const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
@@ -544,7 +565,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       if (active && t - 1 >= t_lo) {
         const float* src = state_at(t - 1);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(rg + RG * i) * D + 4 * cg);
+        for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(RPT * rg + i) * D + 4 * cg);
       }
       if (t > t0) {
         const float* vt = rec + (size_t)(t - 1 - t0) * V::SIZE;
@@ -556,20 +577,20 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
       }
       flush();  // dg of token t + 1, the channel gradients of token t + 2
       lds_barrier();
-      const float* qn = Rt + V::QN;
-      const float* kn = Rt + V::KN;
-      const float* al = Rt + V::AL;
-      // state side
+      // state side; alpha, q^ and k^ of this thread's RPT consecutive rows
+      float qn[RPT], kn[RPT], al[RPT];
+      rows_of(Rt + V::QN, qn);
+      rows_of(Rt + V::KN, kn);
+      rows_of(Rt + V::AL, al);
       f4 sp[RPT];
       f4 dup = f4{0.f, 0.f, 0.f, 0.f};
       if (active) {
         const f4 dz = *reinterpret_cast<const f4*>(&Rt[V::DZ + 4 * cg]);
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          const int r = rg + RG * i;
-          sp[i] = prev[i] * al[r];
-          dS[i] += dz * qn[r];
-          dup += dS[i] * kn[r];
+          sp[i] = prev[i] * al[i];
+          dS[i] += dz * qn[i];
+          dup += dS[i] * kn[i];
         }
       }
       // du = dS^T k^: every thread sums the row groups' partials of its own
@@ -598,14 +619,13 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         float kps[RPT], gps[RPT];
 #pragma unroll
         for (int i = 0; i < RPT; ++i) {
-          const int r = rg + RG * i;
           // dk^ = dS u + S' dy, with dS before the dy term
           float kp = dS[i].x * u.x + dS[i].y * u.y + dS[i].z * u.z + dS[i].w * u.w;
           kp += sp[i].x * dy.x + sp[i].y * dy.y + sp[i].z * dy.z + sp[i].w * dy.w;
-          dS[i] += dy * kn[r];  // dS'
+          dS[i] += dy * kn[i];  // dS'
           kps[i] = kp;
           gps[i] = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
-          dS[i] *= al[r];  // dS_{t-1}
+          dS[i] *= al[i];  // dS_{t-1}
         }
         if constexpr (kButterfly) {
           // 16 sums over 32 lanes by recursive halving: at each exchange a lane
@@ -624,14 +644,14 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
           for (int k = 0; k < 2; ++k) a2[k] = (b2 ? a4[k + 2] : a4[k]) + dpp_mov<0x141>(b2 ? a4[k] : a4[k + 2]);
           float e = (b1 ? a2[1] : a2[0]) + dpp_mov<0x4E>(b1 ? a2[0] : a2[1]);
           e += dpp_mov<0xB1>(e);
-          if (!b4 && !(cg & 1)) dkn[t & 1][rg + RG * bfly_row] = e;
+          if (!b4 && !(cg & 1)) dkn[t & 1][RPT * rg + bfly_row] = e;
           dg_def[0] = e;
         } else {
 #pragma unroll
           for (int i = 0; i < RPT; ++i) {
             const float kp = group_sum<CG>(kps[i]);
             dg_def[i] = group_sum<CG>(gps[i]);
-            if (cg == 0) dkn[t & 1][rg + RG * i] = kp;
+            if (cg == 0) dkn[t & 1][RPT * rg + i] = kp;
           }
         }
       }
@@ -654,7 +674,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     if (active) {
 #pragma unroll
       for (int i = 0; i < RPT; ++i)
-        *reinterpret_cast<f4*>(carry + (size_t)(rg + RG * i) * D + 4 * cg) = dS[i];
+        *reinterpret_cast<f4*>(carry + (size_t)(RPT * rg + i) * D + 4 * cg) = dS[i];
     }
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
@@ -671,7 +691,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
   if (p.dS0 != nullptr && active) {
 #pragma unroll
     for (int i = 0; i < RPT; ++i)
-      *reinterpret_cast<f4*>(p.dS0 + (size_t)bh * D * D + (size_t)(rg + RG * i) * D + 4 * cg) = dS[i];
+      *reinterpret_cast<f4*>(p.dS0 + (size_t)bh * D * D + (size_t)(RPT * rg + i) * D + 4 * cg) = dS[i];
   }
   if (p.dconv_in != nullptr) {
     // history row s + 3 (token s = -3..-1): sum over t = 0 .. s + 3 of w_{s-t+3} da_t
