@@ -89,14 +89,12 @@ struct Rec {
 };
 
 // Workspace, in floats: the stored states [BH][nch][D][D], the carry
-// [BH][D*D + 9D + 512] (dS, then the conv ring [3][3D], then a slot per thread
-// that the reverse's disabled stores go to), and two slab buffers
+// [BH][D*D + 9D] (dS, then the conv ring [3][3D]), and two slab buffers
 // [2][BH][slab stretches][kBwdChunk][D*D] states + [kBwdChunk][Rec SIZE]
 // records (one is recomputed into while the other is walked back).
 template <int D>
 struct BwdLayout {
-  static constexpr size_t SINK = (size_t)D * D + 9 * D;  // per-thread slots, never read
-  static constexpr size_t CARRY = SINK + 512;
+  static constexpr size_t CARRY = (size_t)D * D + 9 * D;
   static constexpr size_t STRETCH = (size_t)kBwdChunk * ((size_t)D * D + Rec<D>::SIZE);
   __host__ __device__ static int nch(int T) { return (T + kBwdChunk - 1) / kBwdChunk; }
   __host__ __device__ static int slab(int T) { return nch(T) < kBwdSlab ? nch(T) : kBwdSlab; }
@@ -469,50 +467,13 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     }
     t_sd = t_cd = -1;
   };
-  // In the loop every vector memory access is issued on every token, from
-  // every lane: a store that has nothing to store goes to the thread's sink
-  // slot, a load that is not needed reads a valid address.  The accesses per
-  // token are then the same on every path, so the compiler waits for exactly
-  // the access a value comes from (the counter is in order) instead of for
-  // every access in flight.
-  float* const sink = carry + L::SINK + tid;
-  auto flush_all = [&]() {
-    const size_t rs = rowidx(t_sd < 0 ? 0 : t_sd), rc = rowidx(t_cd < 0 ? 0 : t_cd);
-    if constexpr (kButterfly) {
-      const bool on = t_sd >= 0 && active && (cg & 17) == 16;
-      *(on ? p.dg + rs * D + RPT * rg + bfly_row : sink) = dg_def[0];
-    } else {
-#pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const bool on = t_sd >= 0 && active && cg == 0;
-        *(on ? p.dg + rs * D + RPT * rg + i : sink) = dg_def[i];
-      }
-    }
-    *(t_cd >= 0 && tid == kDbetaWave * 64 ? p.dbeta + rc : sink) = dbeta_def;
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int c = tid + NT * j;
-      *(t_cd >= 0 && c < NC ? dx_dst[j] + rc * D : sink) = dx_def[j];
-    }
-    t_sd = t_cd = -1;
-  };
   const int wv = tid >> 6, ln = tid & 63;
   // the wave holds k channels (channel c = tid + NT j)
   bool kwave = false;
 #pragma unroll
   for (int j = 0; j < NCT; ++j) kwave |= 64 * wv + NT * j < 2 * D && 64 * wv + NT * j + 64 > D;
   // channel side of token tc (its state side has run and a barrier followed)
-  // the gradient of token tc's raw row in conv_out (its last three tokens are
-  // also conv_out's rows), or an unused read of the sink slot
-  auto conv_out_grad = [&](int tc, float (&xo)[NCT]) {
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      const int c = tid + NT * j;
-      const bool on = p.dconv_out != nullptr && tc >= T - 3 && c < NC;
-      xo[j] = *(on ? p.dconv_out + ((size_t)b * 3 + (tc - (T - 3))) * cch + gch(c) : sink);
-    }
-  };
-  auto channel_side = [&](int tc, const float (&xo)[NCT]) {
+  auto channel_side = [&](int tc) {
     const float* Rc = R[tc % 3];
     const float* dknc = dkn[tc & 1];
     const float* dusc = dus[tc & 1];
@@ -543,7 +504,7 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
         const float4 w = wch[j];
         float dr = w.w * da + w.z * ring[j][0] + w.y * ring[j][1] + w.x * ring[j][2];
         // the last three tokens are also conv_out's rows
-        if (p.dconv_out != nullptr && tc >= T - 3) dr += xo[j];
+        if (p.dconv_out != nullptr && tc >= T - 3) dr += p.dconv_out[((size_t)b * 3 + (tc - (T - 3))) * cch + gch(c)];
         dx_def[j] = dr;
         ring[j][2] = ring[j][1];
         ring[j][1] = ring[j][0];
@@ -568,157 +529,145 @@ __global__ __launch_bounds__(bwd_threads<D>()) void backward_kernel(BwdParams p)
     }
   };
   int t_pend = -1;  // the token whose channel side comes next
-  // Tokens t_hi - 1 down to t_lo of the launch.  Token t's record is
-  // requested during token t + 1, first, and written to LDS at that token's
-  // end; the state entering token t is requested two tokens ahead, into the
-  // register set of the token's position (the loop is unrolled by two, so the
-  // sets alternate without copies).  Requests past t_lo read t_lo's again.
-  const int t_lo = p.ch_lo * kBwdChunk, t_hi = min(T, p.ch_hi * kBwdChunk);
-  const int rg_l = active ? rg : 0;  // inactive threads load a valid row
+  // the state entering token t (stored by the recompute), requested a token
+  // ahead into prev_n
+  const int t_lo = p.ch_lo * kBwdChunk;
   auto state_at = [&](int t) { return slot_st(t / kBwdChunk - p.ch_lo) + (size_t)(t % kBwdChunk) * D * D; };
-  auto rec_at = [&](int t) { return slot_rec(t / kBwdChunk - p.ch_lo) + (size_t)(t % kBwdChunk) * V::SIZE; };
-  auto load_state = [&](int t, f4 (&x)[RPT]) {
-    const float* src = state_at(t < t_lo ? t_lo : t);
+  f4 prev_n[RPT];
+  if (active && p.ch_hi > p.ch_lo) {
+    const float* src = state_at(min(T, p.ch_hi * kBwdChunk) - 1);
 #pragma unroll
-    for (int i = 0; i < RPT; ++i) x[i] = *reinterpret_cast<const f4*>(src + (size_t)(RPT * rg_l + i) * D + 4 * cg);
-  };
-  f4 st0[RPT], st1[RPT];
-  // everything requested so far (dS, the ring) has landed: inside the loop the
-  // compiler then counts only the loop's own accesses
-  __builtin_amdgcn_s_waitcnt(0);
-  if (t_hi > t_lo) {
-    const float* vt = rec_at(t_hi - 1);
-#pragma unroll
-    for (int j = 0; j < NPRE; ++j) {
-      const int i = tid + NT * j;
-      if (i < V::SIZE) R[(t_hi - 1) % 3][i] = vt[i];
-    }
-    load_state(t_hi - 1, st0);
-    load_state(t_hi - 2, st1);
+    for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(RPT * rg + i) * D + 4 * cg);
   }
-  auto step = [&](int t, f4 (&prev)[RPT]) {
-    float* const Rt = R[t % 3];
+  for (int ch = p.ch_hi - 1; ch >= p.ch_lo; --ch) {
+    const int t0 = ch * kBwdChunk, t1 = min(T, t0 + kBwdChunk);
+    const float* rec = slot_rec(ch - p.ch_lo);
+    // the next token's record requested one token ahead
     float pre[NPRE];
     {
-      const float* vt = rec_at(t - 1 < t_lo ? t_lo : t - 1);
+      const float* vt = rec + (size_t)(t1 - 1 - t0) * V::SIZE;
 #pragma unroll
       for (int j = 0; j < NPRE; ++j) {
         const int i = tid + NT * j;
-        pre[j] = vt[i < V::SIZE ? i : V::SIZE - 1];
+        pre[j] = i < V::SIZE ? vt[i] : 0.f;
       }
     }
-    float xo[NCT];
-    conv_out_grad(t_pend < 0 ? T : t_pend, xo);
-    flush_all();  // dg of token t + 1, the channel gradients of token t + 2
-    lds_barrier();
-    // state side; alpha, q^ and k^ of this thread's RPT consecutive rows
-    float qn[RPT], kn[RPT], al[RPT];
-    rows_of(Rt + V::QN, qn);
-    rows_of(Rt + V::KN, kn);
-    rows_of(Rt + V::AL, al);
-    f4 sp[RPT];
-    f4 dup = f4{0.f, 0.f, 0.f, 0.f};
-    if (active) {
-      const f4 dz = *reinterpret_cast<const f4*>(&Rt[V::DZ + 4 * cg]);
+    for (int t = t1 - 1; t >= t0; --t) {
+      float* const Rt = R[t % 3];
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        sp[i] = prev[i] * al[i];
-        dS[i] += dz * qn[i];
-        dup += dS[i] * kn[i];
+      for (int j = 0; j < NPRE; ++j) {
+        const int i = tid + NT * j;
+        if (i < V::SIZE) Rt[i] = pre[j];
       }
-    }
-    // the registers now take the state entering token t - 2
-    load_state(t - 2, prev);
-    // du = dS^T k^: every thread sums the row groups' partials of its own
-    // columns; row group 0 keeps du for the channel side.  With 32 column
-    // groups a wave holds two row groups of the same columns (lanes l and
-    // l + 32): they are added in the wave first, so half as many partials go
-    // through LDS.
-    constexpr int NRED = CG == 32 ? RG / 2 : RG;
-    if constexpr (CG == 32) {
+      f4 prev[RPT];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dup[e] += __shfl_xor(dup[e], 32, 64);
-      if (active && (rg & 1) == 0) *reinterpret_cast<f4*>(&red[rg >> 1][4 * cg]) = dup;
-    } else {
-      if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = dup;
-    }
-    lds_barrier();
-    if (active) {
-      f4 du = f4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 4
-      for (int r = 0; r < NRED; ++r) du += *reinterpret_cast<const f4*>(&red[r][4 * cg]);
-      if (rg == 0) *reinterpret_cast<f4*>(&dus[t & 1][4 * cg]) = du;
-      const f4 u = *reinterpret_cast<const f4*>(&Rt[V::U + 4 * cg]);
-      const f4 dy = -Rt[V::SC + 5] * du;
-      // this thread's 4-column parts of dk^ and of rowsum(dS' * S') (alpha is
-      // inside S') for its rows, summed over the CG threads of the row group
-      float kps[RPT], gps[RPT];
+      for (int i = 0; i < RPT; ++i) prev[i] = prev_n[i];
+      if (active && t - 1 >= t_lo) {
+        const float* src = state_at(t - 1);
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        // dk^ = dS u + S' dy, with dS before the dy term
-        float kp = dS[i].x * u.x + dS[i].y * u.y + dS[i].z * u.z + dS[i].w * u.w;
-        kp += sp[i].x * dy.x + sp[i].y * dy.y + sp[i].z * dy.z + sp[i].w * dy.w;
-        dS[i] += dy * kn[i];  // dS'
-        kps[i] = kp;
-        gps[i] = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
-        dS[i] *= al[i];  // dS_{t-1}
+        for (int i = 0; i < RPT; ++i) prev_n[i] = *reinterpret_cast<const f4*>(src + (size_t)(RPT * rg + i) * D + 4 * cg);
       }
-      if constexpr (kButterfly) {
-        // 16 sums over 32 lanes by recursive halving: at each exchange a lane
-        // keeps half of its values and adds its partner's copy of that half
-        // (partners lane ^ 16, ^ 15, ^ 7, ^ 2, then ^ 1 for the last value).
-        // Lane cg ends with the sum of value 8 b4 + bfly_row (bits b4..b1 of
-        // cg; value k < 8 is row k's dk^ part, k >= 8 row k - 8's dg part).
-        const bool b4 = cg & 16, b3 = cg & 8, b2 = cg & 4, b1 = cg & 2;
-        float a8[8], a4[4], a2[2];
+      if (t > t0) {
+        const float* vt = rec + (size_t)(t - 1 - t0) * V::SIZE;
 #pragma unroll
-        for (int k = 0; k < 8; ++k)
-          a8[k] = (b4 ? gps[k] : kps[k]) + __shfl_xor(b4 ? kps[k] : gps[k], 16, 64);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) a4[k] = (b3 ? a8[k + 4] : a8[k]) + dpp_mov<0x140>(b3 ? a8[k] : a8[k + 4]);
-#pragma unroll
-        for (int k = 0; k < 2; ++k) a2[k] = (b2 ? a4[k + 2] : a4[k]) + dpp_mov<0x141>(b2 ? a4[k] : a4[k + 2]);
-        float e = (b1 ? a2[1] : a2[0]) + dpp_mov<0x4E>(b1 ? a2[0] : a2[1]);
-        e += dpp_mov<0xB1>(e);
-        if (!b4 && !(cg & 1)) dkn[t & 1][RPT * rg + bfly_row] = e;
-        dg_def[0] = e;
-      } else {
-#pragma unroll
-        for (int i = 0; i < RPT; ++i) {
-          const float kp = group_sum<CG>(kps[i]);
-          dg_def[i] = group_sum<CG>(gps[i]);
-          if (cg == 0) dkn[t & 1][RPT * rg + i] = kp;
+        for (int j = 0; j < NPRE; ++j) {
+          const int i = tid + NT * j;
+          pre[j] = i < V::SIZE ? vt[i] : 0.f;
         }
       }
-    }
-    t_sd = t;
-    // channel side of the later token (its du and dk^ were written before
-    // this token's first barrier)
-    if (t_pend >= 0) channel_side(t_pend, xo);
-    t_pend = t;
-    // the next token's record (R[(t - 1) % 3] was last read two tokens ago)
-    if (t > t_lo) {
+      flush();  // dg of token t + 1, the channel gradients of token t + 2
+      lds_barrier();
+      // state side; alpha, q^ and k^ of this thread's RPT consecutive rows
+      float qn[RPT], kn[RPT], al[RPT];
+      rows_of(Rt + V::QN, qn);
+      rows_of(Rt + V::KN, kn);
+      rows_of(Rt + V::AL, al);
+      f4 sp[RPT];
+      f4 dup = f4{0.f, 0.f, 0.f, 0.f};
+      if (active) {
+        const f4 dz = *reinterpret_cast<const f4*>(&Rt[V::DZ + 4 * cg]);
 #pragma unroll
-      for (int j = 0; j < NPRE; ++j) {
-        const int i = tid + NT * j;
-        if (i < V::SIZE) R[(t - 1) % 3][i] = pre[j];
+        for (int i = 0; i < RPT; ++i) {
+          sp[i] = prev[i] * al[i];
+          dS[i] += dz * qn[i];
+          dup += dS[i] * kn[i];
+        }
       }
+      // du = dS^T k^: every thread sums the row groups' partials of its own
+      // columns; row group 0 keeps du for the channel side.  With 32 column
+      // groups a wave holds two row groups of the same columns (lanes l and
+      // l + 32): they are added in the wave first, so half as many partials go
+      // through LDS.
+      constexpr int NRED = CG == 32 ? RG / 2 : RG;
+      if constexpr (CG == 32) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) dup[e] += __shfl_xor(dup[e], 32, 64);
+        if (active && (rg & 1) == 0) *reinterpret_cast<f4*>(&red[rg >> 1][4 * cg]) = dup;
+      } else {
+        if (active) *reinterpret_cast<f4*>(&red[rg][4 * cg]) = dup;
+      }
+      lds_barrier();
+      if (active) {
+        f4 du = f4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 4
+        for (int r = 0; r < NRED; ++r) du += *reinterpret_cast<const f4*>(&red[r][4 * cg]);
+        if (rg == 0) *reinterpret_cast<f4*>(&dus[t & 1][4 * cg]) = du;
+        const f4 u = *reinterpret_cast<const f4*>(&Rt[V::U + 4 * cg]);
+        const f4 dy = -Rt[V::SC + 5] * du;
+        // this thread's 4-column parts of dk^ and of rowsum(dS' * S') (alpha is
+        // inside S') for its rows, summed over the CG threads of the row group
+        float kps[RPT], gps[RPT];
+#pragma unroll
+        for (int i = 0; i < RPT; ++i) {
+          // dk^ = dS u + S' dy, with dS before the dy term
+          float kp = dS[i].x * u.x + dS[i].y * u.y + dS[i].z * u.z + dS[i].w * u.w;
+          kp += sp[i].x * dy.x + sp[i].y * dy.y + sp[i].z * dy.z + sp[i].w * dy.w;
+          dS[i] += dy * kn[i];  // dS'
+          kps[i] = kp;
+          gps[i] = dS[i].x * sp[i].x + dS[i].y * sp[i].y + dS[i].z * sp[i].z + dS[i].w * sp[i].w;
+          dS[i] *= al[i];  // dS_{t-1}
+        }
+        if constexpr (kButterfly) {
+          // 16 sums over 32 lanes by recursive halving: at each exchange a lane
+          // keeps half of its values and adds its partner's copy of that half
+          // (partners lane ^ 16, ^ 15, ^ 7, ^ 2, then ^ 1 for the last value).
+          // Lane cg ends with the sum of value 8 b4 + bfly_row (bits b4..b1 of
+          // cg; value k < 8 is row k's dk^ part, k >= 8 row k - 8's dg part).
+          const bool b4 = cg & 16, b3 = cg & 8, b2 = cg & 4, b1 = cg & 2;
+          float a8[8], a4[4], a2[2];
+#pragma unroll
+          for (int k = 0; k < 8; ++k)
+            a8[k] = (b4 ? gps[k] : kps[k]) + __shfl_xor(b4 ? kps[k] : gps[k], 16, 64);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a4[k] = (b3 ? a8[k + 4] : a8[k]) + dpp_mov<0x140>(b3 ? a8[k] : a8[k + 4]);
+#pragma unroll
+          for (int k = 0; k < 2; ++k) a2[k] = (b2 ? a4[k + 2] : a4[k]) + dpp_mov<0x141>(b2 ? a4[k] : a4[k + 2]);
+          float e = (b1 ? a2[1] : a2[0]) + dpp_mov<0x4E>(b1 ? a2[0] : a2[1]);
+          e += dpp_mov<0xB1>(e);
+          if (!b4 && !(cg & 1)) dkn[t & 1][RPT * rg + bfly_row] = e;
+          dg_def[0] = e;
+        } else {
+#pragma unroll
+          for (int i = 0; i < RPT; ++i) {
+            const float kp = group_sum<CG>(kps[i]);
+            dg_def[i] = group_sum<CG>(gps[i]);
+            if (cg == 0) dkn[t & 1][RPT * rg + i] = kp;
+          }
+        }
+      }
+      t_sd = t;
+      // channel side of the later token (its du and dk^ were written before
+      // this token's first barrier)
+      if (t_pend >= 0) channel_side(t_pend);
+      t_pend = t;
     }
-  };
-  int t = t_hi - 1;
-  for (; t - 1 >= t_lo; t -= 2) {
-    step(t, st0);
-    step(t - 1, st1);
   }
-  if (t == t_lo) step(t, st0);
   // the channel side of the launch's last token, after the stores of the
   // gradients still held (the channel side overwrites them)
   if (t_pend >= 0) {
     flush();
     lds_barrier();
-    float xo[NCT];
-    conv_out_grad(t_pend, xo);
-    channel_side(t_pend, xo);
+    channel_side(t_pend);
   }
   flush();
   if (p.ch_lo > 0) {  // carry dS and the ring to the earlier slab

@@ -262,9 +262,9 @@ def test_prefill_backward_validation_and_workspace(kda):
         a = kda.PrefillBackwardArgs(**{**base, **over})
         assert L.kda_prefill_backward(ctypes.byref(a), None) == code, over
     assert L.kda_prefill_backward(None, None) == -1
-    # n d^2 + d^2 + 9 d + 512 + 2 min(n, 32) 32 (d^2 + 13 d + 8) floats per (b, h), n = ceil(T/32)
+    # n d^2 + d^2 + 9 d + 2 min(n, 32) 32 (d^2 + 13 d + 8) floats per (b, h), n = ceil(T/32)
     a = kda.PrefillBackwardArgs(**base)
-    want = 2 * 3 * (4 * 32 * 32 + 32 * 32 + 9 * 32 + 512 + 2 * 4 * 32 * (32 * 32 + 13 * 32 + 8)) * 4
+    want = 2 * 3 * (4 * 32 * 32 + 32 * 32 + 9 * 32 + 2 * 4 * 32 * (32 * 32 + 13 * 32 + 8)) * 4
     assert L.kda_prefill_backward_workspace_bytes(ctypes.byref(a)) == want
     assert L.kda_prefill_backward_workspace_bytes(None) == 0
 
