@@ -1,0 +1,126 @@
+"""CPU model (float64 NumPy) of a chunkwise backward of the KDA recurrence core,
+per (b, h): the gradients reach every chunk through one reverse recurrence of
+the state gradient over chunks, and each chunk's gradients are matrix products
+over the chunk, the shape a matrix-core kernel takes (the chunkwise form of
+the forward run in reverse, instead of a token-by-token walk).  It uses no
+autograd; tests/test_chunk_backward_model.py compares it with torch autograd of
+the token-serial core.
+
+Core of the recurrence ("Kimi K3, previewed", section "Kimi Delta Attention -
+the workhorse": fine-grained per-channel decay with the delta rule), per token
+t with q^, k^, v^ given (after the conv, SiLU and norms):
+  S' = Diag(e^{g_t}) S_{t-1},  u_t = beta_t (v^_t - S'^T k^_t),
+  S_t = S' + k^_t u_t^T,       o_t = S_t^T q^_t.
+Chunk of C tokens entering with S_in, G the chunk-local inclusive cumulative
+sum of g (per channel), G_C its last row:
+  F = K e^G,  Qg = Q e^G,  H = K e^{G_C - G}            (all factors <= 1)
+  A_ij = beta_i sum_c k_ic k_jc e^{G_ic - G_jc}   (j < i),  T = (I + A)^-1
+  P_ij = sum_c q_ic k_jc e^{G_ic - G_jc}          (j <= i)
+  W = diag(beta) (V - F S_in),  U = T W
+  O = Qg S_in + P U,  S_out = Diag(e^{G_C}) S_in + H^T U.
+Reverse of one chunk, given dO and dS_out:
+  dU = P^T dO + H dS_out,  dW = T^T dU,  dT = dU W^T,  dA = -T^T dT T^T (j < i),
+  dP = dO U^T (j <= i),  dV = diag(beta) dW,  dbeta = rowsum(dW * (V - F S_in)) + ...,
+  dF = -diag(beta) dW S_in^T,  dQg = dO S_in^T,  dH = U dS_out^T,
+  dS_in = Qg^T dO + Diag(e^{G_C}) dS_out + F^T (-diag(beta) dW),
+then through A, P, F, Qg, H and Diag(e^{G_C}) to q, k, beta and G, and from G to
+g by the reverse cumulative sum (G_C depends on every g of the chunk).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _chunk_terms(q, k, v, g, beta, S_in):
+    """Forward quantities of one chunk (rows = tokens)."""
+    C = q.shape[0]
+    G = np.cumsum(g, axis=0)
+    GC = G[-1]
+    E = np.exp(G[:, None, :] - G[None, :, :])         # [i, j, c] e^{G_i - G_j}
+    low = np.tril(np.ones((C, C)), -1)                  # j < i
+    lowd = np.tril(np.ones((C, C)))                     # j <= i
+    Ap = np.einsum("ic,jc,ijc->ij", k, k, E) * low      # A' (without beta)
+    A = beta[:, None] * Ap
+    P = np.einsum("ic,jc,ijc->ij", q, k, E) * lowd
+    T = np.linalg.inv(np.eye(C) + A)
+    F = k * np.exp(G)
+    Qg = q * np.exp(G)
+    H = k * np.exp(GC[None, :] - G)
+    R = v - F @ S_in                                    # V - F S_in
+    W = beta[:, None] * R
+    U = T @ W
+    O = Qg @ S_in + P @ U
+    S_out = np.exp(GC)[:, None] * S_in + H.T @ U
+    return dict(G=G, GC=GC, E=E, low=low, lowd=lowd, Ap=Ap, A=A, P=P, T=T, F=F, Qg=Qg, H=H, R=R, W=W, U=U,
+                O=O, S_out=S_out)
+
+
+def forward(q, k, v, g, beta, S0, C=64):
+    """Chunkwise forward of the core over T tokens: O [T, dv], S_T, and the
+    state entering every chunk."""
+    Tn = q.shape[0]
+    S = S0.copy()
+    O = np.zeros((Tn, v.shape[1]))
+    states = []
+    for c0 in range(0, Tn, C):
+        sl = slice(c0, min(Tn, c0 + C))
+        states.append(S.copy())
+        f = _chunk_terms(q[sl], k[sl], v[sl], g[sl], beta[sl], S)
+        O[sl] = f["O"]
+        S = f["S_out"]
+    return O, S, states
+
+
+def _chunk_backward(q, k, v, g, beta, S_in, dO, dS_out):
+    """Gradients of one chunk's (O, S_out) map; returns dq, dk, dv, dg, dbeta, dS_in."""
+    f = _chunk_terms(q, k, v, g, beta, S_in)
+    T, P, U, W, R, E, H, F, Qg = f["T"], f["P"], f["U"], f["W"], f["R"], f["E"], f["H"], f["F"], f["Qg"]
+    G, GC = f["G"], f["GC"]
+    # through U = T W, O = Qg S_in + P U, S_out = Diag(e^{G_C}) S_in + H^T U
+    dU = P.T @ dO + H @ dS_out
+    dW = T.T @ dU
+    dT = dU @ W.T
+    dA = -(T.T @ dT @ T.T) * f["low"]
+    dP = (dO @ U.T) * f["lowd"]
+    dR = beta[:, None] * dW
+    dbeta = np.sum(dW * R, axis=1) + np.sum(dA * f["Ap"], axis=1)
+    dv = dR.copy()
+    dF = -dR @ S_in.T
+    dQg = dO @ S_in.T
+    dH = U @ dS_out.T
+    dS_in = Qg.T @ dO + np.exp(GC)[:, None] * dS_out - F.T @ dR
+    dGC = np.exp(GC) * np.sum(dS_out * S_in, axis=1)
+    # through A_ij = beta_i sum_c k_ic k_jc E_ijc and P_ij = sum_c q_ic k_jc E_ijc
+    dAb = dA * beta[:, None]                               # d/dA'
+    dq = np.einsum("ij,jc,ijc->ic", dP, k, E)
+    dk = (np.einsum("ij,jc,ijc->ic", dAb, k, E) + np.einsum("ij,ic,ijc->jc", dAb, k, E)
+          + np.einsum("ij,ic,ijc->jc", dP, q, E))
+    # G enters E with + at row i and - at column j
+    tA = np.einsum("ij,ic,jc,ijc->ijc", dAb, k, k, E)
+    tP = np.einsum("ij,ic,jc,ijc->ijc", dP, q, k, E)
+    dG = tA.sum(axis=1) - tA.sum(axis=0) + tP.sum(axis=1) - tP.sum(axis=0)
+    # through F = K e^G, Qg = Q e^G, H = K e^{G_C - G}
+    eG = np.exp(G)
+    dk += dF * eG + dH * np.exp(GC[None, :] - G)
+    dq += dQg * eG
+    dG += dF * F + dQg * Qg - dH * H
+    dGC += np.sum(dH * H, axis=0)
+    # G = cumsum(g) within the chunk; G_C = G[-1] depends on every g
+    dg = np.cumsum(dG[::-1], axis=0)[::-1] + dGC[None, :]
+    return dq, dk, dv, dg, dbeta, dS_in
+
+
+def backward(q, k, v, g, beta, S0, dO, dS_T, C=64):
+    """Gradients of <dO, O> + <dS_T, S_T> with respect to q, k, v, g, beta, S0,
+    chunk by chunk from the last (one state per chunk kept by the forward)."""
+    Tn = q.shape[0]
+    _, _, states = forward(q, k, v, g, beta, S0, C)
+    dq, dk, dv, dg = (np.zeros_like(q), np.zeros_like(k), np.zeros_like(v), np.zeros_like(g))
+    dbeta = np.zeros_like(beta)
+    dS = dS_T.copy()
+    starts = list(range(0, Tn, C))
+    for n in range(len(starts) - 1, -1, -1):
+        sl = slice(starts[n], min(Tn, starts[n] + C))
+        dq[sl], dk[sl], dv[sl], dg[sl], dbeta[sl], dS = _chunk_backward(
+            q[sl], k[sl], v[sl], g[sl], beta[sl], states[n], dO[sl], dS)
+    return dict(q=dq, k=dk, v=dv, g=dg, beta=dbeta, S0=dS)

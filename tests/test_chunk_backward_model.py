@@ -1,0 +1,107 @@
+"""The chunkwise backward model (tests/chunk_backward_model.py) against torch
+autograd of the token-serial recurrence core, in float64: ragged last chunks,
+every chunk size the kernels use, dk != dv, strong decay (g near K3's bound of
+-5 per token) and beta = 0."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import chunk_backward_model as cbm
+
+pytestmark = pytest.mark.filterwarnings("ignore::DeprecationWarning")
+
+
+def _serial_core_grads(q, k, v, g, beta, S0, dO, dS_T):
+    """The definition, token by token (S' = Diag(e^g) S, u = beta (v - S'^T k),
+    S = S' + k u^T, o = S^T q), differentiated by torch autograd."""
+    torch = pytest.importorskip("torch")
+    t = {n: torch.tensor(a, dtype=torch.float64, requires_grad=True)
+         for n, a in dict(q=q, k=k, v=v, g=g, beta=beta, S0=S0).items()}
+    S = t["S0"]
+    outs = []
+    for i in range(q.shape[0]):
+        Sp = torch.exp(t["g"][i])[:, None] * S
+        u = t["beta"][i] * (t["v"][i] - Sp.T @ t["k"][i])
+        S = Sp + torch.outer(t["k"][i], u)
+        outs.append(S.T @ t["q"][i])
+    O = torch.stack(outs) if outs else torch.zeros((0, v.shape[1]), dtype=torch.float64)
+    loss = (O * torch.tensor(dO)).sum() + (S * torch.tensor(dS_T)).sum()
+    loss.backward()
+    return O.detach().numpy(), S.detach().numpy(), {n: x.grad.numpy() if x.grad is not None else np.zeros_like(x.detach().numpy())
+                                                     for n, x in t.items()}
+
+
+def _case(T, dk, dv, seed, g_scale=1.0, beta_zero=False):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((T, dk)) / np.sqrt(dk)
+    k = rng.standard_normal((T, dk))
+    k /= np.linalg.norm(k, axis=1, keepdims=True)       # k^ is unit-norm after the L2 step
+    v = rng.standard_normal((T, dv))
+    g = -g_scale * np.log1p(np.exp(rng.standard_normal((T, dk)) - 3.0))
+    beta = np.zeros(T) if beta_zero else 1.0 / (1.0 + np.exp(-rng.standard_normal(T)))
+    S0 = 0.1 * rng.standard_normal((dk, dv))
+    dO = rng.standard_normal((T, dv))
+    dS_T = rng.standard_normal((dk, dv))
+    return q, k, v, g, beta, S0, dO, dS_T
+
+
+def _check(args, C, tol=1e-10):
+    q, k, v, g, beta, S0, dO, dS_T = args
+    O_ref, S_ref, ref = _serial_core_grads(*args)
+    O, S_T, _ = cbm.forward(q, k, v, g, beta, S0, C)
+    assert np.allclose(O, O_ref, rtol=0, atol=tol * max(1.0, np.abs(O_ref).max()))
+    assert np.allclose(S_T, S_ref, rtol=0, atol=tol * max(1.0, np.abs(S_ref).max()))
+    got = cbm.backward(q, k, v, g, beta, S0, dO, dS_T, C)
+    for n in ("q", "k", "v", "g", "beta", "S0"):
+        scale = max(1e-300, np.sqrt(np.mean(ref[n] ** 2)))
+        err = np.abs(got[n] - ref[n]).max() / scale if ref[n].size else 0.0
+        assert err <= tol, f"d{n}: max|err|/RMS {err:.3e}"
+
+
+@pytest.mark.parametrize("T,C", [(1, 16), (17, 16), (64, 64), (100, 32), (130, 64), (77, 16)])
+def test_matches_autograd(T, C):
+    _check(_case(T, 16, 16, seed=T + C), C)
+
+
+def test_dk_ne_dv():
+    _check(_case(90, 16, 24, seed=5), 32)
+
+
+def test_strong_decay():
+    """g near K3's bound (-5 per token, e^-80 over a 16-token tile): every decay
+    factor the chunk form uses stays <= 1, so the gradients keep full accuracy."""
+    _check(_case(70, 16, 16, seed=9, g_scale=40.0), 64, tol=1e-9)
+
+
+def test_beta_zero():
+    """beta = 0: U = 0, the state only decays and dv vanishes."""
+    args = _case(50, 8, 8, seed=3, beta_zero=True)
+    _check(args, 16)
+    got = cbm.backward(*args, C=16)
+    assert np.abs(got["v"]).max() == 0.0
+
+
+def test_planted_mistakes_are_caught():
+    """A plausible slip in the derivation (dropping the chunk-level G_C term,
+    through Diag(e^{G_C}) S_in, from dg) moves the gradient far beyond the
+    tolerance, so the comparison above is sensitive to it."""
+    args = _case(40, 8, 8, seed=11)
+    q, k, v, g, beta, S0, dO, dS_T = args
+    _, _, ref = _serial_core_grads(*args)
+    good = cbm.backward(q, k, v, g, beta, S0, dO, dS_T, C=16)
+    assert np.abs(good["g"] - ref["g"]).max() < 1e-9
+    orig = cbm._chunk_backward
+
+    def no_gc(*a):
+        dq, dk, dv, dg, dbeta, dS = orig(*a)
+        f = cbm._chunk_terms(*a[:6])
+        dGC = np.exp(f["GC"]) * np.sum(a[7] * a[5], axis=1)
+        return dq, dk, dv, dg - dGC[None, :], dbeta, dS
+
+    cbm._chunk_backward = no_gc
+    try:
+        bad = cbm.backward(q, k, v, g, beta, S0, dO, dS_T, C=16)
+    finally:
+        cbm._chunk_backward = orig
+    assert np.abs(bad["g"] - ref["g"]).max() > 1e-3
