@@ -124,3 +124,35 @@ def backward(q, k, v, g, beta, S0, dO, dS_T, C=64):
         dq[sl], dk[sl], dv[sl], dg[sl], dbeta[sl], dS = _chunk_backward(
             q[sl], k[sl], v[sl], g[sl], beta[sl], states[n], dO[sl], dS)
     return dict(q=dq, k=dk, v=dv, g=dg, beta=dbeta, S0=dS)
+
+
+def backward_phased(q, k, v, g, beta, S0, dO, dS_T, C=64):
+    """The same gradients in the three phases a kernel set would run:
+      1. every chunk at once, from its entering state: the operands Qg, F, H,
+         T diag(beta), P and e^{G_C};
+      2. one serial pass over the chunks, last first, carrying only dS:
+         dS_in = Diag(e^{G_C}) dS_out + Qg^T dO - F^T Z,
+         Z = diag(beta) T^T (P^T dO + H dS_out)
+         (the transpose of the forward's chunk transition, plus the output term);
+      3. every chunk at once again, from its dS_out: the gradients of q, k, v, g
+         and beta (the chunk reverse above, whose dS_in is not used).
+    Phase 2 is the only sequential part; its work per chunk is the forward
+    recurrence's (a d x C by C x d product chain)."""
+    Tn = q.shape[0]
+    _, _, states = forward(q, k, v, g, beta, S0, C)
+    starts = list(range(0, Tn, C))
+    sls = [slice(c0, min(Tn, c0 + C)) for c0 in starts]
+    ops = [_chunk_terms(q[sl], k[sl], v[sl], g[sl], beta[sl], states[n]) for n, sl in enumerate(sls)]
+    dS_out = [None] * len(sls)
+    dS = dS_T.copy()
+    for n in range(len(sls) - 1, -1, -1):
+        f, sl = ops[n], sls[n]
+        dS_out[n] = dS
+        Z = beta[sl][:, None] * (f["T"].T @ (f["P"].T @ dO[sl] + f["H"] @ dS))
+        dS = np.exp(f["GC"])[:, None] * dS + f["Qg"].T @ dO[sl] - f["F"].T @ Z
+    out = dict(q=np.zeros_like(q), k=np.zeros_like(k), v=np.zeros_like(v), g=np.zeros_like(g),
+               beta=np.zeros_like(beta), S0=dS)
+    for n, sl in enumerate(sls):
+        dq, dk, dv, dg, db, _ = _chunk_backward(q[sl], k[sl], v[sl], g[sl], beta[sl], states[n], dO[sl], dS_out[n])
+        out["q"][sl], out["k"][sl], out["v"][sl], out["g"][sl], out["beta"][sl] = dq, dk, dv, dg, db
+    return out

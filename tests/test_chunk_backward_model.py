@@ -105,3 +105,14 @@ def test_planted_mistakes_are_caught():
     finally:
         cbm._chunk_backward = orig
     assert np.abs(bad["g"] - ref["g"]).max() > 1e-3
+
+
+@pytest.mark.parametrize("T,C", [(130, 64), (77, 16)])
+def test_phased_equals_chunk_by_chunk(T, C):
+    """The three-phase order (operands of every chunk, the serial dS pass, the
+    gradients of every chunk) gives the chunk-by-chunk reverse's gradients."""
+    args = _case(T, 16, 16, seed=T)
+    a = cbm.backward(*args, C=C)
+    b = cbm.backward_phased(*args, C=C)
+    for n in a:
+        assert np.allclose(a[n], b[n], rtol=1e-12, atol=1e-12 * max(1.0, np.abs(a[n]).max())), n
