@@ -3,8 +3,8 @@ tests; shares no code with the GPU library).
 
 The forward is written once more, token by token, in plain PyTorch CPU ops in
 float64, and differentiated by torch.autograd: the reference for the backward
-pass the survey's training workload needs (1M-token context in "Gemma 4 31B vs
-Kimi K3", component table, long-context training row).  The definition is the
+pass that training at the pages' long context needs (1M-token context in
+"Gemma 4 31B vs Kimi K3", component table, long-context training row).  The definition is the
 one `oracle.prefill` computes ("Kimi K3, previewed", section "Kimi Delta
 Attention - the workhorse"; the component tables of "Kimi K3.1 Pro vs
 gpt-oss-120b" and "Gemma 4 31B vs Kimi K3", rows "Gated DeltaNet / KDA" and
