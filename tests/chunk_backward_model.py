@@ -156,3 +156,60 @@ def backward_phased(q, k, v, g, beta, S0, dO, dS_T, C=64):
         dq, dk, dv, dg, db, _ = _chunk_backward(q[sl], k[sl], v[sl], g[sl], beta[sl], states[n], dO[sl], dS_out[n])
         out["q"][sl], out["k"][sl], out["v"][sl], out["g"][sl], out["beta"][sl] = dq, dk, dv, dg, db
     return out
+
+
+L2_EPS = 1e-6
+RMS_EPS = 1e-5
+
+
+def _sig(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def backward_pair_chunkwise(raw, hist, w, g, beta, gate, S0, dO, dS_T, chunk=64, dC=None):
+    """The whole backward of one (b, h), with the arguments and results of the
+    token-by-token model (tests/backward_model.py, backward_pair), organised as
+    a chunkwise kernel set would be: per-token work (conv, SiLU, norms, the
+    RMSNorm * sigmoid(gate) backward, the norm / SiLU / conv-transpose backward)
+    on all tokens at once, and the recurrence core's gradients by the three
+    phases of backward_phased."""
+    T, nc = raw.shape
+    d = nc // 3
+    full = np.concatenate([hist, raw], axis=0)              # row t + 3 = token t
+    a = w[:, 0] * full[0:T] + w[:, 1] * full[1:T + 1] + w[:, 2] * full[2:T + 2] + w[:, 3] * full[3:T + 3]
+    x = a * _sig(a)
+    qt, kt, vn = x[:, :d], x[:, d:2 * d], x[:, 2 * d:]
+    nq = np.sum(qt * qt, axis=1) + L2_EPS
+    nk = np.sum(kt * kt, axis=1) + L2_EPS
+    rq, rk = nq ** -0.5 / np.sqrt(d), nk ** -0.5
+    qn, kn = qt * rq[:, None], kt * rk[:, None]
+    z, _, _ = forward(qn, kn, vn, g, beta, S0, chunk)
+    # RMSNorm * sigmoid(gate), per token
+    r = np.sqrt(np.mean(z * z, axis=1) + RMS_EPS)
+    n = z / r[:, None]
+    s = _sig(gate)
+    dgate = dO * n * s * (1 - s)
+    dn = dO * s
+    dz = (dn - n * np.mean(dn * n, axis=1, keepdims=True)) / r[:, None]
+    core = backward_phased(qn, kn, vn, g, beta, S0, dz, dS_T, chunk)
+    dqn, dkn, dvn = core["q"], core["k"], core["v"]
+    # L2 norms, SiLU, conv transpose
+    dqt = rq[:, None] * (dqn - qt * (np.sum(qt * dqn, axis=1) / nq)[:, None])
+    dkt = rk[:, None] * (dkn - kt * (np.sum(kt * dkn, axis=1) / nk)[:, None])
+    dx = np.concatenate([dqt, dkt, dvn], axis=1)
+    sa = _sig(a)
+    da = dx * sa * (1 + a * (1 - sa))
+    pad = np.concatenate([da, np.zeros((3, nc))], axis=0)  # da of tokens t .. t + 3
+    draw = w[:, 3] * pad[0:T] + w[:, 2] * pad[1:T + 1] + w[:, 1] * pad[2:T + 2] + w[:, 0] * pad[3:T + 3]
+    dhist = np.zeros((3, nc))
+    for hr in range(3):                                     # history row hr is token hr - 3
+        for t in range(0, min(hr + 1, T)):
+            dhist[hr] += w[:, hr - t] * da[t]
+    if dC is not None:                                      # conv_out's rows: the last three raw rows
+        for kk in range(3):
+            t = T - 3 + kk
+            if t >= 0:
+                draw[t] += dC[kk]
+            else:
+                dhist[t + 3] += dC[kk]
+    return draw, dhist, core["g"], core["beta"], dgate, core["S0"]

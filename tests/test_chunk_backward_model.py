@@ -116,3 +116,37 @@ def test_phased_equals_chunk_by_chunk(T, C):
     b = cbm.backward_phased(*args, C=C)
     for n in a:
         assert np.allclose(a[n], b[n], rtol=1e-12, atol=1e-12 * max(1.0, np.abs(a[n]).max())), n
+
+
+@pytest.mark.parametrize("T,chunk,dtype", [(20, 8, "f32"), (37, 16, "bf16"), (2, 16, "f32"), (70, 32, "bf16")])
+def test_whole_backward_chunkwise_equals_autograd(T, chunk, dtype):
+    """The whole backward (conv, SiLU, norms, RMSNorm * sigmoid(gate) around the
+    chunkwise core) against the fp64 autograd reference on the prefill inputs:
+    ragged chunks, bf16 inputs, fewer tokens than the conv history."""
+    ob = pytest.importorskip("oracle.backward")
+    import backward_model as bm
+    import kda_synth as syn
+    from kda_synth import Workload
+    w = Workload("cbm", 2, T, 2, 8, 8, 16, dtype, s0_sigma=0.3, conv_hist="normal", seed=7 + T)
+    inp = syn.prefill_inputs_np(w)
+    rng = np.random.default_rng(T + 1)
+    f = ob.forward(inp)
+    dO = rng.standard_normal(f["o"].shape)
+    dS = rng.standard_normal(f["S_T"].shape)
+    dC = rng.standard_normal(f["conv_out"].shape)
+    ref = ob.backward(inp, dO, dS, dC)
+    orig = bm.backward_pair
+    calls = []
+
+    def chunkwise(*a, **kw):
+        calls.append(1)
+        return cbm.backward_pair_chunkwise(*a, **kw)
+
+    bm.backward_pair = chunkwise      # the same per-(b, h) layout handling
+    try:
+        got = bm.backward(inp, dO, dS, chunk=chunk, dconv_out=dC)
+    finally:
+        bm.backward_pair = orig
+    assert len(calls) == 2 * 2        # every (b, h) went through the chunkwise model
+    for x in ref:
+        assert np.abs(got[x] - ref[x]).max() <= 1e-10 * max(1.0, np.abs(ref[x]).max()), x
