@@ -36,7 +36,9 @@ def _chunk_terms(q, k, v, g, beta, S_in):
     C = q.shape[0]
     G = np.cumsum(g, axis=0)
     GC = G[-1]
-    E = np.exp(G[:, None, :] - G[None, :, :])         # [i, j, c] e^{G_i - G_j}
+    # [i, j, c] e^{G_i - G_j}; only j <= i is used (exponent <= 0), the rest is
+    # clamped so that it cannot overflow in float32
+    E = np.exp(np.minimum(G[:, None, :] - G[None, :, :], 0.0))
     low = np.tril(np.ones((C, C)), -1)                  # j < i
     lowd = np.tril(np.ones((C, C)))                     # j <= i
     Ap = np.einsum("ic,jc,ijc->ij", k, k, E) * low      # A' (without beta)

@@ -150,3 +150,20 @@ def test_whole_backward_chunkwise_equals_autograd(T, chunk, dtype):
     assert len(calls) == 2 * 2        # every (b, h) went through the chunkwise model
     for x in ref:
         assert np.abs(got[x] - ref[x]).max() <= 1e-10 * max(1.0, np.abs(ref[x]).max()), x
+
+
+def test_float32_chunks_of_32_within_the_backward_bound():
+    """The chunk form in float32 (the precision a matrix-core kernel would use)
+    at K3-like decay (mean about -0.6 per token, tails near -8): every gradient
+    within 5e-5 x RMS of float64 for 32-token chunks, under the 1e-4 bound of
+    the GPU backward.  Token by token float32 is about 5e-6; the error grows
+    with the chunk length under strong decay (through the decay-weighted row
+    and column sums and the reverse cumulative sum of dG), so longer chunks
+    would need more care."""
+    args = _case(128, 64, 64, seed=64, g_scale=8.0)
+    ref = cbm.backward(*args, C=32)
+    got = cbm.backward(*[np.asarray(x, dtype=np.float32) for x in args], C=32)
+    assert got["g"].dtype == np.float32
+    for n in ref:
+        err = np.abs(got[n].astype(np.float64) - ref[n]).max() / np.sqrt(np.mean(ref[n] ** 2))
+        assert err <= 5e-5, f"d{n}: {err:.2e}"
